@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Throughput of one Parallel Transformer Block layer, forward + backward, on
+one MI355X, in model TFLOP/s and as a fraction of the dense bf16 MFMA peak.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one forward and one backward of the whole layer stack of the
+workload (every kernel of the hot path) on resident, seeded synthetic bf16
+inputs.  W untimed warm-up steps, then exactly K steps between two
+device-synchronised HIP events.  Model FLOPs follow the Megatron tuning post's
+MFU section (6 per weight per token plus the attention term, recompute
+excluded) made exact for the sliding window (transformer_block_amd/flops.py).
+
+Prints one JSON line.  Besides the throughput it carries:
+  roofline:     the dominant kernel (largest device time per step), its
+                algorithmic FLOPs per launch over its mean launch time measured
+                with HIP events recorded around it on the library's stream;
+  cpu_baseline: the fp64 oracle timed on host cores on a bounded sample of the
+                same workload (a reported baseline, not a target);
+  stages:       mean device time per kernel stage.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "model TFLOP/s + MFU vs bf16 MFMA peak, PTB layer fwd+bwd, 1 MI355X"
+DEFAULT_WORKLOAD = "gpt175b_tp8_share_s2048"
+
+
+def stage_work(w):
+    """Algorithmic work per launch of each stage: (kind, amount)."""
+    from transformer_block_amd.flops import window_pairs
+    T, h, hl, f = w.tokens, w.hidden, w.h_local, w.ffn
+    N1, K2 = 3 * hl + f, hl + f
+    attn_pairs = w.batch * w.heads * window_pairs(w.seq, w.window)
+    fwd = {
+        "layernorm_fwd": ("bytes", T * h * 2 * 2 + T * 8),
+        "gemm_qkv_fc1": ("flops", 2 * T * h * N1),
+        "attention_fwd": ("flops", 2 * 2 * attn_pairs * w.head_dim),
+        "gemm_o_fc2_residual": ("flops", 2 * T * K2 * h),
+    }
+    bwd = {
+        "gemm_dgrad_o_fc2": ("flops", 2 * T * h * K2),
+        "attention_bwd": ("flops", 4 * 2 * attn_pairs * w.head_dim),
+        "gemm_wgrad_o_fc2": ("flops", 2 * K2 * T * h),
+        "gemm_dgrad_qkv_fc1": ("flops", 2 * T * N1 * h),
+        "gemm_wgrad_qkv_fc1": ("flops", 2 * h * T * N1),
+        # da (fp32) + x + dy read, dx written
+        "layernorm_bwd": ("bytes", T * h * (4 + 2 + 2 + 2) + T * 8),
+    }
+    return fwd, bwd
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        self.events.extend(out)
+        return out
+
+    def ms(self, a, b) -> float:
+        t = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(t), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return t.value
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the fp64 oracle (as it stands) on a bounded sample of `w`."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import ptb_oracle as O
+    from transformer_block_amd import inputs as I
+    from transformer_block_amd.flops import model_flops
+
+    # One layer; trim the batch, then the sequence, until the estimated fp64
+    # work fits the budget at ~0.25 TFLOP/s.
+    b, s = w.batch, w.seq
+    est = lambda bb, ss: model_flops(bb, ss, w.hidden, w.heads, w.head_dim, w.ffn,
+                                     min(w.window, ss)) / 0.25e12
+    while b > 1 and est(b, s) > budget_s:
+        b -= 1
+    while s > 128 and est(b, s) > budget_s:
+        s //= 2
+    sw = w.replace(batch=b, seq=s, layers=1)
+    inp = I.make_inputs(sw)
+    f = I.bf16_bits_to_f64
+    x, dy = f(inp["x"]), f(inp["dy"])
+    p = {k: f(v) for k, v in inp["layers"][0].items()}
+    t0 = time.perf_counter()
+    y, cache = O.ptb_forward(x, p, sw.batch, sw.seq, sw.heads, sw.head_dim, sw.window,
+                             sw.ln_eps)
+    O.ptb_backward(dy, cache, p, sw.window)
+    dt = time.perf_counter() - t0
+    fl = model_flops(sw.batch, sw.seq, sw.hidden, sw.heads, sw.head_dim, sw.ffn, sw.window)
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()
+                   if d.get("user_api") == "blas"] or [1])
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"one layer fwd+bwd at batch {sw.batch}, seq {sw.seq}, window "
+                      f"{min(sw.window, sw.seq)} (hidden {sw.hidden}, heads {sw.heads}x"
+                      f"{sw.head_dim}, ffn {sw.ffn}); fp64 numpy; {dt:.1f} s wall",
+            "seconds": dt}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is benchmarked on one GPU's share of the work)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from transformer_block_amd import inputs as I
+    from transformer_block_amd import ptb as P
+    from transformer_block_amd.flops import workload_model_flops, workload_recompute_flops
+    from transformer_block_amd.runner import LayerStack
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    P.load_library()
+    w = I.WORKLOADS[args.workload]
+    print(f"bench: workload {w.name} steps {args.steps} warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+    inp = I.make_inputs(w)
+    st = LayerStack(w, inp, "cuda")
+    stream = torch.cuda.current_stream()
+    ev = HipEvents()
+
+    for _ in range(args.warmup):
+        st.step(stream)
+    torch.cuda.synchronize()
+
+    L = w.layers
+    K = args.steps
+    fwd_ev = [[ev.create(2 * P.PTB_FWD_STAGES) for _ in range(L)] for _ in range(K)]
+    bwd_ev = [[ev.create(2 * P.PTB_BWD_STAGES) for _ in range(L)] for _ in range(K)]
+    t_start, t_end = ev.create(2)
+    torch.cuda.synchronize()
+    hip = ev.hip
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    wall0 = time.perf_counter()
+    hip.hipEventRecord(t_start, stream.cuda_stream)
+    for k in range(K):
+        st.step(stream, fwd_ev[k], bwd_ev[k])
+    hip.hipEventRecord(t_end, stream.cuda_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = ev.ms(t_start, t_end) / K
+
+    fwd_work, bwd_work = stage_work(w)
+    stages = {}
+    for names, evs in ((P.FWD_STAGE_NAMES, fwd_ev), (P.BWD_STAGE_NAMES, bwd_ev)):
+        for i, name in enumerate(names):
+            tot = sum(ev.ms(evs[k][l][2 * i], evs[k][l][2 * i + 1])
+                      for k in range(K) for l in range(L))
+            stages[name] = tot / (K * L)            # mean ms per launch
+    ev.close()
+
+    F = workload_model_flops(w)
+    R = workload_recompute_flops(w)
+    tflops = F / (ms_step * 1e-3) / 1e12
+    work = dict(fwd_work)
+    work.update(bwd_work)
+    dom = max(stages, key=lambda n: stages[n])
+    kind, amount = work[dom]
+    if kind == "flops":
+        ach = amount / (stages[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": dom, "per_launch": amount, "ms_per_launch": round(stages[dom], 4)}
+    else:
+        ach = amount / (stages[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": dom, "per_launch": amount, "ms_per_launch": round(stages[dom], 4)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, bf16)",
+        "config": {"workload": w.name, "batch": w.batch, "seq": w.seq, "hidden": w.hidden,
+                   "heads": w.heads, "head_dim": w.head_dim, "ffn": w.ffn,
+                   "window": w.window, "layers": w.layers, "model_flops_per_step": F},
+        "mfu": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "hfu": round((F + R) / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the fp64 oracle on host cores", file=sys.stderr, flush=True)
+        cb = cpu_baseline(w, args.cpu_budget_s)
+        cb.pop("seconds", None)
+        cb["value"] = round(cb["value"], 5)
+        out["cpu_baseline"] = cb
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

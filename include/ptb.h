@@ -1,0 +1,181 @@
+/*
+ * ptb.h -- C ABI of libptb: one Parallel Transformer Block (PTB) layer,
+ * forward and backward, on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer (MegaScale reading notes, "MegaScale: ByteDance 如何在 12,288 块
+ * GPU 上实现 55% MFU 的大规模 LLM 训练", section 1.1, eq (4)):
+ *
+ *     a = LN(x)                       LayerNorm with gamma, beta, eps
+ *     y = x + Attn(a) W_o + GeLU(a W_fc1) W_fc2
+ *     Attn: causal sliding-window attention per head (same notes, section 1.1,
+ *           eq (5)-(6)): query i sees the `window` most recent tokens, itself
+ *           included (keys j with 0 <= i - j < window); softmax scale
+ *           1/sqrt(head_dim); q, k, v are column blocks of a W_qkv.
+ *     MLP:  Y = GeLU(X A) B with exact-erf GeLU, no biases (Megatron-LM
+ *           tensor-parallel explainer, section 2.1).
+ *
+ * Both branches read the same LayerNorm output.  The backward recomputes the
+ * attention probabilities from the saved log-sum-exp instead of storing them
+ * (selective recompute of the core attention: MegaScale notes, section 1.3;
+ * Megatron tuning post "显存与性能调优", recompute section).
+ *
+ * Tensors.  Every tensor argument is a DEVICE pointer to bfloat16 values
+ * (stored as raw 16-bit words), row-major and contiguous, 16-byte aligned.
+ * T = batch*seq tokens, token t = batch_index*seq + position.
+ * h = hidden, h_l = heads*head_dim, f = ffn.
+ *     x, y, dy, dx  [T, h]
+ *     ln_gamma, ln_beta, d_ln_gamma, d_ln_beta  [h]
+ *     w_qkv  [h, 3*h_l]   columns [Q heads | K heads | V heads]; head j's
+ *                         head_dim columns are contiguous inside each block
+ *     w_o    [h_l, h]     rows in the same head order
+ *     w_fc1  [h, f]
+ *     w_fc2  [f, h]
+ * Gradients have the shape of what they differentiate.  Arithmetic is bf16
+ * operands with fp32 accumulation; LayerNorm statistics and the attention
+ * log-sum-exp are fp32.
+ *
+ * Ownership and lifetime.  The caller allocates and owns every buffer,
+ * including `saved` (ptb_saved_bytes) and `workspace` (ptb_workspace_bytes).
+ * The library allocates nothing and holds no mutable global state, so calls
+ * on different streams with different buffers may run concurrently.  `saved`
+ * is written by ptb_forward and read by ptb_backward; it must stay untouched
+ * in between.  Outputs are overwritten, never accumulated into.
+ *
+ * Asynchrony.  `stream` is a hipStream_t (NULL = the default stream).  Calls
+ * only enqueue kernels on it and never synchronise; a fault inside a kernel
+ * surfaces at the caller's next synchronisation of that stream.
+ *
+ * Errors.  Every entry point returns PTB_OK (0) or a negative PTB_ERR_* code.
+ * All argument checks are done on the host before the first HIP call, so an
+ * invalid call enqueues nothing.  PTB_ERR_HIP reports a failed kernel launch
+ * (hipGetLastError after a launch).  No C++ exception crosses this boundary.
+ */
+#ifndef PTB_H_
+#define PTB_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PTB_ABI_VERSION 1
+
+enum ptb_status {
+  PTB_OK = 0,
+  PTB_ERR_NULL = -1,      /* a required pointer is NULL                         */
+  PTB_ERR_DIMS = -2,      /* a size is < 1, not a multiple of 64 where required,
+                             or too large (see ptb_validate_dims)               */
+  PTB_ERR_HEAD_DIM = -3,  /* head_dim is not 64 or 128                          */
+  PTB_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned                   */
+  PTB_ERR_WINDOW = -5,    /* window < 1                                         */
+  PTB_ERR_EPS = -6,       /* ln_eps is not a finite positive number             */
+  PTB_ERR_HIP = -7        /* a kernel launch failed                             */
+};
+
+typedef struct ptb_dims {
+  int32_t batch;     /* b >= 1                                                */
+  int32_t seq;       /* s >= 1                                                */
+  int32_t hidden;    /* h: multiple of 64, 64 <= h <= 16384                   */
+  int32_t heads;     /* n >= 1 (heads of this GPU's share)                    */
+  int32_t head_dim;  /* d: 64 or 128                                          */
+  int32_t ffn;       /* f: multiple of 64, >= 64                              */
+  int32_t window;    /* w >= 1; w >= seq is full causal attention             */
+  float ln_eps;      /* LayerNorm epsilon, added to the variance, > 0         */
+} ptb_dims;
+
+/* Version of this ABI (PTB_ABI_VERSION). */
+int32_t ptb_abi_version(void);
+
+/* Static description of a status code.  Never NULL. */
+const char* ptb_status_string(int32_t status);
+
+/* Check `dims` alone.  Besides the per-field rules above, every tensor of the
+ * layer must hold fewer than 2^31 elements (T*(3*h_l+f), h*(3*h_l+f), ...). */
+int32_t ptb_validate_dims(const ptb_dims* dims);
+
+/* Bytes of the forward->backward stash of one layer (`saved`). */
+int32_t ptb_saved_bytes(const ptb_dims* dims, size_t* bytes);
+
+/* Bytes of backward scratch (`workspace`). */
+int32_t ptb_workspace_bytes(const ptb_dims* dims, size_t* bytes);
+
+/* Byte offsets inside `saved` of what ptb_forward stores there, for
+ * inspection by tests and tools (the backward needs no caller help):
+ *   PTB_SAVED_A    a = LN(x)                 bf16 [T, h]
+ *   PTB_SAVED_MU   row mean of x             fp32 [T]
+ *   PTB_SAVED_RSTD 1/sqrt(var + eps)         fp32 [T]
+ *   PTB_SAVED_QKV  a W_qkv                   bf16 [T, 3*h_l]
+ *   PTB_SAVED_U    a W_fc1 (pre-activation)  bf16 [T, f]
+ *   PTB_SAVED_G    GeLU(u)                   bf16 [T, f]
+ *   PTB_SAVED_C    attention output          bf16 [T, h_l] (head-major cols)
+ *   PTB_SAVED_LSE  base-2 log-sum-exp of the logits scaled by log2(e)/sqrt(d)
+ *                                            fp32 [b, n, s]
+ * `offsets` must have room for PTB_SAVED_COUNT entries. */
+enum ptb_saved_slot {
+  PTB_SAVED_A = 0, PTB_SAVED_MU, PTB_SAVED_RSTD, PTB_SAVED_QKV, PTB_SAVED_U,
+  PTB_SAVED_G, PTB_SAVED_C, PTB_SAVED_LSE, PTB_SAVED_COUNT
+};
+int32_t ptb_saved_layout(const ptb_dims* dims, size_t* offsets);
+
+/* Forward of one layer (MegaScale notes, section 1.1, eq (4)):
+ *   y = x + Attn(LN(x)) + MLP(LN(x)).
+ * Writes y [T, h] and fills `saved` (ptb_saved_bytes(dims) bytes). */
+int32_t ptb_forward(const ptb_dims* dims,
+                    const void* x,
+                    const void* ln_gamma, const void* ln_beta,
+                    const void* w_qkv, const void* w_o,
+                    const void* w_fc1, const void* w_fc2,
+                    void* y, void* saved, void* stream);
+
+/* Backward of one layer for upstream gradient dy [T, h], reading the `saved`
+ * of the matching ptb_forward and the same x and weights.  Writes dx (which
+ * includes the residual path dy), d_ln_gamma, d_ln_beta and the four weight
+ * gradients.  `workspace` holds ptb_workspace_bytes(dims) bytes of scratch. */
+int32_t ptb_backward(const ptb_dims* dims,
+                     const void* dy, const void* x,
+                     const void* ln_gamma,
+                     const void* w_qkv, const void* w_o,
+                     const void* w_fc1, const void* w_fc2,
+                     const void* saved,
+                     void* dx, void* d_ln_gamma, void* d_ln_beta,
+                     void* dw_qkv, void* dw_o, void* dw_fc1, void* dw_fc2,
+                     void* workspace, void* stream);
+
+/* Stage timing.  The same calls with an array of hipEvent_t handles
+ * (`stage_events`, 2 per stage, NULL entries skipped): event 2*i is recorded on
+ * `stream` right before stage i is enqueued and event 2*i+1 right after it, so
+ * hipEventElapsedTime(events[2i], events[2i+1]) is the device time of stage i.
+ * The events are created and owned by the caller.  Stages:
+ *   forward  (PTB_FWD_STAGES = 4): 0 LayerNorm, 1 [QKV | FC1] GEMM + GeLU,
+ *            2 attention, 3 [O ; FC2] GEMM + residual;
+ *   backward (PTB_BWD_STAGES = 6): 0 dgrad [O ; FC2] + GeLU', 1 attention
+ *            backward (3 kernels), 2 wgrad [O ; FC2], 3 dgrad [QKV | FC1],
+ *            4 wgrad [QKV | FC1], 5 LayerNorm backward (2 kernels).
+ * Each GEMM stage is exactly one kernel launch. */
+#define PTB_FWD_STAGES 4
+#define PTB_BWD_STAGES 6
+int32_t ptb_forward_timed(const ptb_dims* dims,
+                          const void* x,
+                          const void* ln_gamma, const void* ln_beta,
+                          const void* w_qkv, const void* w_o,
+                          const void* w_fc1, const void* w_fc2,
+                          void* y, void* saved, void* stream,
+                          void* const* stage_events);
+int32_t ptb_backward_timed(const ptb_dims* dims,
+                           const void* dy, const void* x,
+                           const void* ln_gamma,
+                           const void* w_qkv, const void* w_o,
+                           const void* w_fc1, const void* w_fc2,
+                           const void* saved,
+                           void* dx, void* d_ln_gamma, void* d_ln_beta,
+                           void* dw_qkv, void* dw_o, void* dw_fc1, void* dw_fc2,
+                           void* workspace, void* stream,
+                           void* const* stage_events);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* PTB_H_ */

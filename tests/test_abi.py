@@ -1,0 +1,115 @@
+"""The C-ABI library: it loads, exports every function include/ptb.h declares,
+and rejects invalid arguments with the documented status codes before any HIP
+call (so these run on a machine without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from transformer_block_amd import ptb as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ptb.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ptb_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(P.LIB_PATH):
+        pytest.fail("libptb.so is not built (run __graft_entry__.build())")
+    return P.load_library()
+
+
+def test_library_exports_every_declared_function(lib):
+    declared = _declared_functions()
+    assert declared, "no declarations parsed from include/ptb.h"
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in ptb.h but not exported"
+    assert set(declared) == set(P.exported_symbols())
+
+
+def test_version_and_status_strings(lib):
+    assert P.ptb_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert P.ptb_status_string(code) and P.ptb_status_string(code) != "unknown status"
+    assert P.ptb_status_string(12345) == "unknown status"
+
+
+def good_dims(**kw):
+    base = dict(batch=2, seq=256, hidden=256, heads=4, head_dim=64, ffn=1024, window=64,
+                ln_eps=1e-5)
+    base.update(kw)
+    return P.ptb_dims(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), P.PTB_OK),
+    (dict(batch=0), P.PTB_ERR_DIMS),
+    (dict(seq=0), P.PTB_ERR_DIMS),
+    (dict(heads=0), P.PTB_ERR_DIMS),
+    (dict(hidden=100), P.PTB_ERR_DIMS),
+    (dict(hidden=32768), P.PTB_ERR_DIMS),
+    (dict(ffn=96), P.PTB_ERR_DIMS),
+    (dict(head_dim=96), P.PTB_ERR_HEAD_DIM),
+    (dict(head_dim=256), P.PTB_ERR_HEAD_DIM),
+    (dict(window=0), P.PTB_ERR_WINDOW),
+    (dict(window=-3), P.PTB_ERR_WINDOW),
+    (dict(ln_eps=0.0), P.PTB_ERR_EPS),
+    (dict(ln_eps=float("nan")), P.PTB_ERR_EPS),
+    (dict(ln_eps=float("inf")), P.PTB_ERR_EPS),
+    (dict(batch=65536, seq=65536), P.PTB_ERR_DIMS),   # T*(3*h_l+f) >= 2^31
+    (dict(window=1), P.PTB_OK),
+    (dict(seq=1, window=10 ** 9), P.PTB_OK),
+])
+def test_validate_dims(lib, kw, code):
+    assert P.ptb_validate_dims(good_dims(**kw)) == code
+
+
+def test_null_dims_pointer(lib):
+    assert lib.ptb_validate_dims(None) == P.PTB_ERR_NULL
+    n = ctypes.c_size_t(0)
+    assert lib.ptb_saved_bytes(None, ctypes.byref(n)) == P.PTB_ERR_NULL
+    assert lib.ptb_saved_bytes(ctypes.byref(good_dims()), None) == P.PTB_ERR_NULL
+
+
+def test_saved_layout_is_ordered_aligned_and_sized(lib):
+    d = good_dims()
+    lay = P.ptb_saved_layout(d)
+    offs = [lay[k] for k in P.SAVED_SLOTS]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    T, h, hl, f = 512, 256, 256, 1024
+    sizes = dict(a=T * h * 2, mu=T * 4, rstd=T * 4, qkv=T * 3 * hl * 2, u=T * f * 2,
+                 g=T * f * 2, c=T * hl * 2, lse=2 * 4 * 256 * 4)
+    for a_, b_ in zip(P.SAVED_SLOTS, P.SAVED_SLOTS[1:]):
+        assert lay[b_] - lay[a_] >= sizes[a_]
+    assert P.ptb_saved_bytes(d) >= lay["lse"] + sizes["lse"]
+    assert P.ptb_workspace_bytes(d) >= T * (3 * hl + f) * 2 + T * h * 4
+
+
+def test_forward_backward_reject_null_and_misaligned_before_any_hip_call(lib):
+    d = good_dims()
+    A = 0x10000  # never dereferenced: the checks fail first
+    assert P.ptb_forward(d, *([0] * 9), stream=0, check=False) == P.PTB_ERR_NULL
+    args = [A] * 9
+    args[4] = A + 8
+    assert P.ptb_forward(d, *args, stream=0, check=False) == P.PTB_ERR_ALIGN
+    assert P.ptb_backward(d, *([A] * 15), None, stream=0, check=False) == P.PTB_ERR_NULL
+    bargs = [A] * 16
+    bargs[15] = A + 2
+    assert P.ptb_backward(d, *bargs, stream=0, check=False) == P.PTB_ERR_ALIGN
+    bad = good_dims(head_dim=32)
+    assert P.ptb_forward(bad, *([A] * 9), stream=0, check=False) == P.PTB_ERR_HEAD_DIM
+    assert P.ptb_backward(good_dims(window=0), *([A] * 16), stream=0,
+                          check=False) == P.PTB_ERR_WINDOW
+
+
+def test_error_raises_in_checked_mode(lib):
+    with pytest.raises(P.PtbError) as ei:
+        P.ptb_forward(good_dims(batch=0), *([0x10000] * 9), stream=0)
+    assert ei.value.status == P.PTB_ERR_DIMS

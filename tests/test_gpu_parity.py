@@ -1,0 +1,109 @@
+"""Parity of the HIP path (called through the C ABI) with the fp64 oracle.
+
+Each case draws seeded bf16 inputs, runs the layer (or the stack) forward and
+backward on the GPU and in the oracle, and compares every output by relative
+Frobenius error against the bar REL_TOL = 1e-2 (bf16 operands, fp32
+accumulation).  The residual paths dominate y and dx, so y - x and dx - dy are
+compared as well, against a bar that adds the bf16 rounding floor of the
+output to the 1e-2 relative error of the branch.  The layer-0 intermediates the forward stashes (LayerNorm
+output, QKV, u, GeLU(u), attention output, log-sum-exp) are checked too, which
+localises a failure to one kernel.
+"""
+import numpy as np
+import pytest
+import torch
+
+from transformer_block_amd import inputs as I
+from transformer_block_amd.runner import LayerStack, bf16_to_numpy_f64
+
+from .helpers import REL_TOL, log, oracle_lse2, oracle_run, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+W = I.Workload
+EDGE_CASES = [
+    # name, workload, random LayerNorm parameters
+    ("tiny_workload", I.WORKLOADS["tiny_h256_s256_w64"], False),
+    ("tiny_workload_random_ln", I.WORKLOADS["tiny_h256_s256_w64"], True),
+    ("ragged_s200_w37_d128", W("r1", 1, 200, 256, 2, 128, 320, 37, seed=11), True),
+    ("window1_d128", W("w1", 2, 160, 256, 2, 128, 256, 1, seed=12), False),
+    ("window63", W("w63", 1, 300, 192, 2, 128, 192, 63, seed=13), False),
+    ("window64", W("w64", 1, 300, 192, 2, 128, 192, 64, seed=14), False),
+    ("window65", W("w65", 1, 300, 192, 2, 128, 192, 65, seed=15), False),
+    ("window127", W("w127", 1, 300, 192, 2, 128, 192, 127, seed=16), False),
+    ("window128", W("w128", 1, 300, 192, 2, 128, 192, 128, seed=17), False),
+    ("window129", W("w129", 1, 300, 192, 2, 128, 192, 129, seed=18), False),
+    ("window_eq_seq", W("wseq", 2, 257, 256, 2, 128, 256, 257, seed=19), False),
+    ("window_gt_seq", W("wbig", 1, 131, 256, 3, 64, 320, 100000, seed=20), True),
+    ("d64_ragged", W("d64", 3, 97, 320, 5, 64, 448, 33, seed=21), True),
+    ("single_token", W("s1", 1, 1, 128, 1, 128, 128, 1, seed=22), True),
+    ("two_tokens_batch3", W("s2", 3, 2, 128, 2, 64, 128, 5, seed=23), False),
+    ("stack2_small", W("st2", 2, 130, 256, 2, 128, 512, 48, layers=2, seed=24), True),
+]
+
+
+def _to_np(t):
+    if t.dtype == torch.bfloat16:
+        return bf16_to_numpy_f64(t)
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def run_gpu(w, inp):
+    st = LayerStack(w, inp, "cuda")
+    st.step()
+    torch.cuda.synchronize()
+    return st
+
+
+def compare(w, inp, ref, st, tol=REL_TOL, check_intermediates=True):
+    errs = {}
+    y = _to_np(st.y)
+    dx = _to_np(st.dx)
+    errs["y"] = rel_fro(y, ref["y"])
+    errs["dx"] = rel_fro(dx, ref["dx"])
+    # The branch outputs y - x and dx - dy: y and dx are bf16 outputs, so their
+    # own rounding (at most 2^-8 relative per element) is an error floor that
+    # the subtraction of the residual does not remove.  The bar for these two
+    # is tol * ||branch|| + 2^-8 * ||output||, expressed relative to ||branch||.
+    for key, got, out_ref, res in (("y-x", y, ref["y"], ref["x"]),
+                                   ("dx-dy", dx, ref["dx"], ref["dy"])):
+        branch = out_ref - res
+        floor = 2.0 ** -8 * np.linalg.norm(out_ref) / max(np.linalg.norm(branch), 1e-300)
+        errs[key] = rel_fro(got - res, branch) / (1.0 + floor / tol)
+    for li, g in enumerate(ref["grads"]):
+        for k in ("d_ln_gamma", "d_ln_beta", "dw_qkv", "dw_o", "dw_fc1", "dw_fc2"):
+            errs[f"L{li}.{k}"] = rel_fro(_to_np(st.grads[li][k]), g[k])
+    if check_intermediates:
+        c0 = ref["caches"][0]
+        for name, key in (("a", "a"), ("qkv", "qkv"), ("u", "u"), ("g", "g"), ("c", "c"),
+                          ("mu", "mu"), ("rstd", "rstd")):
+            errs[f"L0.{name}"] = rel_fro(_to_np(st.saved_tensor(0, name)), c0[key])
+        lse = _to_np(st.saved_tensor(0, "lse"))
+        lse_ref = oracle_lse2(c0, w)
+        errs["L0.lse(abs)"] = float(np.max(np.abs(lse - lse_ref)))
+    log(f"[{w.name}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not np.isfinite(v) or v > tol}
+    assert not bad, f"parity failures (tol {tol}): {bad}"
+    return errs
+
+
+@pytest.mark.parametrize("name,w,random_ln", EDGE_CASES, ids=[c[0] for c in EDGE_CASES])
+def test_layer_parity_edge_cases(name, w, random_ln):
+    log(f"case {name}: {w}")
+    inp = I.make_inputs(w, random_ln=random_ln)
+    ref = oracle_run(w, inp)
+    st = run_gpu(w, inp)
+    compare(w, inp, ref, st)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    """No atomics on the path: a second run reproduces the first bit for bit."""
+    w = W("det", 2, 200, 256, 2, 128, 512, 80, seed=30)
+    inp = I.make_inputs(w, random_ln=True)
+    st = run_gpu(w, inp)
+    first = [st.y.clone(), st.dx.clone()] + [t.clone() for t in st.grads[0].values()]
+    st.step()
+    torch.cuda.synchronize()
+    second = [st.y, st.dx] + list(st.grads[0].values())
+    for a, b in zip(first, second):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))

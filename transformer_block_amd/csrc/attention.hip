@@ -1,0 +1,545 @@
+// Sliding-window causal flash attention for gfx950: forward, and backward with
+// the probabilities recomputed from the saved log-sum-exp.
+//
+// What is computed (MegaScale reading notes, section 1.1, eq (5)-(6), and
+// section 1.3): for each (batch, head) and query i, the keys j with
+// 0 <= i - j < window, logits q_i . k_j / sqrt(d), a softmax over them and the
+// weighted sum of v_j.  The s x s probability matrix never reaches HBM: the
+// forward streams key tiles with an online softmax and stores only the
+// per-query log-sum-exp; the backward recomputes P from it (selective
+// recompute of the core attention, same notes section 1.3; Megatron tuning
+// post, recompute section).  Key tiles that lie wholly outside every query's
+// window are never visited, so the work is O(s * w), not O(s^2).
+//
+// Matrix-core mapping.  Every contraction is a v_mfma_f32_32x32x16_bf16.  The
+// forward computes S^T = K Q^T so that each lane owns one query column: the
+// row max and row sum of the online softmax are lane-local plus one exchange
+// with the lane 32 apart, and O^T = V^T P^T reuses the S^T accumulator
+// registers directly as the B operand (the key order inside a 16-key step is
+// permuted identically on both operands, which leaves the sum unchanged).
+// V^T is written transposed into LDS once per tile.  The backward splits into
+// a key-parallel kernel for dK, dV (S = Q K^T, lane = key) and a
+// query-parallel kernel for dQ (S^T, lane = query), so no atomics are needed
+// and results are deterministic.
+#include <math.h>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace ptb {
+namespace {
+
+constexpr int BQ = 128;   // queries per workgroup (forward, dQ): 4 waves x 32
+constexpr int BKV = 64;   // keys per LDS tile (forward, dQ)
+constexpr int BKB = 128;  // keys per workgroup (dK/dV): 4 waves x 32
+constexpr int BQB = 64;   // queries per LDS tile (dK/dV)
+
+// Rows of D bf16 in LDS, addressed in 16-byte chunks, XOR-swizzled.
+template <int D>
+__device__ __forceinline__ int rowswz(int r) {
+  if constexpr (D == 128) return swz256(r);
+  else return swz128(r);
+}
+template <int D>
+__device__ __forceinline__ u16* row_chunk(u16* base, int r, int c) {
+  return base + r * D + ((c ^ rowswz<D>(r)) << 3);
+}
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const u16* base, int r, int c) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(base + r * D + ((c ^ rowswz<D>(r)) << 3)));
+}
+
+// Transposed tiles: D rows of 64 bf16, addressed in 8-byte slots of 4.
+__device__ __forceinline__ uint2 tslot(const u16* base, int r, int slot) {
+  return *reinterpret_cast<const uint2*>(base + r * 64 + ((slot ^ swz8b(r)) << 2));
+}
+// A operand "X^T[d][k]" for k = 4g..4g+3 and 8+4g..8+4g+3 inside a 16-step
+// starting at tile column k0.
+__device__ __forceinline__ bf16x8 tfrag(const u16* base, int r, int k0, int g) {
+  const uint2 lo = tslot(base, r, (k0 >> 2) + g);
+  const uint2 hi = tslot(base, r, (k0 >> 2) + 2 + g);
+  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f32x16& a, int base) {
+  return as_bf16x8(make_uint4(pack2bf(a[base + 0], a[base + 1]), pack2bf(a[base + 2], a[base + 3]),
+                              pack2bf(a[base + 4], a[base + 5]), pack2bf(a[base + 6], a[base + 7])));
+}
+
+// A 64 x D tile of a row-major matrix (row stride ld) held in registers:
+// thread t owns rows 4*kg .. 4*kg+3 and the 8 columns of chunk dc.
+template <int D>
+struct Tile64 {
+  static constexpr int DC = D / 8;          // chunks per row
+  static constexpr int ACTIVE = 16 * DC;    // threads holding data
+  uint4 v[4];
+
+  __device__ __forceinline__ void load(const u16* g, int ld, int row0, int nrows, int tid) {
+    const int dc = tid % DC, kg = tid / DC;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int r = row0 + kg * 4 + kk;
+      v[kk] = make_uint4(0u, 0u, 0u, 0u);
+      if (tid < ACTIVE && r < nrows)
+        v[kk] = *reinterpret_cast<const uint4*>(g + r * ld + dc * 8);
+    }
+  }
+  __device__ __forceinline__ void store_rows(u16* lds, int tid) const {
+    if (tid >= ACTIVE) return;
+    const int dc = tid % DC, kg = tid / DC;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) *reinterpret_cast<uint4*>(row_chunk<D>(lds, kg * 4 + kk, dc)) = v[kk];
+  }
+  // Writes the transpose: LDS row d (= column of the tile) holds 64 values.
+  __device__ __forceinline__ void store_transposed(u16* lds, int tid) const {
+    if (tid >= ACTIVE) return;
+    const int dc = tid % DC, kg = tid / DC;
+    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&v[0]);
+    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&v[1]);
+    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&v[2]);
+    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&v[3]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int d = dc * 8 + j;
+      const int wi = j >> 1;
+      uint32_t a0, a1;
+      if (j & 1) {
+        a0 = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
+        a1 = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
+      } else {
+        a0 = (w0[wi] & 0xffffu) | (w1[wi] << 16);
+        a1 = (w2[wi] & 0xffffu) | (w3[wi] << 16);
+      }
+      *reinterpret_cast<uint2*>(lds + d * 64 + ((kg ^ swz8b(d)) << 2)) = make_uint2(a0, a1);
+    }
+  }
+};
+
+// ------------------------------------------------------------------ forward
+template <int D>
+__global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ qkv,
+                                                       u16* __restrict__ cout,
+                                                       float* __restrict__ lse, int s, int n,
+                                                       int window, int nqt) {
+  constexpr int NKS = D / 16, ND = D / 32;
+  __shared__ __attribute__((aligned(16))) u16 k_lds[BKV * D];
+  __shared__ __attribute__((aligned(16))) u16 vt_lds[D * BKV];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int qt = nqt - 1 - static_cast<int>(blockIdx.x);  // longest rows first
+  const int hd = blockIdx.y, bi = blockIdx.z;
+  const int hl = n * D, ld = 3 * hl;
+  const u16* Qg = qkv + static_cast<size_t>(bi) * s * ld + hd * D;
+  const u16* Kg = Qg + hl;
+  const u16* Vg = Qg + 2 * hl;
+  const int q0 = qt * BQ, qw0 = q0 + wave * 32, qi = qw0 + l32;
+
+  bf16x8 qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    uint4 t = make_uint4(0u, 0u, 0u, 0u);
+    if (qi < s) t = *reinterpret_cast<const uint4*>(Qg + qi * ld + ks * 16 + g * 8);
+    qf[ks] = as_bf16x8(t);
+  }
+
+  const float sc = kLog2e / sqrtf(static_cast<float>(D));
+  float m = -INFINITY, l = 0.0f;
+  f32x16 o[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.0f;
+
+  const int kv_begin = max(0, q0 - window + 1) & ~(BKV - 1);
+  const int kv_end = min(s, q0 + BQ);
+  Tile64<D> kt, vt;
+  for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKV) {
+    kt.load(Kg, ld, kt0, s, tid);
+    vt.load(Vg, ld, kt0, s, tid);
+    __syncthreads();
+    kt.store_rows(k_lds, tid);
+    vt.store_transposed(vt_lds, tid);
+    __syncthreads();
+
+    const bool any = qw0 < s && qw0 + 31 >= kt0 && qw0 - (kt0 + BKV - 1) < window;
+    if (!any) continue;
+    const bool full = kt0 + BKV - 1 <= qw0 && qw0 + 31 - kt0 < window && kt0 + BKV <= s;
+
+    f32x16 st[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st[kb][e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        st[kb] = mfma32x32x16(row_frag<D>(k_lds, kb * 32 + l32, ks * 2 + g), qf[ks], st[kb]);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float x = st[kb][e] * sc;
+        if (!full) {
+          const int key = kt0 + kb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
+          const int diff = qi - key;
+          if (diff < 0 || diff >= window || key >= s) x = -INFINITY;
+        }
+        st[kb][e] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx);
+    const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
+    const float alpha = exp2f(m - msafe);
+    float rs = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = exp2f(st[kb][e] - msafe);
+        st[kb][e] = p;
+        rs += p;
+      }
+    l = l * alpha + rs;
+    m = mnew;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        const bf16x8 pb = pack8(st[kb], e2 * 8);
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+          o[db] = mfma32x32x16(tfrag(vt_lds, db * 32 + l32, kb * 32 + e2 * 16, g), pb, o[db]);
+      }
+  }
+
+  const float lt = l + __shfl_xor(l, 32);
+  if (qi < s) {
+    const float inv = 1.0f / lt;
+    u16* cg = cout + (static_cast<size_t>(bi) * s + qi) * hl + hd * D;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = db * 32 + jj * 8 + g * 4;
+        *reinterpret_cast<uint2*>(cg + d0) =
+            make_uint2(pack2bf(o[db][jj * 4 + 0] * inv, o[db][jj * 4 + 1] * inv),
+                       pack2bf(o[db][jj * 4 + 2] * inv, o[db][jj * 4 + 3] * inv));
+      }
+    if (g == 0) lse[(static_cast<size_t>(bi) * n + hd) * s + qi] = m + log2f(lt);
+  }
+}
+
+// ------------------------------------------------- delta = rowsum(dO * O)
+template <int D>
+__global__ __launch_bounds__(256) void attn_delta_kernel(const u16* __restrict__ dc,
+                                                         const u16* __restrict__ c,
+                                                         float* __restrict__ delta, int T,
+                                                         int s, int n) {
+  constexpr int LPI = D / 8;  // lanes per (token, head)
+  const int item = (blockIdx.x * 256 + threadIdx.x) / LPI;
+  const int sub = threadIdx.x % LPI;
+  const int hl = n * D;
+  float acc = 0.0f;
+  const bool ok = item < T * n;
+  const int t = ok ? item / n : 0, hd = ok ? item % n : 0;
+  if (ok) {
+    const uint4 a = *reinterpret_cast<const uint4*>(dc + t * hl + hd * D + sub * 8);
+    const uint4 b = *reinterpret_cast<const uint4*>(c + t * hl + hd * D + sub * 8);
+    const uint32_t* wa = reinterpret_cast<const uint32_t*>(&a);
+    const uint32_t* wb = reinterpret_cast<const uint32_t*>(&b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc += lo_bf(wa[i]) * lo_bf(wb[i]) + hi_bf(wa[i]) * hi_bf(wb[i]);
+  }
+#pragma unroll
+  for (int o = LPI / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (ok && sub == 0) {
+    const int bi = t / s, i = t % s;
+    delta[(static_cast<size_t>(bi) * n + hd) * s + i] = acc;
+  }
+}
+
+// ------------------------------------------------------------ dK and dV
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+    const u16* __restrict__ qkv, const u16* __restrict__ dcg, const float* __restrict__ lse,
+    const float* __restrict__ delta, u16* __restrict__ dz, int ld_dz, int s, int n,
+    int window) {
+  constexpr int NKS = D / 16, ND = D / 32;
+  __shared__ __attribute__((aligned(16))) u16 q_lds[BQB * D];
+  __shared__ __attribute__((aligned(16))) u16 qt_lds[D * BQB];
+  __shared__ __attribute__((aligned(16))) u16 do_lds[BQB * D];
+  __shared__ __attribute__((aligned(16))) u16 dot_lds[D * BQB];
+  __shared__ float lse_lds[BQB];
+  __shared__ float dl_lds[BQB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int hd = blockIdx.y, bi = blockIdx.z;
+  const int hl = n * D, ld = 3 * hl;
+  const u16* Qg = qkv + static_cast<size_t>(bi) * s * ld + hd * D;
+  const u16* Kg = Qg + hl;
+  const u16* Vg = Qg + 2 * hl;
+  const u16* dOg = dcg + static_cast<size_t>(bi) * s * hl + hd * D;
+  const float* lse_h = lse + (static_cast<size_t>(bi) * n + hd) * s;
+  const float* dl_h = delta + (static_cast<size_t>(bi) * n + hd) * s;
+  const int kb0 = blockIdx.x * BKB, kw0 = kb0 + wave * 32, kj = kw0 + l32;
+
+  bf16x8 kf[NKS], vf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
+    if (kj < s) {
+      a = *reinterpret_cast<const uint4*>(Kg + kj * ld + ks * 16 + g * 8);
+      b = *reinterpret_cast<const uint4*>(Vg + kj * ld + ks * 16 + g * 8);
+    }
+    kf[ks] = as_bf16x8(a);
+    vf[ks] = as_bf16x8(b);
+  }
+  const float sc = kLog2e / sqrtf(static_cast<float>(D));
+  f32x16 dv[ND], dk[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { dv[db][e] = 0.0f; dk[db][e] = 0.0f; }
+
+  const int q_begin = kb0 & ~(BQB - 1);
+  const int q_end = min(s, kb0 + BKB - 1 + window);
+  Tile64<D> qtile, otile;
+  for (int qt0 = q_begin; qt0 < q_end; qt0 += BQB) {
+    qtile.load(Qg, ld, qt0, s, tid);
+    otile.load(dOg, hl, qt0, s, tid);
+    __syncthreads();
+    qtile.store_rows(q_lds, tid);
+    qtile.store_transposed(qt_lds, tid);
+    otile.store_rows(do_lds, tid);
+    otile.store_transposed(dot_lds, tid);
+    if (tid < BQB) {
+      const int q = qt0 + tid;
+      lse_lds[tid] = q < s ? lse_h[q] : 0.0f;
+      dl_lds[tid] = q < s ? dl_h[q] : 0.0f;
+    }
+    __syncthreads();
+
+    const bool any = kw0 < s && qt0 + BQB - 1 >= kw0 && qt0 - (kw0 + 31) < window;
+    if (!any) continue;
+    const bool full = qt0 >= kw0 + 31 && qt0 + BQB - 1 - kw0 < window && qt0 + BQB <= s;
+
+    f32x16 sp[2], dp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { sp[qb][e] = 0.0f; dp[qb][e] = 0.0f; }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        sp[qb] = mfma32x32x16(row_frag<D>(q_lds, qb * 32 + l32, ks * 2 + g), kf[ks], sp[qb]);
+        dp[qb] = mfma32x32x16(row_frag<D>(do_lds, qb * 32 + l32, ks * 2 + g), vf[ks], dp[qb]);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int lq = qb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
+        float p = exp2f(sp[qb][e] * sc - lse_lds[lq]);
+        if (!full) {
+          const int diff = qt0 + lq - kj;
+          if (diff < 0 || diff >= window || qt0 + lq >= s) p = 0.0f;
+        }
+        sp[qb][e] = p;
+        dp[qb][e] = p * (dp[qb][e] - dl_lds[lq]);
+      }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        const bf16x8 pb = pack8(sp[qb], e2 * 8);
+        const bf16x8 dsb = pack8(dp[qb], e2 * 8);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          dv[db] = mfma32x32x16(tfrag(dot_lds, db * 32 + l32, qb * 32 + e2 * 16, g), pb, dv[db]);
+          dk[db] = mfma32x32x16(tfrag(qt_lds, db * 32 + l32, qb * 32 + e2 * 16, g), dsb, dk[db]);
+        }
+      }
+  }
+
+  if (kj < s) {
+    const float rs = 1.0f / sqrtf(static_cast<float>(D));
+    u16* row = dz + (static_cast<size_t>(bi) * s + kj) * ld_dz + hd * D;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = db * 32 + jj * 8 + g * 4;
+        *reinterpret_cast<uint2*>(row + hl + d0) =
+            make_uint2(pack2bf(dk[db][jj * 4 + 0] * rs, dk[db][jj * 4 + 1] * rs),
+                       pack2bf(dk[db][jj * 4 + 2] * rs, dk[db][jj * 4 + 3] * rs));
+        *reinterpret_cast<uint2*>(row + 2 * hl + d0) =
+            make_uint2(pack2bf(dv[db][jj * 4 + 0], dv[db][jj * 4 + 1]),
+                       pack2bf(dv[db][jj * 4 + 2], dv[db][jj * 4 + 3]));
+      }
+  }
+}
+
+// ------------------------------------------------------------------- dQ
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
+    const u16* __restrict__ qkv, const u16* __restrict__ dcg, const float* __restrict__ lse,
+    const float* __restrict__ delta, u16* __restrict__ dz, int ld_dz, int s, int n,
+    int window, int nqt) {
+  constexpr int NKS = D / 16, ND = D / 32;
+  __shared__ __attribute__((aligned(16))) u16 k_lds[BKV * D];
+  __shared__ __attribute__((aligned(16))) u16 kt_lds[D * BKV];
+  __shared__ __attribute__((aligned(16))) u16 v_lds[BKV * D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int qt = nqt - 1 - static_cast<int>(blockIdx.x);
+  const int hd = blockIdx.y, bi = blockIdx.z;
+  const int hl = n * D, ld = 3 * hl;
+  const u16* Qg = qkv + static_cast<size_t>(bi) * s * ld + hd * D;
+  const u16* Kg = Qg + hl;
+  const u16* Vg = Qg + 2 * hl;
+  const u16* dOg = dcg + static_cast<size_t>(bi) * s * hl + hd * D;
+  const int q0 = qt * BQ, qw0 = q0 + wave * 32, qi = qw0 + l32;
+
+  bf16x8 qf[NKS], of[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
+    if (qi < s) {
+      a = *reinterpret_cast<const uint4*>(Qg + qi * ld + ks * 16 + g * 8);
+      b = *reinterpret_cast<const uint4*>(dOg + qi * hl + ks * 16 + g * 8);
+    }
+    qf[ks] = as_bf16x8(a);
+    of[ks] = as_bf16x8(b);
+  }
+  const size_t hrow = (static_cast<size_t>(bi) * n + hd) * s;
+  const float lq = qi < s ? lse[hrow + qi] : 0.0f;
+  const float dq_delta = qi < s ? delta[hrow + qi] : 0.0f;
+  const float sc = kLog2e / sqrtf(static_cast<float>(D));
+
+  f32x16 dq[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq[db][e] = 0.0f;
+
+  const int kv_begin = max(0, q0 - window + 1) & ~(BKV - 1);
+  const int kv_end = min(s, q0 + BQ);
+  Tile64<D> ktile, vtile;
+  for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKV) {
+    ktile.load(Kg, ld, kt0, s, tid);
+    vtile.load(Vg, ld, kt0, s, tid);
+    __syncthreads();
+    ktile.store_rows(k_lds, tid);
+    ktile.store_transposed(kt_lds, tid);
+    vtile.store_rows(v_lds, tid);
+    __syncthreads();
+
+    const bool any = qw0 < s && qw0 + 31 >= kt0 && qw0 - (kt0 + BKV - 1) < window;
+    if (!any) continue;
+    const bool full = kt0 + BKV - 1 <= qw0 && qw0 + 31 - kt0 < window && kt0 + BKV <= s;
+
+    f32x16 st[2], dpt[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { st[kb][e] = 0.0f; dpt[kb][e] = 0.0f; }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        st[kb] = mfma32x32x16(row_frag<D>(k_lds, kb * 32 + l32, ks * 2 + g), qf[ks], st[kb]);
+        dpt[kb] = mfma32x32x16(row_frag<D>(v_lds, kb * 32 + l32, ks * 2 + g), of[ks], dpt[kb]);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float p = exp2f(st[kb][e] * sc - lq);
+        if (!full) {
+          const int key = kt0 + kb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
+          const int diff = qi - key;
+          if (diff < 0 || diff >= window || key >= s) p = 0.0f;
+        }
+        st[kb][e] = p * (dpt[kb][e] - dq_delta);
+      }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        const bf16x8 dsb = pack8(st[kb], e2 * 8);
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+          dq[db] = mfma32x32x16(tfrag(kt_lds, db * 32 + l32, kb * 32 + e2 * 16, g), dsb, dq[db]);
+      }
+  }
+
+  if (qi < s) {
+    const float rs = 1.0f / sqrtf(static_cast<float>(D));
+    u16* row = dz + (static_cast<size_t>(bi) * s + qi) * ld_dz + hd * D;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = db * 32 + jj * 8 + g * 4;
+        *reinterpret_cast<uint2*>(row + d0) =
+            make_uint2(pack2bf(dq[db][jj * 4 + 0] * rs, dq[db][jj * 4 + 1] * rs),
+                       pack2bf(dq[db][jj * 4 + 2] * rs, dq[db][jj * 4 + 3] * rs));
+      }
+  }
+}
+
+template <int D>
+hipError_t fwd_d(const u16* qkv, u16* c, float* lse, int b, int s, int n, int window,
+                 hipStream_t st) {
+  const int nqt = (s + BQ - 1) / BQ;
+  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(nqt, n, b), dim3(256), 0, st, qkv, c, lse, s, n,
+                     window, nqt);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t bwd_d(const u16* qkv, const u16* c, const float* lse, const u16* dc, float* delta,
+                 u16* dz, int ld_dz, int b, int s, int n, int window, hipStream_t st) {
+  const int T = b * s;
+  const long items = static_cast<long>(T) * n;
+  const int per_block = 256 / (D / 8);
+  hipLaunchKernelGGL(attn_delta_kernel<D>, dim3((items + per_block - 1) / per_block), dim3(256),
+                     0, st, dc, c, delta, T, s, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((s + BKB - 1) / BKB, n, b), dim3(256), 0, st,
+                     qkv, dc, lse, delta, dz, ld_dz, s, n, window);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nqt = (s + BQ - 1) / BQ;
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(nqt, n, b), dim3(256), 0, st, qkv, dc, lse,
+                     delta, dz, ld_dz, s, n, window, nqt);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention_fwd(const u16* qkv, u16* c, float* lse, int b, int s, int n, int d,
+                                int window, hipStream_t st) {
+  if (d == 128) return fwd_d<128>(qkv, c, lse, b, s, n, window, st);
+  if (d == 64) return fwd_d<64>(qkv, c, lse, b, s, n, window, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attention_bwd(const u16* qkv, const u16* c, const float* lse, const u16* dc,
+                                float* delta, u16* dz, int ld_dz, int b, int s, int n, int d,
+                                int window, hipStream_t st) {
+  if (d == 128) return bwd_d<128>(qkv, c, lse, dc, delta, dz, ld_dz, b, s, n, window, st);
+  if (d == 64) return bwd_d<64>(qkv, c, lse, dc, delta, dz, ld_dz, b, s, n, window, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ptb

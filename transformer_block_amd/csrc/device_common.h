@@ -1,0 +1,74 @@
+// Device-side helpers shared by the gfx950 kernels of libptb.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ptb {
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf2f(u16 b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ u16 f2bf(float f) {
+  return __builtin_bit_cast(u16, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
+  return static_cast<uint32_t>(f2bf(lo)) | (static_cast<uint32_t>(f2bf(hi)) << 16);
+}
+
+__device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// D = A(32x16) * B(16x32) + C, bf16 in, fp32 accumulate.
+// Lane l supplies A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32];
+// it holds D[8*j + 4*(l/32) + i][l%32] in element 4*j + i.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Exact GeLU u * Phi(u) and its derivative Phi(u) + u * phi(u).
+__device__ __forceinline__ float gelu_f(float u) {
+  return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f));
+}
+__device__ __forceinline__ float gelu_grad_f(float u) {
+  const float cdf = 0.5f * (1.0f + erff(u * 0.70710678118654752f));
+  const float pdf = 0.39894228040143268f * __expf(-0.5f * u * u);
+  return cdf + u * pdf;
+}
+
+// LDS swizzle for tiles stored as rows of 64 bf16 (128 bytes = 8 chunks of
+// 16 bytes): chunk c of row r lives at chunk slot c ^ swz128(r).  Rows r..r+7
+// (and r..r+15 counting the row parity) read at one logical chunk land in
+// distinct banks, and so do rows r, r+8, r+16, ... written at one chunk.
+__device__ __forceinline__ int swz128(int r) { return (r ^ (r >> 3)) & 7; }
+
+// Swizzle for rows of 64 bf16 addressed in 8-byte slots (16 slots per row).
+__device__ __forceinline__ int swz8b(int r) { return (r ^ (r >> 4)) & 15; }
+
+// Swizzle for rows of 128 bf16 (256 bytes = 16 chunks of 16 bytes).
+__device__ __forceinline__ int swz256(int r) { return r & 15; }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+}  // namespace ptb

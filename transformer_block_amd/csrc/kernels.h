@@ -1,0 +1,84 @@
+// Host-side launchers of the gfx950 kernels (internal to libptb).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ptb {
+
+typedef uint16_t u16;
+
+// A GEMM operand made of up to two row-major bf16 segments that together form
+// one logical matrix.  `split` is where segment 1 starts along the split
+// dimension: the contraction index k (split_on_k = 1) or the outer index (the
+// output row for A, the output column for B; split_on_k = 0).  Indices inside
+// segment 1 are taken relative to `split`.  This addresses the concatenated
+// weights [W_qkv | W_fc1] and [W_o ; W_fc2] and the concatenated activations
+// [c | g] in place, without copying them.
+struct Operand {
+  const u16* p0;
+  const u16* p1;
+  int ld0;
+  int ld1;
+  int split;
+  int split_on_k;
+};
+
+// Storage order of an operand: KMAJOR means element (outer r, k) sits at
+// r*ld + k (k contiguous); OUTER_MAJOR means it sits at k*ld + r.
+enum Major { KMAJOR = 0, OUTER_MAJOR = 1 };
+
+// What the GEMM does with each fp32 result v at (row r, column c).
+enum EpiMode {
+  EPI_QKV_GELU = 0,  // c < split: o0[r*ld0+c] = v; else o1 = v (u), o2 = GeLU(v) (g)
+  EPI_RESIDUAL = 1,  // o0[r*ld0+c] = v + i0[r*ld0+c]
+  EPI_DGELU = 2,     // c < split: o0[r*ld0+c] = v; else o1[r*ld1+col_off1+c-split] =
+                     //   v * GeLU'(i0[r*ld2 + c-split])
+  EPI_STORE2_COLS = 3,  // c < split: o0[r*ld0+c]; else o1[r*ld1 + c-split]
+  EPI_STORE2_ROWS = 4,  // r < split: o0[r*ld0+c]; else o1[(r-split)*ld1 + c]
+  EPI_F32 = 5           // of[r*ld0+c] = v (fp32)
+};
+
+struct Epilogue {
+  u16* o0;
+  u16* o1;
+  u16* o2;
+  float* of;
+  const u16* i0;
+  int ld0, ld1, ld2;
+  int col_off1;
+  int split;
+};
+
+// C[M,N] = A[M,K] * B[K,N] with the epilogue applied to C.
+hipError_t launch_gemm(int M, int N, int K, const Operand& A, Major a_major,
+                       const Operand& B, Major b_major, EpiMode mode,
+                       const Epilogue& epi, hipStream_t stream);
+
+// LayerNorm forward over rows of x [T, h]: a (bf16), mu, rstd (fp32).
+hipError_t launch_layernorm_fwd(const u16* x, const u16* gamma, const u16* beta,
+                                u16* a, float* mu, float* rstd, int T, int h,
+                                float eps, hipStream_t stream);
+
+// LayerNorm backward plus residual: dx = dy + LN'(da); per-block partial sums
+// of dgamma, dbeta into `partials` [nblk, 2, h], then reduced into bf16.
+int layernorm_bwd_blocks(int T);
+hipError_t launch_layernorm_bwd(const float* da, const u16* x, const u16* gamma,
+                                const float* mu, const float* rstd, const u16* dy,
+                                u16* dx, float* partials, u16* dgamma, u16* dbeta,
+                                int T, int h, hipStream_t stream);
+
+// Sliding-window causal flash attention, forward: reads q, k, v column blocks
+// of qkv [b*s, 3*n*d]; writes c [b*s, n*d] and the base-2 log-sum-exp
+// lse [b, n, s].
+hipError_t launch_attention_fwd(const u16* qkv, u16* c, float* lse, int b, int s,
+                                int n, int d, int window, hipStream_t stream);
+
+// Attention backward.  delta[b,n,s] = rowsum(dc * c) per head first, then
+// dk, dv and dq written into the first 3*n*d columns of dz [b*s, ld_dz].
+hipError_t launch_attention_bwd(const u16* qkv, const u16* c, const float* lse,
+                                const u16* dc, float* delta, u16* dz, int ld_dz,
+                                int b, int s, int n, int d, int window,
+                                hipStream_t stream);
+
+}  // namespace ptb

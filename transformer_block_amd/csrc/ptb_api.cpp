@@ -1,0 +1,338 @@
+// C ABI of libptb (declared in include/ptb.h): argument checks, the layout of
+// the forward->backward stash and of the backward scratch, and the launch
+// sequence of one Parallel Transformer Block layer
+//   y = x + Attn(LN(x)) + MLP(LN(x))
+// (MegaScale reading notes, section 1.1, eq (4)).
+//
+// Forward, four launches on the caller's stream:
+//   LN(x) -> a;  a x [W_qkv | W_fc1] -> qkv, u, g = GeLU(u);
+//   sliding-window flash attention -> c, lse;  [c | g] x [W_o ; W_fc2] + x -> y.
+// Backward:
+//   dy x [W_o ; W_fc2]^T -> dc, du = dg * GeLU'(u);  attention backward
+//   (probabilities recomputed from lse) -> dq, dk, dv;  [c | g]^T dy -> dW_o, dW_fc2;
+//   dZ x [W_qkv | W_fc1]^T -> da;  a^T dZ -> dW_qkv, dW_fc1;
+//   LayerNorm backward + dy -> dx, dgamma, dbeta.
+// dZ = [dq | dk | dv | du] is one [T, 3*h_l + f] buffer, so the two products
+// with [W_qkv | W_fc1] each run as a single GEMM.
+#include <math.h>
+#include <stdint.h>
+
+#include <climits>
+#include <initializer_list>
+
+#include "../../include/ptb.h"
+#include "kernels.h"
+
+namespace {
+
+using ptb::u16;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+struct Shape {
+  long b, s, h, n, d, f, w, T, hl, N1, K2;
+};
+
+int32_t check_dims(const ptb_dims* dims, Shape* out) {
+  if (dims == nullptr) return PTB_ERR_NULL;
+  const ptb_dims& p = *dims;
+  if (p.batch < 1 || p.seq < 1 || p.heads < 1) return PTB_ERR_DIMS;
+  if (p.head_dim != 64 && p.head_dim != 128) return PTB_ERR_HEAD_DIM;
+  if (p.hidden < 64 || p.hidden % 64 != 0 || p.hidden > 16384) return PTB_ERR_DIMS;
+  if (p.ffn < 64 || p.ffn % 64 != 0) return PTB_ERR_DIMS;
+  if (p.window < 1) return PTB_ERR_WINDOW;
+  if (!(p.ln_eps > 0.0f) || !isfinite(p.ln_eps)) return PTB_ERR_EPS;
+  Shape s;
+  s.b = p.batch; s.s = p.seq; s.h = p.hidden; s.n = p.heads; s.d = p.head_dim; s.f = p.ffn;
+  s.w = p.window < p.seq ? p.window : p.seq;  // a window >= seq is full causal attention
+  s.T = s.b * s.s;
+  s.hl = s.n * s.d;
+  s.N1 = 3 * s.hl + s.f;
+  s.K2 = s.hl + s.f;
+  const long lim = INT_MAX;
+  // every tensor must be indexable with 32-bit element offsets
+  if (s.T > lim / s.N1 || s.h > lim / s.N1 || s.T > lim / s.h || s.K2 > lim / s.h ||
+      s.b * s.n > lim / s.s)
+    return PTB_ERR_DIMS;
+  if (out) *out = s;
+  return PTB_OK;
+}
+
+struct SavedLayout {
+  size_t off[PTB_SAVED_COUNT];
+  size_t total;
+};
+
+SavedLayout saved_layout(const Shape& s) {
+  SavedLayout L;
+  size_t o = 0;
+  auto put = [&](int slot, size_t bytes) { L.off[slot] = o; o = align_up(o + bytes); };
+  put(PTB_SAVED_A, s.T * s.h * 2);
+  put(PTB_SAVED_MU, s.T * 4);
+  put(PTB_SAVED_RSTD, s.T * 4);
+  put(PTB_SAVED_QKV, s.T * 3 * s.hl * 2);
+  put(PTB_SAVED_U, s.T * s.f * 2);
+  put(PTB_SAVED_G, s.T * s.f * 2);
+  put(PTB_SAVED_C, s.T * s.hl * 2);
+  put(PTB_SAVED_LSE, s.b * s.n * s.s * 4);
+  L.total = o;
+  return L;
+}
+
+struct WorkLayout {
+  size_t dc, dz, da, delta, partials, total;
+};
+
+WorkLayout work_layout(const Shape& s) {
+  WorkLayout W;
+  size_t o = 0;
+  W.dc = o; o = align_up(o + s.T * s.hl * 2);
+  W.dz = o; o = align_up(o + s.T * s.N1 * 2);
+  W.da = o; o = align_up(o + s.T * s.h * 4);
+  W.delta = o; o = align_up(o + s.b * s.n * s.s * 4);
+  W.partials = o; o = align_up(o + static_cast<size_t>(ptb::layernorm_bwd_blocks(s.T)) * 2 * s.h * 4);
+  W.total = o;
+  return W;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p == nullptr) return PTB_ERR_NULL;
+  for (const void* p : ps)
+    if (!aligned16(p)) return PTB_ERR_ALIGN;
+  return PTB_OK;
+}
+
+template <typename T>
+T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
+template <typename T>
+const T* at(const void* base, size_t off) {
+  return reinterpret_cast<const T*>(static_cast<const char*>(base) + off);
+}
+
+ptb::Operand one(const u16* p, long ld) {
+  return ptb::Operand{p, p, static_cast<int>(ld), static_cast<int>(ld), INT_MAX, 0};
+}
+ptb::Operand two(const u16* p0, long ld0, const u16* p1, long ld1, long split, int on_k) {
+  return ptb::Operand{p0, p1, static_cast<int>(ld0), static_cast<int>(ld1),
+                      static_cast<int>(split), on_k};
+}
+
+#define PTB_HIP(expr)                              \
+  do {                                             \
+    if ((expr) != hipSuccess) return PTB_ERR_HIP;  \
+  } while (0)
+
+// Enqueue one stage, bracketed by the caller's timing events when given.
+#define PTB_STAGE(i, expr)                                                          \
+  do {                                                                              \
+    if (ev != nullptr && ev[2 * (i)] != nullptr)                                    \
+      PTB_HIP(hipEventRecord(static_cast<hipEvent_t>(ev[2 * (i)]), strm));           \
+    PTB_HIP(expr);                                                                  \
+    if (ev != nullptr && ev[2 * (i) + 1] != nullptr)                                \
+      PTB_HIP(hipEventRecord(static_cast<hipEvent_t>(ev[2 * (i) + 1]), strm));       \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int32_t ptb_abi_version(void) { return PTB_ABI_VERSION; }
+
+const char* ptb_status_string(int32_t status) {
+  switch (status) {
+    case PTB_OK: return "ok";
+    case PTB_ERR_NULL: return "a required pointer is NULL";
+    case PTB_ERR_DIMS: return "invalid or too large dimensions";
+    case PTB_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
+    case PTB_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case PTB_ERR_WINDOW: return "window must be >= 1";
+    case PTB_ERR_EPS: return "ln_eps must be a finite positive number";
+    case PTB_ERR_HIP: return "a HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t ptb_validate_dims(const ptb_dims* dims) { return check_dims(dims, nullptr); }
+
+int32_t ptb_saved_bytes(const ptb_dims* dims, size_t* bytes) {
+  Shape s;
+  const int32_t st = check_dims(dims, &s);
+  if (st != PTB_OK) return st;
+  if (bytes == nullptr) return PTB_ERR_NULL;
+  *bytes = saved_layout(s).total;
+  return PTB_OK;
+}
+
+int32_t ptb_workspace_bytes(const ptb_dims* dims, size_t* bytes) {
+  Shape s;
+  const int32_t st = check_dims(dims, &s);
+  if (st != PTB_OK) return st;
+  if (bytes == nullptr) return PTB_ERR_NULL;
+  *bytes = work_layout(s).total;
+  return PTB_OK;
+}
+
+int32_t ptb_saved_layout(const ptb_dims* dims, size_t* offsets) {
+  Shape s;
+  const int32_t st = check_dims(dims, &s);
+  if (st != PTB_OK) return st;
+  if (offsets == nullptr) return PTB_ERR_NULL;
+  const SavedLayout L = saved_layout(s);
+  for (int i = 0; i < PTB_SAVED_COUNT; ++i) offsets[i] = L.off[i];
+  return PTB_OK;
+}
+
+int32_t ptb_forward_timed(const ptb_dims* dims, const void* x, const void* ln_gamma,
+                          const void* ln_beta, const void* w_qkv, const void* w_o,
+                          const void* w_fc1, const void* w_fc2, void* y, void* saved,
+                          void* stream, void* const* ev) {
+  Shape s;
+  int32_t st = check_dims(dims, &s);
+  if (st != PTB_OK) return st;
+  st = check_ptrs({x, ln_gamma, ln_beta, w_qkv, w_o, w_fc1, w_fc2, y, saved});
+  if (st != PTB_OK) return st;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  const SavedLayout L = saved_layout(s);
+  u16* a = at<u16>(saved, L.off[PTB_SAVED_A]);
+  float* mu = at<float>(saved, L.off[PTB_SAVED_MU]);
+  float* rstd = at<float>(saved, L.off[PTB_SAVED_RSTD]);
+  u16* qkv = at<u16>(saved, L.off[PTB_SAVED_QKV]);
+  u16* u = at<u16>(saved, L.off[PTB_SAVED_U]);
+  u16* g = at<u16>(saved, L.off[PTB_SAVED_G]);
+  u16* c = at<u16>(saved, L.off[PTB_SAVED_C]);
+  float* lse = at<float>(saved, L.off[PTB_SAVED_LSE]);
+  const u16* X = static_cast<const u16*>(x);
+
+  PTB_STAGE(0, ptb::launch_layernorm_fwd(X, static_cast<const u16*>(ln_gamma),
+                                    static_cast<const u16*>(ln_beta), a, mu, rstd,
+                                    static_cast<int>(s.T), static_cast<int>(s.h), dims->ln_eps,
+                                    strm));
+  {  // [QKV | FC1] projection with GeLU on the FC1 columns
+    ptb::Epilogue e{};
+    e.o0 = qkv; e.ld0 = static_cast<int>(3 * s.hl);
+    e.o1 = u; e.o2 = g; e.ld1 = static_cast<int>(s.f);
+    e.split = static_cast<int>(3 * s.hl);
+    PTB_STAGE(1, ptb::launch_gemm(
+        static_cast<int>(s.T), static_cast<int>(s.N1), static_cast<int>(s.h), one(a, s.h),
+        ptb::KMAJOR,
+        two(static_cast<const u16*>(w_qkv), 3 * s.hl, static_cast<const u16*>(w_fc1), s.f,
+            3 * s.hl, 0),
+        ptb::OUTER_MAJOR, ptb::EPI_QKV_GELU, e, strm));
+  }
+  PTB_STAGE(2, ptb::launch_attention_fwd(qkv, c, lse, static_cast<int>(s.b), static_cast<int>(s.s),
+                                    static_cast<int>(s.n), static_cast<int>(s.d),
+                                    static_cast<int>(s.w), strm));
+  {  // [O ; FC2] projection plus the residual
+    ptb::Epilogue e{};
+    e.o0 = static_cast<u16*>(y); e.i0 = X; e.ld0 = static_cast<int>(s.h);
+    PTB_STAGE(3, ptb::launch_gemm(
+        static_cast<int>(s.T), static_cast<int>(s.h), static_cast<int>(s.K2),
+        two(c, s.hl, g, s.f, s.hl, 1), ptb::KMAJOR,
+        two(static_cast<const u16*>(w_o), s.h, static_cast<const u16*>(w_fc2), s.h, s.hl, 1),
+        ptb::OUTER_MAJOR, ptb::EPI_RESIDUAL, e, strm));
+  }
+  return PTB_OK;
+}
+
+int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
+                           const void* ln_gamma, const void* w_qkv, const void* w_o,
+                           const void* w_fc1, const void* w_fc2, const void* saved, void* dx,
+                           void* d_ln_gamma, void* d_ln_beta, void* dw_qkv, void* dw_o,
+                           void* dw_fc1, void* dw_fc2, void* workspace, void* stream,
+                           void* const* ev) {
+  Shape s;
+  int32_t st = check_dims(dims, &s);
+  if (st != PTB_OK) return st;
+  st = check_ptrs({dy, x, ln_gamma, w_qkv, w_o, w_fc1, w_fc2, saved, dx, d_ln_gamma, d_ln_beta,
+                   dw_qkv, dw_o, dw_fc1, dw_fc2, workspace});
+  if (st != PTB_OK) return st;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  const SavedLayout L = saved_layout(s);
+  const WorkLayout W = work_layout(s);
+  const u16* a = at<u16>(saved, L.off[PTB_SAVED_A]);
+  const float* mu = at<float>(saved, L.off[PTB_SAVED_MU]);
+  const float* rstd = at<float>(saved, L.off[PTB_SAVED_RSTD]);
+  const u16* qkv = at<u16>(saved, L.off[PTB_SAVED_QKV]);
+  const u16* u = at<u16>(saved, L.off[PTB_SAVED_U]);
+  const u16* g = at<u16>(saved, L.off[PTB_SAVED_G]);
+  const u16* c = at<u16>(saved, L.off[PTB_SAVED_C]);
+  const float* lse = at<float>(saved, L.off[PTB_SAVED_LSE]);
+  u16* dc = at<u16>(workspace, W.dc);
+  u16* dz = at<u16>(workspace, W.dz);
+  float* da = at<float>(workspace, W.da);
+  float* delta = at<float>(workspace, W.delta);
+  float* partials = at<float>(workspace, W.partials);
+  const u16* DY = static_cast<const u16*>(dy);
+  const int T = static_cast<int>(s.T), h = static_cast<int>(s.h);
+
+  {  // dgrad through [O ; FC2]: dc, and du = dg * GeLU'(u) into dZ's FC1 columns
+    ptb::Epilogue e{};
+    e.o0 = dc; e.ld0 = static_cast<int>(s.hl);
+    e.o1 = dz; e.ld1 = static_cast<int>(s.N1); e.col_off1 = static_cast<int>(3 * s.hl);
+    e.i0 = u; e.ld2 = static_cast<int>(s.f);
+    e.split = static_cast<int>(s.hl);
+    PTB_STAGE(0, ptb::launch_gemm(
+        T, static_cast<int>(s.K2), h, one(DY, s.h), ptb::KMAJOR,
+        two(static_cast<const u16*>(w_o), s.h, static_cast<const u16*>(w_fc2), s.h, s.hl, 0),
+        ptb::KMAJOR, ptb::EPI_DGELU, e, strm));
+  }
+  PTB_STAGE(1, ptb::launch_attention_bwd(qkv, c, lse, dc, delta, dz, static_cast<int>(s.N1),
+                                    static_cast<int>(s.b), static_cast<int>(s.s),
+                                    static_cast<int>(s.n), static_cast<int>(s.d),
+                                    static_cast<int>(s.w), strm));
+  {  // wgrad of [O ; FC2]: [c | g]^T dy
+    ptb::Epilogue e{};
+    e.o0 = static_cast<u16*>(dw_o); e.ld0 = h;
+    e.o1 = static_cast<u16*>(dw_fc2); e.ld1 = h;
+    e.split = static_cast<int>(s.hl);
+    PTB_STAGE(2, ptb::launch_gemm(static_cast<int>(s.K2), h, T, two(c, s.hl, g, s.f, s.hl, 0),
+                             ptb::OUTER_MAJOR, one(DY, s.h), ptb::OUTER_MAJOR,
+                             ptb::EPI_STORE2_ROWS, e, strm));
+  }
+  {  // dgrad through [QKV | FC1]: da = dZ [W_qkv | W_fc1]^T (fp32)
+    ptb::Epilogue e{};
+    e.of = da; e.ld0 = h;
+    PTB_STAGE(3, ptb::launch_gemm(
+        T, h, static_cast<int>(s.N1), one(dz, s.N1), ptb::KMAJOR,
+        two(static_cast<const u16*>(w_qkv), 3 * s.hl, static_cast<const u16*>(w_fc1), s.f,
+            3 * s.hl, 1),
+        ptb::KMAJOR, ptb::EPI_F32, e, strm));
+  }
+  {  // wgrad of [QKV | FC1]: a^T dZ
+    ptb::Epilogue e{};
+    e.o0 = static_cast<u16*>(dw_qkv); e.ld0 = static_cast<int>(3 * s.hl);
+    e.o1 = static_cast<u16*>(dw_fc1); e.ld1 = static_cast<int>(s.f);
+    e.split = static_cast<int>(3 * s.hl);
+    PTB_STAGE(4, ptb::launch_gemm(h, static_cast<int>(s.N1), T, one(a, s.h), ptb::OUTER_MAJOR,
+                             one(dz, s.N1), ptb::OUTER_MAJOR, ptb::EPI_STORE2_COLS, e, strm));
+  }
+  PTB_STAGE(5, ptb::launch_layernorm_bwd(da, static_cast<const u16*>(x),
+                                    static_cast<const u16*>(ln_gamma), mu, rstd, DY,
+                                    static_cast<u16*>(dx), partials,
+                                    static_cast<u16*>(d_ln_gamma), static_cast<u16*>(d_ln_beta),
+                                    T, h, strm));
+  return PTB_OK;
+}
+
+int32_t ptb_forward(const ptb_dims* dims, const void* x, const void* ln_gamma,
+                    const void* ln_beta, const void* w_qkv, const void* w_o, const void* w_fc1,
+                    const void* w_fc2, void* y, void* saved, void* stream) {
+  return ptb_forward_timed(dims, x, ln_gamma, ln_beta, w_qkv, w_o, w_fc1, w_fc2, y, saved,
+                           stream, nullptr);
+}
+
+int32_t ptb_backward(const ptb_dims* dims, const void* dy, const void* x, const void* ln_gamma,
+                     const void* w_qkv, const void* w_o, const void* w_fc1, const void* w_fc2,
+                     const void* saved, void* dx, void* d_ln_gamma, void* d_ln_beta,
+                     void* dw_qkv, void* dw_o, void* dw_fc1, void* dw_fc2, void* workspace,
+                     void* stream) {
+  return ptb_backward_timed(dims, dy, x, ln_gamma, w_qkv, w_o, w_fc1, w_fc2, saved, dx,
+                            d_ln_gamma, d_ln_beta, dw_qkv, dw_o, dw_fc1, dw_fc2, workspace,
+                            stream, nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,207 @@
+"""Thin ctypes binding of libptb (C ABI in include/ptb.h).
+
+Argument marshalling only: tensors are passed as raw device pointers
+(``tensor.data_ptr()``), the stream as the HIP stream handle of a
+``torch.cuda.Stream`` (torch's current stream by default).  Every step of the
+layer runs inside libptb's HIP kernels; nothing here computes, and there is no
+fallback: if the library is missing, loading fails loudly.
+
+The functions carry the C names.  A non-zero status raises ``PtbError`` unless
+``check=False`` is passed, in which case the status code is returned.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libptb.so")
+
+PTB_OK = 0
+PTB_ERR_NULL = -1
+PTB_ERR_DIMS = -2
+PTB_ERR_HEAD_DIM = -3
+PTB_ERR_ALIGN = -4
+PTB_ERR_WINDOW = -5
+PTB_ERR_EPS = -6
+PTB_ERR_HIP = -7
+
+SAVED_SLOTS = ("a", "mu", "rstd", "qkv", "u", "g", "c", "lse")
+
+
+class PtbError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where} failed: status {status} ({ptb_status_string(status)})")
+        self.status = status
+
+
+class ptb_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("ln_eps", ctypes.c_float)]
+
+
+def dims_of(w) -> ptb_dims:
+    """ptb_dims of a Workload (transformer_block_amd.inputs)."""
+    return ptb_dims(w.batch, w.seq, w.hidden, w.heads, w.head_dim, w.ffn, w.window,
+                    w.ln_eps)
+
+
+_lib: Optional[ctypes.CDLL] = None
+_P = ctypes.c_void_p
+_D = ctypes.POINTER(ptb_dims)
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libptb.so (built by transformer_block_amd.build) once."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"libptb.so not found at {path}: build it first with "
+            "`python -m transformer_block_amd.build` (or __graft_entry__.build())")
+    # torch ships its own HIP runtime with the same soname; loading torch first
+    # makes libptb bind to that one copy, so torch's streams and memory are
+    # valid handles inside libptb (two runtimes in one process would not share
+    # them).
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(path)
+    sig = {
+        "ptb_abi_version": (ctypes.c_int32, []),
+        "ptb_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
+        "ptb_validate_dims": (ctypes.c_int32, [_D]),
+        "ptb_saved_bytes": (ctypes.c_int32, [_D, ctypes.POINTER(ctypes.c_size_t)]),
+        "ptb_workspace_bytes": (ctypes.c_int32, [_D, ctypes.POINTER(ctypes.c_size_t)]),
+        "ptb_saved_layout": (ctypes.c_int32, [_D, ctypes.POINTER(ctypes.c_size_t)]),
+        "ptb_forward": (ctypes.c_int32, [_D] + [_P] * 10),
+        "ptb_backward": (ctypes.c_int32, [_D] + [_P] * 17),
+        "ptb_forward_timed": (ctypes.c_int32, [_D] + [_P] * 11),
+        "ptb_backward_timed": (ctypes.c_int32, [_D] + [_P] * 18),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _done(status: int, where: str, check: bool) -> int:
+    if check and status != PTB_OK:
+        raise PtbError(status, where)
+    return status
+
+
+def ptb_abi_version() -> int:
+    return load_library().ptb_abi_version()
+
+
+def ptb_status_string(status: int) -> str:
+    return load_library().ptb_status_string(status).decode()
+
+
+def ptb_validate_dims(dims: ptb_dims) -> int:
+    return load_library().ptb_validate_dims(ctypes.byref(dims) if dims is not None else None)
+
+
+def ptb_saved_bytes(dims: ptb_dims) -> int:
+    n = ctypes.c_size_t(0)
+    _done(load_library().ptb_saved_bytes(ctypes.byref(dims), ctypes.byref(n)),
+          "ptb_saved_bytes", True)
+    return n.value
+
+
+def ptb_workspace_bytes(dims: ptb_dims) -> int:
+    n = ctypes.c_size_t(0)
+    _done(load_library().ptb_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)),
+          "ptb_workspace_bytes", True)
+    return n.value
+
+
+def ptb_saved_layout(dims: ptb_dims) -> dict:
+    arr = (ctypes.c_size_t * len(SAVED_SLOTS))()
+    _done(load_library().ptb_saved_layout(ctypes.byref(dims), arr), "ptb_saved_layout", True)
+    return dict(zip(SAVED_SLOTS, list(arr)))
+
+
+def ptb_forward(dims: ptb_dims, x, ln_gamma, ln_beta, w_qkv, w_o, w_fc1, w_fc2, y,
+                saved, stream=None, check: bool = True) -> int:
+    st = load_library().ptb_forward(
+        ctypes.byref(dims), _ptr(x), _ptr(ln_gamma), _ptr(ln_beta), _ptr(w_qkv), _ptr(w_o),
+        _ptr(w_fc1), _ptr(w_fc2), _ptr(y), _ptr(saved), _stream(stream))
+    return _done(st, "ptb_forward", check)
+
+
+def ptb_backward(dims: ptb_dims, dy, x, ln_gamma, w_qkv, w_o, w_fc1, w_fc2, saved, dx,
+                 d_ln_gamma, d_ln_beta, dw_qkv, dw_o, dw_fc1, dw_fc2, workspace,
+                 stream=None, check: bool = True) -> int:
+    st = load_library().ptb_backward(
+        ctypes.byref(dims), _ptr(dy), _ptr(x), _ptr(ln_gamma), _ptr(w_qkv), _ptr(w_o),
+        _ptr(w_fc1), _ptr(w_fc2), _ptr(saved), _ptr(dx), _ptr(d_ln_gamma), _ptr(d_ln_beta),
+        _ptr(dw_qkv), _ptr(dw_o), _ptr(dw_fc1), _ptr(dw_fc2), _ptr(workspace),
+        _stream(stream))
+    return _done(st, "ptb_backward", check)
+
+
+PTB_FWD_STAGES = 4
+PTB_BWD_STAGES = 6
+FWD_STAGE_NAMES = ("layernorm_fwd", "gemm_qkv_fc1", "attention_fwd", "gemm_o_fc2_residual")
+BWD_STAGE_NAMES = ("gemm_dgrad_o_fc2", "attention_bwd", "gemm_wgrad_o_fc2",
+                   "gemm_dgrad_qkv_fc1", "gemm_wgrad_qkv_fc1", "layernorm_bwd")
+
+
+def _events(stage_events) -> Optional[ctypes.Array]:
+    if stage_events is None:
+        return None
+    arr = (ctypes.c_void_p * len(stage_events))()
+    for i, e in enumerate(stage_events):
+        arr[i] = e
+    return arr
+
+
+def ptb_forward_timed(dims: ptb_dims, x, ln_gamma, ln_beta, w_qkv, w_o, w_fc1, w_fc2, y,
+                      saved, stream, stage_events, check: bool = True) -> int:
+    """ptb_forward plus raw hipEvent_t handles (2 per stage) recorded around
+    each stage on `stream`."""
+    st = load_library().ptb_forward_timed(
+        ctypes.byref(dims), _ptr(x), _ptr(ln_gamma), _ptr(ln_beta), _ptr(w_qkv), _ptr(w_o),
+        _ptr(w_fc1), _ptr(w_fc2), _ptr(y), _ptr(saved), _stream(stream),
+        _events(stage_events))
+    return _done(st, "ptb_forward_timed", check)
+
+
+def ptb_backward_timed(dims: ptb_dims, dy, x, ln_gamma, w_qkv, w_o, w_fc1, w_fc2, saved, dx,
+                       d_ln_gamma, d_ln_beta, dw_qkv, dw_o, dw_fc1, dw_fc2, workspace,
+                       stream, stage_events, check: bool = True) -> int:
+    st = load_library().ptb_backward_timed(
+        ctypes.byref(dims), _ptr(dy), _ptr(x), _ptr(ln_gamma), _ptr(w_qkv), _ptr(w_o),
+        _ptr(w_fc1), _ptr(w_fc2), _ptr(saved), _ptr(dx), _ptr(d_ln_gamma), _ptr(d_ln_beta),
+        _ptr(dw_qkv), _ptr(dw_o), _ptr(dw_fc1), _ptr(dw_fc2), _ptr(workspace),
+        _stream(stream), _events(stage_events))
+    return _done(st, "ptb_backward_timed", check)
+
+
+def exported_symbols() -> Sequence[str]:
+    return ("ptb_abi_version", "ptb_status_string", "ptb_validate_dims", "ptb_saved_bytes",
+            "ptb_workspace_bytes", "ptb_saved_layout", "ptb_forward", "ptb_backward",
+            "ptb_forward_timed", "ptb_backward_timed")

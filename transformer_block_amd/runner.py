@@ -1,0 +1,106 @@
+"""Device buffers for a stack of PTB layers and the calls that run it.
+
+Plumbing only: torch allocates device memory and provides the stream; every
+step of the layer runs in libptb through ``transformer_block_amd.ptb``.
+"""
+from __future__ import annotations
+
+from typing import Dict, List
+
+import numpy as np
+import torch
+
+from . import ptb as P
+from .inputs import Workload
+
+PARAM_NAMES = ("ln_gamma", "ln_beta", "w_qkv", "w_o", "w_fc1", "w_fc2")
+GRAD_NAMES = ("d_ln_gamma", "d_ln_beta", "dw_qkv", "dw_o", "dw_fc1", "dw_fc2")
+
+
+def to_device_bf16(bits: np.ndarray, device) -> torch.Tensor:
+    """uint16 bf16 bits (numpy) -> torch.bfloat16 tensor on `device`."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def bf16_to_numpy_f64(t: torch.Tensor) -> np.ndarray:
+    bits = t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+class LayerStack:
+    """`w.layers` PTB layers applied in sequence, forward then backward."""
+
+    def __init__(self, w: Workload, inputs: dict, device: str = "cuda"):
+        self.w = w
+        self.dims = P.dims_of(w)
+        self.device = torch.device(device)
+        dev = self.device
+        self.x = to_device_bf16(inputs["x"], dev)
+        self.dy = to_device_bf16(inputs["dy"], dev)
+        self.params: List[Dict[str, torch.Tensor]] = [
+            {k: to_device_bf16(lay[k], dev) for k in PARAM_NAMES} for lay in inputs["layers"]]
+        nsaved = P.ptb_saved_bytes(self.dims)
+        nwork = P.ptb_workspace_bytes(self.dims)
+        self.saved = [torch.empty(nsaved, dtype=torch.uint8, device=dev) for _ in self.params]
+        self.workspace = torch.empty(nwork, dtype=torch.uint8, device=dev)
+        self.ys = [torch.empty_like(self.x) for _ in self.params]
+        self.dxs = [torch.empty_like(self.x) for _ in self.params]
+        self.grads: List[Dict[str, torch.Tensor]] = []
+        for p in self.params:
+            self.grads.append({
+                "d_ln_gamma": torch.empty_like(p["ln_gamma"]),
+                "d_ln_beta": torch.empty_like(p["ln_beta"]),
+                "dw_qkv": torch.empty_like(p["w_qkv"]),
+                "dw_o": torch.empty_like(p["w_o"]),
+                "dw_fc1": torch.empty_like(p["w_fc1"]),
+                "dw_fc2": torch.empty_like(p["w_fc2"]),
+            })
+
+    @property
+    def y(self) -> torch.Tensor:
+        return self.ys[-1]
+
+    @property
+    def dx(self) -> torch.Tensor:
+        return self.dxs[0]
+
+    def layer_input(self, li: int) -> torch.Tensor:
+        return self.x if li == 0 else self.ys[li - 1]
+
+    def forward(self, stream=None, events=None) -> None:
+        """events: optional per-layer lists of 2*PTB_FWD_STAGES hipEvent_t handles."""
+        for li, p in enumerate(self.params):
+            P.ptb_forward_timed(self.dims, self.layer_input(li), p["ln_gamma"], p["ln_beta"],
+                                p["w_qkv"], p["w_o"], p["w_fc1"], p["w_fc2"], self.ys[li],
+                                self.saved[li], stream, events[li] if events else None)
+
+    def backward(self, stream=None, events=None) -> None:
+        """events: optional per-layer lists of 2*PTB_BWD_STAGES hipEvent_t handles."""
+        g = self.dy
+        for li in range(len(self.params) - 1, -1, -1):
+            p, gr = self.params[li], self.grads[li]
+            P.ptb_backward_timed(self.dims, g, self.layer_input(li), p["ln_gamma"], p["w_qkv"],
+                                 p["w_o"], p["w_fc1"], p["w_fc2"], self.saved[li], self.dxs[li],
+                                 gr["d_ln_gamma"], gr["d_ln_beta"], gr["dw_qkv"], gr["dw_o"],
+                                 gr["dw_fc1"], gr["dw_fc2"], self.workspace, stream,
+                                 events[li] if events else None)
+            g = self.dxs[li]
+
+    def step(self, stream=None, fwd_events=None, bwd_events=None) -> None:
+        self.forward(stream, fwd_events)
+        self.backward(stream, bwd_events)
+
+    def saved_tensor(self, li: int, name: str) -> torch.Tensor:
+        """A view of one stashed tensor of layer `li` (see ptb_saved_layout)."""
+        w = self.w
+        T, h, hl, f = w.tokens, w.hidden, w.h_local, w.ffn
+        shapes = {"a": ((T, h), torch.bfloat16), "mu": ((T,), torch.float32),
+                  "rstd": ((T,), torch.float32), "qkv": ((T, 3 * hl), torch.bfloat16),
+                  "u": ((T, f), torch.bfloat16), "g": ((T, f), torch.bfloat16),
+                  "c": ((T, hl), torch.bfloat16),
+                  "lse": ((w.batch, w.heads, w.seq), torch.float32)}
+        off = P.ptb_saved_layout(self.dims)[name]
+        shape, dt = shapes[name]
+        nbytes = int(np.prod(shape)) * (2 if dt == torch.bfloat16 else 4)
+        return self.saved[li][off:off + nbytes].view(dt).view(shape)
