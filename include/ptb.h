@@ -92,7 +92,8 @@ int32_t ptb_abi_version(void);
 const char* ptb_status_string(int32_t status);
 
 /* Check `dims` alone.  Besides the per-field rules above, every tensor of the
- * layer must hold fewer than 2^31 elements (T*(3*h_l+f), h*(3*h_l+f), ...). */
+ * layer must hold fewer than 2^30 elements (T*(3*h_l+f), h*(3*h_l+f), ...),
+ * i.e. stay below 2 GiB. */
 int32_t ptb_validate_dims(const ptb_dims* dims);
 
 /* Bytes of the forward->backward stash of one layer (`saved`). */
@@ -112,10 +113,19 @@ int32_t ptb_workspace_bytes(const ptb_dims* dims, size_t* bytes);
  *   PTB_SAVED_C    attention output          bf16 [T, h_l] (head-major cols)
  *   PTB_SAVED_LSE  base-2 log-sum-exp of the logits scaled by log2(e)/sqrt(d)
  *                                            fp32 [b, n, s]
+ *   PTB_SAVED_A_LO rounding residual of a: bf16(LN(x) - a)   bf16 [T, h]
+ *   PTB_SAVED_QK_LO rounding residual of the q and k columns of qkv
+ *                                            bf16 [T, 2*h_l]
+ * The logits q.k/sqrt(d) are formed from q and k carried as such bf16 pairs
+ * (value + residual), computed from [a | a_lo]: with the large logits of wide
+ * layers a plain bf16 rounding of a, q or k shifts every logit by a few
+ * thousandths, which the softmax turns into a comparable relative error of the
+ * attention output and of the q, k gradients.
  * `offsets` must have room for PTB_SAVED_COUNT entries. */
 enum ptb_saved_slot {
   PTB_SAVED_A = 0, PTB_SAVED_MU, PTB_SAVED_RSTD, PTB_SAVED_QKV, PTB_SAVED_U,
-  PTB_SAVED_G, PTB_SAVED_C, PTB_SAVED_LSE, PTB_SAVED_COUNT
+  PTB_SAVED_G, PTB_SAVED_C, PTB_SAVED_LSE, PTB_SAVED_A_LO, PTB_SAVED_QK_LO,
+  PTB_SAVED_COUNT
 };
 int32_t ptb_saved_layout(const ptb_dims* dims, size_t* offsets);
 

@@ -63,7 +63,8 @@ def good_dims(**kw):
     (dict(ln_eps=0.0), P.PTB_ERR_EPS),
     (dict(ln_eps=float("nan")), P.PTB_ERR_EPS),
     (dict(ln_eps=float("inf")), P.PTB_ERR_EPS),
-    (dict(batch=65536, seq=65536), P.PTB_ERR_DIMS),   # T*(3*h_l+f) >= 2^31
+    (dict(batch=65536, seq=65536), P.PTB_ERR_DIMS),   # T*(3*h_l+f) >= 2^30
+    (dict(batch=1024, seq=1024, hidden=1024, ffn=4096), P.PTB_ERR_DIMS),
     (dict(window=1), P.PTB_OK),
     (dict(seq=1, window=10 ** 9), P.PTB_OK),
 ])
@@ -85,10 +86,11 @@ def test_saved_layout_is_ordered_aligned_and_sized(lib):
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     T, h, hl, f = 512, 256, 256, 1024
     sizes = dict(a=T * h * 2, mu=T * 4, rstd=T * 4, qkv=T * 3 * hl * 2, u=T * f * 2,
-                 g=T * f * 2, c=T * hl * 2, lse=2 * 4 * 256 * 4)
+                 g=T * f * 2, c=T * hl * 2, lse=2 * 4 * 256 * 4, a_lo=T * h * 2,
+                 qk_lo=T * 2 * hl * 2)
     for a_, b_ in zip(P.SAVED_SLOTS, P.SAVED_SLOTS[1:]):
         assert lay[b_] - lay[a_] >= sizes[a_]
-    assert P.ptb_saved_bytes(d) >= lay["lse"] + sizes["lse"]
+    assert P.ptb_saved_bytes(d) >= lay["qk_lo"] + sizes["qk_lo"]
     assert P.ptb_workspace_bytes(d) >= T * (3 * hl + f) * 2 + T * h * 4
 
 

@@ -107,3 +107,18 @@ def test_repeat_runs_are_bitwise_identical():
     second = [st.y, st.dx] + list(st.grads[0].values())
     for a, b in zip(first, second):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", I.WORKLOAD_ORDER)
+def test_full_workload_parity(name):
+    """Every workload at its full size, run exactly as bench.py runs it (the
+    whole stack forward then backward through the C ABI), against the full
+    fp64 oracle."""
+    w = I.WORKLOADS[name]
+    log(f"full workload {name}: {w}")
+    inp = I.make_inputs(w)
+    st = run_gpu(w, inp)
+    log(f"[{name}] gpu step done; running the oracle")
+    ref = oracle_run(w, inp)
+    compare(w, inp, ref, st)

@@ -21,6 +21,14 @@
 // a key-parallel kernel for dK, dV (S = Q K^T, lane = key) and a
 // query-parallel kernel for dQ (S^T, lane = query), so no atomics are needed
 // and results are deterministic.
+//
+// Logit precision.  q and k arrive as bf16 pairs (value and rounding residual,
+// both from the fp32 projection), and every logit is formed as
+// q_hi.k_hi + q_lo.k_hi + q_hi.k_lo: three matrix-core products whose sum
+// carries ~16 mantissa bits.  With large logits a single bf16 rounding of q or
+// k would shift every logit by a few thousandths, which the softmax turns into
+// a relative error of the same size in the output and, through dS, in the
+// gradients of q and k.
 #include <math.h>
 
 #include "device_common.h"
@@ -118,11 +126,13 @@ struct Tile64 {
 // ------------------------------------------------------------------ forward
 template <int D>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ qkv,
+                                                       const u16* __restrict__ qk_lo,
                                                        u16* __restrict__ cout,
                                                        float* __restrict__ lse, int s, int n,
                                                        int window, int nqt) {
   constexpr int NKS = D / 16, ND = D / 32;
   __shared__ __attribute__((aligned(16))) u16 k_lds[BKV * D];
+  __shared__ __attribute__((aligned(16))) u16 kl_lds[BKV * D];
   __shared__ __attribute__((aligned(16))) u16 vt_lds[D * BKV];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -133,14 +143,20 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ q
   const u16* Qg = qkv + static_cast<size_t>(bi) * s * ld + hd * D;
   const u16* Kg = Qg + hl;
   const u16* Vg = Qg + 2 * hl;
+  const u16* Qlg = qk_lo + static_cast<size_t>(bi) * s * (2 * hl) + hd * D;
+  const u16* Klg = Qlg + hl;
   const int q0 = qt * BQ, qw0 = q0 + wave * 32, qi = qw0 + l32;
 
-  bf16x8 qf[NKS];
+  bf16x8 qf[NKS], ql[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    uint4 t = make_uint4(0u, 0u, 0u, 0u);
-    if (qi < s) t = *reinterpret_cast<const uint4*>(Qg + qi * ld + ks * 16 + g * 8);
+    uint4 t = make_uint4(0u, 0u, 0u, 0u), u = t;
+    if (qi < s) {
+      t = *reinterpret_cast<const uint4*>(Qg + qi * ld + ks * 16 + g * 8);
+      u = *reinterpret_cast<const uint4*>(Qlg + qi * (2 * hl) + ks * 16 + g * 8);
+    }
     qf[ks] = as_bf16x8(t);
+    ql[ks] = as_bf16x8(u);
   }
 
   const float sc = kLog2e / sqrtf(static_cast<float>(D));
@@ -153,12 +169,14 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ q
 
   const int kv_begin = max(0, q0 - window + 1) & ~(BKV - 1);
   const int kv_end = min(s, q0 + BQ);
-  Tile64<D> kt, vt;
+  Tile64<D> kt, ktl, vt;
   for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKV) {
     kt.load(Kg, ld, kt0, s, tid);
+    ktl.load(Klg, 2 * hl, kt0, s, tid);
     vt.load(Vg, ld, kt0, s, tid);
     __syncthreads();
     kt.store_rows(k_lds, tid);
+    ktl.store_rows(kl_lds, tid);
     vt.store_transposed(vt_lds, tid);
     __syncthreads();
 
@@ -172,8 +190,12 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ q
 #pragma unroll
       for (int e = 0; e < 16; ++e) st[kb][e] = 0.0f;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        st[kb] = mfma32x32x16(row_frag<D>(k_lds, kb * 32 + l32, ks * 2 + g), qf[ks], st[kb]);
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 kh = row_frag<D>(k_lds, kb * 32 + l32, ks * 2 + g);
+        st[kb] = mfma32x32x16(kh, qf[ks], st[kb]);
+        st[kb] = mfma32x32x16(row_frag<D>(kl_lds, kb * 32 + l32, ks * 2 + g), qf[ks], st[kb]);
+        st[kb] = mfma32x32x16(kh, ql[ks], st[kb]);
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -268,11 +290,12 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const u16* __restrict__
 // ------------------------------------------------------------ dK and dV
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
-    const u16* __restrict__ qkv, const u16* __restrict__ dcg, const float* __restrict__ lse,
-    const float* __restrict__ delta, u16* __restrict__ dz, int ld_dz, int s, int n,
-    int window) {
+    const u16* __restrict__ qkv, const u16* __restrict__ qk_lo, const u16* __restrict__ dcg,
+    const float* __restrict__ lse, const float* __restrict__ delta, u16* __restrict__ dz,
+    int ld_dz, int s, int n, int window) {
   constexpr int NKS = D / 16, ND = D / 32;
   __shared__ __attribute__((aligned(16))) u16 q_lds[BQB * D];
+  __shared__ __attribute__((aligned(16))) u16 ql_lds[BQB * D];
   __shared__ __attribute__((aligned(16))) u16 qt_lds[D * BQB];
   __shared__ __attribute__((aligned(16))) u16 do_lds[BQB * D];
   __shared__ __attribute__((aligned(16))) u16 dot_lds[D * BQB];
@@ -287,20 +310,24 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const u16* Kg = Qg + hl;
   const u16* Vg = Qg + 2 * hl;
   const u16* dOg = dcg + static_cast<size_t>(bi) * s * hl + hd * D;
+  const u16* Qlg = qk_lo + static_cast<size_t>(bi) * s * (2 * hl) + hd * D;
+  const u16* Klg = Qlg + hl;
   const float* lse_h = lse + (static_cast<size_t>(bi) * n + hd) * s;
   const float* dl_h = delta + (static_cast<size_t>(bi) * n + hd) * s;
   const int kb0 = blockIdx.x * BKB, kw0 = kb0 + wave * 32, kj = kw0 + l32;
 
-  bf16x8 kf[NKS], vf[NKS];
+  bf16x8 kf[NKS], kl[NKS], vf[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
+    uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a, c = a;
     if (kj < s) {
       a = *reinterpret_cast<const uint4*>(Kg + kj * ld + ks * 16 + g * 8);
       b = *reinterpret_cast<const uint4*>(Vg + kj * ld + ks * 16 + g * 8);
+      c = *reinterpret_cast<const uint4*>(Klg + kj * (2 * hl) + ks * 16 + g * 8);
     }
     kf[ks] = as_bf16x8(a);
     vf[ks] = as_bf16x8(b);
+    kl[ks] = as_bf16x8(c);
   }
   const float sc = kLog2e / sqrtf(static_cast<float>(D));
   f32x16 dv[ND], dk[ND];
@@ -311,12 +338,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 
   const int q_begin = kb0 & ~(BQB - 1);
   const int q_end = min(s, kb0 + BKB - 1 + window);
-  Tile64<D> qtile, otile;
+  Tile64<D> qtile, qltile, otile;
   for (int qt0 = q_begin; qt0 < q_end; qt0 += BQB) {
     qtile.load(Qg, ld, qt0, s, tid);
+    qltile.load(Qlg, 2 * hl, qt0, s, tid);
     otile.load(dOg, hl, qt0, s, tid);
     __syncthreads();
     qtile.store_rows(q_lds, tid);
+    qltile.store_rows(ql_lds, tid);
     qtile.store_transposed(qt_lds, tid);
     otile.store_rows(do_lds, tid);
     otile.store_transposed(dot_lds, tid);
@@ -331,42 +360,42 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     if (!any) continue;
     const bool full = qt0 >= kw0 + 31 && qt0 + BQB - 1 - kw0 < window && qt0 + BQB <= s;
 
-    f32x16 sp[2], dp[2];
-#pragma unroll
+    // the two 32-query halves one after the other (fewer live registers)
+#pragma unroll 1
     for (int qb = 0; qb < 2; ++qb) {
+      f32x16 sp, dp;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) { sp[qb][e] = 0.0f; dp[qb][e] = 0.0f; }
+      for (int e = 0; e < 16; ++e) { sp[e] = 0.0f; dp[e] = 0.0f; }
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        sp[qb] = mfma32x32x16(row_frag<D>(q_lds, qb * 32 + l32, ks * 2 + g), kf[ks], sp[qb]);
-        dp[qb] = mfma32x32x16(row_frag<D>(do_lds, qb * 32 + l32, ks * 2 + g), vf[ks], dp[qb]);
+        const bf16x8 qh = row_frag<D>(q_lds, qb * 32 + l32, ks * 2 + g);
+        sp = mfma32x32x16(qh, kf[ks], sp);
+        sp = mfma32x32x16(row_frag<D>(ql_lds, qb * 32 + l32, ks * 2 + g), kf[ks], sp);
+        sp = mfma32x32x16(qh, kl[ks], sp);
+        dp = mfma32x32x16(row_frag<D>(do_lds, qb * 32 + l32, ks * 2 + g), vf[ks], dp);
       }
-    }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int lq = qb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
-        float p = exp2f(sp[qb][e] * sc - lse_lds[lq]);
+        float p = exp2f(sp[e] * sc - lse_lds[lq]);
         if (!full) {
           const int diff = qt0 + lq - kj;
           if (diff < 0 || diff >= window || qt0 + lq >= s) p = 0.0f;
         }
-        sp[qb][e] = p;
-        dp[qb][e] = p * (dp[qb][e] - dl_lds[lq]);
+        sp[e] = p;
+        dp[e] = p * (dp[e] - dl_lds[lq]);
       }
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
       for (int e2 = 0; e2 < 2; ++e2) {
-        const bf16x8 pb = pack8(sp[qb], e2 * 8);
-        const bf16x8 dsb = pack8(dp[qb], e2 * 8);
+        const bf16x8 pb = pack8(sp, e2 * 8);
+        const bf16x8 dsb = pack8(dp, e2 * 8);
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
           dv[db] = mfma32x32x16(tfrag(dot_lds, db * 32 + l32, qb * 32 + e2 * 16, g), pb, dv[db]);
           dk[db] = mfma32x32x16(tfrag(qt_lds, db * 32 + l32, qb * 32 + e2 * 16, g), dsb, dk[db]);
         }
       }
+    }
   }
 
   if (kj < s) {
@@ -390,11 +419,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 // ------------------------------------------------------------------- dQ
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
-    const u16* __restrict__ qkv, const u16* __restrict__ dcg, const float* __restrict__ lse,
-    const float* __restrict__ delta, u16* __restrict__ dz, int ld_dz, int s, int n,
-    int window, int nqt) {
+    const u16* __restrict__ qkv, const u16* __restrict__ qk_lo, const u16* __restrict__ dcg,
+    const float* __restrict__ lse, const float* __restrict__ delta, u16* __restrict__ dz,
+    int ld_dz, int s, int n, int window, int nqt) {
   constexpr int NKS = D / 16, ND = D / 32;
   __shared__ __attribute__((aligned(16))) u16 k_lds[BKV * D];
+  __shared__ __attribute__((aligned(16))) u16 kl_lds[BKV * D];
   __shared__ __attribute__((aligned(16))) u16 kt_lds[D * BKV];
   __shared__ __attribute__((aligned(16))) u16 v_lds[BKV * D];
 
@@ -407,18 +437,22 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const u16* Kg = Qg + hl;
   const u16* Vg = Qg + 2 * hl;
   const u16* dOg = dcg + static_cast<size_t>(bi) * s * hl + hd * D;
+  const u16* Qlg = qk_lo + static_cast<size_t>(bi) * s * (2 * hl) + hd * D;
+  const u16* Klg = Qlg + hl;
   const int q0 = qt * BQ, qw0 = q0 + wave * 32, qi = qw0 + l32;
 
-  bf16x8 qf[NKS], of[NKS];
+  bf16x8 qf[NKS], ql[NKS], of[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
+    uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a, c = a;
     if (qi < s) {
       a = *reinterpret_cast<const uint4*>(Qg + qi * ld + ks * 16 + g * 8);
       b = *reinterpret_cast<const uint4*>(dOg + qi * hl + ks * 16 + g * 8);
+      c = *reinterpret_cast<const uint4*>(Qlg + qi * (2 * hl) + ks * 16 + g * 8);
     }
     qf[ks] = as_bf16x8(a);
     of[ks] = as_bf16x8(b);
+    ql[ks] = as_bf16x8(c);
   }
   const size_t hrow = (static_cast<size_t>(bi) * n + hd) * s;
   const float lq = qi < s ? lse[hrow + qi] : 0.0f;
@@ -433,12 +467,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 
   const int kv_begin = max(0, q0 - window + 1) & ~(BKV - 1);
   const int kv_end = min(s, q0 + BQ);
-  Tile64<D> ktile, vtile;
+  Tile64<D> ktile, kltile, vtile;
   for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKV) {
     ktile.load(Kg, ld, kt0, s, tid);
+    kltile.load(Klg, 2 * hl, kt0, s, tid);
     vtile.load(Vg, ld, kt0, s, tid);
     __syncthreads();
     ktile.store_rows(k_lds, tid);
+    kltile.store_rows(kl_lds, tid);
     ktile.store_transposed(kt_lds, tid);
     vtile.store_rows(v_lds, tid);
     __syncthreads();
@@ -454,7 +490,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
       for (int e = 0; e < 16; ++e) { st[kb][e] = 0.0f; dpt[kb][e] = 0.0f; }
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        st[kb] = mfma32x32x16(row_frag<D>(k_lds, kb * 32 + l32, ks * 2 + g), qf[ks], st[kb]);
+        const bf16x8 kh = row_frag<D>(k_lds, kb * 32 + l32, ks * 2 + g);
+        st[kb] = mfma32x32x16(kh, qf[ks], st[kb]);
+        st[kb] = mfma32x32x16(row_frag<D>(kl_lds, kb * 32 + l32, ks * 2 + g), qf[ks], st[kb]);
+        st[kb] = mfma32x32x16(kh, ql[ks], st[kb]);
         dpt[kb] = mfma32x32x16(row_frag<D>(v_lds, kb * 32 + l32, ks * 2 + g), of[ks], dpt[kb]);
       }
     }
@@ -497,17 +536,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 }
 
 template <int D>
-hipError_t fwd_d(const u16* qkv, u16* c, float* lse, int b, int s, int n, int window,
-                 hipStream_t st) {
+hipError_t fwd_d(const u16* qkv, const u16* qk_lo, u16* c, float* lse, int b, int s, int n,
+                 int window, hipStream_t st) {
   const int nqt = (s + BQ - 1) / BQ;
-  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(nqt, n, b), dim3(256), 0, st, qkv, c, lse, s, n,
-                     window, nqt);
+  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(nqt, n, b), dim3(256), 0, st, qkv, qk_lo, c, lse,
+                     s, n, window, nqt);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t bwd_d(const u16* qkv, const u16* c, const float* lse, const u16* dc, float* delta,
-                 u16* dz, int ld_dz, int b, int s, int n, int window, hipStream_t st) {
+hipError_t bwd_d(const u16* qkv, const u16* qk_lo, const u16* c, const float* lse,
+                 const u16* dc, float* delta, u16* dz, int ld_dz, int b, int s, int n,
+                 int window, hipStream_t st) {
   const int T = b * s;
   const long items = static_cast<long>(T) * n;
   const int per_block = 256 / (D / 8);
@@ -516,29 +556,30 @@ hipError_t bwd_d(const u16* qkv, const u16* c, const float* lse, const u16* dc, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((s + BKB - 1) / BKB, n, b), dim3(256), 0, st,
-                     qkv, dc, lse, delta, dz, ld_dz, s, n, window);
+                     qkv, qk_lo, dc, lse, delta, dz, ld_dz, s, n, window);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqt = (s + BQ - 1) / BQ;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(nqt, n, b), dim3(256), 0, st, qkv, dc, lse,
-                     delta, dz, ld_dz, s, n, window, nqt);
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(nqt, n, b), dim3(256), 0, st, qkv, qk_lo, dc,
+                     lse, delta, dz, ld_dz, s, n, window, nqt);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attention_fwd(const u16* qkv, u16* c, float* lse, int b, int s, int n, int d,
-                                int window, hipStream_t st) {
-  if (d == 128) return fwd_d<128>(qkv, c, lse, b, s, n, window, st);
-  if (d == 64) return fwd_d<64>(qkv, c, lse, b, s, n, window, st);
+hipError_t launch_attention_fwd(const u16* qkv, const u16* qk_lo, u16* c, float* lse, int b,
+                                int s, int n, int d, int window, hipStream_t st) {
+  if (d == 128) return fwd_d<128>(qkv, qk_lo, c, lse, b, s, n, window, st);
+  if (d == 64) return fwd_d<64>(qkv, qk_lo, c, lse, b, s, n, window, st);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attention_bwd(const u16* qkv, const u16* c, const float* lse, const u16* dc,
-                                float* delta, u16* dz, int ld_dz, int b, int s, int n, int d,
-                                int window, hipStream_t st) {
-  if (d == 128) return bwd_d<128>(qkv, c, lse, dc, delta, dz, ld_dz, b, s, n, window, st);
-  if (d == 64) return bwd_d<64>(qkv, c, lse, dc, delta, dz, ld_dz, b, s, n, window, st);
+hipError_t launch_attention_bwd(const u16* qkv, const u16* qk_lo, const u16* c,
+                                const float* lse, const u16* dc, float* delta, u16* dz,
+                                int ld_dz, int b, int s, int n, int d, int window,
+                                hipStream_t st) {
+  if (d == 128) return bwd_d<128>(qkv, qk_lo, c, lse, dc, delta, dz, ld_dz, b, s, n, window, st);
+  if (d == 64) return bwd_d<64>(qkv, qk_lo, c, lse, dc, delta, dz, ld_dz, b, s, n, window, st);
   return hipErrorInvalidValue;
 }
 

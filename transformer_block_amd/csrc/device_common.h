@@ -38,12 +38,32 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Exact GeLU u * Phi(u) and its derivative Phi(u) + u * phi(u).
+// erf(x) by the rational approximation of Abramowitz & Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26 (|error| <= 1.5e-7 for all x):
+//   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+//   t = 1 / (1 + p x), x >= 0, and erf(-x) = -erf(x).
+// Inline straight-line code: a library call here would force every live
+// accumulator of the GEMM epilogue to be saved around it.
+__device__ __forceinline__ float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
+  float poly = 1.061405429f;
+  poly = poly * t - 1.453152027f;
+  poly = poly * t + 1.421413741f;
+  poly = poly * t - 0.284496736f;
+  poly = poly * t + 0.254829592f;
+  poly *= t;
+  const float r = 1.0f - poly * __expf(-ax * ax);
+  return copysignf(r, x);
+}
+
+// Exact GeLU u * Phi(u) and its derivative Phi(u) + u * phi(u), with
+// Phi(u) = (1 + erf(u / sqrt 2)) / 2 and phi(u) = exp(-u^2 / 2) / sqrt(2 pi).
 __device__ __forceinline__ float gelu_f(float u) {
-  return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f));
+  return 0.5f * u * (1.0f + erf_as(u * 0.70710678118654752f));
 }
 __device__ __forceinline__ float gelu_grad_f(float u) {
-  const float cdf = 0.5f * (1.0f + erff(u * 0.70710678118654752f));
+  const float cdf = 0.5f * (1.0f + erf_as(u * 0.70710678118654752f));
   const float pdf = 0.39894228040143268f * __expf(-0.5f * u * u);
   return cdf + u * pdf;
 }

@@ -15,6 +15,8 @@ typedef uint16_t u16;
 // segment 1 are taken relative to `split`.  This addresses the concatenated
 // weights [W_qkv | W_fc1] and [W_o ; W_fc2] and the concatenated activations
 // [c | g] in place, without copying them.
+// bytes0/bytes1 bound each segment: reads at or past them return zero.  Split
+// points must be multiples of 64.
 struct Operand {
   const u16* p0;
   const u16* p1;
@@ -22,6 +24,8 @@ struct Operand {
   int ld1;
   int split;
   int split_on_k;
+  uint32_t bytes0;
+  uint32_t bytes1;
 };
 
 // Storage order of an operand: KMAJOR means element (outer r, k) sits at
@@ -30,7 +34,9 @@ enum Major { KMAJOR = 0, OUTER_MAJOR = 1 };
 
 // What the GEMM does with each fp32 result v at (row r, column c).
 enum EpiMode {
-  EPI_QKV_GELU = 0,  // c < split: o0[r*ld0+c] = v; else o1 = v (u), o2 = GeLU(v) (g)
+  EPI_QKV_GELU = 0,  // with gc = c + col_base: gc < split: o0[r*ld0+gc] = bf16(v), and
+                     // for gc < lo_cols also o3[r*ld3+gc] = bf16(v - bf16(v));
+                     // else o1 = v (u), o2 = GeLU(v) (g) at column gc - split
   EPI_RESIDUAL = 1,  // o0[r*ld0+c] = v + i0[r*ld0+c]
   EPI_DGELU = 2,     // c < split: o0[r*ld0+c] = v; else o1[r*ld1+col_off1+c-split] =
                      //   v * GeLU'(i0[r*ld2 + c-split])
@@ -43,11 +49,21 @@ struct Epilogue {
   u16* o0;
   u16* o1;
   u16* o2;
+  u16* o3;
   float* of;
   const u16* i0;
-  int ld0, ld1, ld2;
+  int ld0, ld1, ld2, ld3;
   int col_off1;
+  int col_base;
+  int lo_cols;
   int split;
+};
+
+// One matrix product C[M,N] = A[M,K] * B[K,N] and what happens to C.
+struct GemmProblem {
+  int M, N, K;
+  Operand A, B;
+  Epilogue epi;
 };
 
 // C[M,N] = A[M,K] * B[K,N] with the epilogue applied to C.
@@ -55,9 +71,15 @@ hipError_t launch_gemm(int M, int N, int K, const Operand& A, Major a_major,
                        const Operand& B, Major b_major, EpiMode mode,
                        const Epilogue& epi, hipStream_t stream);
 
-// LayerNorm forward over rows of x [T, h]: a (bf16), mu, rstd (fp32).
+// Up to two independent products sharing operand orders and epilogue kind,
+// in one launch (the tiles of both fill the GPU together).
+hipError_t launch_gemm_group(const GemmProblem* probs, int nprob, Major a_major,
+                             Major b_major, EpiMode mode, hipStream_t stream);
+
+// LayerNorm forward over rows of x [T, h]: a = bf16(LN(x)) and its rounding
+// residual a_lo = bf16(LN(x) - a), mu, rstd (fp32).
 hipError_t launch_layernorm_fwd(const u16* x, const u16* gamma, const u16* beta,
-                                u16* a, float* mu, float* rstd, int T, int h,
+                                u16* a, u16* a_lo, float* mu, float* rstd, int T, int h,
                                 float eps, hipStream_t stream);
 
 // LayerNorm backward plus residual: dx = dy + LN'(da); per-block partial sums
@@ -69,16 +91,16 @@ hipError_t launch_layernorm_bwd(const float* da, const u16* x, const u16* gamma,
                                 int T, int h, hipStream_t stream);
 
 // Sliding-window causal flash attention, forward: reads q, k, v column blocks
-// of qkv [b*s, 3*n*d]; writes c [b*s, n*d] and the base-2 log-sum-exp
-// lse [b, n, s].
-hipError_t launch_attention_fwd(const u16* qkv, u16* c, float* lse, int b, int s,
-                                int n, int d, int window, hipStream_t stream);
+// of qkv [b*s, 3*n*d] and the rounding residuals of q and k, qk_lo [b*s, 2*n*d];
+// writes c [b*s, n*d] and the base-2 log-sum-exp lse [b, n, s].
+hipError_t launch_attention_fwd(const u16* qkv, const u16* qk_lo, u16* c, float* lse,
+                                int b, int s, int n, int d, int window, hipStream_t stream);
 
 // Attention backward.  delta[b,n,s] = rowsum(dc * c) per head first, then
 // dk, dv and dq written into the first 3*n*d columns of dz [b*s, ld_dz].
-hipError_t launch_attention_bwd(const u16* qkv, const u16* c, const float* lse,
-                                const u16* dc, float* delta, u16* dz, int ld_dz,
-                                int b, int s, int n, int d, int window,
+hipError_t launch_attention_bwd(const u16* qkv, const u16* qk_lo, const u16* c,
+                                const float* lse, const u16* dc, float* delta, u16* dz,
+                                int ld_dz, int b, int s, int n, int d, int window,
                                 hipStream_t stream);
 
 }  // namespace ptb

@@ -8,7 +8,9 @@
 // Forward: one 256-thread workgroup per token row; the row (h <= 16384 bf16)
 // is read once into registers with 16-byte loads, mean and variance come from
 // two block reductions over the register copy, and a = gamma*(x-mu)*rstd+beta
-// is written back in bf16 with 16-byte stores.
+// is written back in bf16 with 16-byte stores, together with its rounding
+// residual a_lo = bf16(a_fp32 - a) (used where bf16 rounding of a would be
+// amplified: the query/key projection feeding the softmax logits).
 // Backward: each workgroup walks a strided set of rows, computes
 //   dx = dy + rstd * (g - mean(g) - xhat * mean(g * xhat)),  g = da * gamma,
 // and keeps per-column partial sums of dgamma = sum da*xhat and dbeta = sum da
@@ -42,6 +44,7 @@ __global__ __launch_bounds__(LN_THREADS) void ln_fwd_kernel(const u16* __restric
                                                             const u16* __restrict__ gamma,
                                                             const u16* __restrict__ beta,
                                                             u16* __restrict__ a,
+                                                            u16* __restrict__ a_lo,
                                                             float* __restrict__ mu_out,
                                                             float* __restrict__ rstd_out,
                                                             int h, float eps) {
@@ -73,6 +76,7 @@ __global__ __launch_bounds__(LN_THREADS) void ln_fwd_kernel(const u16* __restric
   const float var = block_sum(sq, red) / static_cast<float>(h);
   const float rstd = 1.0f / sqrtf(var + eps);
   u16* ar = a + static_cast<size_t>(row) * h;
+  u16* alr = a_lo + static_cast<size_t>(row) * h;
 #pragma unroll
   for (int i = 0; i < LN_MAXCH; ++i) {
     const int c = tid + i * LN_THREADS;
@@ -80,12 +84,16 @@ __global__ __launch_bounds__(LN_THREADS) void ln_fwd_kernel(const u16* __restric
       float gm[8], bt[8];
       unpack8(*reinterpret_cast<const uint4*>(gamma + c * 8), gm);
       unpack8(*reinterpret_cast<const uint4*>(beta + c * 8), bt);
-      uint32_t o[4];
+      uint32_t o[4], ol[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        o[j] = pack2bf((v[i][2 * j] - mu) * rstd * gm[2 * j] + bt[2 * j],
-                       (v[i][2 * j + 1] - mu) * rstd * gm[2 * j + 1] + bt[2 * j + 1]);
+      for (int j = 0; j < 4; ++j) {
+        const float v0 = (v[i][2 * j] - mu) * rstd * gm[2 * j] + bt[2 * j];
+        const float v1 = (v[i][2 * j + 1] - mu) * rstd * gm[2 * j + 1] + bt[2 * j + 1];
+        o[j] = pack2bf(v0, v1);
+        ol[j] = pack2bf(v0 - lo_bf(o[j]), v1 - hi_bf(o[j]));
+      }
       *reinterpret_cast<uint4*>(ar + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(alr + c * 8) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
     }
   }
   if (tid == 0) { mu_out[row] = mu; rstd_out[row] = rstd; }
@@ -215,11 +223,11 @@ __global__ __launch_bounds__(256) void ln_bwd_reduce_kernel(const float* __restr
 }  // namespace
 
 hipError_t launch_layernorm_fwd(const u16* x, const u16* gamma, const u16* beta, u16* a,
-                                float* mu, float* rstd, int T, int h, float eps,
+                                u16* a_lo, float* mu, float* rstd, int T, int h, float eps,
                                 hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ln_fwd_kernel, dim3(T), dim3(LN_THREADS), 0, s, x, gamma, beta, a, mu,
-                     rstd, h, eps);
+  hipLaunchKernelGGL(ln_fwd_kernel, dim3(T), dim3(LN_THREADS), 0, s, x, gamma, beta, a, a_lo,
+                     mu, rstd, h, eps);
   return hipGetLastError();
 }
 

@@ -5,7 +5,8 @@
 // (MegaScale reading notes, section 1.1, eq (4)).
 //
 // Forward, four launches on the caller's stream:
-//   LN(x) -> a;  a x [W_qkv | W_fc1] -> qkv, u, g = GeLU(u);
+//   LN(x) -> a (+ residual a_lo);  a x [W_qkv | W_fc1] -> qkv, u, g = GeLU(u)
+//   (the q, k columns from [a | a_lo], kept as value + residual);
 //   sliding-window flash attention -> c, lse;  [c | g] x [W_o ; W_fc2] + x -> y.
 // Backward:
 //   dy x [W_o ; W_fc2]^T -> dc, du = dg * GeLU'(u);  attention backward
@@ -50,8 +51,9 @@ int32_t check_dims(const ptb_dims* dims, Shape* out) {
   s.hl = s.n * s.d;
   s.N1 = 3 * s.hl + s.f;
   s.K2 = s.hl + s.f;
-  const long lim = INT_MAX;
-  // every tensor must be indexable with 32-bit element offsets
+  const long lim = 1L << 30;
+  // every tensor must stay below 2^31 bytes: kernels address it with 32-bit
+  // byte offsets
   if (s.T > lim / s.N1 || s.h > lim / s.N1 || s.T > lim / s.h || s.K2 > lim / s.h ||
       s.b * s.n > lim / s.s)
     return PTB_ERR_DIMS;
@@ -76,6 +78,8 @@ SavedLayout saved_layout(const Shape& s) {
   put(PTB_SAVED_G, s.T * s.f * 2);
   put(PTB_SAVED_C, s.T * s.hl * 2);
   put(PTB_SAVED_LSE, s.b * s.n * s.s * 4);
+  put(PTB_SAVED_A_LO, s.T * s.h * 2);
+  put(PTB_SAVED_QK_LO, s.T * 2 * s.hl * 2);
   L.total = o;
   return L;
 }
@@ -113,12 +117,21 @@ const T* at(const void* base, size_t off) {
   return reinterpret_cast<const T*>(static_cast<const char*>(base) + off);
 }
 
-ptb::Operand one(const u16* p, long ld) {
-  return ptb::Operand{p, p, static_cast<int>(ld), static_cast<int>(ld), INT_MAX, 0};
+// A GEMM operand: row-major segments with leading dimension ld and `rows` rows.
+ptb::Operand one(const u16* p, long ld, long rows) {
+  const uint32_t bytes = static_cast<uint32_t>(ld * rows * 2);
+  return ptb::Operand{p, p, static_cast<int>(ld), static_cast<int>(ld), INT_MAX, 0, bytes, bytes};
 }
-ptb::Operand two(const u16* p0, long ld0, const u16* p1, long ld1, long split, int on_k) {
+ptb::Operand two(const u16* p0, long ld0, long rows0, const u16* p1, long ld1, long rows1,
+                 long split, int on_k) {
   return ptb::Operand{p0, p1, static_cast<int>(ld0), static_cast<int>(ld1),
-                      static_cast<int>(split), on_k};
+                      static_cast<int>(split), on_k, static_cast<uint32_t>(ld0 * rows0 * 2),
+                      static_cast<uint32_t>(ld1 * rows1 * 2)};
+}
+// Bytes spanned by `rows` rows of `width` elements at leading dimension ld
+// (a column block of a wider matrix).
+uint32_t view_bytes(long ld, long rows, long width) {
+  return static_cast<uint32_t>(((rows - 1) * ld + width) * 2);
 }
 
 #define PTB_HIP(expr)                              \
@@ -205,34 +218,52 @@ int32_t ptb_forward_timed(const ptb_dims* dims, const void* x, const void* ln_ga
   u16* g = at<u16>(saved, L.off[PTB_SAVED_G]);
   u16* c = at<u16>(saved, L.off[PTB_SAVED_C]);
   float* lse = at<float>(saved, L.off[PTB_SAVED_LSE]);
+  u16* a_lo = at<u16>(saved, L.off[PTB_SAVED_A_LO]);
+  u16* qk_lo = at<u16>(saved, L.off[PTB_SAVED_QK_LO]);
   const u16* X = static_cast<const u16*>(x);
+  const u16* Wqkv = static_cast<const u16*>(w_qkv);
 
   PTB_STAGE(0, ptb::launch_layernorm_fwd(X, static_cast<const u16*>(ln_gamma),
-                                    static_cast<const u16*>(ln_beta), a, mu, rstd,
+                                    static_cast<const u16*>(ln_beta), a, a_lo, mu, rstd,
                                     static_cast<int>(s.T), static_cast<int>(s.h), dims->ln_eps,
                                     strm));
-  {  // [QKV | FC1] projection with GeLU on the FC1 columns
+  {  // [QKV | FC1] projection in one launch of two products:
+     //   [q | k] = [a | a_lo] x [W_q|k ; W_q|k]   (stored as value + residual)
+     //   [v | u] = a x [W_v | W_fc1], with g = GeLU(u) on the FC1 columns
     ptb::Epilogue e{};
     e.o0 = qkv; e.ld0 = static_cast<int>(3 * s.hl);
     e.o1 = u; e.o2 = g; e.ld1 = static_cast<int>(s.f);
+    e.o3 = qk_lo; e.ld3 = static_cast<int>(2 * s.hl); e.lo_cols = static_cast<int>(2 * s.hl);
     e.split = static_cast<int>(3 * s.hl);
-    PTB_STAGE(1, ptb::launch_gemm(
-        static_cast<int>(s.T), static_cast<int>(s.N1), static_cast<int>(s.h), one(a, s.h),
-        ptb::KMAJOR,
-        two(static_cast<const u16*>(w_qkv), 3 * s.hl, static_cast<const u16*>(w_fc1), s.f,
-            3 * s.hl, 0),
-        ptb::OUTER_MAJOR, ptb::EPI_QKV_GELU, e, strm));
+    ptb::GemmProblem pr[2];
+    pr[0].M = static_cast<int>(s.T); pr[0].N = static_cast<int>(2 * s.hl);
+    pr[0].K = static_cast<int>(2 * s.h);
+    pr[0].A = two(a, s.h, s.T, a_lo, s.h, s.T, s.h, 1);
+    pr[0].B = two(Wqkv, 3 * s.hl, s.h, Wqkv, 3 * s.hl, s.h, s.h, 1);
+    pr[0].epi = e;
+    pr[0].epi.col_base = 0;
+    pr[1].M = static_cast<int>(s.T); pr[1].N = static_cast<int>(s.hl + s.f);
+    pr[1].K = static_cast<int>(s.h);
+    pr[1].A = one(a, s.h, s.T);
+    pr[1].B = two(Wqkv + 2 * s.hl, 3 * s.hl, s.h, static_cast<const u16*>(w_fc1), s.f, s.h,
+                  s.hl, 0);
+    pr[1].B.bytes0 = view_bytes(3 * s.hl, s.h, s.hl);
+    pr[1].epi = e;
+    pr[1].epi.col_base = static_cast<int>(2 * s.hl);
+    PTB_STAGE(1, ptb::launch_gemm_group(pr, 2, ptb::KMAJOR, ptb::OUTER_MAJOR,
+                                        ptb::EPI_QKV_GELU, strm));
   }
-  PTB_STAGE(2, ptb::launch_attention_fwd(qkv, c, lse, static_cast<int>(s.b), static_cast<int>(s.s),
-                                    static_cast<int>(s.n), static_cast<int>(s.d),
-                                    static_cast<int>(s.w), strm));
+  PTB_STAGE(2, ptb::launch_attention_fwd(qkv, qk_lo, c, lse, static_cast<int>(s.b),
+                                    static_cast<int>(s.s), static_cast<int>(s.n),
+                                    static_cast<int>(s.d), static_cast<int>(s.w), strm));
   {  // [O ; FC2] projection plus the residual
     ptb::Epilogue e{};
     e.o0 = static_cast<u16*>(y); e.i0 = X; e.ld0 = static_cast<int>(s.h);
     PTB_STAGE(3, ptb::launch_gemm(
         static_cast<int>(s.T), static_cast<int>(s.h), static_cast<int>(s.K2),
-        two(c, s.hl, g, s.f, s.hl, 1), ptb::KMAJOR,
-        two(static_cast<const u16*>(w_o), s.h, static_cast<const u16*>(w_fc2), s.h, s.hl, 1),
+        two(c, s.hl, s.T, g, s.f, s.T, s.hl, 1), ptb::KMAJOR,
+        two(static_cast<const u16*>(w_o), s.h, s.hl, static_cast<const u16*>(w_fc2), s.h, s.f,
+            s.hl, 1),
         ptb::OUTER_MAJOR, ptb::EPI_RESIDUAL, e, strm));
   }
   return PTB_OK;
@@ -261,6 +292,7 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
   const u16* g = at<u16>(saved, L.off[PTB_SAVED_G]);
   const u16* c = at<u16>(saved, L.off[PTB_SAVED_C]);
   const float* lse = at<float>(saved, L.off[PTB_SAVED_LSE]);
+  const u16* qk_lo = at<u16>(saved, L.off[PTB_SAVED_QK_LO]);
   u16* dc = at<u16>(workspace, W.dc);
   u16* dz = at<u16>(workspace, W.dz);
   float* da = at<float>(workspace, W.da);
@@ -276,11 +308,12 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
     e.i0 = u; e.ld2 = static_cast<int>(s.f);
     e.split = static_cast<int>(s.hl);
     PTB_STAGE(0, ptb::launch_gemm(
-        T, static_cast<int>(s.K2), h, one(DY, s.h), ptb::KMAJOR,
-        two(static_cast<const u16*>(w_o), s.h, static_cast<const u16*>(w_fc2), s.h, s.hl, 0),
+        T, static_cast<int>(s.K2), h, one(DY, s.h, s.T), ptb::KMAJOR,
+        two(static_cast<const u16*>(w_o), s.h, s.hl, static_cast<const u16*>(w_fc2), s.h, s.f,
+            s.hl, 0),
         ptb::KMAJOR, ptb::EPI_DGELU, e, strm));
   }
-  PTB_STAGE(1, ptb::launch_attention_bwd(qkv, c, lse, dc, delta, dz, static_cast<int>(s.N1),
+  PTB_STAGE(1, ptb::launch_attention_bwd(qkv, qk_lo, c, lse, dc, delta, dz, static_cast<int>(s.N1),
                                     static_cast<int>(s.b), static_cast<int>(s.s),
                                     static_cast<int>(s.n), static_cast<int>(s.d),
                                     static_cast<int>(s.w), strm));
@@ -289,17 +322,17 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
     e.o0 = static_cast<u16*>(dw_o); e.ld0 = h;
     e.o1 = static_cast<u16*>(dw_fc2); e.ld1 = h;
     e.split = static_cast<int>(s.hl);
-    PTB_STAGE(2, ptb::launch_gemm(static_cast<int>(s.K2), h, T, two(c, s.hl, g, s.f, s.hl, 0),
-                             ptb::OUTER_MAJOR, one(DY, s.h), ptb::OUTER_MAJOR,
+    PTB_STAGE(2, ptb::launch_gemm(static_cast<int>(s.K2), h, T, two(c, s.hl, s.T, g, s.f, s.T, s.hl, 0),
+                             ptb::OUTER_MAJOR, one(DY, s.h, s.T), ptb::OUTER_MAJOR,
                              ptb::EPI_STORE2_ROWS, e, strm));
   }
   {  // dgrad through [QKV | FC1]: da = dZ [W_qkv | W_fc1]^T (fp32)
     ptb::Epilogue e{};
     e.of = da; e.ld0 = h;
     PTB_STAGE(3, ptb::launch_gemm(
-        T, h, static_cast<int>(s.N1), one(dz, s.N1), ptb::KMAJOR,
-        two(static_cast<const u16*>(w_qkv), 3 * s.hl, static_cast<const u16*>(w_fc1), s.f,
-            3 * s.hl, 1),
+        T, h, static_cast<int>(s.N1), one(dz, s.N1, s.T), ptb::KMAJOR,
+        two(static_cast<const u16*>(w_qkv), 3 * s.hl, s.h, static_cast<const u16*>(w_fc1), s.f,
+            s.h, 3 * s.hl, 1),
         ptb::KMAJOR, ptb::EPI_F32, e, strm));
   }
   {  // wgrad of [QKV | FC1]: a^T dZ
@@ -307,8 +340,8 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
     e.o0 = static_cast<u16*>(dw_qkv); e.ld0 = static_cast<int>(3 * s.hl);
     e.o1 = static_cast<u16*>(dw_fc1); e.ld1 = static_cast<int>(s.f);
     e.split = static_cast<int>(3 * s.hl);
-    PTB_STAGE(4, ptb::launch_gemm(h, static_cast<int>(s.N1), T, one(a, s.h), ptb::OUTER_MAJOR,
-                             one(dz, s.N1), ptb::OUTER_MAJOR, ptb::EPI_STORE2_COLS, e, strm));
+    PTB_STAGE(4, ptb::launch_gemm(h, static_cast<int>(s.N1), T, one(a, s.h, s.T), ptb::OUTER_MAJOR,
+                             one(dz, s.N1, s.T), ptb::OUTER_MAJOR, ptb::EPI_STORE2_COLS, e, strm));
   }
   PTB_STAGE(5, ptb::launch_layernorm_bwd(da, static_cast<const u16*>(x),
                                     static_cast<const u16*>(ln_gamma), mu, rstd, DY,

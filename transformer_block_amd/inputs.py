@@ -83,9 +83,13 @@ WORKLOAD_ORDER: List[str] = list(WORKLOADS)
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round fp32 values to bf16 (round-to-nearest-even) and return the bits."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    u = a.view(np.uint32)
+    # finite inputs only: the largest finite pattern plus 0x8000 stays < 2^32
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= 16
+    return r.astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:

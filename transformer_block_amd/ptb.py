@@ -27,7 +27,7 @@ PTB_ERR_WINDOW = -5
 PTB_ERR_EPS = -6
 PTB_ERR_HIP = -7
 
-SAVED_SLOTS = ("a", "mu", "rstd", "qkv", "u", "g", "c", "lse")
+SAVED_SLOTS = ("a", "mu", "rstd", "qkv", "u", "g", "c", "lse", "a_lo", "qk_lo")
 
 
 class PtbError(RuntimeError):

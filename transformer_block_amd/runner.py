@@ -99,7 +99,8 @@ class LayerStack:
                   "rstd": ((T,), torch.float32), "qkv": ((T, 3 * hl), torch.bfloat16),
                   "u": ((T, f), torch.bfloat16), "g": ((T, f), torch.bfloat16),
                   "c": ((T, hl), torch.bfloat16),
-                  "lse": ((w.batch, w.heads, w.seq), torch.float32)}
+                  "lse": ((w.batch, w.heads, w.seq), torch.float32),
+                  "a_lo": ((T, h), torch.bfloat16), "qk_lo": ((T, 2 * hl), torch.bfloat16)}
         off = P.ptb_saved_layout(self.dims)[name]
         shape, dt = shapes[name]
         nbytes = int(np.prod(shape)) * (2 if dt == torch.bfloat16 else 4)
