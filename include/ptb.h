@@ -37,9 +37,11 @@
  * Ownership and lifetime.  The caller allocates and owns every buffer,
  * including `saved` (ptb_saved_bytes) and `workspace` (ptb_workspace_bytes).
  * The library allocates nothing and holds no mutable global state, so calls
- * on different streams with different buffers may run concurrently.  `saved`
- * is written by ptb_forward and read by ptb_backward; it must stay untouched
- * in between.  Outputs are overwritten, never accumulated into.
+ * on different streams with different buffers (workspace included) may run
+ * concurrently.  `saved` is written by ptb_forward and read by ptb_backward;
+ * it must stay untouched in between.  `workspace` is scratch for the duration
+ * of one call: its contents need no initialisation and are not kept.
+ * Outputs are overwritten, never accumulated into.
  *
  * Asynchrony.  `stream` is a hipStream_t (NULL = the default stream).  Calls
  * only enqueue kernels on it and never synchronise; a fault inside a kernel
@@ -60,7 +62,7 @@
 extern "C" {
 #endif
 
-#define PTB_ABI_VERSION 1
+#define PTB_ABI_VERSION 2
 
 enum ptb_status {
   PTB_OK = 0,
@@ -99,7 +101,10 @@ int32_t ptb_validate_dims(const ptb_dims* dims);
 /* Bytes of the forward->backward stash of one layer (`saved`). */
 int32_t ptb_saved_bytes(const ptb_dims* dims, size_t* bytes);
 
-/* Bytes of backward scratch (`workspace`). */
+/* Bytes of scratch (`workspace`) that ptb_forward and ptb_backward need:
+ * fp32 partial sums of matrix-product tiles that are split over several
+ * workgroups, their arrival counters, and the backward's intermediate
+ * gradients (dc, dZ, da, the LayerNorm column partials). */
 int32_t ptb_workspace_bytes(const ptb_dims* dims, size_t* bytes);
 
 /* Byte offsets inside `saved` of what ptb_forward stores there, for
@@ -131,13 +136,14 @@ int32_t ptb_saved_layout(const ptb_dims* dims, size_t* offsets);
 
 /* Forward of one layer (MegaScale notes, section 1.1, eq (4)):
  *   y = x + Attn(LN(x)) + MLP(LN(x)).
- * Writes y [T, h] and fills `saved` (ptb_saved_bytes(dims) bytes). */
+ * Writes y [T, h] and fills `saved` (ptb_saved_bytes(dims) bytes);
+ * `workspace` holds ptb_workspace_bytes(dims) bytes of scratch. */
 int32_t ptb_forward(const ptb_dims* dims,
                     const void* x,
                     const void* ln_gamma, const void* ln_beta,
                     const void* w_qkv, const void* w_o,
                     const void* w_fc1, const void* w_fc2,
-                    void* y, void* saved, void* stream);
+                    void* y, void* saved, void* workspace, void* stream);
 
 /* Backward of one layer for upstream gradient dy [T, h], reading the `saved`
  * of the matching ptb_forward and the same x and weights.  Writes dx (which
@@ -163,7 +169,8 @@ int32_t ptb_backward(const ptb_dims* dims,
  *   backward (PTB_BWD_STAGES = 6): 0 dgrad [O ; FC2] + GeLU', 1 attention
  *            backward (3 kernels), 2 wgrad [O ; FC2], 3 dgrad [QKV | FC1],
  *            4 wgrad [QKV | FC1], 5 LayerNorm backward (2 kernels).
- * Each GEMM stage is exactly one kernel launch. */
+ * Each GEMM stage is exactly one kernel launch.  Each call also clears the
+ * tile counters in `workspace` with one small kernel ahead of stage 0. */
 #define PTB_FWD_STAGES 4
 #define PTB_BWD_STAGES 6
 int32_t ptb_forward_timed(const ptb_dims* dims,
@@ -171,7 +178,7 @@ int32_t ptb_forward_timed(const ptb_dims* dims,
                           const void* ln_gamma, const void* ln_beta,
                           const void* w_qkv, const void* w_o,
                           const void* w_fc1, const void* w_fc2,
-                          void* y, void* saved, void* stream,
+                          void* y, void* saved, void* workspace, void* stream,
                           void* const* stage_events);
 int32_t ptb_backward_timed(const ptb_dims* dims,
                            const void* dy, const void* x,

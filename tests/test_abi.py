@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert P.ptb_abi_version() == 1
+    assert P.ptb_abi_version() == 2
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert P.ptb_status_string(code) and P.ptb_status_string(code) != "unknown status"
     assert P.ptb_status_string(12345) == "unknown status"
@@ -91,27 +91,33 @@ def test_saved_layout_is_ordered_aligned_and_sized(lib):
     for a_, b_ in zip(P.SAVED_SLOTS, P.SAVED_SLOTS[1:]):
         assert lay[b_] - lay[a_] >= sizes[a_]
     assert P.ptb_saved_bytes(d) >= lay["qk_lo"] + sizes["qk_lo"]
-    assert P.ptb_workspace_bytes(d) >= T * (3 * hl + f) * 2 + T * h * 4
+    # split-tile partials (2 fp32 256x256 tiles per workgroup, 256 workgroups)
+    # come first, then the backward's dc, dZ and da
+    assert P.ptb_workspace_bytes(d) >= 2 * 256 * 256 * 256 * 4 + T * (3 * hl + f) * 2 + T * h * 4
 
 
 def test_forward_backward_reject_null_and_misaligned_before_any_hip_call(lib):
     d = good_dims()
     A = 0x10000  # never dereferenced: the checks fail first
-    assert P.ptb_forward(d, *([0] * 9), stream=0, check=False) == P.PTB_ERR_NULL
-    args = [A] * 9
+    assert P.ptb_forward(d, *([0] * 10), stream=0, check=False) == P.PTB_ERR_NULL
+    assert P.ptb_forward(d, *([A] * 9), None, stream=0, check=False) == P.PTB_ERR_NULL
+    args = [A] * 10
     args[4] = A + 8
+    assert P.ptb_forward(d, *args, stream=0, check=False) == P.PTB_ERR_ALIGN
+    args = [A] * 10
+    args[9] = A + 4   # workspace
     assert P.ptb_forward(d, *args, stream=0, check=False) == P.PTB_ERR_ALIGN
     assert P.ptb_backward(d, *([A] * 15), None, stream=0, check=False) == P.PTB_ERR_NULL
     bargs = [A] * 16
     bargs[15] = A + 2
     assert P.ptb_backward(d, *bargs, stream=0, check=False) == P.PTB_ERR_ALIGN
     bad = good_dims(head_dim=32)
-    assert P.ptb_forward(bad, *([A] * 9), stream=0, check=False) == P.PTB_ERR_HEAD_DIM
+    assert P.ptb_forward(bad, *([A] * 10), stream=0, check=False) == P.PTB_ERR_HEAD_DIM
     assert P.ptb_backward(good_dims(window=0), *([A] * 16), stream=0,
                           check=False) == P.PTB_ERR_WINDOW
 
 
 def test_error_raises_in_checked_mode(lib):
     with pytest.raises(P.PtbError) as ei:
-        P.ptb_forward(good_dims(batch=0), *([0x10000] * 9), stream=0)
+        P.ptb_forward(good_dims(batch=0), *([0x10000] * 10), stream=0)
     assert ei.value.status == P.PTB_ERR_DIMS

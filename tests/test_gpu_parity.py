@@ -97,7 +97,8 @@ def test_layer_parity_edge_cases(name, w, random_ln):
 
 
 def test_repeat_runs_are_bitwise_identical():
-    """No atomics on the path: a second run reproduces the first bit for bit."""
+    """A second run reproduces the first bit for bit: split GEMM tiles are
+    summed in a fixed order whatever order their parts finish in."""
     w = W("det", 2, 200, 256, 2, 128, 512, 80, seed=30)
     inp = I.make_inputs(w, random_ln=True)
     st = run_gpu(w, inp)

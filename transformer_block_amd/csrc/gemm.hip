@@ -1,5 +1,6 @@
-// bf16 GEMM on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16) with LDS-staged,
-// double-buffered tiles and fused epilogues.
+// bf16 GEMM on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16): persistent
+// stream-K kernel, operands streamed from global memory straight into LDS,
+// fused epilogues.
 //
 // One kernel template covers the six matrix products of the Parallel
 // Transformer Block layer (MegaScale reading notes, section 1.1, eq (4); fused
@@ -13,169 +14,217 @@
 //                           a^T x dZ                            -> dW_qkv, dW_fc1
 // Concatenations are addressed in place (two-segment operands), never copied.
 //
-// Tiling: a 256-thread workgroup (4 waves of 64 lanes, 2 x 2) owns a BM x BN
-// tile of C and walks K in steps of 64.  Both operands are staged in LDS as
-// rows of 64 k-values (128 bytes, XOR-swizzled) so that every MFMA fragment is
-// one 16-byte LDS read.  An operand whose k index is not contiguous in memory
-// (weights in the forward, activations in the weight gradients) is loaded
-// 16 bytes at a time along its contiguous dimension and transposed in
-// registers on the way into LDS.  The next K tile is fetched into registers
-// while the current one feeds the matrix cores.  Tiles are handed out
-// XCD-aware: consecutive workgroups go round-robin over the 8 XCDs, so the
-// tile index is remapped to give each XCD a contiguous, L2-friendly group of
-// tiles.
+// Tiling.  A 256-thread workgroup (4 waves of 64 lanes, 2 x 2, 128 x 128 of C
+// per wave) owns 256 x 256 tiles of C and walks K in steps of 32.  Operand
+// tiles go from global memory to LDS by buffer_load ... lds (16 bytes per lane,
+// no trip through registers) into a ring of 4 stages, three k-steps ahead of
+// the matrix cores.  Operands stored k-contiguous sit in LDS as rows of 32
+// k-values and feed the MFMAs with one ds_read_b128 per fragment; operands
+// stored outer-contiguous sit as [64-column block][32 k][64 columns] and are
+// transposed by the LDS read itself (ds_read_b64_tr_b16).  Both layouts are
+// XOR-swizzled so that the fragment reads are free of bank conflicts.
+//
+// Scheduling.  The grid is persistent: one workgroup per CU, each taking a
+// contiguous range of (tile, k-step) units ("stream-K": Osama et al., 2023,
+// a published work-decomposition method, restated here).  A tile that one
+// range covers whole is finished in place; a tile split over ranges is summed
+// by whichever contributor arrives last (atomic arrival counter per tile, fp32
+// partial tiles in the scratch buffer), so no workgroup ever waits on
+// another.  When whole tiles divide evenly over the CUs the ranges are cut at
+// tile boundaries instead (no split tiles).  Workgroup ids are remapped so
+// that each XCD (each with its own L2) takes a contiguous run of units.
+#include <algorithm>
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
 namespace ptb {
 namespace {
 
-constexpr int BK = 64;
+constexpr int TILE = 256;                  // BM = BN
+constexpr int BK = 32;                     // k per pipeline stage
+constexpr int NSTAGE = 4;
+constexpr int STAGE = 2 * TILE * BK;       // u16 elements: A tile, then B tile (32 KB)
+constexpr int EPI_LD = 36;                 // fp32 row stride of the epilogue staging
+constexpr int GM = 8;                      // tile rows per L2 group
+constexpr int FM = 4, FN = 4;              // 32 x 32 MFMA blocks per wave
+constexpr int PARTIAL_FLOATS = TILE * TILE;
+constexpr int kOutOfRange = static_cast<int>(0x80000000u);  // beyond any operand (< 2^31 bytes)
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 // Buffer resource over one operand segment: reads at or beyond `bytes` return
-// zero, which covers ragged row counts and the k tail without branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const u16* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(p), static_cast<short>(0),
-                                           static_cast<int>(bytes), 0x00020000);
+// zero (ragged row counts and the k tail need no branches).
+__device__ __forceinline__ i32x4 make_desc(const u16* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  i32x4 d;
+  d[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
+  d[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));
+  d[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  d[3] = 0x00020000;
+  return d;
 }
 
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
+// 16 bytes per lane from global memory (descriptor, per-lane byte offset voff
+// plus wave-uniform byte offset soff) straight to LDS at byte address
+// lds_addr + 16 * lane.  Written as inline assembly so that the compiler does
+// not treat it as an LDS store (it would then wait for every outstanding load
+// before any later LDS read); the kernel orders it with explicit vmcnt waits
+// and barriers.  m0 is written here and read only by the load right after it.
+__device__ __forceinline__ void lds_dma16(i32x4 desc, uint32_t lds_addr, int voff, int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  i32x4 d;  // wave-uniform by construction; keep it in scalar registers
+#pragma unroll
+  for (int k = 0; k < 4; ++k) d[k] = __builtin_amdgcn_readfirstlane(desc[k]);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(static_cast<int>(lds_addr))), "v"(voff),
+                 "s"(d), "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory", "m0");
+#endif
 }
 
-// Segment of the k-tile starting at k0 and k0 relative to that segment.
-// Split points are multiples of 64 (= BK), so a k-tile never straddles one.
-__device__ __forceinline__ void k_segment(const Operand& op, int k0, int& seg, int& krel) {
-  seg = (op.split_on_k && k0 >= op.split) ? 1 : 0;
-  krel = seg ? k0 - op.split : k0;
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)(p)));
+#else
+  return 0;
+#endif
 }
 
-template <int R, int MAJ>
-struct TileLoader;
+// s_waitcnt vmcnt(N) lgkmcnt(0): at most N vector-memory operations of this
+// wave outstanding and all of its LDS reads returned (expcnt not waited on).
+// The barriers that follow it rely on both: gfx950 does not wait for
+// outstanding memory operations at s_barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+}
 
-// k contiguous in memory: thread t loads chunk (t & 7) of rows (t >> 3) + 32*i;
-// the 16-byte chunks go straight to LDS.  A wave's rows for one i lie in one
-// aligned block of 32, so the segment (split points are multiples of 32) is
-// uniform across the wave.
-template <int R>
-struct TileLoader<R, KMAJOR> {
-  static constexpr int NCH = R / 32;
-  uint4 v[NCH];
-  int off0[NCH], off1[NCH];  // byte offset of the row start in either segment
-  int oseg[NCH];             // segment of the row when the split is on the outer index
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j supplies the 4
+// u16 at its address; lane i receives element i % 4 of the values supplied by
+// lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4.
+__device__ __forceinline__ v4s lds_read_tr16(const u16* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+#else
+  return v4s{};
+#endif
+}
 
-  __device__ __forceinline__ void init(const Operand& op, int r0, int tid) {
-    const int rr = tid >> 3, c = tid & 7;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int r = r0 + rr + 32 * i;
-      int sg = (!op.split_on_k && r >= op.split) ? 1 : 0;
-      sg = __builtin_amdgcn_readfirstlane(sg);
-      oseg[i] = sg;
-      const int r1 = op.split_on_k ? r : r - op.split;
-      off0[i] = (r * op.ld0 + c * 8) * 2;
-      off1[i] = (r1 * op.ld1 + c * 8) * 2;
-    }
-  }
-  __device__ __forceinline__ void load(const Operand& op, __amdgpu_buffer_rsrc_t rs0,
-                                       __amdgpu_buffer_rsrc_t rs1, int k0) {
-    int kseg, krel;
-    k_segment(op, k0, kseg, krel);
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int sg = op.split_on_k ? kseg : oseg[i];
-      v[i] = sg ? load16(rs1, off1[i] + krel * 2) : load16(rs0, off0[i] + krel * 2);
-    }
-  }
-  __device__ __forceinline__ void store(u16* lds, int tid) const {
-    const int c = tid & 7, rr = tid >> 3;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int r = rr + 32 * i;
-      *reinterpret_cast<uint4*>(lds + r * BK + ((c ^ swz128(r)) << 3)) = v[i];
-    }
-  }
-};
+// k-contiguous stage tile [256 rows][32 k]: 64-byte rows, 16-byte chunk c of
+// row r at chunk slot c ^ kswz(r).
+__device__ __forceinline__ int kswz(int r) { return (r >> 2) & 3; }
+// outer-contiguous stage tile [4][32 k][64 outer]: 128-byte rows, chunk c of
+// k-row kk at slot c ^ oswz(kk).
+__device__ __forceinline__ int oswz(int kk) { return (kk & 2) << 1; }
 
-// Outer index contiguous in memory: each thread loads a KS x 8 block (KS
-// k-rows of 8 consecutive outer indices) and writes it transposed.  Wave w
-// owns outer indices [R/4*w, R/4*(w+1)) of the tile, an aligned block of 64
-// (R = 256) or 32 (R = 128), so its segment is uniform.
-template <int R>
-struct TileLoader<R, OUTER_MAJOR> {
-  static constexpr int KS = R / 32;   // k rows per thread: 8 (R = 256) or 4 (R = 128)
-  static constexpr int GPW = R / 32;  // 8-wide outer groups per wave
-  uint32_t w[KS][4];
-  int base0, base1;  // byte offset of (k = kg*KS, outer group) in either segment
-  int oseg;
+// The DMA of one operand's stage tile: 16 KB = 16 loads of 1 KB, four per
+// wave.  Load i of wave w (inst = 4w + i) fills LDS bytes [1 KB * inst, +1 KB):
+//   k-contiguous:     rows 16*inst .. +15, all 32 k;
+//   outer-contiguous: k-rows 8*(inst%4) .. +7 of outer block inst/4 (64 wide).
+// A wave's four loads cover one aligned block of 64 outer indices, so with
+// split points at multiples of 64 the segment of an outer split is uniform
+// per wave; the segment of a k-split follows k0.
+template <int MAJ>
+struct StageLoader {
+  // Per-lane byte offset of the lane's 16 bytes at k = 0: offA while k is in
+  // segment 0 of a k-split operand, offB in segment 1; for an outer split
+  // both hold the offset in the wave's segment.
+  int offA[4], offB[4];
+  i32x4 dA, dB;  // buffer resources matching offA and offB
+  int ldA, ldB;  // leading dimensions (the k stride of outer-contiguous tiles) likewise
+  // the operand's shape, held in registers: the loads are inline assembly
+  // with a memory clobber, after which fields read from memory would be
+  // loaded again (and every scalar load waits on the LDS counter too)
+  int ld0, ld1, split, split_on_k;
 
-  __device__ __forceinline__ static void coords(int tid, int& rg, int& kg) {
-    const int wv = tid >> 6, l = tid & 63;
-    rg = GPW * wv + (l % GPW);
-    kg = l / GPW;
-  }
-  __device__ __forceinline__ void init(const Operand& op, int r0, int tid) {
-    int rg, kg;
-    coords(tid, rg, kg);
-    const int outer = r0 + rg * 8;
-    int sg = (!op.split_on_k && outer >= op.split) ? 1 : 0;
-    sg = __builtin_amdgcn_readfirstlane(sg);
-    oseg = sg;
-    const int o1 = op.split_on_k ? outer : outer - op.split;
-    base0 = (kg * KS * op.ld0 + outer) * 2;
-    base1 = (kg * KS * op.ld1 + o1) * 2;
-  }
-  __device__ __forceinline__ void load(const Operand& op, __amdgpu_buffer_rsrc_t rs0,
-                                       __amdgpu_buffer_rsrc_t rs1, int k0) {
-    int kseg, krel;
-    k_segment(op, k0, kseg, krel);
-    const int sg = op.split_on_k ? kseg : oseg;
-    const int ld = sg ? op.ld1 : op.ld0;
-    const int base = sg ? base1 : base0;
+  __device__ __forceinline__ void init(const Operand& op, int r0, int wave, int lane) {
+    ld0 = __builtin_amdgcn_readfirstlane(op.ld0);
+    ld1 = __builtin_amdgcn_readfirstlane(op.ld1);
+    split = __builtin_amdgcn_readfirstlane(op.split);
+    split_on_k = __builtin_amdgcn_readfirstlane(op.split_on_k);
+    const int wseg = (!split_on_k && r0 + 64 * wave >= split) ? 1 : 0;
+    const i32x4 d0 = make_desc(op.p0, op.bytes0), d1 = make_desc(op.p1, op.bytes1);
+    dA = (split_on_k || !wseg) ? d0 : d1;
+    dB = (split_on_k || wseg) ? d1 : d0;
+    ldA = (split_on_k || !wseg) ? ld0 : ld1;
+    ldB = (split_on_k || wseg) ? ld1 : ld0;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const uint4 t = load16(sg ? rs1 : rs0, base + (krel + kk) * ld * 2);
-      w[kk][0] = t.x; w[kk][1] = t.y; w[kk][2] = t.z; w[kk][3] = t.w;
-    }
-  }
-  __device__ __forceinline__ void store(u16* lds, int tid) const {
-    int rg, kg;
-    coords(tid, rg, kg);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = rg * 8 + j;
-      uint32_t o[KS / 2];
-#pragma unroll
-      for (int p = 0; p < KS / 2; ++p) {
-        const uint32_t a = w[2 * p][j >> 1], b = w[2 * p + 1][j >> 1];
-        o[p] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-      }
-      if constexpr (KS == 8) {
-        *reinterpret_cast<uint4*>(lds + row * BK + ((kg ^ swz128(row)) << 3)) =
-            make_uint4(o[0], o[1], o[2], o[3]);
+    for (int i = 0; i < 4; ++i) {
+      const int inst = wave * 4 + i;
+      int o0, o1;
+      if constexpr (MAJ == KMAJOR) {
+        const int r = inst * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ kswz(r);
+        const int R = r0 + r;
+        const int R1 = split_on_k ? R : R - split;
+        o0 = (R * ld0 + c * 8) * 2;
+        o1 = (R1 * ld1 + c * 8) * 2;
       } else {
-        *reinterpret_cast<uint2*>(lds + row * BK + (((kg >> 1) ^ swz128(row)) << 3) +
-                                  ((kg & 1) << 2)) = make_uint2(o[0], o[1]);
+        const int blk = inst >> 2;
+        const int kk = (inst & 3) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ oswz(kk);
+        const int col = r0 + blk * 64 + c * 8;
+        const int col1 = split_on_k ? col : col - split;
+        o0 = (kk * ld0 + col) * 2;
+        o1 = (kk * ld1 + col1) * 2;
       }
+      offA[i] = (split_on_k || !wseg) ? o0 : o1;
+      offB[i] = (split_on_k || wseg) ? o1 : o0;
     }
+  }
+
+  // Loads of the stage tile at k0 into LDS bytes [lds, +16 KB).  valid = 0
+  // makes them out of range: they return zeros without touching memory
+  // (buffer bounds) and keep the count of loads in flight fixed.
+  __device__ __forceinline__ void issue(uint32_t lds, int wave, int k0, bool valid) const {
+    const bool kseg = split_on_k && k0 >= split;
+    const int krel = kseg ? k0 - split : k0;
+    const int kld = kseg ? ldB : ldA;
+    const int soff = valid ? ((MAJ == KMAJOR) ? krel * 2 : krel * kld * 2) : kOutOfRange;
+    const i32x4 d = kseg ? dB : dA;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lds_dma16(d, lds + (wave * 4 + i) * 1024, kseg ? offB[i] : offA[i], soff);
   }
 };
 
-__device__ __forceinline__ bf16x8 frag(const u16* lds, int row, int chunk) {
-  return as_bf16x8(
-      *reinterpret_cast<const uint4*>(lds + row * BK + ((chunk ^ swz128(row)) << 3)));
+// MFMA operand fragment for rows (or columns) [rb, rb + 32) and k-step ks
+// (16 k) of a stage tile: lane l gets X[rb + l % 32][16 ks + 8 (l / 32) .. +7].
+template <int MAJ>
+__device__ __forceinline__ bf16x8 frag(const u16* tile, int rb, int ks, int lane) {
+  if constexpr (MAJ == KMAJOR) {
+    const int r = rb + (lane & 31), c = ks * 2 + (lane >> 5);
+    return as_bf16x8(*reinterpret_cast<const uint4*>(tile + r * BK + ((c ^ kswz(r)) << 3)));
+  } else {
+    // Each 16-lane group reads 4 k-rows x 16 outer indices (4 u16 per lane);
+    // the transposing read hands lane i the 4 k-values of its outer index.
+    const int q = lane >> 4, j = lane & 15;
+    const int m = rb + 16 * (q & 1) + 4 * (j & 3);
+    v4s h[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int kk = ks * 16 + 8 * (q >> 1) + 4 * hh + (j >> 2);
+      h[hh] = lds_read_tr16(tile + (m >> 6) * (BK * 64) + kk * 64 +
+                            ((((m >> 3) & 7) ^ oswz(kk)) << 3) + (m & 7));
+    }
+    uint4 u;
+    u.x = static_cast<uint16_t>(h[0][0]) | (static_cast<uint32_t>(static_cast<uint16_t>(h[0][1])) << 16);
+    u.y = static_cast<uint16_t>(h[0][2]) | (static_cast<uint32_t>(static_cast<uint16_t>(h[0][3])) << 16);
+    u.z = static_cast<uint16_t>(h[1][0]) | (static_cast<uint32_t>(static_cast<uint16_t>(h[1][1])) << 16);
+    u.w = static_cast<uint16_t>(h[1][2]) | (static_cast<uint32_t>(static_cast<uint16_t>(h[1][3])) << 16);
+    return as_bf16x8(u);
+  }
 }
 
 // ---- epilogue
-// Each wave stages one 32 x 32 fp32 accumulator block at a time in a private
-// LDS region (row stride 36 floats), then lane l takes row l/2, columns
-// 16*(l%2) .. +15 of the block: the epilogue math sees 16 consecutive columns
-// and writes them with 16- and 32-byte vector stores.
-constexpr int EPI_LD = 36;
-
 __device__ __forceinline__ void store16bf(u16* p, const float* v) {
   uint4 a, b;
   a.x = pack2bf(v[0], v[1]);   a.y = pack2bf(v[2], v[3]);
@@ -273,226 +322,438 @@ __device__ __forceinline__ int epi_region(const Epilogue& e, int r0, int cb) {
 }
 
 // Scheduling groups (instruction classes for __builtin_amdgcn_sched_group_barrier).
-constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200;
+constexpr int SG_MFMA = 0x008, SG_DS_READ = 0x100;
 
-struct GemmBatch {
+// What one launch computes and how it is cut into work items.  An item is a
+// k-range of one output tile; items are handed out in rounds, item i to
+// workgroup i % G, so that the G items of a round run side by side at the
+// same k positions (their operand panels meet in L2).
+//   base items: tile t of problem p in `pieces[p]` k-pieces (pieces > 1
+//     evens out the item lengths of two problems with different K), ordered
+//     problem, then piece, then tile;
+//   the first `full_items` base items (whole rounds) are items as they are;
+//     each remaining base item is cut into `tail_split` k-pieces, so that the
+//     last round still fills the CUs.
+// A tile made of several items is summed by the last of them to finish.
+struct SkPlan {
   GemmProblem p[2];
-  int tiles0;  // tiles of problem 0; the rest of the grid belongs to problem 1
+  int tiles_m[2], tiles_n[2], tiles[2];
+  int iters[2];      // k-steps per tile
+  int pieces[2];     // base k-pieces per tile
+  int base0;         // base items of problem 0 (tiles[0] * pieces[0])
+  int full_items;    // base items taken whole (whole rounds)
+  int tail_split;    // k-pieces per remaining base item
+  int nitems;
+  int full_slots;    // partial slots of whole-round items (0 when none is split)
+  float* partials;   // kGemmPartialSlots slots of PARTIAL_FLOATS
+  int* counters;     // arrival count per global tile: zero on entry, left zero
 };
 
-template <int BM, int BN>
-__host__ __device__ inline int tile_count(const GemmProblem& p) {
-  return ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+struct Item {
+  int prob, tile, gtile, m0, n0, kb, len;
+};
+
+__device__ __forceinline__ Item decode_item(const SkPlan& pl, int i) {
+  int b, tp = 0, ts = 1;
+  if (i < pl.full_items) {
+    b = i;
+  } else {
+    const int j = i - pl.full_items;
+    ts = pl.tail_split;
+    b = pl.full_items + j / ts;
+    tp = j % ts;
+  }
+  Item it;
+  it.prob = b < pl.base0 ? 0 : 1;
+  const int bb = it.prob ? b - pl.base0 : b;
+  const int T = pl.tiles[it.prob];
+  const int q = bb / T, t = bb % T;
+  const int iters = pl.iters[it.prob], pc = pl.pieces[it.prob];
+  const int kq0 = q * iters / pc, kq1 = (q + 1) * iters / pc;
+  const int ln = kq1 - kq0;
+  it.kb = kq0 + tp * ln / ts;
+  it.len = kq0 + (tp + 1) * ln / ts - it.kb;
+  it.tile = t;
+  it.gtile = it.prob ? pl.tiles[0] + t : t;
+  // tile coordinates: groups of GM tile rows, column-major inside a group
+  const int tm_count = pl.tiles_m[it.prob], tn_count = pl.tiles_n[it.prob];
+  const int span = GM * tn_count;
+  const int first_m = (t / span) * GM;
+  const int gsz = min(tm_count - first_m, GM);
+  it.m0 = (first_m + (t % span) % gsz) * TILE;
+  it.n0 = ((t % span) / gsz) * TILE;
+  return it;
 }
 
-template <int BM, int BN, int AMAJ, int BMAJ, int MODE>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmBatch batch) {
-  constexpr int WM = BM / 2, WN = BN / 2;  // per-wave tile
-  constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int STAGE = (BM + BN) * BK;
-  constexpr int NMF = FM * FN;             // MFMAs per k-step per wave
-  constexpr int NFR = FM + FN;             // fragment reads per k-step per wave
-  __shared__ __attribute__((aligned(16))) u16 smem[2 * STAGE];
+// Items that make up tile t of problem p: for each base piece q, the base
+// item itself (whole round) or its tail_split pieces.  f(item) is called in
+// a fixed order.
+template <typename F>
+__device__ __forceinline__ void for_each_part(const SkPlan& pl, int p, int t, F&& f) {
+  const int first = p ? pl.base0 : 0;
+  for (int q = 0; q < pl.pieces[p]; ++q) {
+    const int b = first + q * pl.tiles[p] + t;
+    if (b < pl.full_items) {
+      f(b);
+    } else {
+      const int i0 = pl.full_items + (b - pl.full_items) * pl.tail_split;
+      for (int tp = 0; tp < pl.tail_split; ++tp) f(i0 + tp);
+    }
+  }
+}
+
+__device__ __forceinline__ int part_slot(const SkPlan& pl, int i) {
+  return i < pl.full_items ? i : pl.full_slots + (i - pl.full_items);
+}
+
+template <int AMAJ, int BMAJ, int MODE>
+__global__ __launch_bounds__(256, 1) void gemm_sk_kernel(SkPlan pl) {
+  constexpr int WM = 128, WN = 128;
+  constexpr int RA = (AMAJ == KMAJOR) ? FM : 2 * FM;  // LDS read instructions per k-step
+  constexpr int RB = (BMAJ == KMAJOR) ? FN : 2 * FN;
+  __shared__ __attribute__((aligned(1024))) u16 ring[NSTAGE * STAGE];
+  __shared__ __attribute__((aligned(16))) float epi_stage[4 * 32 * EPI_LD];
+  __shared__ int arrival;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- tile index.  Consecutive workgroups go round-robin over the 8 XCDs
-  // (each with its own L2), and an XCD runs its workgroups in order.  XCD x
-  // gets an equal share of each problem's tiles, each share a contiguous range
-  // (L2 reuse), problem 0 first (its tiles may be longer: longest first).
-  int pid;
-  bool second;
+  // Workgroups go round-robin over the 8 XCDs; virtual id v gives each XCD a
+  // contiguous run of ranges.
+  const int G = gridDim.x;
+  int v;
   {
-    const int nall = gridDim.x, t0 = batch.tiles0;
     const int xcd = blockIdx.x % 8, loc = blockIdx.x / 8;
-    const int base = nall / 8, rem = nall % 8;
-    const int before = xcd * base + min(xcd, rem);     // workgroups on XCDs < xcd
-    const int cnt = base + (xcd < rem ? 1 : 0);         // workgroups on this XCD
-    // problem-0 tiles in proportion to the XCD's workgroups: n0 <= cnt, and
-    // over all XCDs each tile of either problem is taken exactly once
-    const int s0 = static_cast<int>(static_cast<long long>(t0) * before / nall);
-    const int n0 = static_cast<int>(static_cast<long long>(t0) * (before + cnt) / nall) - s0;
-    second = loc >= n0;
-    pid = second ? (before - s0) + (loc - n0) : s0 + loc;
+    const int base = G / 8, rem = G % 8;
+    v = xcd * base + min(xcd, rem) + loc;
   }
-  const GemmProblem& P = second ? batch.p[1] : batch.p[0];
-  const int M = P.M, N = P.N, K = P.K;
-  const Operand& A = P.A;
-  const Operand& B = P.B;
-  const Epilogue& epi = P.epi;
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  constexpr int GM = 8;
-  const int span = GM * tiles_n;
-  const int first_m = (pid / span) * GM;
-  const int gsz = min(tiles_m - first_m, GM);
-  const int tm = first_m + (pid % span) % gsz;
-  const int tn = (pid % span) / gsz;
-  const int m0 = tm * BM, n0 = tn * BN;
+  if (v >= pl.nitems) return;
+  StageLoader<AMAJ> la;
+  StageLoader<BMAJ> lb;
+  int item = v;
+  Item s = decode_item(pl, item);
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_address(ring));
 
-  TileLoader<BM, AMAJ> la;
-  TileLoader<BN, BMAJ> lb;
-  la.init(A, m0, tid);
-  lb.init(B, n0, tid);
-  const __amdgpu_buffer_rsrc_t ra0 = make_rsrc(A.p0, A.bytes0), ra1 = make_rsrc(A.p1, A.bytes1);
-  const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B.p0, B.bytes0), rb1 = make_rsrc(B.p1, B.bytes1);
+  auto setup = [&](const Item& sg) {
+    const GemmProblem& P = pl.p[sg.prob];
+    la.init(P.A, sg.m0, wave, lane);
+    lb.init(P.B, sg.n0, wave, lane);
+  };
+  // stage tile j (k-step kb + j of the segment) into ring slot j % 4
+  // stage tile j of a segment (k-step kb + j) into ring slot st; past the
+  // segment's end the loads are out of range (zeros, no memory traffic)
+  auto issue_to = [&](const Item& sg, int slot, int j) {
+    const bool valid = j < sg.len;
+    const int k0 = (sg.kb + (valid ? j : 0)) * BK;
+    const uint32_t lds = ring_lds + slot * (STAGE * 2);
+    la.issue(lds, wave, k0, valid);
+    lb.issue(lds + TILE * BK * 2, wave, k0, valid);
+  };
+  auto prologue = [&](const Item& sg) {
+    setup(sg);
+#pragma unroll
+    for (int j = 0; j < NSTAGE; ++j) issue_to(sg, j, j);
+  };
 
   f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  const int lrow = lane & 31, lk = lane >> 5;
-  const int arow = wm * WM + lrow, brow = wn * WN + lrow;
   bf16x8 fa[2][FM], fb[2][FN];
-  auto read_frags = [&](const u16* As, int ks, int slot) {
-    const u16* Bs = As + BM * BK;
+  auto rd = [&](const u16* st, int ks, int slot) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) fa[slot][i] = frag(As, arow + i * 32, ks * 2 + lk);
+    for (int i = 0; i < FM; ++i) fa[slot][i] = frag<AMAJ>(st, wm * WM + i * 32, ks, lane);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) fb[slot][j] = frag(Bs, brow + j * 32, ks * 2 + lk);
+    for (int j = 0; j < FN; ++j) fb[slot][j] = frag<BMAJ>(st + TILE * BK, wn * WN + j * 32, ks, lane);
   };
-  auto mfma_step = [&](int slot) {
+  auto mma = [&](int slot) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(fa[slot][i], fb[slot][j], acc[i][j]);
   };
+  // LDS reads of the next k-step spread between this k-step's MFMAs
+  auto pin = [&]() {
+    constexpr int R = RA + RB;
+#pragma unroll
+    for (int i = 0; i < (R < FM * FN ? R : FM * FN); ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    }
+    if constexpr (R < FM * FN) __builtin_amdgcn_sched_group_barrier(SG_MFMA, FM * FN - R, 0);
+    if constexpr (R > FM * FN) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, R - FM * FN, 0);
+  };
 
-  // Prologue: tile 0 into LDS buffer 0, first fragments into registers.
-  const int nk = (K + BK - 1) / BK;
-  la.load(A, ra0, ra1, 0);
-  lb.load(B, rb0, rb1, 0);
-  la.store(smem, tid);
-  lb.store(smem + BM * BK, tid);
-  __syncthreads();
-  read_frags(smem, 0, 0);
-
-  // Main loop.  Iteration kt computes tile kt from LDS buffer kt&1 while tile
-  // kt+1 streams in: global -> registers at the start, registers -> the other
-  // LDS buffer after k-step 2, one barrier before k-step 3, after which the
-  // first fragments of tile kt+1 are read under the MFMAs of k-step 3.
-  // Fragments are double-buffered in registers, so the LDS reads of k-step
-  // s+1 are in flight while the MFMAs of k-step s run.  The prefetch past the
-  // last tile reads zeros (buffer bounds) and is never used.
-  for (int kt = 0; kt < nk; ++kt) {
-    u16* cur = smem + (kt & 1) * STAGE;
-    u16* nxt = smem + ((kt & 1) ^ 1) * STAGE;
-    la.load(A, ra0, ra1, (kt + 1) * BK);
-    lb.load(B, rb0, rb1, (kt + 1) * BK);
-    read_frags(cur, 1, 1);
-    mfma_step(0);
-    read_frags(cur, 2, 0);
-    mfma_step(1);
-    read_frags(cur, 3, 1);
-    mfma_step(0);
-    la.store(nxt, tid);
-    lb.store(nxt + BM * BK, tid);
-    // interleave: global loads and LDS reads between the MFMAs of k-steps 0-2,
-    // the LDS writes of the next tile after them
-#pragma unroll
-    for (int i = 0; i < NMF; ++i) {
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-      if (i < NFR) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < NMF; ++i) {
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-      if (i < NFR) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < NMF; ++i) {
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-      if (i < NFR) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(SG_DS_WRITE, 64, 0);
+  prologue(s);
+  for (;;) {
+    // ---- main loop over the segment's k-steps.  Every step issues the loads
+    // of tile j+4 (out of range past the segment's end), so 8 loads per
+    // stage tile are always in flight behind the one awaited and every wait
+    // is the same: no branch in the loop, and no MFMA under one.  The ring
+    // slot is a runtime offset added to a few per-lane base addresses (slots
+    // 2 and 3 lie beyond the 16-bit immediate of ds_read).
+    const int len = s.len;
+    // Every memory operation of this wave done, the first stage tiles
+    // included (they went out before the previous tile's epilogue).  A clean
+    // slate here also keeps the compiler's own wait counting from carrying
+    // the epilogue's loads and stores into the loop.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    read_frags(nxt, 0, 0);
-    mfma_step(1);
 #pragma unroll
-    for (int i = 0; i < NMF; ++i) {
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 1);
-      if (i < NFR) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 1);
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    rd(ring, 0, 0);
+    for (int j = 0; j < len; ++j) {
+      u16* cur = ring + (j & 3) * STAGE;
+      rd(cur, 1, 1);
+      mma(0);
+      pin();
+      wait_vm_lds<16>();  // tile j+1 landed (tiles j+2, j+3 may be in flight)
+      __syncthreads();    // tile j+1 in LDS for every wave; tile j read by every wave
+      issue_to(s, j & 3, j + 4);
+      rd(ring + ((j + 1) & 3) * STAGE, 0, 0);  // unused after the last step
+      mma(1);
+      pin();
     }
-  }
 
-  // ---- epilogue, one 32 x 32 block at a time through LDS
-  __syncthreads();
-  float* ep = reinterpret_cast<float*>(smem) + wave * 32 * EPI_LD;
-  const int er = lane >> 1, ec = (lane & 1) * 16;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int r0 = m0 + wm * WM + i * 32, cb = n0 + wn * WN + j * 32;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) ep[((q >> 2) * 8 + lk * 4 + (q & 3)) * EPI_LD + lrow] = acc[i][j][q];
-      __builtin_amdgcn_wave_barrier();
-      float v[16];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float4 x = *reinterpret_cast<const float4*>(ep + er * EPI_LD + ec + 4 * t);
-        v[4 * t] = x.x; v[4 * t + 1] = x.y; v[4 * t + 2] = x.z; v[4 * t + 3] = x.w;
-      }
-      __builtin_amdgcn_wave_barrier();
-      const int region = __builtin_amdgcn_readfirstlane(epi_region<MODE>(epi, r0, cb));
-      const int r = r0 + er;
-      if (cb < N && r < M) epi_row16<MODE>(epi, region, r, cb + ec, v);
-      __builtin_amdgcn_sched_barrier(0);
+    // ---- the next item's first stage tiles go out before this one's epilogue
+    const int next = item + G;
+    const bool more = next < pl.nitems;
+    Item nx;
+    if (more) {
+      wait_vm_lds<0>();  // this item's trailing (out-of-range) loads are done
+      __syncthreads();   // and every wave is done reading the ring
+      nx = decode_item(pl, next);
+      prologue(nx);
     }
+
+    // ---- finish the tile, one 32 x 32 block of each wave at a time: the
+    // block goes through the wave's LDS staging area, after which lane l
+    // holds row l / 2, columns 16 (l % 2) .. +15 of it.
+    //   phase 0 (tile made of several items): store this item's fp32
+    //     partial sums, then count it in; the last item to arrive goes on to
+    //     phase 1 with all the partials;
+    //   phase 1: the epilogue, on the sum of the tile's partials (in a fixed
+    //     order, so the result does not depend on the order of arrival).
+    // Partial slot layout: [wave][i][j][32 rows][32 columns] fp32.
+    {
+      const GemmProblem& P = pl.p[s.prob];
+      const Epilogue& e = P.epi;
+      const int lrow = lane & 31, lk = lane >> 5;
+      const int er = lane >> 1, ec = (lane & 1) * 16;
+      float* ep = epi_stage + wave * 32 * EPI_LD;
+      int nparts = 0;
+      for_each_part(pl, s.prob, s.tile, [&](int) { ++nparts; });
+      int phase = nparts > 1 ? 0 : 1;
+      bool summed = false;  // phase 1 on a sum of partials
+      const int my_slot = part_slot(pl, item);
+      for (;;) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+              ep[((q >> 2) * 8 + lk * 4 + (q & 3)) * EPI_LD + lrow] = acc[i][j][q];
+            __builtin_amdgcn_wave_barrier();
+            float vals[16];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const float4 x = *reinterpret_cast<const float4*>(ep + er * EPI_LD + ec + 4 * t);
+              vals[4 * t] = x.x; vals[4 * t + 1] = x.y; vals[4 * t + 2] = x.z; vals[4 * t + 3] = x.w;
+            }
+            __builtin_amdgcn_wave_barrier();
+            const size_t boff = static_cast<size_t>(((wave * FM + i) * FN + j) * 1024 + er * 32 + ec);
+            if (phase == 0) {
+              float4* pw = reinterpret_cast<float4*>(
+                  pl.partials + static_cast<size_t>(my_slot) * PARTIAL_FLOATS + boff);
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                pw[t] = make_float4(vals[4 * t], vals[4 * t + 1], vals[4 * t + 2], vals[4 * t + 3]);
+            } else {
+              if (summed) {
+                bool first = true;
+                for_each_part(pl, s.prob, s.tile, [&](int part) {
+                  const float4* pr = reinterpret_cast<const float4*>(
+                      pl.partials + static_cast<size_t>(part_slot(pl, part)) * PARTIAL_FLOATS + boff);
+#pragma unroll
+                  for (int t = 0; t < 4; ++t) {
+                    const float4 x = pr[t];
+                    if (first) {
+                      vals[4 * t] = x.x; vals[4 * t + 1] = x.y;
+                      vals[4 * t + 2] = x.z; vals[4 * t + 3] = x.w;
+                    } else {
+                      vals[4 * t] += x.x; vals[4 * t + 1] += x.y;
+                      vals[4 * t + 2] += x.z; vals[4 * t + 3] += x.w;
+                    }
+                  }
+                  first = false;
+                });
+              }
+              const int r0 = s.m0 + wm * WM + i * 32, cb = s.n0 + wn * WN + j * 32;
+              const int region = __builtin_amdgcn_readfirstlane(epi_region<MODE>(e, r0, cb));
+              const int r = r0 + er;
+              if (cb < P.N && r < P.M) epi_row16<MODE>(e, region, r, cb + ec, vals);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        if (phase == 1) break;
+        __threadfence();  // this item's partial is visible device-wide ...
+        __syncthreads();
+        if (tid == 0) arrival = atomicAdd(pl.counters + s.gtile, 1);  // ... before it counts
+        __syncthreads();
+        const int arrived = __builtin_amdgcn_readfirstlane(arrival);
+        if (arrived != nparts - 1) break;  // another item finishes this tile
+        __threadfence();                   // every partial of the tile is written
+        if (tid == 0) pl.counters[s.gtile] = 0;  // clean for the next launch
+        phase = 1;
+        summed = true;
+      }
+    }
+    if (!more) break;
+    s = nx;
+    item = next;
   }
 }
 
-template <int BM, int BN, int AMAJ, int BMAJ, int MODE>
-hipError_t launch_tiles(const GemmProblem* probs, int nprob, hipStream_t s) {
-  GemmBatch b;
-  b.p[0] = probs[0];
-  b.p[1] = nprob > 1 ? probs[1] : probs[0];
-  b.tiles0 = tile_count<BM, BN>(probs[0]);
-  const int nt = b.tiles0 + (nprob > 1 ? tile_count<BM, BN>(probs[1]) : 0);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, AMAJ, BMAJ, MODE>), dim3(nt), dim3(256), 0, s, b);
-  return hipGetLastError();
+__global__ __launch_bounds__(256) void zero_i32_kernel(int* p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
+}
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  return n;
+}
+
+int tiles_of(int M, int N) { return ((M + TILE - 1) / TILE) * ((N + TILE - 1) / TILE); }
+
+bool operand_ok(const Operand& op) {
+  auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  // one-segment operands put the split out of reach (INT_MAX)
+  return al(op.p0) && al(op.p1) && op.ld0 % 8 == 0 && op.ld1 % 8 == 0 && op.ld0 > 0 &&
+         op.ld1 > 0 && op.split >= 0 && (op.split % 64 == 0 || op.split >= (1 << 30));
 }
 
 template <int AMAJ, int BMAJ, int MODE>
-hipError_t launch_sized(const GemmProblem* probs, int nprob, hipStream_t s) {
-  long big = 0;
-  for (int i = 0; i < nprob; ++i) big += tile_count<256, 256>(probs[i]);
-  if (big >= 192) return launch_tiles<256, 256, AMAJ, BMAJ, MODE>(probs, nprob, s);
-  return launch_tiles<128, 128, AMAJ, BMAJ, MODE>(probs, nprob, s);
+hipError_t launch_plan(const SkPlan& pl, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_sk_kernel<AMAJ, BMAJ, MODE>), dim3(grid), dim3(256), 0, s, pl);
+  return hipGetLastError();
+}
+
+// Cut the work of one launch into items (see SkPlan).  `tail_split` > 0
+// forces the k-pieces of the last round's base items (tests and tuning);
+// 0 picks enough pieces to fill the CUs, at least 16 k-steps each.
+hipError_t build_plan(const GemmProblem* probs, int nprob, Major a_major, Major b_major,
+                      const GemmScratch& ws, int tail_split, SkPlan* out, int* grid_out) {
+  if (nprob < 1 || nprob > 2) return hipErrorInvalidValue;
+  SkPlan pl;
+  for (int i = 0; i < 2; ++i) {
+    const GemmProblem& p = probs[i < nprob ? i : 0];
+    // the epilogue writes 16 consecutive columns at a time
+    if (p.M <= 0 || p.N <= 0 || p.K <= 0 || p.N % 16 != 0) return hipErrorInvalidValue;
+    // k-contiguous operands are read in whole 32-wide k-steps
+    if ((a_major == KMAJOR || b_major == KMAJOR) && p.K % BK != 0) return hipErrorInvalidValue;
+    if (!operand_ok(p.A) || !operand_ok(p.B)) return hipErrorInvalidValue;
+    pl.p[i] = p;
+    pl.tiles_m[i] = (p.M + TILE - 1) / TILE;
+    pl.tiles_n[i] = (p.N + TILE - 1) / TILE;
+    pl.iters[i] = (p.K + BK - 1) / BK;
+  }
+  const long t0 = static_cast<long>(pl.tiles_m[0]) * pl.tiles_n[0];
+  const long t1 = nprob > 1 ? static_cast<long>(pl.tiles_m[1]) * pl.tiles_n[1] : 0;
+  if (t0 + t1 > ws.max_tiles || t0 + t1 >= (1L << 24)) return hipErrorInvalidValue;
+  pl.tiles[0] = static_cast<int>(t0);
+  pl.tiles[1] = static_cast<int>(t1);
+  pl.partials = ws.partials;
+  pl.counters = ws.counters;
+
+  int G = device_cus();
+  if (G <= 0) return hipErrorInvalidDevice;
+  if (G > kGemmMaxWorkgroups) G = kGemmMaxWorkgroups;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    // equal item lengths for two problems whose K differ by a whole factor
+    pl.pieces[0] = pl.pieces[1] = 1;
+    if (attempt == 0 && t1 > 0) {
+      if (pl.iters[0] > pl.iters[1] && pl.iters[0] % pl.iters[1] == 0)
+        pl.pieces[0] = pl.iters[0] / pl.iters[1];
+      else if (pl.iters[1] > pl.iters[0] && pl.iters[1] % pl.iters[0] == 0)
+        pl.pieces[1] = pl.iters[1] / pl.iters[0];
+    }
+    const long base0 = t0 * pl.pieces[0];
+    const long nbase = base0 + t1 * pl.pieces[1];
+    const long full = (nbase / G) * G;
+    const long rem = nbase - full;
+    int item_len = pl.iters[0] / pl.pieces[0];
+    if (t1 > 0) item_len = min(item_len, pl.iters[1] / pl.pieces[1]);
+    long st = 1;
+    if (rem > 0) {
+      st = tail_split > 0 ? tail_split : G / rem;
+      st = std::min<long>(st, std::max(1, item_len / 16));
+      st = std::min<long>(st, item_len);
+      st = std::max<long>(st, 1);
+    }
+    const long nitems = full + rem * st;
+    const bool base_split = pl.pieces[0] > 1 || pl.pieces[1] > 1;
+    const long slots = base_split ? nitems : (st > 1 ? nitems - full : 0);
+    if (slots > kGemmPartialSlots && attempt == 0) continue;  // retry without base pieces
+    if (slots > kGemmPartialSlots || nitems >= (1L << 30)) return hipErrorInvalidValue;
+    pl.base0 = static_cast<int>(base0);
+    pl.full_items = static_cast<int>(full);
+    pl.tail_split = static_cast<int>(st);
+    pl.nitems = static_cast<int>(nitems);
+    pl.full_slots = base_split ? static_cast<int>(full) : 0;
+    *out = pl;
+    *grid_out = static_cast<int>(std::min<long>(G, nitems));
+    return hipSuccess;
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+int gemm_tiles(int M, int N) { return tiles_of(M, N); }
+
+hipError_t launch_zero_i32(int* p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = min((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_group(const GemmProblem* probs, int nprob, Major a_major,
-                             Major b_major, EpiMode mode, hipStream_t s) {
-  if (nprob < 1 || nprob > 2) return hipErrorInvalidValue;
-  for (int i = 0; i < nprob; ++i)
-    if (probs[i].M <= 0 || probs[i].N <= 0) return hipErrorInvalidValue;
-  // The combinations used by the layer; anything else is a library bug.
+                             Major b_major, EpiMode mode, const GemmScratch& ws,
+                             hipStream_t s) {
+  SkPlan pl;
+  int grid = 0;
+  const hipError_t e = build_plan(probs, nprob, a_major, b_major, ws, 0, &pl, &grid);
+  if (e != hipSuccess) return e;
   if (a_major == KMAJOR && b_major == OUTER_MAJOR) {
-    if (mode == EPI_QKV_GELU) return launch_sized<KMAJOR, OUTER_MAJOR, EPI_QKV_GELU>(probs, nprob, s);
-    if (mode == EPI_RESIDUAL) return launch_sized<KMAJOR, OUTER_MAJOR, EPI_RESIDUAL>(probs, nprob, s);
+    if (mode == EPI_QKV_GELU) return launch_plan<KMAJOR, OUTER_MAJOR, EPI_QKV_GELU>(pl, grid, s);
+    if (mode == EPI_RESIDUAL) return launch_plan<KMAJOR, OUTER_MAJOR, EPI_RESIDUAL>(pl, grid, s);
   } else if (a_major == KMAJOR && b_major == KMAJOR) {
-    if (mode == EPI_DGELU) return launch_sized<KMAJOR, KMAJOR, EPI_DGELU>(probs, nprob, s);
-    if (mode == EPI_F32) return launch_sized<KMAJOR, KMAJOR, EPI_F32>(probs, nprob, s);
+    if (mode == EPI_DGELU) return launch_plan<KMAJOR, KMAJOR, EPI_DGELU>(pl, grid, s);
+    if (mode == EPI_F32) return launch_plan<KMAJOR, KMAJOR, EPI_F32>(pl, grid, s);
   } else if (a_major == OUTER_MAJOR && b_major == OUTER_MAJOR) {
-    if (mode == EPI_STORE2_ROWS) return launch_sized<OUTER_MAJOR, OUTER_MAJOR, EPI_STORE2_ROWS>(probs, nprob, s);
-    if (mode == EPI_STORE2_COLS) return launch_sized<OUTER_MAJOR, OUTER_MAJOR, EPI_STORE2_COLS>(probs, nprob, s);
+    if (mode == EPI_STORE2_ROWS) return launch_plan<OUTER_MAJOR, OUTER_MAJOR, EPI_STORE2_ROWS>(pl, grid, s);
+    if (mode == EPI_STORE2_COLS) return launch_plan<OUTER_MAJOR, OUTER_MAJOR, EPI_STORE2_COLS>(pl, grid, s);
   }
+  // the combinations the layer uses; anything else is a library bug
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(int M, int N, int K, const Operand& A, Major a_major,
                        const Operand& B, Major b_major, EpiMode mode,
-                       const Epilogue& e, hipStream_t s) {
+                       const Epilogue& e, const GemmScratch& ws, hipStream_t s) {
   GemmProblem p;
   p.M = M; p.N = N; p.K = K; p.A = A; p.B = B; p.epi = e;
-  return launch_gemm_group(&p, 1, a_major, b_major, mode, s);
+  return launch_gemm_group(&p, 1, a_major, b_major, mode, ws, s);
 }
 
 }  // namespace ptb

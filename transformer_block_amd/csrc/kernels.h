@@ -66,15 +66,38 @@ struct GemmProblem {
   Epilogue epi;
 };
 
-// C[M,N] = A[M,K] * B[K,N] with the epilogue applied to C.
+// Scratch of the GEMM launches: fp32 partial sums of 256 x 256 tiles that
+// are split along k (kGemmPartialSlots of them at most) and one arrival
+// counter per output tile.  The counters must be zero before a launch; every
+// launch leaves them zero, so launches on one stream can share them.
+constexpr int kGemmMaxWorkgroups = 256;
+constexpr int kGemmPartialSlots = 512;
+constexpr size_t kGemmPartialBytes =
+    static_cast<size_t>(kGemmPartialSlots) * 256 * 256 * sizeof(float);
+struct GemmScratch {
+  float* partials;  // kGemmPartialBytes
+  int* counters;    // max_tiles ints
+  int max_tiles;
+};
+
+// Output tiles of an M x N product (the counters one launch needs).
+int gemm_tiles(int M, int N);
+
+// p[0 .. n) = 0 (clears the counters at the start of a layer call).
+hipError_t launch_zero_i32(int* p, int n, hipStream_t stream);
+
+// C[M,N] = A[M,K] * B[K,N] with the epilogue applied to C.  Operands must be
+// 16-byte aligned with leading dimensions that are multiples of 8; K must be
+// a multiple of 32 when either operand is k-contiguous.
 hipError_t launch_gemm(int M, int N, int K, const Operand& A, Major a_major,
                        const Operand& B, Major b_major, EpiMode mode,
-                       const Epilogue& epi, hipStream_t stream);
+                       const Epilogue& epi, const GemmScratch& scratch, hipStream_t stream);
 
 // Up to two independent products sharing operand orders and epilogue kind,
 // in one launch (the tiles of both fill the GPU together).
 hipError_t launch_gemm_group(const GemmProblem* probs, int nprob, Major a_major,
-                             Major b_major, EpiMode mode, hipStream_t stream);
+                             Major b_major, EpiMode mode, const GemmScratch& scratch,
+                             hipStream_t stream);
 
 // LayerNorm forward over rows of x [T, h]: a = bf16(LN(x)) and its rounding
 // residual a_lo = bf16(LN(x) - a), mu, rstd (fp32).

@@ -207,17 +207,27 @@ __global__ __launch_bounds__(LNB_THREADS) void ln_bwd_kernel(
   }
 }
 
-// Sum the per-workgroup partials column by column (fixed order: deterministic).
+// Sum the per-workgroup partials column by column.  A workgroup owns 64 of
+// the 2h columns; its 4 waves each sum a quarter of the partial rows (lanes
+// on consecutive columns: coalesced), then wave 0 adds the four quarters.
+// The order is fixed, so the result is deterministic.
 __global__ __launch_bounds__(256) void ln_bwd_reduce_kernel(const float* __restrict__ partials,
                                                             int nblk, int h,
                                                             u16* __restrict__ dgamma,
                                                             u16* __restrict__ dbeta) {
-  const int col = blockIdx.x * 256 + threadIdx.x;
-  if (col >= 2 * h) return;
+  __shared__ float part[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + lane;
   float acc = 0.0f;
-  for (int b = 0; b < nblk; ++b) acc += partials[static_cast<size_t>(b) * 2 * h + col];
-  if (col < h) dgamma[col] = f2bf(acc);
-  else dbeta[col - h] = f2bf(acc);
+  if (col < 2 * h)
+    for (int b = wave; b < nblk; b += 4) acc += partials[static_cast<size_t>(b) * 2 * h + col];
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && col < 2 * h) {
+    const float t = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+    if (col < h) dgamma[col] = f2bf(t);
+    else dbeta[col - h] = f2bf(t);
+  }
 }
 
 }  // namespace
@@ -246,7 +256,7 @@ hipError_t launch_layernorm_bwd(const float* da, const u16* x, const u16* gamma,
                        rstd, dy, dx, partials, T, h);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ln_bwd_reduce_kernel, dim3((2 * h + 255) / 256), dim3(256), 0, s, partials,
+  hipLaunchKernelGGL(ln_bwd_reduce_kernel, dim3((2 * h + 63) / 64), dim3(256), 0, s, partials,
                      nblk, h, dgamma, dbeta);
   return hipGetLastError();
 }

@@ -84,13 +84,31 @@ SavedLayout saved_layout(const Shape& s) {
   return L;
 }
 
+// Output tiles of the largest GEMM launch of the layer (one arrival counter
+// each).
+int max_gemm_tiles(const Shape& s) {
+  const int T = static_cast<int>(s.T), h = static_cast<int>(s.h), hl = static_cast<int>(s.hl);
+  const int K2 = static_cast<int>(s.K2), N1 = static_cast<int>(s.N1), f = static_cast<int>(s.f);
+  int m = ptb::gemm_tiles(T, 2 * hl) + ptb::gemm_tiles(T, hl + f);
+  for (int t : {ptb::gemm_tiles(T, h), ptb::gemm_tiles(T, K2), ptb::gemm_tiles(K2, h),
+                ptb::gemm_tiles(h, N1)})
+    m = t > m ? t : m;
+  return m;
+}
+
 struct WorkLayout {
-  size_t dc, dz, da, delta, partials, total;
+  size_t gemm_partials, counters, dc, dz, da, delta, partials, total;
+  int max_tiles;
 };
 
+// Forward scratch is the leading part (GEMM partial tiles and counters);
+// the backward uses all of it.
 WorkLayout work_layout(const Shape& s) {
   WorkLayout W;
   size_t o = 0;
+  W.max_tiles = max_gemm_tiles(s);
+  W.gemm_partials = o; o = align_up(o + ptb::kGemmPartialBytes);
+  W.counters = o; o = align_up(o + static_cast<size_t>(W.max_tiles) * 4);
   W.dc = o; o = align_up(o + s.T * s.hl * 2);
   W.dz = o; o = align_up(o + s.T * s.N1 * 2);
   W.da = o; o = align_up(o + s.T * s.h * 4);
@@ -202,14 +220,17 @@ int32_t ptb_saved_layout(const ptb_dims* dims, size_t* offsets) {
 int32_t ptb_forward_timed(const ptb_dims* dims, const void* x, const void* ln_gamma,
                           const void* ln_beta, const void* w_qkv, const void* w_o,
                           const void* w_fc1, const void* w_fc2, void* y, void* saved,
-                          void* stream, void* const* ev) {
+                          void* workspace, void* stream, void* const* ev) {
   Shape s;
   int32_t st = check_dims(dims, &s);
   if (st != PTB_OK) return st;
-  st = check_ptrs({x, ln_gamma, ln_beta, w_qkv, w_o, w_fc1, w_fc2, y, saved});
+  st = check_ptrs({x, ln_gamma, ln_beta, w_qkv, w_o, w_fc1, w_fc2, y, saved, workspace});
   if (st != PTB_OK) return st;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
   const SavedLayout L = saved_layout(s);
+  const WorkLayout W = work_layout(s);
+  const ptb::GemmScratch gs{at<float>(workspace, W.gemm_partials),
+                            at<int>(workspace, W.counters), W.max_tiles};
   u16* a = at<u16>(saved, L.off[PTB_SAVED_A]);
   float* mu = at<float>(saved, L.off[PTB_SAVED_MU]);
   float* rstd = at<float>(saved, L.off[PTB_SAVED_RSTD]);
@@ -223,6 +244,7 @@ int32_t ptb_forward_timed(const ptb_dims* dims, const void* x, const void* ln_ga
   const u16* X = static_cast<const u16*>(x);
   const u16* Wqkv = static_cast<const u16*>(w_qkv);
 
+  PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
   PTB_STAGE(0, ptb::launch_layernorm_fwd(X, static_cast<const u16*>(ln_gamma),
                                     static_cast<const u16*>(ln_beta), a, a_lo, mu, rstd,
                                     static_cast<int>(s.T), static_cast<int>(s.h), dims->ln_eps,
@@ -251,7 +273,7 @@ int32_t ptb_forward_timed(const ptb_dims* dims, const void* x, const void* ln_ga
     pr[1].epi = e;
     pr[1].epi.col_base = static_cast<int>(2 * s.hl);
     PTB_STAGE(1, ptb::launch_gemm_group(pr, 2, ptb::KMAJOR, ptb::OUTER_MAJOR,
-                                        ptb::EPI_QKV_GELU, strm));
+                                        ptb::EPI_QKV_GELU, gs, strm));
   }
   PTB_STAGE(2, ptb::launch_attention_fwd(qkv, qk_lo, c, lse, static_cast<int>(s.b),
                                     static_cast<int>(s.s), static_cast<int>(s.n),
@@ -264,7 +286,7 @@ int32_t ptb_forward_timed(const ptb_dims* dims, const void* x, const void* ln_ga
         two(c, s.hl, s.T, g, s.f, s.T, s.hl, 1), ptb::KMAJOR,
         two(static_cast<const u16*>(w_o), s.h, s.hl, static_cast<const u16*>(w_fc2), s.h, s.f,
             s.hl, 1),
-        ptb::OUTER_MAJOR, ptb::EPI_RESIDUAL, e, strm));
+        ptb::OUTER_MAJOR, ptb::EPI_RESIDUAL, e, gs, strm));
   }
   return PTB_OK;
 }
@@ -298,8 +320,12 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
   float* da = at<float>(workspace, W.da);
   float* delta = at<float>(workspace, W.delta);
   float* partials = at<float>(workspace, W.partials);
+  const ptb::GemmScratch gs{at<float>(workspace, W.gemm_partials),
+                            at<int>(workspace, W.counters), W.max_tiles};
   const u16* DY = static_cast<const u16*>(dy);
   const int T = static_cast<int>(s.T), h = static_cast<int>(s.h);
+
+  PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
 
   {  // dgrad through [O ; FC2]: dc, and du = dg * GeLU'(u) into dZ's FC1 columns
     ptb::Epilogue e{};
@@ -311,7 +337,7 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
         T, static_cast<int>(s.K2), h, one(DY, s.h, s.T), ptb::KMAJOR,
         two(static_cast<const u16*>(w_o), s.h, s.hl, static_cast<const u16*>(w_fc2), s.h, s.f,
             s.hl, 0),
-        ptb::KMAJOR, ptb::EPI_DGELU, e, strm));
+        ptb::KMAJOR, ptb::EPI_DGELU, e, gs, strm));
   }
   PTB_STAGE(1, ptb::launch_attention_bwd(qkv, qk_lo, c, lse, dc, delta, dz, static_cast<int>(s.N1),
                                     static_cast<int>(s.b), static_cast<int>(s.s),
@@ -324,7 +350,7 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
     e.split = static_cast<int>(s.hl);
     PTB_STAGE(2, ptb::launch_gemm(static_cast<int>(s.K2), h, T, two(c, s.hl, s.T, g, s.f, s.T, s.hl, 0),
                              ptb::OUTER_MAJOR, one(DY, s.h, s.T), ptb::OUTER_MAJOR,
-                             ptb::EPI_STORE2_ROWS, e, strm));
+                             ptb::EPI_STORE2_ROWS, e, gs, strm));
   }
   {  // dgrad through [QKV | FC1]: da = dZ [W_qkv | W_fc1]^T (fp32)
     ptb::Epilogue e{};
@@ -333,7 +359,7 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
         T, h, static_cast<int>(s.N1), one(dz, s.N1, s.T), ptb::KMAJOR,
         two(static_cast<const u16*>(w_qkv), 3 * s.hl, s.h, static_cast<const u16*>(w_fc1), s.f,
             s.h, 3 * s.hl, 1),
-        ptb::KMAJOR, ptb::EPI_F32, e, strm));
+        ptb::KMAJOR, ptb::EPI_F32, e, gs, strm));
   }
   {  // wgrad of [QKV | FC1]: a^T dZ
     ptb::Epilogue e{};
@@ -341,7 +367,8 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
     e.o1 = static_cast<u16*>(dw_fc1); e.ld1 = static_cast<int>(s.f);
     e.split = static_cast<int>(3 * s.hl);
     PTB_STAGE(4, ptb::launch_gemm(h, static_cast<int>(s.N1), T, one(a, s.h, s.T), ptb::OUTER_MAJOR,
-                             one(dz, s.N1, s.T), ptb::OUTER_MAJOR, ptb::EPI_STORE2_COLS, e, strm));
+                             one(dz, s.N1, s.T), ptb::OUTER_MAJOR, ptb::EPI_STORE2_COLS, e, gs,
+                             strm));
   }
   PTB_STAGE(5, ptb::launch_layernorm_bwd(da, static_cast<const u16*>(x),
                                     static_cast<const u16*>(ln_gamma), mu, rstd, DY,
@@ -353,9 +380,9 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
 
 int32_t ptb_forward(const ptb_dims* dims, const void* x, const void* ln_gamma,
                     const void* ln_beta, const void* w_qkv, const void* w_o, const void* w_fc1,
-                    const void* w_fc2, void* y, void* saved, void* stream) {
+                    const void* w_fc2, void* y, void* saved, void* workspace, void* stream) {
   return ptb_forward_timed(dims, x, ln_gamma, ln_beta, w_qkv, w_o, w_fc1, w_fc2, y, saved,
-                           stream, nullptr);
+                           workspace, stream, nullptr);
 }
 
 int32_t ptb_backward(const ptb_dims* dims, const void* dy, const void* x, const void* ln_gamma,

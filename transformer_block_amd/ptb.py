@@ -76,9 +76,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ptb_saved_bytes": (ctypes.c_int32, [_D, ctypes.POINTER(ctypes.c_size_t)]),
         "ptb_workspace_bytes": (ctypes.c_int32, [_D, ctypes.POINTER(ctypes.c_size_t)]),
         "ptb_saved_layout": (ctypes.c_int32, [_D, ctypes.POINTER(ctypes.c_size_t)]),
-        "ptb_forward": (ctypes.c_int32, [_D] + [_P] * 10),
+        "ptb_forward": (ctypes.c_int32, [_D] + [_P] * 11),
         "ptb_backward": (ctypes.c_int32, [_D] + [_P] * 17),
-        "ptb_forward_timed": (ctypes.c_int32, [_D] + [_P] * 11),
+        "ptb_forward_timed": (ctypes.c_int32, [_D] + [_P] * 12),
         "ptb_backward_timed": (ctypes.c_int32, [_D] + [_P] * 18),
     }
     for name, (res, args) in sig.items():
@@ -145,10 +145,10 @@ def ptb_saved_layout(dims: ptb_dims) -> dict:
 
 
 def ptb_forward(dims: ptb_dims, x, ln_gamma, ln_beta, w_qkv, w_o, w_fc1, w_fc2, y,
-                saved, stream=None, check: bool = True) -> int:
+                saved, workspace, stream=None, check: bool = True) -> int:
     st = load_library().ptb_forward(
         ctypes.byref(dims), _ptr(x), _ptr(ln_gamma), _ptr(ln_beta), _ptr(w_qkv), _ptr(w_o),
-        _ptr(w_fc1), _ptr(w_fc2), _ptr(y), _ptr(saved), _stream(stream))
+        _ptr(w_fc1), _ptr(w_fc2), _ptr(y), _ptr(saved), _ptr(workspace), _stream(stream))
     return _done(st, "ptb_forward", check)
 
 
@@ -180,12 +180,12 @@ def _events(stage_events) -> Optional[ctypes.Array]:
 
 
 def ptb_forward_timed(dims: ptb_dims, x, ln_gamma, ln_beta, w_qkv, w_o, w_fc1, w_fc2, y,
-                      saved, stream, stage_events, check: bool = True) -> int:
+                      saved, workspace, stream, stage_events, check: bool = True) -> int:
     """ptb_forward plus raw hipEvent_t handles (2 per stage) recorded around
     each stage on `stream`."""
     st = load_library().ptb_forward_timed(
         ctypes.byref(dims), _ptr(x), _ptr(ln_gamma), _ptr(ln_beta), _ptr(w_qkv), _ptr(w_o),
-        _ptr(w_fc1), _ptr(w_fc2), _ptr(y), _ptr(saved), _stream(stream),
+        _ptr(w_fc1), _ptr(w_fc2), _ptr(y), _ptr(saved), _ptr(workspace), _stream(stream),
         _events(stage_events))
     return _done(st, "ptb_forward_timed", check)
 

@@ -73,7 +73,8 @@ class LayerStack:
         for li, p in enumerate(self.params):
             P.ptb_forward_timed(self.dims, self.layer_input(li), p["ln_gamma"], p["ln_beta"],
                                 p["w_qkv"], p["w_o"], p["w_fc1"], p["w_fc2"], self.ys[li],
-                                self.saved[li], stream, events[li] if events else None)
+                                self.saved[li], self.workspace, stream,
+                                events[li] if events else None)
 
     def backward(self, stream=None, events=None) -> None:
         """events: optional per-layer lists of 2*PTB_BWD_STAGES hipEvent_t handles."""
