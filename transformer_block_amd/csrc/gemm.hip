@@ -321,6 +321,16 @@ __device__ __forceinline__ int epi_region(const Epilogue& e, int r0, int cb) {
   }
 }
 
+// fp32 store and load at device (agent) scope: coherent across the XCDs, whose
+// L2s are not, without writing back or invalidating a whole L2 as a fence
+// would.  Used for the partial sums of split tiles.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Scheduling groups (instruction classes for __builtin_amdgcn_sched_group_barrier).
 constexpr int SG_MFMA = 0x008, SG_DS_READ = 0x100;
 
@@ -535,7 +545,7 @@ __global__ __launch_bounds__(256, 1) void gemm_sk_kernel(SkPlan pl) {
     //     phase 1 with all the partials;
     //   phase 1: the epilogue, on the sum of the tile's partials (in a fixed
     //     order, so the result does not depend on the order of arrival).
-    // Partial slot layout: [wave][i][j][32 rows][32 columns] fp32.
+    // Partial slot layout: [wave][i][j][16 values][64 lanes] fp32.
     {
       const GemmProblem& P = pl.p[s.prob];
       const Epilogue& e = P.epi;
@@ -563,29 +573,23 @@ __global__ __launch_bounds__(256, 1) void gemm_sk_kernel(SkPlan pl) {
               vals[4 * t] = x.x; vals[4 * t + 1] = x.y; vals[4 * t + 2] = x.z; vals[4 * t + 3] = x.w;
             }
             __builtin_amdgcn_wave_barrier();
-            const size_t boff = static_cast<size_t>(((wave * FM + i) * FN + j) * 1024 + er * 32 + ec);
+            // this lane's 16 values of the block, element t at [t][lane]:
+            // each store or load of one t covers 256 contiguous bytes
+            const size_t boff = static_cast<size_t>(((wave * FM + i) * FN + j) * 1024 + lane);
             if (phase == 0) {
-              float4* pw = reinterpret_cast<float4*>(
-                  pl.partials + static_cast<size_t>(my_slot) * PARTIAL_FLOATS + boff);
+              float* pw = pl.partials + static_cast<size_t>(my_slot) * PARTIAL_FLOATS + boff;
 #pragma unroll
-              for (int t = 0; t < 4; ++t)
-                pw[t] = make_float4(vals[4 * t], vals[4 * t + 1], vals[4 * t + 2], vals[4 * t + 3]);
+              for (int t = 0; t < 16; ++t) store_coherent(pw + t * 64, vals[t]);
             } else {
               if (summed) {
                 bool first = true;
                 for_each_part(pl, s.prob, s.tile, [&](int part) {
-                  const float4* pr = reinterpret_cast<const float4*>(
-                      pl.partials + static_cast<size_t>(part_slot(pl, part)) * PARTIAL_FLOATS + boff);
+                  const float* pr =
+                      pl.partials + static_cast<size_t>(part_slot(pl, part)) * PARTIAL_FLOATS + boff;
 #pragma unroll
-                  for (int t = 0; t < 4; ++t) {
-                    const float4 x = pr[t];
-                    if (first) {
-                      vals[4 * t] = x.x; vals[4 * t + 1] = x.y;
-                      vals[4 * t + 2] = x.z; vals[4 * t + 3] = x.w;
-                    } else {
-                      vals[4 * t] += x.x; vals[4 * t + 1] += x.y;
-                      vals[4 * t + 2] += x.z; vals[4 * t + 3] += x.w;
-                    }
+                  for (int t = 0; t < 16; ++t) {
+                    const float x = load_coherent(pr + t * 64);
+                    vals[t] = first ? x : vals[t] + x;
                   }
                   first = false;
                 });
@@ -599,13 +603,16 @@ __global__ __launch_bounds__(256, 1) void gemm_sk_kernel(SkPlan pl) {
           }
         }
         if (phase == 1) break;
-        __threadfence();  // this item's partial is visible device-wide ...
+        // The partial is written at device scope (past the XCD's own L2);
+        // every store of it has completed before the item counts itself in.
+        wait_vm_lds<0>();
         __syncthreads();
-        if (tid == 0) arrival = atomicAdd(pl.counters + s.gtile, 1);  // ... before it counts
+        if (tid == 0) arrival = atomicAdd(pl.counters + s.gtile, 1);
         __syncthreads();
         const int arrived = __builtin_amdgcn_readfirstlane(arrival);
         if (arrived != nparts - 1) break;  // another item finishes this tile
-        __threadfence();                   // every partial of the tile is written
+        // last to arrive: the other partials are complete at device scope and
+        // are read at device scope
         if (tid == 0) pl.counters[s.gtile] = 0;  // clean for the next launch
         phase = 1;
         summed = true;
