@@ -18,6 +18,14 @@ Prints one JSON line.  Besides the throughput it carries:
   cpu_baseline: the fp64 oracle timed on host cores on a bounded sample of the
                 same workload (a reported baseline, not a target);
   stages:       mean device time per kernel stage.
+
+roofline.traffic is the HBM bytes per launch of the dominant kernel as read
+by rocprofv3 counters (FETCH_SIZE, WRITE_SIZE), each scaled by what the same
+counter reads for a plain copy of known size.  It is taken from the committed
+summary profiles/traffic_<stage>_<workload>.md, and only while the kernel
+source it was measured on is unchanged (SHA-256 recorded there); otherwise it
+is null.  --copy-probe-mib N runs that calibration copy (N MiB read, N MiB
+written, outside the timed region) for the counter runs.
 """
 from __future__ import annotations
 
@@ -60,6 +68,51 @@ def stage_work(w):
         "layernorm_bwd": ("bytes", T * h * (4 + 2 + 2 + 2) + T * 8),
     }
     return fwd, bwd
+
+
+STAGE_SOURCE = {"gemm": "gemm.hip", "attention": "attention.hip", "layernorm": "layernorm.hip"}
+
+
+def source_sha256(stage: str) -> str:
+    import hashlib
+    name = STAGE_SOURCE[stage.split("_")[0]]
+    path = os.path.join(ROOT, "transformer_block_amd", "csrc", name)
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def recorded_traffic(stage: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            item = line.strip().lstrip("-* ")
+            if item.startswith(("traffic_bytes_per_launch:", "source_sha256:")):
+                k, v = item.split(":", 1)
+                fields[k] = v.strip(" `")
+    if fields.get("source_sha256") != source_sha256(stage):
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(mib: int) -> None:
+    """A plain elementwise copy of `mib` MiB (fp32), the calibration kernel of
+    the HBM byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 class HipEvents:
@@ -142,6 +195,8 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run a plain copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -163,6 +218,8 @@ def main() -> int:
     w = I.WORKLOADS[args.workload]
     print(f"bench: workload {w.name} steps {args.steps} warmup {args.warmup}",
           file=sys.stderr, flush=True)
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib)
     inp = I.make_inputs(w)
     st = LayerStack(w, inp, "cuda")
     stream = torch.cuda.current_stream()
@@ -208,12 +265,14 @@ def main() -> int:
     if kind == "flops":
         ach = amount / (stages[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": recorded_traffic(dom, w.name),
                 "kernel": dom, "per_launch": amount, "ms_per_launch": round(stages[dom], 4)}
     else:
         ach = amount / (stages[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                "traffic": recorded_traffic(dom, w.name),
                 "kernel": dom, "per_launch": amount, "ms_per_launch": round(stages[dom], 4)}
 
     out = {

@@ -1,6 +1,6 @@
 // bf16 GEMM on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16): persistent
-// stream-K kernel, operands streamed from global memory straight into LDS,
-// fused epilogues.
+// kernel, operands streamed from global memory straight into LDS, fused
+// epilogues.
 //
 // One kernel template covers the six matrix products of the Parallel
 // Transformer Block layer (MegaScale reading notes, section 1.1, eq (4); fused
@@ -24,15 +24,17 @@
 // transposed by the LDS read itself (ds_read_b64_tr_b16).  Both layouts are
 // XOR-swizzled so that the fragment reads are free of bank conflicts.
 //
-// Scheduling.  The grid is persistent: one workgroup per CU, each taking a
-// contiguous range of (tile, k-step) units ("stream-K": Osama et al., 2023,
-// a published work-decomposition method, restated here).  A tile that one
-// range covers whole is finished in place; a tile split over ranges is summed
-// by whichever contributor arrives last (atomic arrival counter per tile, fp32
-// partial tiles in the scratch buffer), so no workgroup ever waits on
-// another.  When whole tiles divide evenly over the CUs the ranges are cut at
-// tile boundaries instead (no split tiles).  Workgroup ids are remapped so
-// that each XCD (each with its own L2) takes a contiguous run of units.
+// Scheduling.  The grid is persistent: one workgroup per CU.  Output tiles
+// are work items handed out in rounds (item i to workgroup i mod G), so the
+// items of a round run side by side at the same k positions and share their
+// operand panels in L2.  When the tiles do not fill the last round, its items
+// are cut along k into pieces that do; a tile made of several pieces is
+// summed, in a fixed order, by whichever piece finishes last (an arrival
+// counter per tile and fp32 partial tiles written at device scope), so no
+// workgroup ever waits on another.  Two grouped products whose K differ by a
+// whole factor are cut into pieces of equal length first.  Workgroup ids are
+// remapped so that each XCD (each with its own L2) takes a contiguous run of
+// items in every round.
 #include <algorithm>
 #include <type_traits>
 
