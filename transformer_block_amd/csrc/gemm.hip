@@ -15,14 +15,15 @@
 // Concatenations are addressed in place (two-segment operands), never copied.
 //
 // Tiling.  A 256-thread workgroup (4 waves of 64 lanes, 2 x 2, 128 x 128 of C
-// per wave) owns 256 x 256 tiles of C and walks K in steps of 32.  Operand
+// per wave) owns 256 x 256 tiles of C and walks K in steps of 64.  Operand
 // tiles go from global memory to LDS by buffer_load ... lds (16 bytes per lane,
-// no trip through registers) into a ring of 4 stages, three k-steps ahead of
-// the matrix cores.  Operands stored k-contiguous sit in LDS as rows of 32
-// k-values and feed the MFMAs with one ds_read_b128 per fragment; operands
-// stored outer-contiguous sit as [64-column block][32 k][64 columns] and are
-// transposed by the LDS read itself (ds_read_b64_tr_b16).  Both layouts are
-// XOR-swizzled so that the fragment reads are free of bank conflicts.
+// no trip through registers, whole 128-byte lines) into two stages of 64 KB,
+// one k-step ahead of the matrix cores.  Operands stored k-contiguous sit in
+// LDS as rows of 64 k-values and feed the MFMAs with one ds_read_b128 per
+// fragment; operands stored outer-contiguous sit as [64-column block][64 k]
+// [64 columns] and are transposed by the LDS read itself (ds_read_b64_tr_b16).
+// Both layouts are XOR-swizzled so that the fragment reads are free of bank
+// conflicts.
 //
 // Scheduling.  The grid is persistent: one workgroup per CU.  Output tiles
 // are work items handed out in rounds (item i to workgroup i mod G), so the
@@ -45,9 +46,9 @@ namespace ptb {
 namespace {
 
 constexpr int TILE = 256;                  // BM = BN
-constexpr int BK = 32;                     // k per pipeline stage
-constexpr int NSTAGE = 4;
-constexpr int STAGE = 2 * TILE * BK;       // u16 elements: A tile, then B tile (32 KB)
+constexpr int BK = 64;                     // k per pipeline stage
+constexpr int NSTAGE = 2;
+constexpr int STAGE = 2 * TILE * BK;       // u16 elements: A tile, then B tile (64 KB)
 constexpr int EPI_LD = 36;                 // fp32 row stride of the epilogue staging
 constexpr int GM = 8;                      // tile rows per L2 group
 constexpr int FM = 4, FN = 4;              // 32 x 32 MFMA blocks per wave
@@ -120,18 +121,19 @@ __device__ __forceinline__ v4s lds_read_tr16(const u16* p) {
 #endif
 }
 
-// k-contiguous stage tile [256 rows][32 k]: 64-byte rows, 16-byte chunk c of
+// k-contiguous stage tile [256 rows][64 k]: 128-byte rows, 16-byte chunk c of
 // row r at chunk slot c ^ kswz(r).
-__device__ __forceinline__ int kswz(int r) { return (r >> 2) & 3; }
-// outer-contiguous stage tile [4][32 k][64 outer]: 128-byte rows, chunk c of
+__device__ __forceinline__ int kswz(int r) { return (r ^ (r >> 3)) & 7; }
+// outer-contiguous stage tile [4][64 k][64 outer]: 128-byte rows, chunk c of
 // k-row kk at slot c ^ oswz(kk).
 __device__ __forceinline__ int oswz(int kk) { return (kk & 2) << 1; }
 
-// The DMA of one operand's stage tile: 16 KB = 16 loads of 1 KB, four per
-// wave.  Load i of wave w (inst = 4w + i) fills LDS bytes [1 KB * inst, +1 KB):
-//   k-contiguous:     rows 16*inst .. +15, all 32 k;
-//   outer-contiguous: k-rows 8*(inst%4) .. +7 of outer block inst/4 (64 wide).
-// A wave's four loads cover one aligned block of 64 outer indices, so with
+// The DMA of one operand's stage tile: 32 KB = 32 loads of 1 KB, eight per
+// wave, each a run of whole 128-byte lines.  Load i of wave w (inst = 8w + i)
+// fills LDS bytes [1 KB * inst, +1 KB):
+//   k-contiguous:     rows 8*inst .. +7, all 64 k;
+//   outer-contiguous: k-rows 8*(inst%8) .. +7 of outer block inst/8 (64 wide).
+// A wave's eight loads cover one aligned block of 64 outer indices, so with
 // split points at multiples of 64 the segment of an outer split is uniform
 // per wave; the segment of a k-split follows k0.
 template <int MAJ>
@@ -139,7 +141,7 @@ struct StageLoader {
   // Per-lane byte offset of the lane's 16 bytes at k = 0: offA while k is in
   // segment 0 of a k-split operand, offB in segment 1; for an outer split
   // both hold the offset in the wave's segment.
-  int offA[4], offB[4];
+  int offA[8], offB[8];
   i32x4 dA, dB;  // buffer resources matching offA and offB
   int ldA, ldB;  // leading dimensions (the k stride of outer-contiguous tiles) likewise
   // the operand's shape, held in registers: the loads are inline assembly
@@ -159,19 +161,19 @@ struct StageLoader {
     ldA = (split_on_k || !wseg) ? ld0 : ld1;
     ldB = (split_on_k || wseg) ? ld1 : ld0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int inst = wave * 4 + i;
+    for (int i = 0; i < 8; ++i) {
+      const int inst = wave * 8 + i;
       int o0, o1;
       if constexpr (MAJ == KMAJOR) {
-        const int r = inst * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ kswz(r);
+        const int r = inst * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ kswz(r);
         const int R = r0 + r;
         const int R1 = split_on_k ? R : R - split;
         o0 = (R * ld0 + c * 8) * 2;
         o1 = (R1 * ld1 + c * 8) * 2;
       } else {
-        const int blk = inst >> 2;
-        const int kk = (inst & 3) * 8 + (lane >> 3);
+        const int blk = inst >> 3;
+        const int kk = (inst & 7) * 8 + (lane >> 3);
         const int c = (lane & 7) ^ oswz(kk);
         const int col = r0 + blk * 64 + c * 8;
         const int col1 = split_on_k ? col : col - split;
@@ -183,7 +185,7 @@ struct StageLoader {
     }
   }
 
-  // Loads of the stage tile at k0 into LDS bytes [lds, +16 KB).  valid = 0
+  // Loads of the stage tile at k0 into LDS bytes [lds, +32 KB).  valid = 0
   // makes them out of range: they return zeros without touching memory
   // (buffer bounds) and keep the count of loads in flight fixed.
   __device__ __forceinline__ void issue(uint32_t lds, int wave, int k0, bool valid) const {
@@ -193,8 +195,8 @@ struct StageLoader {
     const int soff = valid ? ((MAJ == KMAJOR) ? krel * 2 : krel * kld * 2) : kOutOfRange;
     const i32x4 d = kseg ? dB : dA;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      lds_dma16(d, lds + (wave * 4 + i) * 1024, kseg ? offB[i] : offA[i], soff);
+    for (int i = 0; i < 8; ++i)
+      lds_dma16(d, lds + (wave * 8 + i) * 1024, kseg ? offB[i] : offA[i], soff);
   }
 };
 
@@ -495,12 +497,12 @@ __global__ __launch_bounds__(256, 1) void gemm_sk_kernel(SkPlan pl) {
 
   prologue(s);
   for (;;) {
-    // ---- main loop over the segment's k-steps.  Every step issues the loads
-    // of tile j+4 (out of range past the segment's end), so 8 loads per
-    // stage tile are always in flight behind the one awaited and every wait
-    // is the same: no branch in the loop, and no MFMA under one.  The ring
-    // slot is a runtime offset added to a few per-lane base addresses (slots
-    // 2 and 3 lie beyond the 16-bit immediate of ds_read).
+    // ---- main loop over the segment's 64-wide k-steps, two stages: step j
+    // computes stage tile j (4 MFMA k-steps of 16) while tile j+1 streams
+    // in, then waits for it, and after the barrier the loads of tile j+2 go
+    // into the stage just read (out of range past the segment's end, so the
+    // loop has no branch and no MFMA under one).  Fragments of the next
+    // 16-wide k-step are read under the MFMAs of the current one.
     const int len = s.len;
     // Every memory operation of this wave done, the first stage tiles
     // included (they went out before the previous tile's epilogue).  A clean
@@ -516,14 +518,20 @@ __global__ __launch_bounds__(256, 1) void gemm_sk_kernel(SkPlan pl) {
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
     rd(ring, 0, 0);
     for (int j = 0; j < len; ++j) {
-      u16* cur = ring + (j & 3) * STAGE;
+      u16* cur = ring + (j & 1) * STAGE;
       rd(cur, 1, 1);
       mma(0);
       pin();
-      wait_vm_lds<16>();  // tile j+1 landed (tiles j+2, j+3 may be in flight)
-      __syncthreads();    // tile j+1 in LDS for every wave; tile j read by every wave
-      issue_to(s, j & 3, j + 4);
-      rd(ring + ((j + 1) & 3) * STAGE, 0, 0);  // unused after the last step
+      rd(cur, 2, 0);
+      mma(1);
+      pin();
+      rd(cur, 3, 1);
+      mma(0);
+      pin();
+      wait_vm_lds<0>();  // tile j+1 landed
+      __syncthreads();   // tile j+1 in LDS for every wave; tile j read by every wave
+      issue_to(s, j & 1, j + 2);
+      rd(ring + ((j + 1) & 1) * STAGE, 0, 0);  // unused after the last step
       mma(1);
       pin();
     }
@@ -667,7 +675,7 @@ hipError_t build_plan(const GemmProblem* probs, int nprob, Major a_major, Major 
     const GemmProblem& p = probs[i < nprob ? i : 0];
     // the epilogue writes 16 consecutive columns at a time
     if (p.M <= 0 || p.N <= 0 || p.K <= 0 || p.N % 16 != 0) return hipErrorInvalidValue;
-    // k-contiguous operands are read in whole 32-wide k-steps
+    // k-contiguous operands are read in whole 64-wide k-steps
     if ((a_major == KMAJOR || b_major == KMAJOR) && p.K % BK != 0) return hipErrorInvalidValue;
     if (!operand_ok(p.A) || !operand_ok(p.B)) return hipErrorInvalidValue;
     pl.p[i] = p;
