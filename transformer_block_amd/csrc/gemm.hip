@@ -57,6 +57,7 @@ constexpr int kOutOfRange = static_cast<int>(0x80000000u);  // beyond any operan
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // Buffer resource over one operand segment: reads at or beyond `bytes` return
 // zero (ragged row counts and the k tail need no branches).
@@ -122,8 +123,10 @@ __device__ __forceinline__ v4s lds_read_tr16(const u16* p) {
 }
 
 // k-contiguous stage tile [256 rows][64 k]: 128-byte rows, 16-byte chunk c of
-// row r at chunk slot c ^ kswz(r).
-__device__ __forceinline__ int kswz(int r) { return (r ^ (r >> 3)) & 7; }
+// row r at chunk slot c ^ kswz(r).  The 16 rows of one ds_read_b128 pass hit
+// 16 distinct 16-byte bank groups, and the swizzle of a 1 KB load (8 rows)
+// depends on the load only through its parity.
+__device__ __forceinline__ int kswz(int r) { return (r >> 1) & 7; }
 // outer-contiguous stage tile [4][64 k][64 outer]: 128-byte rows, chunk c of
 // k-row kk at slot c ^ oswz(kk).
 __device__ __forceinline__ int oswz(int kk) { return (kk & 2) << 1; }
@@ -197,6 +200,79 @@ struct StageLoader {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       lds_dma16(d, lds + (wave * 8 + i) * 1024, kseg ? offB[i] : offA[i], soff);
+  }
+};
+
+// The same stage tile loaded through registers instead (global -> VGPR ->
+// ds_write_b128): load i of wave w carries the same 1 KB as DMA load 8w + i
+// and is written to the same LDS bytes.  The lane's offset depends only on
+// the lane (and, for k-contiguous tiles, on the parity of i); the rest is
+// wave-uniform and goes in soffset, which the buffer range check includes
+// like the lane offset (zeros past the end, out-of-range loads included).
+template <int MAJ>
+struct RegLoader {
+  int vA[2], vB[2];       // per-lane byte offsets in segment A / B, [load parity]
+  const u16* pA;
+  const u16* pB;
+  int nA, nB, ldA, ldB;   // segment bytes and leading dimensions
+  int rowA, rowB;         // k-contiguous: the wave's first row inside its segment
+  int split, split_on_k;
+
+  __device__ __forceinline__ void init(const Operand& op, int r0, int wave, int lane) {
+    const int ld0 = __builtin_amdgcn_readfirstlane(op.ld0);
+    const int ld1 = __builtin_amdgcn_readfirstlane(op.ld1);
+    split = __builtin_amdgcn_readfirstlane(op.split);
+    split_on_k = __builtin_amdgcn_readfirstlane(op.split_on_k);
+    const int wseg = (!split_on_k && r0 + 64 * wave >= split) ? 1 : 0;
+    const bool a1 = !split_on_k && wseg;       // segment of A
+    const bool b1 = split_on_k || wseg;        // segment of B
+    pA = a1 ? op.p1 : op.p0;
+    pB = b1 ? op.p1 : op.p0;
+    nA = __builtin_amdgcn_readfirstlane((int)(a1 ? op.bytes1 : op.bytes0));
+    nB = __builtin_amdgcn_readfirstlane((int)(b1 ? op.bytes1 : op.bytes0));
+    ldA = a1 ? ld1 : ld0;
+    ldB = b1 ? ld1 : ld0;
+    const int outer_shift = wseg ? split : 0;  // outer index origin of the wave's segment
+    const int lr = lane >> 3;
+    if constexpr (MAJ == KMAJOR) {
+      rowA = r0 + 64 * wave - outer_shift;
+      rowB = r0 + 64 * wave - outer_shift;
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        const int c = (lane & 7) ^ ((par * 4 + (lr >> 1)) & 7);
+        vA[par] = (lr * ldA + c * 8) * 2;
+        vB[par] = (lr * ldB + c * 8) * 2;
+      }
+    } else {
+      rowA = rowB = 0;
+      const int c = (lane & 7) ^ oswz(lr);
+      const int col = r0 + 64 * wave + c * 8 - outer_shift;
+      vA[0] = vA[1] = (lr * ldA + col) * 2;
+      vB[0] = vB[1] = (lr * ldB + col) * 2;
+    }
+  }
+
+  __device__ __forceinline__ void load(int k0, bool valid, v4u* out) const {
+    const bool kseg = split_on_k && k0 >= split;
+    const int krel = kseg ? k0 - split : k0;
+    const int ld = kseg ? ldB : ldA;
+    const int row = kseg ? rowB : rowA;
+    // wave-uniform by construction; keep descriptor and offsets scalar (a
+    // value the compiler thinks divergent would get a per-lane loop)
+    const uint64_t pa = reinterpret_cast<uint64_t>(kseg ? pB : pA);
+    const uint32_t plo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa));
+    const uint32_t phi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa >> 32));
+    const u16* p = reinterpret_cast<const u16*>((static_cast<uint64_t>(phi) << 32) | plo);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u16*>(p), (short)0, __builtin_amdgcn_readfirstlane(kseg ? nB : nA), 0x00020000);
+    const int v0 = kseg ? vB[0] : vA[0], v1 = kseg ? vB[1] : vA[1];
+    int soff = (MAJ == KMAJOR) ? (row * ld + krel) * 2 : krel * ld * 2;
+    int step = 16 * ld;  // 8 rows (or 8 k-rows) further per load
+    if (!valid) { soff = kOutOfRange; step = 0; }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      out[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (i & 1) ? v1 : v0,
+                                                     __builtin_amdgcn_readfirstlane(soff + i * step), 0);
   }
 };
 
@@ -336,7 +412,7 @@ __device__ __forceinline__ float load_coherent(const float* p) {
 }
 
 // Scheduling groups (instruction classes for __builtin_amdgcn_sched_group_barrier).
-constexpr int SG_MFMA = 0x008, SG_DS_READ = 0x100;
+constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
 
 // What one launch computes and how it is cut into work items.  An item is a
 // k-range of one output tile; items are handed out in rounds, item i to
@@ -442,7 +518,12 @@ __global__ __launch_bounds__(256, 1) void gemm_sk_kernel(SkPlan pl) {
     v = xcd * base + min(xcd, rem) + loc;
   }
   if (v >= pl.nitems) return;
-  StageLoader<AMAJ> la;
+  // Both operands k-contiguous (the two dgrad products): A goes through
+  // registers and B by LDS DMA, which splits the operand stream over both
+  // paths; otherwise both go by DMA (measured per product: see the notes on
+  // the main loop).
+  constexpr bool AREG = (AMAJ == KMAJOR && BMAJ == KMAJOR);
+  std::conditional_t<AREG, RegLoader<AMAJ>, StageLoader<AMAJ>> la;
   StageLoader<BMAJ> lb;
   int item = v;
   Item s = decode_item(pl, item);
@@ -460,13 +541,31 @@ __global__ __launch_bounds__(256, 1) void gemm_sk_kernel(SkPlan pl) {
     const bool valid = j < sg.len;
     const int k0 = (sg.kb + (valid ? j : 0)) * BK;
     const uint32_t lds = ring_lds + slot * (STAGE * 2);
-    la.issue(lds, wave, k0, valid);
+    if constexpr (!AREG) la.issue(lds, wave, k0, valid);
     lb.issue(lds + TILE * BK * 2, wave, k0, valid);
+  };
+  // A through registers (AREG): load stage tile j of A, then write it to LDS
+  v4u stg[AREG ? 8 : 1];
+  auto gload_a = [&](const Item& sg, int j) {
+    if constexpr (AREG) {
+      const bool valid = j < sg.len;
+      const int k0 = (sg.kb + (valid ? j : 0)) * BK;
+      la.load(k0, valid, stg);
+    }
+  };
+  auto commit_a = [&](int slot) {
+    if constexpr (AREG) {
+      u16* st = ring + slot * STAGE + wave * 4096 + lane * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<v4u*>(st + i * 512) = stg[i];
+    }
   };
   auto prologue = [&](const Item& sg) {
     setup(sg);
 #pragma unroll
     for (int j = 0; j < NSTAGE; ++j) issue_to(sg, j, j);
+    gload_a(sg, 0);
+    commit_a(0);
   };
 
   f32x16 acc[FM][FN];
@@ -517,23 +616,54 @@ __global__ __launch_bounds__(256, 1) void gemm_sk_kernel(SkPlan pl) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
     rd(ring, 0, 0);
-    for (int j = 0; j < len; ++j) {
-      u16* cur = ring + (j & 1) * STAGE;
-      rd(cur, 1, 1);
-      mma(0);
-      pin();
-      rd(cur, 2, 0);
-      mma(1);
-      pin();
-      rd(cur, 3, 1);
-      mma(0);
-      pin();
-      wait_vm_lds<0>();  // tile j+1 landed
-      __syncthreads();   // tile j+1 in LDS for every wave; tile j read by every wave
-      issue_to(s, j & 1, j + 2);
-      rd(ring + ((j + 1) & 1) * STAGE, 0, 0);  // unused after the last step
-      mma(1);
-      pin();
+    if constexpr (AREG) {
+      // A's tile j+1 is loaded into registers at the start of step j (its
+      // loads spread between the first k-step's MFMAs) and written to the
+      // free stage at the end; B's tile j+2 goes by DMA after the barrier.
+      for (int j = 0; j < len; ++j) {
+        u16* cur = ring + (j & 1) * STAGE;
+        gload_a(s, j + 1);
+        rd(cur, 1, 1);
+        mma(0);
+#pragma unroll
+        for (int i = 0; i < FM * FN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+        }
+        rd(cur, 2, 0);
+        mma(1);
+        pin();
+        rd(cur, 3, 1);
+        mma(0);
+        pin();
+        commit_a((j + 1) & 1);
+        wait_vm_lds<0>();  // B's tile j+1 landed, A's written
+        __syncthreads();   // tile j+1 in LDS for every wave; tile j read by every wave
+        issue_to(s, j & 1, j + 2);
+        rd(ring + ((j + 1) & 1) * STAGE, 0, 0);  // unused after the last step
+        mma(1);
+        pin();
+      }
+    } else {
+      for (int j = 0; j < len; ++j) {
+        u16* cur = ring + (j & 1) * STAGE;
+        rd(cur, 1, 1);
+        mma(0);
+        pin();
+        rd(cur, 2, 0);
+        mma(1);
+        pin();
+        rd(cur, 3, 1);
+        mma(0);
+        pin();
+        wait_vm_lds<0>();  // tile j+1 landed
+        __syncthreads();   // tile j+1 in LDS for every wave; tile j read by every wave
+        issue_to(s, j & 1, j + 2);
+        rd(ring + ((j + 1) & 1) * STAGE, 0, 0);  // unused after the last step
+        mma(1);
+        pin();
+      }
     }
 
     // ---- the next item's first stage tiles go out before this one's epilogue
@@ -544,7 +674,9 @@ __global__ __launch_bounds__(256, 1) void gemm_sk_kernel(SkPlan pl) {
       wait_vm_lds<0>();  // this item's trailing (out-of-range) loads are done
       __syncthreads();   // and every wave is done reading the ring
       nx = decode_item(pl, next);
-      prologue(nx);
+      // with A through registers the staging registers would stay live
+      // across the epilogue; that prologue runs after it instead
+      if constexpr (!AREG) prologue(nx);
     }
 
     // ---- finish the tile, one 32 x 32 block of each wave at a time: the
@@ -629,6 +761,7 @@ __global__ __launch_bounds__(256, 1) void gemm_sk_kernel(SkPlan pl) {
       }
     }
     if (!more) break;
+    if constexpr (AREG) prologue(nx);
     s = nx;
     item = next;
   }
