@@ -123,21 +123,103 @@ struct Tile64 {
   }
 };
 
+
+// ------------------------------------------------------- row splitting
+// A "row" is one 128-wide block of queries (forward, dQ) or keys (dK/dV);
+// it walks tiles of 64 along the other axis.  Under a causal mask the rows
+// carry very different amounts of work, so long rows are cut into chunks of
+// at most `ch` tiles, one workgroup each; the chunks of a row are combined by
+// the last of them to finish (fp32 partials at device scope, an arrival
+// counter per row).  Rows are taken longest first.
+struct RowSpan {
+  int begin, end;  // [begin, end) along the tiled axis
+};
+__host__ __device__ inline RowSpan query_row(int qt, int s, int window) {
+  const int q0 = qt * BQ;
+  RowSpan r;
+  r.begin = (q0 - window + 1 > 0 ? q0 - window + 1 : 0) & ~(BKV - 1);
+  r.end = q0 + BQ < s ? q0 + BQ : s;
+  return r;
+}
+__host__ __device__ inline RowSpan key_row(int kt, int s, int window) {
+  const int k0 = kt * BKB;
+  RowSpan r;
+  r.begin = k0 & ~(BQB - 1);
+  const long e = static_cast<long>(k0) + BKB - 1 + window;
+  r.end = e < s ? static_cast<int>(e) : s;
+  return r;
+}
+__host__ __device__ inline int row_tiles(RowSpan r) { return (r.end - r.begin + 63) / 64; }
+__host__ __device__ inline int row_chunks(RowSpan r, int ch) {
+  const int nt = row_tiles(r);
+  return nt <= 0 ? 1 : (nt + ch - 1) / ch;
+}
+
+// The work item of workgroup x within one (batch, head): its row, chunk,
+// span, the row's chunk count, and (for split rows) its partial slot.
+struct RowItem {
+  int row, chunk, nchunks, slot;
+  RowSpan span;
+};
+template <bool QUERY_ROWS>
+__device__ __forceinline__ RowItem decode_row_item(int x, int nrows, int s, int window, int ch) {
+  RowItem it{};
+  int slot = 0;
+  for (int i = 0; i < nrows; ++i) {
+    const int row = QUERY_ROWS ? nrows - 1 - i : i;  // longest rows first
+    const RowSpan sp = QUERY_ROWS ? query_row(row, s, window) : key_row(row, s, window);
+    const int nch = row_chunks(sp, ch);
+    if (x < nch) {
+      it.row = row;
+      it.chunk = x;
+      it.nchunks = nch;
+      it.slot = slot + x;
+      it.span.begin = sp.begin + x * ch * 64;
+      const int e = sp.begin + (x + 1) * ch * 64;
+      it.span.end = e < sp.end ? e : sp.end;
+      return it;
+    }
+    x -= nch;
+    if (nch > 1) slot += nch;
+  }
+  it.nchunks = 0;  // past the last item (not launched)
+  return it;
+}
+
+// fp32 store and load at device (agent) scope: coherent across the XCDs
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Scratch of the split rows of one launch.
+struct RowSplit {
+  float* partials;  // slot-major; `per_slot` floats each
+  int* counters;    // one per (batch, head, row): zero on entry, left zero
+  int ch;           // tiles per chunk
+  int split_slots;  // partial slots per (batch, head)
+};
+
 // ------------------------------------------------------------------ forward
 template <int D>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ qkv,
                                                        const u16* __restrict__ qk_lo,
                                                        u16* __restrict__ cout,
                                                        float* __restrict__ lse, int s, int n,
-                                                       int window, int nqt) {
+                                                       int window, int nqt, RowSplit rs) {
   constexpr int NKS = D / 16, ND = D / 32;
   __shared__ __attribute__((aligned(16))) u16 k_lds[BKV * D];
+  __shared__ int arrival;
   __shared__ __attribute__((aligned(16))) u16 kl_lds[BKV * D];
   __shared__ __attribute__((aligned(16))) u16 vt_lds[D * BKV];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int qt = nqt - 1 - static_cast<int>(blockIdx.x);  // longest rows first
+  const RowItem item = decode_row_item<true>(static_cast<int>(blockIdx.x), nqt, s, window, rs.ch);
+  if (item.nchunks == 0) return;
+  const int qt = item.row;
   const int hd = blockIdx.y, bi = blockIdx.z;
   const int hl = n * D, ld = 3 * hl;
   const u16* Qg = qkv + static_cast<size_t>(bi) * s * ld + hd * D;
@@ -167,18 +249,27 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ q
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[db][e] = 0.0f;
 
-  const int kv_begin = max(0, q0 - window + 1) & ~(BKV - 1);
-  const int kv_end = min(s, q0 + BQ);
+  const int kv_begin = item.span.begin;
+  const int kv_end = item.span.end;
+  // The next key tile is loaded into registers while the current one is
+  // computed from LDS; the registers are free again once stored.
   Tile64<D> kt, ktl, vt;
+  if (kv_begin < kv_end) {
+    kt.load(Kg, ld, kv_begin, s, tid);
+    ktl.load(Klg, 2 * hl, kv_begin, s, tid);
+    vt.load(Vg, ld, kv_begin, s, tid);
+  }
   for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKV) {
-    kt.load(Kg, ld, kt0, s, tid);
-    ktl.load(Klg, 2 * hl, kt0, s, tid);
-    vt.load(Vg, ld, kt0, s, tid);
-    __syncthreads();
+    __syncthreads();  // every wave is done with the previous tile in LDS
     kt.store_rows(k_lds, tid);
     ktl.store_rows(kl_lds, tid);
     vt.store_transposed(vt_lds, tid);
     __syncthreads();
+    if (kt0 + BKV < kv_end) {
+      kt.load(Kg, ld, kt0 + BKV, s, tid);
+      ktl.load(Klg, 2 * hl, kt0 + BKV, s, tid);
+      vt.load(Vg, ld, kt0 + BKV, s, tid);
+    }
 
     const bool any = qw0 < s && qw0 + 31 >= kt0 && qw0 - (kt0 + BKV - 1) < window;
     if (!any) continue;
@@ -241,6 +332,49 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ q
       }
   }
 
+  if (item.nchunks > 1) {
+    // A chunk of a split row: store o, m and l (device scope), count in; the
+    // last chunk to arrive merges all of them, in chunk order.
+    constexpr int PER_SLOT = BQ * D + 2 * 256;
+    const size_t row_id = (static_cast<size_t>(bi) * n + hd) * nqt + qt;
+    const size_t slot0 = (static_cast<size_t>(bi) * n + hd) * rs.split_slots;
+    const int first_slot = item.slot - item.chunk;
+    {
+      float* pp = rs.partials + (slot0 + item.slot) * PER_SLOT;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) st_dev(pp + ((wave * ND + db) * 16 + e) * 64 + lane, o[db][e]);
+      st_dev(pp + BQ * D + tid, m);
+      st_dev(pp + BQ * D + 256 + tid, l);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) arrival = atomicAdd(rs.counters + row_id, 1);
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(arrival) != item.nchunks - 1) return;
+    if (tid == 0) rs.counters[row_id] = 0;
+    float mm = -INFINITY;
+    for (int c = 0; c < item.nchunks; ++c)
+      mm = fmaxf(mm, ld_dev(rs.partials + (slot0 + first_slot + c) * PER_SLOT + BQ * D + tid));
+    const float ms = (mm == -INFINITY) ? 0.0f : mm;
+    l = 0.0f;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[db][e] = 0.0f;
+    for (int c = 0; c < item.nchunks; ++c) {
+      const float* pp = rs.partials + (slot0 + first_slot + c) * PER_SLOT;
+      const float f = exp2f(ld_dev(pp + BQ * D + tid) - ms);
+      l += f * ld_dev(pp + BQ * D + 256 + tid);
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] += f * ld_dev(pp + ((wave * ND + db) * 16 + e) * 64 + lane);
+    }
+    m = mm;
+  }
+
   const float lt = l + __shfl_xor(l, 32);
   if (qi < s) {
     const float inv = 1.0f / lt;
@@ -292,8 +426,9 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const u16* __restrict__ qkv, const u16* __restrict__ qk_lo, const u16* __restrict__ dcg,
     const float* __restrict__ lse, const float* __restrict__ delta, u16* __restrict__ dz,
-    int ld_dz, int s, int n, int window) {
+    int ld_dz, int s, int n, int window, int nkt, RowSplit rsp) {
   constexpr int NKS = D / 16, ND = D / 32;
+  __shared__ int arrival;
   __shared__ __attribute__((aligned(16))) u16 q_lds[BQB * D];
   __shared__ __attribute__((aligned(16))) u16 ql_lds[BQB * D];
   __shared__ __attribute__((aligned(16))) u16 qt_lds[D * BQB];
@@ -314,7 +449,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const u16* Klg = Qlg + hl;
   const float* lse_h = lse + (static_cast<size_t>(bi) * n + hd) * s;
   const float* dl_h = delta + (static_cast<size_t>(bi) * n + hd) * s;
-  const int kb0 = blockIdx.x * BKB, kw0 = kb0 + wave * 32, kj = kw0 + l32;
+  const RowItem item = decode_row_item<false>(static_cast<int>(blockIdx.x), nkt, s, window, rsp.ch);
+  if (item.nchunks == 0) return;
+  const int kb0 = item.row * BKB, kw0 = kb0 + wave * 32, kj = kw0 + l32;
 
   bf16x8 kf[NKS], kl[NKS], vf[NKS];
 #pragma unroll
@@ -336,14 +473,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) { dv[db][e] = 0.0f; dk[db][e] = 0.0f; }
 
-  const int q_begin = kb0 & ~(BQB - 1);
-  const int q_end = min(s, kb0 + BKB - 1 + window);
+  const int q_begin = item.span.begin;
+  const int q_end = item.span.end;
+  // The next query tile is loaded into registers while the current one is
+  // computed from LDS.
   Tile64<D> qtile, qltile, otile;
+  if (q_begin < q_end) {
+    qtile.load(Qg, ld, q_begin, s, tid);
+    qltile.load(Qlg, 2 * hl, q_begin, s, tid);
+    otile.load(dOg, hl, q_begin, s, tid);
+  }
   for (int qt0 = q_begin; qt0 < q_end; qt0 += BQB) {
-    qtile.load(Qg, ld, qt0, s, tid);
-    qltile.load(Qlg, 2 * hl, qt0, s, tid);
-    otile.load(dOg, hl, qt0, s, tid);
-    __syncthreads();
+    __syncthreads();  // every wave is done with the previous tile in LDS
     qtile.store_rows(q_lds, tid);
     qltile.store_rows(ql_lds, tid);
     qtile.store_transposed(qt_lds, tid);
@@ -355,6 +496,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
       dl_lds[tid] = q < s ? dl_h[q] : 0.0f;
     }
     __syncthreads();
+    if (qt0 + BQB < q_end) {
+      qtile.load(Qg, ld, qt0 + BQB, s, tid);
+      qltile.load(Qlg, 2 * hl, qt0 + BQB, s, tid);
+      otile.load(dOg, hl, qt0 + BQB, s, tid);
+    }
 
     const bool any = kw0 < s && qt0 + BQB - 1 >= kw0 && qt0 - (kw0 + 31) < window;
     if (!any) continue;
@@ -398,6 +544,43 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     }
   }
 
+  if (item.nchunks > 1) {
+    // A chunk of a split key row: store dk, dv (device scope), count in; the
+    // last chunk to arrive sums all of them, in chunk order.
+    constexpr int PER_SLOT = 2 * BKB * D;
+    const size_t row_id = (static_cast<size_t>(bi) * n + hd) * nkt + item.row;
+    const size_t slot0 = (static_cast<size_t>(bi) * n + hd) * rsp.split_slots;
+    const int first_slot = item.slot - item.chunk;
+    {
+      float* pp = rsp.partials + (slot0 + item.slot) * PER_SLOT;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          st_dev(pp + ((wave * ND + db) * 16 + e) * 64 + lane, dk[db][e]);
+          st_dev(pp + BKB * D + ((wave * ND + db) * 16 + e) * 64 + lane, dv[db][e]);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) arrival = atomicAdd(rsp.counters + row_id, 1);
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(arrival) != item.nchunks - 1) return;
+    if (tid == 0) rsp.counters[row_id] = 0;
+    for (int c = 0; c < item.nchunks; ++c) {
+      const float* pp = rsp.partials + (slot0 + first_slot + c) * PER_SLOT;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float a = ld_dev(pp + ((wave * ND + db) * 16 + e) * 64 + lane);
+          const float v = ld_dev(pp + BKB * D + ((wave * ND + db) * 16 + e) * 64 + lane);
+          dk[db][e] = c == 0 ? a : dk[db][e] + a;
+          dv[db][e] = c == 0 ? v : dv[db][e] + v;
+        }
+    }
+  }
+
   if (kj < s) {
     const float rs = 1.0f / sqrtf(static_cast<float>(D));
     u16* row = dz + (static_cast<size_t>(bi) * s + kj) * ld_dz + hd * D;
@@ -421,8 +604,9 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const u16* __restrict__ qkv, const u16* __restrict__ qk_lo, const u16* __restrict__ dcg,
     const float* __restrict__ lse, const float* __restrict__ delta, u16* __restrict__ dz,
-    int ld_dz, int s, int n, int window, int nqt) {
+    int ld_dz, int s, int n, int window, int nqt, RowSplit rsp) {
   constexpr int NKS = D / 16, ND = D / 32;
+  __shared__ int arrival;
   __shared__ __attribute__((aligned(16))) u16 k_lds[BKV * D];
   __shared__ __attribute__((aligned(16))) u16 kl_lds[BKV * D];
   __shared__ __attribute__((aligned(16))) u16 kt_lds[D * BKV];
@@ -430,7 +614,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int qt = nqt - 1 - static_cast<int>(blockIdx.x);
+  const RowItem item = decode_row_item<true>(static_cast<int>(blockIdx.x), nqt, s, window, rsp.ch);
+  if (item.nchunks == 0) return;
+  const int qt = item.row;
   const int hd = blockIdx.y, bi = blockIdx.z;
   const int hl = n * D, ld = 3 * hl;
   const u16* Qg = qkv + static_cast<size_t>(bi) * s * ld + hd * D;
@@ -465,19 +651,28 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) dq[db][e] = 0.0f;
 
-  const int kv_begin = max(0, q0 - window + 1) & ~(BKV - 1);
-  const int kv_end = min(s, q0 + BQ);
+  const int kv_begin = item.span.begin;
+  const int kv_end = item.span.end;
+  // The next key tile is loaded into registers while the current one is
+  // computed from LDS.
   Tile64<D> ktile, kltile, vtile;
+  if (kv_begin < kv_end) {
+    ktile.load(Kg, ld, kv_begin, s, tid);
+    kltile.load(Klg, 2 * hl, kv_begin, s, tid);
+    vtile.load(Vg, ld, kv_begin, s, tid);
+  }
   for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKV) {
-    ktile.load(Kg, ld, kt0, s, tid);
-    kltile.load(Klg, 2 * hl, kt0, s, tid);
-    vtile.load(Vg, ld, kt0, s, tid);
-    __syncthreads();
+    __syncthreads();  // every wave is done with the previous tile in LDS
     ktile.store_rows(k_lds, tid);
     kltile.store_rows(kl_lds, tid);
     ktile.store_transposed(kt_lds, tid);
     vtile.store_rows(v_lds, tid);
     __syncthreads();
+    if (kt0 + BKV < kv_end) {
+      ktile.load(Kg, ld, kt0 + BKV, s, tid);
+      kltile.load(Klg, 2 * hl, kt0 + BKV, s, tid);
+      vtile.load(Vg, ld, kt0 + BKV, s, tid);
+    }
 
     const bool any = qw0 < s && qw0 + 31 >= kt0 && qw0 - (kt0 + BKV - 1) < window;
     if (!any) continue;
@@ -520,6 +715,38 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
       }
   }
 
+  if (item.nchunks > 1) {
+    // A chunk of a split query row: store dq (device scope), count in; the
+    // last chunk to arrive sums all of them, in chunk order.
+    constexpr int PER_SLOT = BQ * D;
+    const size_t row_id = (static_cast<size_t>(bi) * n + hd) * nqt + qt;
+    const size_t slot0 = (static_cast<size_t>(bi) * n + hd) * rsp.split_slots;
+    const int first_slot = item.slot - item.chunk;
+    {
+      float* pp = rsp.partials + (slot0 + item.slot) * PER_SLOT;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) st_dev(pp + ((wave * ND + db) * 16 + e) * 64 + lane, dq[db][e]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) arrival = atomicAdd(rsp.counters + row_id, 1);
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(arrival) != item.nchunks - 1) return;
+    if (tid == 0) rsp.counters[row_id] = 0;
+    for (int c = 0; c < item.nchunks; ++c) {
+      const float* pp = rsp.partials + (slot0 + first_slot + c) * PER_SLOT;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float a = ld_dev(pp + ((wave * ND + db) * 16 + e) * 64 + lane);
+          dq[db][e] = c == 0 ? a : dq[db][e] + a;
+        }
+    }
+  }
+
   if (qi < s) {
     const float rs = 1.0f / sqrtf(static_cast<float>(D));
     u16* row = dz + (static_cast<size_t>(bi) * s + qi) * ld_dz + hd * D;
@@ -535,19 +762,60 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   }
 }
 
+// Chunk length for the rows of one launch: enough items for about two per
+// CU, whole rows when that already holds, and the partials of the split rows
+// within the scratch (chunks grow until they fit).
+template <bool QUERY_ROWS>
+hipError_t plan_rows(int b, int s, int n, int window, int nrows, int per_slot,
+                     const AttnScratch& sc, RowSplit* rs, int* items_per_head) {
+  long total = 0;
+  for (int r = 0; r < nrows; ++r)
+    total += row_tiles(QUERY_ROWS ? query_row(r, s, window) : key_row(r, s, window));
+  total *= static_cast<long>(b) * n;
+  const long target = 2L * (sc.cus > 0 ? sc.cus : 256);
+  long ch = (total + target - 1) / target;
+  if (ch < 4) ch = 4;
+  if (ch > (1 << 20)) ch = 1 << 20;
+  for (;;) {
+    long items = 0, split = 0;
+    for (int r = 0; r < nrows; ++r) {
+      const int nc = row_chunks(QUERY_ROWS ? query_row(r, s, window) : key_row(r, s, window),
+                                static_cast<int>(ch));
+      items += nc;
+      if (nc > 1) split += nc;
+    }
+    const long need = split * b * n * per_slot;
+    if ((split == 0 || (need <= static_cast<long>(sc.partial_floats) &&
+                        static_cast<long>(b) * n * nrows <= sc.max_counters)) &&
+        items < (1L << 30)) {
+      rs->partials = sc.partials;
+      rs->counters = sc.counters;
+      rs->ch = static_cast<int>(ch);
+      rs->split_slots = static_cast<int>(split);
+      *items_per_head = static_cast<int>(items);
+      return hipSuccess;
+    }
+    ch *= 2;  // fewer, longer chunks
+  }
+}
+
 template <int D>
 hipError_t fwd_d(const u16* qkv, const u16* qk_lo, u16* c, float* lse, int b, int s, int n,
-                 int window, hipStream_t st) {
+                 int window, const AttnScratch& sc, hipStream_t st) {
   const int nqt = (s + BQ - 1) / BQ;
-  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(nqt, n, b), dim3(256), 0, st, qkv, qk_lo, c, lse,
-                     s, n, window, nqt);
+  RowSplit rs;
+  int items = 0;
+  const hipError_t e = plan_rows<true>(b, s, n, window, nqt, BQ * D + 2 * 256, sc, &rs, &items);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(items, n, b), dim3(256), 0, st, qkv, qk_lo, c, lse,
+                     s, n, window, nqt, rs);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t bwd_d(const u16* qkv, const u16* qk_lo, const u16* c, const float* lse,
                  const u16* dc, float* delta, u16* dz, int ld_dz, int b, int s, int n,
-                 int window, hipStream_t st) {
+                 int window, const AttnScratch& sc, hipStream_t st) {
   const int T = b * s;
   const long items = static_cast<long>(T) * n;
   const int per_block = 256 / (D / 8);
@@ -555,31 +823,43 @@ hipError_t bwd_d(const u16* qkv, const u16* qk_lo, const u16* c, const float* ls
                      0, st, dc, c, delta, T, s, n);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((s + BKB - 1) / BKB, n, b), dim3(256), 0, st,
-                     qkv, qk_lo, dc, lse, delta, dz, ld_dz, s, n, window);
+  const int nkt = (s + BKB - 1) / BKB;
+  RowSplit rk;
+  int kitems = 0;
+  e = plan_rows<false>(b, s, n, window, nkt, 2 * BKB * D, sc, &rk, &kitems);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(kitems, n, b), dim3(256), 0, st, qkv, qk_lo,
+                     dc, lse, delta, dz, ld_dz, s, n, window, nkt, rk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqt = (s + BQ - 1) / BQ;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(nqt, n, b), dim3(256), 0, st, qkv, qk_lo, dc,
-                     lse, delta, dz, ld_dz, s, n, window, nqt);
+  RowSplit rq;
+  int qitems = 0;
+  e = plan_rows<true>(b, s, n, window, nqt, BQ * D, sc, &rq, &qitems);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(qitems, n, b), dim3(256), 0, st, qkv, qk_lo, dc,
+                     lse, delta, dz, ld_dz, s, n, window, nqt, rq);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attention_fwd(const u16* qkv, const u16* qk_lo, u16* c, float* lse, int b,
-                                int s, int n, int d, int window, hipStream_t st) {
-  if (d == 128) return fwd_d<128>(qkv, qk_lo, c, lse, b, s, n, window, st);
-  if (d == 64) return fwd_d<64>(qkv, qk_lo, c, lse, b, s, n, window, st);
+                                int s, int n, int d, int window, const AttnScratch& sc,
+                                hipStream_t st) {
+  if (d == 128) return fwd_d<128>(qkv, qk_lo, c, lse, b, s, n, window, sc, st);
+  if (d == 64) return fwd_d<64>(qkv, qk_lo, c, lse, b, s, n, window, sc, st);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attention_bwd(const u16* qkv, const u16* qk_lo, const u16* c,
                                 const float* lse, const u16* dc, float* delta, u16* dz,
                                 int ld_dz, int b, int s, int n, int d, int window,
-                                hipStream_t st) {
-  if (d == 128) return bwd_d<128>(qkv, qk_lo, c, lse, dc, delta, dz, ld_dz, b, s, n, window, st);
-  if (d == 64) return bwd_d<64>(qkv, qk_lo, c, lse, dc, delta, dz, ld_dz, b, s, n, window, st);
+                                const AttnScratch& sc, hipStream_t st) {
+  if (d == 128)
+    return bwd_d<128>(qkv, qk_lo, c, lse, dc, delta, dz, ld_dz, b, s, n, window, sc, st);
+  if (d == 64)
+    return bwd_d<64>(qkv, qk_lo, c, lse, dc, delta, dz, ld_dz, b, s, n, window, sc, st);
   return hipErrorInvalidValue;
 }
 

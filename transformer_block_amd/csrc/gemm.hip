@@ -870,6 +870,8 @@ hipError_t build_plan(const GemmProblem* probs, int nprob, Major a_major, Major 
 
 int gemm_tiles(int M, int N) { return tiles_of(M, N); }
 
+int device_compute_units() { return device_cus(); }
+
 hipError_t launch_zero_i32(int* p, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int blocks = min((n + 255) / 256, 1024);

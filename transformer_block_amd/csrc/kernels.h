@@ -113,17 +113,32 @@ hipError_t launch_layernorm_bwd(const float* da, const u16* x, const u16* gamma,
                                 u16* dx, float* partials, u16* dgamma, u16* dbeta,
                                 int T, int h, hipStream_t stream);
 
+// Scratch of the attention launches: fp32 partial results of rows split into
+// chunks, and one arrival counter per (batch, head, row) (zero on entry, left
+// zero).  cus = compute units of the device (sets the chunking).
+struct AttnScratch {
+  float* partials;
+  size_t partial_floats;
+  int* counters;
+  int max_counters;
+  int cus;
+};
+
+// Compute units of the current device (0 if the query fails).
+int device_compute_units();
+
 // Sliding-window causal flash attention, forward: reads q, k, v column blocks
 // of qkv [b*s, 3*n*d] and the rounding residuals of q and k, qk_lo [b*s, 2*n*d];
 // writes c [b*s, n*d] and the base-2 log-sum-exp lse [b, n, s].
 hipError_t launch_attention_fwd(const u16* qkv, const u16* qk_lo, u16* c, float* lse,
-                                int b, int s, int n, int d, int window, hipStream_t stream);
+                                int b, int s, int n, int d, int window,
+                                const AttnScratch& scratch, hipStream_t stream);
 
 // Attention backward.  delta[b,n,s] = rowsum(dc * c) per head first, then
 // dk, dv and dq written into the first 3*n*d columns of dz [b*s, ld_dz].
 hipError_t launch_attention_bwd(const u16* qkv, const u16* qk_lo, const u16* c,
                                 const float* lse, const u16* dc, float* delta, u16* dz,
                                 int ld_dz, int b, int s, int n, int d, int window,
-                                hipStream_t stream);
+                                const AttnScratch& scratch, hipStream_t stream);
 
 }  // namespace ptb

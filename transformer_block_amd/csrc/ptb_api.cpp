@@ -84,8 +84,8 @@ SavedLayout saved_layout(const Shape& s) {
   return L;
 }
 
-// Output tiles of the largest GEMM launch of the layer (one arrival counter
-// each).
+// Arrival counters one launch of the layer needs at most: output tiles of
+// the largest GEMM launch, rows of the attention launches.
 int max_gemm_tiles(const Shape& s) {
   const int T = static_cast<int>(s.T), h = static_cast<int>(s.h), hl = static_cast<int>(s.hl);
   const int K2 = static_cast<int>(s.K2), N1 = static_cast<int>(s.N1), f = static_cast<int>(s.f);
@@ -93,7 +93,9 @@ int max_gemm_tiles(const Shape& s) {
   for (int t : {ptb::gemm_tiles(T, h), ptb::gemm_tiles(T, K2), ptb::gemm_tiles(K2, h),
                 ptb::gemm_tiles(h, N1)})
     m = t > m ? t : m;
-  return m;
+  // attention: one counter per (batch, head, row of 128)
+  const long rows = s.b * s.n * ((s.s + 127) / 128);
+  return rows > m ? static_cast<int>(rows) : m;
 }
 
 struct WorkLayout {
@@ -275,9 +277,11 @@ int32_t ptb_forward_timed(const ptb_dims* dims, const void* x, const void* ln_ga
     PTB_STAGE(1, ptb::launch_gemm_group(pr, 2, ptb::KMAJOR, ptb::OUTER_MAJOR,
                                         ptb::EPI_QKV_GELU, gs, strm));
   }
+  const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
+                            gs.max_tiles, ptb::device_compute_units()};
   PTB_STAGE(2, ptb::launch_attention_fwd(qkv, qk_lo, c, lse, static_cast<int>(s.b),
                                     static_cast<int>(s.s), static_cast<int>(s.n),
-                                    static_cast<int>(s.d), static_cast<int>(s.w), strm));
+                                    static_cast<int>(s.d), static_cast<int>(s.w), as, strm));
   {  // [O ; FC2] projection plus the residual
     ptb::Epilogue e{};
     e.o0 = static_cast<u16*>(y); e.i0 = X; e.ld0 = static_cast<int>(s.h);
@@ -339,10 +343,12 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
             s.hl, 0),
         ptb::KMAJOR, ptb::EPI_DGELU, e, gs, strm));
   }
+  const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
+                            gs.max_tiles, ptb::device_compute_units()};
   PTB_STAGE(1, ptb::launch_attention_bwd(qkv, qk_lo, c, lse, dc, delta, dz, static_cast<int>(s.N1),
                                     static_cast<int>(s.b), static_cast<int>(s.s),
                                     static_cast<int>(s.n), static_cast<int>(s.d),
-                                    static_cast<int>(s.w), strm));
+                                    static_cast<int>(s.w), as, strm));
   {  // wgrad of [O ; FC2]: [c | g]^T dy
     ptb::Epilogue e{};
     e.o0 = static_cast<u16*>(dw_o); e.ld0 = h;
