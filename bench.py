@@ -64,8 +64,8 @@ def stage_work(w):
         "gemm_wgrad_o_fc2": ("flops", 2 * K2 * T * h),
         "gemm_dgrad_qkv_fc1": ("flops", 2 * T * N1 * h),
         "gemm_wgrad_qkv_fc1": ("flops", 2 * h * T * N1),
-        # da (fp32) + x + dy read, dx written
-        "layernorm_bwd": ("bytes", T * h * (4 + 2 + 2 + 2) + T * 8),
+        # da + x + dy read, dx written (bf16)
+        "layernorm_bwd": ("bytes", T * h * (2 + 2 + 2 + 2) + T * 8),
     }
     return fwd, bwd
 

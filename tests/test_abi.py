@@ -93,7 +93,7 @@ def test_saved_layout_is_ordered_aligned_and_sized(lib):
     assert P.ptb_saved_bytes(d) >= lay["qk_lo"] + sizes["qk_lo"]
     # split-tile partials (2 fp32 256x256 tiles per workgroup, 256 workgroups)
     # come first, then the backward's dc, dZ and da
-    assert P.ptb_workspace_bytes(d) >= 2 * 256 * 256 * 256 * 4 + T * (3 * hl + f) * 2 + T * h * 4
+    assert P.ptb_workspace_bytes(d) >= 2 * 256 * 256 * 256 * 4 + T * (3 * hl + f) * 2 + T * h * 2
 
 
 def test_forward_backward_reject_null_and_misaligned_before_any_hip_call(lib):

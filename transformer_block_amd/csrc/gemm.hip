@@ -9,7 +9,7 @@
 //   forward   [QKV | FC1]:  a [T,h]      x [W_qkv | W_fc1]      -> qkv, u, GeLU(u)
 //             [O ; FC2]:    [c | g]      x [W_o ; W_fc2]  + x   -> y
 //   backward  dgrad:        dy x [W_o ; W_fc2]^T  (x GeLU'(u))  -> dc, du
-//                           dZ x [W_qkv | W_fc1]^T              -> da (fp32)
+//                           dZ x [W_qkv | W_fc1]^T              -> da
 //             wgrad:        [c | g]^T x dy                      -> dW_o, dW_fc2
 //                           a^T x dZ                            -> dW_qkv, dW_fc1
 // Concatenations are addressed in place (two-segment operands), never copied.
@@ -891,7 +891,7 @@ hipError_t launch_gemm_group(const GemmProblem* probs, int nprob, Major a_major,
     if (mode == EPI_RESIDUAL) return launch_plan<KMAJOR, OUTER_MAJOR, EPI_RESIDUAL>(pl, grid, s);
   } else if (a_major == KMAJOR && b_major == KMAJOR) {
     if (mode == EPI_DGELU) return launch_plan<KMAJOR, KMAJOR, EPI_DGELU>(pl, grid, s);
-    if (mode == EPI_F32) return launch_plan<KMAJOR, KMAJOR, EPI_F32>(pl, grid, s);
+    if (mode == EPI_STORE2_COLS) return launch_plan<KMAJOR, KMAJOR, EPI_STORE2_COLS>(pl, grid, s);
   } else if (a_major == OUTER_MAJOR && b_major == OUTER_MAJOR) {
     if (mode == EPI_STORE2_ROWS) return launch_plan<OUTER_MAJOR, OUTER_MAJOR, EPI_STORE2_ROWS>(pl, grid, s);
     if (mode == EPI_STORE2_COLS) return launch_plan<OUTER_MAJOR, OUTER_MAJOR, EPI_STORE2_COLS>(pl, grid, s);

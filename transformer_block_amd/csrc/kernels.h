@@ -108,7 +108,7 @@ hipError_t launch_layernorm_fwd(const u16* x, const u16* gamma, const u16* beta,
 // LayerNorm backward plus residual: dx = dy + LN'(da); per-block partial sums
 // of dgamma, dbeta into `partials` [nblk, 2, h], then reduced into bf16.
 int layernorm_bwd_blocks(int T);
-hipError_t launch_layernorm_bwd(const float* da, const u16* x, const u16* gamma,
+hipError_t launch_layernorm_bwd(const u16* da, const u16* x, const u16* gamma,
                                 const float* mu, const float* rstd, const u16* dy,
                                 u16* dx, float* partials, u16* dgamma, u16* dbeta,
                                 int T, int h, hipStream_t stream);

@@ -11,7 +11,8 @@
 // is written back in bf16 with 16-byte stores, together with its rounding
 // residual a_lo = bf16(a_fp32 - a) (used where bf16 rounding of a would be
 // amplified: the query/key projection feeding the softmax logits).
-// Backward: each workgroup walks a strided set of rows, computes
+// Backward: each workgroup walks a strided set of rows (the next row's loads
+// in flight while the current one is finished), computes
 //   dx = dy + rstd * (g - mean(g) - xhat * mean(g * xhat)),  g = da * gamma,
 // and keeps per-column partial sums of dgamma = sum da*xhat and dbeta = sum da
 // in registers; a second kernel reduces the per-workgroup partials.
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(LN_THREADS) void ln_fwd_kernel(const u16* __restric
   if (tid == 0) { mu_out[row] = mu; rstd_out[row] = rstd; }
 }
 
-constexpr int LNB_THREADS = 1024;
+constexpr int LNB_THREADS = 512;  // 8 waves: two per SIMD, up to 256 VGPRs each
 constexpr int LNB_WAVES = LNB_THREADS / 64;
 
 // Two block-wide sums at once (one pair of barriers).
@@ -116,49 +117,75 @@ __device__ __forceinline__ float2 block_sum2(float a, float b, float* red) {
   return make_float2(sa, sb);
 }
 
-__device__ __forceinline__ void load8f(const float* p, float* f) {
-  const float4 d0 = *reinterpret_cast<const float4*>(p);
-  const float4 d1 = *reinterpret_cast<const float4*>(p + 4);
-  f[0] = d0.x; f[1] = d0.y; f[2] = d0.z; f[3] = d0.w;
-  f[4] = d1.x; f[5] = d1.y; f[6] = d1.z; f[7] = d1.w;
+// One row of the backward's inputs as this thread holds them: NCH 16-byte
+// chunks (8 bf16 each) of x, dy and da, plus the row's statistics.
+template <int NCH>
+struct LnRow {
+  uint4 x[NCH], dy[NCH], da[NCH];
+  float mu, rstd;
+};
+
+template <int NCH>
+__device__ __forceinline__ void load_row(LnRow<NCH>& d, const u16* da, const u16* x,
+                                         const u16* dy, const float* mu, const float* rstd,
+                                         int row, int h, int nch) {
+  d.mu = mu[row];
+  d.rstd = rstd[row];
+  const size_t base = static_cast<size_t>(row) * h;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + i * LNB_THREADS;
+    if (c < nch) {
+      d.x[i] = *reinterpret_cast<const uint4*>(x + base + c * 8);
+      d.da[i] = *reinterpret_cast<const uint4*>(da + base + c * 8);
+      d.dy[i] = *reinterpret_cast<const uint4*>(dy + base + c * 8);
+    }
+  }
 }
 
-// NCH = 16-byte chunks of a row per thread (h <= NCH * 8 * 1024).  The row is
-// read twice: once for the two row sums and the column partials, once more
-// (from cache) for dx, which keeps register use low enough for 16 waves/CU.
+// NCH = 16-byte chunks of a row per thread (h <= NCH * 8 * 512).  Each row is
+// read once, into registers, and the next row of the workgroup is loaded
+// while the current one is reduced and written, so a workgroup always has a
+// row's worth of loads in flight (two rows of registers).
 template <int NCH>
 __global__ __launch_bounds__(LNB_THREADS) void ln_bwd_kernel(
-    const float* __restrict__ da, const u16* __restrict__ x, const u16* __restrict__ gamma,
+    const u16* __restrict__ da, const u16* __restrict__ x, const u16* __restrict__ gamma,
     const float* __restrict__ mu, const float* __restrict__ rstd, const u16* __restrict__ dy,
     u16* __restrict__ dx, float* __restrict__ partials, int T, int h) {
   __shared__ float red[2 * LNB_WAVES];
   const int tid = threadIdx.x;
   const int nch = h >> 3;
   const float inv_h = 1.0f / static_cast<float>(h);
-  float gm[NCH][8], pg[NCH][8], pb[NCH][8];
+  uint4 gmp[NCH];  // gamma, packed: unpacked where used
+  float pg[NCH][8], pb[NCH][8];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = tid + i * LNB_THREADS;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { pg[i][j] = 0.0f; pb[i][j] = 0.0f; gm[i][j] = 0.0f; }
-    if (c < nch) unpack8(*reinterpret_cast<const uint4*>(gamma + c * 8), gm[i]);
+    for (int j = 0; j < 8; ++j) { pg[i][j] = 0.0f; pb[i][j] = 0.0f; }
+    gmp[i] = c < nch ? *reinterpret_cast<const uint4*>(gamma + c * 8) : make_uint4(0, 0, 0, 0);
   }
-  for (int row = blockIdx.x; row < T; row += gridDim.x) {
-    const float m = mu[row], r = rstd[row];
-    const float* dar = da + static_cast<size_t>(row) * h;
-    const u16* xr = x + static_cast<size_t>(row) * h;
+  LnRow<NCH> cur;
+  int row = blockIdx.x;
+  if (row < T) load_row(cur, da, x, dy, mu, rstd, row, h, nch);
+  for (; row < T; row += gridDim.x) {
+    LnRow<NCH> nxt;
+    if (row + static_cast<int>(gridDim.x) < T)
+      load_row(nxt, da, x, dy, mu, rstd, row + gridDim.x, h, nch);
+    const float m = cur.mu, r = cur.rstd;
     float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = tid + i * LNB_THREADS;
       if (c < nch) {
-        float xv[8], dv[8];
-        unpack8(*reinterpret_cast<const uint4*>(xr + c * 8), xv);
-        load8f(dar + c * 8, dv);
+        float xv[8], gm[8], dv[8];
+        unpack8(cur.x[i], xv);
+        unpack8(gmp[i], gm);
+        unpack8(cur.da[i], dv);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float xh = (xv[j] - m) * r;
-          const float gg = dv[j] * gm[i][j];
+          const float gg = dv[j] * gm[j];
           s1 += gg;
           s2 += gg * xh;
           pg[i][j] += dv[j] * xh;
@@ -168,27 +195,28 @@ __global__ __launch_bounds__(LNB_THREADS) void ln_bwd_kernel(
     }
     const float2 sums = block_sum2(s1, s2, red);
     const float mean_g = sums.x * inv_h, mean_gx = sums.y * inv_h;
-    const u16* dyr = dy + static_cast<size_t>(row) * h;
     u16* dxr = dx + static_cast<size_t>(row) * h;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = tid + i * LNB_THREADS;
       if (c < nch) {
-        float xv[8], dv[8], yv[8];
-        unpack8(*reinterpret_cast<const uint4*>(xr + c * 8), xv);
-        load8f(dar + c * 8, dv);
-        unpack8(*reinterpret_cast<const uint4*>(dyr + c * 8), yv);
+        float xv[8], gm[8], yv[8], dv[8];
+        unpack8(cur.da[i], dv);
+        unpack8(cur.x[i], xv);
+        unpack8(gmp[i], gm);
+        unpack8(cur.dy[i], yv);
         uint32_t o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int j0 = 2 * j, j1 = 2 * j + 1;
-          const float v0 = yv[j0] + r * (dv[j0] * gm[i][j0] - mean_g - (xv[j0] - m) * r * mean_gx);
-          const float v1 = yv[j1] + r * (dv[j1] * gm[i][j1] - mean_g - (xv[j1] - m) * r * mean_gx);
+          const float v0 = yv[j0] + r * (dv[j0] * gm[j0] - mean_g - (xv[j0] - m) * r * mean_gx);
+          const float v1 = yv[j1] + r * (dv[j1] * gm[j1] - mean_g - (xv[j1] - m) * r * mean_gx);
           o[j] = pack2bf(v0, v1);
         }
         *reinterpret_cast<uint4*>(dxr + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
       }
     }
+    cur = nxt;
   }
   float* pgr = partials + static_cast<size_t>(blockIdx.x) * 2 * h;
   float* pbr = pgr + h;
@@ -207,26 +235,39 @@ __global__ __launch_bounds__(LNB_THREADS) void ln_bwd_kernel(
   }
 }
 
-// Sum the per-workgroup partials column by column.  A workgroup owns 64 of
-// the 2h columns; its 4 waves each sum a quarter of the partial rows (lanes
-// on consecutive columns: coalesced), then wave 0 adds the four quarters.
-// The order is fixed, so the result is deterministic.
-__global__ __launch_bounds__(256) void ln_bwd_reduce_kernel(const float* __restrict__ partials,
-                                                            int nblk, int h,
-                                                            u16* __restrict__ dgamma,
-                                                            u16* __restrict__ dbeta) {
-  __shared__ float part[4][64];
+// Sum the per-workgroup partials column by column.  A workgroup owns 256 of
+// the 2h columns (64 lanes x 4 consecutive columns, 16-byte loads); its 8
+// waves each sum every 8th partial row, then wave 0 adds the eight in a fixed
+// order, so the result is deterministic.
+constexpr int LNR_WAVES = 8;
+__global__ __launch_bounds__(64 * LNR_WAVES) void ln_bwd_reduce_kernel(
+    const float* __restrict__ partials, int nblk, int h, u16* __restrict__ dgamma,
+    u16* __restrict__ dbeta) {
+  __shared__ float4 part[LNR_WAVES][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = blockIdx.x * 64 + lane;
-  float acc = 0.0f;
-  if (col < 2 * h)
-    for (int b = wave; b < nblk; b += 4) acc += partials[static_cast<size_t>(b) * 2 * h + col];
+  const int c4 = blockIdx.x * 64 + lane;  // float4 column
+  const int n4 = h / 2;                   // 2h columns in float4s
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (c4 < n4) {
+#pragma unroll 8
+    for (int b = wave; b < nblk; b += LNR_WAVES) {
+      const float4 v = reinterpret_cast<const float4*>(partials + static_cast<size_t>(b) * 2 * h)[c4];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+  }
   part[wave][lane] = acc;
   __syncthreads();
-  if (wave == 0 && col < 2 * h) {
-    const float t = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
-    if (col < h) dgamma[col] = f2bf(t);
-    else dbeta[col - h] = f2bf(t);
+  if (wave == 0 && c4 < n4) {
+    float4 t = part[0][lane];
+#pragma unroll
+    for (int w = 1; w < LNR_WAVES; ++w) {
+      const float4 v = part[w][lane];
+      t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+    }
+    const int col = 4 * c4;  // h is a multiple of 4: the four columns lie on one side
+    u16* o = col < h ? dgamma + col : dbeta + (col - h);
+    const uint2 packed = make_uint2(pack2bf(t.x, t.y), pack2bf(t.z, t.w));
+    *reinterpret_cast<uint2*>(o) = packed;
   }
 }
 
@@ -243,21 +284,21 @@ hipError_t launch_layernorm_fwd(const u16* x, const u16* gamma, const u16* beta,
 
 int layernorm_bwd_blocks(int T) { return T < LN_BWD_BLOCKS ? (T < 1 ? 1 : T) : LN_BWD_BLOCKS; }
 
-hipError_t launch_layernorm_bwd(const float* da, const u16* x, const u16* gamma,
+hipError_t launch_layernorm_bwd(const u16* da, const u16* x, const u16* gamma,
                                 const float* mu, const float* rstd, const u16* dy, u16* dx,
                                 float* partials, u16* dgamma, u16* dbeta, int T, int h,
                                 hipStream_t s) {
   const int nblk = layernorm_bwd_blocks(T);
-  if (h <= 8 * LNB_THREADS)
-    hipLaunchKernelGGL(ln_bwd_kernel<1>, dim3(nblk), dim3(LNB_THREADS), 0, s, da, x, gamma, mu,
-                       rstd, dy, dx, partials, T, h);
-  else
-    hipLaunchKernelGGL(ln_bwd_kernel<2>, dim3(nblk), dim3(LNB_THREADS), 0, s, da, x, gamma, mu,
-                       rstd, dy, dx, partials, T, h);
+  auto* kern = h <= 8 * LNB_THREADS    ? ln_bwd_kernel<1>
+               : h <= 16 * LNB_THREADS ? ln_bwd_kernel<2>
+               : h <= 24 * LNB_THREADS ? ln_bwd_kernel<3>
+                                       : ln_bwd_kernel<4>;
+  hipLaunchKernelGGL(kern, dim3(nblk), dim3(LNB_THREADS), 0, s, da, x, gamma, mu, rstd, dy, dx,
+                     partials, T, h);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ln_bwd_reduce_kernel, dim3((2 * h + 63) / 64), dim3(256), 0, s, partials,
-                     nblk, h, dgamma, dbeta);
+  hipLaunchKernelGGL(ln_bwd_reduce_kernel, dim3((h / 2 + 63) / 64), dim3(64 * LNR_WAVES), 0, s,
+                     partials, nblk, h, dgamma, dbeta);
   return hipGetLastError();
 }
 

@@ -113,7 +113,7 @@ WorkLayout work_layout(const Shape& s) {
   W.counters = o; o = align_up(o + static_cast<size_t>(W.max_tiles) * 4);
   W.dc = o; o = align_up(o + s.T * s.hl * 2);
   W.dz = o; o = align_up(o + s.T * s.N1 * 2);
-  W.da = o; o = align_up(o + s.T * s.h * 4);
+  W.da = o; o = align_up(o + s.T * s.h * 2);
   W.delta = o; o = align_up(o + s.b * s.n * s.s * 4);
   W.partials = o; o = align_up(o + static_cast<size_t>(ptb::layernorm_bwd_blocks(s.T)) * 2 * s.h * 4);
   W.total = o;
@@ -321,7 +321,7 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
   const u16* qk_lo = at<u16>(saved, L.off[PTB_SAVED_QK_LO]);
   u16* dc = at<u16>(workspace, W.dc);
   u16* dz = at<u16>(workspace, W.dz);
-  float* da = at<float>(workspace, W.da);
+  u16* da = at<u16>(workspace, W.da);
   float* delta = at<float>(workspace, W.delta);
   float* partials = at<float>(workspace, W.partials);
   const ptb::GemmScratch gs{at<float>(workspace, W.gemm_partials),
@@ -358,14 +358,15 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
                              ptb::OUTER_MAJOR, one(DY, s.h, s.T), ptb::OUTER_MAJOR,
                              ptb::EPI_STORE2_ROWS, e, gs, strm));
   }
-  {  // dgrad through [QKV | FC1]: da = dZ [W_qkv | W_fc1]^T (fp32)
+  {  // dgrad through [QKV | FC1]: da = dZ [W_qkv | W_fc1]^T
     ptb::Epilogue e{};
-    e.of = da; e.ld0 = h;
+    e.o0 = da; e.ld0 = h;
+    e.split = h;  // one output
     PTB_STAGE(3, ptb::launch_gemm(
         T, h, static_cast<int>(s.N1), one(dz, s.N1, s.T), ptb::KMAJOR,
         two(static_cast<const u16*>(w_qkv), 3 * s.hl, s.h, static_cast<const u16*>(w_fc1), s.f,
             s.h, 3 * s.hl, 1),
-        ptb::KMAJOR, ptb::EPI_F32, e, gs, strm));
+        ptb::KMAJOR, ptb::EPI_STORE2_COLS, e, gs, strm));
   }
   {  // wgrad of [QKV | FC1]: a^T dZ
     ptb::Epilogue e{};
