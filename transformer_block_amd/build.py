@@ -19,7 +19,13 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libptb.so")
-SOURCES = ["gemm.hip", "attention.hip", "layernorm.hip", "ptb_api.cpp"]
+SOURCES = ["gemm.hip", "attention_fwd.hip", "attention.hip", "layernorm.hip", "ptb_api.cpp"]
+# Per-source code generation options.  The attention forward rescales its
+# output accumulators with vector ALU instructions; with the accumulators in
+# AGPRs the compiler copies all of them to VGPRs on every key tile, so there
+# the matrix-core results go to VGPRs.  (The backward kernels, which hold
+# twice the accumulators, are faster with the default.)
+EXTRA_FLAGS = {"attention_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 ARCH = "gfx950"
 
 
@@ -41,7 +47,7 @@ def common_flags() -> list:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

@@ -1,5 +1,7 @@
-// Sliding-window causal flash attention for gfx950: forward, and backward with
-// the probabilities recomputed from the saved log-sum-exp.
+// Sliding-window causal flash attention for gfx950: what is computed, and the
+// backward pass with the probabilities recomputed from the saved
+// log-sum-exp (the forward pass is in attention_fwd.hip, the pieces both
+// share in attention_common.h).
 //
 // What is computed (MegaScale reading notes, section 1.1, eq (5)-(6), and
 // section 1.3): for each (batch, head) and query i, the keys j with
@@ -17,7 +19,9 @@
 // with the lane 32 apart, and O^T = V^T P^T reuses the S^T accumulator
 // registers directly as the B operand (the key order inside a 16-key step is
 // permuted identically on both operands, which leaves the sum unchanged).
-// V^T is written transposed into LDS once per tile.  The backward splits into
+// The forward's key tiles reach LDS by DMA one tile ahead, and V^T is read
+// from the row-major V tile by the transposing LDS read (the permutation is
+// applied to V's rows as they are loaded).  The backward splits into
 // a key-parallel kernel for dK, dV (S = Q K^T, lane = key) and a
 // query-parallel kernel for dQ (S^T, lane = query), so no atomics are needed
 // and results are deterministic.
@@ -29,368 +33,10 @@
 // k would shift every logit by a few thousandths, which the softmax turns into
 // a relative error of the same size in the output and, through dS, in the
 // gradients of q and k.
-#include <math.h>
-
-#include "device_common.h"
-#include "kernels.h"
+#include "attention_common.h"
 
 namespace ptb {
 namespace {
-
-constexpr int BQ = 128;   // queries per workgroup (forward, dQ): 4 waves x 32
-constexpr int BKV = 64;   // keys per LDS tile (forward, dQ)
-constexpr int BKB = 128;  // keys per workgroup (dK/dV): 4 waves x 32
-constexpr int BQB = 64;   // queries per LDS tile (dK/dV)
-
-// Rows of D bf16 in LDS, addressed in 16-byte chunks, XOR-swizzled.
-template <int D>
-__device__ __forceinline__ int rowswz(int r) {
-  if constexpr (D == 128) return swz256(r);
-  else return swz128(r);
-}
-template <int D>
-__device__ __forceinline__ u16* row_chunk(u16* base, int r, int c) {
-  return base + r * D + ((c ^ rowswz<D>(r)) << 3);
-}
-template <int D>
-__device__ __forceinline__ bf16x8 row_frag(const u16* base, int r, int c) {
-  return as_bf16x8(*reinterpret_cast<const uint4*>(base + r * D + ((c ^ rowswz<D>(r)) << 3)));
-}
-
-// Transposed tiles: D rows of 64 bf16, addressed in 8-byte slots of 4.
-__device__ __forceinline__ uint2 tslot(const u16* base, int r, int slot) {
-  return *reinterpret_cast<const uint2*>(base + r * 64 + ((slot ^ swz8b(r)) << 2));
-}
-// A operand "X^T[d][k]" for k = 4g..4g+3 and 8+4g..8+4g+3 inside a 16-step
-// starting at tile column k0.
-__device__ __forceinline__ bf16x8 tfrag(const u16* base, int r, int k0, int g) {
-  const uint2 lo = tslot(base, r, (k0 >> 2) + g);
-  const uint2 hi = tslot(base, r, (k0 >> 2) + 2 + g);
-  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
-
-__device__ __forceinline__ bf16x8 pack8(const f32x16& a, int base) {
-  return as_bf16x8(make_uint4(pack2bf(a[base + 0], a[base + 1]), pack2bf(a[base + 2], a[base + 3]),
-                              pack2bf(a[base + 4], a[base + 5]), pack2bf(a[base + 6], a[base + 7])));
-}
-
-// A 64 x D tile of a row-major matrix (row stride ld) held in registers:
-// thread t owns rows 4*kg .. 4*kg+3 and the 8 columns of chunk dc.
-template <int D>
-struct Tile64 {
-  static constexpr int DC = D / 8;          // chunks per row
-  static constexpr int ACTIVE = 16 * DC;    // threads holding data
-  uint4 v[4];
-
-  __device__ __forceinline__ void load(const u16* g, int ld, int row0, int nrows, int tid) {
-    const int dc = tid % DC, kg = tid / DC;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int r = row0 + kg * 4 + kk;
-      v[kk] = make_uint4(0u, 0u, 0u, 0u);
-      if (tid < ACTIVE && r < nrows)
-        v[kk] = *reinterpret_cast<const uint4*>(g + r * ld + dc * 8);
-    }
-  }
-  __device__ __forceinline__ void store_rows(u16* lds, int tid) const {
-    if (tid >= ACTIVE) return;
-    const int dc = tid % DC, kg = tid / DC;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) *reinterpret_cast<uint4*>(row_chunk<D>(lds, kg * 4 + kk, dc)) = v[kk];
-  }
-  // Writes the transpose: LDS row d (= column of the tile) holds 64 values.
-  __device__ __forceinline__ void store_transposed(u16* lds, int tid) const {
-    if (tid >= ACTIVE) return;
-    const int dc = tid % DC, kg = tid / DC;
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&v[0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&v[1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&v[2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&v[3]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d = dc * 8 + j;
-      const int wi = j >> 1;
-      uint32_t a0, a1;
-      if (j & 1) {
-        a0 = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
-        a1 = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
-      } else {
-        a0 = (w0[wi] & 0xffffu) | (w1[wi] << 16);
-        a1 = (w2[wi] & 0xffffu) | (w3[wi] << 16);
-      }
-      *reinterpret_cast<uint2*>(lds + d * 64 + ((kg ^ swz8b(d)) << 2)) = make_uint2(a0, a1);
-    }
-  }
-};
-
-
-// ------------------------------------------------------- row splitting
-// A "row" is one 128-wide block of queries (forward, dQ) or keys (dK/dV);
-// it walks tiles of 64 along the other axis.  Under a causal mask the rows
-// carry very different amounts of work, so long rows are cut into chunks of
-// at most `ch` tiles, one workgroup each; the chunks of a row are combined by
-// the last of them to finish (fp32 partials at device scope, an arrival
-// counter per row).  Rows are taken longest first.
-struct RowSpan {
-  int begin, end;  // [begin, end) along the tiled axis
-};
-__host__ __device__ inline RowSpan query_row(int qt, int s, int window) {
-  const int q0 = qt * BQ;
-  RowSpan r;
-  r.begin = (q0 - window + 1 > 0 ? q0 - window + 1 : 0) & ~(BKV - 1);
-  r.end = q0 + BQ < s ? q0 + BQ : s;
-  return r;
-}
-__host__ __device__ inline RowSpan key_row(int kt, int s, int window) {
-  const int k0 = kt * BKB;
-  RowSpan r;
-  r.begin = k0 & ~(BQB - 1);
-  const long e = static_cast<long>(k0) + BKB - 1 + window;
-  r.end = e < s ? static_cast<int>(e) : s;
-  return r;
-}
-__host__ __device__ inline int row_tiles(RowSpan r) { return (r.end - r.begin + 63) / 64; }
-__host__ __device__ inline int row_chunks(RowSpan r, int ch) {
-  const int nt = row_tiles(r);
-  return nt <= 0 ? 1 : (nt + ch - 1) / ch;
-}
-
-// The work item of workgroup x within one (batch, head): its row, chunk,
-// span, the row's chunk count, and (for split rows) its partial slot.
-struct RowItem {
-  int row, chunk, nchunks, slot;
-  RowSpan span;
-};
-template <bool QUERY_ROWS>
-__device__ __forceinline__ RowItem decode_row_item(int x, int nrows, int s, int window, int ch) {
-  RowItem it{};
-  int slot = 0;
-  for (int i = 0; i < nrows; ++i) {
-    const int row = QUERY_ROWS ? nrows - 1 - i : i;  // longest rows first
-    const RowSpan sp = QUERY_ROWS ? query_row(row, s, window) : key_row(row, s, window);
-    const int nch = row_chunks(sp, ch);
-    if (x < nch) {
-      it.row = row;
-      it.chunk = x;
-      it.nchunks = nch;
-      it.slot = slot + x;
-      it.span.begin = sp.begin + x * ch * 64;
-      const int e = sp.begin + (x + 1) * ch * 64;
-      it.span.end = e < sp.end ? e : sp.end;
-      return it;
-    }
-    x -= nch;
-    if (nch > 1) slot += nch;
-  }
-  it.nchunks = 0;  // past the last item (not launched)
-  return it;
-}
-
-// fp32 store and load at device (agent) scope: coherent across the XCDs
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Scratch of the split rows of one launch.
-struct RowSplit {
-  float* partials;  // slot-major; `per_slot` floats each
-  int* counters;    // one per (batch, head, row): zero on entry, left zero
-  int ch;           // tiles per chunk
-  int split_slots;  // partial slots per (batch, head)
-};
-
-// ------------------------------------------------------------------ forward
-template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ qkv,
-                                                       const u16* __restrict__ qk_lo,
-                                                       u16* __restrict__ cout,
-                                                       float* __restrict__ lse, int s, int n,
-                                                       int window, int nqt, RowSplit rs) {
-  constexpr int NKS = D / 16, ND = D / 32;
-  __shared__ __attribute__((aligned(16))) u16 k_lds[BKV * D];
-  __shared__ int arrival;
-  __shared__ __attribute__((aligned(16))) u16 kl_lds[BKV * D];
-  __shared__ __attribute__((aligned(16))) u16 vt_lds[D * BKV];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, g = lane >> 5;
-  const RowItem item = decode_row_item<true>(static_cast<int>(blockIdx.x), nqt, s, window, rs.ch);
-  if (item.nchunks == 0) return;
-  const int qt = item.row;
-  const int hd = blockIdx.y, bi = blockIdx.z;
-  const int hl = n * D, ld = 3 * hl;
-  const u16* Qg = qkv + static_cast<size_t>(bi) * s * ld + hd * D;
-  const u16* Kg = Qg + hl;
-  const u16* Vg = Qg + 2 * hl;
-  const u16* Qlg = qk_lo + static_cast<size_t>(bi) * s * (2 * hl) + hd * D;
-  const u16* Klg = Qlg + hl;
-  const int q0 = qt * BQ, qw0 = q0 + wave * 32, qi = qw0 + l32;
-
-  bf16x8 qf[NKS], ql[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    uint4 t = make_uint4(0u, 0u, 0u, 0u), u = t;
-    if (qi < s) {
-      t = *reinterpret_cast<const uint4*>(Qg + qi * ld + ks * 16 + g * 8);
-      u = *reinterpret_cast<const uint4*>(Qlg + qi * (2 * hl) + ks * 16 + g * 8);
-    }
-    qf[ks] = as_bf16x8(t);
-    ql[ks] = as_bf16x8(u);
-  }
-
-  const float sc = kLog2e / sqrtf(static_cast<float>(D));
-  float m = -INFINITY, l = 0.0f;
-  f32x16 o[ND];
-#pragma unroll
-  for (int db = 0; db < ND; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[db][e] = 0.0f;
-
-  const int kv_begin = item.span.begin;
-  const int kv_end = item.span.end;
-  // The next key tile is loaded into registers while the current one is
-  // computed from LDS; the registers are free again once stored.
-  Tile64<D> kt, ktl, vt;
-  if (kv_begin < kv_end) {
-    kt.load(Kg, ld, kv_begin, s, tid);
-    ktl.load(Klg, 2 * hl, kv_begin, s, tid);
-    vt.load(Vg, ld, kv_begin, s, tid);
-  }
-  for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKV) {
-    __syncthreads();  // every wave is done with the previous tile in LDS
-    kt.store_rows(k_lds, tid);
-    ktl.store_rows(kl_lds, tid);
-    vt.store_transposed(vt_lds, tid);
-    __syncthreads();
-    if (kt0 + BKV < kv_end) {
-      kt.load(Kg, ld, kt0 + BKV, s, tid);
-      ktl.load(Klg, 2 * hl, kt0 + BKV, s, tid);
-      vt.load(Vg, ld, kt0 + BKV, s, tid);
-    }
-
-    const bool any = qw0 < s && qw0 + 31 >= kt0 && qw0 - (kt0 + BKV - 1) < window;
-    if (!any) continue;
-    const bool full = kt0 + BKV - 1 <= qw0 && qw0 + 31 - kt0 < window && kt0 + BKV <= s;
-
-    f32x16 st[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) st[kb][e] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 kh = row_frag<D>(k_lds, kb * 32 + l32, ks * 2 + g);
-        st[kb] = mfma32x32x16(kh, qf[ks], st[kb]);
-        st[kb] = mfma32x32x16(row_frag<D>(kl_lds, kb * 32 + l32, ks * 2 + g), qf[ks], st[kb]);
-        st[kb] = mfma32x32x16(kh, ql[ks], st[kb]);
-      }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float x = st[kb][e] * sc;
-        if (!full) {
-          const int key = kt0 + kb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
-          const int diff = qi - key;
-          if (diff < 0 || diff >= window || key >= s) x = -INFINITY;
-        }
-        st[kb][e] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx);
-    const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
-    const float alpha = exp2f(m - msafe);
-    float rs = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = exp2f(st[kb][e] - msafe);
-        st[kb][e] = p;
-        rs += p;
-      }
-    l = l * alpha + rs;
-    m = mnew;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
-        const bf16x8 pb = pack8(st[kb], e2 * 8);
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-          o[db] = mfma32x32x16(tfrag(vt_lds, db * 32 + l32, kb * 32 + e2 * 16, g), pb, o[db]);
-      }
-  }
-
-  if (item.nchunks > 1) {
-    // A chunk of a split row: store o, m and l (device scope), count in; the
-    // last chunk to arrive merges all of them, in chunk order.
-    constexpr int PER_SLOT = BQ * D + 2 * 256;
-    const size_t row_id = (static_cast<size_t>(bi) * n + hd) * nqt + qt;
-    const size_t slot0 = (static_cast<size_t>(bi) * n + hd) * rs.split_slots;
-    const int first_slot = item.slot - item.chunk;
-    {
-      float* pp = rs.partials + (slot0 + item.slot) * PER_SLOT;
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) st_dev(pp + ((wave * ND + db) * 16 + e) * 64 + lane, o[db][e]);
-      st_dev(pp + BQ * D + tid, m);
-      st_dev(pp + BQ * D + 256 + tid, l);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) arrival = atomicAdd(rs.counters + row_id, 1);
-    __syncthreads();
-    if (__builtin_amdgcn_readfirstlane(arrival) != item.nchunks - 1) return;
-    if (tid == 0) rs.counters[row_id] = 0;
-    float mm = -INFINITY;
-    for (int c = 0; c < item.nchunks; ++c)
-      mm = fmaxf(mm, ld_dev(rs.partials + (slot0 + first_slot + c) * PER_SLOT + BQ * D + tid));
-    const float ms = (mm == -INFINITY) ? 0.0f : mm;
-    l = 0.0f;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[db][e] = 0.0f;
-    for (int c = 0; c < item.nchunks; ++c) {
-      const float* pp = rs.partials + (slot0 + first_slot + c) * PER_SLOT;
-      const float f = exp2f(ld_dev(pp + BQ * D + tid) - ms);
-      l += f * ld_dev(pp + BQ * D + 256 + tid);
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[db][e] += f * ld_dev(pp + ((wave * ND + db) * 16 + e) * 64 + lane);
-    }
-    m = mm;
-  }
-
-  const float lt = l + __shfl_xor(l, 32);
-  if (qi < s) {
-    const float inv = 1.0f / lt;
-    u16* cg = cout + (static_cast<size_t>(bi) * s + qi) * hl + hd * D;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int d0 = db * 32 + jj * 8 + g * 4;
-        *reinterpret_cast<uint2*>(cg + d0) =
-            make_uint2(pack2bf(o[db][jj * 4 + 0] * inv, o[db][jj * 4 + 1] * inv),
-                       pack2bf(o[db][jj * 4 + 2] * inv, o[db][jj * 4 + 3] * inv));
-      }
-    if (g == 0) lse[(static_cast<size_t>(bi) * n + hd) * s + qi] = m + log2f(lt);
-  }
-}
 
 // ------------------------------------------------- delta = rowsum(dO * O)
 template <int D>
@@ -762,56 +408,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   }
 }
 
-// Chunk length for the rows of one launch: enough items for about two per
-// CU, whole rows when that already holds, and the partials of the split rows
-// within the scratch (chunks grow until they fit).
-template <bool QUERY_ROWS>
-hipError_t plan_rows(int b, int s, int n, int window, int nrows, int per_slot,
-                     const AttnScratch& sc, RowSplit* rs, int* items_per_head) {
-  long total = 0;
-  for (int r = 0; r < nrows; ++r)
-    total += row_tiles(QUERY_ROWS ? query_row(r, s, window) : key_row(r, s, window));
-  total *= static_cast<long>(b) * n;
-  const long target = 2L * (sc.cus > 0 ? sc.cus : 256);
-  long ch = (total + target - 1) / target;
-  if (ch < 4) ch = 4;
-  if (ch > (1 << 20)) ch = 1 << 20;
-  for (;;) {
-    long items = 0, split = 0;
-    for (int r = 0; r < nrows; ++r) {
-      const int nc = row_chunks(QUERY_ROWS ? query_row(r, s, window) : key_row(r, s, window),
-                                static_cast<int>(ch));
-      items += nc;
-      if (nc > 1) split += nc;
-    }
-    const long need = split * b * n * per_slot;
-    if ((split == 0 || (need <= static_cast<long>(sc.partial_floats) &&
-                        static_cast<long>(b) * n * nrows <= sc.max_counters)) &&
-        items < (1L << 30)) {
-      rs->partials = sc.partials;
-      rs->counters = sc.counters;
-      rs->ch = static_cast<int>(ch);
-      rs->split_slots = static_cast<int>(split);
-      *items_per_head = static_cast<int>(items);
-      return hipSuccess;
-    }
-    ch *= 2;  // fewer, longer chunks
-  }
-}
-
-template <int D>
-hipError_t fwd_d(const u16* qkv, const u16* qk_lo, u16* c, float* lse, int b, int s, int n,
-                 int window, const AttnScratch& sc, hipStream_t st) {
-  const int nqt = (s + BQ - 1) / BQ;
-  RowSplit rs;
-  int items = 0;
-  const hipError_t e = plan_rows<true>(b, s, n, window, nqt, BQ * D + 2 * 256, sc, &rs, &items);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(items, n, b), dim3(256), 0, st, qkv, qk_lo, c, lse,
-                     s, n, window, nqt, rs);
-  return hipGetLastError();
-}
-
 template <int D>
 hipError_t bwd_d(const u16* qkv, const u16* qk_lo, const u16* c, const float* lse,
                  const u16* dc, float* delta, u16* dz, int ld_dz, int b, int s, int n,
@@ -843,14 +439,6 @@ hipError_t bwd_d(const u16* qkv, const u16* qk_lo, const u16* c, const float* ls
 }
 
 }  // namespace
-
-hipError_t launch_attention_fwd(const u16* qkv, const u16* qk_lo, u16* c, float* lse, int b,
-                                int s, int n, int d, int window, const AttnScratch& sc,
-                                hipStream_t st) {
-  if (d == 128) return fwd_d<128>(qkv, qk_lo, c, lse, b, s, n, window, sc, st);
-  if (d == 64) return fwd_d<64>(qkv, qk_lo, c, lse, b, s, n, window, sc, st);
-  return hipErrorInvalidValue;
-}
 
 hipError_t launch_attention_bwd(const u16* qkv, const u16* qk_lo, const u16* c,
                                 const float* lse, const u16* dc, float* delta, u16* dz,

@@ -1,0 +1,219 @@
+// Pieces shared by the attention kernels (attention_fwd.hip: forward;
+// attention.hip: backward): tile shapes, LDS layouts and fragment reads, and
+// the cutting of long causal rows into chunks.  See attention.hip for what
+// the kernels compute.
+#pragma once
+
+#include <math.h>
+
+#include "device_common.h"
+#include "kernels.h"
+#include "lds_dma.h"
+
+namespace ptb {
+namespace {
+
+constexpr int BQ = 128;   // queries per workgroup (forward, dQ): 4 waves x 32
+constexpr int BKV = 64;   // keys per LDS tile (forward, dQ)
+constexpr int BKB = 128;  // keys per workgroup (dK/dV): 4 waves x 32
+constexpr int BQB = 64;   // queries per LDS tile (dK/dV)
+
+// Rows of D bf16 in LDS, addressed in 16-byte chunks, XOR-swizzled.
+template <int D>
+__device__ __forceinline__ int rowswz(int r) {
+  if constexpr (D == 128) return swz256(r);
+  else return swz128(r);
+}
+template <int D>
+__device__ __forceinline__ u16* row_chunk(u16* base, int r, int c) {
+  return base + r * D + ((c ^ rowswz<D>(r)) << 3);
+}
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const u16* base, int r, int c) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(base + r * D + ((c ^ rowswz<D>(r)) << 3)));
+}
+
+// Transposed tiles: D rows of 64 bf16, addressed in 8-byte slots of 4.
+__device__ __forceinline__ uint2 tslot(const u16* base, int r, int slot) {
+  return *reinterpret_cast<const uint2*>(base + r * 64 + ((slot ^ swz8b(r)) << 2));
+}
+// A operand "X^T[d][k]" for k = 4g..4g+3 and 8+4g..8+4g+3 inside a 16-step
+// starting at tile column k0.
+__device__ __forceinline__ bf16x8 tfrag(const u16* base, int r, int k0, int g) {
+  const uint2 lo = tslot(base, r, (k0 >> 2) + g);
+  const uint2 hi = tslot(base, r, (k0 >> 2) + 2 + g);
+  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f32x16& a, int base) {
+  return as_bf16x8(make_uint4(pack2bf_pk(a[base + 0], a[base + 1]), pack2bf_pk(a[base + 2], a[base + 3]),
+                              pack2bf_pk(a[base + 4], a[base + 5]), pack2bf_pk(a[base + 6], a[base + 7])));
+}
+
+// A 64 x D tile of a row-major matrix (row stride ld) held in registers:
+// thread t owns rows 4*kg .. 4*kg+3 and the 8 columns of chunk dc.
+template <int D>
+struct Tile64 {
+  static constexpr int DC = D / 8;          // chunks per row
+  static constexpr int ACTIVE = 16 * DC;    // threads holding data
+  uint4 v[4];
+
+  __device__ __forceinline__ void load(const u16* g, int ld, int row0, int nrows, int tid) {
+    const int dc = tid % DC, kg = tid / DC;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int r = row0 + kg * 4 + kk;
+      v[kk] = make_uint4(0u, 0u, 0u, 0u);
+      if (tid < ACTIVE && r < nrows)
+        v[kk] = *reinterpret_cast<const uint4*>(g + r * ld + dc * 8);
+    }
+  }
+  __device__ __forceinline__ void store_rows(u16* lds, int tid) const {
+    if (tid >= ACTIVE) return;
+    const int dc = tid % DC, kg = tid / DC;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) *reinterpret_cast<uint4*>(row_chunk<D>(lds, kg * 4 + kk, dc)) = v[kk];
+  }
+  // Writes the transpose: LDS row d (= column of the tile) holds 64 values.
+  __device__ __forceinline__ void store_transposed(u16* lds, int tid) const {
+    if (tid >= ACTIVE) return;
+    const int dc = tid % DC, kg = tid / DC;
+    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&v[0]);
+    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&v[1]);
+    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&v[2]);
+    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&v[3]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int d = dc * 8 + j;
+      const int wi = j >> 1;
+      uint32_t a0, a1;
+      if (j & 1) {
+        a0 = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
+        a1 = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
+      } else {
+        a0 = (w0[wi] & 0xffffu) | (w1[wi] << 16);
+        a1 = (w2[wi] & 0xffffu) | (w3[wi] << 16);
+      }
+      *reinterpret_cast<uint2*>(lds + d * 64 + ((kg ^ swz8b(d)) << 2)) = make_uint2(a0, a1);
+    }
+  }
+};
+
+
+// ------------------------------------------------------- row splitting
+// A "row" is one 128-wide block of queries (forward, dQ) or keys (dK/dV);
+// it walks tiles of 64 along the other axis.  Under a causal mask the rows
+// carry very different amounts of work, so long rows are cut into chunks of
+// at most `ch` tiles, one workgroup each; the chunks of a row are combined by
+// the last of them to finish (fp32 partials at device scope, an arrival
+// counter per row).  Rows are taken longest first.
+struct RowSpan {
+  int begin, end;  // [begin, end) along the tiled axis
+};
+__host__ __device__ inline RowSpan query_row(int qt, int s, int window) {
+  const int q0 = qt * BQ;
+  RowSpan r;
+  r.begin = (q0 - window + 1 > 0 ? q0 - window + 1 : 0) & ~(BKV - 1);
+  r.end = q0 + BQ < s ? q0 + BQ : s;
+  return r;
+}
+__host__ __device__ inline RowSpan key_row(int kt, int s, int window) {
+  const int k0 = kt * BKB;
+  RowSpan r;
+  r.begin = k0 & ~(BQB - 1);
+  const long e = static_cast<long>(k0) + BKB - 1 + window;
+  r.end = e < s ? static_cast<int>(e) : s;
+  return r;
+}
+__host__ __device__ inline int row_tiles(RowSpan r) { return (r.end - r.begin + 63) / 64; }
+__host__ __device__ inline int row_chunks(RowSpan r, int ch) {
+  const int nt = row_tiles(r);
+  return nt <= 0 ? 1 : (nt + ch - 1) / ch;
+}
+
+// The work item of workgroup x within one (batch, head): its row, chunk,
+// span, the row's chunk count, and (for split rows) its partial slot.
+struct RowItem {
+  int row, chunk, nchunks, slot;
+  RowSpan span;
+};
+template <bool QUERY_ROWS>
+__device__ __forceinline__ RowItem decode_row_item(int x, int nrows, int s, int window, int ch) {
+  RowItem it{};
+  int slot = 0;
+  for (int i = 0; i < nrows; ++i) {
+    const int row = QUERY_ROWS ? nrows - 1 - i : i;  // longest rows first
+    const RowSpan sp = QUERY_ROWS ? query_row(row, s, window) : key_row(row, s, window);
+    const int nch = row_chunks(sp, ch);
+    if (x < nch) {
+      it.row = row;
+      it.chunk = x;
+      it.nchunks = nch;
+      it.slot = slot + x;
+      it.span.begin = sp.begin + x * ch * 64;
+      const int e = sp.begin + (x + 1) * ch * 64;
+      it.span.end = e < sp.end ? e : sp.end;
+      return it;
+    }
+    x -= nch;
+    if (nch > 1) slot += nch;
+  }
+  it.nchunks = 0;  // past the last item (not launched)
+  return it;
+}
+
+// fp32 store and load at device (agent) scope: coherent across the XCDs
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Scratch of the split rows of one launch.
+struct RowSplit {
+  float* partials;  // slot-major; `per_slot` floats each
+  int* counters;    // one per (batch, head, row): zero on entry, left zero
+  int ch;           // tiles per chunk
+  int split_slots;  // partial slots per (batch, head)
+};
+
+// Chunk length for the rows of one launch: enough items for about two per
+// CU, whole rows when that already holds, and the partials of the split rows
+// within the scratch (chunks grow until they fit).
+template <bool QUERY_ROWS>
+hipError_t plan_rows(int b, int s, int n, int window, int nrows, int per_slot,
+                     const AttnScratch& sc, RowSplit* rs, int* items_per_head) {
+  long total = 0;
+  for (int r = 0; r < nrows; ++r)
+    total += row_tiles(QUERY_ROWS ? query_row(r, s, window) : key_row(r, s, window));
+  total *= static_cast<long>(b) * n;
+  const long target = 2L * (sc.cus > 0 ? sc.cus : 256);
+  long ch = (total + target - 1) / target;
+  if (ch < 4) ch = 4;
+  if (ch > (1 << 20)) ch = 1 << 20;
+  for (;;) {
+    long items = 0, split = 0;
+    for (int r = 0; r < nrows; ++r) {
+      const int nc = row_chunks(QUERY_ROWS ? query_row(r, s, window) : key_row(r, s, window),
+                                static_cast<int>(ch));
+      items += nc;
+      if (nc > 1) split += nc;
+    }
+    const long need = split * b * n * per_slot;
+    if ((split == 0 || (need <= static_cast<long>(sc.partial_floats) &&
+                        static_cast<long>(b) * n * nrows <= sc.max_counters)) &&
+        items < (1L << 30)) {
+      rs->partials = sc.partials;
+      rs->counters = sc.counters;
+      rs->ch = static_cast<int>(ch);
+      rs->split_slots = static_cast<int>(split);
+      *items_per_head = static_cast<int>(items);
+      return hipSuccess;
+    }
+    ch *= 2;  // fewer, longer chunks
+  }
+}
+
+}  // namespace
+}  // namespace ptb

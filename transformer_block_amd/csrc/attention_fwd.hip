@@ -1,0 +1,298 @@
+// Sliding-window causal flash attention, forward pass, for gfx950.  What is
+// computed and the matrix-core mapping are described in attention.hip.
+#include "attention_common.h"
+
+namespace ptb {
+namespace {
+
+// ------------------------------------------------------------------ forward
+// Stage of 64 keys in LDS, filled by DMA (buffer_load ... lds) one tile ahead
+// of the matrix cores, two stages:
+//   K, K_lo: [64 keys][D], rows of 2D bytes; 16-byte chunk c of row r at
+//            slot c ^ rowswz<D>(r) (read by row_frag);
+//   V:       [D / 64 blocks][64 kappa][64 d], read transposed by
+//            frag_outer64.  Row kappa holds key perm16(kappa): inside each 16,
+//            keys 4..7 and 8..11 trade places, which is the key order of the
+//            S^T accumulator packed as the B operand of O^T = V^T P^T.
+// A 1 KB DMA load (64 lanes x 16 bytes) fills 1 KB of a tile; the source of
+// each lane applies the swizzle and the permutation.
+constexpr float kStale = 8.0f;
+
+__device__ __forceinline__ int perm16(int kappa) {
+  const int p = kappa & 15;
+  return (kappa & ~15) | ((p >= 4 && p < 12) ? (p ^ 12) : p);
+}
+
+template <int D>
+struct KvDma {
+  static constexpr int OPB = 64 * D;   // u16 elements of one operand's tile
+  static constexpr int NL = D / 8;     // 1 KB loads per operand tile
+  static constexpr int LPW = NL / 4;   // ... per wave
+  static constexpr int RB = 2 * D;     // bytes per K row
+  static constexpr int RPL = 1024 / RB;  // K rows per load
+  i32x4 dk, dkl, dv;
+  int ok[LPW], okl[LPW], ov[LPW];      // per-lane byte offsets at key 0
+  int ld, ldl;
+
+  // K, K_lo and V of one (batch, head): row stride ld (K, V) and ldl (K_lo),
+  // s rows; rows at or beyond s read as zeros.
+  __device__ __forceinline__ void init(const u16* K, const u16* Kl, const u16* V, int ld_, int ldl_,
+                                       int s, int wave, int lane) {
+    ld = ld_;
+    ldl = ldl_;
+    dk = make_desc(K, static_cast<uint32_t>(((s - 1) * ld + D) * 2));
+    dkl = make_desc(Kl, static_cast<uint32_t>(((s - 1) * ldl + D) * 2));
+    dv = make_desc(V, static_cast<uint32_t>(((s - 1) * ld + D) * 2));
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int inst = wave * LPW + i;
+      const int r = inst * RPL + lane / (RB / 16);
+      const int c = (lane % (RB / 16)) ^ rowswz<D>(r);
+      ok[i] = (r * ld + c * 8) * 2;
+      okl[i] = (r * ldl + c * 8) * 2;
+      const int blk = inst >> 3, kap = (inst & 7) * 8 + (lane >> 3);
+      const int cv = (lane & 7) ^ oswz(kap);
+      ov[i] = (perm16(kap) * ld + blk * 64 + cv * 8) * 2;
+    }
+  }
+  // the tile of keys kt0 .. kt0 + 63 into the stage at LDS byte address lds
+  __device__ __forceinline__ void issue(uint32_t lds, int kt0, int wave) const {
+    const int sk = kt0 * ld * 2, skl = kt0 * ldl * 2;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const uint32_t off = (wave * LPW + i) * 1024;
+      lds_dma16(dk, lds + off, ok[i], sk);
+      lds_dma16(dkl, lds + OPB * 2 + off, okl[i], skl);
+      lds_dma16(dv, lds + 2 * OPB * 2 + off, ov[i], sk);
+    }
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ qkv,
+                                                       const u16* __restrict__ qk_lo,
+                                                       u16* __restrict__ cout,
+                                                       float* __restrict__ lse, int s, int n,
+                                                       int window, int nqt, RowSplit rs) {
+  constexpr int NKS = D / 16, ND = D / 32;
+  constexpr int OPB = KvDma<D>::OPB;
+  __shared__ __attribute__((aligned(1024))) u16 kv[2 * 3 * OPB];
+  __shared__ int arrival;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const RowItem item = decode_row_item<true>(static_cast<int>(blockIdx.x), nqt, s, window, rs.ch);
+  if (item.nchunks == 0) return;
+  const int qt = item.row;
+  const int hd = blockIdx.y, bi = blockIdx.z;
+  const int hl = n * D, ld = 3 * hl;
+  const u16* Qg = qkv + static_cast<size_t>(bi) * s * ld + hd * D;
+  const u16* Kg = Qg + hl;
+  const u16* Vg = Qg + 2 * hl;
+  const u16* Qlg = qk_lo + static_cast<size_t>(bi) * s * (2 * hl) + hd * D;
+  const u16* Klg = Qlg + hl;
+  const int q0 = qt * BQ, qw0 = q0 + wave * 32, qi = qw0 + l32;
+
+  const int kv_begin = item.span.begin;
+  const int kv_end = item.span.end;
+  KvDma<D> dma;
+  dma.init(Kg, Klg, Vg, ld, 2 * hl, s, wave, lane);
+  const uint32_t kv_lds = __builtin_amdgcn_readfirstlane(lds_address(kv));
+  if (kv_begin < kv_end) dma.issue(kv_lds, kv_begin, wave);
+
+  bf16x8 qf[NKS], ql[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    uint4 t = make_uint4(0u, 0u, 0u, 0u), u = t;
+    if (qi < s) {
+      t = *reinterpret_cast<const uint4*>(Qg + qi * ld + ks * 16 + g * 8);
+      u = *reinterpret_cast<const uint4*>(Qlg + qi * (2 * hl) + ks * 16 + g * 8);
+    }
+    qf[ks] = as_bf16x8(t);
+    ql[ks] = as_bf16x8(u);
+  }
+
+  // Running max m is kept in scaled (log2) units: p = exp2(logit * sc - m).
+  const float sc = kLog2e / sqrtf(static_cast<float>(D));
+  float m = -INFINITY, l = 0.0f;
+  f32x16 o[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.0f;
+
+  int stage = 0;
+  for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKV) {
+    wait_vm_lds<0>();  // this wave's loads of tile kt0 landed
+    __syncthreads();   // every wave's; the other stage is free again
+    if (kt0 + BKV < kv_end) dma.issue(kv_lds + (stage ^ 1) * (3 * OPB * 2), kt0 + BKV, wave);
+    const u16* k_lds = kv + stage * 3 * OPB;
+    const u16* kl_lds = k_lds + OPB;
+    const u16* v_lds = k_lds + 2 * OPB;
+    stage ^= 1;
+
+    const bool any = qw0 < s && qw0 + 31 >= kt0 && qw0 - (kt0 + BKV - 1) < window;
+    if (!any) continue;
+    const bool full = kt0 + BKV - 1 <= qw0 && qw0 + 31 - kt0 < window && kt0 + BKV <= s;
+
+    f32x16 st[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st[kb][e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 kh = row_frag<D>(k_lds, kb * 32 + l32, ks * 2 + g);
+        st[kb] = mfma32x32x16(kh, qf[ks], st[kb]);
+        st[kb] = mfma32x32x16(row_frag<D>(kl_lds, kb * 32 + l32, ks * 2 + g), qf[ks], st[kb]);
+        st[kb] = mfma32x32x16(kh, ql[ks], st[kb]);
+      }
+    }
+    float mx = -INFINITY;
+    if (full) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st[kb][e]);
+    } else {
+      // a tile on the diagonal or the window's edge: keep keys in [lo, hi]
+      // of this lane's query, as offsets from the lane's first key
+      asm volatile("; masked key tile");  // keeps this path a real branch
+      const int base = kt0 + g * 4;
+      const int lo = max(qi - window + 1, 0) - base;
+      const int hi = min(qi, s - 1) - base;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int off = kb * 32 + (e >> 2) * 8 + (e & 3);
+          if (off < lo || off > hi) st[kb][e] = -INFINITY;
+          mx = fmaxf(mx, st[kb][e]);
+        }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // The reference point m of the exponentials moves only when some query
+    // of the wave sees a logit more than kStale (log2 units) above it: below
+    // that, p = exp2(logit * sc - m) <= 2^kStale stays well inside fp32 and
+    // bf16 range, and o and l stay consistent with the same m, so the final
+    // o / l and lse = m + log2 l do not depend on when m moved.
+    const float mcand = mx * sc;
+    if (__builtin_amdgcn_ballot_w64(mcand > m + kStale) != 0) {
+      const float mnew = fmaxf(m, mcand);
+      // a lane with no key yet keeps m = -inf: its alpha is exp2(-inf) = 0
+      const float alpha = __builtin_amdgcn_exp2f(m - (mnew == -INFINITY ? 0.0f : mnew));
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+      m = mnew;
+    }
+    const float msafe = (m == -INFINITY) ? 0.0f : m;
+    float rsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(st[kb][e], sc, -msafe));
+        st[kb][e] = p;
+        rsum += p;
+      }
+    l += rsum;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        const bf16x8 pb = pack8(st[kb], e2 * 8);
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+          o[db] = mfma32x32x16(frag_outer64(v_lds, db * 32, kb * 2 + e2, lane), pb, o[db]);
+      }
+  }
+
+  if (item.nchunks > 1) {
+    // A chunk of a split row: store o, m and l (device scope), count in; the
+    // last chunk to arrive merges all of them, in chunk order.
+    constexpr int PER_SLOT = BQ * D + 2 * 256;
+    const size_t row_id = (static_cast<size_t>(bi) * n + hd) * nqt + qt;
+    const size_t slot0 = (static_cast<size_t>(bi) * n + hd) * rs.split_slots;
+    const int first_slot = item.slot - item.chunk;
+    {
+      float* pp = rs.partials + (slot0 + item.slot) * PER_SLOT;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) st_dev(pp + ((wave * ND + db) * 16 + e) * 64 + lane, o[db][e]);
+      st_dev(pp + BQ * D + tid, m);
+      st_dev(pp + BQ * D + 256 + tid, l);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) arrival = atomicAdd(rs.counters + row_id, 1);
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(arrival) != item.nchunks - 1) return;
+    if (tid == 0) rs.counters[row_id] = 0;
+    float mm = -INFINITY;
+    for (int c = 0; c < item.nchunks; ++c)
+      mm = fmaxf(mm, ld_dev(rs.partials + (slot0 + first_slot + c) * PER_SLOT + BQ * D + tid));
+    const float ms = (mm == -INFINITY) ? 0.0f : mm;
+    l = 0.0f;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[db][e] = 0.0f;
+    for (int c = 0; c < item.nchunks; ++c) {
+      const float* pp = rs.partials + (slot0 + first_slot + c) * PER_SLOT;
+      const float f = exp2f(ld_dev(pp + BQ * D + tid) - ms);
+      l += f * ld_dev(pp + BQ * D + 256 + tid);
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] += f * ld_dev(pp + ((wave * ND + db) * 16 + e) * 64 + lane);
+    }
+    m = mm;
+  }
+
+  const float lt = l + __shfl_xor(l, 32);
+  if (qi < s) {
+    const float inv = 1.0f / lt;
+    u16* cg = cout + (static_cast<size_t>(bi) * s + qi) * hl + hd * D;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = db * 32 + jj * 8 + g * 4;
+        *reinterpret_cast<uint2*>(cg + d0) =
+            make_uint2(pack2bf(o[db][jj * 4 + 0] * inv, o[db][jj * 4 + 1] * inv),
+                       pack2bf(o[db][jj * 4 + 2] * inv, o[db][jj * 4 + 3] * inv));
+      }
+    if (g == 0) lse[(static_cast<size_t>(bi) * n + hd) * s + qi] = m + log2f(lt);
+  }
+}
+
+template <int D>
+hipError_t fwd_d(const u16* qkv, const u16* qk_lo, u16* c, float* lse, int b, int s, int n,
+                 int window, const AttnScratch& sc, hipStream_t st) {
+  const int nqt = (s + BQ - 1) / BQ;
+  RowSplit rs;
+  int items = 0;
+  const hipError_t e = plan_rows<true>(b, s, n, window, nqt, BQ * D + 2 * 256, sc, &rs, &items);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(items, n, b), dim3(256), 0, st, qkv, qk_lo, c, lse,
+                     s, n, window, nqt, rs);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention_fwd(const u16* qkv, const u16* qk_lo, u16* c, float* lse, int b,
+                                int s, int n, int d, int window, const AttnScratch& sc,
+                                hipStream_t st) {
+  if (d == 128) return fwd_d<128>(qkv, qk_lo, c, lse, b, s, n, window, sc, st);
+  if (d == 64) return fwd_d<64>(qkv, qk_lo, c, lse, b, s, n, window, sc, st);
+  return hipErrorInvalidValue;
+}
+
+
+}  // namespace ptb
