@@ -246,19 +246,22 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 }
 
 // ------------------------------------------------------------------- dQ
+// Query rows of 128 (4 waves x 32), key tiles of 64 staged by DMA one tile
+// ahead, two stages of four tiles: K, K_lo and V row-major (the A operands of
+// S^T = K Q^T and dP^T = V dO^T) and K once more in the outer layout, rows in
+// the accumulator's order, for the transposed A operand of dQ^T += K^T dS^T.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const u16* __restrict__ qkv, const u16* __restrict__ qk_lo, const u16* __restrict__ dcg,
     const float* __restrict__ lse, const float* __restrict__ delta, u16* __restrict__ dz,
     int ld_dz, int s, int n, int window, int nqt, RowSplit rsp) {
   constexpr int NKS = D / 16, ND = D / 32;
+  constexpr int OPB = 64 * D;  // u16 elements of one operand's tile
+  __shared__ __attribute__((aligned(1024))) u16 kv[2 * 4 * OPB];
   __shared__ int arrival;
-  __shared__ __attribute__((aligned(16))) u16 k_lds[BKV * D];
-  __shared__ __attribute__((aligned(16))) u16 kl_lds[BKV * D];
-  __shared__ __attribute__((aligned(16))) u16 kt_lds[D * BKV];
-  __shared__ __attribute__((aligned(16))) u16 v_lds[BKV * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const RowItem item = decode_row_item<true>(static_cast<int>(blockIdx.x), nqt, s, window, rsp.ch);
   if (item.nchunks == 0) return;
@@ -272,6 +275,23 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const u16* Qlg = qk_lo + static_cast<size_t>(bi) * s * (2 * hl) + hd * D;
   const u16* Klg = Qlg + hl;
   const int q0 = qt * BQ, qw0 = q0 + wave * 32, qi = qw0 + l32;
+
+  const int kv_begin = item.span.begin;
+  const int kv_end = item.span.end;
+  TileDma<D, 64, false> dk, dkl, dv;
+  TileDma<D, 64, true> dkt;
+  dk.init(Kg, ld, s, wave, lane);
+  dkl.init(Klg, 2 * hl, s, wave, lane);
+  dv.init(Vg, ld, s, wave, lane);
+  dkt.init(Kg, ld, s, wave, lane);
+  const uint32_t kv_lds = __builtin_amdgcn_readfirstlane(lds_address(kv));
+  auto issue = [&](uint32_t lds, int kt0) {
+    dk.issue(lds, kt0, wave);
+    dkl.issue(lds + OPB * 2, kt0, wave);
+    dv.issue(lds + 2 * OPB * 2, kt0, wave);
+    dkt.issue(lds + 3 * OPB * 2, kt0, wave);
+  };
+  if (kv_begin < kv_end) issue(kv_lds, kv_begin);
 
   bf16x8 qf[NKS], ql[NKS], of[NKS];
 #pragma unroll
@@ -297,28 +317,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) dq[db][e] = 0.0f;
 
-  const int kv_begin = item.span.begin;
-  const int kv_end = item.span.end;
-  // The next key tile is loaded into registers while the current one is
-  // computed from LDS.
-  Tile64<D> ktile, kltile, vtile;
-  if (kv_begin < kv_end) {
-    ktile.load(Kg, ld, kv_begin, s, tid);
-    kltile.load(Klg, 2 * hl, kv_begin, s, tid);
-    vtile.load(Vg, ld, kv_begin, s, tid);
-  }
+  int stage = 0;
   for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKV) {
-    __syncthreads();  // every wave is done with the previous tile in LDS
-    ktile.store_rows(k_lds, tid);
-    kltile.store_rows(kl_lds, tid);
-    ktile.store_transposed(kt_lds, tid);
-    vtile.store_rows(v_lds, tid);
-    __syncthreads();
-    if (kt0 + BKV < kv_end) {
-      ktile.load(Kg, ld, kt0 + BKV, s, tid);
-      kltile.load(Klg, 2 * hl, kt0 + BKV, s, tid);
-      vtile.load(Vg, ld, kt0 + BKV, s, tid);
-    }
+    wait_vm_lds<0>();  // this wave's loads of tile kt0 landed
+    __syncthreads();   // every wave's; the other stage is free again
+    if (kt0 + BKV < kv_end) issue(kv_lds + (stage ^ 1) * (4 * OPB * 2), kt0 + BKV);
+    const u16* k_lds = kv + stage * 4 * OPB;
+    const u16* kl_lds = k_lds + OPB;
+    const u16* v_lds = k_lds + 2 * OPB;
+    const u16* kt_lds = k_lds + 3 * OPB;
+    stage ^= 1;
 
     const bool any = qw0 < s && qw0 + 31 >= kt0 && qw0 - (kt0 + BKV - 1) < window;
     if (!any) continue;
@@ -338,16 +346,26 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
         dpt[kb] = mfma32x32x16(row_frag<D>(v_lds, kb * 32 + l32, ks * 2 + g), of[ks], dpt[kb]);
       }
     }
+    if (!full) {
+      // a tile on the diagonal or the window's edge: keep keys in [lo, hi]
+      // of this lane's query, as offsets from the lane's first key
+      asm volatile("; masked key tile");  // keeps this path a real branch
+      const int base = kt0 + g * 4;
+      const int lo = max(qi - window + 1, 0) - base;
+      const int hi = min(qi, s - 1) - base;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int off = kb * 32 + (e >> 2) * 8 + (e & 3);
+          if (off < lo || off > hi) st[kb][e] = -INFINITY;
+        }
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float p = exp2f(st[kb][e] * sc - lq);
-        if (!full) {
-          const int key = kt0 + kb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
-          const int diff = qi - key;
-          if (diff < 0 || diff >= window || key >= s) p = 0.0f;
-        }
+        const float p = __builtin_amdgcn_exp2f(fmaf(st[kb][e], sc, -lq));
         st[kb][e] = p * (dpt[kb][e] - dq_delta);
       }
 #pragma unroll
@@ -357,7 +375,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
         const bf16x8 dsb = pack8(st[kb], e2 * 8);
 #pragma unroll
         for (int db = 0; db < ND; ++db)
-          dq[db] = mfma32x32x16(tfrag(kt_lds, db * 32 + l32, kb * 32 + e2 * 16, g), dsb, dq[db]);
+          dq[db] = mfma32x32x16(frag_outer<64>(kt_lds, db * 32, kb * 2 + e2, lane), dsb, dq[db]);
       }
   }
 

@@ -100,6 +100,64 @@ struct Tile64 {
 };
 
 
+// ------------------------------------------------- DMA-staged tiles
+// A tile of R rows (keys or queries) x D columns goes from HBM to LDS by DMA
+// (buffer_load ... lds, 64 lanes x 16 bytes = 1 KB per load), in one of two
+// layouts:
+//   rows  (OUTER = false): [R][D], rows of 2D bytes, 16-byte chunk c of row r
+//         at slot c ^ rowswz<D>(r); MFMA fragments by row_frag;
+//   outer (OUTER = true):  [D / 64][R][64], row rho of a 64-column block
+//         holding tile row perm16(rho), chunk c at slot c ^ oswz(rho);
+//         fragments of the transpose by frag_outer<R>.
+// perm16 swaps rows 4..7 and 8..11 inside every 16.  A 32 x 32 MFMA
+// accumulator holds, per lane and 16-row step, rows 4g..4g+3 and 8+4g..8+4g+3
+// (g = lane / 32); packed as the B operand of a second product it therefore
+// runs over the rows in perm16 order, and the outer tile's rows are stored in
+// that order so that both operands agree.  The source row of each lane applies
+// the swizzle and the permutation; rows at or beyond the operand's end read
+// as zeros (buffer range check).
+__device__ __forceinline__ int perm16(int r) {
+  const int p = r & 15;
+  return (r & ~15) | ((p >= 4 && p < 12) ? (p ^ 12) : p);
+}
+
+template <int D, int R, bool OUTER>
+struct TileDma {
+  static constexpr int NL = R * D * 2 / 1024;  // loads per tile
+  static constexpr int LPW = NL / 4;            // ... per wave
+  static_assert(LPW >= 1 && NL % 4 == 0, "tile too small for four waves");
+  i32x4 desc;
+  int off[LPW];  // per-lane byte offsets at tile row 0
+  int ld;
+
+  // rows of the operand at base + row * ld_ (elements), nrows of them
+  __device__ __forceinline__ void init(const u16* base, int ld_, int nrows, int wave, int lane) {
+    ld = ld_;
+    desc = make_desc(base, static_cast<uint32_t>(((nrows - 1) * ld + D) * 2));
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int inst = wave * LPW + i;
+      if constexpr (!OUTER) {
+        constexpr int CPR = 2 * D / 16;  // chunks per row
+        const int r = inst * (64 / CPR) + lane / CPR;
+        const int c = (lane % CPR) ^ rowswz<D>(r);
+        off[i] = (r * ld + c * 8) * 2;
+      } else {
+        constexpr int LPB = R / 8;  // loads per 64-column block
+        const int blk = inst / LPB, rho = (inst % LPB) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ oswz(rho);
+        off[i] = (perm16(rho) * ld + blk * 64 + c * 8) * 2;
+      }
+    }
+  }
+  // tile rows row0 .. row0 + R - 1 into LDS bytes [lds, lds + 2 R D)
+  __device__ __forceinline__ void issue(uint32_t lds, int row0, int wave) const {
+    const int soff = row0 * ld * 2;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) lds_dma16(desc, lds + (wave * LPW + i) * 1024, off[i], soff);
+  }
+};
+
 // ------------------------------------------------------- row splitting
 // A "row" is one 128-wide block of queries (forward, dQ) or keys (dK/dV);
 // it walks tiles of 64 along the other axis.  Under a causal mask the rows

@@ -6,67 +6,10 @@ namespace ptb {
 namespace {
 
 // ------------------------------------------------------------------ forward
-// Stage of 64 keys in LDS, filled by DMA (buffer_load ... lds) one tile ahead
-// of the matrix cores, two stages:
-//   K, K_lo: [64 keys][D], rows of 2D bytes; 16-byte chunk c of row r at
-//            slot c ^ rowswz<D>(r) (read by row_frag);
-//   V:       [D / 64 blocks][64 kappa][64 d], read transposed by
-//            frag_outer64.  Row kappa holds key perm16(kappa): inside each 16,
-//            keys 4..7 and 8..11 trade places, which is the key order of the
-//            S^T accumulator packed as the B operand of O^T = V^T P^T.
-// A 1 KB DMA load (64 lanes x 16 bytes) fills 1 KB of a tile; the source of
-// each lane applies the swizzle and the permutation.
+// Stage of 64 keys in LDS, filled by DMA one tile ahead of the matrix cores,
+// two stages: K and K_lo row-major (read by row_frag), V in the outer layout
+// with its rows in the S^T accumulator's key order (read transposed).
 constexpr float kStale = 8.0f;
-
-__device__ __forceinline__ int perm16(int kappa) {
-  const int p = kappa & 15;
-  return (kappa & ~15) | ((p >= 4 && p < 12) ? (p ^ 12) : p);
-}
-
-template <int D>
-struct KvDma {
-  static constexpr int OPB = 64 * D;   // u16 elements of one operand's tile
-  static constexpr int NL = D / 8;     // 1 KB loads per operand tile
-  static constexpr int LPW = NL / 4;   // ... per wave
-  static constexpr int RB = 2 * D;     // bytes per K row
-  static constexpr int RPL = 1024 / RB;  // K rows per load
-  i32x4 dk, dkl, dv;
-  int ok[LPW], okl[LPW], ov[LPW];      // per-lane byte offsets at key 0
-  int ld, ldl;
-
-  // K, K_lo and V of one (batch, head): row stride ld (K, V) and ldl (K_lo),
-  // s rows; rows at or beyond s read as zeros.
-  __device__ __forceinline__ void init(const u16* K, const u16* Kl, const u16* V, int ld_, int ldl_,
-                                       int s, int wave, int lane) {
-    ld = ld_;
-    ldl = ldl_;
-    dk = make_desc(K, static_cast<uint32_t>(((s - 1) * ld + D) * 2));
-    dkl = make_desc(Kl, static_cast<uint32_t>(((s - 1) * ldl + D) * 2));
-    dv = make_desc(V, static_cast<uint32_t>(((s - 1) * ld + D) * 2));
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int inst = wave * LPW + i;
-      const int r = inst * RPL + lane / (RB / 16);
-      const int c = (lane % (RB / 16)) ^ rowswz<D>(r);
-      ok[i] = (r * ld + c * 8) * 2;
-      okl[i] = (r * ldl + c * 8) * 2;
-      const int blk = inst >> 3, kap = (inst & 7) * 8 + (lane >> 3);
-      const int cv = (lane & 7) ^ oswz(kap);
-      ov[i] = (perm16(kap) * ld + blk * 64 + cv * 8) * 2;
-    }
-  }
-  // the tile of keys kt0 .. kt0 + 63 into the stage at LDS byte address lds
-  __device__ __forceinline__ void issue(uint32_t lds, int kt0, int wave) const {
-    const int sk = kt0 * ld * 2, skl = kt0 * ldl * 2;
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const uint32_t off = (wave * LPW + i) * 1024;
-      lds_dma16(dk, lds + off, ok[i], sk);
-      lds_dma16(dkl, lds + OPB * 2 + off, okl[i], skl);
-      lds_dma16(dv, lds + 2 * OPB * 2 + off, ov[i], sk);
-    }
-  }
-};
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ qkv,
@@ -75,7 +18,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ q
                                                        float* __restrict__ lse, int s, int n,
                                                        int window, int nqt, RowSplit rs) {
   constexpr int NKS = D / 16, ND = D / 32;
-  constexpr int OPB = KvDma<D>::OPB;
+  constexpr int OPB = 64 * D;  // u16 elements of one operand's tile
   __shared__ __attribute__((aligned(1024))) u16 kv[2 * 3 * OPB];
   __shared__ int arrival;
 
@@ -96,10 +39,18 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ q
 
   const int kv_begin = item.span.begin;
   const int kv_end = item.span.end;
-  KvDma<D> dma;
-  dma.init(Kg, Klg, Vg, ld, 2 * hl, s, wave, lane);
+  TileDma<D, 64, false> dk, dkl;
+  TileDma<D, 64, true> dv;
+  dk.init(Kg, ld, s, wave, lane);
+  dkl.init(Klg, 2 * hl, s, wave, lane);
+  dv.init(Vg, ld, s, wave, lane);
   const uint32_t kv_lds = __builtin_amdgcn_readfirstlane(lds_address(kv));
-  if (kv_begin < kv_end) dma.issue(kv_lds, kv_begin, wave);
+  auto issue = [&](uint32_t lds, int kt0) {
+    dk.issue(lds, kt0, wave);
+    dkl.issue(lds + OPB * 2, kt0, wave);
+    dv.issue(lds + 2 * OPB * 2, kt0, wave);
+  };
+  if (kv_begin < kv_end) issue(kv_lds, kv_begin);
 
   bf16x8 qf[NKS], ql[NKS];
 #pragma unroll
@@ -126,7 +77,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ q
   for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKV) {
     wait_vm_lds<0>();  // this wave's loads of tile kt0 landed
     __syncthreads();   // every wave's; the other stage is free again
-    if (kt0 + BKV < kv_end) dma.issue(kv_lds + (stage ^ 1) * (3 * OPB * 2), kt0 + BKV, wave);
+    if (kt0 + BKV < kv_end) issue(kv_lds + (stage ^ 1) * (3 * OPB * 2), kt0 + BKV);
     const u16* k_lds = kv + stage * 3 * OPB;
     const u16* kl_lds = k_lds + OPB;
     const u16* v_lds = k_lds + 2 * OPB;
@@ -207,7 +158,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ q
         const bf16x8 pb = pack8(st[kb], e2 * 8);
 #pragma unroll
         for (int db = 0; db < ND; ++db)
-          o[db] = mfma32x32x16(frag_outer64(v_lds, db * 32, kb * 2 + e2, lane), pb, o[db]);
+          o[db] = mfma32x32x16(frag_outer<64>(v_lds, db * 32, kb * 2 + e2, lane), pb, o[db]);
       }
   }
 

@@ -215,7 +215,7 @@ __device__ __forceinline__ bf16x8 frag(const u16* tile, int rb, int ks, int lane
     return as_bf16x8(*reinterpret_cast<const uint4*>(tile + r * BK + ((c ^ kswz(r)) << 3)));
   } else {
     static_assert(BK == 64, "outer-contiguous tiles are [64][64 k][64]");
-    return frag_outer64(tile, rb, ks, lane);
+    return frag_outer<BK>(tile, rb, ks, lane);
   }
 }
 

@@ -76,7 +76,7 @@ __device__ __forceinline__ v4s lds_read_tr16(const u16* p) {
 #endif
 }
 
-// Tiles stored outer-contiguous as [64-wide outer block][64 k][64 outer]
+// Tiles stored outer-contiguous as [64-wide outer block][KR k][64 outer]
 // (128-byte rows): chunk c of k-row kk sits at chunk slot c ^ oswz(kk).
 __device__ __forceinline__ int oswz(int kk) { return (kk & 2) << 1; }
 
@@ -84,14 +84,15 @@ __device__ __forceinline__ int oswz(int kk) { return (kk & 2) << 1; }
 // [rb, rb + 32), k-step ks (16 k); lane l gets X[rb + l % 32][16 ks + 8 (l / 32)
 // .. +7].  Each 16-lane group reads 4 k-rows x 16 outer indices (4 u16 per
 // lane), and the transposing read hands lane i the 4 k-values of its index.
-__device__ __forceinline__ bf16x8 frag_outer64(const u16* tile, int rb, int ks, int lane) {
+template <int KR>
+__device__ __forceinline__ bf16x8 frag_outer(const u16* tile, int rb, int ks, int lane) {
   const int q = lane >> 4, j = lane & 15;
   const int m = rb + 16 * (q & 1) + 4 * (j & 3);
   v4s h[2];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     const int kk = ks * 16 + 8 * (q >> 1) + 4 * hh + (j >> 2);
-    h[hh] = lds_read_tr16(tile + (m >> 6) * (64 * 64) + kk * 64 + ((((m >> 3) & 7) ^ oswz(kk)) << 3) +
+    h[hh] = lds_read_tr16(tile + (m >> 6) * (KR * 64) + kk * 64 + ((((m >> 3) & 7) ^ oswz(kk)) << 3) +
                           (m & 7));
   }
   uint4 u;
