@@ -68,22 +68,28 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const u16* __restrict__
 }
 
 // ------------------------------------------------------------ dK and dV
+// Key rows of 128 (4 waves x 32, lane = key), query stages of QS = 32 staged
+// by DMA one stage ahead, two stages of five tiles: Q, Q_lo and dO row-major
+// (A operands of S = Q K^T and dP = dO V^T) and Q and dO once more in the
+// outer layout, rows in the accumulator's order, for the transposed A
+// operands of dK^T += Q^T dS and dV^T += dO^T P.  The stage's log-sum-exp
+// and delta go to LDS through registers, loaded one stage ahead.
+constexpr int QS = 32;
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const u16* __restrict__ qkv, const u16* __restrict__ qk_lo, const u16* __restrict__ dcg,
     const float* __restrict__ lse, const float* __restrict__ delta, u16* __restrict__ dz,
     int ld_dz, int s, int n, int window, int nkt, RowSplit rsp) {
   constexpr int NKS = D / 16, ND = D / 32;
+  constexpr int OPB = QS * D;  // u16 elements of one operand's tile
+  constexpr int STG = 5 * OPB;
+  __shared__ __attribute__((aligned(1024))) u16 qs[2 * STG];
+  __shared__ __attribute__((aligned(16))) float ld_lds[2][2][QS];  // [stage][lse, delta][query]
   __shared__ int arrival;
-  __shared__ __attribute__((aligned(16))) u16 q_lds[BQB * D];
-  __shared__ __attribute__((aligned(16))) u16 ql_lds[BQB * D];
-  __shared__ __attribute__((aligned(16))) u16 qt_lds[D * BQB];
-  __shared__ __attribute__((aligned(16))) u16 do_lds[BQB * D];
-  __shared__ __attribute__((aligned(16))) u16 dot_lds[D * BQB];
-  __shared__ float lse_lds[BQB];
-  __shared__ float dl_lds[BQB];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int hd = blockIdx.y, bi = blockIdx.z;
   const int hl = n * D, ld = 3 * hl;
@@ -98,6 +104,35 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const RowItem item = decode_row_item<false>(static_cast<int>(blockIdx.x), nkt, s, window, rsp.ch);
   if (item.nchunks == 0) return;
   const int kb0 = item.row * BKB, kw0 = kb0 + wave * 32, kj = kw0 + l32;
+
+  const int q_begin = item.span.begin;
+  const int q_end = item.span.end;
+  TileDma<D, QS, false> dq_r, dql_r, do_r;
+  TileDma<D, QS, true> dq_t, do_t;
+  dq_r.init(Qg, ld, s, wave, lane);
+  dql_r.init(Qlg, 2 * hl, s, wave, lane);
+  do_r.init(dOg, hl, s, wave, lane);
+  dq_t.init(Qg, ld, s, wave, lane);
+  do_t.init(dOg, hl, s, wave, lane);
+  const uint32_t qs_lds = __builtin_amdgcn_readfirstlane(lds_address(qs));
+  auto issue = [&](uint32_t lds, int qt0) {
+    dq_r.issue(lds, qt0, wave);
+    dql_r.issue(lds + OPB * 2, qt0, wave);
+    do_r.issue(lds + 2 * OPB * 2, qt0, wave);
+    dq_t.issue(lds + 3 * OPB * 2, qt0, wave);
+    do_t.issue(lds + 4 * OPB * 2, qt0, wave);
+  };
+  // log-sum-exp (threads 0..31) and delta (32..63) of one stage's queries
+  auto load_ld = [&](int qt0) {
+    const int q = qt0 + (tid & 31);
+    return (tid < 64 && q < s) ? (tid < 32 ? lse_h[q] : dl_h[q]) : 0.0f;
+  };
+  float ldv = 0.0f;
+  if (q_begin < q_end) {
+    issue(qs_lds, q_begin);
+    ldv = load_ld(q_begin);
+    if (tid < 64) ld_lds[0][tid >> 5][tid & 31] = ldv;
+  }
 
   bf16x8 kf[NKS], kl[NKS], vf[NKS];
 #pragma unroll
@@ -119,63 +154,64 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) { dv[db][e] = 0.0f; dk[db][e] = 0.0f; }
 
-  const int q_begin = item.span.begin;
-  const int q_end = item.span.end;
-  // The next query tile is loaded into registers while the current one is
-  // computed from LDS.
-  Tile64<D> qtile, qltile, otile;
-  if (q_begin < q_end) {
-    qtile.load(Qg, ld, q_begin, s, tid);
-    qltile.load(Qlg, 2 * hl, q_begin, s, tid);
-    otile.load(dOg, hl, q_begin, s, tid);
-  }
-  for (int qt0 = q_begin; qt0 < q_end; qt0 += BQB) {
-    __syncthreads();  // every wave is done with the previous tile in LDS
-    qtile.store_rows(q_lds, tid);
-    qltile.store_rows(ql_lds, tid);
-    qtile.store_transposed(qt_lds, tid);
-    otile.store_rows(do_lds, tid);
-    otile.store_transposed(dot_lds, tid);
-    if (tid < BQB) {
-      const int q = qt0 + tid;
-      lse_lds[tid] = q < s ? lse_h[q] : 0.0f;
-      dl_lds[tid] = q < s ? dl_h[q] : 0.0f;
+  int stage = 0;
+  for (int qt0 = q_begin; qt0 < q_end; qt0 += QS) {
+    wait_vm_lds<0>();  // this wave's loads of stage qt0 landed (and its lse/delta stores)
+    __syncthreads();   // every wave's; the other stage is free again
+    const bool more = qt0 + QS < q_end;
+    if (more) {
+      issue(qs_lds + (stage ^ 1) * (STG * 2), qt0 + QS);
+      ldv = load_ld(qt0 + QS);
     }
-    __syncthreads();
-    if (qt0 + BQB < q_end) {
-      qtile.load(Qg, ld, qt0 + BQB, s, tid);
-      qltile.load(Qlg, 2 * hl, qt0 + BQB, s, tid);
-      otile.load(dOg, hl, qt0 + BQB, s, tid);
-    }
+    const u16* q_lds = qs + stage * STG;
+    const u16* ql_lds = q_lds + OPB;
+    const u16* do_lds = q_lds + 2 * OPB;
+    const u16* qt_lds = q_lds + 3 * OPB;
+    const u16* dot_lds = q_lds + 4 * OPB;
+    const float* lse_s = ld_lds[stage][0];
+    const float* dl_s = ld_lds[stage][1];
 
-    const bool any = kw0 < s && qt0 + BQB - 1 >= kw0 && qt0 - (kw0 + 31) < window;
-    if (!any) continue;
-    const bool full = qt0 >= kw0 + 31 && qt0 + BQB - 1 - kw0 < window && qt0 + BQB <= s;
-
-    // the two 32-query halves one after the other (fewer live registers)
-#pragma unroll 1
-    for (int qb = 0; qb < 2; ++qb) {
+    const bool any = kw0 < s && qt0 + QS - 1 >= kw0 && qt0 - (kw0 + 31) < window;
+    if (any) {
+      const bool full = qt0 >= kw0 + 31 && qt0 + QS - 1 - kw0 < window && qt0 + QS <= s;
       f32x16 sp, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) { sp[e] = 0.0f; dp[e] = 0.0f; }
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 qh = row_frag<D>(q_lds, qb * 32 + l32, ks * 2 + g);
+        const bf16x8 qh = row_frag<D>(q_lds, l32, ks * 2 + g);
         sp = mfma32x32x16(qh, kf[ks], sp);
-        sp = mfma32x32x16(row_frag<D>(ql_lds, qb * 32 + l32, ks * 2 + g), kf[ks], sp);
+        sp = mfma32x32x16(row_frag<D>(ql_lds, l32, ks * 2 + g), kf[ks], sp);
         sp = mfma32x32x16(qh, kl[ks], sp);
-        dp = mfma32x32x16(row_frag<D>(do_lds, qb * 32 + l32, ks * 2 + g), vf[ks], dp);
+        dp = mfma32x32x16(row_frag<D>(do_lds, l32, ks * 2 + g), vf[ks], dp);
       }
+      if (!full) {
+        // a stage on the diagonal or the window's edge: keep queries in
+        // [lo, hi] of this lane's key, as offsets from the lane's first query
+        asm volatile("; masked query stage");  // keeps this path a real branch
+        const int base = qt0 + g * 4;
+        const int lo = kj - base;
+        const int hi = min(kj + window - 1, s - 1) - base;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int lq = qb * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
-        float p = exp2f(sp[e] * sc - lse_lds[lq]);
-        if (!full) {
-          const int diff = qt0 + lq - kj;
-          if (diff < 0 || diff >= window || qt0 + lq >= s) p = 0.0f;
+        for (int e = 0; e < 16; ++e) {
+          const int off = (e >> 2) * 8 + (e & 3);
+          if (off < lo || off > hi) sp[e] = -INFINITY;
         }
-        sp[e] = p;
-        dp[e] = p * (dp[e] - dl_lds[lq]);
+      }
+      // accumulator element e holds query 8 (e / 4) + 4 g + e % 4
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 lv = *reinterpret_cast<const float4*>(lse_s + 8 * j + 4 * g);
+        const float4 dlv = *reinterpret_cast<const float4*>(dl_s + 8 * j + 4 * g);
+        const float lq[4] = {lv.x, lv.y, lv.z, lv.w};
+        const float dq[4] = {dlv.x, dlv.y, dlv.z, dlv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * j + i;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sp[e], sc, -lq[i]));
+          sp[e] = p;
+          dp[e] = p * (dp[e] - dq[i]);
+        }
       }
 #pragma unroll
       for (int e2 = 0; e2 < 2; ++e2) {
@@ -183,11 +219,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
         const bf16x8 dsb = pack8(dp, e2 * 8);
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
-          dv[db] = mfma32x32x16(tfrag(dot_lds, db * 32 + l32, qb * 32 + e2 * 16, g), pb, dv[db]);
-          dk[db] = mfma32x32x16(tfrag(qt_lds, db * 32 + l32, qb * 32 + e2 * 16, g), dsb, dk[db]);
+          dv[db] = mfma32x32x16(frag_outer<QS>(dot_lds, db * 32, e2, lane), pb, dv[db]);
+          dk[db] = mfma32x32x16(frag_outer<QS>(qt_lds, db * 32, e2, lane), dsb, dk[db]);
         }
       }
     }
+    // the next stage's log-sum-exp and delta (every wave done with that stage)
+    if (more && tid < 64) ld_lds[stage ^ 1][tid >> 5][tid & 31] = ldv;
+    stage ^= 1;
   }
 
   if (item.nchunks > 1) {
