@@ -52,7 +52,10 @@ constexpr int NSTAGE = 2;
 constexpr int STAGE = 2 * TILE * BK;       // u16 elements: A tile, then B tile (64 KB)
 constexpr int EPI_LD = 36;                 // fp32 row stride of the epilogue staging
 constexpr int GM = 8;                      // tile rows per L2 group
-constexpr int FM = 4, FN = 4;              // 32 x 32 MFMA blocks per wave
+constexpr int WAVES = 8;                   // 2 per SIMD: 2 (rows) x 4 (columns)
+constexpr int LOADERS = 4;                 // waves 0-3 issue every DMA load
+constexpr int WM = 128, WN = 64;           // outputs per wave
+constexpr int FM = WM / 32, FN = WN / 32;  // 32 x 32 MFMA blocks per wave
 constexpr int PARTIAL_FLOATS = TILE * TILE;
 
 // k-contiguous stage tile [256 rows][64 k]: 128-byte rows, 16-byte chunk c of
@@ -62,7 +65,8 @@ constexpr int PARTIAL_FLOATS = TILE * TILE;
 __device__ __forceinline__ int kswz(int r) { return (r >> 1) & 7; }
 
 // The DMA of one operand's stage tile: 32 KB = 32 loads of 1 KB, eight per
-// wave, each a run of whole 128-byte lines.  Load i of wave w (inst = 8w + i)
+// loader wave, each a run of whole 128-byte lines.  Load i of loader wave w
+// (inst = 8w + i)
 // fills LDS bytes [1 KB * inst, +1 KB):
 //   k-contiguous:     rows 8*inst .. +7, all 64 k;
 //   outer-contiguous: k-rows 8*(inst%8) .. +7 of outer block inst/8 (64 wide).
@@ -133,9 +137,75 @@ struct StageLoader {
   }
 };
 
+// The same DMA with per-lane offsets by load parity (eight-wave kernel, where
+// registers are scarcer): within a wave the swizzle depends on the load only
+// through its parity (k-contiguous) or not at all (outer-contiguous), so a
+// lane needs two offsets per segment and the rest of each load's address is
+// wave-uniform (soffset).
+template <int MAJ>
+struct StageLoaderP {
+  int vA[2], vB[2];  // per-lane byte offsets in segment A / B, [load parity]
+  i32x4 dA, dB;      // buffer resources of segments A and B
+  int ldA, ldB;      // leading dimensions (the k stride of outer-contiguous tiles)
+  int rowA, rowB;    // k-contiguous: the wave's first row inside segment A / B
+  int split, split_on_k;
+
+  // segment A: segment 0 of a k-split operand, else the wave's segment;
+  // segment B: segment 1 of a k-split operand, else the wave's segment
+  __device__ __forceinline__ void init(const Operand& op, int r0, int wave, int lane) {
+    const int ld0 = __builtin_amdgcn_readfirstlane(op.ld0);
+    const int ld1 = __builtin_amdgcn_readfirstlane(op.ld1);
+    split = __builtin_amdgcn_readfirstlane(op.split);
+    split_on_k = __builtin_amdgcn_readfirstlane(op.split_on_k);
+    const int wseg = (!split_on_k && r0 + 64 * wave >= split) ? 1 : 0;
+    const bool a1 = !split_on_k && wseg;
+    const bool b1 = split_on_k || wseg;
+    const i32x4 d0 = make_desc(op.p0, op.bytes0), d1 = make_desc(op.p1, op.bytes1);
+    dA = a1 ? d1 : d0;
+    dB = b1 ? d1 : d0;
+    ldA = a1 ? ld1 : ld0;
+    ldB = b1 ? ld1 : ld0;
+    const int outer_shift = wseg ? split : 0;  // outer index origin of the wave's segment
+    const int lr = lane >> 3;
+    if constexpr (MAJ == KMAJOR) {
+      // load i covers rows 64 * wave + 8 * i + lr
+      rowA = rowB = r0 + 64 * wave - outer_shift;
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        const int c = (lane & 7) ^ kswz(8 * par + lr);
+        vA[par] = (lr * ldA + c * 8) * 2;
+        vB[par] = (lr * ldB + c * 8) * 2;
+      }
+    } else {
+      // load i covers k-rows 8 * i + lr of outer block `wave`
+      rowA = rowB = 0;
+      const int c = (lane & 7) ^ oswz(lr);
+      const int col = r0 + 64 * wave + c * 8 - outer_shift;
+      vA[0] = vA[1] = (lr * ldA + col) * 2;
+      vB[0] = vB[1] = (lr * ldB + col) * 2;
+    }
+  }
+
+  // as StageLoader::issue
+  __device__ __forceinline__ void issue(uint32_t lds, int wave, int k0, bool valid) const {
+    const bool kseg = split_on_k && k0 >= split;
+    const int krel = kseg ? k0 - split : k0;
+    const int ld = kseg ? ldB : ldA;
+    const int row = kseg ? rowB : rowA;
+    const i32x4 d = kseg ? dB : dA;
+    const int v0 = kseg ? vB[0] : vA[0], v1 = kseg ? vB[1] : vA[1];
+    int soff = (MAJ == KMAJOR) ? (row * ld + krel) * 2 : krel * ld * 2;
+    int step = 16 * ld;  // 8 rows (or 8 k-rows) further per load
+    if (!valid) { soff = kOutOfRange; step = 0; }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      lds_dma16(d, lds + (wave * 8 + i) * 1024, (i & 1) ? v1 : v0, soff + i * step);
+  }
+};
+
 // The same stage tile loaded through registers instead (global -> VGPR ->
-// ds_write_b128): load i of wave w carries the same 1 KB as DMA load 8w + i
-// and is written to the same LDS bytes.  The lane's offset depends only on
+// ds_write_b128; used by the four-wave kernel): load i of wave w carries the
+// same 1 KB as DMA load 8w + i and is written to the same LDS bytes.  The lane's offset depends only on
 // the lane (and, for k-contiguous tiles, on the parity of i); the rest is
 // wave-uniform and goes in soffset, which the buffer range check includes
 // like the lane offset (zeros past the end, out-of-range loads included).
@@ -208,11 +278,29 @@ struct RegLoader {
 
 // MFMA operand fragment for rows (or columns) [rb, rb + 32) and k-step ks
 // (16 k) of a stage tile: lane l gets X[rb + l % 32][16 ks + 8 (l / 32) .. +7].
+// For k-contiguous tiles koff is the lane's element offset of k-step ks in any
+// 32-row block (rb a multiple of 32 leaves the swizzle unchanged), so a
+// fragment's address is one register plus an immediate.
+__device__ __forceinline__ int kfrag_offset(int ks, int lane) {
+  const int r = lane & 31, c = ks * 2 + (lane >> 5);
+  return r * BK + ((c ^ kswz(r)) << 3);
+}
+
+// The same fragment with the address computed in full (four-wave kernel).
 template <int MAJ>
-__device__ __forceinline__ bf16x8 frag(const u16* tile, int rb, int ks, int lane) {
+__device__ __forceinline__ bf16x8 frag4(const u16* tile, int rb, int ks, int lane) {
   if constexpr (MAJ == KMAJOR) {
     const int r = rb + (lane & 31), c = ks * 2 + (lane >> 5);
     return as_bf16x8(*reinterpret_cast<const uint4*>(tile + r * BK + ((c ^ kswz(r)) << 3)));
+  } else {
+    return frag_outer<BK>(tile, rb, ks, lane);
+  }
+}
+
+template <int MAJ>
+__device__ __forceinline__ bf16x8 frag(const u16* tile, int rb, int ks, int lane, int koff) {
+  if constexpr (MAJ == KMAJOR) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(tile + rb * BK + koff));
   } else {
     static_assert(BK == 64, "outer-contiguous tiles are [64][64 k][64]");
     return frag_outer<BK>(tile, rb, ks, lane);
@@ -412,8 +500,239 @@ __device__ __forceinline__ int part_slot(const SkPlan& pl, int i) {
 }
 
 template <int AMAJ, int BMAJ, int MODE>
-__global__ __launch_bounds__(256, 1) void gemm_sk_kernel(SkPlan pl) {
-  constexpr int WM = 128, WN = 128;
+__global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
+  constexpr int RA = (AMAJ == KMAJOR) ? FM : 2 * FM;  // LDS read instructions per k-step
+  constexpr int RB = (BMAJ == KMAJOR) ? FN : 2 * FN;
+  // Two stages of 64 KB.  The epilogue's staging area (8 waves x 32 rows x
+  // EPI_LD fp32) lies in stage 1, which is idle from an item's last k-step
+  // until the next item's second stage tile goes out after the epilogue.
+  __shared__ __attribute__((aligned(1024))) u16 ring[NSTAGE * STAGE];
+  __shared__ int arrival;
+  float* const epi_stage = reinterpret_cast<float*>(ring + STAGE);
+  static_assert(WAVES * 32 * EPI_LD * 4 <= STAGE * 2, "epilogue staging fits in one stage");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const bool loader = wave < LOADERS;
+
+  // Workgroups go round-robin over the 8 XCDs; virtual id v gives each XCD a
+  // contiguous run of ranges.
+  const int G = gridDim.x;
+  int v;
+  {
+    const int xcd = blockIdx.x % 8, loc = blockIdx.x / 8;
+    const int base = G / 8, rem = G % 8;
+    v = xcd * base + min(xcd, rem) + loc;
+  }
+  if (v >= pl.nitems) return;
+  StageLoaderP<AMAJ> la;
+  StageLoaderP<BMAJ> lb;
+  int item = v;
+  Item s = decode_item(pl, item);
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_address(ring));
+
+  auto setup = [&](const Item& sg) {
+    const GemmProblem& P = pl.p[sg.prob];
+    la.init(P.A, sg.m0, wave, lane);
+    lb.init(P.B, sg.n0, wave, lane);
+  };
+  // stage tile j of an item (k-step kb + j) into ring slot `slot`, by the
+  // loader waves; past the item's end the loads are out of range (zeros, no
+  // memory traffic)
+  auto issue_to = [&](const Item& sg, int slot, int j) {
+    if (!loader) return;
+    const bool valid = j < sg.len;
+    const int k0 = (sg.kb + (valid ? j : 0)) * BK;
+    const uint32_t lds = ring_lds + slot * (STAGE * 2);
+    la.issue(lds, wave, k0, valid);
+    lb.issue(lds + TILE * BK * 2, wave, k0, valid);
+  };
+
+  int koff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) koff[ks] = kfrag_offset(ks, lane);
+  f32x16 acc[FM][FN];
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto rd = [&](const u16* st, int ks, int slot) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[slot][i] = frag<AMAJ>(st, wm * WM + i * 32, ks, lane, koff[ks]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[slot][j] = frag<BMAJ>(st + TILE * BK, wn * WN + j * 32, ks, lane, koff[ks]);
+  };
+  auto mma = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(fa[slot][i], fb[slot][j], acc[i][j]);
+  };
+  // LDS reads of the next k-step spread between this k-step's MFMAs
+  auto pin = [&]() {
+    constexpr int R = RA + RB;
+#pragma unroll
+    for (int i = 0; i < (R < FM * FN ? R : FM * FN); ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    }
+    if constexpr (R < FM * FN) __builtin_amdgcn_sched_group_barrier(SG_MFMA, FM * FN - R, 0);
+    if constexpr (R > FM * FN) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, R - FM * FN, 0);
+  };
+
+  setup(s);
+  issue_to(s, 0, 0);
+  issue_to(s, 1, 1);
+  for (;;) {
+    // ---- main loop over the item's 64-wide k-steps, two stages: step j
+    // computes stage tile j (4 MFMA k-steps of 16) while tile j+1 streams
+    // in, then waits for it, and after the barrier the loads of tile j+2 go
+    // into the stage just read (out of range past the item's end, so the
+    // loop has no branch and no MFMA under one).  Fragments of the next
+    // 16-wide k-step are read under the MFMAs of the current one.  Two waves
+    // share each SIMD, so one wave's MFMAs cover the other's waits.
+    const int len = s.len;
+    // Every memory operation of this wave done, the first stage tiles
+    // included.  A clean slate also keeps the compiler's own wait counting
+    // from carrying the epilogue's loads and stores into the loop.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    rd(ring, 0, 0);
+    for (int j = 0; j < len; ++j) {
+      u16* cur = ring + (j & 1) * STAGE;
+      rd(cur, 1, 1);
+      mma(0);
+      pin();
+      rd(cur, 2, 0);
+      mma(1);
+      pin();
+      rd(cur, 3, 1);
+      mma(0);
+      pin();
+      wait_vm_lds<0>();  // tile j+1 landed (the loader waves' loads)
+      __syncthreads();   // tile j+1 in LDS for every wave; tile j read by every wave
+      issue_to(s, j & 1, j + 2);
+      rd(ring + ((j + 1) & 1) * STAGE, 0, 0);  // unused after the last step
+      mma(1);
+      pin();
+    }
+
+    // ---- the next item's first stage tile goes out before this one's
+    // epilogue (into stage 0; stage 1 holds the epilogue's staging)
+    const int next = item + G;
+    const bool more = next < pl.nitems;
+    wait_vm_lds<0>();  // this item's trailing (out-of-range) loads are done
+    __syncthreads();   // and every wave is done reading the ring
+    Item nx;
+    if (more) {
+      nx = decode_item(pl, next);
+      setup(nx);
+      issue_to(nx, 0, 0);
+    }
+
+    // ---- finish the tile, one 32 x 32 block of each wave at a time: the
+    // block goes through the wave's LDS staging area, after which lane l
+    // holds row l / 2, columns 16 (l % 2) .. +15 of it.
+    //   phase 0 (tile made of several items): store this item's fp32
+    //     partial sums, then count it in; the last item to arrive goes on to
+    //     phase 1 with all the partials;
+    //   phase 1: the epilogue, on the sum of the tile's partials (in a fixed
+    //     order, so the result does not depend on the order of arrival).
+    // Partial slot layout: [wave][i][j][16 values][64 lanes] fp32.
+    {
+      const GemmProblem& P = pl.p[s.prob];
+      const Epilogue& e = P.epi;
+      const int lrow = lane & 31, lk = lane >> 5;
+      const int er = lane >> 1, ec = (lane & 1) * 16;
+      float* ep = epi_stage + wave * 32 * EPI_LD;
+      int nparts = 0;
+      for_each_part(pl, s.prob, s.tile, [&](int) { ++nparts; });
+      int phase = nparts > 1 ? 0 : 1;
+      bool summed = false;  // phase 1 on a sum of partials
+      const int my_slot = part_slot(pl, item);
+      for (;;) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+              ep[((q >> 2) * 8 + lk * 4 + (q & 3)) * EPI_LD + lrow] = acc[i][j][q];
+            __builtin_amdgcn_wave_barrier();
+            float vals[16];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const float4 x = *reinterpret_cast<const float4*>(ep + er * EPI_LD + ec + 4 * t);
+              vals[4 * t] = x.x; vals[4 * t + 1] = x.y; vals[4 * t + 2] = x.z; vals[4 * t + 3] = x.w;
+            }
+            __builtin_amdgcn_wave_barrier();
+            // this lane's 16 values of the block, element t at [t][lane]:
+            // each store or load of one t covers 256 contiguous bytes
+            const size_t boff = static_cast<size_t>(((wave * FM + i) * FN + j) * 1024 + lane);
+            if (phase == 0) {
+              float* pw = pl.partials + static_cast<size_t>(my_slot) * PARTIAL_FLOATS + boff;
+#pragma unroll
+              for (int t = 0; t < 16; ++t) store_coherent(pw + t * 64, vals[t]);
+            } else {
+              if (summed) {
+                bool first = true;
+                for_each_part(pl, s.prob, s.tile, [&](int part) {
+                  const float* pr =
+                      pl.partials + static_cast<size_t>(part_slot(pl, part)) * PARTIAL_FLOATS + boff;
+#pragma unroll
+                  for (int t = 0; t < 16; ++t) {
+                    const float x = load_coherent(pr + t * 64);
+                    vals[t] = first ? x : vals[t] + x;
+                  }
+                  first = false;
+                });
+              }
+              const int r0 = s.m0 + wm * WM + i * 32, cb = s.n0 + wn * WN + j * 32;
+              const int region = __builtin_amdgcn_readfirstlane(epi_region<MODE>(e, r0, cb));
+              const int r = r0 + er;
+              if (cb < P.N && r < P.M) epi_row16<MODE>(e, region, r, cb + ec, vals);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        if (phase == 1) break;
+        // The partial is written at device scope (past the XCD's own L2);
+        // every store of it has completed before the item counts itself in.
+        wait_vm_lds<0>();
+        __syncthreads();
+        if (tid == 0) arrival = atomicAdd(pl.counters + s.gtile, 1);
+        __syncthreads();
+        const int arrived = __builtin_amdgcn_readfirstlane(arrival);
+        if (arrived != nparts - 1) break;  // another item finishes this tile
+        // last to arrive: the other partials are complete at device scope and
+        // are read at device scope
+        if (tid == 0) pl.counters[s.gtile] = 0;  // clean for the next launch
+        phase = 1;
+        summed = true;
+      }
+    }
+    if (!more) break;
+    __syncthreads();  // every wave done with the staging area in stage 1
+    issue_to(nx, 1, 1);
+    s = nx;
+    item = next;
+  }
+}
+
+// The four-wave kernel (one wave per SIMD, 128 x 128 outputs per wave),
+// kept for the two products whose operands are both k-contiguous (the dgrad
+// products): there A goes through registers (loaded at the start of a k-step,
+// written at its end) and B by DMA, which splits the operand stream over both
+// paths, and that measures faster than the eight-wave kernel's DMA-only
+// stream.  Same items, epilogue and partials as the eight-wave kernel.
+template <int AMAJ, int BMAJ, int MODE>
+__global__ __launch_bounds__(256, 1) void gemm_kernel4(SkPlan pl) {
+  constexpr int WM = 128, WN = 128, FM = 4, FN = 4;
   constexpr int RA = (AMAJ == KMAJOR) ? FM : 2 * FM;  // LDS read instructions per k-step
   constexpr int RB = (BMAJ == KMAJOR) ? FN : 2 * FN;
   __shared__ __attribute__((aligned(1024))) u16 ring[NSTAGE * STAGE];
@@ -487,9 +806,9 @@ __global__ __launch_bounds__(256, 1) void gemm_sk_kernel(SkPlan pl) {
   bf16x8 fa[2][FM], fb[2][FN];
   auto rd = [&](const u16* st, int ks, int slot) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) fa[slot][i] = frag<AMAJ>(st, wm * WM + i * 32, ks, lane);
+    for (int i = 0; i < FM; ++i) fa[slot][i] = frag4<AMAJ>(st, wm * WM + i * 32, ks, lane);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) fb[slot][j] = frag<BMAJ>(st + TILE * BK, wn * WN + j * 32, ks, lane);
+    for (int j = 0; j < FN; ++j) fb[slot][j] = frag4<BMAJ>(st + TILE * BK, wn * WN + j * 32, ks, lane);
   };
   auto mma = [&](int slot) {
 #pragma unroll
@@ -708,7 +1027,10 @@ bool operand_ok(const Operand& op) {
 
 template <int AMAJ, int BMAJ, int MODE>
 hipError_t launch_plan(const SkPlan& pl, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_sk_kernel<AMAJ, BMAJ, MODE>), dim3(grid), dim3(256), 0, s, pl);
+  if constexpr (AMAJ == KMAJOR && BMAJ == KMAJOR)
+    hipLaunchKernelGGL((gemm_kernel4<AMAJ, BMAJ, MODE>), dim3(grid), dim3(256), 0, s, pl);
+  else
+    hipLaunchKernelGGL((gemm_sk_kernel<AMAJ, BMAJ, MODE>), dim3(grid), dim3(64 * WAVES), 0, s, pl);
   return hipGetLastError();
 }
 

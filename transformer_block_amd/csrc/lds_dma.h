@@ -30,13 +30,20 @@ __device__ __forceinline__ i32x4 make_desc(const u16* p, uint32_t bytes) {
 // lds_addr + 16 * lane.  Written as inline assembly so that the compiler does
 // not treat it as an LDS store (it would then wait for every outstanding load
 // before any later LDS read); the kernel orders it with explicit vmcnt waits
-// and barriers.  m0 is written here and read only by the load right after it.
+// and barriers.  m0 is written here and read only by the load after it.
+// Wait states: the compiler does not apply its hazard rules to operands of
+// inline assembly, and the scalar operands here typically come from
+// v_readfirstlane just before.  A vector-memory instruction reading an SGPR
+// written by a VALU instruction needs 5 wait states, and one reading m0 after
+// s_mov needs 1; s_mov + s_nop 3 give 5 before the load.  Without them the
+// load can see a stale descriptor or offset: wrong data, or, when the range
+// check of an out-of-range load is lost with the descriptor, a memory fault.
 __device__ __forceinline__ void lds_dma16(i32x4 desc, uint32_t lds_addr, int voff, int soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
   i32x4 d;  // wave-uniform by construction; keep it in scalar registers
 #pragma unroll
   for (int k = 0; k < 4; ++k) d[k] = __builtin_amdgcn_readfirstlane(desc[k]);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 3\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(__builtin_amdgcn_readfirstlane(static_cast<int>(lds_addr))), "v"(voff),
                  "s"(d), "s"(__builtin_amdgcn_readfirstlane(soff))
