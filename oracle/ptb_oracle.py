@@ -10,7 +10,8 @@ is computed in float64 with plain numpy.
 Pages followed (cited by title and section):
   [MS]  Zhongzhu Zhou, "MegaScale: ByteDance 如何在 12,288 块 GPU 上实现 55% MFU
         的大规模 LLM 训练" (reading notes on MegaScale, NSDI'24):
-        section 1.1 eq (4) parallel block, eq (5)-(6) sliding-window attention;
+        section 1.1 eq (4) parallel block, eq (3) serial block (for
+        comparison), eq (5)-(6) sliding-window attention;
         section 1.3 flash attention as an exact re-tiling, selective recompute.
   [TP]  "Megatron-LM：张量并行与大规模训练": section 2.1 MLP ``Y = GeLU(XA)B``
         with ``A: [h,4h]``, ``B: [4h,h]``; section 2.2 fused QKV ``[b,s,3h]``
@@ -286,3 +287,66 @@ def ptb_stack_backward(dy: np.ndarray, caches: list,
         grads[li] = ptb_backward(dy, caches[li], params[li], window, fc)
         dy = grads[li]["dx"]
     return dy, grads
+
+
+# ---------------------------------------------------------------------------
+# Serial (standard) block, [MS] 1.1 eq (3), the block the parallel one
+# replaces.  Reading: the notes print eq (3) with x alone in the outer sum,
+# y = x + MLP(LN(x + Attn(LN(x)))), but describe the parallel block (eq (4))
+# as the standard one with LN(x) in place of LN(x + h2), h2 = Attn(LN(x)), as
+# the MLP's input and nothing else changed; eq (4) keeps h2 in the outer sum,
+# so the standard block is read with it there as well:
+#     a1 = LN1(x),  h2 = Attn(a1) W_o,  x1 = x + h2,
+#     y  = x1 + MLP(LN2(x1)),
+# the two LayerNorms with their own gamma and beta (p["ln_gamma"],
+# p["ln_beta"] for LN1 as in the parallel block, p["ln2_gamma"],
+# p["ln2_beta"] for LN2).
+# ---------------------------------------------------------------------------
+def serial_forward(x: np.ndarray, p: Dict[str, np.ndarray], batch: int, seq: int,
+                   heads: int, head_dim: int, window: int, eps: float,
+                   fc: FlopCounter | None = None):
+    """x: [T, h] -> (y, cache) for the serial block above."""
+    hl = heads * head_dim
+    a1, mu1, rstd1 = layernorm_forward(x, p["ln_gamma"], p["ln_beta"], eps)
+    qkv = _mm(a1, p["w_qkv"], fc)
+    q = split_heads(qkv[:, :hl], batch, seq, heads, head_dim)
+    k = split_heads(qkv[:, hl:2 * hl], batch, seq, heads, head_dim)
+    v = split_heads(qkv[:, 2 * hl:], batch, seq, heads, head_dim)
+    c = merge_heads(attention_forward(q, k, v, window, fc))
+    x1 = x + _mm(c, p["w_o"], fc)
+    a2, mu2, rstd2 = layernorm_forward(x1, p["ln2_gamma"], p["ln2_beta"], eps)
+    u = _mm(a2, p["w_fc1"], fc)
+    g = gelu(u)
+    y = x1 + _mm(g, p["w_fc2"], fc)
+    cache = dict(x=x, a1=a1, mu1=mu1, rstd1=rstd1, qkv=qkv, q=q, k=k, v=v, c=c,
+                 x1=x1, a2=a2, mu2=mu2, rstd2=rstd2, u=u, g=g)
+    return y, cache
+
+
+def serial_backward(dy: np.ndarray, cache: dict, p: Dict[str, np.ndarray],
+                    window: int, fc: FlopCounter | None = None) -> Dict[str, np.ndarray]:
+    """Gradients of serial_forward for upstream gradient dy [T, h]: the MLP
+    sub-block first, then the attention sub-block, each with its residual."""
+    # MLP sub-block: y = x1 + GeLU(LN2(x1) W_fc1) W_fc2
+    dg = _mm(dy, p["w_fc2"].T, fc)
+    dw_fc2 = _mm(cache["g"].T, dy, fc)
+    du = dg * gelu_grad(cache["u"])
+    dw_fc1 = _mm(cache["a2"].T, du, fc)
+    da2 = _mm(du, p["w_fc1"].T, fc)
+    dx1_ln, dgamma2, dbeta2 = layernorm_backward(da2, cache["x1"], p["ln2_gamma"],
+                                                 cache["mu2"], cache["rstd2"])
+    dx1 = dy + dx1_ln
+    # attention sub-block: x1 = x + Attn(LN1(x)) W_o
+    dc = _mm(dx1, p["w_o"].T, fc)
+    dw_o = _mm(cache["c"].T, dx1, fc)
+    q, k, v = cache["q"], cache["k"], cache["v"]
+    b, n, s, d = q.shape
+    dq, dk, dv = attention_backward(q, k, v, split_heads(dc, b, s, n, d), window, fc)
+    dqkv = np.concatenate([merge_heads(dq), merge_heads(dk), merge_heads(dv)], axis=1)
+    dw_qkv = _mm(cache["a1"].T, dqkv, fc)
+    da1 = _mm(dqkv, p["w_qkv"].T, fc)
+    dx_ln, dgamma1, dbeta1 = layernorm_backward(da1, cache["x"], p["ln_gamma"],
+                                                cache["mu1"], cache["rstd1"])
+    return dict(dx=dx1 + dx_ln, d_ln_gamma=dgamma1, d_ln_beta=dbeta1,
+                d_ln2_gamma=dgamma2, d_ln2_beta=dbeta2, dw_qkv=dw_qkv, dw_o=dw_o,
+                dw_fc1=dw_fc1, dw_fc2=dw_fc2)

@@ -19,7 +19,9 @@ beta = 0, dy ~ N(0,1); all drawn in fp32 with ``numpy.random.default_rng(seed)``
 and rounded to bf16 with round-to-nearest-even.  Draw order: x, then per layer
 (W_qkv, W_o, W_fc1, W_fc2), then dy.  An optional non-trivial gamma/beta
 (gamma ~ 1 + N(0, 0.1^2), beta ~ N(0, 0.1^2)) is drawn after dy, so it never
-changes the default streams.
+changes the default streams; the second LayerNorm of the serial block
+(``ln2_gamma``, ``ln2_beta``, unused by the parallel block) is drawn after
+that, layer by layer, so it changes nothing drawn before it either.
 """
 from __future__ import annotations
 
@@ -115,7 +117,8 @@ def make_inputs(w: Workload, seed: int | None = None,
 
     Returns a dict with ``x [T,h]``, ``dy [T,h]`` and a list ``layers`` of dicts
     holding ``ln_gamma [h]``, ``ln_beta [h]``, ``w_qkv [h, 3*h_l]``,
-    ``w_o [h_l, h]``, ``w_fc1 [h, f]``, ``w_fc2 [f, h]`` (all ``uint16``).
+    ``w_o [h_l, h]``, ``w_fc1 [h, f]``, ``w_fc2 [f, h]`` and the serial block's
+    ``ln2_gamma [h]``, ``ln2_beta [h]`` (all ``uint16``).
     """
     rng = np.random.default_rng(w.seed if seed is None else seed)
     T, h, hl, f = w.tokens, w.hidden, w.h_local, w.ffn
@@ -131,14 +134,15 @@ def make_inputs(w: Workload, seed: int | None = None,
     out["dy"] = _normal_bf16(rng, (T, h), 1.0)
     one = f32_to_bf16_bits(np.ones(h, np.float32))
     zero = f32_to_bf16_bits(np.zeros(h, np.float32))
-    for lay in layers:
-        if random_ln:
-            g = 1.0 + 0.1 * rng.standard_normal(size=h, dtype=np.float32)
-            b = 0.1 * rng.standard_normal(size=h, dtype=np.float32)
-            lay["ln_gamma"] = f32_to_bf16_bits(g)
-            lay["ln_beta"] = f32_to_bf16_bits(b)
-        else:
-            lay["ln_gamma"] = one.copy()
-            lay["ln_beta"] = zero.copy()
+    for pre in ("ln", "ln2"):
+        for lay in layers:
+            if random_ln:
+                g = 1.0 + 0.1 * rng.standard_normal(size=h, dtype=np.float32)
+                b = 0.1 * rng.standard_normal(size=h, dtype=np.float32)
+                lay[pre + "_gamma"] = f32_to_bf16_bits(g)
+                lay[pre + "_beta"] = f32_to_bf16_bits(b)
+            else:
+                lay[pre + "_gamma"] = one.copy()
+                lay[pre + "_beta"] = zero.copy()
     out["layers"] = layers
     return out
