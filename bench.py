@@ -17,7 +17,10 @@ Prints one JSON line.  Besides the throughput it carries:
                 with HIP events recorded around it on the library's stream;
   cpu_baseline: the fp64 oracle timed on host cores on a bounded sample of the
                 same workload (a reported baseline, not a target);
-  stages:       mean device time per kernel stage.
+  stages:       mean device time per kernel stage;
+  serial_block: the same workload through the serial (standard) block of the
+                MegaScale notes' eq (3), timed the same way: what the parallel
+                block buys on one GPU (--no-serial skips it).
 
 roofline.traffic is the HBM bytes per launch of the dominant kernel as read
 by rocprofv3 counters (FETCH_SIZE, WRITE_SIZE), each scaled by what the same
@@ -187,6 +190,46 @@ def cpu_baseline(w, budget_s: float):
             "seconds": dt}
 
 
+def time_serial(w, inp, warmup: int, steps: int, ptb_ms: float) -> dict:
+    """The serial block (MegaScale notes, eq (3)) on the same inputs: mean
+    ms per forward+backward step and per stage, HIP events on one stream."""
+    import torch
+
+    from transformer_block_amd import ptb as P
+    from transformer_block_amd.flops import workload_model_flops
+    from transformer_block_amd.runner import SerialBlock
+
+    print("bench: timing the serial block", file=sys.stderr, flush=True)
+    blk = SerialBlock(w, inp, "cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        blk.step(stream)
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    fwd_ev = [ev.create(2 * P.PTB_SERIAL_FWD_STAGES) for _ in range(steps)]
+    bwd_ev = [ev.create(2 * P.PTB_SERIAL_BWD_STAGES) for _ in range(steps)]
+    t0, t1 = ev.create(2)
+    ev.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    ev.hip.hipEventRecord(t0, stream.cuda_stream)
+    for k in range(steps):
+        blk.step(stream, fwd_ev[k], bwd_ev[k])
+    ev.hip.hipEventRecord(t1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(t0, t1) / steps
+    stages = {}
+    for names, evs in ((P.SERIAL_FWD_STAGE_NAMES, fwd_ev), (P.SERIAL_BWD_STAGE_NAMES, bwd_ev)):
+        for i, name in enumerate(names):
+            stages[name] = round(sum(ev.ms(evs[k][2 * i], evs[k][2 * i + 1])
+                                     for k in range(steps)) / steps, 4)
+    ev.close()
+    tflops = workload_model_flops(w) / (ms * 1e-3) / 1e12
+    del blk
+    return {"ms_per_step": round(ms, 4), "value": round(tflops, 2), "unit": "TFLOP/s",
+            "mfu": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "parallel_speedup": round(ms / ptb_ms, 4), "stages_ms": stages}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,6 +238,8 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--no-serial", action="store_true",
+                    help="skip timing the serial-block comparison")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -297,6 +342,8 @@ def main() -> int:
         "roofline": roof,
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
     }
+    if not args.no_serial and w.layers == 1:
+        out["serial_block"] = time_serial(w, inp, args.warmup, K, ms_step)
     if not args.no_cpu_baseline:
         print("bench: timing the fp64 oracle on host cores", file=sys.stderr, flush=True)
         cb = cpu_baseline(w, args.cpu_budget_s)

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define PTB_ABI_VERSION 2
+#define PTB_ABI_VERSION 3
 
 enum ptb_status {
   PTB_OK = 0,
@@ -190,6 +190,98 @@ int32_t ptb_backward_timed(const ptb_dims* dims,
                            void* dw_qkv, void* dw_o, void* dw_fc1, void* dw_fc2,
                            void* workspace, void* stream,
                            void* const* stage_events);
+
+/* ------------------------------------------------------------------------
+ * Serial (standard) block, for comparison with the parallel one: the same
+ * notes, section 1.1, eq (3), built from the same kernels.  The notes print
+ * eq (3) with x alone in the outer sum, y = x + MLP(LN(x + Attn(LN(x)))), but
+ * describe the parallel block, eq (4), as this standard block with LN(x) in
+ * place of LN(x + Attn(LN(x))) as the MLP's input and nothing else changed;
+ * eq (4) keeps Attn(LN(x)) in the outer sum, so the standard block is read
+ * with it there too, and with two LayerNorms of their own gamma and beta:
+ *     a1 = LN1(x);  x1 = x + Attn(a1) W_o;  a2 = LN2(x1)
+ *     y  = x1 + GeLU(a2 W_fc1) W_fc2
+ * Attention, GeLU, dims, layouts, weights, ownership, asynchrony and errors
+ * are exactly as for ptb_forward / ptb_backward; ln1_* are the parameters of
+ * the first LayerNorm (the one ptb_forward calls ln_*), ln2_* [h] those of the
+ * second.  The QKV, O, FC1 and FC2 products are separate launches, and the
+ * MLP waits for the attention output.  `saved` and `workspace` have their own
+ * sizes (ptb_serial_saved_bytes, ptb_serial_workspace_bytes).
+ * ------------------------------------------------------------------------ */
+
+/* What ptb_serial_forward stores in `saved` (byte offsets from
+ * ptb_serial_saved_layout; `offsets` must have room for
+ * PTB_SERIAL_SAVED_COUNT entries):
+ *   A1, MU1, RSTD1, A1_LO   LN1(x) as for the parallel block (PTB_SAVED_A ...)
+ *   QKV, QK_LO, C, LSE      as PTB_SAVED_QKV, _QK_LO, _C, _LSE
+ *   X1                      x + Attn(a1) W_o          bf16 [T, h]
+ *   A2, MU2, RSTD2          LN2(x1) and its row statistics
+ *   U, G                    a2 W_fc1 and GeLU of it   bf16 [T, f] */
+enum ptb_serial_saved_slot {
+  PTB_SERIAL_A1 = 0, PTB_SERIAL_MU1, PTB_SERIAL_RSTD1, PTB_SERIAL_A1_LO,
+  PTB_SERIAL_QKV, PTB_SERIAL_QK_LO, PTB_SERIAL_C, PTB_SERIAL_LSE,
+  PTB_SERIAL_X1, PTB_SERIAL_A2, PTB_SERIAL_MU2, PTB_SERIAL_RSTD2,
+  PTB_SERIAL_U, PTB_SERIAL_G,
+  PTB_SERIAL_SAVED_COUNT
+};
+int32_t ptb_serial_saved_bytes(const ptb_dims* dims, size_t* bytes);
+int32_t ptb_serial_workspace_bytes(const ptb_dims* dims, size_t* bytes);
+int32_t ptb_serial_saved_layout(const ptb_dims* dims, size_t* offsets);
+
+/* Forward of one serial block: writes y [T, h] and fills `saved`. */
+int32_t ptb_serial_forward(const ptb_dims* dims,
+                           const void* x,
+                           const void* ln1_gamma, const void* ln1_beta,
+                           const void* ln2_gamma, const void* ln2_beta,
+                           const void* w_qkv, const void* w_o,
+                           const void* w_fc1, const void* w_fc2,
+                           void* y, void* saved, void* workspace, void* stream);
+
+/* Backward of one serial block for upstream gradient dy [T, h], reading the
+ * `saved` of the matching ptb_serial_forward and the same x and weights.
+ * Writes dx (residual paths included), the gradients of both LayerNorms'
+ * gamma and beta, and the four weight gradients. */
+int32_t ptb_serial_backward(const ptb_dims* dims,
+                            const void* dy, const void* x,
+                            const void* ln1_gamma, const void* ln2_gamma,
+                            const void* w_qkv, const void* w_o,
+                            const void* w_fc1, const void* w_fc2,
+                            const void* saved,
+                            void* dx,
+                            void* d_ln1_gamma, void* d_ln1_beta,
+                            void* d_ln2_gamma, void* d_ln2_beta,
+                            void* dw_qkv, void* dw_o, void* dw_fc1, void* dw_fc2,
+                            void* workspace, void* stream);
+
+/* Stage timing as for ptb_forward_timed.  Stages:
+ *   forward  (PTB_SERIAL_FWD_STAGES = 7): 0 LN1, 1 QKV GEMM, 2 attention,
+ *            3 O GEMM + residual, 4 LN2, 5 FC1 GEMM + GeLU, 6 FC2 GEMM + residual;
+ *   backward (PTB_SERIAL_BWD_STAGES = 11): 0 dgrad FC2 + GeLU', 1 wgrad FC2,
+ *            2 dgrad FC1, 3 wgrad FC1, 4 LN2 backward (+ dy), 5 dgrad O,
+ *            6 wgrad O, 7 attention backward, 8 dgrad QKV, 9 wgrad QKV,
+ *            10 LN1 backward (+ dx1). */
+#define PTB_SERIAL_FWD_STAGES 7
+#define PTB_SERIAL_BWD_STAGES 11
+int32_t ptb_serial_forward_timed(const ptb_dims* dims,
+                                 const void* x,
+                                 const void* ln1_gamma, const void* ln1_beta,
+                                 const void* ln2_gamma, const void* ln2_beta,
+                                 const void* w_qkv, const void* w_o,
+                                 const void* w_fc1, const void* w_fc2,
+                                 void* y, void* saved, void* workspace, void* stream,
+                                 void* const* stage_events);
+int32_t ptb_serial_backward_timed(const ptb_dims* dims,
+                                  const void* dy, const void* x,
+                                  const void* ln1_gamma, const void* ln2_gamma,
+                                  const void* w_qkv, const void* w_o,
+                                  const void* w_fc1, const void* w_fc2,
+                                  const void* saved,
+                                  void* dx,
+                                  void* d_ln1_gamma, void* d_ln1_beta,
+                                  void* d_ln2_gamma, void* d_ln2_beta,
+                                  void* dw_qkv, void* dw_o, void* dw_fc1, void* dw_fc2,
+                                  void* workspace, void* stream,
+                                  void* const* stage_events);
 
 #ifdef __cplusplus
 }  /* extern "C" */

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert P.ptb_abi_version() == 2
+    assert P.ptb_abi_version() == 3
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert P.ptb_status_string(code) and P.ptb_status_string(code) != "unknown status"
     assert P.ptb_status_string(12345) == "unknown status"
@@ -121,3 +121,42 @@ def test_error_raises_in_checked_mode(lib):
     with pytest.raises(P.PtbError) as ei:
         P.ptb_forward(good_dims(batch=0), *([0x10000] * 10), stream=0)
     assert ei.value.status == P.PTB_ERR_DIMS
+
+
+def test_serial_saved_layout_is_ordered_aligned_and_sized(lib):
+    d = good_dims()
+    lay = P.ptb_serial_saved_layout(d)
+    offs = [lay[k] for k in P.SERIAL_SAVED_SLOTS]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    T, h, hl, f = 512, 256, 256, 1024
+    sizes = dict(a1=T * h * 2, mu1=T * 4, rstd1=T * 4, a1_lo=T * h * 2, qkv=T * 3 * hl * 2,
+                 qk_lo=T * 2 * hl * 2, c=T * hl * 2, lse=2 * 4 * 256 * 4, x1=T * h * 2,
+                 a2=T * h * 2, mu2=T * 4, rstd2=T * 4, u=T * f * 2, g=T * f * 2)
+    for a_, b_ in zip(P.SERIAL_SAVED_SLOTS, P.SERIAL_SAVED_SLOTS[1:]):
+        assert lay[b_] - lay[a_] >= sizes[a_]
+    assert P.ptb_serial_saved_bytes(d) >= lay["g"] + sizes["g"]
+    # split-tile partials first, then du, da, dx1, dc and dZ of the backward
+    assert P.ptb_serial_workspace_bytes(d) >= (2 * 256 * 256 * 256 * 4 + T * f * 2
+                                               + 2 * T * h * 2 + T * hl * 2 + T * 3 * hl * 2)
+    n = ctypes.c_size_t(0)
+    assert lib.ptb_serial_saved_bytes(ctypes.byref(good_dims(batch=0)),
+                                      ctypes.byref(n)) == P.PTB_ERR_DIMS
+    assert lib.ptb_serial_workspace_bytes(ctypes.byref(d), None) == P.PTB_ERR_NULL
+
+
+def test_serial_forward_backward_reject_null_and_misaligned_before_any_hip_call(lib):
+    d = good_dims()
+    A = 0x10000  # never dereferenced: the checks fail first
+    assert P.ptb_serial_forward(d, *([0] * 12), stream=0, check=False) == P.PTB_ERR_NULL
+    assert P.ptb_serial_forward(d, *([A] * 11), None, stream=0, check=False) == P.PTB_ERR_NULL
+    args = [A] * 12
+    args[3] = A + 8   # ln2_gamma
+    assert P.ptb_serial_forward(d, *args, stream=0, check=False) == P.PTB_ERR_ALIGN
+    assert P.ptb_serial_backward(d, *([A] * 18), None, stream=0, check=False) == P.PTB_ERR_NULL
+    bargs = [A] * 19
+    bargs[11] = A + 2  # d_ln2_beta
+    assert P.ptb_serial_backward(d, *bargs, stream=0, check=False) == P.PTB_ERR_ALIGN
+    assert P.ptb_serial_forward(good_dims(head_dim=32), *([A] * 12), stream=0,
+                                check=False) == P.PTB_ERR_HEAD_DIM
+    assert P.ptb_serial_backward(good_dims(window=0), *([A] * 19), stream=0,
+                                 check=False) == P.PTB_ERR_WINDOW

@@ -100,7 +100,7 @@ hipError_t launch_gemm_group(const GemmProblem* probs, int nprob, Major a_major,
                              hipStream_t stream);
 
 // LayerNorm forward over rows of x [T, h]: a = bf16(LN(x)) and its rounding
-// residual a_lo = bf16(LN(x) - a), mu, rstd (fp32).
+// residual a_lo = bf16(LN(x) - a) (skipped when a_lo is null), mu, rstd (fp32).
 hipError_t launch_layernorm_fwd(const u16* x, const u16* gamma, const u16* beta,
                                 u16* a, u16* a_lo, float* mu, float* rstd, int T, int h,
                                 float eps, hipStream_t stream);

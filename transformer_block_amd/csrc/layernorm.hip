@@ -77,7 +77,7 @@ __global__ __launch_bounds__(LN_THREADS) void ln_fwd_kernel(const u16* __restric
   const float var = block_sum(sq, red) / static_cast<float>(h);
   const float rstd = 1.0f / sqrtf(var + eps);
   u16* ar = a + static_cast<size_t>(row) * h;
-  u16* alr = a_lo + static_cast<size_t>(row) * h;
+  u16* alr = a_lo != nullptr ? a_lo + static_cast<size_t>(row) * h : nullptr;
 #pragma unroll
   for (int i = 0; i < LN_MAXCH; ++i) {
     const int c = tid + i * LN_THREADS;
@@ -94,7 +94,8 @@ __global__ __launch_bounds__(LN_THREADS) void ln_fwd_kernel(const u16* __restric
         ol[j] = pack2bf(v0 - lo_bf(o[j]), v1 - hi_bf(o[j]));
       }
       *reinterpret_cast<uint4*>(ar + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<uint4*>(alr + c * 8) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+      if (a_lo != nullptr)
+        *reinterpret_cast<uint4*>(alr + c * 8) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
     }
   }
   if (tid == 0) { mu_out[row] = mu; rstd_out[row] = rstd; }

@@ -15,6 +15,10 @@
 //   LayerNorm backward + dy -> dx, dgamma, dbeta.
 // dZ = [dq | dk | dv | du] is one [T, 3*h_l + f] buffer, so the two products
 // with [W_qkv | W_fc1] each run as a single GEMM.
+//
+// The serial block (same notes, eq (3), read with the attention residual:
+// x1 = x + Attn(LN1(x)) W_o, y = x1 + MLP(LN2(x1))) runs the same kernels with
+// the products separate: seven forward and eleven backward stages.
 #include <math.h>
 #include <stdint.h>
 
@@ -114,6 +118,72 @@ WorkLayout work_layout(const Shape& s) {
   W.dc = o; o = align_up(o + s.T * s.hl * 2);
   W.dz = o; o = align_up(o + s.T * s.N1 * 2);
   W.da = o; o = align_up(o + s.T * s.h * 2);
+  W.delta = o; o = align_up(o + s.b * s.n * s.s * 4);
+  W.partials = o; o = align_up(o + static_cast<size_t>(ptb::layernorm_bwd_blocks(s.T)) * 2 * s.h * 4);
+  W.total = o;
+  return W;
+}
+
+// The serial block's stash (ptb_serial_saved_slot order).
+struct SerialSavedLayout {
+  size_t off[PTB_SERIAL_SAVED_COUNT];
+  size_t total;
+};
+
+SerialSavedLayout serial_saved_layout(const Shape& s) {
+  SerialSavedLayout L;
+  size_t o = 0;
+  auto put = [&](int slot, size_t bytes) { L.off[slot] = o; o = align_up(o + bytes); };
+  put(PTB_SERIAL_A1, s.T * s.h * 2);
+  put(PTB_SERIAL_MU1, s.T * 4);
+  put(PTB_SERIAL_RSTD1, s.T * 4);
+  put(PTB_SERIAL_A1_LO, s.T * s.h * 2);
+  put(PTB_SERIAL_QKV, s.T * 3 * s.hl * 2);
+  put(PTB_SERIAL_QK_LO, s.T * 2 * s.hl * 2);
+  put(PTB_SERIAL_C, s.T * s.hl * 2);
+  put(PTB_SERIAL_LSE, s.b * s.n * s.s * 4);
+  put(PTB_SERIAL_X1, s.T * s.h * 2);
+  put(PTB_SERIAL_A2, s.T * s.h * 2);
+  put(PTB_SERIAL_MU2, s.T * 4);
+  put(PTB_SERIAL_RSTD2, s.T * 4);
+  put(PTB_SERIAL_U, s.T * s.f * 2);
+  put(PTB_SERIAL_G, s.T * s.f * 2);
+  L.total = o;
+  return L;
+}
+
+// Arrival counters one launch of the serial block needs at most.
+int serial_max_tiles(const Shape& s) {
+  const int T = static_cast<int>(s.T), h = static_cast<int>(s.h), hl = static_cast<int>(s.hl);
+  const int f = static_cast<int>(s.f);
+  int m = ptb::gemm_tiles(T, 2 * hl) + ptb::gemm_tiles(T, hl);
+  for (int t : {ptb::gemm_tiles(T, h), ptb::gemm_tiles(T, f), ptb::gemm_tiles(f, h),
+                ptb::gemm_tiles(h, f), ptb::gemm_tiles(T, hl), ptb::gemm_tiles(hl, h),
+                ptb::gemm_tiles(h, 3 * hl)})
+    m = t > m ? t : m;
+  const long rows = s.b * s.n * ((s.s + 127) / 128);
+  return rows > m ? static_cast<int>(rows) : m;
+}
+
+// The serial block's scratch: GEMM partial tiles and counters first (all the
+// forward needs), then the backward's intermediate gradients.  da holds the
+// LN2 input gradient, then the LN1 one.
+struct SerialWorkLayout {
+  size_t gemm_partials, counters, du, da, dx1, dc, dz, delta, partials, total;
+  int max_tiles;
+};
+
+SerialWorkLayout serial_work_layout(const Shape& s) {
+  SerialWorkLayout W;
+  size_t o = 0;
+  W.max_tiles = serial_max_tiles(s);
+  W.gemm_partials = o; o = align_up(o + ptb::kGemmPartialBytes);
+  W.counters = o; o = align_up(o + static_cast<size_t>(W.max_tiles) * 4);
+  W.du = o; o = align_up(o + s.T * s.f * 2);
+  W.da = o; o = align_up(o + s.T * s.h * 2);
+  W.dx1 = o; o = align_up(o + s.T * s.h * 2);
+  W.dc = o; o = align_up(o + s.T * s.hl * 2);
+  W.dz = o; o = align_up(o + s.T * 3 * s.hl * 2);
   W.delta = o; o = align_up(o + s.b * s.n * s.s * 4);
   W.partials = o; o = align_up(o + static_cast<size_t>(ptb::layernorm_bwd_blocks(s.T)) * 2 * s.h * 4);
   W.total = o;
@@ -400,6 +470,273 @@ int32_t ptb_backward(const ptb_dims* dims, const void* dy, const void* x, const 
   return ptb_backward_timed(dims, dy, x, ln_gamma, w_qkv, w_o, w_fc1, w_fc2, saved, dx,
                             d_ln_gamma, d_ln_beta, dw_qkv, dw_o, dw_fc1, dw_fc2, workspace,
                             stream, nullptr);
+}
+
+int32_t ptb_serial_saved_bytes(const ptb_dims* dims, size_t* bytes) {
+  Shape s;
+  const int32_t st = check_dims(dims, &s);
+  if (st != PTB_OK) return st;
+  if (bytes == nullptr) return PTB_ERR_NULL;
+  *bytes = serial_saved_layout(s).total;
+  return PTB_OK;
+}
+
+int32_t ptb_serial_workspace_bytes(const ptb_dims* dims, size_t* bytes) {
+  Shape s;
+  const int32_t st = check_dims(dims, &s);
+  if (st != PTB_OK) return st;
+  if (bytes == nullptr) return PTB_ERR_NULL;
+  *bytes = serial_work_layout(s).total;
+  return PTB_OK;
+}
+
+int32_t ptb_serial_saved_layout(const ptb_dims* dims, size_t* offsets) {
+  Shape s;
+  const int32_t st = check_dims(dims, &s);
+  if (st != PTB_OK) return st;
+  if (offsets == nullptr) return PTB_ERR_NULL;
+  const SerialSavedLayout L = serial_saved_layout(s);
+  for (int i = 0; i < PTB_SERIAL_SAVED_COUNT; ++i) offsets[i] = L.off[i];
+  return PTB_OK;
+}
+
+int32_t ptb_serial_forward_timed(const ptb_dims* dims, const void* x, const void* ln1_gamma,
+                                 const void* ln1_beta, const void* ln2_gamma,
+                                 const void* ln2_beta, const void* w_qkv, const void* w_o,
+                                 const void* w_fc1, const void* w_fc2, void* y, void* saved,
+                                 void* workspace, void* stream, void* const* ev) {
+  Shape s;
+  int32_t st = check_dims(dims, &s);
+  if (st != PTB_OK) return st;
+  st = check_ptrs({x, ln1_gamma, ln1_beta, ln2_gamma, ln2_beta, w_qkv, w_o, w_fc1, w_fc2, y,
+                   saved, workspace});
+  if (st != PTB_OK) return st;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  const SerialSavedLayout L = serial_saved_layout(s);
+  const SerialWorkLayout W = serial_work_layout(s);
+  const ptb::GemmScratch gs{at<float>(workspace, W.gemm_partials),
+                            at<int>(workspace, W.counters), W.max_tiles};
+  u16* a1 = at<u16>(saved, L.off[PTB_SERIAL_A1]);
+  float* mu1 = at<float>(saved, L.off[PTB_SERIAL_MU1]);
+  float* rstd1 = at<float>(saved, L.off[PTB_SERIAL_RSTD1]);
+  u16* a1_lo = at<u16>(saved, L.off[PTB_SERIAL_A1_LO]);
+  u16* qkv = at<u16>(saved, L.off[PTB_SERIAL_QKV]);
+  u16* qk_lo = at<u16>(saved, L.off[PTB_SERIAL_QK_LO]);
+  u16* c = at<u16>(saved, L.off[PTB_SERIAL_C]);
+  float* lse = at<float>(saved, L.off[PTB_SERIAL_LSE]);
+  u16* x1 = at<u16>(saved, L.off[PTB_SERIAL_X1]);
+  u16* a2 = at<u16>(saved, L.off[PTB_SERIAL_A2]);
+  float* mu2 = at<float>(saved, L.off[PTB_SERIAL_MU2]);
+  float* rstd2 = at<float>(saved, L.off[PTB_SERIAL_RSTD2]);
+  u16* u = at<u16>(saved, L.off[PTB_SERIAL_U]);
+  u16* g = at<u16>(saved, L.off[PTB_SERIAL_G]);
+  const u16* X = static_cast<const u16*>(x);
+  const u16* Wqkv = static_cast<const u16*>(w_qkv);
+  const int T = static_cast<int>(s.T), h = static_cast<int>(s.h);
+
+  PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
+  PTB_STAGE(0, ptb::launch_layernorm_fwd(X, static_cast<const u16*>(ln1_gamma),
+                                         static_cast<const u16*>(ln1_beta), a1, a1_lo, mu1,
+                                         rstd1, T, h, dims->ln_eps, strm));
+  {  // QKV projection, one launch of two products: [q | k] from [a1 | a1_lo]
+     // (value + residual, as in the parallel block) and v from a1
+    ptb::Epilogue e{};
+    e.o0 = qkv; e.ld0 = static_cast<int>(3 * s.hl);
+    e.o3 = qk_lo; e.ld3 = static_cast<int>(2 * s.hl); e.lo_cols = static_cast<int>(2 * s.hl);
+    e.split = static_cast<int>(3 * s.hl);
+    ptb::GemmProblem pr[2];
+    pr[0].M = T; pr[0].N = static_cast<int>(2 * s.hl); pr[0].K = static_cast<int>(2 * s.h);
+    pr[0].A = two(a1, s.h, s.T, a1_lo, s.h, s.T, s.h, 1);
+    pr[0].B = two(Wqkv, 3 * s.hl, s.h, Wqkv, 3 * s.hl, s.h, s.h, 1);
+    pr[0].epi = e;
+    pr[0].epi.col_base = 0;
+    pr[1].M = T; pr[1].N = static_cast<int>(s.hl); pr[1].K = h;
+    pr[1].A = one(a1, s.h, s.T);
+    pr[1].B = one(Wqkv + 2 * s.hl, 3 * s.hl, s.h);
+    pr[1].B.bytes0 = pr[1].B.bytes1 = view_bytes(3 * s.hl, s.h, s.hl);
+    pr[1].epi = e;
+    pr[1].epi.col_base = static_cast<int>(2 * s.hl);
+    PTB_STAGE(1, ptb::launch_gemm_group(pr, 2, ptb::KMAJOR, ptb::OUTER_MAJOR,
+                                        ptb::EPI_QKV_GELU, gs, strm));
+  }
+  const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
+                            gs.max_tiles, ptb::device_compute_units()};
+  PTB_STAGE(2, ptb::launch_attention_fwd(qkv, qk_lo, c, lse, static_cast<int>(s.b),
+                                         static_cast<int>(s.s), static_cast<int>(s.n),
+                                         static_cast<int>(s.d), static_cast<int>(s.w), as, strm));
+  {  // x1 = x + c W_o
+    ptb::Epilogue e{};
+    e.o0 = x1; e.i0 = X; e.ld0 = h;
+    PTB_STAGE(3, ptb::launch_gemm(T, h, static_cast<int>(s.hl), one(c, s.hl, s.T), ptb::KMAJOR,
+                                  one(static_cast<const u16*>(w_o), s.h, s.hl), ptb::OUTER_MAJOR,
+                                  ptb::EPI_RESIDUAL, e, gs, strm));
+  }
+  PTB_STAGE(4, ptb::launch_layernorm_fwd(x1, static_cast<const u16*>(ln2_gamma),
+                                         static_cast<const u16*>(ln2_beta), a2, nullptr, mu2,
+                                         rstd2, T, h, dims->ln_eps, strm));
+  {  // u = a2 W_fc1, g = GeLU(u): every column on the FC1 side of the split
+    ptb::Epilogue e{};
+    e.o1 = u; e.o2 = g; e.ld1 = static_cast<int>(s.f);
+    e.split = 0; e.lo_cols = 0; e.col_base = 0;
+    PTB_STAGE(5, ptb::launch_gemm(T, static_cast<int>(s.f), h, one(a2, s.h, s.T), ptb::KMAJOR,
+                                  one(static_cast<const u16*>(w_fc1), s.f, s.h),
+                                  ptb::OUTER_MAJOR, ptb::EPI_QKV_GELU, e, gs, strm));
+  }
+  {  // y = x1 + g W_fc2
+    ptb::Epilogue e{};
+    e.o0 = static_cast<u16*>(y); e.i0 = x1; e.ld0 = h;
+    PTB_STAGE(6, ptb::launch_gemm(T, h, static_cast<int>(s.f), one(g, s.f, s.T), ptb::KMAJOR,
+                                  one(static_cast<const u16*>(w_fc2), s.h, s.f),
+                                  ptb::OUTER_MAJOR, ptb::EPI_RESIDUAL, e, gs, strm));
+  }
+  return PTB_OK;
+}
+
+int32_t ptb_serial_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
+                                  const void* ln1_gamma, const void* ln2_gamma,
+                                  const void* w_qkv, const void* w_o, const void* w_fc1,
+                                  const void* w_fc2, const void* saved, void* dx,
+                                  void* d_ln1_gamma, void* d_ln1_beta, void* d_ln2_gamma,
+                                  void* d_ln2_beta, void* dw_qkv, void* dw_o, void* dw_fc1,
+                                  void* dw_fc2, void* workspace, void* stream,
+                                  void* const* ev) {
+  Shape s;
+  int32_t st = check_dims(dims, &s);
+  if (st != PTB_OK) return st;
+  st = check_ptrs({dy, x, ln1_gamma, ln2_gamma, w_qkv, w_o, w_fc1, w_fc2, saved, dx,
+                   d_ln1_gamma, d_ln1_beta, d_ln2_gamma, d_ln2_beta, dw_qkv, dw_o, dw_fc1,
+                   dw_fc2, workspace});
+  if (st != PTB_OK) return st;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  const SerialSavedLayout L = serial_saved_layout(s);
+  const SerialWorkLayout W = serial_work_layout(s);
+  const u16* a1 = at<u16>(saved, L.off[PTB_SERIAL_A1]);
+  const float* mu1 = at<float>(saved, L.off[PTB_SERIAL_MU1]);
+  const float* rstd1 = at<float>(saved, L.off[PTB_SERIAL_RSTD1]);
+  const u16* qkv = at<u16>(saved, L.off[PTB_SERIAL_QKV]);
+  const u16* qk_lo = at<u16>(saved, L.off[PTB_SERIAL_QK_LO]);
+  const u16* c = at<u16>(saved, L.off[PTB_SERIAL_C]);
+  const float* lse = at<float>(saved, L.off[PTB_SERIAL_LSE]);
+  const u16* x1 = at<u16>(saved, L.off[PTB_SERIAL_X1]);
+  const u16* a2 = at<u16>(saved, L.off[PTB_SERIAL_A2]);
+  const float* mu2 = at<float>(saved, L.off[PTB_SERIAL_MU2]);
+  const float* rstd2 = at<float>(saved, L.off[PTB_SERIAL_RSTD2]);
+  const u16* u = at<u16>(saved, L.off[PTB_SERIAL_U]);
+  const u16* g = at<u16>(saved, L.off[PTB_SERIAL_G]);
+  u16* du = at<u16>(workspace, W.du);
+  u16* da = at<u16>(workspace, W.da);
+  u16* dx1 = at<u16>(workspace, W.dx1);
+  u16* dc = at<u16>(workspace, W.dc);
+  u16* dz = at<u16>(workspace, W.dz);
+  float* delta = at<float>(workspace, W.delta);
+  float* partials = at<float>(workspace, W.partials);
+  const ptb::GemmScratch gs{at<float>(workspace, W.gemm_partials),
+                            at<int>(workspace, W.counters), W.max_tiles};
+  const u16* DY = static_cast<const u16*>(dy);
+  const int T = static_cast<int>(s.T), h = static_cast<int>(s.h);
+  const int hl = static_cast<int>(s.hl), f = static_cast<int>(s.f);
+
+  PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
+  {  // du = (dy W_fc2^T) * GeLU'(u): every column on the GeLU side of the split
+    ptb::Epilogue e{};
+    e.o1 = du; e.ld1 = f; e.col_off1 = 0;
+    e.i0 = u; e.ld2 = f;
+    e.split = 0;
+    PTB_STAGE(0, ptb::launch_gemm(T, f, h, one(DY, s.h, s.T), ptb::KMAJOR,
+                                  one(static_cast<const u16*>(w_fc2), s.h, s.f), ptb::KMAJOR,
+                                  ptb::EPI_DGELU, e, gs, strm));
+  }
+  {  // dW_fc2 = g^T dy
+    ptb::Epilogue e{};
+    e.o0 = static_cast<u16*>(dw_fc2); e.ld0 = h;
+    e.split = f;  // one output
+    PTB_STAGE(1, ptb::launch_gemm(f, h, T, one(g, s.f, s.T), ptb::OUTER_MAJOR, one(DY, s.h, s.T),
+                                  ptb::OUTER_MAJOR, ptb::EPI_STORE2_ROWS, e, gs, strm));
+  }
+  {  // da2 = du W_fc1^T
+    ptb::Epilogue e{};
+    e.o0 = da; e.ld0 = h;
+    e.split = h;
+    PTB_STAGE(2, ptb::launch_gemm(T, h, f, one(du, s.f, s.T), ptb::KMAJOR,
+                                  one(static_cast<const u16*>(w_fc1), s.f, s.h), ptb::KMAJOR,
+                                  ptb::EPI_STORE2_COLS, e, gs, strm));
+  }
+  {  // dW_fc1 = a2^T du
+    ptb::Epilogue e{};
+    e.o0 = static_cast<u16*>(dw_fc1); e.ld0 = f;
+    e.split = f;
+    PTB_STAGE(3, ptb::launch_gemm(h, f, T, one(a2, s.h, s.T), ptb::OUTER_MAJOR, one(du, s.f, s.T),
+                                  ptb::OUTER_MAJOR, ptb::EPI_STORE2_COLS, e, gs, strm));
+  }
+  // dx1 = dy + LN2'(da2)
+  PTB_STAGE(4, ptb::launch_layernorm_bwd(da, x1, static_cast<const u16*>(ln2_gamma), mu2, rstd2,
+                                         DY, dx1, partials, static_cast<u16*>(d_ln2_gamma),
+                                         static_cast<u16*>(d_ln2_beta), T, h, strm));
+  {  // dc = dx1 W_o^T
+    ptb::Epilogue e{};
+    e.o0 = dc; e.ld0 = hl;
+    e.split = hl;
+    PTB_STAGE(5, ptb::launch_gemm(T, hl, h, one(dx1, s.h, s.T), ptb::KMAJOR,
+                                  one(static_cast<const u16*>(w_o), s.h, s.hl), ptb::KMAJOR,
+                                  ptb::EPI_STORE2_COLS, e, gs, strm));
+  }
+  {  // dW_o = c^T dx1
+    ptb::Epilogue e{};
+    e.o0 = static_cast<u16*>(dw_o); e.ld0 = h;
+    e.split = hl;
+    PTB_STAGE(6, ptb::launch_gemm(hl, h, T, one(c, s.hl, s.T), ptb::OUTER_MAJOR,
+                                  one(dx1, s.h, s.T), ptb::OUTER_MAJOR, ptb::EPI_STORE2_ROWS, e,
+                                  gs, strm));
+  }
+  const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
+                            gs.max_tiles, ptb::device_compute_units()};
+  PTB_STAGE(7, ptb::launch_attention_bwd(qkv, qk_lo, c, lse, dc, delta, dz, 3 * hl,
+                                         static_cast<int>(s.b), static_cast<int>(s.s),
+                                         static_cast<int>(s.n), static_cast<int>(s.d),
+                                         static_cast<int>(s.w), as, strm));
+  {  // da1 = dZ W_qkv^T
+    ptb::Epilogue e{};
+    e.o0 = da; e.ld0 = h;
+    e.split = h;
+    PTB_STAGE(8, ptb::launch_gemm(T, h, 3 * hl, one(dz, 3 * s.hl, s.T), ptb::KMAJOR,
+                                  one(static_cast<const u16*>(w_qkv), 3 * s.hl, s.h), ptb::KMAJOR,
+                                  ptb::EPI_STORE2_COLS, e, gs, strm));
+  }
+  {  // dW_qkv = a1^T dZ
+    ptb::Epilogue e{};
+    e.o0 = static_cast<u16*>(dw_qkv); e.ld0 = 3 * hl;
+    e.split = 3 * hl;
+    PTB_STAGE(9, ptb::launch_gemm(h, 3 * hl, T, one(a1, s.h, s.T), ptb::OUTER_MAJOR,
+                                  one(dz, 3 * s.hl, s.T), ptb::OUTER_MAJOR, ptb::EPI_STORE2_COLS,
+                                  e, gs, strm));
+  }
+  // dx = dx1 + LN1'(da1)
+  PTB_STAGE(10, ptb::launch_layernorm_bwd(da, static_cast<const u16*>(x),
+                                          static_cast<const u16*>(ln1_gamma), mu1, rstd1, dx1,
+                                          static_cast<u16*>(dx), partials,
+                                          static_cast<u16*>(d_ln1_gamma),
+                                          static_cast<u16*>(d_ln1_beta), T, h, strm));
+  return PTB_OK;
+}
+
+int32_t ptb_serial_forward(const ptb_dims* dims, const void* x, const void* ln1_gamma,
+                           const void* ln1_beta, const void* ln2_gamma, const void* ln2_beta,
+                           const void* w_qkv, const void* w_o, const void* w_fc1,
+                           const void* w_fc2, void* y, void* saved, void* workspace,
+                           void* stream) {
+  return ptb_serial_forward_timed(dims, x, ln1_gamma, ln1_beta, ln2_gamma, ln2_beta, w_qkv, w_o,
+                                  w_fc1, w_fc2, y, saved, workspace, stream, nullptr);
+}
+
+int32_t ptb_serial_backward(const ptb_dims* dims, const void* dy, const void* x,
+                            const void* ln1_gamma, const void* ln2_gamma, const void* w_qkv,
+                            const void* w_o, const void* w_fc1, const void* w_fc2,
+                            const void* saved, void* dx, void* d_ln1_gamma, void* d_ln1_beta,
+                            void* d_ln2_gamma, void* d_ln2_beta, void* dw_qkv, void* dw_o,
+                            void* dw_fc1, void* dw_fc2, void* workspace, void* stream) {
+  return ptb_serial_backward_timed(dims, dy, x, ln1_gamma, ln2_gamma, w_qkv, w_o, w_fc1, w_fc2,
+                                   saved, dx, d_ln1_gamma, d_ln1_beta, d_ln2_gamma, d_ln2_beta,
+                                   dw_qkv, dw_o, dw_fc1, dw_fc2, workspace, stream, nullptr);
 }
 
 }  // extern "C"

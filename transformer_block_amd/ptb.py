@@ -28,6 +28,8 @@ PTB_ERR_EPS = -6
 PTB_ERR_HIP = -7
 
 SAVED_SLOTS = ("a", "mu", "rstd", "qkv", "u", "g", "c", "lse", "a_lo", "qk_lo")
+SERIAL_SAVED_SLOTS = ("a1", "mu1", "rstd1", "a1_lo", "qkv", "qk_lo", "c", "lse", "x1", "a2",
+                      "mu2", "rstd2", "u", "g")
 
 
 class PtbError(RuntimeError):
@@ -80,6 +82,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ptb_backward": (ctypes.c_int32, [_D] + [_P] * 17),
         "ptb_forward_timed": (ctypes.c_int32, [_D] + [_P] * 12),
         "ptb_backward_timed": (ctypes.c_int32, [_D] + [_P] * 18),
+        "ptb_serial_saved_bytes": (ctypes.c_int32, [_D, ctypes.POINTER(ctypes.c_size_t)]),
+        "ptb_serial_workspace_bytes": (ctypes.c_int32, [_D, ctypes.POINTER(ctypes.c_size_t)]),
+        "ptb_serial_saved_layout": (ctypes.c_int32, [_D, ctypes.POINTER(ctypes.c_size_t)]),
+        "ptb_serial_forward": (ctypes.c_int32, [_D] + [_P] * 13),
+        "ptb_serial_backward": (ctypes.c_int32, [_D] + [_P] * 20),
+        "ptb_serial_forward_timed": (ctypes.c_int32, [_D] + [_P] * 14),
+        "ptb_serial_backward_timed": (ctypes.c_int32, [_D] + [_P] * 21),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -201,7 +210,85 @@ def ptb_backward_timed(dims: ptb_dims, dy, x, ln_gamma, w_qkv, w_o, w_fc1, w_fc2
     return _done(st, "ptb_backward_timed", check)
 
 
+# ---- serial (standard) block, for comparison: see include/ptb.h
+PTB_SERIAL_FWD_STAGES = 7
+PTB_SERIAL_BWD_STAGES = 11
+SERIAL_FWD_STAGE_NAMES = ("layernorm1_fwd", "gemm_qkv", "attention_fwd", "gemm_o_residual",
+                          "layernorm2_fwd", "gemm_fc1_gelu", "gemm_fc2_residual")
+SERIAL_BWD_STAGE_NAMES = ("gemm_dgrad_fc2", "gemm_wgrad_fc2", "gemm_dgrad_fc1",
+                          "gemm_wgrad_fc1", "layernorm2_bwd", "gemm_dgrad_o", "gemm_wgrad_o",
+                          "attention_bwd", "gemm_dgrad_qkv", "gemm_wgrad_qkv",
+                          "layernorm1_bwd")
+
+
+def ptb_serial_saved_bytes(dims: ptb_dims) -> int:
+    n = ctypes.c_size_t(0)
+    _done(load_library().ptb_serial_saved_bytes(ctypes.byref(dims), ctypes.byref(n)),
+          "ptb_serial_saved_bytes", True)
+    return n.value
+
+
+def ptb_serial_workspace_bytes(dims: ptb_dims) -> int:
+    n = ctypes.c_size_t(0)
+    _done(load_library().ptb_serial_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)),
+          "ptb_serial_workspace_bytes", True)
+    return n.value
+
+
+def ptb_serial_saved_layout(dims: ptb_dims) -> dict:
+    arr = (ctypes.c_size_t * len(SERIAL_SAVED_SLOTS))()
+    _done(load_library().ptb_serial_saved_layout(ctypes.byref(dims), arr),
+          "ptb_serial_saved_layout", True)
+    return dict(zip(SERIAL_SAVED_SLOTS, list(arr)))
+
+
+def ptb_serial_forward(dims: ptb_dims, x, ln1_gamma, ln1_beta, ln2_gamma, ln2_beta, w_qkv,
+                       w_o, w_fc1, w_fc2, y, saved, workspace, stream=None,
+                       check: bool = True) -> int:
+    st = load_library().ptb_serial_forward(
+        ctypes.byref(dims), _ptr(x), _ptr(ln1_gamma), _ptr(ln1_beta), _ptr(ln2_gamma),
+        _ptr(ln2_beta), _ptr(w_qkv), _ptr(w_o), _ptr(w_fc1), _ptr(w_fc2), _ptr(y), _ptr(saved),
+        _ptr(workspace), _stream(stream))
+    return _done(st, "ptb_serial_forward", check)
+
+
+def ptb_serial_backward(dims: ptb_dims, dy, x, ln1_gamma, ln2_gamma, w_qkv, w_o, w_fc1, w_fc2,
+                        saved, dx, d_ln1_gamma, d_ln1_beta, d_ln2_gamma, d_ln2_beta, dw_qkv,
+                        dw_o, dw_fc1, dw_fc2, workspace, stream=None,
+                        check: bool = True) -> int:
+    st = load_library().ptb_serial_backward(
+        ctypes.byref(dims), _ptr(dy), _ptr(x), _ptr(ln1_gamma), _ptr(ln2_gamma), _ptr(w_qkv),
+        _ptr(w_o), _ptr(w_fc1), _ptr(w_fc2), _ptr(saved), _ptr(dx), _ptr(d_ln1_gamma),
+        _ptr(d_ln1_beta), _ptr(d_ln2_gamma), _ptr(d_ln2_beta), _ptr(dw_qkv), _ptr(dw_o),
+        _ptr(dw_fc1), _ptr(dw_fc2), _ptr(workspace), _stream(stream))
+    return _done(st, "ptb_serial_backward", check)
+
+
+def ptb_serial_forward_timed(dims: ptb_dims, x, ln1_gamma, ln1_beta, ln2_gamma, ln2_beta,
+                             w_qkv, w_o, w_fc1, w_fc2, y, saved, workspace, stream,
+                             stage_events, check: bool = True) -> int:
+    st = load_library().ptb_serial_forward_timed(
+        ctypes.byref(dims), _ptr(x), _ptr(ln1_gamma), _ptr(ln1_beta), _ptr(ln2_gamma),
+        _ptr(ln2_beta), _ptr(w_qkv), _ptr(w_o), _ptr(w_fc1), _ptr(w_fc2), _ptr(y), _ptr(saved),
+        _ptr(workspace), _stream(stream), _events(stage_events))
+    return _done(st, "ptb_serial_forward_timed", check)
+
+
+def ptb_serial_backward_timed(dims: ptb_dims, dy, x, ln1_gamma, ln2_gamma, w_qkv, w_o, w_fc1,
+                              w_fc2, saved, dx, d_ln1_gamma, d_ln1_beta, d_ln2_gamma,
+                              d_ln2_beta, dw_qkv, dw_o, dw_fc1, dw_fc2, workspace, stream,
+                              stage_events, check: bool = True) -> int:
+    st = load_library().ptb_serial_backward_timed(
+        ctypes.byref(dims), _ptr(dy), _ptr(x), _ptr(ln1_gamma), _ptr(ln2_gamma), _ptr(w_qkv),
+        _ptr(w_o), _ptr(w_fc1), _ptr(w_fc2), _ptr(saved), _ptr(dx), _ptr(d_ln1_gamma),
+        _ptr(d_ln1_beta), _ptr(d_ln2_gamma), _ptr(d_ln2_beta), _ptr(dw_qkv), _ptr(dw_o),
+        _ptr(dw_fc1), _ptr(dw_fc2), _ptr(workspace), _stream(stream), _events(stage_events))
+    return _done(st, "ptb_serial_backward_timed", check)
+
+
 def exported_symbols() -> Sequence[str]:
     return ("ptb_abi_version", "ptb_status_string", "ptb_validate_dims", "ptb_saved_bytes",
             "ptb_workspace_bytes", "ptb_saved_layout", "ptb_forward", "ptb_backward",
-            "ptb_forward_timed", "ptb_backward_timed")
+            "ptb_forward_timed", "ptb_backward_timed", "ptb_serial_saved_bytes",
+            "ptb_serial_workspace_bytes", "ptb_serial_saved_layout", "ptb_serial_forward",
+            "ptb_serial_backward", "ptb_serial_forward_timed", "ptb_serial_backward_timed")

@@ -106,3 +106,66 @@ class LayerStack:
         shape, dt = shapes[name]
         nbytes = int(np.prod(shape)) * (2 if dt == torch.bfloat16 else 4)
         return self.saved[li][off:off + nbytes].view(dt).view(shape)
+
+
+class SerialBlock:
+    """One serial (standard) block, the comparison point of the parallel one
+    (include/ptb.h, ptb_serial_*): LN1 and LN2 take `ln_*` and `ln2_*` of the
+    inputs' first layer."""
+
+    def __init__(self, w: Workload, inputs: dict, device: str = "cuda"):
+        if w.layers != 1:
+            raise ValueError("SerialBlock runs one block")
+        self.w = w
+        self.dims = P.dims_of(w)
+        dev = torch.device(device)
+        self.x = to_device_bf16(inputs["x"], dev)
+        self.dy = to_device_bf16(inputs["dy"], dev)
+        lay = inputs["layers"][0]
+        self.p = {k: to_device_bf16(lay[k], dev) for k in PARAM_NAMES + ("ln2_gamma", "ln2_beta")}
+        self.saved = torch.empty(P.ptb_serial_saved_bytes(self.dims), dtype=torch.uint8, device=dev)
+        self.workspace = torch.empty(P.ptb_serial_workspace_bytes(self.dims), dtype=torch.uint8,
+                                     device=dev)
+        self.y = torch.empty_like(self.x)
+        self.dx = torch.empty_like(self.x)
+        p = self.p
+        self.grads = {"d_ln_gamma": torch.empty_like(p["ln_gamma"]),
+                      "d_ln_beta": torch.empty_like(p["ln_beta"]),
+                      "d_ln2_gamma": torch.empty_like(p["ln2_gamma"]),
+                      "d_ln2_beta": torch.empty_like(p["ln2_beta"]),
+                      "dw_qkv": torch.empty_like(p["w_qkv"]), "dw_o": torch.empty_like(p["w_o"]),
+                      "dw_fc1": torch.empty_like(p["w_fc1"]),
+                      "dw_fc2": torch.empty_like(p["w_fc2"])}
+
+    def forward(self, stream=None, events=None) -> None:
+        p = self.p
+        P.ptb_serial_forward_timed(self.dims, self.x, p["ln_gamma"], p["ln_beta"], p["ln2_gamma"],
+                                   p["ln2_beta"], p["w_qkv"], p["w_o"], p["w_fc1"], p["w_fc2"],
+                                   self.y, self.saved, self.workspace, stream, events)
+
+    def backward(self, stream=None, events=None) -> None:
+        p, g = self.p, self.grads
+        P.ptb_serial_backward_timed(self.dims, self.dy, self.x, p["ln_gamma"], p["ln2_gamma"],
+                                    p["w_qkv"], p["w_o"], p["w_fc1"], p["w_fc2"], self.saved,
+                                    self.dx, g["d_ln_gamma"], g["d_ln_beta"], g["d_ln2_gamma"],
+                                    g["d_ln2_beta"], g["dw_qkv"], g["dw_o"], g["dw_fc1"],
+                                    g["dw_fc2"], self.workspace, stream, events)
+
+    def step(self, stream=None, fwd_events=None, bwd_events=None) -> None:
+        self.forward(stream, fwd_events)
+        self.backward(stream, bwd_events)
+
+    def saved_tensor(self, name: str) -> torch.Tensor:
+        """A view of one stashed tensor (see ptb_serial_saved_layout)."""
+        w = self.w
+        T, h, hl, f = w.tokens, w.hidden, w.h_local, w.ffn
+        bf, f32 = torch.bfloat16, torch.float32
+        shapes = {"a1": ((T, h), bf), "mu1": ((T,), f32), "rstd1": ((T,), f32),
+                  "a1_lo": ((T, h), bf), "qkv": ((T, 3 * hl), bf), "qk_lo": ((T, 2 * hl), bf),
+                  "c": ((T, hl), bf), "lse": ((w.batch, w.heads, w.seq), f32),
+                  "x1": ((T, h), bf), "a2": ((T, h), bf), "mu2": ((T,), f32),
+                  "rstd2": ((T,), f32), "u": ((T, f), bf), "g": ((T, f), bf)}
+        off = P.ptb_serial_saved_layout(self.dims)[name]
+        shape, dt = shapes[name]
+        nbytes = int(np.prod(shape)) * (2 if dt == bf else 4)
+        return self.saved[off:off + nbytes].view(dt).view(shape)
