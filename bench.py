@@ -20,7 +20,11 @@ Prints one JSON line.  Besides the throughput it carries:
   stages:       mean device time per kernel stage;
   serial_block: the same workload through the serial (standard) block of the
                 MegaScale notes' eq (3), timed the same way: what the parallel
-                block buys on one GPU (--no-serial skips it).
+                block buys on one GPU (--no-serial skips it);
+  optimizer:    one LAMB step (the notes' eq (7)) over every parameter tensor
+                of the workload, fp32 masters and moments, against the HBM
+                roofline (40 algorithmic bytes per parameter); --no-optimizer
+                skips it.  Neither leg is part of `value`.
 
 roofline.traffic is the HBM bytes per launch of the dominant kernel as read
 by rocprofv3 counters (FETCH_SIZE, WRITE_SIZE), each scaled by what the same
@@ -230,6 +234,54 @@ def time_serial(w, inp, warmup: int, steps: int, ptb_ms: float) -> dict:
             "parallel_speedup": round(ms / ptb_ms, 4), "stages_ms": stages}
 
 
+LAMB_BYTES_PER_PARAM = 40  # moments pass: g 2 + theta, m, v 12 read, m, v 8 written;
+                           # update pass: theta, m, v 12 read, theta 4 + bf16 copy 2 written
+
+
+def time_lamb(st, warmup: int, steps: int) -> dict:
+    """One LAMB step over every parameter tensor of the stack (fp32 masters
+    widened from the bf16 weights, zero moments, the stack's own gradients):
+    mean device time per step between HIP events, and its HBM roofline."""
+    import torch
+
+    from transformer_block_amd import ptb as P
+
+    print("bench: timing the LAMB step", file=sys.stderr, flush=True)
+    names = ("ln_gamma", "ln_beta", "w_qkv", "w_o", "w_fc1", "w_fc2")
+    grad_of = {"ln_gamma": "d_ln_gamma", "ln_beta": "d_ln_beta", "w_qkv": "dw_qkv",
+               "w_o": "dw_o", "w_fc1": "dw_fc1", "w_fc2": "dw_fc2"}
+    tensors = []
+    for p, g in zip(st.params, st.grads):
+        for k in names:
+            theta = p[k].float()
+            # a separate bf16 output: the bench's own weights stay as they are
+            tensors.append((theta, torch.zeros_like(theta), torch.zeros_like(theta),
+                            g[grad_of[k]], torch.empty_like(p[k])))
+    nparam = sum(t[0].numel() for t in tensors)
+    norms = torch.empty((len(tensors), 2), dtype=torch.float32, device="cuda")
+    work = torch.empty(P.ptb_lamb_workspace_bytes(tensors), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        P.ptb_lamb_step(P.ptb_lamb_hyper(1e-3, 0.9, 0.999, 1e-6, i + 1), tensors, norms, work,
+                        stream)
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    t0, t1 = ev.create(2)
+    ev.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    ev.hip.hipEventRecord(t0, stream.cuda_stream)
+    for i in range(steps):
+        P.ptb_lamb_step(P.ptb_lamb_hyper(1e-3, 0.9, 0.999, 1e-6, warmup + i + 1), tensors,
+                        norms, work, stream)
+    ev.hip.hipEventRecord(t1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(t0, t1) / steps
+    ev.close()
+    gbs = nparam * LAMB_BYTES_PER_PARAM / (ms * 1e-3) / 1e9
+    return {"kernel": "lamb", "tensors": len(tensors), "params": nparam, "ms": round(ms, 4),
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_param": LAMB_BYTES_PER_PARAM}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +292,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-serial", action="store_true",
                     help="skip timing the serial-block comparison")
+    ap.add_argument("--no-optimizer", action="store_true",
+                    help="skip timing the LAMB optimizer step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -344,6 +398,8 @@ def main() -> int:
     }
     if not args.no_serial and w.layers == 1:
         out["serial_block"] = time_serial(w, inp, args.warmup, K, ms_step)
+    if not args.no_optimizer:
+        out["optimizer"] = time_lamb(st, args.warmup, K)
     if not args.no_cpu_baseline:
         print("bench: timing the fp64 oracle on host cores", file=sys.stderr, flush=True)
         cb = cpu_baseline(w, args.cpu_budget_s)

@@ -73,7 +73,8 @@ enum ptb_status {
   PTB_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned                   */
   PTB_ERR_WINDOW = -5,    /* window < 1                                         */
   PTB_ERR_EPS = -6,       /* ln_eps is not a finite positive number             */
-  PTB_ERR_HIP = -7        /* a kernel launch failed                             */
+  PTB_ERR_HIP = -7,       /* a kernel launch failed                             */
+  PTB_ERR_ARG = -8        /* invalid optimizer hyper-parameters or tensor list  */
 };
 
 typedef struct ptb_dims {
@@ -282,6 +283,55 @@ int32_t ptb_serial_backward_timed(const ptb_dims* dims,
                                   void* dw_qkv, void* dw_o, void* dw_fc1, void* dw_fc2,
                                   void* workspace, void* stream,
                                   void* const* stage_events);
+
+/* ------------------------------------------------------------------------
+ * LAMB optimizer step (the same notes, section 1.1, eq (7)) over a list of
+ * parameter tensors, each its own "layer" for the trust ratio:
+ *     m <- beta1 m + (1 - beta1) g,      v <- beta2 v + (1 - beta2) g^2
+ *     r  = (m / (1 - beta1^step)) / (sqrt(v / (1 - beta2^step)) + eps)
+ *     theta <- theta - lr * (||theta|| / ||r||) * r
+ * with the norms taken over the whole tensor (theta before the update) and a
+ * trust ratio of 1 when either norm is zero.  Eq (7) gives the trust ratio's
+ * denominator as ||m/sqrt(v) + eps||; it is read as the norm of the same
+ * direction r that the step applies.  No weight decay.  theta, m, v are the
+ * fp32 master weights and moments (mixed precision: Megatron tuning post,
+ * mixed-precision section), updated in place; the gradient is the bf16
+ * output of ptb_backward; `weight` receives bf16(theta) for the next forward
+ * (it may be the tensor the gradient belongs to, never the gradient itself).
+ * ------------------------------------------------------------------------ */
+#define PTB_LAMB_MAX_TENSORS 32
+
+typedef struct ptb_lamb_hyper {
+  float lr;      /* learning rate eta, finite                          */
+  float beta1;   /* 0 <= beta1 < 1                                     */
+  float beta2;   /* 0 <= beta2 < 1                                     */
+  float eps;     /* > 0                                                */
+  int32_t step;  /* t >= 1: bias corrections 1 - beta^t                */
+} ptb_lamb_hyper;
+
+typedef struct ptb_lamb_tensor {
+  float* theta;       /* device fp32 [numel], in/out                  */
+  float* m;           /* device fp32 [numel], in/out (zero at step 1)  */
+  float* v;           /* device fp32 [numel], in/out (zero at step 1)  */
+  const void* grad;   /* device bf16 [numel]                           */
+  void* weight;       /* device bf16 [numel], out: bf16(theta)         */
+  int64_t numel;      /* >= 8, a multiple of 8; < 2^31                 */
+} ptb_lamb_tensor;
+
+/* Scratch bytes of one ptb_lamb_step over `tensors` (host array of n). */
+int32_t ptb_lamb_workspace_bytes(const ptb_lamb_tensor* tensors, int32_t n, size_t* bytes);
+
+/* One LAMB step over n (1..PTB_LAMB_MAX_TENSORS) tensors, enqueued on
+ * `stream`: three kernels (moments and partial norms; norms; update).
+ * `tensors` and `hyper` are host memory, read before the call returns.
+ * `norms` (device fp32 [n][2], caller-owned) receives ||theta|| (before the
+ * update) and ||r|| of each tensor; their ratio is the trust ratio applied.
+ * Every device pointer must be non-NULL and 16-byte aligned, tensors must not
+ * overlap.  PTB_ERR_ARG for an invalid list or hyper-parameters,
+ * PTB_ERR_NULL / PTB_ERR_ALIGN as for the layer calls.  The result is
+ * deterministic (fixed reduction order). */
+int32_t ptb_lamb_step(const ptb_lamb_hyper* hyper, const ptb_lamb_tensor* tensors, int32_t n,
+                      float* norms, void* workspace, void* stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function(lib):
 
 def test_version_and_status_strings(lib):
     assert P.ptb_abi_version() == 3
-    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert P.ptb_status_string(code) and P.ptb_status_string(code) != "unknown status"
     assert P.ptb_status_string(12345) == "unknown status"
 
@@ -160,3 +160,40 @@ def test_serial_forward_backward_reject_null_and_misaligned_before_any_hip_call(
                                 check=False) == P.PTB_ERR_HEAD_DIM
     assert P.ptb_serial_backward(good_dims(window=0), *([A] * 19), stream=0,
                                  check=False) == P.PTB_ERR_WINDOW
+
+
+def _lamb_list(n=2, numel=64, **over):
+    A = 0x10000  # never dereferenced: the checks fail first
+    ts = []
+    for i in range(n):
+        t = dict(theta=A, m=A, v=A, grad=A, weight=A, numel=numel)
+        t.update(over)
+        ts.append((t["theta"], t["m"], t["v"], t["grad"], t["weight"], t["numel"]))
+    return ts
+
+
+def test_lamb_workspace_and_argument_checks(lib):
+    assert P.ptb_lamb_workspace_bytes(_lamb_list(1, 16384)) >= 16
+    assert P.ptb_lamb_workspace_bytes(_lamb_list(3, 16384 * 5 + 8)) >= 3 * 6 * 16
+    hp = P.ptb_lamb_hyper(1e-3, 0.9, 0.999, 1e-6, 1)
+    A = 0x10000
+    ok = _lamb_list()
+    # invalid tensor lists
+    for bad in (_lamb_list(numel=12), _lamb_list(numel=0), _lamb_list(numel=2 ** 31),
+                _lamb_list(n=33)):
+        assert P.ptb_lamb_step(hp, bad, A, A, stream=0, check=False) == P.PTB_ERR_ARG
+    arr = P.lamb_tensor_list(ok)
+    assert lib.ptb_lamb_step(ctypes.byref(hp), arr, 0, A, A, 0) == P.PTB_ERR_ARG
+    assert lib.ptb_lamb_step(None, arr, 2, A, A, 0) == P.PTB_ERR_NULL
+    # invalid hyper-parameters
+    for h in (P.ptb_lamb_hyper(float("nan"), 0.9, 0.999, 1e-6, 1),
+              P.ptb_lamb_hyper(1e-3, 1.0, 0.999, 1e-6, 1),
+              P.ptb_lamb_hyper(1e-3, 0.9, -0.1, 1e-6, 1),
+              P.ptb_lamb_hyper(1e-3, 0.9, 0.999, 0.0, 1),
+              P.ptb_lamb_hyper(1e-3, 0.9, 0.999, 1e-6, 0)):
+        assert P.ptb_lamb_step(h, ok, A, A, stream=0, check=False) == P.PTB_ERR_ARG
+    # null and misaligned pointers
+    assert P.ptb_lamb_step(hp, _lamb_list(grad=0), A, A, stream=0, check=False) == P.PTB_ERR_NULL
+    assert P.ptb_lamb_step(hp, _lamb_list(v=A + 4), A, A, stream=0, check=False) == P.PTB_ERR_ALIGN
+    assert P.ptb_lamb_step(hp, ok, 0, A, stream=0, check=False) == P.PTB_ERR_NULL
+    assert P.ptb_lamb_step(hp, ok, A, A + 8, stream=0, check=False) == P.PTB_ERR_ALIGN

@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libptb.so")
-SOURCES = ["gemm.hip", "attention_fwd.hip", "attention.hip", "layernorm.hip", "ptb_api.cpp"]
+SOURCES = ["gemm.hip", "attention_fwd.hip", "attention.hip", "layernorm.hip", "lamb.hip",
+           "ptb_api.cpp"]
 # Per-source code generation options.  The attention forward rescales its
 # output accumulators with vector ALU instructions; with the accumulators in
 # AGPRs the compiler copies all of them to VGPRs on every key tile, so there

@@ -141,4 +141,27 @@ hipError_t launch_attention_bwd(const u16* qkv, const u16* qk_lo, const u16* c,
                                 int ld_dz, int b, int s, int n, int d, int window,
                                 const AttnScratch& scratch, hipStream_t stream);
 
+// LAMB step over up to kLambMaxTensors parameter tensors (each its own
+// "layer" for the trust ratio): fp32 master weights theta and moments m, v
+// updated in place from the bf16 gradient, and the bf16 copy of theta written
+// to `weight`.  numel must be a multiple of 8 and every pointer 16-byte
+// aligned.  `partial` holds 2 doubles per workgroup (sum of lamb_blocks over
+// the tensors), `norms` 2 floats per tensor (||theta||, ||r|| of this step).
+constexpr int kLambMaxTensors = 32;
+struct LambTensor {
+  float* theta;
+  float* m;
+  float* v;
+  const u16* grad;
+  u16* weight;
+  long numel;
+};
+struct LambHyper {
+  float lr, beta1, beta2, eps;
+  int step;
+};
+int lamb_blocks(long numel);
+hipError_t launch_lamb(const LambTensor* ts, int n, const LambHyper& hp, double* partial,
+                       float* norms, hipStream_t stream);
+
 }  // namespace ptb

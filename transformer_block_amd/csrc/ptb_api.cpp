@@ -255,6 +255,7 @@ const char* ptb_status_string(int32_t status) {
     case PTB_ERR_WINDOW: return "window must be >= 1";
     case PTB_ERR_EPS: return "ln_eps must be a finite positive number";
     case PTB_ERR_HIP: return "a HIP kernel launch failed";
+    case PTB_ERR_ARG: return "invalid optimizer hyper-parameters or tensor list";
     default: return "unknown status";
   }
 }
@@ -737,6 +738,47 @@ int32_t ptb_serial_backward(const ptb_dims* dims, const void* dy, const void* x,
   return ptb_serial_backward_timed(dims, dy, x, ln1_gamma, ln2_gamma, w_qkv, w_o, w_fc1, w_fc2,
                                    saved, dx, d_ln1_gamma, d_ln1_beta, d_ln2_gamma, d_ln2_beta,
                                    dw_qkv, dw_o, dw_fc1, dw_fc2, workspace, stream, nullptr);
+}
+
+int32_t ptb_lamb_workspace_bytes(const ptb_lamb_tensor* tensors, int32_t n, size_t* bytes) {
+  if (tensors == nullptr || bytes == nullptr) return PTB_ERR_NULL;
+  if (n < 1 || n > PTB_LAMB_MAX_TENSORS) return PTB_ERR_ARG;
+  size_t blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t ne = tensors[i].numel;
+    if (ne < 8 || ne % 8 != 0 || ne >= (int64_t(1) << 31)) return PTB_ERR_ARG;
+    blocks += static_cast<size_t>(ptb::lamb_blocks(ne));
+  }
+  *bytes = align_up(blocks * 2 * sizeof(double));
+  return PTB_OK;
+}
+
+int32_t ptb_lamb_step(const ptb_lamb_hyper* hyper, const ptb_lamb_tensor* tensors, int32_t n,
+                      float* norms, void* workspace, void* stream) {
+  if (hyper == nullptr || tensors == nullptr) return PTB_ERR_NULL;
+  size_t need = 0;
+  const int32_t st = ptb_lamb_workspace_bytes(tensors, n, &need);
+  if (st != PTB_OK) return st;
+  const ptb_lamb_hyper& h = *hyper;
+  if (!isfinite(h.lr) || !(h.beta1 >= 0.0f && h.beta1 < 1.0f) ||
+      !(h.beta2 >= 0.0f && h.beta2 < 1.0f) || !(h.eps > 0.0f) || !isfinite(h.eps) || h.step < 1)
+    return PTB_ERR_ARG;
+  for (int i = 0; i < n; ++i) {
+    const ptb_lamb_tensor& t = tensors[i];
+    const int32_t pc = check_ptrs({t.theta, t.m, t.v, t.grad, t.weight});
+    if (pc != PTB_OK) return pc;
+  }
+  const int32_t pc = check_ptrs({norms, workspace});
+  if (pc != PTB_OK) return pc;
+  ptb::LambTensor ts[PTB_LAMB_MAX_TENSORS];
+  for (int i = 0; i < n; ++i)
+    ts[i] = ptb::LambTensor{tensors[i].theta, tensors[i].m, tensors[i].v,
+                            static_cast<const u16*>(tensors[i].grad),
+                            static_cast<u16*>(tensors[i].weight), static_cast<long>(tensors[i].numel)};
+  const ptb::LambHyper hp{h.lr, h.beta1, h.beta2, h.eps, h.step};
+  PTB_HIP(ptb::launch_lamb(ts, n, hp, static_cast<double*>(workspace), norms,
+                           reinterpret_cast<hipStream_t>(stream)));
+  return PTB_OK;
 }
 
 }  // extern "C"

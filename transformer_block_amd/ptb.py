@@ -26,6 +26,8 @@ PTB_ERR_ALIGN = -4
 PTB_ERR_WINDOW = -5
 PTB_ERR_EPS = -6
 PTB_ERR_HIP = -7
+PTB_ERR_ARG = -8
+PTB_LAMB_MAX_TENSORS = 32
 
 SAVED_SLOTS = ("a", "mu", "rstd", "qkv", "u", "g", "c", "lse", "a_lo", "qk_lo")
 SERIAL_SAVED_SLOTS = ("a1", "mu1", "rstd1", "a1_lo", "qkv", "qk_lo", "c", "lse", "x1", "a2",
@@ -49,6 +51,17 @@ def dims_of(w) -> ptb_dims:
     """ptb_dims of a Workload (transformer_block_amd.inputs)."""
     return ptb_dims(w.batch, w.seq, w.hidden, w.heads, w.head_dim, w.ffn, w.window,
                     w.ln_eps)
+
+
+class ptb_lamb_hyper(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("step", ctypes.c_int32)]
+
+
+class ptb_lamb_tensor(ctypes.Structure):
+    _fields_ = [("theta", ctypes.c_void_p), ("m", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("grad", ctypes.c_void_p), ("weight", ctypes.c_void_p),
+                ("numel", ctypes.c_int64)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -89,6 +102,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ptb_serial_backward": (ctypes.c_int32, [_D] + [_P] * 20),
         "ptb_serial_forward_timed": (ctypes.c_int32, [_D] + [_P] * 14),
         "ptb_serial_backward_timed": (ctypes.c_int32, [_D] + [_P] * 21),
+        "ptb_lamb_workspace_bytes": (ctypes.c_int32, [ctypes.POINTER(ptb_lamb_tensor),
+                                                      ctypes.c_int32,
+                                                      ctypes.POINTER(ctypes.c_size_t)]),
+        "ptb_lamb_step": (ctypes.c_int32, [ctypes.POINTER(ptb_lamb_hyper),
+                                           ctypes.POINTER(ptb_lamb_tensor), ctypes.c_int32,
+                                           _P, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -286,9 +305,38 @@ def ptb_serial_backward_timed(dims: ptb_dims, dy, x, ln1_gamma, ln2_gamma, w_qkv
     return _done(st, "ptb_serial_backward_timed", check)
 
 
+# ---- LAMB optimizer step: see include/ptb.h
+def lamb_tensor_list(tensors) -> ctypes.Array:
+    """ptb_lamb_tensor array from (theta, m, v, grad, weight) tuples of
+    tensors (or raw addresses plus a numel: (theta, m, v, grad, weight, numel))."""
+    arr = (ptb_lamb_tensor * len(tensors))()
+    for i, t in enumerate(tensors):
+        numel = t[5] if len(t) > 5 else t[0].numel()
+        arr[i] = ptb_lamb_tensor(*(_ptr(x) for x in t[:5]), numel)
+    return arr
+
+
+def ptb_lamb_workspace_bytes(tensors) -> int:
+    arr = lamb_tensor_list(tensors)
+    n = ctypes.c_size_t(0)
+    _done(load_library().ptb_lamb_workspace_bytes(arr, len(arr), ctypes.byref(n)),
+          "ptb_lamb_workspace_bytes", True)
+    return n.value
+
+
+def ptb_lamb_step(hyper: ptb_lamb_hyper, tensors, norms, workspace, stream=None,
+                  check: bool = True) -> int:
+    """tensors: (theta, m, v, grad, weight) per parameter tensor."""
+    arr = lamb_tensor_list(tensors)
+    st = load_library().ptb_lamb_step(ctypes.byref(hyper), arr, len(arr), _ptr(norms),
+                                      _ptr(workspace), _stream(stream))
+    return _done(st, "ptb_lamb_step", check)
+
+
 def exported_symbols() -> Sequence[str]:
     return ("ptb_abi_version", "ptb_status_string", "ptb_validate_dims", "ptb_saved_bytes",
             "ptb_workspace_bytes", "ptb_saved_layout", "ptb_forward", "ptb_backward",
             "ptb_forward_timed", "ptb_backward_timed", "ptb_serial_saved_bytes",
             "ptb_serial_workspace_bytes", "ptb_serial_saved_layout", "ptb_serial_forward",
-            "ptb_serial_backward", "ptb_serial_forward_timed", "ptb_serial_backward_timed")
+            "ptb_serial_backward", "ptb_serial_forward_timed", "ptb_serial_backward_timed",
+            "ptb_lamb_workspace_bytes", "ptb_lamb_step")
