@@ -30,6 +30,13 @@ the rows of ``W_o``.
 
 Layout: every activation is token-major ``[T, .]`` with ``T = b*s`` and token
 index ``t = batch_index*s + position``.
+
+Variants ([MS] 1.3 names MegaScale's own fused RMSNorm and SwiGLU kernels):
+``norm="rmsnorm"`` replaces each LayerNorm by a = gamma * x / sqrt(mean(x^2) +
+eps) (no beta); ``mlp="swiglu"`` replaces GeLU(a W_fc1) by silu(a W1) * (a W3),
+silu(u) = u sigmoid(u), with W1 and W3 carried in one w_fc1 [h, 2f] whose
+32-column blocks alternate W1 and W3 (the library's layout; split_w13 and
+merge_w13 below are that permutation and nothing else).
 """
 from __future__ import annotations
 
@@ -97,6 +104,35 @@ def layernorm_backward(da: np.ndarray, x: np.ndarray, gamma: np.ndarray,
     return dx, (da * xhat).sum(axis=0), da.sum(axis=0)
 
 
+def rmsnorm_forward(x: np.ndarray, gamma: np.ndarray,
+                    eps: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """a = gamma * x / sqrt(mean(x^2) + eps) per row; returns (a, 0, rstd)
+    (a zero row mean, so that xhat = (x - mean) * rstd holds as for LN)."""
+    rstd = 1.0 / np.sqrt((x * x).mean(axis=1) + eps)
+    return x * rstd[:, None] * gamma[None, :], np.zeros(x.shape[0]), rstd
+
+
+def rmsnorm_backward(da: np.ndarray, x: np.ndarray, gamma: np.ndarray, rstd: np.ndarray):
+    """Gradient of rmsnorm_forward: (dx, dgamma, dbeta = 0).  With
+    xhat = x * rstd and g = da * gamma, dx = rstd * (g - xhat * mean_k(g * xhat))."""
+    xhat = x * rstd[:, None]
+    g = da * gamma[None, :]
+    dx = rstd[:, None] * (g - xhat * (g * xhat).mean(axis=1, keepdims=True))
+    return dx, (da * xhat).sum(axis=0), np.zeros(x.shape[1])
+
+
+def norm_forward(kind: str, x, gamma, beta, eps):
+    if kind == "rmsnorm":
+        return rmsnorm_forward(x, gamma, eps)
+    return layernorm_forward(x, gamma, beta, eps)
+
+
+def norm_backward(kind: str, da, x, gamma, mu, rstd):
+    if kind == "rmsnorm":
+        return rmsnorm_backward(da, x, gamma, rstd)
+    return layernorm_backward(da, x, gamma, mu, rstd)
+
+
 # ---------------------------------------------------------------------------
 # GeLU ([TP] 2.1): exact form u * Phi(u), Phi the standard normal CDF.
 # ---------------------------------------------------------------------------
@@ -115,6 +151,61 @@ def gelu(u: np.ndarray) -> np.ndarray:
 def gelu_grad(u: np.ndarray) -> np.ndarray:
     """d/du [u Phi(u)] = Phi(u) + u phi(u)."""
     return normal_cdf(u) + u * normal_pdf(u)
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU ([MS] 1.3): silu(a W1) * (a W3), silu(u) = u * sigmoid(u).
+# ---------------------------------------------------------------------------
+def sigmoid(u: np.ndarray) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-u))
+
+
+def silu(u: np.ndarray) -> np.ndarray:
+    return u * sigmoid(u)
+
+
+def silu_grad(u: np.ndarray) -> np.ndarray:
+    """d/du [u sigmoid(u)] = sigmoid(u) + u sigmoid(u) (1 - sigmoid(u))."""
+    s = sigmoid(u)
+    return s + u * s * (1.0 - s)
+
+
+def split_w13(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """[rows, 2f] with 32-column blocks alternating W1, W3 -> (W1, W3) [rows, f]."""
+    rows, two_f = w.shape
+    blocks = w.reshape(rows, two_f // 64, 2, 32)
+    return blocks[:, :, 0, :].reshape(rows, two_f // 2), blocks[:, :, 1, :].reshape(rows, two_f // 2)
+
+
+def merge_w13(w1: np.ndarray, w3: np.ndarray) -> np.ndarray:
+    """Inverse of split_w13."""
+    rows, f = w1.shape
+    return np.stack([w1.reshape(rows, f // 32, 32), w3.reshape(rows, f // 32, 32)],
+                    axis=2).reshape(rows, 2 * f)
+
+
+def mlp_forward(kind: str, a: np.ndarray, w_fc1: np.ndarray, fc):
+    """(u, g): u the pre-activation in w_fc1's column layout, g the activation."""
+    if kind == "swiglu":
+        w1, w3 = split_w13(w_fc1)
+        u1, u3 = _mm(a, w1, fc), _mm(a, w3, fc)
+        return merge_w13(u1, u3), silu(u1) * u3
+    u = _mm(a, w_fc1, fc)
+    return u, gelu(u)
+
+
+def mlp_backward(kind: str, dg: np.ndarray, u: np.ndarray, a: np.ndarray, w_fc1: np.ndarray,
+                 fc):
+    """(dw_fc1, da) of mlp_forward for upstream gradient dg of g."""
+    if kind == "swiglu":
+        u1, u3 = split_w13(u)
+        w1, w3 = split_w13(w_fc1)
+        du1 = dg * u3 * silu_grad(u1)
+        du3 = dg * silu(u1)
+        dw = merge_w13(_mm(a.T, du1, fc), _mm(a.T, du3, fc))
+        return dw, _mm(du1, w1.T, fc) + _mm(du3, w3.T, fc)
+    du = dg * gelu_grad(u)
+    return _mm(a.T, du, fc), _mm(du, w_fc1.T, fc)
 
 
 # ---------------------------------------------------------------------------
@@ -213,11 +304,11 @@ def merge_heads(t: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 def ptb_forward(x: np.ndarray, p: Dict[str, np.ndarray], batch: int, seq: int,
                 heads: int, head_dim: int, window: int, eps: float,
-                fc: FlopCounter | None = None):
+                fc: FlopCounter | None = None, norm: str = "layernorm", mlp: str = "gelu"):
     """x: [T, h]; p holds ln_gamma, ln_beta, w_qkv [h,3hl], w_o [hl,h],
-    w_fc1 [h,f], w_fc2 [f,h] (float64).  Returns (y, cache)."""
+    w_fc1 [h,f] ([h,2f] for SwiGLU), w_fc2 [f,h] (float64).  Returns (y, cache)."""
     hl = heads * head_dim
-    a, mu, rstd = layernorm_forward(x, p["ln_gamma"], p["ln_beta"], eps)
+    a, mu, rstd = norm_forward(norm, x, p["ln_gamma"], p["ln_beta"], eps)
     # attention branch
     qkv = _mm(a, p["w_qkv"], fc)
     q = split_heads(qkv[:, :hl], batch, seq, heads, head_dim)
@@ -227,12 +318,11 @@ def ptb_forward(x: np.ndarray, p: Dict[str, np.ndarray], batch: int, seq: int,
     c = merge_heads(o)
     attn_out = _mm(c, p["w_o"], fc)
     # MLP branch on the same LN output
-    u = _mm(a, p["w_fc1"], fc)
-    g = gelu(u)
+    u, g = mlp_forward(mlp, a, p["w_fc1"], fc)
     mlp_out = _mm(g, p["w_fc2"], fc)
     y = x + attn_out + mlp_out
     cache = dict(x=x, a=a, mu=mu, rstd=rstd, q=q, k=k, v=v, c=c, u=u, g=g,
-                 qkv=qkv)
+                 qkv=qkv, norm=norm, mlp=mlp)
     return y, cache
 
 
@@ -247,9 +337,7 @@ def ptb_backward(dy: np.ndarray, cache: dict, p: Dict[str, np.ndarray],
     dw_o = _mm(c.T, dy, fc)
     dw_fc2 = _mm(g.T, dy, fc)
     # MLP branch
-    du = dg * gelu_grad(u)
-    dw_fc1 = _mm(a.T, du, fc)
-    da_mlp = _mm(du, p["w_fc1"].T, fc)
+    dw_fc1, da_mlp = mlp_backward(cache["mlp"], dg, u, a, p["w_fc1"], fc)
     # attention branch
     b, n, s, d = q.shape
     dq, dk, dv = attention_backward(q, k, v, split_heads(dc, b, s, n, d),
@@ -259,20 +347,20 @@ def ptb_backward(dy: np.ndarray, cache: dict, p: Dict[str, np.ndarray],
     dw_qkv = _mm(a.T, dqkv, fc)
     da_attn = _mm(dqkv, p["w_qkv"].T, fc)
     # shared LayerNorm and the residual
-    dx_ln, dgamma, dbeta = layernorm_backward(da_attn + da_mlp, x,
-                                              p["ln_gamma"], cache["mu"],
-                                              cache["rstd"])
+    dx_ln, dgamma, dbeta = norm_backward(cache["norm"], da_attn + da_mlp, x,
+                                         p["ln_gamma"], cache["mu"], cache["rstd"])
     return dict(dx=dy + dx_ln, d_ln_gamma=dgamma, d_ln_beta=dbeta,
                 dw_qkv=dw_qkv, dw_o=dw_o, dw_fc1=dw_fc1, dw_fc2=dw_fc2)
 
 
 def ptb_stack_forward(x: np.ndarray, params: List[Dict[str, np.ndarray]],
                       batch: int, seq: int, heads: int, head_dim: int,
-                      window: int, eps: float, fc: FlopCounter | None = None):
+                      window: int, eps: float, fc: FlopCounter | None = None,
+                      norm: str = "layernorm", mlp: str = "gelu"):
     """L stacked layers: x_{l+1} = PTB(x_l; theta_l).  Returns (y, caches)."""
     caches = []
     for p in params:
-        x, cache = ptb_forward(x, p, batch, seq, heads, head_dim, window, eps, fc)
+        x, cache = ptb_forward(x, p, batch, seq, heads, head_dim, window, eps, fc, norm, mlp)
         caches.append(cache)
     return x, caches
 
@@ -304,22 +392,21 @@ def ptb_stack_backward(dy: np.ndarray, caches: list,
 # ---------------------------------------------------------------------------
 def serial_forward(x: np.ndarray, p: Dict[str, np.ndarray], batch: int, seq: int,
                    heads: int, head_dim: int, window: int, eps: float,
-                   fc: FlopCounter | None = None):
+                   fc: FlopCounter | None = None, norm: str = "layernorm", mlp: str = "gelu"):
     """x: [T, h] -> (y, cache) for the serial block above."""
     hl = heads * head_dim
-    a1, mu1, rstd1 = layernorm_forward(x, p["ln_gamma"], p["ln_beta"], eps)
+    a1, mu1, rstd1 = norm_forward(norm, x, p["ln_gamma"], p["ln_beta"], eps)
     qkv = _mm(a1, p["w_qkv"], fc)
     q = split_heads(qkv[:, :hl], batch, seq, heads, head_dim)
     k = split_heads(qkv[:, hl:2 * hl], batch, seq, heads, head_dim)
     v = split_heads(qkv[:, 2 * hl:], batch, seq, heads, head_dim)
     c = merge_heads(attention_forward(q, k, v, window, fc))
     x1 = x + _mm(c, p["w_o"], fc)
-    a2, mu2, rstd2 = layernorm_forward(x1, p["ln2_gamma"], p["ln2_beta"], eps)
-    u = _mm(a2, p["w_fc1"], fc)
-    g = gelu(u)
+    a2, mu2, rstd2 = norm_forward(norm, x1, p["ln2_gamma"], p["ln2_beta"], eps)
+    u, g = mlp_forward(mlp, a2, p["w_fc1"], fc)
     y = x1 + _mm(g, p["w_fc2"], fc)
     cache = dict(x=x, a1=a1, mu1=mu1, rstd1=rstd1, qkv=qkv, q=q, k=k, v=v, c=c,
-                 x1=x1, a2=a2, mu2=mu2, rstd2=rstd2, u=u, g=g)
+                 x1=x1, a2=a2, mu2=mu2, rstd2=rstd2, u=u, g=g, norm=norm, mlp=mlp)
     return y, cache
 
 
@@ -330,11 +417,9 @@ def serial_backward(dy: np.ndarray, cache: dict, p: Dict[str, np.ndarray],
     # MLP sub-block: y = x1 + GeLU(LN2(x1) W_fc1) W_fc2
     dg = _mm(dy, p["w_fc2"].T, fc)
     dw_fc2 = _mm(cache["g"].T, dy, fc)
-    du = dg * gelu_grad(cache["u"])
-    dw_fc1 = _mm(cache["a2"].T, du, fc)
-    da2 = _mm(du, p["w_fc1"].T, fc)
-    dx1_ln, dgamma2, dbeta2 = layernorm_backward(da2, cache["x1"], p["ln2_gamma"],
-                                                 cache["mu2"], cache["rstd2"])
+    dw_fc1, da2 = mlp_backward(cache["mlp"], dg, cache["u"], cache["a2"], p["w_fc1"], fc)
+    dx1_ln, dgamma2, dbeta2 = norm_backward(cache["norm"], da2, cache["x1"], p["ln2_gamma"],
+                                            cache["mu2"], cache["rstd2"])
     dx1 = dy + dx1_ln
     # attention sub-block: x1 = x + Attn(LN1(x)) W_o
     dc = _mm(dx1, p["w_o"].T, fc)
@@ -345,8 +430,8 @@ def serial_backward(dy: np.ndarray, cache: dict, p: Dict[str, np.ndarray],
     dqkv = np.concatenate([merge_heads(dq), merge_heads(dk), merge_heads(dv)], axis=1)
     dw_qkv = _mm(cache["a1"].T, dqkv, fc)
     da1 = _mm(dqkv, p["w_qkv"].T, fc)
-    dx_ln, dgamma1, dbeta1 = layernorm_backward(da1, cache["x"], p["ln_gamma"],
-                                                cache["mu1"], cache["rstd1"])
+    dx_ln, dgamma1, dbeta1 = norm_backward(cache["norm"], da1, cache["x"], p["ln_gamma"],
+                                           cache["mu1"], cache["rstd1"])
     return dict(dx=dx1 + dx_ln, d_ln_gamma=dgamma1, d_ln_beta=dbeta1,
                 d_ln2_gamma=dgamma2, d_ln2_beta=dbeta2, dw_qkv=dw_qkv, dw_o=dw_o,
                 dw_fc1=dw_fc1, dw_fc2=dw_fc2)
