@@ -21,6 +21,9 @@ Prints one JSON line.  Besides the throughput it carries:
   serial_block: the same workload through the serial (standard) block of the
                 MegaScale notes' eq (3), timed the same way: what the parallel
                 block buys on one GPU (--no-serial skips it);
+  variant:      the same workload with RMSNorm and the SwiGLU MLP (MegaScale's
+                own fused kernels, notes section 1.3; --no-variant skips it),
+                model FLOPs counting the SwiGLU MLP's 3 h f weights;
   optimizer:    one LAMB step (the notes' eq (7)) over every parameter tensor
                 of the workload, fp32 masters and moments, against the HBM
                 roofline (40 algorithmic bytes per parameter); --no-optimizer
@@ -234,6 +237,50 @@ def time_serial(w, inp, warmup: int, steps: int, ptb_ms: float) -> dict:
             "parallel_speedup": round(ms / ptb_ms, 4), "stages_ms": stages}
 
 
+def time_variant(w, warmup: int, steps: int, base_ms: float) -> dict:
+    """The layer stack with RMSNorm and the SwiGLU MLP on the same shape:
+    mean ms per fwd+bwd step and per stage (HIP events, one stream)."""
+    import torch
+
+    from transformer_block_amd import inputs as I
+    from transformer_block_amd import ptb as P
+    from transformer_block_amd.flops import workload_model_flops
+    from transformer_block_amd.runner import LayerStack
+
+    print("bench: timing the RMSNorm + SwiGLU variant", file=sys.stderr, flush=True)
+    wv = w.replace(name=w.name + "_rmsnorm_swiglu", norm="rmsnorm", mlp="swiglu")
+    st = LayerStack(wv, I.make_inputs(wv), "cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        st.step(stream)
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    L = wv.layers
+    fwd_ev = [[ev.create(2 * P.PTB_FWD_STAGES) for _ in range(L)] for _ in range(steps)]
+    bwd_ev = [[ev.create(2 * P.PTB_BWD_STAGES) for _ in range(L)] for _ in range(steps)]
+    t0, t1 = ev.create(2)
+    ev.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    ev.hip.hipEventRecord(t0, stream.cuda_stream)
+    for k in range(steps):
+        st.step(stream, fwd_ev[k], bwd_ev[k])
+    ev.hip.hipEventRecord(t1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(t0, t1) / steps
+    stages = {}
+    for names, evs in ((P.FWD_STAGE_NAMES, fwd_ev), (P.BWD_STAGE_NAMES, bwd_ev)):
+        for i, name in enumerate(names):
+            stages[name] = round(sum(ev.ms(evs[k][l][2 * i], evs[k][l][2 * i + 1])
+                                     for k in range(steps) for l in range(L)) / (steps * L), 4)
+    ev.close()
+    F = workload_model_flops(wv)
+    tflops = F / (ms * 1e-3) / 1e12
+    del st
+    return {"norm": "rmsnorm", "mlp": "swiglu", "ms_per_step": round(ms, 4),
+            "value": round(tflops, 2), "unit": "TFLOP/s", "mfu": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "model_flops_per_step": F, "stages_ms": stages}
+
+
 LAMB_BYTES_PER_PARAM = 40  # moments pass: g 2 + theta, m, v 12 read, m, v 8 written;
                            # update pass: theta, m, v 12 read, theta 4 + bf16 copy 2 written
 
@@ -292,6 +339,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-serial", action="store_true",
                     help="skip timing the serial-block comparison")
+    ap.add_argument("--no-variant", action="store_true",
+                    help="skip timing the RMSNorm + SwiGLU variant")
     ap.add_argument("--no-optimizer", action="store_true",
                     help="skip timing the LAMB optimizer step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -400,6 +449,8 @@ def main() -> int:
         out["serial_block"] = time_serial(w, inp, args.warmup, K, ms_step)
     if not args.no_optimizer:
         out["optimizer"] = time_lamb(st, args.warmup, K)
+    if not args.no_variant:
+        out["variant"] = time_variant(w, args.warmup, K, ms_step)
     if not args.no_cpu_baseline:
         print("bench: timing the fp64 oracle on host cores", file=sys.stderr, flush=True)
         cb = cpu_baseline(w, args.cpu_budget_s)

@@ -28,7 +28,7 @@
  *     w_qkv  [h, 3*h_l]   columns [Q heads | K heads | V heads]; head j's
  *                         head_dim columns are contiguous inside each block
  *     w_o    [h_l, h]     rows in the same head order
- *     w_fc1  [h, f]
+ *     w_fc1  [h, f]       ([h, 2f] for the SwiGLU variant, see ptb_dims.mlp)
  *     w_fc2  [f, h]
  * Gradients have the shape of what they differentiate.  Arithmetic is bf16
  * operands with fp32 accumulation; LayerNorm statistics and the attention
@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define PTB_ABI_VERSION 3
+#define PTB_ABI_VERSION 4
 
 enum ptb_status {
   PTB_OK = 0,
@@ -74,7 +74,8 @@ enum ptb_status {
   PTB_ERR_WINDOW = -5,    /* window < 1                                         */
   PTB_ERR_EPS = -6,       /* ln_eps is not a finite positive number             */
   PTB_ERR_HIP = -7,       /* a kernel launch failed                             */
-  PTB_ERR_ARG = -8        /* invalid optimizer hyper-parameters or tensor list  */
+  PTB_ERR_ARG = -8        /* invalid layer variant (norm, mlp), optimizer
+                             hyper-parameters or tensor list                    */
 };
 
 typedef struct ptb_dims {
@@ -86,7 +87,23 @@ typedef struct ptb_dims {
   int32_t ffn;       /* f: multiple of 64, >= 64                              */
   int32_t window;    /* w >= 1; w >= seq is full causal attention             */
   float ln_eps;      /* LayerNorm epsilon, added to the variance, > 0         */
+  int32_t norm;      /* PTB_NORM_LAYERNORM (0) or PTB_NORM_RMSNORM (1)         */
+  int32_t mlp;       /* PTB_MLP_GELU (0) or PTB_MLP_SWIGLU (1)                 */
 } ptb_dims;
+
+/* Layer variants (MegaScale notes, section 1.3: the fused RMSNorm and SwiGLU
+ * kernels of MegaScale's own model; the default is the layer above).
+ *   PTB_NORM_RMSNORM: a = gamma * x / sqrt(mean(x^2) + ln_eps); ln_beta is
+ *     ignored (it must still be a valid pointer) and d_ln_beta is written as
+ *     zeros; the stashed row mean (PTB_SAVED_MU) is 0.
+ *   PTB_MLP_SWIGLU: MLP(a) = (silu(a W1) * (a W3)) W2, silu(u) = u sigmoid(u),
+ *     no biases.  W1 and W3 [h, f] travel as one w_fc1 [h, 2f] whose columns
+ *     are 32-wide blocks alternating W1 and W3: block 2j holds W1 columns
+ *     32j .. 32j+31 and block 2j+1 the same columns of W3; dw_fc1 has the same
+ *     layout, w_fc2 stays [f, h]; PTB_SAVED_U holds [a W1 | a W3] in that
+ *     layout ([T, 2f]) and PTB_SAVED_G silu(a W1) * (a W3) [T, f]. */
+enum ptb_norm_kind { PTB_NORM_LAYERNORM = 0, PTB_NORM_RMSNORM = 1 };
+enum ptb_mlp_kind { PTB_MLP_GELU = 0, PTB_MLP_SWIGLU = 1 };
 
 /* Version of this ABI (PTB_ABI_VERSION). */
 int32_t ptb_abi_version(void);
@@ -114,7 +131,7 @@ int32_t ptb_workspace_bytes(const ptb_dims* dims, size_t* bytes);
  *   PTB_SAVED_MU   row mean of x             fp32 [T]
  *   PTB_SAVED_RSTD 1/sqrt(var + eps)         fp32 [T]
  *   PTB_SAVED_QKV  a W_qkv                   bf16 [T, 3*h_l]
- *   PTB_SAVED_U    a W_fc1 (pre-activation)  bf16 [T, f]
+ *   PTB_SAVED_U    a W_fc1 (pre-activation)  bf16 [T, f] ([T, 2f] for SwiGLU)
  *   PTB_SAVED_G    GeLU(u)                   bf16 [T, f]
  *   PTB_SAVED_C    attention output          bf16 [T, h_l] (head-major cols)
  *   PTB_SAVED_LSE  base-2 log-sum-exp of the logits scaled by log2(e)/sqrt(d)

@@ -35,7 +35,7 @@ def oracle_run(w: I.Workload, inp: dict) -> dict:
     dy = f(inp["dy"])
     params = [{k: f(v) for k, v in lay.items()} for lay in inp["layers"]]
     y, caches = O.ptb_stack_forward(x, params, w.batch, w.seq, w.heads, w.head_dim,
-                                    w.window, w.ln_eps)
+                                    w.window, w.ln_eps, norm=w.norm, mlp=w.mlp)
     dx, grads = O.ptb_stack_backward(dy, caches, params, w.window)
     return dict(x=x, dy=dy, y=y, dx=dx, grads=grads, caches=caches)
 

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert P.ptb_abi_version() == 3
+    assert P.ptb_abi_version() == 4
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert P.ptb_status_string(code) and P.ptb_status_string(code) != "unknown status"
     assert P.ptb_status_string(12345) == "unknown status"
@@ -67,6 +67,12 @@ def good_dims(**kw):
     (dict(batch=1024, seq=1024, hidden=1024, ffn=4096), P.PTB_ERR_DIMS),
     (dict(window=1), P.PTB_OK),
     (dict(seq=1, window=10 ** 9), P.PTB_OK),
+    (dict(norm=1), P.PTB_OK),
+    (dict(mlp=1), P.PTB_OK),
+    (dict(norm=1, mlp=1), P.PTB_OK),
+    (dict(norm=2), P.PTB_ERR_ARG),
+    (dict(norm=-1), P.PTB_ERR_ARG),
+    (dict(mlp=2), P.PTB_ERR_ARG),
 ])
 def test_validate_dims(lib, kw, code):
     assert P.ptb_validate_dims(good_dims(**kw)) == code
@@ -197,3 +203,16 @@ def test_lamb_workspace_and_argument_checks(lib):
     assert P.ptb_lamb_step(hp, _lamb_list(v=A + 4), A, A, stream=0, check=False) == P.PTB_ERR_ALIGN
     assert P.ptb_lamb_step(hp, ok, 0, A, stream=0, check=False) == P.PTB_ERR_NULL
     assert P.ptb_lamb_step(hp, ok, A, A + 8, stream=0, check=False) == P.PTB_ERR_ALIGN
+
+
+def test_swiglu_widens_the_fc1_stash_and_workspace(lib):
+    T, h, hl, f = 512, 256, 256, 1024
+    g_lay = P.ptb_saved_layout(good_dims())
+    s_lay = P.ptb_saved_layout(good_dims(mlp=1))
+    assert s_lay["g"] - s_lay["u"] >= T * 2 * f * 2 > g_lay["g"] - g_lay["u"] - 256
+    assert P.ptb_saved_bytes(good_dims(mlp=1)) >= P.ptb_saved_bytes(good_dims()) + T * f * 2
+    # dZ = [dq | dk | dv | du1 du3] is T x (3 h_l + 2 f)
+    assert P.ptb_workspace_bytes(good_dims(mlp=1)) >= P.ptb_workspace_bytes(good_dims()) + T * f * 2
+    assert P.ptb_serial_saved_bytes(good_dims(mlp=1)) >= P.ptb_serial_saved_bytes(good_dims()) + T * f * 2
+    # RMSNorm changes no size
+    assert P.ptb_saved_bytes(good_dims(norm=1)) == P.ptb_saved_bytes(good_dims())

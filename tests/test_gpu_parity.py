@@ -39,6 +39,14 @@ EDGE_CASES = [
     ("single_token", W("s1", 1, 1, 128, 1, 128, 128, 1, seed=22), True),
     ("two_tokens_batch3", W("s2", 3, 2, 128, 2, 64, 128, 5, seed=23), False),
     ("stack2_small", W("st2", 2, 130, 256, 2, 128, 512, 48, layers=2, seed=24), True),
+    # the RMSNorm / SwiGLU variants (include/ptb.h, ptb_dims.norm and .mlp)
+    ("rmsnorm_tiny", W("rms", 2, 256, 256, 4, 64, 1024, 64, seed=25, norm="rmsnorm"), True),
+    ("swiglu_ragged_s200_w37", W("swi", 1, 200, 256, 2, 128, 320, 37, seed=26, mlp="swiglu"),
+     True),
+    ("rmsnorm_swiglu_d64_ragged", W("rsw", 3, 97, 320, 5, 64, 448, 33, seed=27, norm="rmsnorm",
+                                    mlp="swiglu"), True),
+    ("rmsnorm_swiglu_stack2", W("rsw2", 2, 130, 256, 2, 128, 512, 48, layers=2, seed=28,
+                                norm="rmsnorm", mlp="swiglu"), True),
 ]
 
 
@@ -108,6 +116,20 @@ def test_repeat_runs_are_bitwise_identical():
     second = [st.y, st.dx] + list(st.grads[0].values())
     for a, b in zip(first, second):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.timeout(900)
+def test_rmsnorm_swiglu_variant_at_the_175b_share():
+    """The RMSNorm + SwiGLU variant at the 175B share's full size (FFN shard
+    6144, so w_fc1 is [12288, 12288])."""
+    w = I.WORKLOADS["gpt175b_tp8_share_s2048"].replace(name="gpt175b_share_rms_swiglu",
+                                                       norm="rmsnorm", mlp="swiglu")
+    log(f"full variant workload: {w}")
+    inp = I.make_inputs(w)
+    st = run_gpu(w, inp)
+    log("[variant] gpu step done; running the oracle")
+    ref = oracle_run(w, inp)
+    compare(w, inp, ref, st)
 
 
 @pytest.mark.timeout(900)

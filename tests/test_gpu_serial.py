@@ -26,6 +26,8 @@ CASES = [
     ("window_gt_seq", W("swbig", 1, 131, 256, 3, 64, 320, 100000, seed=120), True),
     ("d64_ragged", W("sd64", 3, 97, 320, 5, 64, 448, 33, seed=121), True),
     ("single_token", W("ss1", 1, 1, 128, 1, 128, 128, 1, seed=122), True),
+    ("rmsnorm_swiglu", W("ssw", 2, 160, 256, 2, 128, 256, 40, seed=140, norm="rmsnorm",
+                         mlp="swiglu"), True),
     ("h2048_s2048_w512", I.WORKLOADS["h2048_s2048_w512"], False),
     ("gpt175b_tp8_share_s2048", I.WORKLOADS["gpt175b_tp8_share_s2048"], False),
 ]
@@ -49,7 +51,8 @@ def test_serial_block_parity(name, w, random_ln):
     f = I.bf16_bits_to_f64
     x, dy = f(inp["x"]), f(inp["dy"])
     p = {k: f(v) for k, v in inp["layers"][0].items()}
-    y, cache = O.serial_forward(x, p, w.batch, w.seq, w.heads, w.head_dim, w.window, w.ln_eps)
+    y, cache = O.serial_forward(x, p, w.batch, w.seq, w.heads, w.head_dim, w.window, w.ln_eps,
+                                norm=w.norm, mlp=w.mlp)
     g = O.serial_backward(dy, cache, p, w.window)
     errs = {"y": rel_fro(_np(blk.y), y), "dx": rel_fro(_np(blk.dx), g["dx"])}
     for key, got, ref, res in (("y-x", _np(blk.y), y, x), ("dx-dy", _np(blk.dx), g["dx"], dy)):

@@ -75,6 +75,17 @@ __device__ __forceinline__ float gelu_grad_f(float u) {
   return cdf + u * pdf;
 }
 
+// SiLU u * sigmoid(u) and its derivative s + u s (1 - s), s = sigmoid(u)
+// (SwiGLU's gate, MegaScale reading notes, section 1.3).
+__device__ __forceinline__ float sigmoid_f(float u) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-u));
+}
+__device__ __forceinline__ float silu_f(float u) { return u * sigmoid_f(u); }
+__device__ __forceinline__ float silu_grad_f(float u) {
+  const float sg = sigmoid_f(u);
+  return sg + u * sg * (1.0f - sg);
+}
+
 // LDS swizzle for tiles stored as rows of 64 bf16 (128 bytes = 8 chunks of
 // 16 bytes): chunk c of row r lives at chunk slot c ^ swz128(r).  Rows r..r+7
 // (and r..r+15 counting the row parity) read at one logical chunk land in

@@ -329,9 +329,22 @@ __device__ __forceinline__ void load16bf(const u16* p, float* v) {
 // Apply the epilogue to v[0..15] = C[r][c .. c+15].  `region` is the
 // wave-uniform side of the split the 32 x 32 block lies on (split points are
 // multiples of 64, blocks start at multiples of 32).
+// SwiGLU pair (EPI_QKV_SWIGLU, FC1 side): u1[0..15] and u3[0..15] are the
+// same rows and columns of a W1 block and its W3 block, cc the FC1-side
+// column of u1's first value.
+__device__ __forceinline__ void epi_swiglu16(const Epilogue& e, int r, int cc, float* u1,
+                                             float* u3) {
+  const int j = cc >> 6, w = cc & 31;
+  store16bf(e.o1 + r * e.ld1 + cc, u1);
+  store16bf(e.o1 + r * e.ld1 + cc + 32, u3);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) u1[i] = silu_f(u1[i]) * u3[i];
+  store16bf(e.o2 + r * e.ld2 + 32 * j + w, u1);
+}
+
 template <int MODE>
 __device__ __forceinline__ void epi_row16(const Epilogue& e, int region, int r, int c, float* v) {
-  if constexpr (MODE == EPI_QKV_GELU) {
+  if constexpr (MODE == EPI_QKV_GELU || MODE == EPI_QKV_SWIGLU) {
     const int gc = c + e.col_base;
     if (region == 0) {
       float lo[16];
@@ -351,7 +364,7 @@ __device__ __forceinline__ void epi_row16(const Epilogue& e, int region, int r, 
       o[0] = a;
       o[1] = b;
       store16bf(e.o3 + r * e.ld3 + gc, lo);
-    } else if (region == 1) {
+    } else if (region == 1 || MODE == EPI_QKV_SWIGLU) {  // SwiGLU's FC1 side: epi_swiglu16
       store16bf(e.o0 + r * e.ld0 + gc, v);
     } else {
       const int cc = gc - e.split;
@@ -377,6 +390,24 @@ __device__ __forceinline__ void epi_row16(const Epilogue& e, int region, int r, 
       for (int i = 0; i < 16; ++i) v[i] *= gelu_grad_f(u[i]);
       store16bf(e.o1 + r * e.ld1 + e.col_off1 + cc, v);
     }
+  } else if constexpr (MODE == EPI_DSWIGLU) {
+    if (region == 0) {
+      store16bf(e.o0 + r * e.ld0 + c, v);
+    } else {
+      const int cc = c - e.split;
+      const int uc = 64 * (cc >> 5) + (cc & 31);
+      float u1[16], u3[16];
+      load16bf(e.i0 + r * e.ld2 + uc, u1);
+      load16bf(e.i0 + r * e.ld2 + uc + 32, u3);
+      float d1[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        d1[i] = v[i] * u3[i] * silu_grad_f(u1[i]);
+        v[i] = v[i] * silu_f(u1[i]);
+      }
+      store16bf(e.o1 + r * e.ld1 + e.col_off1 + uc, d1);
+      store16bf(e.o1 + r * e.ld1 + e.col_off1 + uc + 32, v);
+    }
   } else if constexpr (MODE == EPI_STORE2_COLS) {
     if (region == 0) store16bf(e.o0 + r * e.ld0 + c, v);
     else store16bf(e.o1 + r * e.ld1 + (c - e.split), v);
@@ -392,10 +423,10 @@ __device__ __forceinline__ void epi_row16(const Epilogue& e, int region, int r, 
 
 template <int MODE>
 __device__ __forceinline__ int epi_region(const Epilogue& e, int r0, int cb) {
-  if constexpr (MODE == EPI_QKV_GELU) {
+  if constexpr (MODE == EPI_QKV_GELU || MODE == EPI_QKV_SWIGLU) {
     const int g = cb + e.col_base;
     return g < e.lo_cols ? 0 : (g < e.split ? 1 : 2);
-  } else if constexpr (MODE == EPI_DGELU || MODE == EPI_STORE2_COLS) {
+  } else if constexpr (MODE == EPI_DGELU || MODE == EPI_DSWIGLU || MODE == EPI_STORE2_COLS) {
     return cb < e.split ? 0 : 1;
   } else if constexpr (MODE == EPI_STORE2_ROWS) {
     return r0 < e.split ? 0 : 1;
@@ -655,6 +686,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
       int phase = nparts > 1 ? 0 : 1;
       bool summed = false;  // phase 1 on a sum of partials
       const int my_slot = part_slot(pl, item);
+      float held[MODE == EPI_QKV_SWIGLU ? 16 : 1];
       for (;;) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -695,7 +727,23 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
               const int r0 = s.m0 + wm * WM + i * 32, cb = s.n0 + wn * WN + j * 32;
               const int region = __builtin_amdgcn_readfirstlane(epi_region<MODE>(e, r0, cb));
               const int r = r0 + er;
-              if (cb < P.N && r < P.M) epi_row16<MODE>(e, region, r, cb + ec, vals);
+              if constexpr (MODE == EPI_QKV_SWIGLU) {
+                // FC1 side: the wave's two blocks are W1 and W3 of the same
+                // columns; block 0's values wait in `held` for block 1
+                static_assert(FN == 2 && WN == 64, "a wave holds one W1 | W3 pair");
+                if (region == 2) {
+                  if (j == 0) {
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) held[t] = vals[t];
+                  } else if (cb - 32 < P.N && r < P.M) {
+                    epi_swiglu16(e, r, cb - 32 + e.col_base - e.split + ec, held, vals);
+                  }
+                } else if (cb < P.N && r < P.M) {
+                  epi_row16<MODE>(e, region, r, cb + ec, vals);
+                }
+              } else {
+                if (cb < P.N && r < P.M) epi_row16<MODE>(e, region, r, cb + ec, vals);
+              }
             }
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -1125,9 +1173,12 @@ hipError_t launch_gemm_group(const GemmProblem* probs, int nprob, Major a_major,
   if (e != hipSuccess) return e;
   if (a_major == KMAJOR && b_major == OUTER_MAJOR) {
     if (mode == EPI_QKV_GELU) return launch_plan<KMAJOR, OUTER_MAJOR, EPI_QKV_GELU>(pl, grid, s);
+    if (mode == EPI_QKV_SWIGLU)
+      return launch_plan<KMAJOR, OUTER_MAJOR, EPI_QKV_SWIGLU>(pl, grid, s);
     if (mode == EPI_RESIDUAL) return launch_plan<KMAJOR, OUTER_MAJOR, EPI_RESIDUAL>(pl, grid, s);
   } else if (a_major == KMAJOR && b_major == KMAJOR) {
     if (mode == EPI_DGELU) return launch_plan<KMAJOR, KMAJOR, EPI_DGELU>(pl, grid, s);
+    if (mode == EPI_DSWIGLU) return launch_plan<KMAJOR, KMAJOR, EPI_DSWIGLU>(pl, grid, s);
     if (mode == EPI_STORE2_COLS) return launch_plan<KMAJOR, KMAJOR, EPI_STORE2_COLS>(pl, grid, s);
   } else if (a_major == OUTER_MAJOR && b_major == OUTER_MAJOR) {
     if (mode == EPI_STORE2_ROWS) return launch_plan<OUTER_MAJOR, OUTER_MAJOR, EPI_STORE2_ROWS>(pl, grid, s);

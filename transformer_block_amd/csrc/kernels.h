@@ -42,7 +42,18 @@ enum EpiMode {
                      //   v * GeLU'(i0[r*ld2 + c-split])
   EPI_STORE2_COLS = 3,  // c < split: o0[r*ld0+c]; else o1[r*ld1 + c-split]
   EPI_STORE2_ROWS = 4,  // r < split: o0[r*ld0+c]; else o1[(r-split)*ld1 + c]
-  EPI_F32 = 5           // of[r*ld0+c] = v (fp32)
+  EPI_F32 = 5,          // of[r*ld0+c] = v (fp32)
+  EPI_QKV_SWIGLU = 6,   // as EPI_QKV_GELU below `split`; at and above it the columns
+                        // are SwiGLU's [W1 | W3] in 32-wide blocks alternating W1, W3:
+                        // with cc = gc - split, the pair of blocks at cc = 64 j (W1)
+                        // and 64 j + 32 (W3) is stored as is to o1 (ld1) and
+                        // g = silu(u1) * u3 to o2[r*ld2 + 32 j ..] (eight-wave
+                        // kernel: a wave's two 32-column blocks are such a pair)
+  EPI_DSWIGLU = 7       // c < split: o0[r*ld0+c] = v; else, with cc = c - split in
+                        // [32 j, 32 j + 32) and u1, u3 read from i0 (ld2) at
+                        // columns 64 j + cc % 32 and + 32:
+                        // o1[r*ld1 + col_off1 + 64 j + cc % 32] = v * u3 * silu'(u1),
+                        // o1[... + 32] = v * silu(u1)
 };
 
 struct Epilogue {
@@ -71,7 +82,7 @@ struct GemmProblem {
 // counter per output tile.  The counters must be zero before a launch; every
 // launch leaves them zero, so launches on one stream can share them.
 constexpr int kGemmMaxWorkgroups = 256;
-constexpr int kGemmPartialSlots = 512;
+constexpr int kGemmPartialSlots = 1024;
 constexpr size_t kGemmPartialBytes =
     static_cast<size_t>(kGemmPartialSlots) * 256 * 256 * sizeof(float);
 struct GemmScratch {
@@ -101,9 +112,10 @@ hipError_t launch_gemm_group(const GemmProblem* probs, int nprob, Major a_major,
 
 // LayerNorm forward over rows of x [T, h]: a = bf16(LN(x)) and its rounding
 // residual a_lo = bf16(LN(x) - a) (skipped when a_lo is null), mu, rstd (fp32).
+// rms: RMSNorm instead (no mean, no beta; mu is written as 0).
 hipError_t launch_layernorm_fwd(const u16* x, const u16* gamma, const u16* beta,
                                 u16* a, u16* a_lo, float* mu, float* rstd, int T, int h,
-                                float eps, hipStream_t stream);
+                                float eps, hipStream_t stream, bool rms = false);
 
 // LayerNorm backward plus residual: dx = dy + LN'(da); per-block partial sums
 // of dgamma, dbeta into `partials` [nblk, 2, h], then reduced into bf16.
@@ -111,7 +123,7 @@ int layernorm_bwd_blocks(int T);
 hipError_t launch_layernorm_bwd(const u16* da, const u16* x, const u16* gamma,
                                 const float* mu, const float* rstd, const u16* dy,
                                 u16* dx, float* partials, u16* dgamma, u16* dbeta,
-                                int T, int h, hipStream_t stream);
+                                int T, int h, hipStream_t stream, bool rms = false);
 
 // Scratch of the attention launches: fp32 partial results of rows split into
 // chunks, and one arrival counter per (batch, head, row) (zero on entry, left

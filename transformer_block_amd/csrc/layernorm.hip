@@ -41,6 +41,9 @@ __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
   for (int i = 0; i < 4; ++i) { f[2 * i] = lo_bf(w[i]); f[2 * i + 1] = hi_bf(w[i]); }
 }
 
+// RMS: RMSNorm instead, a = gamma * x / sqrt(mean(x^2) + eps), no beta; the
+// row mean is stored as 0 so that the backward's xhat = (x - mu) * rstd holds.
+template <bool RMS>
 __global__ __launch_bounds__(LN_THREADS) void ln_fwd_kernel(const u16* __restrict__ x,
                                                             const u16* __restrict__ gamma,
                                                             const u16* __restrict__ beta,
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(LN_THREADS) void ln_fwd_kernel(const u16* __restric
       for (int j = 0; j < 8; ++j) sum += v[i][j];
     }
   }
-  const float mu = block_sum(sum, red) / static_cast<float>(h);
+  const float mu = RMS ? 0.0f : block_sum(sum, red) / static_cast<float>(h);
   float sq = 0.0f;
 #pragma unroll
   for (int i = 0; i < LN_MAXCH; ++i) {
@@ -84,12 +87,12 @@ __global__ __launch_bounds__(LN_THREADS) void ln_fwd_kernel(const u16* __restric
     if (c < nch) {
       float gm[8], bt[8];
       unpack8(*reinterpret_cast<const uint4*>(gamma + c * 8), gm);
-      unpack8(*reinterpret_cast<const uint4*>(beta + c * 8), bt);
+      if (!RMS) unpack8(*reinterpret_cast<const uint4*>(beta + c * 8), bt);
       uint32_t o[4], ol[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float v0 = (v[i][2 * j] - mu) * rstd * gm[2 * j] + bt[2 * j];
-        const float v1 = (v[i][2 * j + 1] - mu) * rstd * gm[2 * j + 1] + bt[2 * j + 1];
+        const float v0 = (v[i][2 * j] - mu) * rstd * gm[2 * j] + (RMS ? 0.0f : bt[2 * j]);
+        const float v1 = (v[i][2 * j + 1] - mu) * rstd * gm[2 * j + 1] + (RMS ? 0.0f : bt[2 * j + 1]);
         o[j] = pack2bf(v0, v1);
         ol[j] = pack2bf(v0 - lo_bf(o[j]), v1 - hi_bf(o[j]));
       }
@@ -144,11 +147,13 @@ __device__ __forceinline__ void load_row(LnRow<NCH>& d, const u16* da, const u16
   }
 }
 
-// NCH = 16-byte chunks of a row per thread (h <= NCH * 8 * 512).  Each row is
+// NCH = 16-byte chunks of a row per thread (h <= NCH * 8 * 512).  RMS: the
+// RMSNorm backward, dx = dy + rstd * (g - xhat * mean(g * xhat)) (no mean(g)
+// term; xhat = x * rstd from the stored mean 0), and dbeta = 0.  Each row is
 // read once, into registers, and the next row of the workgroup is loaded
 // while the current one is reduced and written, so a workgroup always has a
 // row's worth of loads in flight (two rows of registers).
-template <int NCH>
+template <int NCH, bool RMS>
 __global__ __launch_bounds__(LNB_THREADS) void ln_bwd_kernel(
     const u16* __restrict__ da, const u16* __restrict__ x, const u16* __restrict__ gamma,
     const float* __restrict__ mu, const float* __restrict__ rstd, const u16* __restrict__ dy,
@@ -190,12 +195,12 @@ __global__ __launch_bounds__(LNB_THREADS) void ln_bwd_kernel(
           s1 += gg;
           s2 += gg * xh;
           pg[i][j] += dv[j] * xh;
-          pb[i][j] += dv[j];
+          if (!RMS) pb[i][j] += dv[j];
         }
       }
     }
     const float2 sums = block_sum2(s1, s2, red);
-    const float mean_g = sums.x * inv_h, mean_gx = sums.y * inv_h;
+    const float mean_g = RMS ? 0.0f : sums.x * inv_h, mean_gx = sums.y * inv_h;
     u16* dxr = dx + static_cast<size_t>(row) * h;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -276,10 +281,10 @@ __global__ __launch_bounds__(64 * LNR_WAVES) void ln_bwd_reduce_kernel(
 
 hipError_t launch_layernorm_fwd(const u16* x, const u16* gamma, const u16* beta, u16* a,
                                 u16* a_lo, float* mu, float* rstd, int T, int h, float eps,
-                                hipStream_t s) {
+                                hipStream_t s, bool rms) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ln_fwd_kernel, dim3(T), dim3(LN_THREADS), 0, s, x, gamma, beta, a, a_lo,
-                     mu, rstd, h, eps);
+  hipLaunchKernelGGL(rms ? ln_fwd_kernel<true> : ln_fwd_kernel<false>, dim3(T), dim3(LN_THREADS),
+                     0, s, x, gamma, beta, a, a_lo, mu, rstd, h, eps);
   return hipGetLastError();
 }
 
@@ -288,12 +293,12 @@ int layernorm_bwd_blocks(int T) { return T < LN_BWD_BLOCKS ? (T < 1 ? 1 : T) : L
 hipError_t launch_layernorm_bwd(const u16* da, const u16* x, const u16* gamma,
                                 const float* mu, const float* rstd, const u16* dy, u16* dx,
                                 float* partials, u16* dgamma, u16* dbeta, int T, int h,
-                                hipStream_t s) {
+                                hipStream_t s, bool rms) {
   const int nblk = layernorm_bwd_blocks(T);
-  auto* kern = h <= 8 * LNB_THREADS    ? ln_bwd_kernel<1>
-               : h <= 16 * LNB_THREADS ? ln_bwd_kernel<2>
-               : h <= 24 * LNB_THREADS ? ln_bwd_kernel<3>
-                                       : ln_bwd_kernel<4>;
+  auto* kern = h <= 8 * LNB_THREADS    ? (rms ? ln_bwd_kernel<1, true> : ln_bwd_kernel<1, false>)
+               : h <= 16 * LNB_THREADS ? (rms ? ln_bwd_kernel<2, true> : ln_bwd_kernel<2, false>)
+               : h <= 24 * LNB_THREADS ? (rms ? ln_bwd_kernel<3, true> : ln_bwd_kernel<3, false>)
+                                       : (rms ? ln_bwd_kernel<4, true> : ln_bwd_kernel<4, false>);
   hipLaunchKernelGGL(kern, dim3(nblk), dim3(LNB_THREADS), 0, s, da, x, gamma, mu, rstd, dy, dx,
                      partials, T, h);
   hipError_t e = hipGetLastError();

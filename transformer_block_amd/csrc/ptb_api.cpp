@@ -37,6 +37,9 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 struct Shape {
   long b, s, h, n, d, f, w, T, hl, N1, K2;
+  long f1;      // FC1 output width: f (GeLU) or 2f (SwiGLU's [W1 | W3])
+  bool rms;     // RMSNorm instead of LayerNorm
+  bool swiglu;  // SwiGLU MLP instead of GeLU
 };
 
 int32_t check_dims(const ptb_dims* dims, Shape* out) {
@@ -48,12 +51,18 @@ int32_t check_dims(const ptb_dims* dims, Shape* out) {
   if (p.ffn < 64 || p.ffn % 64 != 0) return PTB_ERR_DIMS;
   if (p.window < 1) return PTB_ERR_WINDOW;
   if (!(p.ln_eps > 0.0f) || !isfinite(p.ln_eps)) return PTB_ERR_EPS;
+  if ((p.norm != PTB_NORM_LAYERNORM && p.norm != PTB_NORM_RMSNORM) ||
+      (p.mlp != PTB_MLP_GELU && p.mlp != PTB_MLP_SWIGLU))
+    return PTB_ERR_ARG;
   Shape s;
   s.b = p.batch; s.s = p.seq; s.h = p.hidden; s.n = p.heads; s.d = p.head_dim; s.f = p.ffn;
   s.w = p.window < p.seq ? p.window : p.seq;  // a window >= seq is full causal attention
   s.T = s.b * s.s;
   s.hl = s.n * s.d;
-  s.N1 = 3 * s.hl + s.f;
+  s.rms = p.norm == PTB_NORM_RMSNORM;
+  s.swiglu = p.mlp == PTB_MLP_SWIGLU;
+  s.f1 = s.swiglu ? 2 * s.f : s.f;
+  s.N1 = 3 * s.hl + s.f1;
   s.K2 = s.hl + s.f;
   const long lim = 1L << 30;
   // every tensor must stay below 2^31 bytes: kernels address it with 32-bit
@@ -78,7 +87,7 @@ SavedLayout saved_layout(const Shape& s) {
   put(PTB_SAVED_MU, s.T * 4);
   put(PTB_SAVED_RSTD, s.T * 4);
   put(PTB_SAVED_QKV, s.T * 3 * s.hl * 2);
-  put(PTB_SAVED_U, s.T * s.f * 2);
+  put(PTB_SAVED_U, s.T * s.f1 * 2);
   put(PTB_SAVED_G, s.T * s.f * 2);
   put(PTB_SAVED_C, s.T * s.hl * 2);
   put(PTB_SAVED_LSE, s.b * s.n * s.s * 4);
@@ -93,7 +102,7 @@ SavedLayout saved_layout(const Shape& s) {
 int max_gemm_tiles(const Shape& s) {
   const int T = static_cast<int>(s.T), h = static_cast<int>(s.h), hl = static_cast<int>(s.hl);
   const int K2 = static_cast<int>(s.K2), N1 = static_cast<int>(s.N1), f = static_cast<int>(s.f);
-  int m = ptb::gemm_tiles(T, 2 * hl) + ptb::gemm_tiles(T, hl + f);
+  int m = ptb::gemm_tiles(T, 2 * hl) + ptb::gemm_tiles(T, hl + static_cast<int>(s.f1));
   for (int t : {ptb::gemm_tiles(T, h), ptb::gemm_tiles(T, K2), ptb::gemm_tiles(K2, h),
                 ptb::gemm_tiles(h, N1)})
     m = t > m ? t : m;
@@ -146,7 +155,7 @@ SerialSavedLayout serial_saved_layout(const Shape& s) {
   put(PTB_SERIAL_A2, s.T * s.h * 2);
   put(PTB_SERIAL_MU2, s.T * 4);
   put(PTB_SERIAL_RSTD2, s.T * 4);
-  put(PTB_SERIAL_U, s.T * s.f * 2);
+  put(PTB_SERIAL_U, s.T * s.f1 * 2);
   put(PTB_SERIAL_G, s.T * s.f * 2);
   L.total = o;
   return L;
@@ -157,8 +166,9 @@ int serial_max_tiles(const Shape& s) {
   const int T = static_cast<int>(s.T), h = static_cast<int>(s.h), hl = static_cast<int>(s.hl);
   const int f = static_cast<int>(s.f);
   int m = ptb::gemm_tiles(T, 2 * hl) + ptb::gemm_tiles(T, hl);
-  for (int t : {ptb::gemm_tiles(T, h), ptb::gemm_tiles(T, f), ptb::gemm_tiles(f, h),
-                ptb::gemm_tiles(h, f), ptb::gemm_tiles(T, hl), ptb::gemm_tiles(hl, h),
+  const int f1 = static_cast<int>(s.f1);
+  for (int t : {ptb::gemm_tiles(T, h), ptb::gemm_tiles(T, f1), ptb::gemm_tiles(f, h),
+                ptb::gemm_tiles(h, f1), ptb::gemm_tiles(T, hl), ptb::gemm_tiles(hl, h),
                 ptb::gemm_tiles(h, 3 * hl)})
     m = t > m ? t : m;
   const long rows = s.b * s.n * ((s.s + 127) / 128);
@@ -179,7 +189,7 @@ SerialWorkLayout serial_work_layout(const Shape& s) {
   W.max_tiles = serial_max_tiles(s);
   W.gemm_partials = o; o = align_up(o + ptb::kGemmPartialBytes);
   W.counters = o; o = align_up(o + static_cast<size_t>(W.max_tiles) * 4);
-  W.du = o; o = align_up(o + s.T * s.f * 2);
+  W.du = o; o = align_up(o + s.T * s.f1 * 2);
   W.da = o; o = align_up(o + s.T * s.h * 2);
   W.dx1 = o; o = align_up(o + s.T * s.h * 2);
   W.dc = o; o = align_up(o + s.T * s.hl * 2);
@@ -255,7 +265,7 @@ const char* ptb_status_string(int32_t status) {
     case PTB_ERR_WINDOW: return "window must be >= 1";
     case PTB_ERR_EPS: return "ln_eps must be a finite positive number";
     case PTB_ERR_HIP: return "a HIP kernel launch failed";
-    case PTB_ERR_ARG: return "invalid optimizer hyper-parameters or tensor list";
+    case PTB_ERR_ARG: return "invalid layer variant, optimizer hyper-parameters or tensor list";
     default: return "unknown status";
   }
 }
@@ -321,13 +331,14 @@ int32_t ptb_forward_timed(const ptb_dims* dims, const void* x, const void* ln_ga
   PTB_STAGE(0, ptb::launch_layernorm_fwd(X, static_cast<const u16*>(ln_gamma),
                                     static_cast<const u16*>(ln_beta), a, a_lo, mu, rstd,
                                     static_cast<int>(s.T), static_cast<int>(s.h), dims->ln_eps,
-                                    strm));
+                                    strm, s.rms));
   {  // [QKV | FC1] projection in one launch of two products:
      //   [q | k] = [a | a_lo] x [W_q|k ; W_q|k]   (stored as value + residual)
      //   [v | u] = a x [W_v | W_fc1], with g = GeLU(u) on the FC1 columns
+     //   (SwiGLU: u = [u1 | u3] in 32-column blocks, g = silu(u1) * u3)
     ptb::Epilogue e{};
     e.o0 = qkv; e.ld0 = static_cast<int>(3 * s.hl);
-    e.o1 = u; e.o2 = g; e.ld1 = static_cast<int>(s.f);
+    e.o1 = u; e.o2 = g; e.ld1 = static_cast<int>(s.f1); e.ld2 = static_cast<int>(s.f);
     e.o3 = qk_lo; e.ld3 = static_cast<int>(2 * s.hl); e.lo_cols = static_cast<int>(2 * s.hl);
     e.split = static_cast<int>(3 * s.hl);
     ptb::GemmProblem pr[2];
@@ -337,16 +348,17 @@ int32_t ptb_forward_timed(const ptb_dims* dims, const void* x, const void* ln_ga
     pr[0].B = two(Wqkv, 3 * s.hl, s.h, Wqkv, 3 * s.hl, s.h, s.h, 1);
     pr[0].epi = e;
     pr[0].epi.col_base = 0;
-    pr[1].M = static_cast<int>(s.T); pr[1].N = static_cast<int>(s.hl + s.f);
+    pr[1].M = static_cast<int>(s.T); pr[1].N = static_cast<int>(s.hl + s.f1);
     pr[1].K = static_cast<int>(s.h);
     pr[1].A = one(a, s.h, s.T);
-    pr[1].B = two(Wqkv + 2 * s.hl, 3 * s.hl, s.h, static_cast<const u16*>(w_fc1), s.f, s.h,
+    pr[1].B = two(Wqkv + 2 * s.hl, 3 * s.hl, s.h, static_cast<const u16*>(w_fc1), s.f1, s.h,
                   s.hl, 0);
     pr[1].B.bytes0 = view_bytes(3 * s.hl, s.h, s.hl);
     pr[1].epi = e;
     pr[1].epi.col_base = static_cast<int>(2 * s.hl);
     PTB_STAGE(1, ptb::launch_gemm_group(pr, 2, ptb::KMAJOR, ptb::OUTER_MAJOR,
-                                        ptb::EPI_QKV_GELU, gs, strm));
+                                        s.swiglu ? ptb::EPI_QKV_SWIGLU : ptb::EPI_QKV_GELU, gs,
+                                        strm));
   }
   const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
                             gs.max_tiles, ptb::device_compute_units()};
@@ -403,16 +415,17 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
   PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
 
   {  // dgrad through [O ; FC2]: dc, and du = dg * GeLU'(u) into dZ's FC1 columns
+     // (SwiGLU: du1 = dg * u3 * silu'(u1), du3 = dg * silu(u1))
     ptb::Epilogue e{};
     e.o0 = dc; e.ld0 = static_cast<int>(s.hl);
     e.o1 = dz; e.ld1 = static_cast<int>(s.N1); e.col_off1 = static_cast<int>(3 * s.hl);
-    e.i0 = u; e.ld2 = static_cast<int>(s.f);
+    e.i0 = u; e.ld2 = static_cast<int>(s.f1);
     e.split = static_cast<int>(s.hl);
     PTB_STAGE(0, ptb::launch_gemm(
         T, static_cast<int>(s.K2), h, one(DY, s.h, s.T), ptb::KMAJOR,
         two(static_cast<const u16*>(w_o), s.h, s.hl, static_cast<const u16*>(w_fc2), s.h, s.f,
             s.hl, 0),
-        ptb::KMAJOR, ptb::EPI_DGELU, e, gs, strm));
+        ptb::KMAJOR, s.swiglu ? ptb::EPI_DSWIGLU : ptb::EPI_DGELU, e, gs, strm));
   }
   const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
                             gs.max_tiles, ptb::device_compute_units()};
@@ -435,14 +448,14 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
     e.split = h;  // one output
     PTB_STAGE(3, ptb::launch_gemm(
         T, h, static_cast<int>(s.N1), one(dz, s.N1, s.T), ptb::KMAJOR,
-        two(static_cast<const u16*>(w_qkv), 3 * s.hl, s.h, static_cast<const u16*>(w_fc1), s.f,
+        two(static_cast<const u16*>(w_qkv), 3 * s.hl, s.h, static_cast<const u16*>(w_fc1), s.f1,
             s.h, 3 * s.hl, 1),
         ptb::KMAJOR, ptb::EPI_STORE2_COLS, e, gs, strm));
   }
   {  // wgrad of [QKV | FC1]: a^T dZ
     ptb::Epilogue e{};
     e.o0 = static_cast<u16*>(dw_qkv); e.ld0 = static_cast<int>(3 * s.hl);
-    e.o1 = static_cast<u16*>(dw_fc1); e.ld1 = static_cast<int>(s.f);
+    e.o1 = static_cast<u16*>(dw_fc1); e.ld1 = static_cast<int>(s.f1);
     e.split = static_cast<int>(3 * s.hl);
     PTB_STAGE(4, ptb::launch_gemm(h, static_cast<int>(s.N1), T, one(a, s.h, s.T), ptb::OUTER_MAJOR,
                              one(dz, s.N1, s.T), ptb::OUTER_MAJOR, ptb::EPI_STORE2_COLS, e, gs,
@@ -452,7 +465,7 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
                                     static_cast<const u16*>(ln_gamma), mu, rstd, DY,
                                     static_cast<u16*>(dx), partials,
                                     static_cast<u16*>(d_ln_gamma), static_cast<u16*>(d_ln_beta),
-                                    T, h, strm));
+                                    T, h, strm, s.rms));
   return PTB_OK;
 }
 
@@ -538,7 +551,7 @@ int32_t ptb_serial_forward_timed(const ptb_dims* dims, const void* x, const void
   PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
   PTB_STAGE(0, ptb::launch_layernorm_fwd(X, static_cast<const u16*>(ln1_gamma),
                                          static_cast<const u16*>(ln1_beta), a1, a1_lo, mu1,
-                                         rstd1, T, h, dims->ln_eps, strm));
+                                         rstd1, T, h, dims->ln_eps, strm, s.rms));
   {  // QKV projection, one launch of two products: [q | k] from [a1 | a1_lo]
      // (value + residual, as in the parallel block) and v from a1
     ptb::Epilogue e{};
@@ -574,14 +587,17 @@ int32_t ptb_serial_forward_timed(const ptb_dims* dims, const void* x, const void
   }
   PTB_STAGE(4, ptb::launch_layernorm_fwd(x1, static_cast<const u16*>(ln2_gamma),
                                          static_cast<const u16*>(ln2_beta), a2, nullptr, mu2,
-                                         rstd2, T, h, dims->ln_eps, strm));
-  {  // u = a2 W_fc1, g = GeLU(u): every column on the FC1 side of the split
+                                         rstd2, T, h, dims->ln_eps, strm, s.rms));
+  {  // u = a2 W_fc1, g = GeLU(u) (SwiGLU: silu(u1) * u3): every column on the
+     // FC1 side of the split
     ptb::Epilogue e{};
-    e.o1 = u; e.o2 = g; e.ld1 = static_cast<int>(s.f);
+    e.o1 = u; e.o2 = g; e.ld1 = static_cast<int>(s.f1); e.ld2 = static_cast<int>(s.f);
     e.split = 0; e.lo_cols = 0; e.col_base = 0;
-    PTB_STAGE(5, ptb::launch_gemm(T, static_cast<int>(s.f), h, one(a2, s.h, s.T), ptb::KMAJOR,
-                                  one(static_cast<const u16*>(w_fc1), s.f, s.h),
-                                  ptb::OUTER_MAJOR, ptb::EPI_QKV_GELU, e, gs, strm));
+    PTB_STAGE(5, ptb::launch_gemm(T, static_cast<int>(s.f1), h, one(a2, s.h, s.T), ptb::KMAJOR,
+                                  one(static_cast<const u16*>(w_fc1), s.f1, s.h),
+                                  ptb::OUTER_MAJOR,
+                                  s.swiglu ? ptb::EPI_QKV_SWIGLU : ptb::EPI_QKV_GELU, e, gs,
+                                  strm));
   }
   {  // y = x1 + g W_fc2
     ptb::Epilogue e{};
@@ -636,16 +652,18 @@ int32_t ptb_serial_backward_timed(const ptb_dims* dims, const void* dy, const vo
   const u16* DY = static_cast<const u16*>(dy);
   const int T = static_cast<int>(s.T), h = static_cast<int>(s.h);
   const int hl = static_cast<int>(s.hl), f = static_cast<int>(s.f);
+  const int f1 = static_cast<int>(s.f1);
 
   PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
-  {  // du = (dy W_fc2^T) * GeLU'(u): every column on the GeLU side of the split
+  {  // du = (dy W_fc2^T) * GeLU'(u) (SwiGLU: du1, du3): every column on the
+     // activation side of the split
     ptb::Epilogue e{};
-    e.o1 = du; e.ld1 = f; e.col_off1 = 0;
-    e.i0 = u; e.ld2 = f;
+    e.o1 = du; e.ld1 = f1; e.col_off1 = 0;
+    e.i0 = u; e.ld2 = f1;
     e.split = 0;
     PTB_STAGE(0, ptb::launch_gemm(T, f, h, one(DY, s.h, s.T), ptb::KMAJOR,
                                   one(static_cast<const u16*>(w_fc2), s.h, s.f), ptb::KMAJOR,
-                                  ptb::EPI_DGELU, e, gs, strm));
+                                  s.swiglu ? ptb::EPI_DSWIGLU : ptb::EPI_DGELU, e, gs, strm));
   }
   {  // dW_fc2 = g^T dy
     ptb::Epilogue e{};
@@ -658,21 +676,22 @@ int32_t ptb_serial_backward_timed(const ptb_dims* dims, const void* dy, const vo
     ptb::Epilogue e{};
     e.o0 = da; e.ld0 = h;
     e.split = h;
-    PTB_STAGE(2, ptb::launch_gemm(T, h, f, one(du, s.f, s.T), ptb::KMAJOR,
-                                  one(static_cast<const u16*>(w_fc1), s.f, s.h), ptb::KMAJOR,
+    PTB_STAGE(2, ptb::launch_gemm(T, h, f1, one(du, s.f1, s.T), ptb::KMAJOR,
+                                  one(static_cast<const u16*>(w_fc1), s.f1, s.h), ptb::KMAJOR,
                                   ptb::EPI_STORE2_COLS, e, gs, strm));
   }
   {  // dW_fc1 = a2^T du
     ptb::Epilogue e{};
-    e.o0 = static_cast<u16*>(dw_fc1); e.ld0 = f;
-    e.split = f;
-    PTB_STAGE(3, ptb::launch_gemm(h, f, T, one(a2, s.h, s.T), ptb::OUTER_MAJOR, one(du, s.f, s.T),
-                                  ptb::OUTER_MAJOR, ptb::EPI_STORE2_COLS, e, gs, strm));
+    e.o0 = static_cast<u16*>(dw_fc1); e.ld0 = f1;
+    e.split = f1;
+    PTB_STAGE(3, ptb::launch_gemm(h, f1, T, one(a2, s.h, s.T), ptb::OUTER_MAJOR,
+                                  one(du, s.f1, s.T), ptb::OUTER_MAJOR, ptb::EPI_STORE2_COLS, e,
+                                  gs, strm));
   }
   // dx1 = dy + LN2'(da2)
   PTB_STAGE(4, ptb::launch_layernorm_bwd(da, x1, static_cast<const u16*>(ln2_gamma), mu2, rstd2,
                                          DY, dx1, partials, static_cast<u16*>(d_ln2_gamma),
-                                         static_cast<u16*>(d_ln2_beta), T, h, strm));
+                                         static_cast<u16*>(d_ln2_beta), T, h, strm, s.rms));
   {  // dc = dx1 W_o^T
     ptb::Epilogue e{};
     e.o0 = dc; e.ld0 = hl;
@@ -716,7 +735,7 @@ int32_t ptb_serial_backward_timed(const ptb_dims* dims, const void* dy, const vo
                                           static_cast<const u16*>(ln1_gamma), mu1, rstd1, dx1,
                                           static_cast<u16*>(dx), partials,
                                           static_cast<u16*>(d_ln1_gamma),
-                                          static_cast<u16*>(d_ln1_beta), T, h, strm));
+                                          static_cast<u16*>(d_ln1_beta), T, h, strm, s.rms));
   return PTB_OK;
 }
 

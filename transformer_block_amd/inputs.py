@@ -44,6 +44,8 @@ class Workload:
     layers: int = 1
     seed: int = 1000
     ln_eps: float = 1e-5
+    norm: str = "layernorm"   # or "rmsnorm"
+    mlp: str = "gelu"         # or "swiglu" (W1 | W3 in w_fc1, 32-column blocks)
 
     @property
     def tokens(self) -> int:
@@ -52,6 +54,11 @@ class Workload:
     @property
     def h_local(self) -> int:
         return self.heads * self.head_dim
+
+    @property
+    def fc1_width(self) -> int:
+        """Columns of w_fc1: f, or 2f for SwiGLU's [W1 | W3]."""
+        return 2 * self.ffn if self.mlp == "swiglu" else self.ffn
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -117,7 +124,8 @@ def make_inputs(w: Workload, seed: int | None = None,
 
     Returns a dict with ``x [T,h]``, ``dy [T,h]`` and a list ``layers`` of dicts
     holding ``ln_gamma [h]``, ``ln_beta [h]``, ``w_qkv [h, 3*h_l]``,
-    ``w_o [h_l, h]``, ``w_fc1 [h, f]``, ``w_fc2 [f, h]`` and the serial block's
+    ``w_o [h_l, h]``, ``w_fc1 [h, f]`` (``[h, 2f]`` for SwiGLU),
+    ``w_fc2 [f, h]`` and the serial block's
     ``ln2_gamma [h]``, ``ln2_beta [h]`` (all ``uint16``).
     """
     rng = np.random.default_rng(w.seed if seed is None else seed)
@@ -128,7 +136,7 @@ def make_inputs(w: Workload, seed: int | None = None,
         layers.append({
             "w_qkv": _normal_bf16(rng, (h, 3 * hl), 0.02),
             "w_o": _normal_bf16(rng, (hl, h), 0.02),
-            "w_fc1": _normal_bf16(rng, (h, f), 0.02),
+            "w_fc1": _normal_bf16(rng, (h, w.fc1_width), 0.02),
             "w_fc2": _normal_bf16(rng, (f, h), 0.02),
         })
     out["dy"] = _normal_bf16(rng, (T, h), 1.0)

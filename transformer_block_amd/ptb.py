@@ -44,13 +44,20 @@ class ptb_dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seq", ctypes.c_int32),
                 ("hidden", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
-                ("window", ctypes.c_int32), ("ln_eps", ctypes.c_float)]
+                ("window", ctypes.c_int32), ("ln_eps", ctypes.c_float),
+                ("norm", ctypes.c_int32), ("mlp", ctypes.c_int32)]
+
+
+PTB_NORM_LAYERNORM, PTB_NORM_RMSNORM = 0, 1
+PTB_MLP_GELU, PTB_MLP_SWIGLU = 0, 1
+NORM_KINDS = {"layernorm": PTB_NORM_LAYERNORM, "rmsnorm": PTB_NORM_RMSNORM}
+MLP_KINDS = {"gelu": PTB_MLP_GELU, "swiglu": PTB_MLP_SWIGLU}
 
 
 def dims_of(w) -> ptb_dims:
     """ptb_dims of a Workload (transformer_block_amd.inputs)."""
     return ptb_dims(w.batch, w.seq, w.hidden, w.heads, w.head_dim, w.ffn, w.window,
-                    w.ln_eps)
+                    w.ln_eps, NORM_KINDS[w.norm], MLP_KINDS[w.mlp])
 
 
 class ptb_lamb_hyper(ctypes.Structure):

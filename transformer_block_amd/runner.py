@@ -98,7 +98,7 @@ class LayerStack:
         T, h, hl, f = w.tokens, w.hidden, w.h_local, w.ffn
         shapes = {"a": ((T, h), torch.bfloat16), "mu": ((T,), torch.float32),
                   "rstd": ((T,), torch.float32), "qkv": ((T, 3 * hl), torch.bfloat16),
-                  "u": ((T, f), torch.bfloat16), "g": ((T, f), torch.bfloat16),
+                  "u": ((T, w.fc1_width), torch.bfloat16), "g": ((T, f), torch.bfloat16),
                   "c": ((T, hl), torch.bfloat16),
                   "lse": ((w.batch, w.heads, w.seq), torch.float32),
                   "a_lo": ((T, h), torch.bfloat16), "qk_lo": ((T, 2 * hl), torch.bfloat16)}
@@ -164,7 +164,7 @@ class SerialBlock:
                   "a1_lo": ((T, h), bf), "qkv": ((T, 3 * hl), bf), "qk_lo": ((T, 2 * hl), bf),
                   "c": ((T, hl), bf), "lse": ((w.batch, w.heads, w.seq), f32),
                   "x1": ((T, h), bf), "a2": ((T, h), bf), "mu2": ((T,), f32),
-                  "rstd2": ((T,), f32), "u": ((T, f), bf), "g": ((T, f), bf)}
+                  "rstd2": ((T,), f32), "u": ((T, w.fc1_width), bf), "g": ((T, f), bf)}
         off = P.ptb_serial_saved_layout(self.dims)[name]
         shape, dt = shapes[name]
         nbytes = int(np.prod(shape)) * (2 if dt == bf else 4)
