@@ -6,19 +6,25 @@ namespace ptb {
 namespace {
 
 // ------------------------------------------------------------------ forward
-// Stage of 64 keys in LDS, filled by DMA one tile ahead of the matrix cores,
+// Stage of BKF keys in LDS, filled by DMA one tile ahead of the matrix cores,
 // two stages: K and K_lo row-major (read by row_frag), V in the outer layout
 // with its rows in the S^T accumulator's key order (read transposed).
 constexpr float kStale = 8.0f;
 
+// Keys per LDS tile: 32 keys keep the two stages at 48 KB for D = 128, so two
+// workgroups share a CU and one's softmax and barrier waits run beside the
+// other's MFMAs (64-key tiles, 96 KB, allow one).
+constexpr int BKF = 32;
+constexpr int KB = BKF / 32;  // 32 x 32 S^T blocks per tile
+
 template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ qkv,
+__global__ __launch_bounds__(256, BKF == 32 ? 2 : 1) void attn_fwd_kernel(const u16* __restrict__ qkv,
                                                        const u16* __restrict__ qk_lo,
                                                        u16* __restrict__ cout,
                                                        float* __restrict__ lse, int s, int n,
                                                        int window, int nqt, RowSplit rs) {
   constexpr int NKS = D / 16, ND = D / 32;
-  constexpr int OPB = 64 * D;  // u16 elements of one operand's tile
+  constexpr int OPB = BKF * D;  // u16 elements of one operand's tile
   __shared__ __attribute__((aligned(1024))) u16 kv[2 * 3 * OPB];
   __shared__ int arrival;
 
@@ -39,8 +45,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ q
 
   const int kv_begin = item.span.begin;
   const int kv_end = item.span.end;
-  TileDma<D, 64, false> dk, dkl;
-  TileDma<D, 64, true> dv;
+  TileDma<D, BKF, false> dk, dkl;
+  TileDma<D, BKF, true> dv;
   dk.init(Kg, ld, s, wave, lane);
   dkl.init(Klg, 2 * hl, s, wave, lane);
   dv.init(Vg, ld, s, wave, lane);
@@ -74,22 +80,22 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ q
     for (int e = 0; e < 16; ++e) o[db][e] = 0.0f;
 
   int stage = 0;
-  for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKV) {
+  for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKF) {
     wait_vm_lds<0>();  // this wave's loads of tile kt0 landed
     __syncthreads();   // every wave's; the other stage is free again
-    if (kt0 + BKV < kv_end) issue(kv_lds + (stage ^ 1) * (3 * OPB * 2), kt0 + BKV);
+    if (kt0 + BKF < kv_end) issue(kv_lds + (stage ^ 1) * (3 * OPB * 2), kt0 + BKF);
     const u16* k_lds = kv + stage * 3 * OPB;
     const u16* kl_lds = k_lds + OPB;
     const u16* v_lds = k_lds + 2 * OPB;
     stage ^= 1;
 
-    const bool any = qw0 < s && qw0 + 31 >= kt0 && qw0 - (kt0 + BKV - 1) < window;
+    const bool any = qw0 < s && qw0 + 31 >= kt0 && qw0 - (kt0 + BKF - 1) < window;
     if (!any) continue;
-    const bool full = kt0 + BKV - 1 <= qw0 && qw0 + 31 - kt0 < window && kt0 + BKV <= s;
+    const bool full = kt0 + BKF - 1 <= qw0 && qw0 + 31 - kt0 < window && kt0 + BKF <= s;
 
-    f32x16 st[2];
+    f32x16 st[KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) st[kb][e] = 0.0f;
 #pragma unroll
@@ -103,7 +109,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ q
     float mx = -INFINITY;
     if (full) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st[kb][e]);
     } else {
@@ -114,7 +120,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ q
       const int lo = max(qi - window + 1, 0) - base;
       const int hi = min(qi, s - 1) - base;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int off = kb * 32 + (e >> 2) * 8 + (e & 3);
@@ -143,7 +149,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ q
     const float msafe = (m == -INFINITY) ? 0.0f : m;
     float rsum = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float p = __builtin_amdgcn_exp2f(fmaf(st[kb][e], sc, -msafe));
@@ -152,13 +158,13 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const u16* __restrict__ q
       }
     l += rsum;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int e2 = 0; e2 < 2; ++e2) {
         const bf16x8 pb = pack8(st[kb], e2 * 8);
 #pragma unroll
         for (int db = 0; db < ND; ++db)
-          o[db] = mfma32x32x16(frag_outer<64>(v_lds, db * 32, kb * 2 + e2, lane), pb, o[db]);
+          o[db] = mfma32x32x16(frag_outer<BKF>(v_lds, db * 32, kb * 2 + e2, lane), pb, o[db]);
       }
   }
 
