@@ -69,11 +69,11 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const u16* __restrict__
 
 // ------------------------------------------------------------ dK and dV
 // Key rows of 128 (4 waves x 32, lane = key), query stages of QS = 32 staged
-// by DMA one stage ahead, two stages of five tiles: Q, Q_lo and dO row-major
-// (A operands of S = Q K^T and dP = dO V^T) and Q and dO once more in the
-// outer layout, rows in the accumulator's order, for the transposed A
-// operands of dK^T += Q^T dS and dV^T += dO^T P.  The stage's log-sum-exp
-// and delta go to LDS through registers, loaded one stage ahead.
+// by DMA one stage ahead, two stages of three row-major tiles: Q, Q_lo and dO
+// (A operands of S = Q K^T and dP = dO V^T, and, read transposed with the
+// rows in the accumulator's order, of dK^T += Q^T dS and dV^T += dO^T P).
+// The stage's log-sum-exp and delta go to LDS through registers, loaded one
+// stage ahead.
 constexpr int QS = 32;
 
 template <int D>
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     int ld_dz, int s, int n, int window, int nkt, RowSplit rsp) {
   constexpr int NKS = D / 16, ND = D / 32;
   constexpr int OPB = QS * D;  // u16 elements of one operand's tile
-  constexpr int STG = 5 * OPB;
+  constexpr int STG = 3 * OPB;
   __shared__ __attribute__((aligned(1024))) u16 qs[2 * STG];
   __shared__ __attribute__((aligned(16))) float ld_lds[2][2][QS];  // [stage][lse, delta][query]
   __shared__ int arrival;
@@ -108,19 +108,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const int q_begin = item.span.begin;
   const int q_end = item.span.end;
   TileDma<D, QS, false> dq_r, dql_r, do_r;
-  TileDma<D, QS, true> dq_t, do_t;
   dq_r.init(Qg, ld, s, wave, lane);
   dql_r.init(Qlg, 2 * hl, s, wave, lane);
   do_r.init(dOg, hl, s, wave, lane);
-  dq_t.init(Qg, ld, s, wave, lane);
-  do_t.init(dOg, hl, s, wave, lane);
   const uint32_t qs_lds = __builtin_amdgcn_readfirstlane(lds_address(qs));
   auto issue = [&](uint32_t lds, int qt0) {
     dq_r.issue(lds, qt0, wave);
     dql_r.issue(lds + OPB * 2, qt0, wave);
     do_r.issue(lds + 2 * OPB * 2, qt0, wave);
-    dq_t.issue(lds + 3 * OPB * 2, qt0, wave);
-    do_t.issue(lds + 4 * OPB * 2, qt0, wave);
   };
   // log-sum-exp (threads 0..31) and delta (32..63) of one stage's queries
   auto load_ld = [&](int qt0) {
@@ -166,24 +161,23 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const u16* q_lds = qs + stage * STG;
     const u16* ql_lds = q_lds + OPB;
     const u16* do_lds = q_lds + 2 * OPB;
-    const u16* qt_lds = q_lds + 3 * OPB;
-    const u16* dot_lds = q_lds + 4 * OPB;
     const float* lse_s = ld_lds[stage][0];
     const float* dl_s = ld_lds[stage][1];
 
     const bool any = kw0 < s && qt0 + QS - 1 >= kw0 && qt0 - (kw0 + 31) < window;
     if (any) {
       const bool full = qt0 >= kw0 + 31 && qt0 + QS - 1 - kw0 < window && qt0 + QS <= s;
-      f32x16 sp, dp;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) { sp[e] = 0.0f; dp[e] = 0.0f; }
+      // each chain's first product takes a literal zero accumulator (no
+      // per-stage zeroing copies of the accumulator registers)
+      const f32x16 zero = {};
+      f32x16 sp = zero, dp = zero;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const bf16x8 qh = row_frag<D>(q_lds, l32, ks * 2 + g);
-        sp = mfma32x32x16(qh, kf[ks], sp);
+        sp = mfma32x32x16(qh, kf[ks], ks == 0 ? zero : sp);
         sp = mfma32x32x16(row_frag<D>(ql_lds, l32, ks * 2 + g), kf[ks], sp);
         sp = mfma32x32x16(qh, kl[ks], sp);
-        dp = mfma32x32x16(row_frag<D>(do_lds, l32, ks * 2 + g), vf[ks], dp);
+        dp = mfma32x32x16(row_frag<D>(do_lds, l32, ks * 2 + g), vf[ks], ks == 0 ? zero : dp);
       }
       if (!full) {
         // a stage on the diagonal or the window's edge: keep queries in
@@ -219,8 +213,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
         const bf16x8 dsb = pack8(dp, e2 * 8);
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
-          dv[db] = mfma32x32x16(frag_outer<QS>(dot_lds, db * 32, e2, lane), pb, dv[db]);
-          dk[db] = mfma32x32x16(frag_outer<QS>(qt_lds, db * 32, e2, lane), dsb, dk[db]);
+          dv[db] = mfma32x32x16(frag_rows_tr<D>(do_lds, db * 32, e2, lane), pb, dv[db]);
+          dk[db] = mfma32x32x16(frag_rows_tr<D>(q_lds, db * 32, e2, lane), dsb, dk[db]);
         }
       }
     }
@@ -286,9 +280,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 
 // ------------------------------------------------------------------- dQ
 // Query rows of 128 (4 waves x 32), key tiles of 64 staged by DMA one tile
-// ahead, two stages of four tiles: K, K_lo and V row-major (the A operands of
-// S^T = K Q^T and dP^T = V dO^T) and K once more in the outer layout, rows in
-// the accumulator's order, for the transposed A operand of dQ^T += K^T dS^T.
+// ahead, two stages of three row-major tiles: K, K_lo and V (the A operands
+// of S^T = K Q^T and dP^T = V dO^T; K read transposed, rows in the
+// accumulator's order, is also the A operand of dQ^T += K^T dS^T).
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const u16* __restrict__ qkv, const u16* __restrict__ qk_lo, const u16* __restrict__ dcg,
@@ -296,7 +290,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     int ld_dz, int s, int n, int window, int nqt, RowSplit rsp) {
   constexpr int NKS = D / 16, ND = D / 32;
   constexpr int OPB = 64 * D;  // u16 elements of one operand's tile
-  __shared__ __attribute__((aligned(1024))) u16 kv[2 * 4 * OPB];
+  __shared__ __attribute__((aligned(1024))) u16 kv[2 * 3 * OPB];
   __shared__ int arrival;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -318,17 +312,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const int kv_begin = item.span.begin;
   const int kv_end = item.span.end;
   TileDma<D, 64, false> dk, dkl, dv;
-  TileDma<D, 64, true> dkt;
   dk.init(Kg, ld, s, wave, lane);
   dkl.init(Klg, 2 * hl, s, wave, lane);
   dv.init(Vg, ld, s, wave, lane);
-  dkt.init(Kg, ld, s, wave, lane);
   const uint32_t kv_lds = __builtin_amdgcn_readfirstlane(lds_address(kv));
   auto issue = [&](uint32_t lds, int kt0) {
     dk.issue(lds, kt0, wave);
     dkl.issue(lds + OPB * 2, kt0, wave);
     dv.issue(lds + 2 * OPB * 2, kt0, wave);
-    dkt.issue(lds + 3 * OPB * 2, kt0, wave);
   };
   if (kv_begin < kv_end) issue(kv_lds, kv_begin);
 
@@ -360,29 +351,31 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKV) {
     wait_vm_lds<0>();  // this wave's loads of tile kt0 landed
     __syncthreads();   // every wave's; the other stage is free again
-    if (kt0 + BKV < kv_end) issue(kv_lds + (stage ^ 1) * (4 * OPB * 2), kt0 + BKV);
-    const u16* k_lds = kv + stage * 4 * OPB;
+    if (kt0 + BKV < kv_end) issue(kv_lds + (stage ^ 1) * (3 * OPB * 2), kt0 + BKV);
+    const u16* k_lds = kv + stage * 3 * OPB;
     const u16* kl_lds = k_lds + OPB;
     const u16* v_lds = k_lds + 2 * OPB;
-    const u16* kt_lds = k_lds + 3 * OPB;
     stage ^= 1;
 
     const bool any = qw0 < s && qw0 + 31 >= kt0 && qw0 - (kt0 + BKV - 1) < window;
     if (!any) continue;
     const bool full = kt0 + BKV - 1 <= qw0 && qw0 + 31 - kt0 < window && kt0 + BKV <= s;
 
+    // each chain's first product takes a literal zero accumulator
+    const f32x16 zero = {};
     f32x16 st[2], dpt[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) { st[kb][e] = 0.0f; dpt[kb][e] = 0.0f; }
+      st[kb] = zero;
+      dpt[kb] = zero;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const bf16x8 kh = row_frag<D>(k_lds, kb * 32 + l32, ks * 2 + g);
-        st[kb] = mfma32x32x16(kh, qf[ks], st[kb]);
+        st[kb] = mfma32x32x16(kh, qf[ks], ks == 0 ? zero : st[kb]);
         st[kb] = mfma32x32x16(row_frag<D>(kl_lds, kb * 32 + l32, ks * 2 + g), qf[ks], st[kb]);
         st[kb] = mfma32x32x16(kh, ql[ks], st[kb]);
-        dpt[kb] = mfma32x32x16(row_frag<D>(v_lds, kb * 32 + l32, ks * 2 + g), of[ks], dpt[kb]);
+        dpt[kb] = mfma32x32x16(row_frag<D>(v_lds, kb * 32 + l32, ks * 2 + g), of[ks],
+                               ks == 0 ? zero : dpt[kb]);
       }
     }
     if (!full) {
@@ -414,7 +407,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
         const bf16x8 dsb = pack8(st[kb], e2 * 8);
 #pragma unroll
         for (int db = 0; db < ND; ++db)
-          dq[db] = mfma32x32x16(frag_outer<64>(kt_lds, db * 32, kb * 2 + e2, lane), dsb, dq[db]);
+          dq[db] = mfma32x32x16(frag_rows_tr<D>(k_lds, db * 32, kb * 2 + e2, lane), dsb, dq[db]);
       }
   }
 

@@ -33,6 +33,38 @@ __device__ __forceinline__ bf16x8 row_frag(const u16* base, int r, int c) {
   return as_bf16x8(*reinterpret_cast<const uint4*>(base + r * D + ((c ^ rowswz<D>(r)) << 3)));
 }
 
+// perm16 swaps rows 4..7 and 8..11 inside every 16 (see the DMA-staged
+// tiles below).
+__device__ __forceinline__ int perm16(int r) {
+  const int p = r & 15;
+  return (r & ~15) | ((p >= 4 && p < 12) ? (p ^ 12) : p);
+}
+
+// MFMA A operand of the transpose of a row tile [R][D] (rows swizzled by
+// rowswz<D>) over columns [rb, rb + 32) and the 16 tile rows of step ks, the
+// rows taken in perm16 order (the order in which a packed 32 x 32 accumulator
+// runs over them): lane l gets X^T[rb + l % 32][perm16(16 ks + 8 (l / 32) ..
+// +7)].  Each 16-lane group reads 4 rows x 16 columns (4 u16 per lane, 8
+// bytes inside one 16-byte chunk), transposed by ds_read_b64_tr_b16.
+template <int D>
+__device__ __forceinline__ bf16x8 frag_rows_tr(const u16* tile, int rb, int ks, int lane) {
+  const int q = lane >> 4, j = lane & 15;
+  const int m = rb + 16 * (q & 1) + 4 * (j & 3);
+  v4s h[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int kk = ks * 16 + 8 * (q >> 1) + 4 * hh + (j >> 2);
+    const int r = perm16(kk);
+    h[hh] = lds_read_tr16(tile + r * D + (((m >> 3) ^ rowswz<D>(r)) << 3) + (m & 7));
+  }
+  uint4 u;
+  u.x = static_cast<uint16_t>(h[0][0]) | (static_cast<uint32_t>(static_cast<uint16_t>(h[0][1])) << 16);
+  u.y = static_cast<uint16_t>(h[0][2]) | (static_cast<uint32_t>(static_cast<uint16_t>(h[0][3])) << 16);
+  u.z = static_cast<uint16_t>(h[1][0]) | (static_cast<uint32_t>(static_cast<uint16_t>(h[1][1])) << 16);
+  u.w = static_cast<uint16_t>(h[1][2]) | (static_cast<uint32_t>(static_cast<uint16_t>(h[1][3])) << 16);
+  return as_bf16x8(u);
+}
+
 // Transposed tiles: D rows of 64 bf16, addressed in 8-byte slots of 4.
 __device__ __forceinline__ uint2 tslot(const u16* base, int r, int slot) {
   return *reinterpret_cast<const uint2*>(base + r * 64 + ((slot ^ swz8b(r)) << 2));
@@ -116,10 +148,7 @@ struct Tile64 {
 // that order so that both operands agree.  The source row of each lane applies
 // the swizzle and the permutation; rows at or beyond the operand's end read
 // as zeros (buffer range check).
-__device__ __forceinline__ int perm16(int r) {
-  const int p = r & 15;
-  return (r & ~15) | ((p >= 4 && p < 12) ? (p ^ 12) : p);
-}
+
 
 template <int D, int R, bool OUTER>
 struct TileDma {

@@ -93,15 +93,16 @@ __global__ __launch_bounds__(256, BKF == 32 ? 2 : 1) void attn_fwd_kernel(const 
     if (!any) continue;
     const bool full = kt0 + BKF - 1 <= qw0 && qw0 + 31 - kt0 < window && kt0 + BKF <= s;
 
+    // each chain's first product takes a literal zero accumulator
+    const f32x16 zero = {};
     f32x16 st[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) st[kb][e] = 0.0f;
+      st[kb] = zero;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const bf16x8 kh = row_frag<D>(k_lds, kb * 32 + l32, ks * 2 + g);
-        st[kb] = mfma32x32x16(kh, qf[ks], st[kb]);
+        st[kb] = mfma32x32x16(kh, qf[ks], ks == 0 ? zero : st[kb]);
         st[kb] = mfma32x32x16(row_frag<D>(kl_lds, kb * 32 + l32, ks * 2 + g), qf[ks], st[kb]);
         st[kb] = mfma32x32x16(kh, ql[ks], st[kb]);
       }

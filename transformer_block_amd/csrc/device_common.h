@@ -95,8 +95,12 @@ __device__ __forceinline__ int swz128(int r) { return (r ^ (r >> 3)) & 7; }
 // Swizzle for rows of 64 bf16 addressed in 8-byte slots (16 slots per row).
 __device__ __forceinline__ int swz8b(int r) { return (r ^ (r >> 4)) & 15; }
 
-// Swizzle for rows of 128 bf16 (256 bytes = 16 chunks of 16 bytes).
-__device__ __forceinline__ int swz256(int r) { return r & 15; }
+// Swizzle for rows of 128 bf16 (256 bytes = 16 chunks of 16 bytes): chunk c
+// of row r at slot c ^ swz256(r).  Conflict-free for 16-byte row reads (8 or
+// 16 consecutive rows at one chunk) and for the transposing 8-byte reads of
+// two adjacent chunks in 4 rows (every 16-lane group of ds_read_b64_tr_b16,
+// rows in perm16 order).
+__device__ __forceinline__ int swz256(int r) { return ((2 * (r & 7)) ^ ((r >> 3) & 1)) & 15; }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
