@@ -27,7 +27,12 @@ Prints one JSON line.  Besides the throughput it carries:
   optimizer:    one LAMB step (the notes' eq (7)) over every parameter tensor
                 of the workload, fp32 masters and moments, against the HBM
                 roofline (40 algorithmic bytes per parameter); --no-optimizer
-                skips it.  Neither leg is part of `value`.
+                skips it;
+  fp8:          the same layer with its four GEMM parts on FP8 operands (E4M3
+                forward, E5M2 gradients, current scaling: Megatron tuning
+                post, mixed-precision section), the weight cast included in
+                the step, model FLOPs as for `value`; --no-fp8 skips it.
+                None of these legs is part of `value`.
 
 roofline.traffic is the HBM bytes per launch of the dominant kernel as read
 by rocprofv3 counters (FETCH_SIZE, WRITE_SIZE), each scaled by what the same
@@ -52,6 +57,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 METRIC = "model TFLOP/s + MFU vs bf16 MFMA peak, PTB layer fwd+bwd, 1 MI355X"
 DEFAULT_WORKLOAD = "gpt175b_tp8_share_s2048"
 
@@ -281,6 +287,56 @@ def time_variant(w, warmup: int, steps: int, base_ms: float) -> dict:
             "model_flops_per_step": F, "stages_ms": stages}
 
 
+def time_fp8(w, inp, warmup: int, steps: int, base_ms: float) -> dict:
+    """The FP8-GEMM layer on the same inputs: mean ms per step (weight cast,
+    forward, backward) and per stage, HIP events on one stream."""
+    import torch
+
+    from transformer_block_amd import ptb as P
+    from transformer_block_amd.flops import workload_model_flops
+    from transformer_block_amd.runner import Fp8Layer
+
+    print("bench: timing the FP8 GEMM variant", file=sys.stderr, flush=True)
+    lyr = Fp8Layer(w, inp, "cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        lyr.step(stream)
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    fwd_ev = [ev.create(2 * P.PTB_FP8_FWD_STAGES) for _ in range(steps)]
+    bwd_ev = [ev.create(2 * P.PTB_FP8_BWD_STAGES) for _ in range(steps)]
+    cast_ev = [ev.create(2) for _ in range(steps)]
+    t0, t1 = ev.create(2)
+    ev.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    ev.hip.hipEventRecord(t0, stream.cuda_stream)
+    for k in range(steps):
+        ev.hip.hipEventRecord(cast_ev[k][0], stream.cuda_stream)
+        lyr.cast_weights(stream)
+        ev.hip.hipEventRecord(cast_ev[k][1], stream.cuda_stream)
+        lyr.forward(stream, fwd_ev[k])
+        lyr.backward(stream, bwd_ev[k])
+    ev.hip.hipEventRecord(t1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(t0, t1) / steps
+    stages = {"cast_weights": round(sum(ev.ms(c[0], c[1]) for c in cast_ev) / steps, 4)}
+    for names, evs in ((P.FP8_FWD_STAGE_NAMES, fwd_ev), (P.FP8_BWD_STAGE_NAMES, bwd_ev)):
+        for i, name in enumerate(names):
+            stages[name] = round(sum(ev.ms(evs[k][2 * i], evs[k][2 * i + 1])
+                                     for k in range(steps)) / steps, 4)
+    ev.close()
+    F = workload_model_flops(w)
+    tflops = F / (ms * 1e-3) / 1e12
+    gemm_ms = sum(v for k, v in stages.items() if k.startswith("gemm_"))
+    del lyr
+    return {"formats": "E4M3 fwd / E5M2 grad, per-operand current scaling",
+            "ms_per_step": round(ms, 4), "value": round(tflops, 2), "unit": "TFLOP/s",
+            "mfu_vs_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "frac_of_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4),
+            "speedup_vs_bf16": round(base_ms / ms, 4),
+            "gemm_ms": round(gemm_ms, 4), "stages_ms": stages}
+
+
 LAMB_BYTES_PER_PARAM = 40  # moments pass: g 2 + theta, m, v 12 read, m, v 8 written;
                            # update pass: theta, m, v 12 read, theta 4 + bf16 copy 2 written
 
@@ -343,6 +399,8 @@ def main() -> int:
                     help="skip timing the RMSNorm + SwiGLU variant")
     ap.add_argument("--no-optimizer", action="store_true",
                     help="skip timing the LAMB optimizer step")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip timing the FP8 GEMM variant")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -451,6 +509,8 @@ def main() -> int:
         out["optimizer"] = time_lamb(st, args.warmup, K)
     if not args.no_variant:
         out["variant"] = time_variant(w, args.warmup, K, ms_step)
+    if not args.no_fp8 and w.layers == 1:
+        out["fp8"] = time_fp8(w, inp, args.warmup, K, ms_step)
     if not args.no_cpu_baseline:
         print("bench: timing the fp64 oracle on host cores", file=sys.stderr, flush=True)
         cb = cpu_baseline(w, args.cpu_budget_s)

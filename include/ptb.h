@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define PTB_ABI_VERSION 4
+#define PTB_ABI_VERSION 5
 
 enum ptb_status {
   PTB_OK = 0,
@@ -349,6 +349,93 @@ int32_t ptb_lamb_workspace_bytes(const ptb_lamb_tensor* tensors, int32_t n, size
  * deterministic (fixed reduction order). */
 int32_t ptb_lamb_step(const ptb_lamb_hyper* hyper, const ptb_lamb_tensor* tensors, int32_t n,
                       float* norms, void* workspace, void* stream);
+
+/* ------------------------------------------------------------------------
+ * FP8 GEMM variant of the parallel block (Megatron-LM tuning post,
+ * mixed-precision section): the four GEMM parts, forward [QKV | FC1] and
+ * [O ; FC2] and their dgrad and wgrad products, run on 8-bit float operands
+ * with fp32 accumulation; LayerNorm, attention, GeLU, the residual sums and
+ * every stored tensor stay bf16/fp32.
+ *   formats   E4M3 (OCP; largest 448) for the forward operands and the
+ *             weights, E5M2 (largest 57344) for the gradient operands dy and
+ *             dZ = [dqkv | du]; the weight gradients take the saved
+ *             activations in E4M3;
+ *   scaling   current scaling, one scale per GEMM operand, a concatenated
+ *             operand ([W_qkv | W_fc1], [W_o ; W_fc2], [c | g], dZ) being one
+ *             tensor: s = FMAX / amax (fp32 division; s = 1 for an all-zero
+ *             tensor), code = round-to-nearest-even(clamp(x s, -FMAX, FMAX))
+ *             with x s one fp32 multiply, and the product's fp32 sums are
+ *             multiplied by (1/sA)(1/sB) before the epilogue.
+ * dims as for ptb_forward; norm LayerNorm or RMSNorm, mlp GeLU only
+ * (PTB_ERR_ARG for SwiGLU).  Any b, s, h, f allowed by ptb_validate_dims:
+ * the FP8 copies pad their contiguous dimension with zero codes to a
+ * multiple of 128.  Inputs, outputs, `saved` (same size and slots as for
+ * ptb_forward; A_LO is not written) and ownership are as for the bf16 calls;
+ * the calls are asynchronous on `stream` and return PTB_ERR_HIP if a launch
+ * fails.  stage_events: NULL, or 2 hipEvent_t per stage (start, end; NULL
+ * entries skipped) recorded around each stage as for ptb_forward_timed.
+ * ------------------------------------------------------------------------ */
+#define PTB_FP8_FWD_STAGES 6
+#define PTB_FP8_BWD_STAGES 10
+
+/* Bytes of the FP8 weight buffer (amax of W1 = [W_qkv | W_fc1] and
+ * W2 = [W_o ; W_fc2], then W1^T, W1, W2^T and W2 in E4M3) and of the FP8
+ * layer's workspace. */
+int32_t ptb_fp8_weights_bytes(const ptb_dims* dims, size_t* bytes);
+int32_t ptb_fp8_workspace_bytes(const ptb_dims* dims, size_t* bytes);
+
+/* Byte offsets of the parts of the FP8 weight buffer (`offsets` has room
+ * for PTB_FP8_WEIGHT_PARTS entries):
+ *   AMAX   fp32 [2]: amax of W1, amax of W2
+ *   W1T    E4M3 [N1][pad128(h)]   W1^T, N1 = 3 n d + f
+ *   W1     E4M3 [h][pad128(N1)]   W1
+ *   W2T    E4M3 [h][pad128(K2)]   W2^T, K2 = n d + f
+ *   W2     E4M3 [K2][pad128(h)]   W2
+ * pad128(v) rounds up to a multiple of 128; padding codes are zero. */
+enum ptb_fp8_weight_part {
+  PTB_FP8_AMAX = 0, PTB_FP8_W1T, PTB_FP8_W1, PTB_FP8_W2T, PTB_FP8_W2,
+  PTB_FP8_WEIGHT_PARTS
+};
+int32_t ptb_fp8_weights_layout(const ptb_dims* dims, size_t* offsets);
+
+/* The current-scaling cast on its own, for any bf16 matrix x [rows][cols]
+ * (device, row-major, cols a multiple of 8, rows * cols < 2^30):
+ * *amax = max |x| (device fp32), s = FMAX / *amax, and the codes of x s in
+ * `format` (PTB_FP8_E4M3 or PTB_FP8_E5M2) written row-wise to
+ * q [rows][pad64(cols)] and/or transposed to qt [cols][pad64(rows)]
+ * (either may be NULL; padding codes are zero).  The same kernels as the
+ * layer's casts.  Pointers 16-byte aligned. */
+enum ptb_fp8_format { PTB_FP8_E4M3 = 0, PTB_FP8_E5M2 = 1 };
+int32_t ptb_fp8_quantize(const void* x, int32_t rows, int32_t cols, int32_t format, float* amax,
+                         void* q, void* qt, void* stream);
+
+/* Casts the four bf16 weights (as for ptb_forward) into `fp8_weights`
+ * (device, caller-owned, ptb_fp8_weights_bytes), both orientations of each
+ * concatenated weight on one current scale.  Call it after every change of
+ * the weights (once per optimizer step); forward and backward read it. */
+int32_t ptb_fp8_cast_weights(const ptb_dims* dims, const void* w_qkv, const void* w_o,
+                             const void* w_fc1, const void* w_fc2, void* fp8_weights,
+                             void* stream);
+
+/* Forward: y [T, h] and `saved`.  Stages: 0 LayerNorm, 1 cast a, 2 [QKV | FC1]
+ * FP8 product + GeLU, 3 attention, 4 cast [c | g], 5 [O ; FC2] FP8 product +
+ * residual. */
+int32_t ptb_fp8_forward(const ptb_dims* dims, const void* x, const void* ln_gamma,
+                        const void* ln_beta, const void* fp8_weights, void* y, void* saved,
+                        void* workspace, void* stream, void* const* stage_events);
+
+/* Backward for upstream gradient dy [T, h] from the `saved` of the matching
+ * ptb_fp8_forward (same x, same fp8_weights); writes what ptb_backward
+ * writes.  It recomputes every amax it uses, so it does not depend on the
+ * forward's workspace contents.  Stages: 0 cast dy, 1 dgrad [O ; FC2] +
+ * GeLU', 2 attention backward, 3 cast [c | g]^T, 4 wgrad [O ; FC2], 5 cast dZ,
+ * 6 dgrad [QKV | FC1], 7 cast a^T, 8 wgrad [QKV | FC1], 9 LayerNorm backward
+ * (+ dy). */
+int32_t ptb_fp8_backward(const ptb_dims* dims, const void* dy, const void* x,
+                         const void* ln_gamma, const void* fp8_weights, const void* saved,
+                         void* dx, void* d_ln_gamma, void* d_ln_beta, void* dw_qkv, void* dw_o,
+                         void* dw_fc1, void* dw_fc2, void* workspace, void* stream,
+                         void* const* stage_events);
 
 #ifdef __cplusplus
 }  /* extern "C" */

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "ptb.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ptb_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ptb_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert P.ptb_abi_version() == 4
+    assert P.ptb_abi_version() == 5
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert P.ptb_status_string(code) and P.ptb_status_string(code) != "unknown status"
     assert P.ptb_status_string(12345) == "unknown status"
@@ -216,3 +216,62 @@ def test_swiglu_widens_the_fc1_stash_and_workspace(lib):
     assert P.ptb_serial_saved_bytes(good_dims(mlp=1)) >= P.ptb_serial_saved_bytes(good_dims()) + T * f * 2
     # RMSNorm changes no size
     assert P.ptb_saved_bytes(good_dims(norm=1)) == P.ptb_saved_bytes(good_dims())
+
+
+def test_fp8_weight_layout_and_sizes(lib):
+    """FP8 weight buffer: amax, then W1^T [N1, pad128(h)], W1 [h, pad128(N1)],
+    W2^T [h, pad128(K2)], W2 [K2, pad128(h)], 1 byte per element."""
+    d = good_dims()  # h 256, 4 x 64 heads, f 1024
+    h, hl, f = 256, 256, 1024
+    N1, K2 = 3 * hl + f, hl + f
+    pad = lambda v: (v + 127) // 128 * 128
+    lay = P.ptb_fp8_weights_layout(d)
+    sizes = dict(amax=8, w1t=N1 * pad(h), w1=h * pad(N1), w2t=h * pad(K2), w2=K2 * pad(h))
+    offs = [lay[k] for k in P.FP8_WEIGHT_PARTS]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    for a_, b_ in zip(P.FP8_WEIGHT_PARTS, P.FP8_WEIGHT_PARTS[1:]):
+        assert lay[b_] - lay[a_] >= sizes[a_]
+    assert P.ptb_fp8_weights_bytes(d) >= lay["w2"] + sizes["w2"]
+    # a ragged hidden size pads the contiguous dimension to 128
+    r = good_dims(hidden=192, heads=3, ffn=768)
+    lr = P.ptb_fp8_weights_layout(r)
+    assert lr["w1"] - lr["w1t"] >= (3 * 192 + 768) * 256
+    # the workspace holds the bf16 layer's plus the FP8 activation copies
+    T = 512
+    assert P.ptb_fp8_workspace_bytes(d) >= P.ptb_workspace_bytes(d) + T * (
+        pad(h) * 2 + pad(K2) + pad(N1)) + pad(T) * (2 * h + K2 + N1)
+
+
+def test_fp8_calls_reject_bad_arguments_before_any_hip_call(lib):
+    A = 0x10000
+    d = good_dims()
+    # SwiGLU has no FP8 variant
+    for fn in (P.ptb_fp8_weights_bytes, P.ptb_fp8_workspace_bytes):
+        with pytest.raises(P.PtbError) as ei:
+            fn(good_dims(mlp=1))
+        assert ei.value.status == P.PTB_ERR_ARG
+    assert P.ptb_fp8_forward(good_dims(mlp=1), *([A] * 7), stream=0,
+                             check=False) == P.PTB_ERR_ARG
+    assert P.ptb_fp8_forward(d, *([A] * 6), 0, stream=0, check=False) == P.PTB_ERR_NULL
+    args = [A] * 7
+    args[3] = A + 8
+    assert P.ptb_fp8_forward(d, *args, stream=0, check=False) == P.PTB_ERR_ALIGN
+    assert P.ptb_fp8_backward(d, *([A] * 12), 0, stream=0, check=False) == P.PTB_ERR_NULL
+    assert P.ptb_fp8_backward(good_dims(window=0), *([A] * 13), stream=0,
+                              check=False) == P.PTB_ERR_WINDOW
+    assert P.ptb_fp8_cast_weights(d, A, A, 0, A, A, stream=0, check=False) == P.PTB_ERR_NULL
+    # the stand-alone cast
+    assert P.ptb_fp8_quantize(A, 64, 64, "e4m3", A, 0, 0, stream=0,
+                              check=False) == P.PTB_ERR_NULL
+    assert P.ptb_fp8_quantize(A, 64, 60, "e4m3", A, A, 0, stream=0,
+                              check=False) == P.PTB_ERR_DIMS
+    assert P.ptb_fp8_quantize(A, 0, 64, "e5m2", A, A, 0, stream=0,
+                              check=False) == P.PTB_ERR_DIMS
+    assert P.ptb_fp8_quantize(A + 4, 64, 64, "e5m2", A, A, 0, stream=0,
+                              check=False) == P.PTB_ERR_ALIGN
+    assert load_fmt_error(lib) == P.PTB_ERR_ARG
+
+
+def load_fmt_error(lib):
+    """An unknown format code is rejected."""
+    return lib.ptb_fp8_quantize(0x10000, 64, 64, 7, 0x10000, 0x10000, None, None)

@@ -1,0 +1,170 @@
+"""Parity of the FP8 GEMM variant (ptb_fp8_* through the C ABI) with the fp64
+FP8 oracle (oracle/fp8_oracle.py) on the same seeded bf16 inputs.
+
+* The current-scaling cast (ptb_fp8_quantize, ptb_fp8_cast_weights) is
+  compared code by code: both sides decide each code in fp32 (x * s one fp32
+  multiply, s = FMAX / amax one fp32 division), so the codes must be
+  identical, padding included.
+* The layer is compared by relative Frobenius error per output tensor against
+  FP8_TOL.  Where the two sides feed a cast slightly different bf16 values (an
+  upstream difference of relative size delta, at most the bf16 path's bar
+  1e-2), a value near an FP8 rounding boundary lands on the neighbouring code:
+  with probability about delta / u per element, u the format's relative step
+  (2^-3 E4M3, 2^-2 E5M2), each time one whole step.  The RMS effect is about
+  sqrt(delta u) = sqrt(1e-2 * 2^-2) = 0.05, which is the bar.  The residual
+  paths dominate y and dx, so y - x and dx - dy are compared with the bf16
+  rounding floor of the output added, as for the bf16 layer."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import fp8_oracle as F8
+from transformer_block_amd import inputs as I
+from transformer_block_amd import ptb as P
+from transformer_block_amd.runner import Fp8Layer, bf16_to_numpy_f64
+
+from .helpers import log, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+FP8_TOL = math.sqrt(1e-2 * 2.0 ** -2)
+
+W = I.Workload
+
+
+def _np(t):
+    if t.dtype == torch.bfloat16:
+        return bf16_to_numpy_f64(t)
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def _probe_matrix(rows, cols, seed):
+    """bf16 values: every significand of the binades 2^-33 .. 2^1 (both signs),
+    the largest magnitude 3 exactly once, zeros, and N(0, 0.5) filler; shuffled."""
+    rng = np.random.default_rng(seed)
+    e = np.arange(-33, 2)
+    m = 1 + np.arange(128) / 128.0
+    grid = (m[None, :] * 2.0 ** e[:, None]).ravel()
+    grid = grid[grid < 3.0]
+    vals = np.concatenate([grid, -grid, [3.0, 0.0, 0.0]])
+    n = rows * cols
+    assert vals.size <= n
+    fill = rng.standard_normal(n - vals.size) * 0.5
+    allv = np.concatenate([vals, np.clip(fill, -2.9, 2.9)])
+    rng.shuffle(allv)
+    bits = I.f32_to_bf16_bits(allv.astype(np.float32)).reshape(rows, cols)
+    return bits, I.bf16_bits_to_f64(bits)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("rows,cols", [(130, 264), (64, 512)])
+def test_quantize_codes_match_the_oracle(fmt, rows, cols):
+    log(f"fp8 quantize {fmt} {rows}x{cols}")
+    bits, x = _probe_matrix(rows, cols, 900 + rows)
+    dev = torch.device("cuda")
+    xt = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    ldq, ldqt = (cols + 63) // 64 * 64, (rows + 63) // 64 * 64
+    q = torch.full((rows, ldq), 0x55, dtype=torch.uint8, device=dev)
+    qt = torch.full((cols, ldqt), 0x55, dtype=torch.uint8, device=dev)
+    amax = torch.full((4,), -1.0, dtype=torch.float32, device=dev)
+    P.ptb_fp8_quantize(xt, rows, cols, fmt, amax, q, qt)
+    torch.cuda.synchronize()
+    assert amax[0].item() == 3.0
+    s = F8.current_scale(x, fmt)
+    codes, _ = F8.quantize(x, s, fmt)
+    got = q.cpu().numpy()
+    np.testing.assert_array_equal(got[:, :cols], codes)
+    assert not got[:, cols:].any()
+    gott = qt.cpu().numpy()
+    np.testing.assert_array_equal(gott[:, :rows], codes.T)
+    assert not gott[:, rows:].any()
+
+
+def test_cast_weights_match_the_oracle():
+    w = W("f8w", 1, 128, 192, 3, 64, 768, 32, seed=901)
+    inp = I.make_inputs(w, random_ln=True)
+    dev = torch.device("cuda")
+    lay = inp["layers"][0]
+    t = {k: torch.from_numpy(lay[k].view(np.int16)).to(dev).view(torch.bfloat16)
+         for k in ("w_qkv", "w_o", "w_fc1", "w_fc2")}
+    dims = P.dims_of(w)
+    buf = torch.zeros(P.ptb_fp8_weights_bytes(dims), dtype=torch.uint8, device=dev)
+    P.ptb_fp8_cast_weights(dims, t["w_qkv"], t["w_o"], t["w_fc1"], t["w_fc2"], buf)
+    torch.cuda.synchronize()
+    off = P.ptb_fp8_weights_layout(dims)
+    host = buf.cpu().numpy()
+    f = I.bf16_bits_to_f64
+    w1 = np.concatenate([f(lay["w_qkv"]), f(lay["w_fc1"])], axis=1)
+    w2 = np.concatenate([f(lay["w_o"]), f(lay["w_fc2"])], axis=0)
+    amax = host[off["amax"]:off["amax"] + 8].view(np.float32)
+    assert amax[0] == np.abs(w1).max() and amax[1] == np.abs(w2).max()
+    pad = lambda v: (v + 127) // 128 * 128
+    for name, mat, tname in (("w1", w1, "w1t"), ("w2", w2, "w2t")):
+        codes, _ = F8.quantize(mat, F8.current_scale(mat, F8.E4M3), F8.E4M3)
+        R, C = mat.shape
+        rowwise = host[off[name]:off[name] + R * pad(C)].reshape(R, pad(C))
+        np.testing.assert_array_equal(rowwise[:, :C], codes)
+        assert not rowwise[:, C:].any()
+        trans = host[off[tname]:off[tname] + C * pad(R)].reshape(C, pad(R))
+        np.testing.assert_array_equal(trans[:, :R], codes.T)
+        assert not trans[:, R:].any()
+
+
+CASES = [
+    ("tiny_workload", I.WORKLOADS["tiny_h256_s256_w64"], True),
+    ("ragged_h192_s200_w37", W("f8r", 1, 200, 192, 3, 64, 768, 37, seed=910), True),
+    ("d128_b3_s97_w33", W("f8d", 3, 97, 256, 2, 128, 512, 33, seed=911), True),
+    ("rmsnorm", W("f8rms", 2, 160, 256, 2, 128, 256, 40, seed=912, norm="rmsnorm"), True),
+    ("single_token", W("f8s1", 1, 1, 128, 1, 128, 128, 1, seed=913), True),
+    ("h2048_s2048_w512", I.WORKLOADS["h2048_s2048_w512"], False),
+    ("gpt175b_tp8_share_s2048", I.WORKLOADS["gpt175b_tp8_share_s2048"], False),
+]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,w,random_ln", CASES, ids=[c[0] for c in CASES])
+def test_fp8_layer_parity(name, w, random_ln):
+    log(f"fp8 case {name}: {w}")
+    inp = I.make_inputs(w, random_ln=random_ln)
+    lyr = Fp8Layer(w, inp, "cuda")
+    lyr.step()
+    torch.cuda.synchronize()
+    log(f"[fp8 {name}] gpu step done; running the oracle")
+    f = I.bf16_bits_to_f64
+    x, dy = f(inp["x"]), f(inp["dy"])
+    p = {k: f(v) for k, v in inp["layers"][0].items()}
+    y, cache = F8.fp8_ptb_forward(x, p, w.batch, w.seq, w.heads, w.head_dim, w.window,
+                                  w.ln_eps, norm=w.norm)
+    log(f"[fp8 {name}] oracle forward done")
+    g = F8.fp8_ptb_backward(dy, cache, p, w.window)
+    errs = {}
+    for key, got, ref, res in (("y-x", _np(lyr.y), y, x), ("dx-dy", _np(lyr.dx), g["dx"], dy)):
+        branch = ref - res
+        floor = 2.0 ** -8 * np.linalg.norm(ref) / max(np.linalg.norm(branch), 1e-300)
+        errs[key] = rel_fro(got - res, branch) / (1.0 + floor / FP8_TOL)
+    for k in ("d_ln_gamma", "d_ln_beta", "dw_qkv", "dw_o", "dw_fc1", "dw_fc2"):
+        ref = g[k]
+        if w.norm == "rmsnorm" and k == "d_ln_beta":
+            assert not _np(lyr.grads[k]).any()
+            continue
+        errs[k] = rel_fro(_np(lyr.grads[k]), ref)
+    for k in ("a", "qkv", "u", "g", "c"):
+        errs[f"saved.{k}"] = rel_fro(_np(lyr.saved_tensor(k)), cache[k])
+    log(f"[fp8 {name}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not np.isfinite(v) or v > FP8_TOL}
+    assert not bad, f"parity failures (tol {FP8_TOL:.3f}): {bad}"
+
+
+def test_fp8_repeat_runs_are_bitwise_identical():
+    w = W("f8det", 2, 200, 256, 2, 128, 512, 80, seed=920)
+    lyr = Fp8Layer(w, I.make_inputs(w, random_ln=True), "cuda")
+    lyr.step()
+    torch.cuda.synchronize()
+    first = [lyr.y.clone(), lyr.dx.clone()] + [t.clone() for t in lyr.grads.values()]
+    lyr.step()
+    torch.cuda.synchronize()
+    again = [lyr.y, lyr.dx] + list(lyr.grads.values())
+    for a, b in zip(first, again):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))

@@ -45,6 +45,35 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ i32x8 cat8(uint4 lo, uint4 hi) {
+  return (i32x8){static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z),
+                 static_cast<int>(lo.w), static_cast<int>(hi.x), static_cast<int>(hi.y),
+                 static_cast<int>(hi.z), static_cast<int>(hi.w)};
+}
+
+// D = A(32x64) * B(64x32) + C with 8-bit float operands (FA, FB: 0 E4M3,
+// 1 E5M2), fp32 accumulate (v_mfma_f32_32x32x64_f8f6f4, no block scales).
+// Lane l supplies 32 bytes of row l%32 of A and of column l%32 of B, the same
+// k-values for both; D is laid out as in mfma32x32x16.
+template <int FA, int FB>
+__device__ __forceinline__ f32x16 mfma32x32x64_f8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
+}
+
+// Largest finite value of the 8-bit formats: E4M3 448, E5M2 57344.
+__device__ __forceinline__ constexpr float fp8_max(int fmt) { return fmt ? 57344.0f : 448.0f; }
+
+// Current scaling: s = FMAX / amax (1 for an all-zero tensor); the GEMM
+// undoes it with 1 / s.  One fp32 division each, the same on both sides.
+__device__ __forceinline__ float fp8_scale(float amax, float fmax) {
+  return amax > 0.0f ? fmax / amax : 1.0f;
+}
+__device__ __forceinline__ float inv_scale(float amax, float fmax) {
+  return 1.0f / fp8_scale(amax, fmax);
+}
+
 // erf(x) by the rational approximation of Abramowitz & Stegun, Handbook of
 // Mathematical Functions, formula 7.1.26 (|error| <= 1.5e-7 for all x):
 //   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),

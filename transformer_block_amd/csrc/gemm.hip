@@ -36,6 +36,17 @@
 // whole factor are cut into pieces of equal length first.  Workgroup ids are
 // remapped so that each XCD (each with its own L2) takes a contiguous run of
 // items in every round.
+//
+// FP8.  The same eight-wave kernel multiplies 8-bit operands (E4M3 or E5M2,
+// Megatron-LM tuning post, mixed-precision section) with
+// v_mfma_f32_32x32x64_f8f6f4.  Both operands are then k-contiguous and a
+// 128-byte LDS row holds 128 k-values instead of 64, so the DMA, the swizzle
+// and the fragment reads are the bf16 ones byte for byte; one FP8 MFMA takes
+// the 32 bytes that two consecutive bf16 k-steps would (A and B see the same
+// k order, so the sum is the product).  The epilogue first multiplies the
+// fp32 sums by the dequantization factor 1/(sA sB) of the operands' current
+// scales, sX = FMAX / amax(X), which it derives from the amax values the
+// cast kernels left in device memory.
 #include <algorithm>
 #include <type_traits>
 
@@ -142,8 +153,9 @@ struct StageLoader {
 // through its parity (k-contiguous) or not at all (outer-contiguous), so a
 // lane needs two offsets per segment and the rest of each load's address is
 // wave-uniform (soffset).
-template <int MAJ>
+template <int MAJ, int ESZ = 2>
 struct StageLoaderP {
+  static_assert(ESZ == 2 || (ESZ == 1 && MAJ == KMAJOR), "8-bit operands are k-contiguous");
   int vA[2], vB[2];  // per-lane byte offsets in segment A / B, [load parity]
   i32x4 dA, dB;      // buffer resources of segments A and B
   int ldA, ldB;      // leading dimensions (the k stride of outer-contiguous tiles)
@@ -173,8 +185,8 @@ struct StageLoaderP {
 #pragma unroll
       for (int par = 0; par < 2; ++par) {
         const int c = (lane & 7) ^ kswz(8 * par + lr);
-        vA[par] = (lr * ldA + c * 8) * 2;
-        vB[par] = (lr * ldB + c * 8) * 2;
+        vA[par] = ESZ == 2 ? (lr * ldA + c * 8) * 2 : lr * ldA + c * 16;
+        vB[par] = ESZ == 2 ? (lr * ldB + c * 8) * 2 : lr * ldB + c * 16;
       }
     } else {
       // load i covers k-rows 8 * i + lr of outer block `wave`
@@ -194,8 +206,8 @@ struct StageLoaderP {
     const int row = kseg ? rowB : rowA;
     const i32x4 d = kseg ? dB : dA;
     const int v0 = kseg ? vB[0] : vA[0], v1 = kseg ? vB[1] : vA[1];
-    int soff = (MAJ == KMAJOR) ? (row * ld + krel) * 2 : krel * ld * 2;
-    int step = 16 * ld;  // 8 rows (or 8 k-rows) further per load
+    int soff = (MAJ == KMAJOR) ? (row * ld + krel) * ESZ : krel * ld * 2;
+    int step = 8 * ld * ESZ;  // 8 rows (or 8 k-rows) further per load
     if (!valid) { soff = kOutOfRange; step = 0; }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -471,6 +483,8 @@ struct SkPlan {
   int full_slots;    // partial slots of whole-round items (0 when none is split)
   float* partials;   // kGemmPartialSlots slots of PARTIAL_FLOATS
   int* counters;     // arrival count per global tile: zero on entry, left zero
+  const float* amax_a;  // FP8: amax of the operands (device), else null
+  const float* amax_b;
 };
 
 struct Item {
@@ -530,8 +544,15 @@ __device__ __forceinline__ int part_slot(const SkPlan& pl, int i) {
   return i < pl.full_items ? i : pl.full_slots + (i - pl.full_items);
 }
 
-template <int AMAJ, int BMAJ, int MODE>
+// FMT 0: bf16 operands; FP8 operands otherwise, FMT - 1 = fa + 2 fb with
+// fa, fb the operands' formats (Fp8Format: 0 E4M3, 1 E5M2).
+template <int AMAJ, int BMAJ, int MODE, int FMT = 0>
 __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
+  constexpr bool F8 = FMT != 0;
+  constexpr int FA = F8 ? (FMT - 1) & 1 : 0, FB = F8 ? (FMT - 1) >> 1 : 0;
+  constexpr int ESZ = F8 ? 1 : 2;          // operand bytes per element
+  constexpr int KSTEP = BK * 2 / ESZ;      // k-values per stage tile (128-byte rows)
+  static_assert(!F8 || (AMAJ == KMAJOR && BMAJ == KMAJOR), "FP8 operands are k-contiguous");
   constexpr int RA = (AMAJ == KMAJOR) ? FM : 2 * FM;  // LDS read instructions per k-step
   constexpr int RB = (BMAJ == KMAJOR) ? FN : 2 * FN;
   // Two stages of 64 KB.  The epilogue's staging area (8 waves x 32 rows x
@@ -557,8 +578,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
     v = xcd * base + min(xcd, rem) + loc;
   }
   if (v >= pl.nitems) return;
-  StageLoaderP<AMAJ> la;
-  StageLoaderP<BMAJ> lb;
+  StageLoaderP<AMAJ, ESZ> la;
+  StageLoaderP<BMAJ, ESZ> lb;
   int item = v;
   Item s = decode_item(pl, item);
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_address(ring));
@@ -574,7 +595,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
   auto issue_to = [&](const Item& sg, int slot, int j) {
     if (!loader) return;
     const bool valid = j < sg.len;
-    const int k0 = (sg.kb + (valid ? j : 0)) * BK;
+    const int k0 = (sg.kb + (valid ? j : 0)) * KSTEP;
     const uint32_t lds = ring_lds + slot * (STAGE * 2);
     la.issue(lds, wave, k0, valid);
     lb.issue(lds + TILE * BK * 2, wave, k0, valid);
@@ -597,6 +618,39 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(fa[slot][i], fb[slot][j], acc[i][j]);
+  };
+  // FP8: the 32 bytes of bf16 k-steps 2 half and 2 half + 1 (64 k-values)
+  i32x8 ga[2][FM], gb[2][FN];
+  auto rd8 = [&](const u16* st, int half, int slot) {
+    const int k0 = koff[2 * half], k1 = koff[2 * half + 1];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const u16* t = st + (wm * WM + i * 32) * BK;
+      ga[slot][i] = cat8(*reinterpret_cast<const uint4*>(t + k0),
+                         *reinterpret_cast<const uint4*>(t + k1));
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const u16* t = st + TILE * BK + (wn * WN + j * 32) * BK;
+      gb[slot][j] = cat8(*reinterpret_cast<const uint4*>(t + k0),
+                         *reinterpret_cast<const uint4*>(t + k1));
+    }
+  };
+  auto mma8 = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = mfma32x32x64_f8<FA, FB>(ga[slot][i], gb[slot][j], acc[i][j]);
+  };
+  auto pin8 = [&]() {
+    constexpr int R = 2 * (FM + FN);
+#pragma unroll
+    for (int i = 0; i < FM * FN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, R - FM * FN, 0);
   };
   // LDS reads of the next k-step spread between this k-step's MFMAs
   auto pin = [&]() {
@@ -633,6 +687,22 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    if constexpr (F8) {
+      // the same pipeline with two FP8 MFMA steps of 64 k per stage tile
+      rd8(ring, 0, 0);
+      for (int j = 0; j < len; ++j) {
+        u16* cur = ring + (j & 1) * STAGE;
+        rd8(cur, 1, 1);
+        mma8(0);
+        pin8();
+        wait_vm_lds<0>();
+        __syncthreads();
+        issue_to(s, j & 1, j + 2);
+        rd8(ring + ((j + 1) & 1) * STAGE, 0, 0);  // unused after the last step
+        mma8(1);
+        pin8();
+      }
+    } else {
     rd(ring, 0, 0);
     for (int j = 0; j < len; ++j) {
       u16* cur = ring + (j & 1) * STAGE;
@@ -651,6 +721,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
       rd(ring + ((j + 1) & 1) * STAGE, 0, 0);  // unused after the last step
       mma(1);
       pin();
+    }
     }
 
     // ---- the next item's first stage tile goes out before this one's
@@ -687,6 +758,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
       bool summed = false;  // phase 1 on a sum of partials
       const int my_slot = part_slot(pl, item);
       float held[MODE == EPI_QKV_SWIGLU ? 16 : 1];
+      float dq = 1.0f;  // FP8: 1 / (sA sB)
+      if constexpr (F8) dq = inv_scale(*pl.amax_a, fp8_max(FA)) * inv_scale(*pl.amax_b, fp8_max(FB));
       for (;;) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -723,6 +796,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
                   }
                   first = false;
                 });
+              }
+              if constexpr (F8) {
+#pragma unroll
+                for (int t = 0; t < 16; ++t) vals[t] *= dq;
               }
               const int r0 = s.m0 + wm * WM + i * 32, cb = s.n0 + wn * WN + j * 32;
               const int region = __builtin_amdgcn_readfirstlane(epi_region<MODE>(e, r0, cb));
@@ -1073,6 +1150,13 @@ bool operand_ok(const Operand& op) {
          op.ld1 > 0 && op.split >= 0 && (op.split % 64 == 0 || op.split >= (1 << 30));
 }
 
+template <int MODE, int FMT>
+hipError_t launch_plan_fp8(const SkPlan& pl, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_sk_kernel<KMAJOR, KMAJOR, MODE, FMT>), dim3(grid), dim3(64 * WAVES), 0,
+                     s, pl);
+  return hipGetLastError();
+}
+
 template <int AMAJ, int BMAJ, int MODE>
 hipError_t launch_plan(const SkPlan& pl, int grid, hipStream_t s) {
   if constexpr (AMAJ == KMAJOR && BMAJ == KMAJOR)
@@ -1084,22 +1168,24 @@ hipError_t launch_plan(const SkPlan& pl, int grid, hipStream_t s) {
 
 // Cut the work of one launch into items (see SkPlan).  `tail_split` > 0
 // forces the k-pieces of the last round's base items (tests and tuning);
-// 0 picks enough pieces to fill the CUs, at least 16 k-steps each.
+// 0 picks enough pieces to fill the CUs, at least 16 k-steps each.  kstep:
+// k-values per stage tile (64 bf16, 128 FP8).
 hipError_t build_plan(const GemmProblem* probs, int nprob, Major a_major, Major b_major,
-                      const GemmScratch& ws, int tail_split, SkPlan* out, int* grid_out) {
+                      const GemmScratch& ws, int tail_split, SkPlan* out, int* grid_out,
+                      int kstep = BK) {
   if (nprob < 1 || nprob > 2) return hipErrorInvalidValue;
   SkPlan pl;
   for (int i = 0; i < 2; ++i) {
     const GemmProblem& p = probs[i < nprob ? i : 0];
     // the epilogue writes 16 consecutive columns at a time
     if (p.M <= 0 || p.N <= 0 || p.K <= 0 || p.N % 16 != 0) return hipErrorInvalidValue;
-    // k-contiguous operands are read in whole 64-wide k-steps
-    if ((a_major == KMAJOR || b_major == KMAJOR) && p.K % BK != 0) return hipErrorInvalidValue;
+    // k-contiguous operands are read in whole k-steps
+    if ((a_major == KMAJOR || b_major == KMAJOR) && p.K % kstep != 0) return hipErrorInvalidValue;
     if (!operand_ok(p.A) || !operand_ok(p.B)) return hipErrorInvalidValue;
     pl.p[i] = p;
     pl.tiles_m[i] = (p.M + TILE - 1) / TILE;
     pl.tiles_n[i] = (p.N + TILE - 1) / TILE;
-    pl.iters[i] = (p.K + BK - 1) / BK;
+    pl.iters[i] = (p.K + kstep - 1) / kstep;
   }
   const long t0 = static_cast<long>(pl.tiles_m[0]) * pl.tiles_n[0];
   const long t1 = nprob > 1 ? static_cast<long>(pl.tiles_m[1]) * pl.tiles_n[1] : 0;
@@ -1108,6 +1194,7 @@ hipError_t build_plan(const GemmProblem* probs, int nprob, Major a_major, Major 
   pl.tiles[1] = static_cast<int>(t1);
   pl.partials = ws.partials;
   pl.counters = ws.counters;
+  pl.amax_a = pl.amax_b = nullptr;
 
   int G = device_cus();
   if (G <= 0) return hipErrorInvalidDevice;
@@ -1186,6 +1273,29 @@ hipError_t launch_gemm_group(const GemmProblem* probs, int nprob, Major a_major,
   }
   // the combinations the layer uses; anything else is a library bug
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_fp8(const GemmProblem& prob, Fp8Format fa, const float* amax_a,
+                           Fp8Format fb, const float* amax_b, EpiMode mode,
+                           const GemmScratch& ws, hipStream_t s) {
+  // 16-byte rows of 8-bit elements; both scales present
+  if (prob.A.ld0 % 16 != 0 || prob.A.ld1 % 16 != 0 || prob.B.ld0 % 16 != 0 ||
+      prob.B.ld1 % 16 != 0 || amax_a == nullptr || amax_b == nullptr)
+    return hipErrorInvalidValue;
+  SkPlan pl;
+  int grid = 0;
+  const hipError_t e = build_plan(&prob, 1, KMAJOR, KMAJOR, ws, 0, &pl, &grid, 2 * BK);
+  if (e != hipSuccess) return e;
+  pl.amax_a = amax_a;
+  pl.amax_b = amax_b;
+  const int fmt = 1 + fa + 2 * fb;
+  if (fmt == 1 && mode == EPI_QKV_GELU) return launch_plan_fp8<EPI_QKV_GELU, 1>(pl, grid, s);
+  if (fmt == 1 && mode == EPI_RESIDUAL) return launch_plan_fp8<EPI_RESIDUAL, 1>(pl, grid, s);
+  if (fmt == 2 && mode == EPI_DGELU) return launch_plan_fp8<EPI_DGELU, 2>(pl, grid, s);
+  if (fmt == 2 && mode == EPI_STORE2_COLS) return launch_plan_fp8<EPI_STORE2_COLS, 2>(pl, grid, s);
+  if (fmt == 3 && mode == EPI_STORE2_ROWS) return launch_plan_fp8<EPI_STORE2_ROWS, 3>(pl, grid, s);
+  if (fmt == 3 && mode == EPI_STORE2_COLS) return launch_plan_fp8<EPI_STORE2_COLS, 3>(pl, grid, s);
+  return hipErrorInvalidValue;  // a combination the FP8 layer does not use
 }
 
 hipError_t launch_gemm(int M, int N, int K, const Operand& A, Major a_major,

@@ -77,6 +77,10 @@ struct GemmProblem {
   Epilogue epi;
 };
 
+// The two 8-bit float formats (Megatron-LM tuning post, mixed precision):
+// E4M3 (largest 448) and E5M2 (largest 57344), OCP encodings.
+enum Fp8Format { FP8_E4M3 = 0, FP8_E5M2 = 1 };
+
 // Scratch of the GEMM launches: fp32 partial sums of 256 x 256 tiles that
 // are split along k (kGemmPartialSlots of them at most) and one arrival
 // counter per output tile.  The counters must be zero before a launch; every
@@ -109,6 +113,39 @@ hipError_t launch_gemm(int M, int N, int K, const Operand& A, Major a_major,
 hipError_t launch_gemm_group(const GemmProblem* probs, int nprob, Major a_major,
                              Major b_major, EpiMode mode, const GemmScratch& scratch,
                              hipStream_t stream);
+
+// FP8 product: both operands k-contiguous 8-bit matrices (element (r, k) at
+// byte r*ld + k, ld a multiple of 16), K a multiple of 128, fa / fb their
+// formats and amax_a / amax_b their amax (device memory, written by
+// launch_amax): the epilogue sees C / (sA sB) with sX = FMAX_X / amax_X.  The modes the FP8 layer uses: EPI_QKV_GELU and EPI_RESIDUAL
+// (E4M3 x E4M3), EPI_DGELU and EPI_STORE2_COLS (E5M2 x E4M3),
+// EPI_STORE2_ROWS and EPI_STORE2_COLS (E4M3 x E5M2).
+hipError_t launch_gemm_fp8(const GemmProblem& prob, Fp8Format fa, const float* amax_a,
+                           Fp8Format fb, const float* amax_b, EpiMode mode,
+                           const GemmScratch& scratch, hipStream_t stream);
+
+// A logical bf16 matrix X [R, C] made of up to two row-major segments:
+// columns [0, split) from p0 (ld0) and [split, C) from p1 (ld1) when
+// split_on_rows = 0, rows likewise when it is 1 (split >= C or R: one
+// segment).  Leading dimensions and split are multiples of 8.
+struct CastSrc {
+  const u16* p0;
+  const u16* p1;
+  int ld0, ld1;
+  int split, split_on_rows;
+  int R, C;
+};
+
+// *amax = max(*amax, max |X|) (as float bits; *amax starts at 0).
+hipError_t launch_amax(const CastSrc& x, float* amax, hipStream_t stream);
+
+// FP8 copies of X on its current scale s = FMAX / *amax: rows[r*ldr + c]
+// (ldr >= C) and/or cols[c*ldc + r] (the transpose, ldc >= R), each code
+// round-to-nearest-even of clamp(x * s) with x * s in fp32; padding columns
+// (c in [C, ldr) of rows, r in [R, ldc) of cols) are written as zero.
+// ldr and ldc are multiples of 64; either output may be null.
+hipError_t launch_cast_fp8(const CastSrc& x, Fp8Format fmt, const float* amax, uint8_t* rows,
+                           int ldr, uint8_t* cols, int ldc, hipStream_t stream);
 
 // LayerNorm forward over rows of x [T, h]: a = bf16(LN(x)) and its rounding
 // residual a_lo = bf16(LN(x) - a) (skipped when a_lo is null), mu, rstd (fp32).

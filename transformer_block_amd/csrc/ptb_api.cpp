@@ -200,6 +200,84 @@ SerialWorkLayout serial_work_layout(const Shape& s) {
   return W;
 }
 
+// ---- FP8 variant.  Every FP8 product reads two k-contiguous operands whose
+// k extent is padded with zero codes to a multiple of 128 (one stage tile).
+size_t pad128(size_t v) { return (v + 127) & ~static_cast<size_t>(127); }
+
+// The FP8 weight buffer: amax of W1 = [W_qkv | W_fc1] and W2 = [W_o ; W_fc2],
+// then both orientations of each in E4M3.
+struct Fp8WeightLayout {
+  size_t amax, w1t, w1r, w2t, w2r, total;
+};
+Fp8WeightLayout fp8_weight_layout(const Shape& s) {
+  Fp8WeightLayout L;
+  size_t o = 0;
+  L.amax = o; o = align_up(o + 2 * sizeof(float));
+  L.w1t = o; o = align_up(o + s.N1 * pad128(s.h));   // W1^T [N1, h]   (forward)
+  L.w1r = o; o = align_up(o + s.h * pad128(s.N1));   // W1   [h, N1]   (dgrad)
+  L.w2t = o; o = align_up(o + s.h * pad128(s.K2));   // W2^T [h, K2]   (forward)
+  L.w2r = o; o = align_up(o + s.K2 * pad128(s.h));   // W2   [K2, h]   (dgrad)
+  L.total = o;
+  return L;
+}
+
+// The FP8 workspace: the bf16 layer's workspace, then the amax of the
+// activation operands and their FP8 copies.
+enum Fp8Amax { AMAX_A = 0, AMAX_CG, AMAX_DY, AMAX_DZ, AMAX_A_BWD, AMAX_CG_BWD, AMAX_COUNT };
+struct Fp8WorkLayout {
+  WorkLayout base;
+  size_t amax, a8, cg8, dy8, dy8t, cg8t, dz8, dz8t, a8t, total;
+};
+Fp8WorkLayout fp8_work_layout(const Shape& s) {
+  Fp8WorkLayout W;
+  W.base = work_layout(s);
+  size_t o = W.base.total;
+  const size_t Tp = pad128(s.T);
+  W.amax = o; o = align_up(o + AMAX_COUNT * sizeof(float));
+  W.a8 = o; o = align_up(o + s.T * pad128(s.h));     // a       [T, h]
+  W.cg8 = o; o = align_up(o + s.T * pad128(s.K2));   // [c | g] [T, K2]
+  W.dy8 = o; o = align_up(o + s.T * pad128(s.h));    // dy      [T, h]
+  W.dy8t = o; o = align_up(o + s.h * Tp);            // dy^T    [h, T]
+  W.cg8t = o; o = align_up(o + s.K2 * Tp);           // [c | g]^T
+  W.dz8 = o; o = align_up(o + s.T * pad128(s.N1));   // dZ      [T, N1]
+  W.dz8t = o; o = align_up(o + s.N1 * Tp);           // dZ^T
+  W.a8t = o; o = align_up(o + s.h * Tp);             // a^T
+  W.total = o;
+  return W;
+}
+
+// The variant covers LayerNorm or RMSNorm with the GeLU MLP.
+int32_t check_fp8_dims(const ptb_dims* dims, Shape* s) {
+  const int32_t st = check_dims(dims, s);
+  if (st != PTB_OK) return st;
+  if (s->swiglu) return PTB_ERR_ARG;
+  // FP8 operands are addressed with 32-bit byte offsets as well
+  if (pad128(s->T) * s->N1 >= (1UL << 31) || pad128(s->N1) * s->h >= (1UL << 31))
+    return PTB_ERR_DIMS;
+  return PTB_OK;
+}
+
+constexpr int kOneSegment = 1 << 30;
+
+ptb::CastSrc cast_one(const void* p, long ld, long R, long C) {
+  const u16* q = static_cast<const u16*>(p);
+  return ptb::CastSrc{q, q, static_cast<int>(ld), static_cast<int>(ld), kOneSegment, 0,
+                      static_cast<int>(R), static_cast<int>(C)};
+}
+ptb::CastSrc cast_two(const void* p0, long ld0, const void* p1, long ld1, long split,
+                      int on_rows, long R, long C) {
+  return ptb::CastSrc{static_cast<const u16*>(p0), static_cast<const u16*>(p1),
+                      static_cast<int>(ld0), static_cast<int>(ld1), static_cast<int>(split),
+                      on_rows, static_cast<int>(R), static_cast<int>(C)};
+}
+
+// An FP8 operand [rows, ld] (bytes, k-contiguous).
+ptb::Operand one8(const uint8_t* p, long ld, long rows) {
+  const u16* q = reinterpret_cast<const u16*>(p);
+  const uint32_t bytes = static_cast<uint32_t>(ld * rows);
+  return ptb::Operand{q, q, static_cast<int>(ld), static_cast<int>(ld), INT_MAX, 0, bytes, bytes};
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int32_t check_ptrs(std::initializer_list<const void*> ps) {
@@ -232,6 +310,15 @@ ptb::Operand two(const u16* p0, long ld0, long rows0, const u16* p1, long ld1, l
 // (a column block of a wider matrix).
 uint32_t view_bytes(long ld, long rows, long width) {
   return static_cast<uint32_t>(((rows - 1) * ld + width) * 2);
+}
+
+// amax of x into *amax (zero on entry), then its FP8 copies.
+hipError_t cast_fp8(const ptb::CastSrc& x, ptb::Fp8Format fmt, float* amax, uint8_t* rows,
+                    size_t ldr, uint8_t* cols, size_t ldc, hipStream_t strm) {
+  const hipError_t e = ptb::launch_amax(x, amax, strm);
+  if (e != hipSuccess) return e;
+  return ptb::launch_cast_fp8(x, fmt, amax, rows, static_cast<int>(ldr), cols,
+                              static_cast<int>(ldc), strm);
 }
 
 #define PTB_HIP(expr)                              \
@@ -797,6 +884,272 @@ int32_t ptb_lamb_step(const ptb_lamb_hyper* hyper, const ptb_lamb_tensor* tensor
   const ptb::LambHyper hp{h.lr, h.beta1, h.beta2, h.eps, h.step};
   PTB_HIP(ptb::launch_lamb(ts, n, hp, static_cast<double*>(workspace), norms,
                            reinterpret_cast<hipStream_t>(stream)));
+  return PTB_OK;
+}
+
+// ---- FP8 GEMM variant
+
+int32_t ptb_fp8_weights_bytes(const ptb_dims* dims, size_t* bytes) {
+  Shape s;
+  const int32_t st = check_fp8_dims(dims, &s);
+  if (st != PTB_OK) return st;
+  if (bytes == nullptr) return PTB_ERR_NULL;
+  *bytes = fp8_weight_layout(s).total;
+  return PTB_OK;
+}
+
+int32_t ptb_fp8_workspace_bytes(const ptb_dims* dims, size_t* bytes) {
+  Shape s;
+  const int32_t st = check_fp8_dims(dims, &s);
+  if (st != PTB_OK) return st;
+  if (bytes == nullptr) return PTB_ERR_NULL;
+  *bytes = fp8_work_layout(s).total;
+  return PTB_OK;
+}
+
+int32_t ptb_fp8_weights_layout(const ptb_dims* dims, size_t* offsets) {
+  Shape s;
+  const int32_t st = check_fp8_dims(dims, &s);
+  if (st != PTB_OK) return st;
+  if (offsets == nullptr) return PTB_ERR_NULL;
+  const Fp8WeightLayout L = fp8_weight_layout(s);
+  offsets[PTB_FP8_AMAX] = L.amax;
+  offsets[PTB_FP8_W1T] = L.w1t;
+  offsets[PTB_FP8_W1] = L.w1r;
+  offsets[PTB_FP8_W2T] = L.w2t;
+  offsets[PTB_FP8_W2] = L.w2r;
+  return PTB_OK;
+}
+
+int32_t ptb_fp8_quantize(const void* x, int32_t rows, int32_t cols, int32_t format, float* amax,
+                         void* q, void* qt, void* stream) {
+  if (x == nullptr || amax == nullptr || (q == nullptr && qt == nullptr)) return PTB_ERR_NULL;
+  if ((format != PTB_FP8_E4M3 && format != PTB_FP8_E5M2)) return PTB_ERR_ARG;
+  if (rows < 1 || cols < 8 || cols % 8 != 0 || static_cast<long>(rows) * cols >= (1L << 30))
+    return PTB_ERR_DIMS;
+  if (!aligned16(x) || !aligned16(amax) || (q != nullptr && !aligned16(q)) ||
+      (qt != nullptr && !aligned16(qt)))
+    return PTB_ERR_ALIGN;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  const size_t ldq = (static_cast<size_t>(cols) + 63) & ~static_cast<size_t>(63);
+  const size_t ldqt = (static_cast<size_t>(rows) + 63) & ~static_cast<size_t>(63);
+  PTB_HIP(ptb::launch_zero_i32(reinterpret_cast<int*>(amax), 1, strm));
+  PTB_HIP(cast_fp8(cast_one(x, cols, rows, cols),
+                   format == PTB_FP8_E4M3 ? ptb::FP8_E4M3 : ptb::FP8_E5M2, amax,
+                   static_cast<uint8_t*>(q), ldq, static_cast<uint8_t*>(qt), ldqt, strm));
+  return PTB_OK;
+}
+
+int32_t ptb_fp8_cast_weights(const ptb_dims* dims, const void* w_qkv, const void* w_o,
+                             const void* w_fc1, const void* w_fc2, void* fp8_weights,
+                             void* stream) {
+  Shape s;
+  int32_t st = check_fp8_dims(dims, &s);
+  if (st != PTB_OK) return st;
+  st = check_ptrs({w_qkv, w_o, w_fc1, w_fc2, fp8_weights});
+  if (st != PTB_OK) return st;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  const Fp8WeightLayout L = fp8_weight_layout(s);
+  float* amax = at<float>(fp8_weights, L.amax);
+  PTB_HIP(ptb::launch_zero_i32(reinterpret_cast<int*>(amax), 2, strm));
+  // W1 = [W_qkv | W_fc1] [h, N1]: row-wise for the dgrad, transposed for the forward
+  PTB_HIP(cast_fp8(cast_two(w_qkv, 3 * s.hl, w_fc1, s.f, 3 * s.hl, 0, s.h, s.N1), ptb::FP8_E4M3,
+                   amax, at<uint8_t>(fp8_weights, L.w1r), pad128(s.N1),
+                   at<uint8_t>(fp8_weights, L.w1t), pad128(s.h), strm));
+  // W2 = [W_o ; W_fc2] [K2, h]
+  PTB_HIP(cast_fp8(cast_two(w_o, s.h, w_fc2, s.h, s.hl, 1, s.K2, s.h), ptb::FP8_E4M3, amax + 1,
+                   at<uint8_t>(fp8_weights, L.w2r), pad128(s.h),
+                   at<uint8_t>(fp8_weights, L.w2t), pad128(s.K2), strm));
+  return PTB_OK;
+}
+
+int32_t ptb_fp8_forward(const ptb_dims* dims, const void* x, const void* ln_gamma,
+                        const void* ln_beta, const void* fp8_weights, void* y, void* saved,
+                        void* workspace, void* stream, void* const* ev) {
+  Shape s;
+  int32_t st = check_fp8_dims(dims, &s);
+  if (st != PTB_OK) return st;
+  st = check_ptrs({x, ln_gamma, ln_beta, fp8_weights, y, saved, workspace});
+  if (st != PTB_OK) return st;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  const SavedLayout L = saved_layout(s);
+  const Fp8WorkLayout W = fp8_work_layout(s);
+  const Fp8WeightLayout WL = fp8_weight_layout(s);
+  const ptb::GemmScratch gs{at<float>(workspace, W.base.gemm_partials),
+                            at<int>(workspace, W.base.counters), W.base.max_tiles};
+  u16* a = at<u16>(saved, L.off[PTB_SAVED_A]);
+  float* mu = at<float>(saved, L.off[PTB_SAVED_MU]);
+  float* rstd = at<float>(saved, L.off[PTB_SAVED_RSTD]);
+  u16* qkv = at<u16>(saved, L.off[PTB_SAVED_QKV]);
+  u16* u = at<u16>(saved, L.off[PTB_SAVED_U]);
+  u16* g = at<u16>(saved, L.off[PTB_SAVED_G]);
+  u16* c = at<u16>(saved, L.off[PTB_SAVED_C]);
+  float* lse = at<float>(saved, L.off[PTB_SAVED_LSE]);
+  u16* qk_lo = at<u16>(saved, L.off[PTB_SAVED_QK_LO]);
+  float* amax = at<float>(workspace, W.amax);
+  const float* wamax = at<float>(fp8_weights, WL.amax);
+  uint8_t* a8 = at<uint8_t>(workspace, W.a8);
+  uint8_t* cg8 = at<uint8_t>(workspace, W.cg8);
+  const size_t hp = pad128(s.h), K2p = pad128(s.K2);
+
+  PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
+  PTB_HIP(ptb::launch_zero_i32(reinterpret_cast<int*>(amax), AMAX_COUNT, strm));
+  PTB_STAGE(0, ptb::launch_layernorm_fwd(static_cast<const u16*>(x),
+                                    static_cast<const u16*>(ln_gamma),
+                                    static_cast<const u16*>(ln_beta), a, nullptr, mu, rstd,
+                                    static_cast<int>(s.T), static_cast<int>(s.h), dims->ln_eps,
+                                    strm, s.rms));
+  PTB_STAGE(1, cast_fp8(cast_one(a, s.h, s.T, s.h), ptb::FP8_E4M3, amax + AMAX_A, a8, hp,
+                        nullptr, 0, strm));
+  {  // [qkv | u] = a W1 in one FP8 product; q, k stored as value + residual, g = GeLU(u)
+    ptb::GemmProblem pr;
+    pr.M = static_cast<int>(s.T); pr.N = static_cast<int>(s.N1); pr.K = static_cast<int>(hp);
+    pr.A = one8(a8, hp, s.T);
+    pr.B = one8(at<uint8_t>(fp8_weights, WL.w1t), hp, s.N1);
+    pr.epi = ptb::Epilogue{};
+    pr.epi.o0 = qkv; pr.epi.ld0 = static_cast<int>(3 * s.hl);
+    pr.epi.o1 = u; pr.epi.o2 = g; pr.epi.ld1 = static_cast<int>(s.f);
+    pr.epi.ld2 = static_cast<int>(s.f);
+    pr.epi.o3 = qk_lo; pr.epi.ld3 = static_cast<int>(2 * s.hl);
+    pr.epi.lo_cols = static_cast<int>(2 * s.hl);
+    pr.epi.split = static_cast<int>(3 * s.hl);
+    PTB_STAGE(2, ptb::launch_gemm_fp8(pr, ptb::FP8_E4M3, amax + AMAX_A, ptb::FP8_E4M3,
+                                      wamax, ptb::EPI_QKV_GELU, gs, strm));
+  }
+  const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
+                            gs.max_tiles, ptb::device_compute_units()};
+  PTB_STAGE(3, ptb::launch_attention_fwd(qkv, qk_lo, c, lse, static_cast<int>(s.b),
+                                    static_cast<int>(s.s), static_cast<int>(s.n),
+                                    static_cast<int>(s.d), static_cast<int>(s.w), as, strm));
+  PTB_STAGE(4, cast_fp8(cast_two(c, s.hl, g, s.f, s.hl, 0, s.T, s.K2), ptb::FP8_E4M3,
+                        amax + AMAX_CG, cg8, K2p, nullptr, 0, strm));
+  {  // y = x + [c | g] W2
+    ptb::GemmProblem pr;
+    pr.M = static_cast<int>(s.T); pr.N = static_cast<int>(s.h); pr.K = static_cast<int>(K2p);
+    pr.A = one8(cg8, K2p, s.T);
+    pr.B = one8(at<uint8_t>(fp8_weights, WL.w2t), K2p, s.h);
+    pr.epi = ptb::Epilogue{};
+    pr.epi.o0 = static_cast<u16*>(y); pr.epi.i0 = static_cast<const u16*>(x);
+    pr.epi.ld0 = static_cast<int>(s.h);
+    PTB_STAGE(5, ptb::launch_gemm_fp8(pr, ptb::FP8_E4M3, amax + AMAX_CG, ptb::FP8_E4M3,
+                                      wamax + 1, ptb::EPI_RESIDUAL, gs, strm));
+  }
+  return PTB_OK;
+}
+
+int32_t ptb_fp8_backward(const ptb_dims* dims, const void* dy, const void* x,
+                         const void* ln_gamma, const void* fp8_weights, const void* saved,
+                         void* dx, void* d_ln_gamma, void* d_ln_beta, void* dw_qkv, void* dw_o,
+                         void* dw_fc1, void* dw_fc2, void* workspace, void* stream,
+                         void* const* ev) {
+  Shape s;
+  int32_t st = check_fp8_dims(dims, &s);
+  if (st != PTB_OK) return st;
+  st = check_ptrs({dy, x, ln_gamma, fp8_weights, saved, dx, d_ln_gamma, d_ln_beta, dw_qkv, dw_o,
+                   dw_fc1, dw_fc2, workspace});
+  if (st != PTB_OK) return st;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  const SavedLayout L = saved_layout(s);
+  const Fp8WorkLayout W = fp8_work_layout(s);
+  const Fp8WeightLayout WL = fp8_weight_layout(s);
+  const u16* a = at<u16>(saved, L.off[PTB_SAVED_A]);
+  const float* mu = at<float>(saved, L.off[PTB_SAVED_MU]);
+  const float* rstd = at<float>(saved, L.off[PTB_SAVED_RSTD]);
+  const u16* qkv = at<u16>(saved, L.off[PTB_SAVED_QKV]);
+  const u16* u = at<u16>(saved, L.off[PTB_SAVED_U]);
+  const u16* g = at<u16>(saved, L.off[PTB_SAVED_G]);
+  const u16* c = at<u16>(saved, L.off[PTB_SAVED_C]);
+  const float* lse = at<float>(saved, L.off[PTB_SAVED_LSE]);
+  const u16* qk_lo = at<u16>(saved, L.off[PTB_SAVED_QK_LO]);
+  u16* dc = at<u16>(workspace, W.base.dc);
+  u16* dz = at<u16>(workspace, W.base.dz);
+  u16* da = at<u16>(workspace, W.base.da);
+  float* delta = at<float>(workspace, W.base.delta);
+  float* partials = at<float>(workspace, W.base.partials);
+  const ptb::GemmScratch gs{at<float>(workspace, W.base.gemm_partials),
+                            at<int>(workspace, W.base.counters), W.base.max_tiles};
+  float* amax = at<float>(workspace, W.amax);
+  const float* wamax = at<float>(fp8_weights, WL.amax);
+  uint8_t* dy8 = at<uint8_t>(workspace, W.dy8);
+  uint8_t* dy8t = at<uint8_t>(workspace, W.dy8t);
+  uint8_t* cg8t = at<uint8_t>(workspace, W.cg8t);
+  uint8_t* dz8 = at<uint8_t>(workspace, W.dz8);
+  uint8_t* dz8t = at<uint8_t>(workspace, W.dz8t);
+  uint8_t* a8t = at<uint8_t>(workspace, W.a8t);
+  const u16* DY = static_cast<const u16*>(dy);
+  const size_t hp = pad128(s.h), Tp = pad128(s.T), N1p = pad128(s.N1);
+  const int T = static_cast<int>(s.T), h = static_cast<int>(s.h);
+
+  PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
+  PTB_HIP(ptb::launch_zero_i32(reinterpret_cast<int*>(amax), AMAX_COUNT, strm));
+  PTB_STAGE(0, cast_fp8(cast_one(DY, s.h, s.T, s.h), ptb::FP8_E5M2, amax + AMAX_DY, dy8, hp,
+                        dy8t, Tp, strm));
+  {  // dgrad through [O ; FC2]: dc, and du = dg * GeLU'(u) into dZ's FC1 columns
+    ptb::GemmProblem pr;
+    pr.M = T; pr.N = static_cast<int>(s.K2); pr.K = static_cast<int>(hp);
+    pr.A = one8(dy8, hp, s.T);
+    pr.B = one8(at<uint8_t>(fp8_weights, WL.w2r), hp, s.K2);
+    pr.epi = ptb::Epilogue{};
+    pr.epi.o0 = dc; pr.epi.ld0 = static_cast<int>(s.hl);
+    pr.epi.o1 = dz; pr.epi.ld1 = static_cast<int>(s.N1);
+    pr.epi.col_off1 = static_cast<int>(3 * s.hl);
+    pr.epi.i0 = u; pr.epi.ld2 = static_cast<int>(s.f);
+    pr.epi.split = static_cast<int>(s.hl);
+    PTB_STAGE(1, ptb::launch_gemm_fp8(pr, ptb::FP8_E5M2, amax + AMAX_DY, ptb::FP8_E4M3,
+                                      wamax + 1, ptb::EPI_DGELU, gs, strm));
+  }
+  const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
+                            gs.max_tiles, ptb::device_compute_units()};
+  PTB_STAGE(2, ptb::launch_attention_bwd(qkv, qk_lo, c, lse, dc, delta, dz, static_cast<int>(s.N1),
+                                    static_cast<int>(s.b), static_cast<int>(s.s),
+                                    static_cast<int>(s.n), static_cast<int>(s.d),
+                                    static_cast<int>(s.w), as, strm));
+  PTB_STAGE(3, cast_fp8(cast_two(c, s.hl, g, s.f, s.hl, 0, s.T, s.K2), ptb::FP8_E4M3,
+                        amax + AMAX_CG_BWD, nullptr, 0, cg8t, Tp, strm));
+  {  // wgrad of [O ; FC2]: [c | g]^T dy
+    ptb::GemmProblem pr;
+    pr.M = static_cast<int>(s.K2); pr.N = h; pr.K = static_cast<int>(Tp);
+    pr.A = one8(cg8t, Tp, s.K2);
+    pr.B = one8(dy8t, Tp, s.h);
+    pr.epi = ptb::Epilogue{};
+    pr.epi.o0 = static_cast<u16*>(dw_o); pr.epi.ld0 = h;
+    pr.epi.o1 = static_cast<u16*>(dw_fc2); pr.epi.ld1 = h;
+    pr.epi.split = static_cast<int>(s.hl);
+    PTB_STAGE(4, ptb::launch_gemm_fp8(pr, ptb::FP8_E4M3, amax + AMAX_CG_BWD, ptb::FP8_E5M2,
+                                      amax + AMAX_DY, ptb::EPI_STORE2_ROWS, gs, strm));
+  }
+  PTB_STAGE(5, cast_fp8(cast_one(dz, s.N1, s.T, s.N1), ptb::FP8_E5M2, amax + AMAX_DZ, dz8, N1p,
+                        dz8t, Tp, strm));
+  {  // dgrad through [QKV | FC1]: da = dZ W1^T
+    ptb::GemmProblem pr;
+    pr.M = T; pr.N = h; pr.K = static_cast<int>(N1p);
+    pr.A = one8(dz8, N1p, s.T);
+    pr.B = one8(at<uint8_t>(fp8_weights, WL.w1r), N1p, s.h);
+    pr.epi = ptb::Epilogue{};
+    pr.epi.o0 = da; pr.epi.ld0 = h;
+    pr.epi.split = h;  // one output
+    PTB_STAGE(6, ptb::launch_gemm_fp8(pr, ptb::FP8_E5M2, amax + AMAX_DZ, ptb::FP8_E4M3,
+                                      wamax, ptb::EPI_STORE2_COLS, gs, strm));
+  }
+  PTB_STAGE(7, cast_fp8(cast_one(a, s.h, s.T, s.h), ptb::FP8_E4M3, amax + AMAX_A_BWD, nullptr, 0,
+                        a8t, Tp, strm));
+  {  // wgrad of [QKV | FC1]: a^T dZ
+    ptb::GemmProblem pr;
+    pr.M = h; pr.N = static_cast<int>(s.N1); pr.K = static_cast<int>(Tp);
+    pr.A = one8(a8t, Tp, s.h);
+    pr.B = one8(dz8t, Tp, s.N1);
+    pr.epi = ptb::Epilogue{};
+    pr.epi.o0 = static_cast<u16*>(dw_qkv); pr.epi.ld0 = static_cast<int>(3 * s.hl);
+    pr.epi.o1 = static_cast<u16*>(dw_fc1); pr.epi.ld1 = static_cast<int>(s.f);
+    pr.epi.split = static_cast<int>(3 * s.hl);
+    PTB_STAGE(8, ptb::launch_gemm_fp8(pr, ptb::FP8_E4M3, amax + AMAX_A_BWD, ptb::FP8_E5M2,
+                                      amax + AMAX_DZ, ptb::EPI_STORE2_COLS, gs, strm));
+  }
+  PTB_STAGE(9, ptb::launch_layernorm_bwd(da, static_cast<const u16*>(x),
+                                    static_cast<const u16*>(ln_gamma), mu, rstd, DY,
+                                    static_cast<u16*>(dx), partials,
+                                    static_cast<u16*>(d_ln_gamma), static_cast<u16*>(d_ln_beta),
+                                    T, h, strm, s.rms));
   return PTB_OK;
 }
 

@@ -169,3 +169,67 @@ class SerialBlock:
         shape, dt = shapes[name]
         nbytes = int(np.prod(shape)) * (2 if dt == bf else 4)
         return self.saved[off:off + nbytes].view(dt).view(shape)
+
+
+class Fp8Layer:
+    """One parallel block with its four GEMM parts in FP8 (include/ptb.h,
+    ptb_fp8_*).  A step is the weight cast, the forward and the backward: the
+    weights change at every optimizer step, so their FP8 copies do too."""
+
+    def __init__(self, w: Workload, inputs: dict, device: str = "cuda"):
+        if w.layers != 1:
+            raise ValueError("Fp8Layer runs one layer")
+        self.w = w
+        self.dims = P.dims_of(w)
+        dev = torch.device(device)
+        self.x = to_device_bf16(inputs["x"], dev)
+        self.dy = to_device_bf16(inputs["dy"], dev)
+        lay = inputs["layers"][0]
+        self.p = {k: to_device_bf16(lay[k], dev) for k in PARAM_NAMES}
+        self.fp8_weights = torch.empty(P.ptb_fp8_weights_bytes(self.dims), dtype=torch.uint8,
+                                       device=dev)
+        self.saved = torch.empty(P.ptb_saved_bytes(self.dims), dtype=torch.uint8, device=dev)
+        self.workspace = torch.empty(P.ptb_fp8_workspace_bytes(self.dims), dtype=torch.uint8,
+                                     device=dev)
+        self.y = torch.empty_like(self.x)
+        self.dx = torch.empty_like(self.x)
+        p = self.p
+        self.grads = {"d_ln_gamma": torch.empty_like(p["ln_gamma"]),
+                      "d_ln_beta": torch.empty_like(p["ln_beta"]),
+                      "dw_qkv": torch.empty_like(p["w_qkv"]), "dw_o": torch.empty_like(p["w_o"]),
+                      "dw_fc1": torch.empty_like(p["w_fc1"]),
+                      "dw_fc2": torch.empty_like(p["w_fc2"])}
+
+    def cast_weights(self, stream=None) -> None:
+        p = self.p
+        P.ptb_fp8_cast_weights(self.dims, p["w_qkv"], p["w_o"], p["w_fc1"], p["w_fc2"],
+                               self.fp8_weights, stream)
+
+    def forward(self, stream=None, events=None) -> None:
+        p = self.p
+        P.ptb_fp8_forward(self.dims, self.x, p["ln_gamma"], p["ln_beta"], self.fp8_weights,
+                          self.y, self.saved, self.workspace, stream, events)
+
+    def backward(self, stream=None, events=None) -> None:
+        p, g = self.p, self.grads
+        P.ptb_fp8_backward(self.dims, self.dy, self.x, p["ln_gamma"], self.fp8_weights,
+                           self.saved, self.dx, g["d_ln_gamma"], g["d_ln_beta"], g["dw_qkv"],
+                           g["dw_o"], g["dw_fc1"], g["dw_fc2"], self.workspace, stream, events)
+
+    def step(self, stream=None, fwd_events=None, bwd_events=None) -> None:
+        self.cast_weights(stream)
+        self.forward(stream, fwd_events)
+        self.backward(stream, bwd_events)
+
+    def saved_tensor(self, name: str) -> torch.Tensor:
+        """A view of one stashed tensor (the parallel block's slots)."""
+        w = self.w
+        T, h, hl, f = w.tokens, w.hidden, w.h_local, w.ffn
+        bf, f32 = torch.bfloat16, torch.float32
+        shapes = {"a": ((T, h), bf), "mu": ((T,), f32), "rstd": ((T,), f32),
+                  "qkv": ((T, 3 * hl), bf), "qk_lo": ((T, 2 * hl), bf), "c": ((T, hl), bf),
+                  "lse": ((w.batch, w.heads, w.seq), f32), "u": ((T, f), bf), "g": ((T, f), bf)}
+        off = P.ptb_saved_layout(self.dims)[name]
+        shape, dt = shapes[name]
+        nbytes = int(np.prod(shape)) * (2 if dt == bf else 4)
+        return self.saved[off:off + nbytes].view(dt).view(shape)
