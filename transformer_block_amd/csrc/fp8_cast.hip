@@ -3,16 +3,18 @@
 // tensor taken from the tensor itself).
 //
 //   amax:  max |x| over a logical bf16 matrix (one or two segments), one
+//          workgroup per CU with four rows' loads in flight per thread, one
 //          vector atomic max per workgroup on the float's bits (non-negative
 //          floats order like their bit patterns).
 //   cast:  code = RNE(clamp(x * s, -FMAX, FMAX)) with s = FMAX / amax, x * s
 //          one fp32 multiply; written row-wise (same layout) and/or
 //          transposed, so that every FP8 product reads two k-contiguous
-//          operands.  64 x 64 tiles: each thread loads a 4 x 4 block (four
-//          8-byte loads), the transpose goes through LDS as 4-byte columns
-//          of codes and leaves as 16-byte rows.  Padding (up to the output's
-//          leading dimension) is written as zero codes, so that products
-//          can run K up to a whole number of 128-wide k-steps.
+//          operands.  Tiles of 64 rows x 128 columns: each thread converts a
+//          4 x 8 block from four 16-byte loads; the transpose goes through
+//          LDS as 4-byte columns of codes and leaves as 16-byte rows.
+//          Padding (up to the output's leading dimension) is written as zero
+//          codes, so that products can run K up to a whole number of
+//          128-wide k-steps.
 #include <algorithm>
 
 #include "device_common.h"
@@ -21,8 +23,9 @@
 namespace ptb {
 namespace {
 
-constexpr int CT = 64;      // cast tile (rows and columns of X)
-constexpr int TS = CT + 4;  // LDS row stride in bytes of the transposed tile
+constexpr int CR = 64;        // cast tile: rows of X
+constexpr int CC = 128;       // cast tile: columns of X
+constexpr int TSW = CR / 4 + 1;  // LDS words per transposed row (64 codes + 4 bytes of pad)
 
 __device__ __forceinline__ const u16* src_at(const CastSrc& x, int r, int c) {
   if (x.split_on_rows)
@@ -34,19 +37,32 @@ __device__ __forceinline__ const u16* src_at(const CastSrc& x, int r, int c) {
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
-__global__ __launch_bounds__(256) void amax_kernel(CastSrc x, float* amax) {
-  __shared__ uint32_t part[4];
-  const uint32_t cpr = static_cast<uint32_t>(x.C) / 8;  // 16-byte chunks per row
-  const uint32_t total = static_cast<uint32_t>(x.R) * cpr;
+// Workgroup b takes rows AR b .. +AR-1, then AR G further, ...; a thread loads
+// one 16-byte chunk of each of the AR rows before it reduces them (AR loads
+// in flight).  The grid is small (one workgroup per CU): the workgroups' one
+// atomic each all go to the same address and are served one at a time.
+constexpr int AR = 4;
+constexpr int AMAX_THREADS = 1024;
+__global__ __launch_bounds__(AMAX_THREADS) void amax_kernel(CastSrc x, float* amax) {
+  __shared__ uint32_t part[AMAX_THREADS / 64];
+  const int nch = x.C / 8;  // 16-byte chunks per row
   uint32_t m = 0;
-  for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
-    const int r = static_cast<int>(i / cpr), c = static_cast<int>(i % cpr) * 8;
-    const uint4 v = *reinterpret_cast<const uint4*>(src_at(x, r, c));
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int r0 = blockIdx.x * AR; r0 < x.R; r0 += gridDim.x * AR) {
+    for (int c = threadIdx.x; c < nch; c += AMAX_THREADS) {
+      uint4 v[AR];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      m = umax(m, (w[k] & 0x7fffu) << 16);
-      m = umax(m, w[k] & 0x7fff0000u);
+      for (int u = 0; u < AR; ++u)
+        v[u] = r0 + u < x.R ? *reinterpret_cast<const uint4*>(src_at(x, r0 + u, c * 8))
+                            : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int u = 0; u < AR; ++u) {
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          m = umax(m, (w[k] & 0x7fffu) << 16);
+          m = umax(m, w[k] & 0x7fff0000u);
+        }
+      }
     }
   }
 #pragma unroll
@@ -54,7 +70,8 @@ __global__ __launch_bounds__(256) void amax_kernel(CastSrc x, float* amax) {
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    m = umax(umax(part[0], part[1]), umax(part[2], part[3]));
+#pragma unroll
+    for (int w = 1; w < AMAX_THREADS / 64; ++w) m = umax(m, part[w]);
     atomicMax(reinterpret_cast<unsigned int*>(amax), m);
   }
 }
@@ -76,49 +93,54 @@ __device__ __forceinline__ uint32_t quant4(float x0, float x1, float x2, float x
   return static_cast<uint32_t>(w);
 }
 
-// One 64 x 64 tile of X at (r0, c0).  Thread (br, bc) = (tid / 16, tid % 16)
-// owns rows r0 + 4 br .. +3 and columns c0 + 4 bc .. +3.
+// One tile of X, CR rows x CC columns at (r0, c0).  Thread (br, bc) =
+// (tid / 16, tid % 16) owns rows r0 + 4 br .. +3 and columns c0 + 8 bc .. +7
+// (four 16-byte loads).  Codes go out row-wise as 8-byte stores; for the
+// transpose each thread writes its 8 columns x 4 rows into LDS as 4-byte
+// column pieces, and each output row of 64 codes leaves as two 16-byte
+// stores from a pair of threads.
 template <int FMT>
 __global__ __launch_bounds__(256) void cast_kernel(CastSrc x, const float* amax, uint8_t* rows,
                                                    int ldr, uint8_t* cols, int ldc) {
-  __shared__ uint32_t tt[CT * TS / 4];
+  __shared__ uint32_t tt[CC * TSW];
   const float s = fp8_scale(*amax, fp8_max(FMT));
-  const int r0 = blockIdx.y * CT, c0 = blockIdx.x * CT;
+  const int r0 = blockIdx.y * CR, c0 = blockIdx.x * CC;
   const int tid = threadIdx.x, br = tid >> 4, bc = tid & 15;
-  const int c = c0 + 4 * bc;
-  uint32_t q[4];  // q[i]: codes of row r0 + 4 br + i, columns c .. c+3
+  const int c = c0 + 8 * bc;
+  uint2 q[4];  // q[i]: codes of row r0 + 4 br + i, columns c .. c+7
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = r0 + 4 * br + i;
-    uint2 v = make_uint2(0u, 0u);
-    if (r < x.R && c < x.C) v = *reinterpret_cast<const uint2*>(src_at(x, r, c));
-    q[i] = quant4<FMT>(lo_bf(v.x), hi_bf(v.x), lo_bf(v.y), hi_bf(v.y), s);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < x.R && c < x.C) v = *reinterpret_cast<const uint4*>(src_at(x, r, c));
+    q[i].x = quant4<FMT>(lo_bf(v.x), hi_bf(v.x), lo_bf(v.y), hi_bf(v.y), s);
+    q[i].y = quant4<FMT>(lo_bf(v.z), hi_bf(v.z), lo_bf(v.w), hi_bf(v.w), s);
   }
-  if (rows != nullptr && c0 < ldr) {
+  if (rows != nullptr && c < ldr) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = r0 + 4 * br + i;
-      if (r < x.R) *reinterpret_cast<uint32_t*>(rows + static_cast<size_t>(r) * ldr + c) = q[i];
+      if (r < x.R) *reinterpret_cast<uint2*>(rows + static_cast<size_t>(r) * ldr + c) = q[i];
     }
   }
   if (cols == nullptr || r0 >= ldc) return;
-  // column j of the 4 x 4 block: rows 4 br .. +3 as one 4-byte word
+  // column j of the thread's block: rows 4 br .. +3 as one 4-byte word
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t w = ((q[0] >> (8 * j)) & 0xffu) | (((q[1] >> (8 * j)) & 0xffu) << 8) |
-                       (((q[2] >> (8 * j)) & 0xffu) << 16) | (((q[3] >> (8 * j)) & 0xffu) << 24);
-    tt[((4 * bc + j) * TS + 4 * br) / 4] = w;
+  for (int j = 0; j < 8; ++j) {
+    const int sh = 8 * (j & 3);
+    const uint32_t w0 = j < 4 ? q[0].x : q[0].y, w1 = j < 4 ? q[1].x : q[1].y;
+    const uint32_t w2 = j < 4 ? q[2].x : q[2].y, w3 = j < 4 ? q[3].x : q[3].y;
+    tt[(8 * bc + j) * TSW + br] = ((w0 >> sh) & 0xffu) | (((w1 >> sh) & 0xffu) << 8) |
+                                  (((w2 >> sh) & 0xffu) << 16) | (((w3 >> sh) & 0xffu) << 24);
   }
   __syncthreads();
-  // output row oc = column c0 + oc of X, bytes 16 (tid % 4) .. +15
-  const int oc = tid >> 2, ob = (tid & 3) * 16;
+  // output row oc = column c0 + oc of X, codes of rows r0 + 32 (tid % 2) .. +31
+  const int oc = tid >> 1, ow = (tid & 1) * 8;
   if (c0 + oc >= x.C) return;
-  uint4 o;
-  o.x = tt[(oc * TS + ob) / 4];
-  o.y = tt[(oc * TS + ob + 4) / 4];
-  o.z = tt[(oc * TS + ob + 8) / 4];
-  o.w = tt[(oc * TS + ob + 12) / 4];
-  *reinterpret_cast<uint4*>(cols + static_cast<size_t>(c0 + oc) * ldc + r0 + ob) = o;
+  const uint32_t* t = tt + oc * TSW + ow;
+  uint8_t* o = cols + static_cast<size_t>(c0 + oc) * ldc + r0 + ow * 4;
+  reinterpret_cast<uint4*>(o)[0] = make_uint4(t[0], t[1], t[2], t[3]);
+  reinterpret_cast<uint4*>(o)[1] = make_uint4(t[4], t[5], t[6], t[7]);
 }
 
 bool src_ok(const CastSrc& x) {
@@ -131,10 +153,10 @@ bool src_ok(const CastSrc& x) {
 
 hipError_t launch_amax(const CastSrc& x, float* amax, hipStream_t s) {
   if (!src_ok(x) || amax == nullptr) return hipErrorInvalidValue;
-  const long chunks = static_cast<long>(x.R) * (x.C / 8);
-  if (chunks >= (1L << 31)) return hipErrorInvalidValue;
-  const int blocks = static_cast<int>(std::min<long>((chunks + 255) / 256, 1024));
-  hipLaunchKernelGGL(amax_kernel, dim3(blocks), dim3(256), 0, s, x, amax);
+  int cus = device_compute_units();
+  if (cus <= 0) cus = 256;
+  const int blocks = std::min((x.R + AR - 1) / AR, cus);
+  hipLaunchKernelGGL(amax_kernel, dim3(blocks), dim3(AMAX_THREADS), 0, s, x, amax);
   return hipGetLastError();
 }
 
@@ -143,11 +165,11 @@ hipError_t launch_cast_fp8(const CastSrc& x, Fp8Format fmt, const float* amax, u
   if (!src_ok(x) || amax == nullptr || (rows == nullptr && cols == nullptr))
     return hipErrorInvalidValue;
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  if (rows != nullptr && (ldr < x.C || ldr % CT != 0 || !al(rows))) return hipErrorInvalidValue;
-  if (cols != nullptr && (ldc < x.R || ldc % CT != 0 || !al(cols))) return hipErrorInvalidValue;
+  if (rows != nullptr && (ldr < x.C || ldr % 64 != 0 || !al(rows))) return hipErrorInvalidValue;
+  if (cols != nullptr && (ldc < x.R || ldc % 64 != 0 || !al(cols))) return hipErrorInvalidValue;
   const int rspan = cols != nullptr ? std::max(x.R, ldc) : x.R;
   const int cspan = rows != nullptr ? std::max(x.C, ldr) : x.C;
-  const dim3 grid((cspan + CT - 1) / CT, (rspan + CT - 1) / CT);
+  const dim3 grid((cspan + CC - 1) / CC, (rspan + CR - 1) / CR);
   if (fmt == FP8_E4M3)
     hipLaunchKernelGGL(cast_kernel<FP8_E4M3>, grid, dim3(256), 0, s, x, amax, rows, ldr, cols, ldc);
   else
