@@ -251,9 +251,14 @@ int32_t check_fp8_dims(const ptb_dims* dims, Shape* s) {
   const int32_t st = check_dims(dims, s);
   if (st != PTB_OK) return st;
   if (s->swiglu) return PTB_ERR_ARG;
-  // FP8 operands are addressed with 32-bit byte offsets as well
-  if (pad128(s->T) * s->N1 >= (1UL << 31) || pad128(s->N1) * s->h >= (1UL << 31))
-    return PTB_ERR_DIMS;
+  // FP8 operands are addressed with 32-bit byte offsets as well: every copy
+  // (rows x padded contiguous dimension, one byte each) stays below 2^31
+  const size_t T = s->T, h = s->h, N1 = s->N1, K2 = s->K2;
+  const size_t sizes[] = {T * pad128(h),  T * pad128(K2), T * pad128(N1), h * pad128(T),
+                          K2 * pad128(T), N1 * pad128(T), N1 * pad128(h), h * pad128(N1),
+                          h * pad128(K2), K2 * pad128(h)};
+  for (size_t b : sizes)
+    if (b >= (1UL << 31)) return PTB_ERR_DIMS;
   return PTB_OK;
 }
 
