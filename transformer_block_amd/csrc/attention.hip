@@ -171,13 +171,29 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
       // per-stage zeroing copies of the accumulator registers)
       const f32x16 zero = {};
       f32x16 sp = zero, dp = zero;
+      // query fragments of k-step ks + 1 read under the MFMAs of k-step ks
+      // (one wave per SIMD: a read issued just before its MFMA would leave
+      // the LDS latency exposed)
+      bf16x8 fq[2], fql[2], fdo[2];
+      fq[0] = row_frag<D>(q_lds, l32, g);
+      fql[0] = row_frag<D>(ql_lds, l32, g);
+      fdo[0] = row_frag<D>(do_lds, l32, g);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 qh = row_frag<D>(q_lds, l32, ks * 2 + g);
-        sp = mfma32x32x16(qh, kf[ks], ks == 0 ? zero : sp);
-        sp = mfma32x32x16(row_frag<D>(ql_lds, l32, ks * 2 + g), kf[ks], sp);
-        sp = mfma32x32x16(qh, kl[ks], sp);
-        dp = mfma32x32x16(row_frag<D>(do_lds, l32, ks * 2 + g), vf[ks], ks == 0 ? zero : dp);
+        const int c = ks & 1;
+        if (ks + 1 < NKS) {
+          fq[c ^ 1] = row_frag<D>(q_lds, l32, (ks + 1) * 2 + g);
+          fql[c ^ 1] = row_frag<D>(ql_lds, l32, (ks + 1) * 2 + g);
+          fdo[c ^ 1] = row_frag<D>(do_lds, l32, (ks + 1) * 2 + g);
+        }
+        sp = mfma32x32x16(fq[c], kf[ks], ks == 0 ? zero : sp);
+        sp = mfma32x32x16(fql[c], kf[ks], sp);
+        sp = mfma32x32x16(fq[c], kl[ks], sp);
+        dp = mfma32x32x16(fdo[c], vf[ks], ks == 0 ? zero : dp);
+        if (ks + 1 < NKS) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMAs
+        }
       }
       if (!full) {
         // a stage on the diagonal or the window's edge: keep queries in

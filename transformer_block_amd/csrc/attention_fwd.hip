@@ -96,15 +96,26 @@ __global__ __launch_bounds__(256, BKF == 32 ? 2 : 1) void attn_fwd_kernel(const 
     // each chain's first product takes a literal zero accumulator
     const f32x16 zero = {};
     f32x16 st[KB];
+    // key fragments of step t + 1 (t = 16-wide k-step ks of key block kb)
+    // read under the MFMAs of step t
+    constexpr int NT = KB * NKS;
+    bf16x8 fk[2], fkl[2];
+    fk[0] = row_frag<D>(k_lds, l32, g);
+    fkl[0] = row_frag<D>(kl_lds, l32, g);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      st[kb] = zero;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 kh = row_frag<D>(k_lds, kb * 32 + l32, ks * 2 + g);
-        st[kb] = mfma32x32x16(kh, qf[ks], ks == 0 ? zero : st[kb]);
-        st[kb] = mfma32x32x16(row_frag<D>(kl_lds, kb * 32 + l32, ks * 2 + g), qf[ks], st[kb]);
-        st[kb] = mfma32x32x16(kh, ql[ks], st[kb]);
+    for (int t = 0; t < NT; ++t) {
+      const int kb = t / NKS, ks = t % NKS, c = t & 1;
+      if (t + 1 < NT) {
+        const int r = ((t + 1) / NKS) * 32 + l32, kk = ((t + 1) % NKS) * 2 + g;
+        fk[c ^ 1] = row_frag<D>(k_lds, r, kk);
+        fkl[c ^ 1] = row_frag<D>(kl_lds, r, kk);
+      }
+      st[kb] = mfma32x32x16(fk[c], qf[ks], ks == 0 ? zero : st[kb]);
+      st[kb] = mfma32x32x16(fkl[c], qf[ks], st[kb]);
+      st[kb] = mfma32x32x16(fk[c], ql[ks], st[kb]);
+      if (t + 1 < NT) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // MFMAs
       }
     }
     float mx = -INFINITY;
