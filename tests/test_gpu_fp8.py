@@ -168,3 +168,32 @@ def test_fp8_repeat_runs_are_bitwise_identical():
     again = [lyr.y, lyr.dx] + list(lyr.grads.values())
     for a, b in zip(first, again):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_fp8_zero_output_weights_give_the_identity():
+    """W_o = W_fc2 = 0: the operand [W_o ; W_fc2] has amax 0, so its scale is
+    1 and its codes are all zero; the layer is then exactly y = x and
+    dx = dy (da = 0), while dW_o and dW_fc2 still match the oracle."""
+    w = W("f8zero", 2, 96, 256, 2, 128, 512, 40, seed=930)
+    inp = I.make_inputs(w, random_ln=True)
+    lay = inp["layers"][0]
+    lay["w_o"] = np.zeros_like(lay["w_o"])
+    lay["w_fc2"] = np.zeros_like(lay["w_fc2"])
+    lyr = Fp8Layer(w, inp, "cuda")
+    lyr.step()
+    torch.cuda.synchronize()
+    assert torch.equal(lyr.y.view(torch.int16), lyr.x.view(torch.int16))
+    assert torch.equal(lyr.dx.view(torch.int16), lyr.dy.view(torch.int16))
+    for k in ("d_ln_gamma", "d_ln_beta", "dw_qkv", "dw_fc1"):
+        assert not _np(lyr.grads[k]).any(), k
+    f = I.bf16_bits_to_f64
+    x, dy = f(inp["x"]), f(inp["dy"])
+    p = {k: f(v) for k, v in lay.items()}
+    y, cache = F8.fp8_ptb_forward(x, p, w.batch, w.seq, w.heads, w.head_dim, w.window,
+                                  w.ln_eps)
+    g = F8.fp8_ptb_backward(dy, cache, p, w.window)
+    assert np.array_equal(y, x) and np.array_equal(g["dx"], dy)
+    for k in ("dw_o", "dw_fc2"):
+        e = rel_fro(_np(lyr.grads[k]), g[k])
+        log(f"[fp8 zero] {k}={e:.2e}")
+        assert e < FP8_TOL, (k, e)

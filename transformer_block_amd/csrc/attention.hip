@@ -295,17 +295,21 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 }
 
 // ------------------------------------------------------------------- dQ
-// Query rows of 128 (4 waves x 32), key tiles of 64 staged by DMA one tile
+// Query rows of 128 (4 waves x 32), key tiles of BKQ staged by DMA one tile
 // ahead, two stages of three row-major tiles: K, K_lo and V (the A operands
 // of S^T = K Q^T and dP^T = V dO^T; K read transposed, rows in the
-// accumulator's order, is also the A operand of dQ^T += K^T dS^T).
+// accumulator's order, is also the A operand of dQ^T += K^T dS^T).  With
+// 32-key tiles the two stages take 48 KB for D = 128 and two workgroups share
+// a CU, so one wave's softmax runs under the other's MFMAs.
+constexpr int BKQ = 32;
+constexpr int KBQ = BKQ / 32;  // 32 x 32 S^T blocks per tile
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(256, BKQ == 32 ? 2 : 1) void attn_bwd_dq_kernel(
     const u16* __restrict__ qkv, const u16* __restrict__ qk_lo, const u16* __restrict__ dcg,
     const float* __restrict__ lse, const float* __restrict__ delta, u16* __restrict__ dz,
     int ld_dz, int s, int n, int window, int nqt, RowSplit rsp) {
   constexpr int NKS = D / 16, ND = D / 32;
-  constexpr int OPB = 64 * D;  // u16 elements of one operand's tile
+  constexpr int OPB = BKQ * D;  // u16 elements of one operand's tile
   __shared__ __attribute__((aligned(1024))) u16 kv[2 * 3 * OPB];
   __shared__ int arrival;
 
@@ -327,7 +331,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 
   const int kv_begin = item.span.begin;
   const int kv_end = item.span.end;
-  TileDma<D, 64, false> dk, dkl, dv;
+  TileDma<D, BKQ, false> dk, dkl, dv;
   dk.init(Kg, ld, s, wave, lane);
   dkl.init(Klg, 2 * hl, s, wave, lane);
   dv.init(Vg, ld, s, wave, lane);
@@ -364,24 +368,24 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     for (int e = 0; e < 16; ++e) dq[db][e] = 0.0f;
 
   int stage = 0;
-  for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKV) {
+  for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKQ) {
     wait_vm_lds<0>();  // this wave's loads of tile kt0 landed
     __syncthreads();   // every wave's; the other stage is free again
-    if (kt0 + BKV < kv_end) issue(kv_lds + (stage ^ 1) * (3 * OPB * 2), kt0 + BKV);
+    if (kt0 + BKQ < kv_end) issue(kv_lds + (stage ^ 1) * (3 * OPB * 2), kt0 + BKQ);
     const u16* k_lds = kv + stage * 3 * OPB;
     const u16* kl_lds = k_lds + OPB;
     const u16* v_lds = k_lds + 2 * OPB;
     stage ^= 1;
 
-    const bool any = qw0 < s && qw0 + 31 >= kt0 && qw0 - (kt0 + BKV - 1) < window;
+    const bool any = qw0 < s && qw0 + 31 >= kt0 && qw0 - (kt0 + BKQ - 1) < window;
     if (!any) continue;
-    const bool full = kt0 + BKV - 1 <= qw0 && qw0 + 31 - kt0 < window && kt0 + BKV <= s;
+    const bool full = kt0 + BKQ - 1 <= qw0 && qw0 + 31 - kt0 < window && kt0 + BKQ <= s;
 
     // each chain's first product takes a literal zero accumulator
     const f32x16 zero = {};
-    f32x16 st[2], dpt[2];
+    f32x16 st[KBQ], dpt[KBQ];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KBQ; ++kb) {
       st[kb] = zero;
       dpt[kb] = zero;
 #pragma unroll
@@ -402,7 +406,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
       const int lo = max(qi - window + 1, 0) - base;
       const int hi = min(qi, s - 1) - base;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KBQ; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int off = kb * 32 + (e >> 2) * 8 + (e & 3);
@@ -410,14 +414,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
         }
     }
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KBQ; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float p = __builtin_amdgcn_exp2f(fmaf(st[kb][e], sc, -lq));
         st[kb][e] = p * (dpt[kb][e] - dq_delta);
       }
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KBQ; ++kb)
 #pragma unroll
       for (int e2 = 0; e2 < 2; ++e2) {
         const bf16x8 dsb = pack8(st[kb], e2 * 8);
