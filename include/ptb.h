@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define PTB_ABI_VERSION 5
+#define PTB_ABI_VERSION 6
 
 enum ptb_status {
   PTB_OK = 0,
@@ -369,19 +369,23 @@ int32_t ptb_lamb_step(const ptb_lamb_hyper* hyper, const ptb_lamb_tensor* tensor
  * dims as for ptb_forward; norm LayerNorm or RMSNorm, mlp GeLU only
  * (PTB_ERR_ARG for SwiGLU).  Any b, s, h, f allowed by ptb_validate_dims:
  * the FP8 copies pad their contiguous dimension with zero codes to a
- * multiple of 128.  Inputs, outputs, `saved` (same size and slots as for
- * ptb_forward; A_LO is not written) and ownership are as for the bf16 calls;
+ * multiple of 128.  Inputs, outputs and ownership are as for the bf16 calls.
+ * `saved` (ptb_fp8_saved_bytes) holds the parallel block's slots at the
+ * offsets ptb_saved_layout gives (A_LO is not written), followed by the
+ * transposed E4M3 copies of a and [c | g] and their amax, which the forward
+ * casts for the weight gradients;
  * the calls are asynchronous on `stream` and return PTB_ERR_HIP if a launch
  * fails.  stage_events: NULL, or 2 hipEvent_t per stage (start, end; NULL
  * entries skipped) recorded around each stage as for ptb_forward_timed.
  * ------------------------------------------------------------------------ */
 #define PTB_FP8_FWD_STAGES 6
-#define PTB_FP8_BWD_STAGES 10
+#define PTB_FP8_BWD_STAGES 8
 
 /* Bytes of the FP8 weight buffer (amax of W1 = [W_qkv | W_fc1] and
- * W2 = [W_o ; W_fc2], then W1^T, W1, W2^T and W2 in E4M3) and of the FP8
- * layer's workspace. */
+ * W2 = [W_o ; W_fc2], then W1^T, W1, W2^T and W2 in E4M3), of the FP8
+ * layer's stash and of its workspace. */
 int32_t ptb_fp8_weights_bytes(const ptb_dims* dims, size_t* bytes);
+int32_t ptb_fp8_saved_bytes(const ptb_dims* dims, size_t* bytes);
 int32_t ptb_fp8_workspace_bytes(const ptb_dims* dims, size_t* bytes);
 
 /* Byte offsets of the parts of the FP8 weight buffer (`offsets` has room
@@ -417,19 +421,20 @@ int32_t ptb_fp8_cast_weights(const ptb_dims* dims, const void* w_qkv, const void
                              const void* w_fc1, const void* w_fc2, void* fp8_weights,
                              void* stream);
 
-/* Forward: y [T, h] and `saved`.  Stages: 0 LayerNorm, 1 cast a, 2 [QKV | FC1]
- * FP8 product + GeLU, 3 attention, 4 cast [c | g], 5 [O ; FC2] FP8 product +
- * residual. */
+/* Forward: y [T, h] and `saved`.  Stages: 0 LayerNorm, 1 cast a (row-wise
+ * and transposed), 2 [QKV | FC1] FP8 product + GeLU, 3 attention, 4 cast
+ * [c | g] (both ways), 5 [O ; FC2] FP8 product + residual. */
 int32_t ptb_fp8_forward(const ptb_dims* dims, const void* x, const void* ln_gamma,
                         const void* ln_beta, const void* fp8_weights, void* y, void* saved,
                         void* workspace, void* stream, void* const* stage_events);
 
 /* Backward for upstream gradient dy [T, h] from the `saved` of the matching
  * ptb_fp8_forward (same x, same fp8_weights); writes what ptb_backward
- * writes.  It recomputes every amax it uses, so it does not depend on the
- * forward's workspace contents.  Stages: 0 cast dy, 1 dgrad [O ; FC2] +
- * GeLU', 2 attention backward, 3 cast [c | g]^T, 4 wgrad [O ; FC2], 5 cast dZ,
- * 6 dgrad [QKV | FC1], 7 cast a^T, 8 wgrad [QKV | FC1], 9 LayerNorm backward
+ * writes.  It reads the forward's FP8 copies of a and [c | g] from `saved`
+ * and casts the gradient operands itself; it does not depend on the
+ * forward's workspace contents.  Stages: 0 cast dy (both ways), 1 dgrad
+ * [O ; FC2] + GeLU', 2 attention backward, 3 wgrad [O ; FC2], 4 cast dZ (both
+ * ways), 5 dgrad [QKV | FC1], 6 wgrad [QKV | FC1], 7 LayerNorm backward
  * (+ dy). */
 int32_t ptb_fp8_backward(const ptb_dims* dims, const void* dy, const void* x,
                          const void* ln_gamma, const void* fp8_weights, const void* saved,

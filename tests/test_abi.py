@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert P.ptb_abi_version() == 5
+    assert P.ptb_abi_version() == 6
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert P.ptb_status_string(code) and P.ptb_status_string(code) != "unknown status"
     assert P.ptb_status_string(12345) == "unknown status"
@@ -236,10 +236,12 @@ def test_fp8_weight_layout_and_sizes(lib):
     r = good_dims(hidden=192, heads=3, ffn=768)
     lr = P.ptb_fp8_weights_layout(r)
     assert lr["w1"] - lr["w1t"] >= (3 * 192 + 768) * 256
-    # the workspace holds the bf16 layer's plus the FP8 activation copies
+    # the workspace holds the bf16 layer's plus the FP8 copies that live
+    # within one call; the stash adds the transposed copies of a and [c | g]
     T = 512
     assert P.ptb_fp8_workspace_bytes(d) >= P.ptb_workspace_bytes(d) + T * (
-        pad(h) * 2 + pad(K2) + pad(N1)) + pad(T) * (2 * h + K2 + N1)
+        pad(h) * 2 + pad(K2) + pad(N1)) + pad(T) * (h + N1)
+    assert P.ptb_fp8_saved_bytes(d) >= P.ptb_saved_bytes(d) + 8 + pad(T) * (h + K2)
 
 
 def test_fp8_calls_reject_bad_arguments_before_any_hip_call(lib):

@@ -222,11 +222,11 @@ Fp8WeightLayout fp8_weight_layout(const Shape& s) {
 }
 
 // The FP8 workspace: the bf16 layer's workspace, then the amax of the
-// activation operands and their FP8 copies.
-enum Fp8Amax { AMAX_A = 0, AMAX_CG, AMAX_DY, AMAX_DZ, AMAX_A_BWD, AMAX_CG_BWD, AMAX_COUNT };
+// gradient operands and the FP8 copies that live within one call.
+enum Fp8Amax { AMAX_DY = 0, AMAX_DZ, AMAX_COUNT };
 struct Fp8WorkLayout {
   WorkLayout base;
-  size_t amax, a8, cg8, dy8, dy8t, cg8t, dz8, dz8t, a8t, total;
+  size_t amax, a8, cg8, dy8, dy8t, dz8, dz8t, total;
 };
 Fp8WorkLayout fp8_work_layout(const Shape& s) {
   Fp8WorkLayout W;
@@ -234,16 +234,33 @@ Fp8WorkLayout fp8_work_layout(const Shape& s) {
   size_t o = W.base.total;
   const size_t Tp = pad128(s.T);
   W.amax = o; o = align_up(o + AMAX_COUNT * sizeof(float));
-  W.a8 = o; o = align_up(o + s.T * pad128(s.h));     // a       [T, h]
-  W.cg8 = o; o = align_up(o + s.T * pad128(s.K2));   // [c | g] [T, K2]
+  W.a8 = o; o = align_up(o + s.T * pad128(s.h));     // a       [T, h]  (forward)
+  W.cg8 = o; o = align_up(o + s.T * pad128(s.K2));   // [c | g] [T, K2] (forward)
   W.dy8 = o; o = align_up(o + s.T * pad128(s.h));    // dy      [T, h]
   W.dy8t = o; o = align_up(o + s.h * Tp);            // dy^T    [h, T]
-  W.cg8t = o; o = align_up(o + s.K2 * Tp);           // [c | g]^T
   W.dz8 = o; o = align_up(o + s.T * pad128(s.N1));   // dZ      [T, N1]
   W.dz8t = o; o = align_up(o + s.N1 * Tp);           // dZ^T
-  W.a8t = o; o = align_up(o + s.h * Tp);             // a^T
   W.total = o;
   return W;
+}
+
+// The FP8 layer's stash: the parallel block's slots, then what the forward
+// casts for the weight gradients (the transposed E4M3 copies of a and
+// [c | g] and their amax).
+struct Fp8SavedLayout {
+  SavedLayout base;
+  size_t amax, a8t, cg8t, total;
+};
+Fp8SavedLayout fp8_saved_layout(const Shape& s) {
+  Fp8SavedLayout L;
+  L.base = saved_layout(s);
+  size_t o = L.base.total;
+  const size_t Tp = pad128(s.T);
+  L.amax = o; o = align_up(o + 2 * sizeof(float));   // amax of a, of [c | g]
+  L.a8t = o; o = align_up(o + s.h * Tp);             // a^T       [h, T]
+  L.cg8t = o; o = align_up(o + s.K2 * Tp);           // [c | g]^T [K2, T]
+  L.total = o;
+  return L;
 }
 
 // The variant covers LayerNorm or RMSNorm with the GeLU MLP.
@@ -903,6 +920,15 @@ int32_t ptb_fp8_weights_bytes(const ptb_dims* dims, size_t* bytes) {
   return PTB_OK;
 }
 
+int32_t ptb_fp8_saved_bytes(const ptb_dims* dims, size_t* bytes) {
+  Shape s;
+  const int32_t st = check_fp8_dims(dims, &s);
+  if (st != PTB_OK) return st;
+  if (bytes == nullptr) return PTB_ERR_NULL;
+  *bytes = fp8_saved_layout(s).total;
+  return PTB_OK;
+}
+
 int32_t ptb_fp8_workspace_bytes(const ptb_dims* dims, size_t* bytes) {
   Shape s;
   const int32_t st = check_fp8_dims(dims, &s);
@@ -977,7 +1003,8 @@ int32_t ptb_fp8_forward(const ptb_dims* dims, const void* x, const void* ln_gamm
   st = check_ptrs({x, ln_gamma, ln_beta, fp8_weights, y, saved, workspace});
   if (st != PTB_OK) return st;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
-  const SavedLayout L = saved_layout(s);
+  const Fp8SavedLayout SL = fp8_saved_layout(s);
+  const SavedLayout& L = SL.base;
   const Fp8WorkLayout W = fp8_work_layout(s);
   const Fp8WeightLayout WL = fp8_weight_layout(s);
   const ptb::GemmScratch gs{at<float>(workspace, W.base.gemm_partials),
@@ -991,21 +1018,24 @@ int32_t ptb_fp8_forward(const ptb_dims* dims, const void* x, const void* ln_gamm
   u16* c = at<u16>(saved, L.off[PTB_SAVED_C]);
   float* lse = at<float>(saved, L.off[PTB_SAVED_LSE]);
   u16* qk_lo = at<u16>(saved, L.off[PTB_SAVED_QK_LO]);
-  float* amax = at<float>(workspace, W.amax);
+  float* samax = at<float>(saved, SL.amax);  // [0] a, [1] [c | g]
   const float* wamax = at<float>(fp8_weights, WL.amax);
   uint8_t* a8 = at<uint8_t>(workspace, W.a8);
   uint8_t* cg8 = at<uint8_t>(workspace, W.cg8);
-  const size_t hp = pad128(s.h), K2p = pad128(s.K2);
+  uint8_t* a8t = at<uint8_t>(saved, SL.a8t);
+  uint8_t* cg8t = at<uint8_t>(saved, SL.cg8t);
+  const size_t hp = pad128(s.h), K2p = pad128(s.K2), Tp = pad128(s.T);
 
   PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
-  PTB_HIP(ptb::launch_zero_i32(reinterpret_cast<int*>(amax), AMAX_COUNT, strm));
+  PTB_HIP(ptb::launch_zero_i32(reinterpret_cast<int*>(samax), 2, strm));
   PTB_STAGE(0, ptb::launch_layernorm_fwd(static_cast<const u16*>(x),
                                     static_cast<const u16*>(ln_gamma),
                                     static_cast<const u16*>(ln_beta), a, nullptr, mu, rstd,
                                     static_cast<int>(s.T), static_cast<int>(s.h), dims->ln_eps,
                                     strm, s.rms));
-  PTB_STAGE(1, cast_fp8(cast_one(a, s.h, s.T, s.h), ptb::FP8_E4M3, amax + AMAX_A, a8, hp,
-                        nullptr, 0, strm));
+  // a row-wise for the [QKV | FC1] product, transposed (stashed) for its
+  // weight gradient
+  PTB_STAGE(1, cast_fp8(cast_one(a, s.h, s.T, s.h), ptb::FP8_E4M3, samax, a8, hp, a8t, Tp, strm));
   {  // [qkv | u] = a W1 in one FP8 product; q, k stored as value + residual, g = GeLU(u)
     ptb::GemmProblem pr;
     pr.M = static_cast<int>(s.T); pr.N = static_cast<int>(s.N1); pr.K = static_cast<int>(hp);
@@ -1018,7 +1048,7 @@ int32_t ptb_fp8_forward(const ptb_dims* dims, const void* x, const void* ln_gamm
     pr.epi.o3 = qk_lo; pr.epi.ld3 = static_cast<int>(2 * s.hl);
     pr.epi.lo_cols = static_cast<int>(2 * s.hl);
     pr.epi.split = static_cast<int>(3 * s.hl);
-    PTB_STAGE(2, ptb::launch_gemm_fp8(pr, ptb::FP8_E4M3, amax + AMAX_A, ptb::FP8_E4M3,
+    PTB_STAGE(2, ptb::launch_gemm_fp8(pr, ptb::FP8_E4M3, samax, ptb::FP8_E4M3,
                                       wamax, ptb::EPI_QKV_GELU, gs, strm));
   }
   const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
@@ -1027,7 +1057,7 @@ int32_t ptb_fp8_forward(const ptb_dims* dims, const void* x, const void* ln_gamm
                                     static_cast<int>(s.s), static_cast<int>(s.n),
                                     static_cast<int>(s.d), static_cast<int>(s.w), as, strm));
   PTB_STAGE(4, cast_fp8(cast_two(c, s.hl, g, s.f, s.hl, 0, s.T, s.K2), ptb::FP8_E4M3,
-                        amax + AMAX_CG, cg8, K2p, nullptr, 0, strm));
+                        samax + 1, cg8, K2p, cg8t, Tp, strm));
   {  // y = x + [c | g] W2
     ptb::GemmProblem pr;
     pr.M = static_cast<int>(s.T); pr.N = static_cast<int>(s.h); pr.K = static_cast<int>(K2p);
@@ -1036,7 +1066,7 @@ int32_t ptb_fp8_forward(const ptb_dims* dims, const void* x, const void* ln_gamm
     pr.epi = ptb::Epilogue{};
     pr.epi.o0 = static_cast<u16*>(y); pr.epi.i0 = static_cast<const u16*>(x);
     pr.epi.ld0 = static_cast<int>(s.h);
-    PTB_STAGE(5, ptb::launch_gemm_fp8(pr, ptb::FP8_E4M3, amax + AMAX_CG, ptb::FP8_E4M3,
+    PTB_STAGE(5, ptb::launch_gemm_fp8(pr, ptb::FP8_E4M3, samax + 1, ptb::FP8_E4M3,
                                       wamax + 1, ptb::EPI_RESIDUAL, gs, strm));
   }
   return PTB_OK;
@@ -1054,15 +1084,14 @@ int32_t ptb_fp8_backward(const ptb_dims* dims, const void* dy, const void* x,
                    dw_fc1, dw_fc2, workspace});
   if (st != PTB_OK) return st;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
-  const SavedLayout L = saved_layout(s);
+  const Fp8SavedLayout SL = fp8_saved_layout(s);
+  const SavedLayout& L = SL.base;
   const Fp8WorkLayout W = fp8_work_layout(s);
   const Fp8WeightLayout WL = fp8_weight_layout(s);
-  const u16* a = at<u16>(saved, L.off[PTB_SAVED_A]);
   const float* mu = at<float>(saved, L.off[PTB_SAVED_MU]);
   const float* rstd = at<float>(saved, L.off[PTB_SAVED_RSTD]);
   const u16* qkv = at<u16>(saved, L.off[PTB_SAVED_QKV]);
   const u16* u = at<u16>(saved, L.off[PTB_SAVED_U]);
-  const u16* g = at<u16>(saved, L.off[PTB_SAVED_G]);
   const u16* c = at<u16>(saved, L.off[PTB_SAVED_C]);
   const float* lse = at<float>(saved, L.off[PTB_SAVED_LSE]);
   const u16* qk_lo = at<u16>(saved, L.off[PTB_SAVED_QK_LO]);
@@ -1074,13 +1103,14 @@ int32_t ptb_fp8_backward(const ptb_dims* dims, const void* dy, const void* x,
   const ptb::GemmScratch gs{at<float>(workspace, W.base.gemm_partials),
                             at<int>(workspace, W.base.counters), W.base.max_tiles};
   float* amax = at<float>(workspace, W.amax);
+  const float* samax = at<float>(saved, SL.amax);  // the forward's: [0] a, [1] [c | g]
   const float* wamax = at<float>(fp8_weights, WL.amax);
   uint8_t* dy8 = at<uint8_t>(workspace, W.dy8);
   uint8_t* dy8t = at<uint8_t>(workspace, W.dy8t);
-  uint8_t* cg8t = at<uint8_t>(workspace, W.cg8t);
+  const uint8_t* cg8t = at<uint8_t>(saved, SL.cg8t);
   uint8_t* dz8 = at<uint8_t>(workspace, W.dz8);
   uint8_t* dz8t = at<uint8_t>(workspace, W.dz8t);
-  uint8_t* a8t = at<uint8_t>(workspace, W.a8t);
+  const uint8_t* a8t = at<uint8_t>(saved, SL.a8t);
   const u16* DY = static_cast<const u16*>(dy);
   const size_t hp = pad128(s.h), Tp = pad128(s.T), N1p = pad128(s.N1);
   const int T = static_cast<int>(s.T), h = static_cast<int>(s.h);
@@ -1109,8 +1139,6 @@ int32_t ptb_fp8_backward(const ptb_dims* dims, const void* dy, const void* x,
                                     static_cast<int>(s.b), static_cast<int>(s.s),
                                     static_cast<int>(s.n), static_cast<int>(s.d),
                                     static_cast<int>(s.w), as, strm));
-  PTB_STAGE(3, cast_fp8(cast_two(c, s.hl, g, s.f, s.hl, 0, s.T, s.K2), ptb::FP8_E4M3,
-                        amax + AMAX_CG_BWD, nullptr, 0, cg8t, Tp, strm));
   {  // wgrad of [O ; FC2]: [c | g]^T dy
     ptb::GemmProblem pr;
     pr.M = static_cast<int>(s.K2); pr.N = h; pr.K = static_cast<int>(Tp);
@@ -1120,10 +1148,10 @@ int32_t ptb_fp8_backward(const ptb_dims* dims, const void* dy, const void* x,
     pr.epi.o0 = static_cast<u16*>(dw_o); pr.epi.ld0 = h;
     pr.epi.o1 = static_cast<u16*>(dw_fc2); pr.epi.ld1 = h;
     pr.epi.split = static_cast<int>(s.hl);
-    PTB_STAGE(4, ptb::launch_gemm_fp8(pr, ptb::FP8_E4M3, amax + AMAX_CG_BWD, ptb::FP8_E5M2,
+    PTB_STAGE(3, ptb::launch_gemm_fp8(pr, ptb::FP8_E4M3, samax + 1, ptb::FP8_E5M2,
                                       amax + AMAX_DY, ptb::EPI_STORE2_ROWS, gs, strm));
   }
-  PTB_STAGE(5, cast_fp8(cast_one(dz, s.N1, s.T, s.N1), ptb::FP8_E5M2, amax + AMAX_DZ, dz8, N1p,
+  PTB_STAGE(4, cast_fp8(cast_one(dz, s.N1, s.T, s.N1), ptb::FP8_E5M2, amax + AMAX_DZ, dz8, N1p,
                         dz8t, Tp, strm));
   {  // dgrad through [QKV | FC1]: da = dZ W1^T
     ptb::GemmProblem pr;
@@ -1133,11 +1161,9 @@ int32_t ptb_fp8_backward(const ptb_dims* dims, const void* dy, const void* x,
     pr.epi = ptb::Epilogue{};
     pr.epi.o0 = da; pr.epi.ld0 = h;
     pr.epi.split = h;  // one output
-    PTB_STAGE(6, ptb::launch_gemm_fp8(pr, ptb::FP8_E5M2, amax + AMAX_DZ, ptb::FP8_E4M3,
+    PTB_STAGE(5, ptb::launch_gemm_fp8(pr, ptb::FP8_E5M2, amax + AMAX_DZ, ptb::FP8_E4M3,
                                       wamax, ptb::EPI_STORE2_COLS, gs, strm));
   }
-  PTB_STAGE(7, cast_fp8(cast_one(a, s.h, s.T, s.h), ptb::FP8_E4M3, amax + AMAX_A_BWD, nullptr, 0,
-                        a8t, Tp, strm));
   {  // wgrad of [QKV | FC1]: a^T dZ
     ptb::GemmProblem pr;
     pr.M = h; pr.N = static_cast<int>(s.N1); pr.K = static_cast<int>(Tp);
@@ -1147,10 +1173,10 @@ int32_t ptb_fp8_backward(const ptb_dims* dims, const void* dy, const void* x,
     pr.epi.o0 = static_cast<u16*>(dw_qkv); pr.epi.ld0 = static_cast<int>(3 * s.hl);
     pr.epi.o1 = static_cast<u16*>(dw_fc1); pr.epi.ld1 = static_cast<int>(s.f);
     pr.epi.split = static_cast<int>(3 * s.hl);
-    PTB_STAGE(8, ptb::launch_gemm_fp8(pr, ptb::FP8_E4M3, amax + AMAX_A_BWD, ptb::FP8_E5M2,
+    PTB_STAGE(6, ptb::launch_gemm_fp8(pr, ptb::FP8_E4M3, samax, ptb::FP8_E5M2,
                                       amax + AMAX_DZ, ptb::EPI_STORE2_COLS, gs, strm));
   }
-  PTB_STAGE(9, ptb::launch_layernorm_bwd(da, static_cast<const u16*>(x),
+  PTB_STAGE(7, ptb::launch_layernorm_bwd(da, static_cast<const u16*>(x),
                                     static_cast<const u16*>(ln_gamma), mu, rstd, DY,
                                     static_cast<u16*>(dx), partials,
                                     static_cast<u16*>(d_ln_gamma), static_cast<u16*>(d_ln_beta),

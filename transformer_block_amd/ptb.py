@@ -120,6 +120,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ptb_fp8_quantize": (ctypes.c_int32, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                               _P, _P, _P, _P]),
         "ptb_fp8_workspace_bytes": (ctypes.c_int32, [_D, ctypes.POINTER(ctypes.c_size_t)]),
+        "ptb_fp8_saved_bytes": (ctypes.c_int32, [_D, ctypes.POINTER(ctypes.c_size_t)]),
         "ptb_fp8_cast_weights": (ctypes.c_int32, [_D] + [_P] * 6),
         "ptb_fp8_forward": (ctypes.c_int32, [_D] + [_P] * 9),
         "ptb_fp8_backward": (ctypes.c_int32, [_D] + [_P] * 15),
@@ -350,11 +351,11 @@ def ptb_lamb_step(hyper: ptb_lamb_hyper, tensors, norms, workspace, stream=None,
 
 # ---- FP8 GEMM variant: see include/ptb.h
 PTB_FP8_FWD_STAGES = 6
-PTB_FP8_BWD_STAGES = 10
+PTB_FP8_BWD_STAGES = 8
 FP8_FWD_STAGE_NAMES = ("layernorm_fwd", "cast_a", "gemm_qkv_fc1_fp8", "attention_fwd",
                        "cast_cg", "gemm_o_fc2_residual_fp8")
-FP8_BWD_STAGE_NAMES = ("cast_dy", "gemm_dgrad_o_fc2_fp8", "attention_bwd", "cast_cg_t",
-                       "gemm_wgrad_o_fc2_fp8", "cast_dz", "gemm_dgrad_qkv_fc1_fp8", "cast_a_t",
+FP8_BWD_STAGE_NAMES = ("cast_dy", "gemm_dgrad_o_fc2_fp8", "attention_bwd",
+                       "gemm_wgrad_o_fc2_fp8", "cast_dz", "gemm_dgrad_qkv_fc1_fp8",
                        "gemm_wgrad_qkv_fc1_fp8", "layernorm_bwd")
 
 
@@ -381,6 +382,13 @@ def ptb_fp8_quantize(x, rows: int, cols: int, fmt: str, amax, q, qt, stream=None
     st = load_library().ptb_fp8_quantize(_ptr(x), rows, cols, FP8_FORMATS[fmt], _ptr(amax),
                                          _ptr(q), _ptr(qt), _stream(stream))
     return _done(st, "ptb_fp8_quantize", check)
+
+
+def ptb_fp8_saved_bytes(dims: ptb_dims) -> int:
+    n = ctypes.c_size_t(0)
+    _done(load_library().ptb_fp8_saved_bytes(ctypes.byref(dims), ctypes.byref(n)),
+          "ptb_fp8_saved_bytes", True)
+    return n.value
 
 
 def ptb_fp8_workspace_bytes(dims: ptb_dims) -> int:
@@ -423,6 +431,6 @@ def exported_symbols() -> Sequence[str]:
             "ptb_serial_workspace_bytes", "ptb_serial_saved_layout", "ptb_serial_forward",
             "ptb_serial_backward", "ptb_serial_forward_timed", "ptb_serial_backward_timed",
             "ptb_lamb_workspace_bytes", "ptb_lamb_step", "ptb_fp8_weights_bytes",
-            "ptb_fp8_weights_layout", "ptb_fp8_quantize",
+            "ptb_fp8_weights_layout", "ptb_fp8_quantize", "ptb_fp8_saved_bytes",
             "ptb_fp8_workspace_bytes", "ptb_fp8_cast_weights", "ptb_fp8_forward",
             "ptb_fp8_backward")

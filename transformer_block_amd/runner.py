@@ -188,7 +188,7 @@ class Fp8Layer:
         self.p = {k: to_device_bf16(lay[k], dev) for k in PARAM_NAMES}
         self.fp8_weights = torch.empty(P.ptb_fp8_weights_bytes(self.dims), dtype=torch.uint8,
                                        device=dev)
-        self.saved = torch.empty(P.ptb_saved_bytes(self.dims), dtype=torch.uint8, device=dev)
+        self.saved = torch.empty(P.ptb_fp8_saved_bytes(self.dims), dtype=torch.uint8, device=dev)
         self.workspace = torch.empty(P.ptb_fp8_workspace_bytes(self.dims), dtype=torch.uint8,
                                      device=dev)
         self.y = torch.empty_like(self.x)
