@@ -2,8 +2,8 @@
 // section: E4M3 / E5M2 operands for the matrix products, the scale of a
 // tensor taken from the tensor itself).
 //
-//   amax:  max |x| over a logical bf16 matrix (one or two segments), one
-//          workgroup per CU with four rows' loads in flight per thread, one
+//   amax:  max |x| over a logical bf16 matrix (one or two unpadded
+//          segments), one workgroup per CU walking them as flat arrays, one
 //          vector atomic max per workgroup on the float's bits (non-negative
 //          floats order like their bit patterns).
 //   cast:  code = RNE(clamp(x * s, -FMAX, FMAX)) with s = FMAX / amax, x * s
@@ -37,25 +37,35 @@ __device__ __forceinline__ const u16* src_at(const CastSrc& x, int r, int c) {
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
-// Workgroup b takes rows AR b .. +AR-1, then AR G further, ...; a thread loads
-// one 16-byte chunk of each of the AR rows before it reduces them (AR loads
-// in flight).  The grid is small (one workgroup per CU): the workgroups' one
-// atomic each all go to the same address and are served one at a time.
-constexpr int AR = 4;
 constexpr int AMAX_THREADS = 1024;
-__global__ __launch_bounds__(AMAX_THREADS) void amax_kernel(CastSrc x, float* amax) {
+constexpr int AMAX_UNROLL = 8;  // 16-byte loads in flight per thread
+
+// max |x| over up to two contiguous arrays of n0 and n1 16-byte chunks (the
+// segments of a logical matrix without padding): a grid-stride walk in which
+// consecutive threads read consecutive chunks, eight in flight each.  The
+// grid is one workgroup per CU: the workgroups' one atomic each all go to
+// the same address and are served one at a time (a grid of 1024 workgroups
+// spent a third of an activation's amax on them).
+__global__ __launch_bounds__(AMAX_THREADS) void amax_flat_kernel(const uint4* p0, long n0,
+                                                                 const uint4* p1, long n1,
+                                                                 float* amax) {
   __shared__ uint32_t part[AMAX_THREADS / 64];
-  const int nch = x.C / 8;  // 16-byte chunks per row
   uint32_t m = 0;
-  for (int r0 = blockIdx.x * AR; r0 < x.R; r0 += gridDim.x * AR) {
-    for (int c = threadIdx.x; c < nch; c += AMAX_THREADS) {
-      uint4 v[AR];
+  const long stride = static_cast<long>(gridDim.x) * AMAX_THREADS;
 #pragma unroll
-      for (int u = 0; u < AR; ++u)
-        v[u] = r0 + u < x.R ? *reinterpret_cast<const uint4*>(src_at(x, r0 + u, c * 8))
-                            : make_uint4(0u, 0u, 0u, 0u);
+  for (int seg = 0; seg < 2; ++seg) {
+    const uint4* p = seg ? p1 : p0;
+    const long n = seg ? n1 : n0;
+    for (long i0 = static_cast<long>(blockIdx.x) * AMAX_THREADS + threadIdx.x; i0 < n;
+         i0 += AMAX_UNROLL * stride) {
+      uint4 v[AMAX_UNROLL];
 #pragma unroll
-      for (int u = 0; u < AR; ++u) {
+      for (int u = 0; u < AMAX_UNROLL; ++u) {
+        const long i = i0 + u * stride;
+        v[u] = i < n ? p[i] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < AMAX_UNROLL; ++u) {
         const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -155,8 +165,19 @@ hipError_t launch_amax(const CastSrc& x, float* amax, hipStream_t s) {
   if (!src_ok(x) || amax == nullptr) return hipErrorInvalidValue;
   int cus = device_compute_units();
   if (cus <= 0) cus = 256;
-  const int blocks = std::min((x.R + AR - 1) / AR, cus);
-  hipLaunchKernelGGL(amax_kernel, dim3(blocks), dim3(AMAX_THREADS), 0, s, x, amax);
+  // the segments must be plain arrays (leading dimension = segment width)
+  const bool one = x.split_on_rows ? x.split >= x.R : x.split >= x.C;
+  const long R0 = x.split_on_rows && !one ? x.split : x.R;
+  const long C0 = !x.split_on_rows && !one ? x.split : x.C;
+  const long R1 = one ? 0 : (x.split_on_rows ? x.R - x.split : x.R);
+  const long C1 = one ? 0 : (x.split_on_rows ? x.C : x.C - x.split);
+  if (x.ld0 != C0 || (!one && x.ld1 != C1)) return hipErrorInvalidValue;
+  const long n0 = R0 * C0 / 8, n1 = R1 * C1 / 8;
+  const int blocks =
+      static_cast<int>(std::min<long>((n0 + n1 + AMAX_THREADS - 1) / AMAX_THREADS, cus));
+  hipLaunchKernelGGL(amax_flat_kernel, dim3(blocks), dim3(AMAX_THREADS), 0, s,
+                     reinterpret_cast<const uint4*>(x.p0), n0,
+                     reinterpret_cast<const uint4*>(x.p1), n1, amax);
   return hipGetLastError();
 }
 

@@ -136,7 +136,8 @@ struct CastSrc {
   int R, C;
 };
 
-// *amax = max(*amax, max |X|) (as float bits; *amax starts at 0).
+// *amax = max(*amax, max |X|) (as float bits; *amax starts at 0).  Each
+// segment must be a plain array (its leading dimension equal to its width).
 hipError_t launch_amax(const CastSrc& x, float* amax, hipStream_t stream);
 
 // FP8 copies of X on its current scale s = FMAX / *amax: rows[r*ldr + c]
