@@ -31,7 +31,9 @@ Prints one JSON line.  Besides the throughput it carries:
   fp8:          the same layer with its four GEMM parts on FP8 operands (E4M3
                 forward, E5M2 gradients, current scaling: Megatron tuning
                 post, mixed-precision section), the weight cast included in
-                the step, model FLOPs as for `value`; --no-fp8 skips it.
+                the step, model FLOPs as for `value`, with its own roofline
+                (dominant FP8 product against the 5.0 PFLOP/s dense FP8
+                peak); --no-fp8 skips it.
                 None of these legs is part of `value`.
 
 roofline.traffic is the HBM bytes per launch of the dominant kernel as read
@@ -328,13 +330,24 @@ def time_fp8(w, inp, warmup: int, steps: int, base_ms: float) -> dict:
     F = workload_model_flops(w)
     tflops = F / (ms * 1e-3) / 1e12
     gemm_ms = sum(v for k, v in stages.items() if k.startswith("gemm_"))
+    # the leg's dominant kernel against the dense FP8 peak: the six products
+    # have the bf16 layer's model FLOPs (stage_work), named with an _fp8 suffix
+    fwd_work, bwd_work = stage_work(w)
+    work = dict(fwd_work)
+    work.update(bwd_work)
+    dom = max((k for k in stages if k.startswith("gemm_")), key=lambda k: stages[k])
+    flops = work[dom[:-len("_fp8")]][1]
+    ach = flops / (stages[dom] * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": None, "kernel": dom,
+            "per_launch": flops, "ms_per_launch": stages[dom]}
     del lyr
     return {"formats": "E4M3 fwd / E5M2 grad, per-operand current scaling",
             "ms_per_step": round(ms, 4), "value": round(tflops, 2), "unit": "TFLOP/s",
             "mfu_vs_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
             "frac_of_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4),
             "speedup_vs_bf16": round(base_ms / ms, 4),
-            "gemm_ms": round(gemm_ms, 4), "stages_ms": stages}
+            "gemm_ms": round(gemm_ms, 4), "roofline": roof, "stages_ms": stages}
 
 
 LAMB_BYTES_PER_PARAM = 40  # moments pass: g 2 + theta, m, v 12 read, m, v 8 written;

@@ -248,7 +248,7 @@ def test_fp8_calls_reject_bad_arguments_before_any_hip_call(lib):
     A = 0x10000
     d = good_dims()
     # SwiGLU has no FP8 variant
-    for fn in (P.ptb_fp8_weights_bytes, P.ptb_fp8_workspace_bytes):
+    for fn in (P.ptb_fp8_weights_bytes, P.ptb_fp8_workspace_bytes, P.ptb_fp8_saved_bytes):
         with pytest.raises(P.PtbError) as ei:
             fn(good_dims(mlp=1))
         assert ei.value.status == P.PTB_ERR_ARG
