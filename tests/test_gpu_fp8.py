@@ -82,6 +82,32 @@ def test_quantize_codes_match_the_oracle(fmt, rows, cols):
     assert not gott[:, rows:].any()
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("rows,cols", [(1, 8), (65, 8), (3, 200)])
+def test_quantize_small_and_ragged_shapes(fmt, rows, cols):
+    """One row, one 16-byte chunk per row, and a ragged row count: the codes,
+    the zero padding of both copies (to multiples of 64) and the amax."""
+    rng = np.random.default_rng(950 + rows)
+    x = (rng.standard_normal((rows, cols)) * 1.7).astype(np.float32)
+    bits = I.f32_to_bf16_bits(x)
+    xv = I.bf16_bits_to_f64(bits)
+    dev = torch.device("cuda")
+    xt = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    ldq, ldqt = (cols + 63) // 64 * 64, (rows + 63) // 64 * 64
+    q = torch.full((rows, ldq), 0x55, dtype=torch.uint8, device=dev)
+    qt = torch.full((cols, ldqt), 0x55, dtype=torch.uint8, device=dev)
+    amax = torch.full((4,), -1.0, dtype=torch.float32, device=dev)
+    P.ptb_fp8_quantize(xt, rows, cols, fmt, amax, q, qt)
+    torch.cuda.synchronize()
+    assert amax[0].item() == np.abs(xv).max()
+    codes, _ = F8.quantize(xv, F8.current_scale(xv, fmt), fmt)
+    got, gott = q.cpu().numpy(), qt.cpu().numpy()
+    np.testing.assert_array_equal(got[:, :cols], codes)
+    assert not got[:, cols:].any()
+    np.testing.assert_array_equal(gott[:, :rows], codes.T)
+    assert not gott[:, rows:].any()
+
+
 def test_cast_weights_match_the_oracle():
     w = W("f8w", 1, 128, 192, 3, 64, 768, 32, seed=901)
     inp = I.make_inputs(w, random_ln=True)
@@ -118,6 +144,7 @@ CASES = [
     ("d128_b3_s97_w33", W("f8d", 3, 97, 256, 2, 128, 512, 33, seed=911), True),
     ("rmsnorm", W("f8rms", 2, 160, 256, 2, 128, 256, 40, seed=912, norm="rmsnorm"), True),
     ("single_token", W("f8s1", 1, 1, 128, 1, 128, 128, 1, seed=913), True),
+    ("window1_d64_s77", W("f8w1", 2, 77, 192, 3, 64, 384, 1, seed=914), True),
     ("h2048_s2048_w512", I.WORKLOADS["h2048_s2048_w512"], False),
     ("gpt175b_tp8_share_s2048", I.WORKLOADS["gpt175b_tp8_share_s2048"], False),
 ]
