@@ -20,7 +20,9 @@ Readings where the pages leave a step open (each is also the library's):
     point): E4M3 with exponent bias 7, no infinities, S.1111.111 the only NaN,
     largest finite 448; E5M2 with bias 15 and IEEE-style infinities and NaNs,
     largest finite 57344.  Both have subnormals.
-  * Recipe: current scaling, one scale per GEMM operand.  An operand that is a
+  * Recipes: current scaling (below) and block scaling (mxfp8, further
+    below); a layer call uses one of them for all six products.
+  * Current scaling: one scale per GEMM operand.  An operand that is a
     concatenation of tensors ([W_qkv | W_fc1], [c | g], [W_o ; W_fc2],
     [dqkv | du]) is one tensor for scaling.  s = fp32(FMAX / amax) with amax
     the largest magnitude of the bf16 operand (s = 1 when amax = 0).
@@ -30,6 +32,19 @@ Readings where the pages leave a step open (each is also the library's):
   * Which operands: forward a, [W_qkv | W_fc1], [c | g], [W_o ; W_fc2] in
     E4M3; backward dy and [dqkv | du] in E5M2 against E4M3 weights and E4M3
     saved activations (the weight gradients take E4M3 a^T, [c | g]^T).
+  * Block scaling: the pages name mxfp8 and nothing more; its published
+    definition (OCP Microscaling Formats v1.0) is taken as is.  Blocks of 32
+    consecutive values along the product's contraction axis (a short last
+    block where the axis is not a multiple of 32), one E8M0 scale per block
+    (a power of two, code e meaning 2^(e - 127), e in 0..254),
+    X = floor(log2 amax_block) - emax with emax the exponent of the format's
+    largest power of two (8 for E4M3, 15 for E5M2), an all-zero block taking
+    X = 0; element codes = RNE(clamp(fp32(x * 2^-X), -FMAX, FMAX)) (the
+    multiply is exact).  Dequantized product: sum over k of
+    qa 2^Xa qb 2^Xb, the block scales of the two operands at the same k.
+    Each product quantizes its operands along its own contraction axis, so
+    a tensor that feeds two products (dy, dZ, the weights) is quantized
+    twice, once per orientation.
   * BF16 points: the tensors the pages keep in BF16 and that feed a product
     (a, c, g, dqkv, du) are rounded to bf16 (round to nearest even) before
     they are quantized; dy and the weights are bf16 already.  Everything else
@@ -139,19 +154,76 @@ def fp8_matmul(a: np.ndarray, b: np.ndarray, fmt_a: str, fmt_b: str,
 
 
 # ---------------------------------------------------------------------------
+# Block (MX) scaling
+# ---------------------------------------------------------------------------
+MX_BLOCK = 32
+
+
+def emax(fmt: str) -> int:
+    """Exponent of the format's largest power of two: 8 (E4M3), 15 (E5M2)."""
+    return math.frexp(fmax(fmt))[1] - 1
+
+
+def mx_scale_code(amax: np.ndarray, fmt: str) -> np.ndarray:
+    """E8M0 code of each block: 127 + floor(log2 amax) - emax, within
+    0..254; 127 (scale 1) for an all-zero block."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, e = np.frexp(amax)               # amax = m 2^e, 0.5 <= m < 1
+    x = np.where(amax > 0, e - 1 - emax(fmt), 0)
+    return np.clip(x + 127, 0, 254).astype(np.int64)
+
+
+def mx_quantize(x: np.ndarray, fmt: str, axis: int):
+    """(codes uint8, scale codes int64, values float64) of a 2-D x with blocks
+    of 32 along `axis`.  Scale codes have the blocks' shape: [R, ceil(C/32)]
+    for axis 1, [ceil(R/32), C] for axis 0."""
+    x = np.asarray(x, dtype=np.float64)
+    xt = x if axis == 1 else x.T
+    rows, n = xt.shape
+    nb = -(-n // MX_BLOCK)
+    padded = np.zeros((rows, nb * MX_BLOCK))
+    padded[:, :n] = xt
+    blocks = padded.reshape(rows, nb, MX_BLOCK)
+    sc = mx_scale_code(np.abs(blocks).max(axis=2), fmt)
+    mult = np.ldexp(np.float32(1.0), 127 - sc).astype(np.float32)   # 2^-X, exact
+    codes, vals = quantize(blocks, mult[:, :, None], fmt)
+    vals = vals * np.ldexp(1.0, sc - 127)[:, :, None]
+    codes = codes.reshape(rows, -1)[:, :n]
+    vals = vals.reshape(rows, -1)[:, :n]
+    if axis == 0:
+        return codes.T, sc.T, vals.T
+    return codes, sc, vals
+
+
+def mx_matmul(a: np.ndarray, b: np.ndarray, fmt_a: str, fmt_b: str,
+              record: list | None = None) -> np.ndarray:
+    """C = A B with both operands block-scaled along the contraction axis."""
+    _, _, qa = mx_quantize(a, fmt_a, axis=1)
+    _, _, qb = mx_quantize(b, fmt_b, axis=0)
+    if record is not None:
+        record.append((fmt_a, fmt_b))
+    return qa @ qb
+
+
+_RECIPES = {"current": fp8_matmul, "mx": mx_matmul}
+
+
+# ---------------------------------------------------------------------------
 # The layer ([MS] 1.1 eq (4)) with its four GEMM parts in FP8 ([MT]).
 # ---------------------------------------------------------------------------
 def fp8_ptb_forward(x: np.ndarray, p: Dict[str, np.ndarray], batch: int, seq: int,
                     heads: int, head_dim: int, window: int, eps: float,
-                    norm: str = "layernorm"):
+                    norm: str = "layernorm", recipe: str = "current"):
     """y = x + Attn(LN(x)) + MLP(LN(x)) with [QKV | FC1] and [O ; FC2] as FP8
-    products.  p as in ptb_oracle.ptb_forward (GeLU MLP)."""
+    products, scaled by `recipe` ("current" or "mx").  p as in
+    ptb_oracle.ptb_forward (GeLU MLP)."""
     hl = heads * head_dim
     rec: list = []
+    fp8_mm = _RECIPES[recipe]
     a_full, mu, rstd = norm_forward(norm, x, p["ln_gamma"], p["ln_beta"], eps)
     a = round_bf16(a_full)
     w1 = np.concatenate([p["w_qkv"], p["w_fc1"]], axis=1)
-    z = fp8_matmul(a, w1, E4M3, E4M3, rec)
+    z = fp8_mm(a, w1, E4M3, E4M3, rec)
     qkv, u = z[:, :3 * hl], z[:, 3 * hl:]
     g = gelu(u)
     q = split_heads(qkv[:, :hl], batch, seq, heads, head_dim)
@@ -160,9 +232,9 @@ def fp8_ptb_forward(x: np.ndarray, p: Dict[str, np.ndarray], batch: int, seq: in
     c = merge_heads(attention_forward(q, k, v, window))
     cg = round_bf16(np.concatenate([c, g], axis=1))
     w2 = np.concatenate([p["w_o"], p["w_fc2"]], axis=0)
-    y = x + fp8_matmul(cg, w2, E4M3, E4M3, rec)
+    y = x + fp8_mm(cg, w2, E4M3, E4M3, rec)
     cache = dict(x=x, a=a, mu=mu, rstd=rstd, q=q, k=k, v=v, c=c, u=u, g=g, qkv=qkv, cg=cg,
-                 norm=norm, formats=rec)
+                 norm=norm, formats=rec, recipe=recipe)
     return y, cache
 
 
@@ -171,6 +243,7 @@ def fp8_ptb_backward(dy: np.ndarray, cache: dict, p: Dict[str, np.ndarray],
     """Gradients of fp8_ptb_forward: the same four GEMM parts in FP8 (gradient
     operands E5M2), quantization passed straight through."""
     rec = cache["formats"]
+    fp8_matmul = _RECIPES[cache["recipe"]]
     x, a, u, cg = cache["x"], cache["a"], cache["u"], cache["cg"]
     q, k, v = cache["q"], cache["k"], cache["v"]
     hl = cache["c"].shape[1]
