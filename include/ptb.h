@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define PTB_ABI_VERSION 6
+#define PTB_ABI_VERSION 7
 
 enum ptb_status {
   PTB_OK = 0,
@@ -365,14 +365,22 @@ int32_t ptb_lamb_step(const ptb_lamb_hyper* hyper, const ptb_lamb_tensor* tensor
  *             tensor: s = FMAX / amax (fp32 division; s = 1 for an all-zero
  *             tensor), code = round-to-nearest-even(clamp(x s, -FMAX, FMAX))
  *             with x s one fp32 multiply, and the product's fp32 sums are
- *             multiplied by (1/sA)(1/sB) before the epilogue.
+ *             multiplied by (1/sA)(1/sB) before the epilogue
+ *             (PTB_FP8_CURRENT); or block scaling, mxfp8 as the OCP
+ *             Microscaling Formats v1.0 define it (PTB_FP8_MX): blocks of 32
+ *             values along each product's contraction dimension, one E8M0
+ *             scale 2^X per block with X = floor(log2 amax_block) - emax
+ *             (emax 8 for E4M3, 15 for E5M2; X = 0 for an all-zero block),
+ *             code = RNE(clamp(x 2^-X, -FMAX, FMAX)); the matrix cores apply
+ *             the block scales.  A tensor that feeds two products is
+ *             quantized once per orientation.
  * dims as for ptb_forward; norm LayerNorm or RMSNorm, mlp GeLU only
  * (PTB_ERR_ARG for SwiGLU).  Any b, s, h, f allowed by ptb_validate_dims:
  * the FP8 copies pad their contiguous dimension with zero codes to a
  * multiple of 128.  Inputs, outputs and ownership are as for the bf16 calls.
  * `saved` (ptb_fp8_saved_bytes) holds the parallel block's slots at the
  * offsets ptb_saved_layout gives (A_LO is not written), followed by the
- * transposed E4M3 copies of a and [c | g] and their amax, which the forward
+ * transposed E4M3 copies of a and [c | g] and their amax or block scales, which the forward
  * casts for the weight gradients;
  * the calls are asynchronous on `stream` and return PTB_ERR_HIP if a launch
  * fails.  stage_events: NULL, or 2 hipEvent_t per stage (start, end; NULL
@@ -381,12 +389,16 @@ int32_t ptb_lamb_step(const ptb_lamb_hyper* hyper, const ptb_lamb_tensor* tensor
 #define PTB_FP8_FWD_STAGES 6
 #define PTB_FP8_BWD_STAGES 8
 
+/* Every FP8 call takes the scaling recipe; PTB_ERR_ARG for another value.
+ * Buffers sized, cast or saved under one recipe are read under the same. */
+enum ptb_fp8_recipe { PTB_FP8_CURRENT = 0, PTB_FP8_MX = 1 };
+
 /* Bytes of the FP8 weight buffer (amax of W1 = [W_qkv | W_fc1] and
- * W2 = [W_o ; W_fc2], then W1^T, W1, W2^T and W2 in E4M3), of the FP8
- * layer's stash and of its workspace. */
-int32_t ptb_fp8_weights_bytes(const ptb_dims* dims, size_t* bytes);
-int32_t ptb_fp8_saved_bytes(const ptb_dims* dims, size_t* bytes);
-int32_t ptb_fp8_workspace_bytes(const ptb_dims* dims, size_t* bytes);
+ * W2 = [W_o ; W_fc2] or the block scales of each copy, and W1^T, W1, W2^T
+ * and W2 in E4M3), of the FP8 layer's stash and of its workspace. */
+int32_t ptb_fp8_weights_bytes(const ptb_dims* dims, int32_t recipe, size_t* bytes);
+int32_t ptb_fp8_saved_bytes(const ptb_dims* dims, int32_t recipe, size_t* bytes);
+int32_t ptb_fp8_workspace_bytes(const ptb_dims* dims, int32_t recipe, size_t* bytes);
 
 /* Byte offsets of the parts of the FP8 weight buffer (`offsets` has room
  * for PTB_FP8_WEIGHT_PARTS entries):
@@ -395,12 +407,20 @@ int32_t ptb_fp8_workspace_bytes(const ptb_dims* dims, size_t* bytes);
  *   W1     E4M3 [h][pad128(N1)]   W1
  *   W2T    E4M3 [h][pad128(K2)]   W2^T, K2 = n d + f
  *   W2     E4M3 [K2][pad128(h)]   W2
- * pad128(v) rounds up to a multiple of 128; padding codes are zero. */
+ *   W1T_S, W1_S, W2T_S, W2_S  PTB_FP8_MX only: the block scales of each
+ *          copy, uint32 words [pad128(k)/128][pad64(rows)] for a copy of
+ *          `rows` rows and contraction extent k: word [j][r] holds in byte b
+ *          the E8M0 scale of row r's k-block 4 j + b (32 values)
+ * pad128(v) / pad64(v) round up to a multiple of 128 / 64; padding codes
+ * are zero, padding blocks and rows have scale code 127.  Parts a recipe
+ * does not use (AMAX under PTB_FP8_MX, the scales under PTB_FP8_CURRENT)
+ * get offset SIZE_MAX. */
 enum ptb_fp8_weight_part {
   PTB_FP8_AMAX = 0, PTB_FP8_W1T, PTB_FP8_W1, PTB_FP8_W2T, PTB_FP8_W2,
+  PTB_FP8_W1T_S, PTB_FP8_W1_S, PTB_FP8_W2T_S, PTB_FP8_W2_S,
   PTB_FP8_WEIGHT_PARTS
 };
-int32_t ptb_fp8_weights_layout(const ptb_dims* dims, size_t* offsets);
+int32_t ptb_fp8_weights_layout(const ptb_dims* dims, int32_t recipe, size_t* offsets);
 
 /* The current-scaling cast on its own, for any bf16 matrix x [rows][cols]
  * (device, row-major, cols a multiple of 8, rows * cols < 2^30):
@@ -413,20 +433,31 @@ enum ptb_fp8_format { PTB_FP8_E4M3 = 0, PTB_FP8_E5M2 = 1 };
 int32_t ptb_fp8_quantize(const void* x, int32_t rows, int32_t cols, int32_t format, float* amax,
                          void* q, void* qt, void* stream);
 
+/* The block-scaled (PTB_FP8_MX) cast on its own, for the same x: codes
+ * row-wise to q [rows][pad128(cols)] with scale words q_scales
+ * [pad128(cols)/128][pad64(rows)] (blocks along each row), and/or
+ * transposed to qt [cols][pad128(rows)] with qt_scales
+ * [pad128(rows)/128][pad64(cols)] (blocks along each column of x); word
+ * layout as for the weight buffer's scale parts.  A copy is written when
+ * both its pointers are non-NULL.  The same kernel as the layer's casts. */
+int32_t ptb_fp8_quantize_mx(const void* x, int32_t rows, int32_t cols, int32_t format, void* q,
+                            void* q_scales, void* qt, void* qt_scales, void* stream);
+
 /* Casts the four bf16 weights (as for ptb_forward) into `fp8_weights`
  * (device, caller-owned, ptb_fp8_weights_bytes), both orientations of each
  * concatenated weight on one current scale.  Call it after every change of
  * the weights (once per optimizer step); forward and backward read it. */
-int32_t ptb_fp8_cast_weights(const ptb_dims* dims, const void* w_qkv, const void* w_o,
-                             const void* w_fc1, const void* w_fc2, void* fp8_weights,
-                             void* stream);
+int32_t ptb_fp8_cast_weights(const ptb_dims* dims, int32_t recipe, const void* w_qkv,
+                             const void* w_o, const void* w_fc1, const void* w_fc2,
+                             void* fp8_weights, void* stream);
 
 /* Forward: y [T, h] and `saved`.  Stages: 0 LayerNorm, 1 cast a (row-wise
  * and transposed), 2 [QKV | FC1] FP8 product + GeLU, 3 attention, 4 cast
  * [c | g] (both ways), 5 [O ; FC2] FP8 product + residual. */
-int32_t ptb_fp8_forward(const ptb_dims* dims, const void* x, const void* ln_gamma,
-                        const void* ln_beta, const void* fp8_weights, void* y, void* saved,
-                        void* workspace, void* stream, void* const* stage_events);
+int32_t ptb_fp8_forward(const ptb_dims* dims, int32_t recipe, const void* x,
+                        const void* ln_gamma, const void* ln_beta, const void* fp8_weights,
+                        void* y, void* saved, void* workspace, void* stream,
+                        void* const* stage_events);
 
 /* Backward for upstream gradient dy [T, h] from the `saved` of the matching
  * ptb_fp8_forward (same x, same fp8_weights); writes what ptb_backward
@@ -436,11 +467,11 @@ int32_t ptb_fp8_forward(const ptb_dims* dims, const void* x, const void* ln_gamm
  * [O ; FC2] + GeLU', 2 attention backward, 3 wgrad [O ; FC2], 4 cast dZ (both
  * ways), 5 dgrad [QKV | FC1], 6 wgrad [QKV | FC1], 7 LayerNorm backward
  * (+ dy). */
-int32_t ptb_fp8_backward(const ptb_dims* dims, const void* dy, const void* x,
-                         const void* ln_gamma, const void* fp8_weights, const void* saved,
-                         void* dx, void* d_ln_gamma, void* d_ln_beta, void* dw_qkv, void* dw_o,
-                         void* dw_fc1, void* dw_fc2, void* workspace, void* stream,
-                         void* const* stage_events);
+int32_t ptb_fp8_backward(const ptb_dims* dims, int32_t recipe, const void* dy,
+                         const void* x, const void* ln_gamma, const void* fp8_weights,
+                         const void* saved, void* dx, void* d_ln_gamma, void* d_ln_beta,
+                         void* dw_qkv, void* dw_o, void* dw_fc1, void* dw_fc2, void* workspace,
+                         void* stream, void* const* stage_events);
 
 #ifdef __cplusplus
 }  /* extern "C" */

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert P.ptb_abi_version() == 6
+    assert P.ptb_abi_version() == 7
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert P.ptb_status_string(code) and P.ptb_status_string(code) != "unknown status"
     assert P.ptb_status_string(12345) == "unknown status"
@@ -227,10 +227,13 @@ def test_fp8_weight_layout_and_sizes(lib):
     pad = lambda v: (v + 127) // 128 * 128
     lay = P.ptb_fp8_weights_layout(d)
     sizes = dict(amax=8, w1t=N1 * pad(h), w1=h * pad(N1), w2t=h * pad(K2), w2=K2 * pad(h))
-    offs = [lay[k] for k in P.FP8_WEIGHT_PARTS]
+    parts = ("amax", "w1t", "w1", "w2t", "w2")
+    offs = [lay[k] for k in parts]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
-    for a_, b_ in zip(P.FP8_WEIGHT_PARTS, P.FP8_WEIGHT_PARTS[1:]):
+    for a_, b_ in zip(parts, parts[1:]):
         assert lay[b_] - lay[a_] >= sizes[a_]
+    # current scaling has no block scales
+    assert all(lay[k] == P.FP8_ABSENT for k in ("w1t_s", "w1_s", "w2t_s", "w2_s"))
     assert P.ptb_fp8_weights_bytes(d) >= lay["w2"] + sizes["w2"]
     # a ragged hidden size pads the contiguous dimension to 128
     r = good_dims(hidden=192, heads=3, ffn=768)
@@ -243,6 +246,32 @@ def test_fp8_weight_layout_and_sizes(lib):
         pad(h) * 2 + pad(K2) + pad(N1)) + pad(T) * (h + N1)
     assert P.ptb_fp8_saved_bytes(d) >= P.ptb_saved_bytes(d) + 8 + pad(T) * (h + K2)
 
+
+def test_fp8_mx_weight_layout_and_sizes(lib):
+    """Block scaling: no amax; each copy followed by its scale words
+    [pad128(k)/128][pad64(rows)] (4 bytes each); the workspace and the stash
+    grow by the scale words of their copies."""
+    d = good_dims()
+    h, hl, f, T = 256, 256, 1024, 512
+    N1, K2 = 3 * hl + f, hl + f
+    pad = lambda v: (v + 127) // 128 * 128
+    p64 = lambda v: (v + 63) // 64 * 64
+    words = lambda rows, k: pad(k) // 128 * p64(rows) * 4
+    lay = P.ptb_fp8_weights_layout(d, "mx")
+    assert lay["amax"] == P.FP8_ABSENT
+    order = ("w1t", "w1t_s", "w1", "w1_s", "w2t", "w2t_s", "w2", "w2_s")
+    sizes = dict(w1t=N1 * pad(h), w1t_s=words(N1, h), w1=h * pad(N1), w1_s=words(h, N1),
+                 w2t=h * pad(K2), w2t_s=words(h, K2), w2=K2 * pad(h), w2_s=words(K2, h))
+    offs = [lay[k] for k in order]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    for a_, b_ in zip(order, order[1:]):
+        assert lay[b_] - lay[a_] >= sizes[a_]
+    assert P.ptb_fp8_weights_bytes(d, "mx") >= lay["w2_s"] + sizes["w2_s"]
+    extra_ws = (words(T, h) * 2 + words(T, K2) + words(T, N1) + words(h, T) + words(N1, T))
+    assert (P.ptb_fp8_workspace_bytes(d, "mx") >=
+            P.ptb_fp8_workspace_bytes(d) + extra_ws - 256)
+    assert (P.ptb_fp8_saved_bytes(d, "mx") >=
+            P.ptb_fp8_saved_bytes(d) + words(h, T) + words(K2, T))
 
 def test_fp8_calls_reject_bad_arguments_before_any_hip_call(lib):
     A = 0x10000
@@ -272,6 +301,18 @@ def test_fp8_calls_reject_bad_arguments_before_any_hip_call(lib):
     assert P.ptb_fp8_quantize(A + 4, 64, 64, "e5m2", A, A, 0, stream=0,
                               check=False) == P.PTB_ERR_ALIGN
     assert load_fmt_error(lib) == P.PTB_ERR_ARG
+    # an unknown recipe
+    n = ctypes.c_size_t(0)
+    assert lib.ptb_fp8_weights_bytes(ctypes.byref(d), 2, ctypes.byref(n)) == P.PTB_ERR_ARG
+    assert lib.ptb_fp8_forward(ctypes.byref(d), -1, *([A] * 7), None, None) == P.PTB_ERR_ARG
+    # the block-scaled stand-alone cast: a copy needs both its pointers
+    assert P.ptb_fp8_quantize_mx(A, 64, 64, "e4m3", A, 0, 0, A, stream=0,
+                                 check=False) == P.PTB_ERR_NULL
+    assert P.ptb_fp8_quantize_mx(A, 64, 60, "e4m3", A, A, 0, 0, stream=0,
+                                 check=False) == P.PTB_ERR_DIMS
+    assert P.ptb_fp8_quantize_mx(A, 64, 64, "e4m3", A, A + 4, 0, 0, stream=0,
+                                 check=False) == P.PTB_ERR_ALIGN
+    assert lib.ptb_fp8_quantize_mx(A, 64, 64, 3, A, A, None, None, None) == P.PTB_ERR_ARG
 
 
 def load_fmt_error(lib):

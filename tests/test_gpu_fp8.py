@@ -5,7 +5,11 @@ FP8 oracle (oracle/fp8_oracle.py) on the same seeded bf16 inputs.
   compared code by code: both sides decide each code in fp32 (x * s one fp32
   multiply, s = FMAX / amax one fp32 division), so the codes must be
   identical, padding included.
-* The layer is compared by relative Frobenius error per output tensor against
+* The block-scaled cast (ptb_fp8_quantize_mx, and the weight cast under
+  PTB_FP8_MX) is compared the same way, codes and scale words: the scale of
+  a block comes from its bf16 maximum's exponent and x 2^-X is exact.
+* The layer, under either recipe, is compared by relative Frobenius error
+  per output tensor against
   FP8_TOL.  Where the two sides feed a cast slightly different bf16 values (an
   upstream difference of relative size delta, at most the bf16 path's bar
   1e-2), a value near an FP8 rounding boundary lands on the neighbouring code:
@@ -108,6 +112,102 @@ def test_quantize_small_and_ragged_shapes(fmt, rows, cols):
     assert not gott[:, rows:].any()
 
 
+def _mx_words(sc, kp, rows_p):
+    """Scale words [kp/128][rows_p] from block codes sc [rows, nblocks]
+    (blocks along k): byte b of word [j][r] = sc[r, 4 j + b], 127 where the
+    block or the row is padding."""
+    rows, nb = sc.shape
+    full = np.full((rows_p, kp // 32), 127, dtype=np.uint32)
+    full[:rows, :nb] = sc
+    full = full.reshape(rows_p, kp // 128, 4)
+    words = full[:, :, 0] | full[:, :, 1] << 8 | full[:, :, 2] << 16 | full[:, :, 3] << 24
+    return words.T.copy()
+
+
+def _check_mx_copies(q, qs, qt, qts, x, fmt):
+    """Row-wise and transposed block-scaled copies (device tensors) of x
+    against the oracle, padding included."""
+    rows, cols = x.shape
+    p128 = lambda v: (v + 127) // 128 * 128
+    p64 = lambda v: (v + 63) // 64 * 64
+    codes, sc, _ = F8.mx_quantize(x, fmt, axis=1)
+    got = q.cpu().numpy()
+    np.testing.assert_array_equal(got[:, :cols], codes)
+    assert not got[:, cols:].any()
+    np.testing.assert_array_equal(qs.cpu().numpy().view(np.uint32),
+                                  _mx_words(sc, p128(cols), p64(rows)))
+    codes0, sc0, _ = F8.mx_quantize(x, fmt, axis=0)
+    gott = qt.cpu().numpy()
+    np.testing.assert_array_equal(gott[:, :rows], codes0.T)
+    assert not gott[:, rows:].any()
+    np.testing.assert_array_equal(qts.cpu().numpy().view(np.uint32),
+                                  _mx_words(sc0.T, p128(rows), p64(cols)))
+
+
+def _mx_buffers(rows, cols, dev):
+    p128 = lambda v: (v + 127) // 128 * 128
+    p64 = lambda v: (v + 63) // 64 * 64
+    fill = lambda shape, dt: torch.full(shape, 0x55, dtype=dt, device=dev)
+    return (fill((rows, p128(cols)), torch.uint8), fill((p128(cols) // 128, p64(rows)), torch.int32),
+            fill((cols, p128(rows)), torch.uint8), fill((p128(rows) // 128, p64(cols)), torch.int32))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("rows,cols", [(130, 264), (64, 512), (1, 8), (65, 8), (3, 200)])
+def test_quantize_mx_codes_and_scales_match_the_oracle(fmt, rows, cols):
+    """Every significand of 35 binades in random places (so the blocks' scales
+    spread over many binades), rows scaled by 2^-20 .. 2^20, a zero block, and
+    ragged shapes: codes, scale words and padding of both copies."""
+    log(f"fp8 mx quantize {fmt} {rows}x{cols}")
+    dev = torch.device("cuda")
+    if rows * cols >= 8960:
+        bits, x = _probe_matrix(rows, cols, 960 + rows)
+    else:
+        rng = np.random.default_rng(960 + rows)
+        x32 = (rng.standard_normal((rows, cols)) * 1.7).astype(np.float32)
+        bits = I.f32_to_bf16_bits(x32)
+        x = I.bf16_bits_to_f64(bits)
+    rng = np.random.default_rng(970 + cols)
+    scale = np.exp2(rng.integers(-20, 21, (rows, 1))).astype(np.float32)
+    bits = I.f32_to_bf16_bits((x * scale).astype(np.float32))
+    if cols >= 64:
+        bits[0, 32:64] = 0
+    x = I.bf16_bits_to_f64(bits)
+    xt = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, qs, qt, qts = _mx_buffers(rows, cols, dev)
+    P.ptb_fp8_quantize_mx(xt, rows, cols, fmt, q, qs, qt, qts)
+    torch.cuda.synchronize()
+    _check_mx_copies(q, qs, qt, qts, x, fmt)
+
+
+def test_cast_weights_mx_match_the_oracle():
+    w = W("f8wmx", 1, 128, 192, 3, 64, 768, 32, seed=902)
+    inp = I.make_inputs(w, random_ln=True)
+    dev = torch.device("cuda")
+    lay = inp["layers"][0]
+    t = {k: torch.from_numpy(lay[k].view(np.int16)).to(dev).view(torch.bfloat16)
+         for k in ("w_qkv", "w_o", "w_fc1", "w_fc2")}
+    dims = P.dims_of(w)
+    buf = torch.full((P.ptb_fp8_weights_bytes(dims, "mx"),), 0x55, dtype=torch.uint8, device=dev)
+    P.ptb_fp8_cast_weights(dims, t["w_qkv"], t["w_o"], t["w_fc1"], t["w_fc2"], buf, recipe="mx")
+    torch.cuda.synchronize()
+    off = P.ptb_fp8_weights_layout(dims, "mx")
+    f = I.bf16_bits_to_f64
+    w1 = np.concatenate([f(lay["w_qkv"]), f(lay["w_fc1"])], axis=1)
+    w2 = np.concatenate([f(lay["w_o"]), f(lay["w_fc2"])], axis=0)
+    p128 = lambda v: (v + 127) // 128 * 128
+    p64 = lambda v: (v + 63) // 64 * 64
+    for name, mat, tname in (("w1", w1, "w1t"), ("w2", w2, "w2t")):
+        R, C = mat.shape
+        view = lambda o, shape, dt: buf[o:o + int(np.prod(shape)) * (4 if dt == torch.int32 else 1)
+                                        ].view(dt).view(shape)
+        q = view(off[name], (R, p128(C)), torch.uint8)
+        qs = view(off[name + "_s"], (p128(C) // 128, p64(R)), torch.int32)
+        qt = view(off[tname], (C, p128(R)), torch.uint8)
+        qts = view(off[tname + "_s"], (p128(R) // 128, p64(C)), torch.int32)
+        _check_mx_copies(q, qs, qt, qts, mat, F8.E4M3)
+
+
 def test_cast_weights_match_the_oracle():
     w = W("f8w", 1, 128, 192, 3, 64, 768, 32, seed=901)
     inp = I.make_inputs(w, random_ln=True)
@@ -151,11 +251,12 @@ CASES = [
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("recipe", ["current", "mx"])
 @pytest.mark.parametrize("name,w,random_ln", CASES, ids=[c[0] for c in CASES])
-def test_fp8_layer_parity(name, w, random_ln):
-    log(f"fp8 case {name}: {w}")
+def test_fp8_layer_parity(name, w, random_ln, recipe):
+    log(f"fp8 case {name} ({recipe}): {w}")
     inp = I.make_inputs(w, random_ln=random_ln)
-    lyr = Fp8Layer(w, inp, "cuda")
+    lyr = Fp8Layer(w, inp, "cuda", recipe)
     lyr.step()
     torch.cuda.synchronize()
     log(f"[fp8 {name}] gpu step done; running the oracle")
@@ -163,7 +264,7 @@ def test_fp8_layer_parity(name, w, random_ln):
     x, dy = f(inp["x"]), f(inp["dy"])
     p = {k: f(v) for k, v in inp["layers"][0].items()}
     y, cache = F8.fp8_ptb_forward(x, p, w.batch, w.seq, w.heads, w.head_dim, w.window,
-                                  w.ln_eps, norm=w.norm)
+                                  w.ln_eps, norm=w.norm, recipe=recipe)
     log(f"[fp8 {name}] oracle forward done")
     g = F8.fp8_ptb_backward(dy, cache, p, w.window)
     errs = {}
@@ -184,9 +285,10 @@ def test_fp8_layer_parity(name, w, random_ln):
     assert not bad, f"parity failures (tol {FP8_TOL:.3f}): {bad}"
 
 
-def test_fp8_repeat_runs_are_bitwise_identical():
+@pytest.mark.parametrize("recipe", ["current", "mx"])
+def test_fp8_repeat_runs_are_bitwise_identical(recipe):
     w = W("f8det", 2, 200, 256, 2, 128, 512, 80, seed=920)
-    lyr = Fp8Layer(w, I.make_inputs(w, random_ln=True), "cuda")
+    lyr = Fp8Layer(w, I.make_inputs(w, random_ln=True), "cuda", recipe)
     lyr.step()
     torch.cuda.synchronize()
     first = [lyr.y.clone(), lyr.dx.clone()] + [t.clone() for t in lyr.grads.values()]
@@ -197,16 +299,18 @@ def test_fp8_repeat_runs_are_bitwise_identical():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_fp8_zero_output_weights_give_the_identity():
-    """W_o = W_fc2 = 0: the operand [W_o ; W_fc2] has amax 0, so its scale is
-    1 and its codes are all zero; the layer is then exactly y = x and
-    dx = dy (da = 0), while dW_o and dW_fc2 still match the oracle."""
+@pytest.mark.parametrize("recipe", ["current", "mx"])
+def test_fp8_zero_output_weights_give_the_identity(recipe):
+    """W_o = W_fc2 = 0: the operand [W_o ; W_fc2] has amax 0 (every block
+    too), so its scale is 1 and its codes are all zero; the layer is then
+    exactly y = x and dx = dy (da = 0), while dW_o and dW_fc2 still match the
+    oracle."""
     w = W("f8zero", 2, 96, 256, 2, 128, 512, 40, seed=930)
     inp = I.make_inputs(w, random_ln=True)
     lay = inp["layers"][0]
     lay["w_o"] = np.zeros_like(lay["w_o"])
     lay["w_fc2"] = np.zeros_like(lay["w_fc2"])
-    lyr = Fp8Layer(w, inp, "cuda")
+    lyr = Fp8Layer(w, inp, "cuda", recipe)
     lyr.step()
     torch.cuda.synchronize()
     assert torch.equal(lyr.y.view(torch.int16), lyr.x.view(torch.int16))
@@ -217,7 +321,7 @@ def test_fp8_zero_output_weights_give_the_identity():
     x, dy = f(inp["x"]), f(inp["dy"])
     p = {k: f(v) for k, v in lay.items()}
     y, cache = F8.fp8_ptb_forward(x, p, w.batch, w.seq, w.heads, w.head_dim, w.window,
-                                  w.ln_eps)
+                                  w.ln_eps, recipe=recipe)
     g = F8.fp8_ptb_backward(dy, cache, p, w.window)
     assert np.array_equal(y, x) and np.array_equal(g["dx"], dy)
     for k in ("dw_o", "dw_fc2"):

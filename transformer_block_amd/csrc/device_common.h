@@ -62,6 +62,36 @@ __device__ __forceinline__ f32x16 mfma32x32x64_f8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
 }
 
+// The same with block scales: E8M0 codes (2^(e - 127)) in byte OS of sa and
+// sb.  Lane l holds row l%32 at k [16 (l/32), +16) in bytes 0-15 and at
+// k [32 + 16 (l/32), +16) in bytes 16-31, so the 32-wide block b of row i
+// (k [32 b, 32 b + 32)) is bytes 16 b .. 16 b + 15 of lanes i and i + 32; its
+// scale comes from lane i + 32 b.  The same for B's columns.
+template <int FA, int FB, int OSA, int OSB>
+__device__ __forceinline__ f32x16 mfma32x32x64_f8_mx(i32x8 a, i32x8 b, f32x16 c, uint32_t sa,
+                                                     uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, OSA,
+                                                         static_cast<int>(sa), OSB,
+                                                         static_cast<int>(sb));
+}
+
+// The scaled MFMA with A's scale in byte i of sa and B's in byte j of sb
+// (i < 4, j < 2 known at compile time after unrolling).
+template <int FA, int FB>
+__device__ __forceinline__ f32x16 mx_step(int i, int j, i32x8 a, i32x8 b, f32x16 c, uint32_t sa,
+                                          uint32_t sb) {
+  if (j == 0) {
+    if (i == 0) return mfma32x32x64_f8_mx<FA, FB, 0, 0>(a, b, c, sa, sb);
+    if (i == 1) return mfma32x32x64_f8_mx<FA, FB, 1, 0>(a, b, c, sa, sb);
+    if (i == 2) return mfma32x32x64_f8_mx<FA, FB, 2, 0>(a, b, c, sa, sb);
+    return mfma32x32x64_f8_mx<FA, FB, 3, 0>(a, b, c, sa, sb);
+  }
+  if (i == 0) return mfma32x32x64_f8_mx<FA, FB, 0, 1>(a, b, c, sa, sb);
+  if (i == 1) return mfma32x32x64_f8_mx<FA, FB, 1, 1>(a, b, c, sa, sb);
+  if (i == 2) return mfma32x32x64_f8_mx<FA, FB, 2, 1>(a, b, c, sa, sb);
+  return mfma32x32x64_f8_mx<FA, FB, 3, 1>(a, b, c, sa, sb);
+}
+
 // Largest finite value of the 8-bit formats: E4M3 448, E5M2 57344.
 __device__ __forceinline__ constexpr float fp8_max(int fmt) { return fmt ? 57344.0f : 448.0f; }
 

@@ -15,6 +15,12 @@
 //          Padding (up to the output's leading dimension) is written as zero
 //          codes, so that products can run K up to a whole number of
 //          128-wide k-steps.
+//   mx:    block scaling (mxfp8): the same tiles, each copy quantized on
+//          blocks of 32 along its own contiguous dimension, so the row-wise
+//          and the transposed copy get codes and scales of their own.  A
+//          row's block maximum comes from a 4-lane shuffle (32 columns = 4
+//          threads); a column's from a shuffle over the wave's 16 rows and
+//          one LDS exchange between the two waves of a 32-row block.
 #include <algorithm>
 
 #include "device_common.h"
@@ -153,6 +159,111 @@ __global__ __launch_bounds__(256) void cast_kernel(CastSrc x, const float* amax,
   reinterpret_cast<uint4*>(o)[1] = make_uint4(t[4], t[5], t[6], t[7]);
 }
 
+// E8M0 scale code of a block whose largest magnitude has the bf16 bits m
+// (sign cleared): 127 + floor(log2 amax) - emax, within 0..254; 127 (scale 1)
+// for an all-zero block.
+template <int FMT>
+__device__ __forceinline__ uint32_t mx_code(uint32_t m) {
+  constexpr int EMAX = FMT == FP8_E4M3 ? 8 : 15;
+  if (m == 0) return 127u;
+  const int e = static_cast<int>(m >> 7);
+  const int fl = e != 0 ? e - 127 : (31 - __clz(static_cast<int>(m))) - 133;  // subnormal: m 2^-133
+  return static_cast<uint32_t>(min(max(fl - EMAX + 127, 0), 254));
+}
+
+// 2^-X for scale code c (X = c - 127); exact, never subnormal for the codes
+// a finite bf16 block produces.
+__device__ __forceinline__ float mx_mult(uint32_t c) {
+  return __builtin_amdgcn_ldexpf(1.0f, 127 - static_cast<int>(c));
+}
+
+// One tile of X as cast_kernel, block-scaled.  Thread (br, bc) owns rows
+// r0 + 4 br .. +3 and columns c0 + 8 bc .. +7.  Row-wise: the 32-column
+// block of a row spans threads bc & ~3 .. +3; threads bc = 0 collect the four
+// block codes of their rows (the k-step's scale word) and write four words.
+// Transposed: the 32-row block of a column spans waves 2 blk and 2 blk + 1;
+// each wave reduces its 16 rows by shuffles and leaves the column maxima in
+// LDS.
+template <int FMT>
+__global__ __launch_bounds__(256) void mx_cast_kernel(CastSrc x, uint8_t* rows, int ldr,
+                                                      uint32_t* rs, int rs_ld, uint8_t* cols,
+                                                      int ldc, uint32_t* cs, int cs_ld) {
+  __shared__ uint32_t tt[CC * TSW];
+  __shared__ uint32_t cmax[4 * CC];  // [wave][column]: max |x| bits over the wave's 16 rows
+  const int r0 = blockIdx.y * CR, c0 = blockIdx.x * CC;
+  const int tid = threadIdx.x, br = tid >> 4, bc = tid & 15, wave = tid >> 6, lane = tid & 63;
+  const int c = c0 + 8 * bc;
+  uint32_t w[4][4];  // w[i][j/2]: bf16 pair of row r0 + 4 br + i, columns c + j, c + j + 1
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + 4 * br + i;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < x.R && c < x.C) v = *reinterpret_cast<const uint4*>(src_at(x, r, c));
+    w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
+  }
+  auto mag = [&](int i, int j) { return (w[i][j >> 1] >> (16 * (j & 1))) & 0x7fffu; };
+  auto val = [&](int i, int j) { return (j & 1) ? hi_bf(w[i][j >> 1]) : lo_bf(w[i][j >> 1]); };
+  auto xmax = [](uint32_t m, int o) {
+    return umax(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), o)));
+  };
+
+  if (rows != nullptr && c0 < ldr) {
+    uint32_t code[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = umax(m, mag(i, j));
+      m = xmax(xmax(m, 1), 2);
+      code[i] = mx_code<FMT>(m);
+      const float s = mx_mult(code[i]);
+      uint2 q;
+      q.x = quant4<FMT>(val(i, 0), val(i, 1), val(i, 2), val(i, 3), s);
+      q.y = quant4<FMT>(val(i, 4), val(i, 5), val(i, 6), val(i, 7), s);
+      const int r = r0 + 4 * br + i;
+      if (r < x.R) *reinterpret_cast<uint2*>(rows + static_cast<size_t>(r) * ldr + c) = q;
+    }
+    uint32_t word[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      word[i] = code[i] | static_cast<uint32_t>(__shfl(static_cast<int>(code[i]), lane + 4)) << 8 |
+                static_cast<uint32_t>(__shfl(static_cast<int>(code[i]), lane + 8)) << 16 |
+                static_cast<uint32_t>(__shfl(static_cast<int>(code[i]), lane + 12)) << 24;
+    if (bc == 0 && r0 < rs_ld)
+      *reinterpret_cast<uint4*>(rs + static_cast<size_t>(c0 / CC) * rs_ld + r0 + 4 * br) =
+          make_uint4(word[0], word[1], word[2], word[3]);
+  }
+  if (cols == nullptr || r0 >= ldc) return;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t m = umax(umax(mag(0, j), mag(1, j)), umax(mag(2, j), mag(3, j)));
+    m = xmax(xmax(m, 16), 32);
+    if (lane < 16) cmax[wave * CC + 8 * bc + j] = m;
+  }
+  __syncthreads();
+  const int blk = wave >> 1;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int col = 8 * bc + j;
+    const float s = mx_mult(mx_code<FMT>(umax(cmax[2 * blk * CC + col], cmax[(2 * blk + 1) * CC + col])));
+    tt[col * TSW + br] = quant4<FMT>(val(0, j), val(1, j), val(2, j), val(3, j), s);
+  }
+  if (tid < CC && c0 + tid < cs_ld) {
+    // this tile's two k-blocks of column c0 + tid: bytes (r0 % 128) / 32 + 0, 1
+    const uint32_t pair = mx_code<FMT>(umax(cmax[tid], cmax[CC + tid])) |
+                          mx_code<FMT>(umax(cmax[2 * CC + tid], cmax[3 * CC + tid])) << 8;
+    uint8_t* base = reinterpret_cast<uint8_t*>(cs + static_cast<size_t>(r0 / 128) * cs_ld + c0 + tid);
+    *reinterpret_cast<uint16_t*>(base + (r0 % 128) / 32) = static_cast<uint16_t>(pair);
+  }
+  __syncthreads();
+  const int oc = tid >> 1, ow = (tid & 1) * 8;
+  if (c0 + oc >= x.C) return;
+  const uint32_t* t = tt + oc * TSW + ow;
+  uint8_t* o = cols + static_cast<size_t>(c0 + oc) * ldc + r0 + ow * 4;
+  reinterpret_cast<uint4*>(o)[0] = make_uint4(t[0], t[1], t[2], t[3]);
+  reinterpret_cast<uint4*>(o)[1] = make_uint4(t[4], t[5], t[6], t[7]);
+}
+
 bool src_ok(const CastSrc& x) {
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   return x.p0 != nullptr && x.p1 != nullptr && al(x.p0) && al(x.p1) && x.R > 0 && x.C > 0 &&
@@ -195,6 +306,31 @@ hipError_t launch_cast_fp8(const CastSrc& x, Fp8Format fmt, const float* amax, u
     hipLaunchKernelGGL(cast_kernel<FP8_E4M3>, grid, dim3(256), 0, s, x, amax, rows, ldr, cols, ldc);
   else
     hipLaunchKernelGGL(cast_kernel<FP8_E5M2>, grid, dim3(256), 0, s, x, amax, rows, ldr, cols, ldc);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_mx(const CastSrc& x, Fp8Format fmt, uint8_t* rows, int ldr, uint32_t* rs,
+                          int rs_ld, uint8_t* cols, int ldc, uint32_t* cs, int cs_ld,
+                          hipStream_t s) {
+  if (!src_ok(x) || (rows == nullptr && cols == nullptr)) return hipErrorInvalidValue;
+  auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (rows != nullptr && (ldr < x.C || ldr % CC != 0 || !al(rows) || rs == nullptr || !al(rs) ||
+                          rs_ld < x.R || rs_ld % 64 != 0))
+    return hipErrorInvalidValue;
+  if (cols != nullptr && (ldc < x.R || ldc % CC != 0 || !al(cols) || cs == nullptr || !al(cs) ||
+                          cs_ld < x.C || cs_ld % 64 != 0))
+    return hipErrorInvalidValue;
+  // tiles over every code and scale word either copy holds (padding included)
+  int rspan = x.R, cspan = x.C;
+  if (rows != nullptr) { cspan = std::max(cspan, ldr); rspan = std::max(rspan, rs_ld); }
+  if (cols != nullptr) { rspan = std::max(rspan, ldc); cspan = std::max(cspan, cs_ld); }
+  const dim3 grid((cspan + CC - 1) / CC, (rspan + CR - 1) / CR);
+  if (fmt == FP8_E4M3)
+    hipLaunchKernelGGL(mx_cast_kernel<FP8_E4M3>, grid, dim3(256), 0, s, x, rows, ldr, rs, rs_ld,
+                       cols, ldc, cs, cs_ld);
+  else
+    hipLaunchKernelGGL(mx_cast_kernel<FP8_E5M2>, grid, dim3(256), 0, s, x, rows, ldr, rs, rs_ld,
+                       cols, ldc, cs, cs_ld);
   return hipGetLastError();
 }
 

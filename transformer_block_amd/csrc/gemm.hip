@@ -46,7 +46,11 @@
 // k order, so the sum is the product).  The epilogue first multiplies the
 // fp32 sums by the dequantization factor 1/(sA sB) of the operands' current
 // scales, sX = FMAX / amax(X), which it derives from the amax values the
-// cast kernels left in device memory.
+// cast kernels left in device memory.  With block (MX) scales the matrix
+// cores apply the scales themselves (v_mfma_scale_f32_32x32x64_f8f6f4): the
+// loader waves bring each stage tile's scale words (one 32-bit word per row
+// and 128-wide k-step) into a small LDS ring beside the operand ring, and
+// each lane passes the byte of its row's 32-wide k-block.
 #include <algorithm>
 #include <type_traits>
 
@@ -485,6 +489,10 @@ struct SkPlan {
   int* counters;     // arrival count per global tile: zero on entry, left zero
   const float* amax_a;  // FP8: amax of the operands (device), else null
   const float* amax_b;
+  const uint32_t* scale_a;  // MX: block-scale words [k-step][row] of A and B, else null
+  const uint32_t* scale_b;
+  int scale_lda, scale_ldb;  // words per k-step (>= rows)
+  uint32_t scale_bytes_a, scale_bytes_b;
 };
 
 struct Item {
@@ -545,10 +553,12 @@ __device__ __forceinline__ int part_slot(const SkPlan& pl, int i) {
 }
 
 // FMT 0: bf16 operands; FP8 operands otherwise, FMT - 1 = fa + 2 fb with
-// fa, fb the operands' formats (Fp8Format: 0 E4M3, 1 E5M2).
-template <int AMAJ, int BMAJ, int MODE, int FMT = 0>
+// fa, fb the operands' formats (Fp8Format: 0 E4M3, 1 E5M2).  MX: FP8 with
+// block scales instead of current scales.
+template <int AMAJ, int BMAJ, int MODE, int FMT = 0, bool MX = false>
 __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
   constexpr bool F8 = FMT != 0;
+  static_assert(!MX || F8, "block scales come with FP8 operands");
   constexpr int FA = F8 ? (FMT - 1) & 1 : 0, FB = F8 ? (FMT - 1) >> 1 : 0;
   constexpr int ESZ = F8 ? 1 : 2;          // operand bytes per element
   constexpr int KSTEP = BK * 2 / ESZ;      // k-values per stage tile (128-byte rows)
@@ -559,6 +569,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
   // EPI_LD fp32) lies in stage 1, which is idle from an item's last k-step
   // until the next item's second stage tile goes out after the epilogue.
   __shared__ __attribute__((aligned(1024))) u16 ring[NSTAGE * STAGE];
+  // MX: per stage the scale words of the A tile's 256 rows, then the B tile's
+  __shared__ __attribute__((aligned(1024))) uint32_t sring[MX ? NSTAGE * 2 * TILE : 1];
   __shared__ int arrival;
   float* const epi_stage = reinterpret_cast<float*>(ring + STAGE);
   static_assert(WAVES * 32 * EPI_LD * 4 <= STAGE * 2, "epilogue staging fits in one stage");
@@ -583,6 +595,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
   int item = v;
   Item s = decode_item(pl, item);
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_address(ring));
+  const uint32_t sring_lds = __builtin_amdgcn_readfirstlane(lds_address(sring));
 
   auto setup = [&](const Item& sg) {
     const GemmProblem& P = pl.p[sg.prob];
@@ -599,6 +612,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
     const uint32_t lds = ring_lds + slot * (STAGE * 2);
     la.issue(lds, wave, k0, valid);
     lb.issue(lds + TILE * BK * 2, wave, k0, valid);
+    if constexpr (MX) {
+      // scale words of the tile's 256 rows at this k-step: 1 KB per operand,
+      // one load by wave 0 (A) and one by wave 1 (B); rows past the array
+      // read as zero (their operand rows are zero too)
+      if (wave < 2) {
+        const int ks = sg.kb + (valid ? j : 0);
+        const int row0 = wave ? sg.n0 : sg.m0;
+        const int ld = wave ? pl.scale_ldb : pl.scale_lda;
+        const i32x4 d = wave ? make_desc(reinterpret_cast<const u16*>(pl.scale_b), pl.scale_bytes_b)
+                             : make_desc(reinterpret_cast<const u16*>(pl.scale_a), pl.scale_bytes_a);
+        lds_dma16(d, sring_lds + (slot * 2 + wave) * (TILE * 4), lane * 16,
+                  valid ? (ks * ld + row0) * 4 : kOutOfRange);
+      }
+    }
   };
 
   int koff[4];
@@ -619,10 +646,28 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(fa[slot][i], fb[slot][j], acc[i][j]);
   };
-  // FP8: the 32 bytes of bf16 k-steps 2 half and 2 half + 1 (64 k-values)
+  // FP8: the 32 bytes of bf16 k-steps 2 half and 2 half + 1 (64 k-values):
+  // lane half h holds k [64 half + 16 h, +16) and [64 half + 32 + 16 h, +16)
+  // of the stage tile, so the matrix cores' k-block b of this half is the
+  // tile's 32-wide block 2 half + b.  MX: the scale codes of that block
+  // for the lane's row in each of its fragments, packed one byte per
+  // fragment (sa8: A fragment i in byte i, sb8: B fragment j in byte j); the
+  // MFMA's byte selects are immediates.
   i32x8 ga[2][FM], gb[2][FN];
+  uint32_t sa8[2], sb8[2];
   auto rd8 = [&](const u16* st, int half, int slot) {
     const int k0 = koff[2 * half], k1 = koff[2 * half + 1];
+    if constexpr (MX) {
+      const uint32_t* sw = sring + ((st - ring) / STAGE) * (2 * TILE) + (lane & 31);
+      const uint32_t bit = 16 * half + 8 * (lane >> 5);  // byte 2 half + h of the row's word
+      uint32_t pa = 0, pb = 0;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) pa |= ((sw[wm * WM + i * 32] >> bit) & 0xffu) << (8 * i);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) pb |= ((sw[TILE + wn * WN + j * 32] >> bit) & 0xffu) << (8 * j);
+      sa8[slot] = pa;
+      sb8[slot] = pb;
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const u16* t = st + (wm * WM + i * 32) * BK;
@@ -640,11 +685,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = mfma32x32x64_f8<FA, FB>(ga[slot][i], gb[slot][j], acc[i][j]);
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (!MX)
+          acc[i][j] = mfma32x32x64_f8<FA, FB>(ga[slot][i], gb[slot][j], acc[i][j]);
+        else
+          acc[i][j] = mx_step<FA, FB>(i, j, ga[slot][i], gb[slot][j], acc[i][j], sa8[slot], sb8[slot]);
+      }
   };
   auto pin8 = [&]() {
-    constexpr int R = 2 * (FM + FN);
+    constexpr int R = (MX ? 3 : 2) * (FM + FN);
 #pragma unroll
     for (int i = 0; i < FM * FN; ++i) {
       __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
@@ -759,7 +808,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
       const int my_slot = part_slot(pl, item);
       float held[MODE == EPI_QKV_SWIGLU ? 16 : 1];
       float dq = 1.0f;  // FP8: 1 / (sA sB)
-      if constexpr (F8) dq = inv_scale(*pl.amax_a, fp8_max(FA)) * inv_scale(*pl.amax_b, fp8_max(FB));
+      if constexpr (F8 && !MX)
+        dq = inv_scale(*pl.amax_a, fp8_max(FA)) * inv_scale(*pl.amax_b, fp8_max(FB));
       for (;;) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -1150,10 +1200,10 @@ bool operand_ok(const Operand& op) {
          op.ld1 > 0 && op.split >= 0 && (op.split % 64 == 0 || op.split >= (1 << 30));
 }
 
-template <int MODE, int FMT>
+template <int MODE, int FMT, bool MX = false>
 hipError_t launch_plan_fp8(const SkPlan& pl, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_sk_kernel<KMAJOR, KMAJOR, MODE, FMT>), dim3(grid), dim3(64 * WAVES), 0,
-                     s, pl);
+  hipLaunchKernelGGL((gemm_sk_kernel<KMAJOR, KMAJOR, MODE, FMT, MX>), dim3(grid), dim3(64 * WAVES),
+                     0, s, pl);
   return hipGetLastError();
 }
 
@@ -1195,6 +1245,9 @@ hipError_t build_plan(const GemmProblem* probs, int nprob, Major a_major, Major 
   pl.partials = ws.partials;
   pl.counters = ws.counters;
   pl.amax_a = pl.amax_b = nullptr;
+  pl.scale_a = pl.scale_b = nullptr;
+  pl.scale_lda = pl.scale_ldb = 0;
+  pl.scale_bytes_a = pl.scale_bytes_b = 0;
 
   int G = device_cus();
   if (G <= 0) return hipErrorInvalidDevice;
@@ -1295,6 +1348,37 @@ hipError_t launch_gemm_fp8(const GemmProblem& prob, Fp8Format fa, const float* a
   if (fmt == 2 && mode == EPI_STORE2_COLS) return launch_plan_fp8<EPI_STORE2_COLS, 2>(pl, grid, s);
   if (fmt == 3 && mode == EPI_STORE2_ROWS) return launch_plan_fp8<EPI_STORE2_ROWS, 3>(pl, grid, s);
   if (fmt == 3 && mode == EPI_STORE2_COLS) return launch_plan_fp8<EPI_STORE2_COLS, 3>(pl, grid, s);
+  return hipErrorInvalidValue;  // a combination the FP8 layer does not use
+}
+
+hipError_t launch_gemm_mx(const GemmProblem& prob, Fp8Format fa, const MxScales& sa,
+                          Fp8Format fb, const MxScales& sb, EpiMode mode,
+                          const GemmScratch& ws, hipStream_t s) {
+  // 16-byte rows of 8-bit elements, whole 128-wide k-steps, scale words for
+  // every row of both operands
+  if (prob.A.ld0 % 16 != 0 || prob.A.ld1 % 16 != 0 || prob.B.ld0 % 16 != 0 ||
+      prob.B.ld1 % 16 != 0 || prob.K % (2 * BK) != 0 || sa.p == nullptr || sb.p == nullptr ||
+      sa.ld < prob.M || sb.ld < prob.N || sa.ld % 64 != 0 || sb.ld % 64 != 0)
+    return hipErrorInvalidValue;
+  const size_t ks = static_cast<size_t>(prob.K) / (2 * BK);
+  if (ks * sa.ld * 4 >= (1UL << 31) || ks * sb.ld * 4 >= (1UL << 31)) return hipErrorInvalidValue;
+  SkPlan pl;
+  int grid = 0;
+  const hipError_t e = build_plan(&prob, 1, KMAJOR, KMAJOR, ws, 0, &pl, &grid, 2 * BK);
+  if (e != hipSuccess) return e;
+  pl.scale_a = sa.p;
+  pl.scale_b = sb.p;
+  pl.scale_lda = sa.ld;
+  pl.scale_ldb = sb.ld;
+  pl.scale_bytes_a = static_cast<uint32_t>(ks * sa.ld * 4);
+  pl.scale_bytes_b = static_cast<uint32_t>(ks * sb.ld * 4);
+  const int fmt = 1 + fa + 2 * fb;
+  if (fmt == 1 && mode == EPI_QKV_GELU) return launch_plan_fp8<EPI_QKV_GELU, 1, true>(pl, grid, s);
+  if (fmt == 1 && mode == EPI_RESIDUAL) return launch_plan_fp8<EPI_RESIDUAL, 1, true>(pl, grid, s);
+  if (fmt == 2 && mode == EPI_DGELU) return launch_plan_fp8<EPI_DGELU, 2, true>(pl, grid, s);
+  if (fmt == 2 && mode == EPI_STORE2_COLS) return launch_plan_fp8<EPI_STORE2_COLS, 2, true>(pl, grid, s);
+  if (fmt == 3 && mode == EPI_STORE2_ROWS) return launch_plan_fp8<EPI_STORE2_ROWS, 3, true>(pl, grid, s);
+  if (fmt == 3 && mode == EPI_STORE2_COLS) return launch_plan_fp8<EPI_STORE2_COLS, 3, true>(pl, grid, s);
   return hipErrorInvalidValue;  // a combination the FP8 layer does not use
 }
 

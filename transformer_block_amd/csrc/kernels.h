@@ -81,6 +81,16 @@ struct GemmProblem {
 // E4M3 (largest 448) and E5M2 (largest 57344), OCP encodings.
 enum Fp8Format { FP8_E4M3 = 0, FP8_E5M2 = 1 };
 
+// Block-scaled (MX) FP8: blocks of 32 consecutive values along a copy's
+// contiguous (contraction) dimension, one E8M0 scale each (code e means
+// 2^(e - 127)).  A copy's scales are 32-bit words, one per (128-wide k-step,
+// row): word[ks * ld + r] holds in byte b the code of k-block 4 ks + b of row
+// r; ld >= rows and a multiple of 64.  The GEMM reads them as they are.
+struct MxScales {
+  const uint32_t* p;
+  int ld;
+};
+
 // Scratch of the GEMM launches: fp32 partial sums of 256 x 256 tiles that
 // are split along k (kGemmPartialSlots of them at most) and one arrival
 // counter per output tile.  The counters must be zero before a launch; every
@@ -124,6 +134,14 @@ hipError_t launch_gemm_fp8(const GemmProblem& prob, Fp8Format fa, const float* a
                            Fp8Format fb, const float* amax_b, EpiMode mode,
                            const GemmScratch& scratch, hipStream_t stream);
 
+// The same products on block-scaled (MX) operands: the scales are applied by
+// the matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4), so the epilogue sees C
+// itself.  sa holds the scale words of A's M rows, sb those of B's N rows
+// (B stored k-contiguous, [N][K]), K a multiple of 128.
+hipError_t launch_gemm_mx(const GemmProblem& prob, Fp8Format fa, const MxScales& sa,
+                          Fp8Format fb, const MxScales& sb, EpiMode mode,
+                          const GemmScratch& scratch, hipStream_t stream);
+
 // A logical bf16 matrix X [R, C] made of up to two row-major segments:
 // columns [0, split) from p0 (ld0) and [split, C) from p1 (ld1) when
 // split_on_rows = 0, rows likewise when it is 1 (split >= C or R: one
@@ -147,6 +165,16 @@ hipError_t launch_amax(const CastSrc& x, float* amax, hipStream_t stream);
 // ldr and ldc are multiples of 64; either output may be null.
 hipError_t launch_cast_fp8(const CastSrc& x, Fp8Format fmt, const float* amax, uint8_t* rows,
                            int ldr, uint8_t* cols, int ldc, hipStream_t stream);
+
+// Block-scaled FP8 copies of X: code = RNE(clamp(x 2^-X, -FMAX, FMAX)) with
+// X = floor(log2 amax_block) - emax (emax 8 for E4M3, 15 for E5M2; 0 for an
+// all-zero block), written row-wise to rows [R][ldr] with scale words rs
+// (ld rs_ld >= R) and/or transposed to cols [C][ldc] with scale words cs
+// (ld cs_ld >= C).  ldr and ldc are multiples of 128 (whole k-steps);
+// padding codes are zero, padding blocks and rows get code 127.
+hipError_t launch_cast_mx(const CastSrc& x, Fp8Format fmt, uint8_t* rows, int ldr, uint32_t* rs,
+                          int rs_ld, uint8_t* cols, int ldc, uint32_t* cs, int cs_ld,
+                          hipStream_t stream);
 
 // LayerNorm forward over rows of x [T, h]: a = bf16(LN(x)) and its rounding
 // residual a_lo = bf16(LN(x) - a) (skipped when a_lo is null), mu, rstd (fp32).

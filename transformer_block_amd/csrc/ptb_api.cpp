@@ -203,71 +203,102 @@ SerialWorkLayout serial_work_layout(const Shape& s) {
 // ---- FP8 variant.  Every FP8 product reads two k-contiguous operands whose
 // k extent is padded with zero codes to a multiple of 128 (one stage tile).
 size_t pad128(size_t v) { return (v + 127) & ~static_cast<size_t>(127); }
+size_t pad64(size_t v) { return (v + 63) & ~static_cast<size_t>(63); }
 
-// The FP8 weight buffer: amax of W1 = [W_qkv | W_fc1] and W2 = [W_o ; W_fc2],
-// then both orientations of each in E4M3.
-struct Fp8WeightLayout {
-  size_t amax, w1t, w1r, w2t, w2r, total;
+// One FP8 copy of an operand: `rows` rows of codes, contraction extent k
+// padded to kp = pad128(k), and under block scaling its scale words
+// [kp / 128][pad64(rows)].
+struct Fp8Copy {
+  size_t codes, scales;  // byte offsets (scales: SIZE_MAX when absent)
+  size_t rows, kp;
 };
-Fp8WeightLayout fp8_weight_layout(const Shape& s) {
+// Appends a copy at offset *o.
+Fp8Copy add_copy(size_t* o, size_t rows, size_t k, bool mx) {
+  Fp8Copy c;
+  c.rows = rows;
+  c.kp = pad128(k);
+  c.codes = *o;
+  *o = align_up(*o + rows * c.kp);
+  c.scales = SIZE_MAX;
+  if (mx) {
+    c.scales = *o;
+    *o = align_up(*o + c.kp / 128 * pad64(rows) * sizeof(uint32_t));
+  }
+  return c;
+}
+
+// The FP8 weight buffer: amax of W1 = [W_qkv | W_fc1] and W2 = [W_o ; W_fc2]
+// (current scaling), then both orientations of each in E4M3 (with their
+// block scales under MX).
+struct Fp8WeightLayout {
+  size_t amax;
+  Fp8Copy w1t, w1r, w2t, w2r;
+  size_t total;
+};
+Fp8WeightLayout fp8_weight_layout(const Shape& s, bool mx) {
   Fp8WeightLayout L;
   size_t o = 0;
-  L.amax = o; o = align_up(o + 2 * sizeof(float));
-  L.w1t = o; o = align_up(o + s.N1 * pad128(s.h));   // W1^T [N1, h]   (forward)
-  L.w1r = o; o = align_up(o + s.h * pad128(s.N1));   // W1   [h, N1]   (dgrad)
-  L.w2t = o; o = align_up(o + s.h * pad128(s.K2));   // W2^T [h, K2]   (forward)
-  L.w2r = o; o = align_up(o + s.K2 * pad128(s.h));   // W2   [K2, h]   (dgrad)
+  L.amax = SIZE_MAX;
+  if (!mx) { L.amax = o; o = align_up(o + 2 * sizeof(float)); }
+  L.w1t = add_copy(&o, s.N1, s.h, mx);   // W1^T [N1, h]   (forward)
+  L.w1r = add_copy(&o, s.h, s.N1, mx);   // W1   [h, N1]   (dgrad)
+  L.w2t = add_copy(&o, s.h, s.K2, mx);   // W2^T [h, K2]   (forward)
+  L.w2r = add_copy(&o, s.K2, s.h, mx);   // W2   [K2, h]   (dgrad)
   L.total = o;
   return L;
 }
 
 // The FP8 workspace: the bf16 layer's workspace, then the amax of the
-// gradient operands and the FP8 copies that live within one call.
+// gradient operands (current scaling) and the FP8 copies that live within
+// one call.
 enum Fp8Amax { AMAX_DY = 0, AMAX_DZ, AMAX_COUNT };
 struct Fp8WorkLayout {
   WorkLayout base;
-  size_t amax, a8, cg8, dy8, dy8t, dz8, dz8t, total;
+  size_t amax;
+  Fp8Copy a8, cg8, dy8, dy8t, dz8, dz8t;
+  size_t total;
 };
-Fp8WorkLayout fp8_work_layout(const Shape& s) {
+Fp8WorkLayout fp8_work_layout(const Shape& s, bool mx) {
   Fp8WorkLayout W;
   W.base = work_layout(s);
   size_t o = W.base.total;
-  const size_t Tp = pad128(s.T);
   W.amax = o; o = align_up(o + AMAX_COUNT * sizeof(float));
-  W.a8 = o; o = align_up(o + s.T * pad128(s.h));     // a       [T, h]  (forward)
-  W.cg8 = o; o = align_up(o + s.T * pad128(s.K2));   // [c | g] [T, K2] (forward)
-  W.dy8 = o; o = align_up(o + s.T * pad128(s.h));    // dy      [T, h]
-  W.dy8t = o; o = align_up(o + s.h * Tp);            // dy^T    [h, T]
-  W.dz8 = o; o = align_up(o + s.T * pad128(s.N1));   // dZ      [T, N1]
-  W.dz8t = o; o = align_up(o + s.N1 * Tp);           // dZ^T
+  W.a8 = add_copy(&o, s.T, s.h, mx);     // a       [T, h]  (forward)
+  W.cg8 = add_copy(&o, s.T, s.K2, mx);   // [c | g] [T, K2] (forward)
+  W.dy8 = add_copy(&o, s.T, s.h, mx);    // dy      [T, h]
+  W.dy8t = add_copy(&o, s.h, s.T, mx);   // dy^T    [h, T]
+  W.dz8 = add_copy(&o, s.T, s.N1, mx);   // dZ      [T, N1]
+  W.dz8t = add_copy(&o, s.N1, s.T, mx);  // dZ^T    [N1, T]
   W.total = o;
   return W;
 }
 
 // The FP8 layer's stash: the parallel block's slots, then what the forward
 // casts for the weight gradients (the transposed E4M3 copies of a and
-// [c | g] and their amax).
+// [c | g] and their amax or block scales).
 struct Fp8SavedLayout {
   SavedLayout base;
-  size_t amax, a8t, cg8t, total;
+  size_t amax;
+  Fp8Copy a8t, cg8t;
+  size_t total;
 };
-Fp8SavedLayout fp8_saved_layout(const Shape& s) {
+Fp8SavedLayout fp8_saved_layout(const Shape& s, bool mx) {
   Fp8SavedLayout L;
   L.base = saved_layout(s);
   size_t o = L.base.total;
-  const size_t Tp = pad128(s.T);
   L.amax = o; o = align_up(o + 2 * sizeof(float));   // amax of a, of [c | g]
-  L.a8t = o; o = align_up(o + s.h * Tp);             // a^T       [h, T]
-  L.cg8t = o; o = align_up(o + s.K2 * Tp);           // [c | g]^T [K2, T]
+  L.a8t = add_copy(&o, s.h, s.T, mx);                // a^T       [h, T]
+  L.cg8t = add_copy(&o, s.K2, s.T, mx);              // [c | g]^T [K2, T]
   L.total = o;
   return L;
 }
 
-// The variant covers LayerNorm or RMSNorm with the GeLU MLP.
-int32_t check_fp8_dims(const ptb_dims* dims, Shape* s) {
+// The variant covers LayerNorm or RMSNorm with the GeLU MLP, under either
+// recipe.
+int32_t check_fp8_dims(const ptb_dims* dims, int32_t recipe, Shape* s) {
   const int32_t st = check_dims(dims, s);
   if (st != PTB_OK) return st;
-  if (s->swiglu) return PTB_ERR_ARG;
+  if (s->swiglu || (recipe != PTB_FP8_CURRENT && recipe != PTB_FP8_MX)) return PTB_ERR_ARG;
   // FP8 operands are addressed with 32-bit byte offsets as well: every copy
   // (rows x padded contiguous dimension, one byte each) stays below 2^31
   const size_t T = s->T, h = s->h, N1 = s->N1, K2 = s->K2;
@@ -347,6 +378,52 @@ hipError_t cast_fp8(const ptb::CastSrc& x, ptb::Fp8Format fmt, float* amax, uint
   do {                                             \
     if ((expr) != hipSuccess) return PTB_ERR_HIP;  \
   } while (0)
+
+// An FP8 copy in a caller buffer: codes [rows][kp] and, under block
+// scaling, scale words [kp / 128][pad64(rows)].
+struct Copy8 {
+  uint8_t* q;
+  uint32_t* s;
+  size_t ld;   // kp
+  int sld;     // pad64(rows)
+  size_t rows;
+};
+Copy8 copy_at(void* base, const Fp8Copy& c) {
+  return Copy8{at<uint8_t>(base, c.codes),
+               c.scales == SIZE_MAX ? nullptr : at<uint32_t>(base, c.scales), c.kp,
+               static_cast<int>(pad64(c.rows)), c.rows};
+}
+Copy8 copy_at(const void* base, const Fp8Copy& c) {
+  return copy_at(const_cast<void*>(base), c);
+}
+
+// The two FP8 copies of x under the layer's recipe (rows: contraction along
+// x's columns; cols: the transpose).  Current scaling: amax of x into
+// *amax (zero on entry), then the cast; block scaling: one pass.
+hipError_t cast_copies(bool mx, const ptb::CastSrc& x, ptb::Fp8Format fmt, float* amax,
+                       const Copy8& rows, const Copy8& cols, hipStream_t strm) {
+  if (mx)
+    return ptb::launch_cast_mx(x, fmt, rows.q, static_cast<int>(rows.ld), rows.s, rows.sld,
+                               cols.q, static_cast<int>(cols.ld), cols.s, cols.sld, strm);
+  return cast_fp8(x, fmt, amax, rows.q, rows.ld, cols.q, cols.ld, strm);
+}
+
+// An FP8 product C = A B^T of two copies (A [M][K], B [N][K]) with the
+// problem's epilogue, scaled by the operands' amax or block scales.
+hipError_t gemm8(bool mx, ptb::GemmProblem pr, const Copy8& a, ptb::Fp8Format fa,
+                 const float* amax_a, const Copy8& b, ptb::Fp8Format fb, const float* amax_b,
+                 ptb::EpiMode mode, const ptb::GemmScratch& gs, hipStream_t strm) {
+  pr.M = static_cast<int>(a.rows);
+  pr.N = static_cast<int>(b.rows);
+  pr.K = static_cast<int>(a.ld);
+  pr.A = one8(a.q, a.ld, a.rows);
+  pr.B = one8(b.q, b.ld, b.rows);
+  if (mx)
+    return ptb::launch_gemm_mx(pr, fa, ptb::MxScales{a.s, a.sld}, fb, ptb::MxScales{b.s, b.sld},
+                               mode, gs, strm);
+  return ptb::launch_gemm_fp8(pr, fa, amax_a, fb, amax_b, mode, gs, strm);
+}
+
 
 // Enqueue one stage, bracketed by the caller's timing events when given.
 #define PTB_STAGE(i, expr)                                                          \
@@ -911,44 +988,48 @@ int32_t ptb_lamb_step(const ptb_lamb_hyper* hyper, const ptb_lamb_tensor* tensor
 
 // ---- FP8 GEMM variant
 
-int32_t ptb_fp8_weights_bytes(const ptb_dims* dims, size_t* bytes) {
+int32_t ptb_fp8_weights_bytes(const ptb_dims* dims, int32_t recipe, size_t* bytes) {
   Shape s;
-  const int32_t st = check_fp8_dims(dims, &s);
+  const int32_t st = check_fp8_dims(dims, recipe, &s);
   if (st != PTB_OK) return st;
   if (bytes == nullptr) return PTB_ERR_NULL;
-  *bytes = fp8_weight_layout(s).total;
+  *bytes = fp8_weight_layout(s, recipe == PTB_FP8_MX).total;
   return PTB_OK;
 }
 
-int32_t ptb_fp8_saved_bytes(const ptb_dims* dims, size_t* bytes) {
+int32_t ptb_fp8_saved_bytes(const ptb_dims* dims, int32_t recipe, size_t* bytes) {
   Shape s;
-  const int32_t st = check_fp8_dims(dims, &s);
+  const int32_t st = check_fp8_dims(dims, recipe, &s);
   if (st != PTB_OK) return st;
   if (bytes == nullptr) return PTB_ERR_NULL;
-  *bytes = fp8_saved_layout(s).total;
+  *bytes = fp8_saved_layout(s, recipe == PTB_FP8_MX).total;
   return PTB_OK;
 }
 
-int32_t ptb_fp8_workspace_bytes(const ptb_dims* dims, size_t* bytes) {
+int32_t ptb_fp8_workspace_bytes(const ptb_dims* dims, int32_t recipe, size_t* bytes) {
   Shape s;
-  const int32_t st = check_fp8_dims(dims, &s);
+  const int32_t st = check_fp8_dims(dims, recipe, &s);
   if (st != PTB_OK) return st;
   if (bytes == nullptr) return PTB_ERR_NULL;
-  *bytes = fp8_work_layout(s).total;
+  *bytes = fp8_work_layout(s, recipe == PTB_FP8_MX).total;
   return PTB_OK;
 }
 
-int32_t ptb_fp8_weights_layout(const ptb_dims* dims, size_t* offsets) {
+int32_t ptb_fp8_weights_layout(const ptb_dims* dims, int32_t recipe, size_t* offsets) {
   Shape s;
-  const int32_t st = check_fp8_dims(dims, &s);
+  const int32_t st = check_fp8_dims(dims, recipe, &s);
   if (st != PTB_OK) return st;
   if (offsets == nullptr) return PTB_ERR_NULL;
-  const Fp8WeightLayout L = fp8_weight_layout(s);
+  const Fp8WeightLayout L = fp8_weight_layout(s, recipe == PTB_FP8_MX);
   offsets[PTB_FP8_AMAX] = L.amax;
-  offsets[PTB_FP8_W1T] = L.w1t;
-  offsets[PTB_FP8_W1] = L.w1r;
-  offsets[PTB_FP8_W2T] = L.w2t;
-  offsets[PTB_FP8_W2] = L.w2r;
+  offsets[PTB_FP8_W1T] = L.w1t.codes;
+  offsets[PTB_FP8_W1] = L.w1r.codes;
+  offsets[PTB_FP8_W2T] = L.w2t.codes;
+  offsets[PTB_FP8_W2] = L.w2r.codes;
+  offsets[PTB_FP8_W1T_S] = L.w1t.scales;
+  offsets[PTB_FP8_W1_S] = L.w1r.scales;
+  offsets[PTB_FP8_W2T_S] = L.w2t.scales;
+  offsets[PTB_FP8_W2_S] = L.w2r.scales;
   return PTB_OK;
 }
 
@@ -962,8 +1043,8 @@ int32_t ptb_fp8_quantize(const void* x, int32_t rows, int32_t cols, int32_t form
       (qt != nullptr && !aligned16(qt)))
     return PTB_ERR_ALIGN;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
-  const size_t ldq = (static_cast<size_t>(cols) + 63) & ~static_cast<size_t>(63);
-  const size_t ldqt = (static_cast<size_t>(rows) + 63) & ~static_cast<size_t>(63);
+  const size_t ldq = pad64(static_cast<size_t>(cols));
+  const size_t ldqt = pad64(static_cast<size_t>(rows));
   PTB_HIP(ptb::launch_zero_i32(reinterpret_cast<int*>(amax), 1, strm));
   PTB_HIP(cast_fp8(cast_one(x, cols, rows, cols),
                    format == PTB_FP8_E4M3 ? ptb::FP8_E4M3 : ptb::FP8_E5M2, amax,
@@ -971,42 +1052,68 @@ int32_t ptb_fp8_quantize(const void* x, int32_t rows, int32_t cols, int32_t form
   return PTB_OK;
 }
 
-int32_t ptb_fp8_cast_weights(const ptb_dims* dims, const void* w_qkv, const void* w_o,
-                             const void* w_fc1, const void* w_fc2, void* fp8_weights,
-                             void* stream) {
-  Shape s;
-  int32_t st = check_fp8_dims(dims, &s);
-  if (st != PTB_OK) return st;
-  st = check_ptrs({w_qkv, w_o, w_fc1, w_fc2, fp8_weights});
-  if (st != PTB_OK) return st;
-  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
-  const Fp8WeightLayout L = fp8_weight_layout(s);
-  float* amax = at<float>(fp8_weights, L.amax);
-  PTB_HIP(ptb::launch_zero_i32(reinterpret_cast<int*>(amax), 2, strm));
-  // W1 = [W_qkv | W_fc1] [h, N1]: row-wise for the dgrad, transposed for the forward
-  PTB_HIP(cast_fp8(cast_two(w_qkv, 3 * s.hl, w_fc1, s.f, 3 * s.hl, 0, s.h, s.N1), ptb::FP8_E4M3,
-                   amax, at<uint8_t>(fp8_weights, L.w1r), pad128(s.N1),
-                   at<uint8_t>(fp8_weights, L.w1t), pad128(s.h), strm));
-  // W2 = [W_o ; W_fc2] [K2, h]
-  PTB_HIP(cast_fp8(cast_two(w_o, s.h, w_fc2, s.h, s.hl, 1, s.K2, s.h), ptb::FP8_E4M3, amax + 1,
-                   at<uint8_t>(fp8_weights, L.w2r), pad128(s.h),
-                   at<uint8_t>(fp8_weights, L.w2t), pad128(s.K2), strm));
+int32_t ptb_fp8_quantize_mx(const void* x, int32_t rows, int32_t cols, int32_t format, void* q,
+                            void* q_scales, void* qt, void* qt_scales, void* stream) {
+  const bool row_copy = q != nullptr && q_scales != nullptr;
+  const bool col_copy = qt != nullptr && qt_scales != nullptr;
+  if (x == nullptr || (!row_copy && !col_copy)) return PTB_ERR_NULL;
+  if ((format != PTB_FP8_E4M3 && format != PTB_FP8_E5M2)) return PTB_ERR_ARG;
+  if (rows < 1 || cols < 8 || cols % 8 != 0 || static_cast<long>(rows) * cols >= (1L << 30))
+    return PTB_ERR_DIMS;
+  if (!aligned16(x) || (row_copy && (!aligned16(q) || !aligned16(q_scales))) ||
+      (col_copy && (!aligned16(qt) || !aligned16(qt_scales))))
+    return PTB_ERR_ALIGN;
+  const size_t R = static_cast<size_t>(rows), C = static_cast<size_t>(cols);
+  PTB_HIP(ptb::launch_cast_mx(
+      cast_one(x, cols, rows, cols), format == PTB_FP8_E4M3 ? ptb::FP8_E4M3 : ptb::FP8_E5M2,
+      row_copy ? static_cast<uint8_t*>(q) : nullptr, static_cast<int>(pad128(C)),
+      row_copy ? static_cast<uint32_t*>(q_scales) : nullptr, static_cast<int>(pad64(R)),
+      col_copy ? static_cast<uint8_t*>(qt) : nullptr, static_cast<int>(pad128(R)),
+      col_copy ? static_cast<uint32_t*>(qt_scales) : nullptr, static_cast<int>(pad64(C)),
+      reinterpret_cast<hipStream_t>(stream)));
   return PTB_OK;
 }
 
-int32_t ptb_fp8_forward(const ptb_dims* dims, const void* x, const void* ln_gamma,
-                        const void* ln_beta, const void* fp8_weights, void* y, void* saved,
-                        void* workspace, void* stream, void* const* ev) {
+
+int32_t ptb_fp8_cast_weights(const ptb_dims* dims, int32_t recipe, const void* w_qkv,
+                             const void* w_o, const void* w_fc1, const void* w_fc2,
+                             void* fp8_weights, void* stream) {
   Shape s;
-  int32_t st = check_fp8_dims(dims, &s);
+  int32_t st = check_fp8_dims(dims, recipe, &s);
+  if (st != PTB_OK) return st;
+  st = check_ptrs({w_qkv, w_o, w_fc1, w_fc2, fp8_weights});
+  if (st != PTB_OK) return st;
+  const bool mx = recipe == PTB_FP8_MX;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  const Fp8WeightLayout L = fp8_weight_layout(s, mx);
+  float* amax = mx ? nullptr : at<float>(fp8_weights, L.amax);
+  if (!mx) PTB_HIP(ptb::launch_zero_i32(reinterpret_cast<int*>(amax), 2, strm));
+  // W1 = [W_qkv | W_fc1] [h, N1]: row-wise for the dgrad, transposed for the forward
+  PTB_HIP(cast_copies(mx, cast_two(w_qkv, 3 * s.hl, w_fc1, s.f, 3 * s.hl, 0, s.h, s.N1),
+                      ptb::FP8_E4M3, amax, copy_at(fp8_weights, L.w1r),
+                      copy_at(fp8_weights, L.w1t), strm));
+  // W2 = [W_o ; W_fc2] [K2, h]
+  PTB_HIP(cast_copies(mx, cast_two(w_o, s.h, w_fc2, s.h, s.hl, 1, s.K2, s.h), ptb::FP8_E4M3,
+                      mx ? nullptr : amax + 1, copy_at(fp8_weights, L.w2r),
+                      copy_at(fp8_weights, L.w2t), strm));
+  return PTB_OK;
+}
+
+int32_t ptb_fp8_forward(const ptb_dims* dims, int32_t recipe, const void* x,
+                        const void* ln_gamma, const void* ln_beta, const void* fp8_weights,
+                        void* y, void* saved, void* workspace, void* stream,
+                        void* const* ev) {
+  Shape s;
+  int32_t st = check_fp8_dims(dims, recipe, &s);
   if (st != PTB_OK) return st;
   st = check_ptrs({x, ln_gamma, ln_beta, fp8_weights, y, saved, workspace});
   if (st != PTB_OK) return st;
+  const bool mx = recipe == PTB_FP8_MX;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
-  const Fp8SavedLayout SL = fp8_saved_layout(s);
+  const Fp8SavedLayout SL = fp8_saved_layout(s, mx);
   const SavedLayout& L = SL.base;
-  const Fp8WorkLayout W = fp8_work_layout(s);
-  const Fp8WeightLayout WL = fp8_weight_layout(s);
+  const Fp8WorkLayout W = fp8_work_layout(s, mx);
+  const Fp8WeightLayout WL = fp8_weight_layout(s, mx);
   const ptb::GemmScratch gs{at<float>(workspace, W.base.gemm_partials),
                             at<int>(workspace, W.base.counters), W.base.max_tiles};
   u16* a = at<u16>(saved, L.off[PTB_SAVED_A]);
@@ -1018,13 +1125,8 @@ int32_t ptb_fp8_forward(const ptb_dims* dims, const void* x, const void* ln_gamm
   u16* c = at<u16>(saved, L.off[PTB_SAVED_C]);
   float* lse = at<float>(saved, L.off[PTB_SAVED_LSE]);
   u16* qk_lo = at<u16>(saved, L.off[PTB_SAVED_QK_LO]);
-  float* samax = at<float>(saved, SL.amax);  // [0] a, [1] [c | g]
-  const float* wamax = at<float>(fp8_weights, WL.amax);
-  uint8_t* a8 = at<uint8_t>(workspace, W.a8);
-  uint8_t* cg8 = at<uint8_t>(workspace, W.cg8);
-  uint8_t* a8t = at<uint8_t>(saved, SL.a8t);
-  uint8_t* cg8t = at<uint8_t>(saved, SL.cg8t);
-  const size_t hp = pad128(s.h), K2p = pad128(s.K2), Tp = pad128(s.T);
+  float* samax = at<float>(saved, SL.amax);  // [0] a, [1] [c | g] (current scaling)
+  const float* wamax = mx ? nullptr : at<float>(fp8_weights, WL.amax);
 
   PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
   PTB_HIP(ptb::launch_zero_i32(reinterpret_cast<int*>(samax), 2, strm));
@@ -1035,12 +1137,10 @@ int32_t ptb_fp8_forward(const ptb_dims* dims, const void* x, const void* ln_gamm
                                     strm, s.rms));
   // a row-wise for the [QKV | FC1] product, transposed (stashed) for its
   // weight gradient
-  PTB_STAGE(1, cast_fp8(cast_one(a, s.h, s.T, s.h), ptb::FP8_E4M3, samax, a8, hp, a8t, Tp, strm));
+  PTB_STAGE(1, cast_copies(mx, cast_one(a, s.h, s.T, s.h), ptb::FP8_E4M3, samax,
+                           copy_at(workspace, W.a8), copy_at(saved, SL.a8t), strm));
   {  // [qkv | u] = a W1 in one FP8 product; q, k stored as value + residual, g = GeLU(u)
     ptb::GemmProblem pr;
-    pr.M = static_cast<int>(s.T); pr.N = static_cast<int>(s.N1); pr.K = static_cast<int>(hp);
-    pr.A = one8(a8, hp, s.T);
-    pr.B = one8(at<uint8_t>(fp8_weights, WL.w1t), hp, s.N1);
     pr.epi = ptb::Epilogue{};
     pr.epi.o0 = qkv; pr.epi.ld0 = static_cast<int>(3 * s.hl);
     pr.epi.o1 = u; pr.epi.o2 = g; pr.epi.ld1 = static_cast<int>(s.f);
@@ -1048,46 +1148,46 @@ int32_t ptb_fp8_forward(const ptb_dims* dims, const void* x, const void* ln_gamm
     pr.epi.o3 = qk_lo; pr.epi.ld3 = static_cast<int>(2 * s.hl);
     pr.epi.lo_cols = static_cast<int>(2 * s.hl);
     pr.epi.split = static_cast<int>(3 * s.hl);
-    PTB_STAGE(2, ptb::launch_gemm_fp8(pr, ptb::FP8_E4M3, samax, ptb::FP8_E4M3,
-                                      wamax, ptb::EPI_QKV_GELU, gs, strm));
+    PTB_STAGE(2, gemm8(mx, pr, copy_at(workspace, W.a8), ptb::FP8_E4M3, samax,
+                       copy_at(fp8_weights, WL.w1t), ptb::FP8_E4M3, wamax, ptb::EPI_QKV_GELU,
+                       gs, strm));
   }
   const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
                             gs.max_tiles, ptb::device_compute_units()};
   PTB_STAGE(3, ptb::launch_attention_fwd(qkv, qk_lo, c, lse, static_cast<int>(s.b),
                                     static_cast<int>(s.s), static_cast<int>(s.n),
                                     static_cast<int>(s.d), static_cast<int>(s.w), as, strm));
-  PTB_STAGE(4, cast_fp8(cast_two(c, s.hl, g, s.f, s.hl, 0, s.T, s.K2), ptb::FP8_E4M3,
-                        samax + 1, cg8, K2p, cg8t, Tp, strm));
+  PTB_STAGE(4, cast_copies(mx, cast_two(c, s.hl, g, s.f, s.hl, 0, s.T, s.K2), ptb::FP8_E4M3,
+                           samax + 1, copy_at(workspace, W.cg8), copy_at(saved, SL.cg8t), strm));
   {  // y = x + [c | g] W2
     ptb::GemmProblem pr;
-    pr.M = static_cast<int>(s.T); pr.N = static_cast<int>(s.h); pr.K = static_cast<int>(K2p);
-    pr.A = one8(cg8, K2p, s.T);
-    pr.B = one8(at<uint8_t>(fp8_weights, WL.w2t), K2p, s.h);
     pr.epi = ptb::Epilogue{};
     pr.epi.o0 = static_cast<u16*>(y); pr.epi.i0 = static_cast<const u16*>(x);
     pr.epi.ld0 = static_cast<int>(s.h);
-    PTB_STAGE(5, ptb::launch_gemm_fp8(pr, ptb::FP8_E4M3, samax + 1, ptb::FP8_E4M3,
-                                      wamax + 1, ptb::EPI_RESIDUAL, gs, strm));
+    PTB_STAGE(5, gemm8(mx, pr, copy_at(workspace, W.cg8), ptb::FP8_E4M3, samax + 1,
+                       copy_at(fp8_weights, WL.w2t), ptb::FP8_E4M3, mx ? nullptr : wamax + 1,
+                       ptb::EPI_RESIDUAL, gs, strm));
   }
   return PTB_OK;
 }
 
-int32_t ptb_fp8_backward(const ptb_dims* dims, const void* dy, const void* x,
-                         const void* ln_gamma, const void* fp8_weights, const void* saved,
-                         void* dx, void* d_ln_gamma, void* d_ln_beta, void* dw_qkv, void* dw_o,
-                         void* dw_fc1, void* dw_fc2, void* workspace, void* stream,
-                         void* const* ev) {
+int32_t ptb_fp8_backward(const ptb_dims* dims, int32_t recipe, const void* dy,
+                         const void* x, const void* ln_gamma, const void* fp8_weights,
+                         const void* saved, void* dx, void* d_ln_gamma, void* d_ln_beta,
+                         void* dw_qkv, void* dw_o, void* dw_fc1, void* dw_fc2, void* workspace,
+                         void* stream, void* const* ev) {
   Shape s;
-  int32_t st = check_fp8_dims(dims, &s);
+  int32_t st = check_fp8_dims(dims, recipe, &s);
   if (st != PTB_OK) return st;
   st = check_ptrs({dy, x, ln_gamma, fp8_weights, saved, dx, d_ln_gamma, d_ln_beta, dw_qkv, dw_o,
                    dw_fc1, dw_fc2, workspace});
   if (st != PTB_OK) return st;
+  const bool mx = recipe == PTB_FP8_MX;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
-  const Fp8SavedLayout SL = fp8_saved_layout(s);
+  const Fp8SavedLayout SL = fp8_saved_layout(s, mx);
   const SavedLayout& L = SL.base;
-  const Fp8WorkLayout W = fp8_work_layout(s);
-  const Fp8WeightLayout WL = fp8_weight_layout(s);
+  const Fp8WorkLayout W = fp8_work_layout(s, mx);
+  const Fp8WeightLayout WL = fp8_weight_layout(s, mx);
   const float* mu = at<float>(saved, L.off[PTB_SAVED_MU]);
   const float* rstd = at<float>(saved, L.off[PTB_SAVED_RSTD]);
   const u16* qkv = at<u16>(saved, L.off[PTB_SAVED_QKV]);
@@ -1104,34 +1204,25 @@ int32_t ptb_fp8_backward(const ptb_dims* dims, const void* dy, const void* x,
                             at<int>(workspace, W.base.counters), W.base.max_tiles};
   float* amax = at<float>(workspace, W.amax);
   const float* samax = at<float>(saved, SL.amax);  // the forward's: [0] a, [1] [c | g]
-  const float* wamax = at<float>(fp8_weights, WL.amax);
-  uint8_t* dy8 = at<uint8_t>(workspace, W.dy8);
-  uint8_t* dy8t = at<uint8_t>(workspace, W.dy8t);
-  const uint8_t* cg8t = at<uint8_t>(saved, SL.cg8t);
-  uint8_t* dz8 = at<uint8_t>(workspace, W.dz8);
-  uint8_t* dz8t = at<uint8_t>(workspace, W.dz8t);
-  const uint8_t* a8t = at<uint8_t>(saved, SL.a8t);
+  const float* wamax = mx ? nullptr : at<float>(fp8_weights, WL.amax);
   const u16* DY = static_cast<const u16*>(dy);
-  const size_t hp = pad128(s.h), Tp = pad128(s.T), N1p = pad128(s.N1);
   const int T = static_cast<int>(s.T), h = static_cast<int>(s.h);
 
   PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
   PTB_HIP(ptb::launch_zero_i32(reinterpret_cast<int*>(amax), AMAX_COUNT, strm));
-  PTB_STAGE(0, cast_fp8(cast_one(DY, s.h, s.T, s.h), ptb::FP8_E5M2, amax + AMAX_DY, dy8, hp,
-                        dy8t, Tp, strm));
+  PTB_STAGE(0, cast_copies(mx, cast_one(DY, s.h, s.T, s.h), ptb::FP8_E5M2, amax + AMAX_DY,
+                           copy_at(workspace, W.dy8), copy_at(workspace, W.dy8t), strm));
   {  // dgrad through [O ; FC2]: dc, and du = dg * GeLU'(u) into dZ's FC1 columns
     ptb::GemmProblem pr;
-    pr.M = T; pr.N = static_cast<int>(s.K2); pr.K = static_cast<int>(hp);
-    pr.A = one8(dy8, hp, s.T);
-    pr.B = one8(at<uint8_t>(fp8_weights, WL.w2r), hp, s.K2);
     pr.epi = ptb::Epilogue{};
     pr.epi.o0 = dc; pr.epi.ld0 = static_cast<int>(s.hl);
     pr.epi.o1 = dz; pr.epi.ld1 = static_cast<int>(s.N1);
     pr.epi.col_off1 = static_cast<int>(3 * s.hl);
     pr.epi.i0 = u; pr.epi.ld2 = static_cast<int>(s.f);
     pr.epi.split = static_cast<int>(s.hl);
-    PTB_STAGE(1, ptb::launch_gemm_fp8(pr, ptb::FP8_E5M2, amax + AMAX_DY, ptb::FP8_E4M3,
-                                      wamax + 1, ptb::EPI_DGELU, gs, strm));
+    PTB_STAGE(1, gemm8(mx, pr, copy_at(workspace, W.dy8), ptb::FP8_E5M2, amax + AMAX_DY,
+                       copy_at(fp8_weights, WL.w2r), ptb::FP8_E4M3, mx ? nullptr : wamax + 1,
+                       ptb::EPI_DGELU, gs, strm));
   }
   const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
                             gs.max_tiles, ptb::device_compute_units()};
@@ -1141,40 +1232,34 @@ int32_t ptb_fp8_backward(const ptb_dims* dims, const void* dy, const void* x,
                                     static_cast<int>(s.w), as, strm));
   {  // wgrad of [O ; FC2]: [c | g]^T dy
     ptb::GemmProblem pr;
-    pr.M = static_cast<int>(s.K2); pr.N = h; pr.K = static_cast<int>(Tp);
-    pr.A = one8(cg8t, Tp, s.K2);
-    pr.B = one8(dy8t, Tp, s.h);
     pr.epi = ptb::Epilogue{};
     pr.epi.o0 = static_cast<u16*>(dw_o); pr.epi.ld0 = h;
     pr.epi.o1 = static_cast<u16*>(dw_fc2); pr.epi.ld1 = h;
     pr.epi.split = static_cast<int>(s.hl);
-    PTB_STAGE(3, ptb::launch_gemm_fp8(pr, ptb::FP8_E4M3, samax + 1, ptb::FP8_E5M2,
-                                      amax + AMAX_DY, ptb::EPI_STORE2_ROWS, gs, strm));
+    PTB_STAGE(3, gemm8(mx, pr, copy_at(saved, SL.cg8t), ptb::FP8_E4M3, samax + 1,
+                       copy_at(workspace, W.dy8t), ptb::FP8_E5M2, amax + AMAX_DY,
+                       ptb::EPI_STORE2_ROWS, gs, strm));
   }
-  PTB_STAGE(4, cast_fp8(cast_one(dz, s.N1, s.T, s.N1), ptb::FP8_E5M2, amax + AMAX_DZ, dz8, N1p,
-                        dz8t, Tp, strm));
+  PTB_STAGE(4, cast_copies(mx, cast_one(dz, s.N1, s.T, s.N1), ptb::FP8_E5M2, amax + AMAX_DZ,
+                           copy_at(workspace, W.dz8), copy_at(workspace, W.dz8t), strm));
   {  // dgrad through [QKV | FC1]: da = dZ W1^T
     ptb::GemmProblem pr;
-    pr.M = T; pr.N = h; pr.K = static_cast<int>(N1p);
-    pr.A = one8(dz8, N1p, s.T);
-    pr.B = one8(at<uint8_t>(fp8_weights, WL.w1r), N1p, s.h);
     pr.epi = ptb::Epilogue{};
     pr.epi.o0 = da; pr.epi.ld0 = h;
     pr.epi.split = h;  // one output
-    PTB_STAGE(5, ptb::launch_gemm_fp8(pr, ptb::FP8_E5M2, amax + AMAX_DZ, ptb::FP8_E4M3,
-                                      wamax, ptb::EPI_STORE2_COLS, gs, strm));
+    PTB_STAGE(5, gemm8(mx, pr, copy_at(workspace, W.dz8), ptb::FP8_E5M2, amax + AMAX_DZ,
+                       copy_at(fp8_weights, WL.w1r), ptb::FP8_E4M3, wamax,
+                       ptb::EPI_STORE2_COLS, gs, strm));
   }
   {  // wgrad of [QKV | FC1]: a^T dZ
     ptb::GemmProblem pr;
-    pr.M = h; pr.N = static_cast<int>(s.N1); pr.K = static_cast<int>(Tp);
-    pr.A = one8(a8t, Tp, s.h);
-    pr.B = one8(dz8t, Tp, s.N1);
     pr.epi = ptb::Epilogue{};
     pr.epi.o0 = static_cast<u16*>(dw_qkv); pr.epi.ld0 = static_cast<int>(3 * s.hl);
     pr.epi.o1 = static_cast<u16*>(dw_fc1); pr.epi.ld1 = static_cast<int>(s.f);
     pr.epi.split = static_cast<int>(3 * s.hl);
-    PTB_STAGE(6, ptb::launch_gemm_fp8(pr, ptb::FP8_E4M3, samax, ptb::FP8_E5M2,
-                                      amax + AMAX_DZ, ptb::EPI_STORE2_COLS, gs, strm));
+    PTB_STAGE(6, gemm8(mx, pr, copy_at(saved, SL.a8t), ptb::FP8_E4M3, samax,
+                       copy_at(workspace, W.dz8t), ptb::FP8_E5M2, amax + AMAX_DZ,
+                       ptb::EPI_STORE2_COLS, gs, strm));
   }
   PTB_STAGE(7, ptb::launch_layernorm_bwd(da, static_cast<const u16*>(x),
                                     static_cast<const u16*>(ln_gamma), mu, rstd, DY,

@@ -74,6 +74,7 @@ class ptb_lamb_tensor(ctypes.Structure):
 _lib: Optional[ctypes.CDLL] = None
 _P = ctypes.c_void_p
 _D = ctypes.POINTER(ptb_dims)
+_I = ctypes.c_int32
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -115,15 +116,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ptb_lamb_step": (ctypes.c_int32, [ctypes.POINTER(ptb_lamb_hyper),
                                            ctypes.POINTER(ptb_lamb_tensor), ctypes.c_int32,
                                            _P, _P, _P]),
-        "ptb_fp8_weights_bytes": (ctypes.c_int32, [_D, ctypes.POINTER(ctypes.c_size_t)]),
-        "ptb_fp8_weights_layout": (ctypes.c_int32, [_D, ctypes.POINTER(ctypes.c_size_t)]),
-        "ptb_fp8_quantize": (ctypes.c_int32, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                              _P, _P, _P, _P]),
-        "ptb_fp8_workspace_bytes": (ctypes.c_int32, [_D, ctypes.POINTER(ctypes.c_size_t)]),
-        "ptb_fp8_saved_bytes": (ctypes.c_int32, [_D, ctypes.POINTER(ctypes.c_size_t)]),
-        "ptb_fp8_cast_weights": (ctypes.c_int32, [_D] + [_P] * 6),
-        "ptb_fp8_forward": (ctypes.c_int32, [_D] + [_P] * 9),
-        "ptb_fp8_backward": (ctypes.c_int32, [_D] + [_P] * 15),
+        "ptb_fp8_weights_bytes": (ctypes.c_int32, [_D, _I, ctypes.POINTER(ctypes.c_size_t)]),
+        "ptb_fp8_weights_layout": (ctypes.c_int32, [_D, _I, ctypes.POINTER(ctypes.c_size_t)]),
+        "ptb_fp8_quantize": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _P]),
+        "ptb_fp8_quantize_mx": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _P, _P]),
+        "ptb_fp8_workspace_bytes": (ctypes.c_int32, [_D, _I, ctypes.POINTER(ctypes.c_size_t)]),
+        "ptb_fp8_saved_bytes": (ctypes.c_int32, [_D, _I, ctypes.POINTER(ctypes.c_size_t)]),
+        "ptb_fp8_cast_weights": (ctypes.c_int32, [_D, _I] + [_P] * 6),
+        "ptb_fp8_forward": (ctypes.c_int32, [_D, _I] + [_P] * 9),
+        "ptb_fp8_backward": (ctypes.c_int32, [_D, _I] + [_P] * 15),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -359,20 +360,34 @@ FP8_BWD_STAGE_NAMES = ("cast_dy", "gemm_dgrad_o_fc2_fp8", "attention_bwd",
                        "gemm_wgrad_qkv_fc1_fp8", "layernorm_bwd")
 
 
-def ptb_fp8_weights_bytes(dims: ptb_dims) -> int:
+FP8_RECIPES = {"current": 0, "mx": 1}
+FP8_WEIGHT_PARTS = ("amax", "w1t", "w1", "w2t", "w2", "w1t_s", "w1_s", "w2t_s", "w2_s")
+FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
+FP8_ABSENT = ctypes.c_size_t(-1).value  # offset of a part the recipe does not use
+
+
+def _size_query(name: str, dims: ptb_dims, recipe: str) -> int:
     n = ctypes.c_size_t(0)
-    _done(load_library().ptb_fp8_weights_bytes(ctypes.byref(dims), ctypes.byref(n)),
-          "ptb_fp8_weights_bytes", True)
+    _done(getattr(load_library(), name)(ctypes.byref(dims), FP8_RECIPES[recipe], ctypes.byref(n)),
+          name, True)
     return n.value
 
 
-FP8_WEIGHT_PARTS = ("amax", "w1t", "w1", "w2t", "w2")
-FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
+def ptb_fp8_weights_bytes(dims: ptb_dims, recipe: str = "current") -> int:
+    return _size_query("ptb_fp8_weights_bytes", dims, recipe)
 
 
-def ptb_fp8_weights_layout(dims: ptb_dims) -> dict:
+def ptb_fp8_saved_bytes(dims: ptb_dims, recipe: str = "current") -> int:
+    return _size_query("ptb_fp8_saved_bytes", dims, recipe)
+
+
+def ptb_fp8_workspace_bytes(dims: ptb_dims, recipe: str = "current") -> int:
+    return _size_query("ptb_fp8_workspace_bytes", dims, recipe)
+
+
+def ptb_fp8_weights_layout(dims: ptb_dims, recipe: str = "current") -> dict:
     arr = (ctypes.c_size_t * len(FP8_WEIGHT_PARTS))()
-    _done(load_library().ptb_fp8_weights_layout(ctypes.byref(dims), arr),
+    _done(load_library().ptb_fp8_weights_layout(ctypes.byref(dims), FP8_RECIPES[recipe], arr),
           "ptb_fp8_weights_layout", True)
     return dict(zip(FP8_WEIGHT_PARTS, list(arr)))
 
@@ -384,43 +399,40 @@ def ptb_fp8_quantize(x, rows: int, cols: int, fmt: str, amax, q, qt, stream=None
     return _done(st, "ptb_fp8_quantize", check)
 
 
-def ptb_fp8_saved_bytes(dims: ptb_dims) -> int:
-    n = ctypes.c_size_t(0)
-    _done(load_library().ptb_fp8_saved_bytes(ctypes.byref(dims), ctypes.byref(n)),
-          "ptb_fp8_saved_bytes", True)
-    return n.value
-
-
-def ptb_fp8_workspace_bytes(dims: ptb_dims) -> int:
-    n = ctypes.c_size_t(0)
-    _done(load_library().ptb_fp8_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)),
-          "ptb_fp8_workspace_bytes", True)
-    return n.value
+def ptb_fp8_quantize_mx(x, rows: int, cols: int, fmt: str, q, q_scales, qt, qt_scales,
+                        stream=None, check: bool = True) -> int:
+    st = load_library().ptb_fp8_quantize_mx(_ptr(x), rows, cols, FP8_FORMATS[fmt], _ptr(q),
+                                            _ptr(q_scales), _ptr(qt), _ptr(qt_scales),
+                                            _stream(stream))
+    return _done(st, "ptb_fp8_quantize_mx", check)
 
 
 def ptb_fp8_cast_weights(dims: ptb_dims, w_qkv, w_o, w_fc1, w_fc2, fp8_weights, stream=None,
-                         check: bool = True) -> int:
+                         check: bool = True, recipe: str = "current") -> int:
     st = load_library().ptb_fp8_cast_weights(
-        ctypes.byref(dims), _ptr(w_qkv), _ptr(w_o), _ptr(w_fc1), _ptr(w_fc2), _ptr(fp8_weights),
-        _stream(stream))
+        ctypes.byref(dims), FP8_RECIPES[recipe], _ptr(w_qkv), _ptr(w_o), _ptr(w_fc1),
+        _ptr(w_fc2), _ptr(fp8_weights), _stream(stream))
     return _done(st, "ptb_fp8_cast_weights", check)
 
 
 def ptb_fp8_forward(dims: ptb_dims, x, ln_gamma, ln_beta, fp8_weights, y, saved, workspace,
-                    stream=None, stage_events=None, check: bool = True) -> int:
+                    stream=None, stage_events=None, check: bool = True,
+                    recipe: str = "current") -> int:
     st = load_library().ptb_fp8_forward(
-        ctypes.byref(dims), _ptr(x), _ptr(ln_gamma), _ptr(ln_beta), _ptr(fp8_weights), _ptr(y),
-        _ptr(saved), _ptr(workspace), _stream(stream), _events(stage_events))
+        ctypes.byref(dims), FP8_RECIPES[recipe], _ptr(x), _ptr(ln_gamma), _ptr(ln_beta),
+        _ptr(fp8_weights), _ptr(y), _ptr(saved), _ptr(workspace), _stream(stream),
+        _events(stage_events))
     return _done(st, "ptb_fp8_forward", check)
 
 
 def ptb_fp8_backward(dims: ptb_dims, dy, x, ln_gamma, fp8_weights, saved, dx, d_ln_gamma,
                      d_ln_beta, dw_qkv, dw_o, dw_fc1, dw_fc2, workspace, stream=None,
-                     stage_events=None, check: bool = True) -> int:
+                     stage_events=None, check: bool = True, recipe: str = "current") -> int:
     st = load_library().ptb_fp8_backward(
-        ctypes.byref(dims), _ptr(dy), _ptr(x), _ptr(ln_gamma), _ptr(fp8_weights), _ptr(saved),
-        _ptr(dx), _ptr(d_ln_gamma), _ptr(d_ln_beta), _ptr(dw_qkv), _ptr(dw_o), _ptr(dw_fc1),
-        _ptr(dw_fc2), _ptr(workspace), _stream(stream), _events(stage_events))
+        ctypes.byref(dims), FP8_RECIPES[recipe], _ptr(dy), _ptr(x), _ptr(ln_gamma),
+        _ptr(fp8_weights), _ptr(saved), _ptr(dx), _ptr(d_ln_gamma), _ptr(d_ln_beta),
+        _ptr(dw_qkv), _ptr(dw_o), _ptr(dw_fc1), _ptr(dw_fc2), _ptr(workspace), _stream(stream),
+        _events(stage_events))
     return _done(st, "ptb_fp8_backward", check)
 
 
@@ -431,6 +443,7 @@ def exported_symbols() -> Sequence[str]:
             "ptb_serial_workspace_bytes", "ptb_serial_saved_layout", "ptb_serial_forward",
             "ptb_serial_backward", "ptb_serial_forward_timed", "ptb_serial_backward_timed",
             "ptb_lamb_workspace_bytes", "ptb_lamb_step", "ptb_fp8_weights_bytes",
-            "ptb_fp8_weights_layout", "ptb_fp8_quantize", "ptb_fp8_saved_bytes",
+            "ptb_fp8_weights_layout", "ptb_fp8_quantize", "ptb_fp8_quantize_mx",
+            "ptb_fp8_saved_bytes",
             "ptb_fp8_workspace_bytes", "ptb_fp8_cast_weights", "ptb_fp8_forward",
             "ptb_fp8_backward")

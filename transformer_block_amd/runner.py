@@ -173,24 +173,27 @@ class SerialBlock:
 
 class Fp8Layer:
     """One parallel block with its four GEMM parts in FP8 (include/ptb.h,
-    ptb_fp8_*).  A step is the weight cast, the forward and the backward: the
-    weights change at every optimizer step, so their FP8 copies do too."""
+    ptb_fp8_*), scaled by `recipe`: "current" (one scale per operand) or "mx"
+    (block scales).  A step is the weight cast, the forward and the backward:
+    the weights change at every optimizer step, so their FP8 copies do too."""
 
-    def __init__(self, w: Workload, inputs: dict, device: str = "cuda"):
+    def __init__(self, w: Workload, inputs: dict, device: str = "cuda", recipe: str = "current"):
         if w.layers != 1:
             raise ValueError("Fp8Layer runs one layer")
         self.w = w
+        self.recipe = recipe
         self.dims = P.dims_of(w)
         dev = torch.device(device)
         self.x = to_device_bf16(inputs["x"], dev)
         self.dy = to_device_bf16(inputs["dy"], dev)
         lay = inputs["layers"][0]
         self.p = {k: to_device_bf16(lay[k], dev) for k in PARAM_NAMES}
-        self.fp8_weights = torch.empty(P.ptb_fp8_weights_bytes(self.dims), dtype=torch.uint8,
-                                       device=dev)
-        self.saved = torch.empty(P.ptb_fp8_saved_bytes(self.dims), dtype=torch.uint8, device=dev)
-        self.workspace = torch.empty(P.ptb_fp8_workspace_bytes(self.dims), dtype=torch.uint8,
-                                     device=dev)
+        self.fp8_weights = torch.empty(P.ptb_fp8_weights_bytes(self.dims, recipe),
+                                       dtype=torch.uint8, device=dev)
+        self.saved = torch.empty(P.ptb_fp8_saved_bytes(self.dims, recipe), dtype=torch.uint8,
+                                 device=dev)
+        self.workspace = torch.empty(P.ptb_fp8_workspace_bytes(self.dims, recipe),
+                                     dtype=torch.uint8, device=dev)
         self.y = torch.empty_like(self.x)
         self.dx = torch.empty_like(self.x)
         p = self.p
@@ -203,18 +206,20 @@ class Fp8Layer:
     def cast_weights(self, stream=None) -> None:
         p = self.p
         P.ptb_fp8_cast_weights(self.dims, p["w_qkv"], p["w_o"], p["w_fc1"], p["w_fc2"],
-                               self.fp8_weights, stream)
+                               self.fp8_weights, stream, recipe=self.recipe)
 
     def forward(self, stream=None, events=None) -> None:
         p = self.p
         P.ptb_fp8_forward(self.dims, self.x, p["ln_gamma"], p["ln_beta"], self.fp8_weights,
-                          self.y, self.saved, self.workspace, stream, events)
+                          self.y, self.saved, self.workspace, stream, events,
+                          recipe=self.recipe)
 
     def backward(self, stream=None, events=None) -> None:
         p, g = self.p, self.grads
         P.ptb_fp8_backward(self.dims, self.dy, self.x, p["ln_gamma"], self.fp8_weights,
                            self.saved, self.dx, g["d_ln_gamma"], g["d_ln_beta"], g["dw_qkv"],
-                           g["dw_o"], g["dw_fc1"], g["dw_fc2"], self.workspace, stream, events)
+                           g["dw_o"], g["dw_fc1"], g["dw_fc2"], self.workspace, stream, events,
+                           recipe=self.recipe)
 
     def step(self, stream=None, fwd_events=None, bwd_events=None) -> None:
         self.cast_weights(stream)
