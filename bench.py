@@ -33,7 +33,9 @@ Prints one JSON line.  Besides the throughput it carries:
                 post, mixed-precision section), the weight cast included in
                 the step, model FLOPs as for `value`, with its own roofline
                 (dominant FP8 product against the 5.0 PFLOP/s dense FP8
-                peak); --no-fp8 skips it.
+                peak);
+  fp8_mx:       the same with block (MX) scaling (E8M0 scale per 32
+                values, applied by the matrix cores); --no-fp8 skips both.
                 None of these legs is part of `value`.
 
 roofline.traffic is the HBM bytes per launch of the dominant kernel as read
@@ -289,17 +291,18 @@ def time_variant(w, warmup: int, steps: int, base_ms: float) -> dict:
             "model_flops_per_step": F, "stages_ms": stages}
 
 
-def time_fp8(w, inp, warmup: int, steps: int, base_ms: float) -> dict:
-    """The FP8-GEMM layer on the same inputs: mean ms per step (weight cast,
-    forward, backward) and per stage, HIP events on one stream."""
+def time_fp8(w, inp, warmup: int, steps: int, base_ms: float, recipe: str = "current") -> dict:
+    """The FP8-GEMM layer on the same inputs, scaled by `recipe`: mean ms per
+    step (weight cast, forward, backward) and per stage, HIP events on one
+    stream."""
     import torch
 
     from transformer_block_amd import ptb as P
     from transformer_block_amd.flops import workload_model_flops
     from transformer_block_amd.runner import Fp8Layer
 
-    print("bench: timing the FP8 GEMM variant", file=sys.stderr, flush=True)
-    lyr = Fp8Layer(w, inp, "cuda")
+    print(f"bench: timing the FP8 GEMM variant ({recipe} scaling)", file=sys.stderr, flush=True)
+    lyr = Fp8Layer(w, inp, "cuda", recipe)
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         lyr.step(stream)
@@ -342,7 +345,9 @@ def time_fp8(w, inp, warmup: int, steps: int, base_ms: float) -> dict:
             "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": None, "kernel": dom,
             "per_launch": flops, "ms_per_launch": stages[dom]}
     del lyr
-    return {"formats": "E4M3 fwd / E5M2 grad, per-operand current scaling",
+    scaling = {"current": "per-operand current scaling",
+               "mx": "block (MX) scaling, E8M0 per 32 values"}[recipe]
+    return {"formats": f"E4M3 fwd / E5M2 grad, {scaling}",
             "ms_per_step": round(ms, 4), "value": round(tflops, 2), "unit": "TFLOP/s",
             "mfu_vs_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
             "frac_of_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4),
@@ -524,6 +529,7 @@ def main() -> int:
         out["variant"] = time_variant(w, args.warmup, K, ms_step)
     if not args.no_fp8 and w.layers == 1:
         out["fp8"] = time_fp8(w, inp, args.warmup, K, ms_step)
+        out["fp8_mx"] = time_fp8(w, inp, args.warmup, K, ms_step, "mx")
     if not args.no_cpu_baseline:
         print("bench: timing the fp64 oracle on host cores", file=sys.stderr, flush=True)
         cb = cpu_baseline(w, args.cpu_budget_s)

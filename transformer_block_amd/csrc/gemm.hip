@@ -646,28 +646,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(fa[slot][i], fb[slot][j], acc[i][j]);
   };
-  // FP8: the 32 bytes of bf16 k-steps 2 half and 2 half + 1 (64 k-values):
-  // lane half h holds k [64 half + 16 h, +16) and [64 half + 32 + 16 h, +16)
-  // of the stage tile, so the matrix cores' k-block b of this half is the
-  // tile's 32-wide block 2 half + b.  MX: the scale codes of that block
-  // for the lane's row in each of its fragments, packed one byte per
-  // fragment (sa8: A fragment i in byte i, sb8: B fragment j in byte j); the
-  // MFMA's byte selects are immediates.
+  // FP8: the 32 bytes of bf16 k-steps 2 half and 2 half + 1 (64 k-values)
   i32x8 ga[2][FM], gb[2][FN];
-  uint32_t sa8[2], sb8[2];
   auto rd8 = [&](const u16* st, int half, int slot) {
     const int k0 = koff[2 * half], k1 = koff[2 * half + 1];
-    if constexpr (MX) {
-      const uint32_t* sw = sring + ((st - ring) / STAGE) * (2 * TILE) + (lane & 31);
-      const uint32_t bit = 16 * half + 8 * (lane >> 5);  // byte 2 half + h of the row's word
-      uint32_t pa = 0, pb = 0;
-#pragma unroll
-      for (int i = 0; i < FM; ++i) pa |= ((sw[wm * WM + i * 32] >> bit) & 0xffu) << (8 * i);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) pb |= ((sw[TILE + wn * WN + j * 32] >> bit) & 0xffu) << (8 * j);
-      sa8[slot] = pa;
-      sb8[slot] = pb;
-    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const u16* t = st + (wm * WM + i * 32) * BK;
@@ -685,21 +667,65 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        if constexpr (!MX)
-          acc[i][j] = mfma32x32x64_f8<FA, FB>(ga[slot][i], gb[slot][j], acc[i][j]);
-        else
-          acc[i][j] = mx_step<FA, FB>(i, j, ga[slot][i], gb[slot][j], acc[i][j], sa8[slot], sb8[slot]);
-      }
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = mfma32x32x64_f8<FA, FB>(ga[slot][i], gb[slot][j], acc[i][j]);
   };
   auto pin8 = [&]() {
-    constexpr int R = (MX ? 3 : 2) * (FM + FN);
+    constexpr int R = 2 * (FM + FN);
 #pragma unroll
     for (int i = 0; i < FM * FN; ++i) {
       __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
       __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, R - FM * FN, 0);
+  };
+  // MX.  Lane half h holds k [64 half + 16 h, +16) and [64 half + 32 + 16 h,
+  // +16) of the stage tile, so the matrix cores' k-block b of this half is
+  // the tile's 32-wide block 2 half + b, whose scale they take from lane half
+  // b: each lane reads byte 2 half + h of its row's scale word.  The scaled
+  // MFMA needs about 20 registers more than the plain one, so the A fragments
+  // are single-buffered here: fragment i is read again, for the next half,
+  // right after its last MFMA, with the other fragments' MFMAs to cover the
+  // read; the B fragments stay double-buffered.
+  uint32_t xsa[FM], xsb[2][FN];
+  const uint8_t* const sbytes = reinterpret_cast<const uint8_t*>(sring);
+  auto xbyte = [&](int stage, int row, int half) -> uint32_t {
+    return sbytes[(stage * 2 * TILE + row) * 4 + 2 * half + (lane >> 5)];
+  };
+  auto xrdA = [&](const u16* st, int stage, int half, int i) {
+    const u16* t = st + (wm * WM + i * 32) * BK;
+    ga[0][i] = cat8(*reinterpret_cast<const uint4*>(t + koff[2 * half]),
+                    *reinterpret_cast<const uint4*>(t + koff[2 * half + 1]));
+    xsa[i] = xbyte(stage, wm * WM + i * 32 + (lane & 31), half);
+  };
+  auto xrdB = [&](const u16* st, int stage, int half, int slot) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const u16* t = st + TILE * BK + (wn * WN + j * 32) * BK;
+      gb[slot][j] = cat8(*reinterpret_cast<const uint4*>(t + koff[2 * half]),
+                         *reinterpret_cast<const uint4*>(t + koff[2 * half + 1]));
+      xsb[slot][j] = xbyte(stage, TILE + wn * WN + j * 32 + (lane & 31), half);
+    }
+  };
+  // one half-step: the MFMAs of A fragment i against both B fragments, then
+  // fragment i of the next half (tile st, half `half`)
+  auto xhalf = [&](int slot, const u16* st, int stage, int half) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = mfma32x32x64_f8_mx<FA, FB, 0, 0>(ga[0][i], gb[slot][j], acc[i][j], xsa[i],
+                                                     xsb[slot][j]);
+      xrdA(st, stage, half, i);
+    }
+  };
+  auto xpin = [&]() {
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 3 * FN, 0);  // next B fragments + scales
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, FN, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 3, 0);  // next A fragment i + scale
+    }
   };
   // LDS reads of the next k-step spread between this k-step's MFMAs
   auto pin = [&]() {
@@ -736,7 +762,26 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    if constexpr (F8) {
+    if constexpr (MX) {
+      // two scaled FP8 MFMA half-steps of 64 k per stage tile
+#pragma unroll
+      for (int i = 0; i < FM; ++i) xrdA(ring, 0, 0, i);
+      xrdB(ring, 0, 0, 0);
+      for (int j = 0; j < len; ++j) {
+        const int stg = j & 1, nst = (j + 1) & 1;
+        const u16* cur = ring + stg * STAGE;
+        xrdB(cur, stg, 1, 1);
+        xhalf(0, cur, stg, 1);
+        xpin();
+        wait_vm_lds<0>();
+        __syncthreads();
+        issue_to(s, j & 1, j + 2);
+        const u16* nxt = ring + nst * STAGE;
+        xrdB(nxt, nst, 0, 0);  // unused after the last step
+        xhalf(1, nxt, nst, 0);
+        xpin();
+      }
+    } else if constexpr (F8) {
       // the same pipeline with two FP8 MFMA steps of 64 k per stage tile
       rd8(ring, 0, 0);
       for (int j = 0; j < len; ++j) {
