@@ -76,6 +76,22 @@ __device__ __forceinline__ f32x16 mfma32x32x64_f8_mx(i32x8 a, i32x8 b, f32x16 c,
 }
 
 
+// The scaled MFMA with A's scale in byte i of sa and B's in byte j of sb
+// (i < 4, j < 2 known at compile time after unrolling).
+template <int FA, int FB>
+__device__ __forceinline__ f32x16 mx_step(int i, int j, i32x8 a, i32x8 b, f32x16 c, uint32_t sa,
+                                          uint32_t sb) {
+  if (j == 0) {
+    if (i == 0) return mfma32x32x64_f8_mx<FA, FB, 0, 0>(a, b, c, sa, sb);
+    if (i == 1) return mfma32x32x64_f8_mx<FA, FB, 1, 0>(a, b, c, sa, sb);
+    if (i == 2) return mfma32x32x64_f8_mx<FA, FB, 2, 0>(a, b, c, sa, sb);
+    return mfma32x32x64_f8_mx<FA, FB, 3, 0>(a, b, c, sa, sb);
+  }
+  if (i == 0) return mfma32x32x64_f8_mx<FA, FB, 0, 1>(a, b, c, sa, sb);
+  if (i == 1) return mfma32x32x64_f8_mx<FA, FB, 1, 1>(a, b, c, sa, sb);
+  if (i == 2) return mfma32x32x64_f8_mx<FA, FB, 2, 1>(a, b, c, sa, sb);
+  return mfma32x32x64_f8_mx<FA, FB, 3, 1>(a, b, c, sa, sb);
+}
 // Largest finite value of the 8-bit formats: E4M3 448, E5M2 57344.
 __device__ __forceinline__ constexpr float fp8_max(int fmt) { return fmt ? 57344.0f : 448.0f; }
 

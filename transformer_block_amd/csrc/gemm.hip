@@ -559,6 +559,12 @@ template <int AMAJ, int BMAJ, int MODE, int FMT = 0, bool MX = false>
 __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
   constexpr bool F8 = FMT != 0;
   static_assert(!MX || F8, "block scales come with FP8 operands");
+  // MX loop: XS single-buffers the A fragments (below); the other MX modes
+  // keep the double-buffered FP8 loop with packed scale bytes.  Each mode
+  // takes the variant that measured faster for it: the scaled MFMA leaves
+  // the kernel short of registers either way, and the epilogue decides how
+  // the spills fall.
+  constexpr bool XS = MX && (MODE == EPI_QKV_GELU || MODE == EPI_DGELU);
   constexpr int FA = F8 ? (FMT - 1) & 1 : 0, FB = F8 ? (FMT - 1) >> 1 : 0;
   constexpr int ESZ = F8 ? 1 : 2;          // operand bytes per element
   constexpr int KSTEP = BK * 2 / ESZ;      // k-values per stage tile (128-byte rows)
@@ -646,10 +652,27 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(fa[slot][i], fb[slot][j], acc[i][j]);
   };
-  // FP8: the 32 bytes of bf16 k-steps 2 half and 2 half + 1 (64 k-values)
+  // FP8: the 32 bytes of bf16 k-steps 2 half and 2 half + 1 (64 k-values).
+  // MX (double-buffered loop): the scale codes of the lane's row in each
+  // fragment, for the block the matrix cores take from this lane (byte
+  // 2 half + h of the row's word, see below), packed one byte per fragment
+  // (sa8: A fragment i in byte i, sb8: B fragment j in byte j) for the
+  // MFMA's immediate byte selects.
   i32x8 ga[2][FM], gb[2][FN];
+  uint32_t sa8[2], sb8[2];
   auto rd8 = [&](const u16* st, int half, int slot) {
     const int k0 = koff[2 * half], k1 = koff[2 * half + 1];
+    if constexpr (MX && !XS) {
+      const uint32_t* sw = sring + ((st - ring) / STAGE) * (2 * TILE) + (lane & 31);
+      const uint32_t bit = 16 * half + 8 * (lane >> 5);
+      uint32_t pa = 0, pb = 0;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) pa |= ((sw[wm * WM + i * 32] >> bit) & 0xffu) << (8 * i);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) pb |= ((sw[TILE + wn * WN + j * 32] >> bit) & 0xffu) << (8 * j);
+      sa8[slot] = pa;
+      sb8[slot] = pb;
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const u16* t = st + (wm * WM + i * 32) * BK;
@@ -667,11 +690,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = mfma32x32x64_f8<FA, FB>(ga[slot][i], gb[slot][j], acc[i][j]);
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (!MX)
+          acc[i][j] = mfma32x32x64_f8<FA, FB>(ga[slot][i], gb[slot][j], acc[i][j]);
+        else
+          acc[i][j] = mx_step<FA, FB>(i, j, ga[slot][i], gb[slot][j], acc[i][j], sa8[slot], sb8[slot]);
+      }
   };
   auto pin8 = [&]() {
-    constexpr int R = 2 * (FM + FN);
+    constexpr int R = (MX ? 3 : 2) * (FM + FN);
 #pragma unroll
     for (int i = 0; i < FM * FN; ++i) {
       __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
@@ -762,7 +789,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    if constexpr (MX) {
+    if constexpr (XS) {
       // two scaled FP8 MFMA half-steps of 64 k per stage tile
 #pragma unroll
       for (int i = 0; i < FM; ++i) xrdA(ring, 0, 0, i);
