@@ -7,7 +7,9 @@ one MI355X, in model TFLOP/s and as a fraction of the dense bf16 MFMA peak.
 A step is one forward and one backward of the whole layer stack of the
 workload (every kernel of the hot path) on resident, seeded synthetic bf16
 inputs.  W untimed warm-up steps, then exactly K steps between two
-device-synchronised HIP events.  Model FLOPs follow the Megatron tuning post's
+device-synchronised HIP events, with one more event at each step boundary
+(the median step is reported beside the mean); per-stage times come from a
+separate pass of K steps with events around every stage.  Model FLOPs follow the Megatron tuning post's
 MFU section (6 per weight per token plus the attention term, recompute
 excluded) made exact for the sliding window (transformer_block_amd/flops.py).
 
@@ -59,9 +61,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
-PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
-PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
+# MI355X dense peaks: 256 CUs x 2.4 GHz x 4096 bf16 FLOP per clock per CU
+# (published as 2.5 PFLOP/s), twice that for FP8; HBM3E 8 TB/s.
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5033.2
 METRIC = "model TFLOP/s + MFU vs bf16 MFMA peak, PTB layer fwd+bwd, 1 MI355X"
 DEFAULT_WORKLOAD = "gpt175b_tp8_share_s2048"
 
@@ -204,7 +208,19 @@ def cpu_baseline(w, budget_s: float):
             "sample": f"one layer fwd+bwd at batch {sw.batch}, seq {sw.seq}, window "
                       f"{min(sw.window, sw.seq)} (hidden {sw.hidden}, heads {sw.heads}x"
                       f"{sw.head_dim}, ffn {sw.ffn}); fp64 numpy; {dt:.1f} s wall",
-            "seconds": dt}
+            "seconds": dt, "nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model(), "blas_threads": int(threads)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def time_serial(w, inp, warmup: int, steps: int, ptb_ms: float) -> dict:
@@ -455,21 +471,32 @@ def main() -> int:
 
     L = w.layers
     K = args.steps
-    fwd_ev = [[ev.create(2 * P.PTB_FWD_STAGES) for _ in range(L)] for _ in range(K)]
-    bwd_ev = [[ev.create(2 * P.PTB_BWD_STAGES) for _ in range(L)] for _ in range(K)]
-    t_start, t_end = ev.create(2)
-    torch.cuda.synchronize()
     hip = ev.hip
     hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    # The timed region: K steps with one HIP event at each step boundary and
+    # nothing else inside it.
+    bounds = ev.create(K + 1)
+    torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    hip.hipEventRecord(t_start, stream.cuda_stream)
+    hip.hipEventRecord(bounds[0], stream.cuda_stream)
     for k in range(K):
-        st.step(stream, fwd_ev[k], bwd_ev[k])
-    hip.hipEventRecord(t_end, stream.cuda_stream)
+        st.step(stream)
+        hip.hipEventRecord(bounds[k + 1], stream.cuda_stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = ev.ms(t_start, t_end) / K
+    ms_step = ev.ms(bounds[0], bounds[K]) / K
+    per_step = sorted(ev.ms(bounds[k], bounds[k + 1]) for k in range(K))
+    ms_median = per_step[K // 2] if K % 2 else 0.5 * (per_step[K // 2 - 1] + per_step[K // 2])
 
+    # Per-kernel times come from a separate pass of K steps with HIP events
+    # around every stage (each GEMM stage is one launch).
+    print("bench: stage pass", file=sys.stderr, flush=True)
+    fwd_ev = [[ev.create(2 * P.PTB_FWD_STAGES) for _ in range(L)] for _ in range(K)]
+    bwd_ev = [[ev.create(2 * P.PTB_BWD_STAGES) for _ in range(L)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for k in range(K):
+        st.step(stream, fwd_ev[k], bwd_ev[k])
+    torch.cuda.synchronize()
     fwd_work, bwd_work = stage_work(w)
     stages = {}
     for names, evs in ((P.FWD_STAGE_NAMES, fwd_ev), (P.BWD_STAGE_NAMES, bwd_ev)):
@@ -517,9 +544,12 @@ def main() -> int:
                    "window": w.window, "layers": w.layers, "model_flops_per_step": F},
         "mfu": round(tflops / PEAK_BF16_TFLOPS, 4),
         "hfu": round((F + R) / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "ms_per_step_median": round(ms_median, 4),
+        "mfu_median": round(F / (ms_median * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "stages_from": f"a separate pass of {K} steps with HIP events around each stage",
     }
     if not args.no_serial and w.layers == 1:
         out["serial_block"] = time_serial(w, inp, args.warmup, K, ms_step)
