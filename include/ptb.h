@@ -36,9 +36,12 @@
  *
  * Ownership and lifetime.  The caller allocates and owns every buffer,
  * including `saved` (ptb_saved_bytes) and `workspace` (ptb_workspace_bytes).
- * The library allocates nothing and holds no mutable global state, so calls
- * on different streams with different buffers (workspace included) may run
- * concurrently.  `saved` is written by ptb_forward and read by ptb_backward;
+ * The library allocates nothing.  Its only mutable global state is a
+ * per-device cache of the compute-unit count (set once, with the same value,
+ * by whichever call comes first) and, for the one allocation-free call
+ * (ptb_lamb_step_noalloc), the per-device address of its static scratch
+ * array.  Calls on different streams with different buffers (workspace
+ * included) may run concurrently.  `saved` is written by ptb_forward and read by ptb_backward;
  * it must stay untouched in between.  `workspace` is scratch for the duration
  * of one call: its contents need no initialisation and are not kept.
  * Outputs are overwritten, never accumulated into.
@@ -62,7 +65,7 @@
 extern "C" {
 #endif
 
-#define PTB_ABI_VERSION 7
+#define PTB_ABI_VERSION 8
 
 enum ptb_status {
   PTB_OK = 0,
@@ -74,8 +77,10 @@ enum ptb_status {
   PTB_ERR_WINDOW = -5,    /* window < 1                                         */
   PTB_ERR_EPS = -6,       /* ln_eps is not a finite positive number             */
   PTB_ERR_HIP = -7,       /* a kernel launch failed                             */
-  PTB_ERR_ARG = -8        /* invalid layer variant (norm, mlp), optimizer
+  PTB_ERR_ARG = -8,       /* invalid layer variant (norm, mlp), optimizer
                              hyper-parameters or tensor list                    */
+  PTB_ERR_SCRATCH = -9    /* an allocation-free call needs more scratch than
+                             the library's static buffer holds                 */
 };
 
 typedef struct ptb_dims {
@@ -349,6 +354,22 @@ int32_t ptb_lamb_workspace_bytes(const ptb_lamb_tensor* tensors, int32_t n, size
  * deterministic (fixed reduction order). */
 int32_t ptb_lamb_step(const ptb_lamb_hyper* hyper, const ptb_lamb_tensor* tensors, int32_t n,
                       float* norms, void* workspace, void* stream);
+
+/* The same step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight training loops, harnesses that forbid hipMalloc.
+ * It takes no workspace: its scratch (two fp64 partial sums per 16384
+ * elements of each tensor) lives in a static device array of
+ * PTB_LAMB_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds
+ * from the first such call until the process ends (its address is looked up
+ * once per device).  It calls no allocating routine.  Calls whose
+ * ptb_lamb_workspace_bytes exceed that size return PTB_ERR_SCRATCH (the
+ * limit is 262144 such blocks, 4.29e9 elements per call); every other check
+ * and result is exactly ptb_lamb_step's, with the same kernels.  Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (different
+ * streams, no ordering between them) race and must not be issued. */
+#define PTB_LAMB_NOALLOC_SCRATCH_BYTES (4u << 20)
+int32_t ptb_lamb_step_noalloc(const ptb_lamb_hyper* hyper, const ptb_lamb_tensor* tensors,
+                              int32_t n, float* norms, void* stream);
 
 /* ------------------------------------------------------------------------
  * FP8 GEMM variant of the parallel block (Megatron-LM tuning post,

@@ -35,8 +35,8 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert P.ptb_abi_version() == 7
-    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+    assert P.ptb_abi_version() == 8
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert P.ptb_status_string(code) and P.ptb_status_string(code) != "unknown status"
     assert P.ptb_status_string(12345) == "unknown status"
 
@@ -203,6 +203,30 @@ def test_lamb_workspace_and_argument_checks(lib):
     assert P.ptb_lamb_step(hp, _lamb_list(v=A + 4), A, A, stream=0, check=False) == P.PTB_ERR_ALIGN
     assert P.ptb_lamb_step(hp, ok, 0, A, stream=0, check=False) == P.PTB_ERR_NULL
     assert P.ptb_lamb_step(hp, ok, A, A + 8, stream=0, check=False) == P.PTB_ERR_ALIGN
+
+
+def test_lamb_noalloc_argument_checks(lib):
+    """The allocation-free step makes the same checks as ptb_lamb_step and
+    rejects a list whose scratch exceeds its static buffer, before any HIP
+    call."""
+    hp = P.ptb_lamb_hyper(1e-3, 0.9, 0.999, 1e-6, 1)
+    A = 0x10000
+    for bad in (_lamb_list(numel=12), _lamb_list(numel=0), _lamb_list(n=33)):
+        assert P.ptb_lamb_step_noalloc(hp, bad, A, stream=0, check=False) == P.PTB_ERR_ARG
+    assert P.ptb_lamb_step_noalloc(hp, _lamb_list(grad=0), A, stream=0,
+                                   check=False) == P.PTB_ERR_NULL
+    assert P.ptb_lamb_step_noalloc(hp, _lamb_list(), 0, stream=0, check=False) == P.PTB_ERR_NULL
+    assert P.ptb_lamb_step_noalloc(hp, _lamb_list(m=A + 4), A, stream=0,
+                                   check=False) == P.PTB_ERR_ALIGN
+    assert P.ptb_lamb_step_noalloc(P.ptb_lamb_hyper(1e-3, 0.9, 0.999, 1e-6, 0), _lamb_list(), A,
+                                   stream=0, check=False) == P.PTB_ERR_ARG
+    # scratch: 16 bytes per 16384 elements; the static buffer holds 2^18 such blocks
+    limit_blocks = P.PTB_LAMB_NOALLOC_SCRATCH_BYTES // 16
+    big = _lamb_list(n=3, numel=2 ** 31 - 8)     # 3 * 131072 blocks > 262144
+    assert P.ptb_lamb_workspace_bytes(big) > P.PTB_LAMB_NOALLOC_SCRATCH_BYTES
+    assert P.ptb_lamb_step_noalloc(hp, big, A, stream=0, check=False) == P.PTB_ERR_SCRATCH
+    assert 3 * 131072 > limit_blocks >= 2 * 131072
+    assert "static buffer" in P.ptb_status_string(P.PTB_ERR_SCRATCH)
 
 
 def test_swiglu_widens_the_fc1_stash_and_workspace(lib):

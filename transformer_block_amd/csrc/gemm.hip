@@ -52,6 +52,7 @@
 // and 128-wide k-step) into a small LDS ring beside the operand ring, and
 // each lane passes the byte of its row's 32-wide k-block.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -1252,14 +1253,21 @@ __global__ __launch_bounds__(256) void zero_i32_kernel(int* p, int n) {
   for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
 }
 
+// Compute units of the current device, cached per device.  The cache is the
+// library's one piece of mutable global state besides the per-device address
+// of its static scratch array: each slot only ever goes from 0 to the
+// device's count, with relaxed atomics, so concurrent first calls are benign.
 int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev >= 0 && dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64) cached[dev] = n;
+  if (dev >= 0 && dev < 64 && n > 0) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 

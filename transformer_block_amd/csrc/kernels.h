@@ -239,6 +239,12 @@ struct LambHyper {
   int step;
 };
 int lamb_blocks(long numel);
+// The allocation-free step's scratch: a static device array of this many
+// bytes (room for the partial sums of this many / 16 workgroups), one per
+// GPU.  lamb_static_scratch returns its address on the current device,
+// looked up once per device.
+constexpr size_t kLambStaticScratchBytes = size_t(4) << 20;
+hipError_t lamb_static_scratch(double** out);
 hipError_t launch_lamb(const LambTensor* ts, int n, const LambHyper& hp, double* partial,
                        float* norms, hipStream_t stream);
 

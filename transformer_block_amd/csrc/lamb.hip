@@ -15,11 +15,20 @@
 //      the same r), theta -= lr * trust * r; write theta and bf16(theta).
 // Every thread moves 8 consecutive elements per iteration with 16-byte
 // accesses.  Results do not depend on timing (fixed reduction order).
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
 
 namespace ptb {
 namespace {
+
+// Static scratch of the allocation-free step (launch_lamb with the pointer
+// from lamb_static_scratch): each GPU the library runs on holds its own copy
+// until the process ends.  Host code never passes this name to a kernel (in
+// host code it is a stand-in, not a device address): the per-device address
+// comes from hipGetSymbolAddress.
+static __device__ __align__(256) double scratch[kLambStaticScratchBytes / sizeof(double)];
 
 constexpr int LAMB_THREADS = 256;
 constexpr int LAMB_VEC = 8;                                      // elements per thread per pass
@@ -152,7 +161,29 @@ __global__ __launch_bounds__(LAMB_THREADS) void lamb_update_kernel(LambArgs a) {
   }
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+double* scratch_ptr[kMaxDevices];  // guarded by scratch_mutex
+
 }  // namespace
+
+hipError_t lamb_static_scratch(double** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = static_cast<double*>(p);
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
+}
 
 int lamb_blocks(long numel) { return static_cast<int>((numel + LAMB_CHUNK - 1) / LAMB_CHUNK); }
 

@@ -32,6 +32,9 @@ namespace {
 
 using ptb::u16;
 
+static_assert(PTB_LAMB_NOALLOC_SCRATCH_BYTES == ptb::kLambStaticScratchBytes,
+              "the header's static scratch size is the library's");
+
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
@@ -452,6 +455,7 @@ const char* ptb_status_string(int32_t status) {
     case PTB_ERR_EPS: return "ln_eps must be a finite positive number";
     case PTB_ERR_HIP: return "a HIP kernel launch failed";
     case PTB_ERR_ARG: return "invalid layer variant, optimizer hyper-parameters or tensor list";
+    case PTB_ERR_SCRATCH: return "the call needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -958,11 +962,13 @@ int32_t ptb_lamb_workspace_bytes(const ptb_lamb_tensor* tensors, int32_t n, size
   return PTB_OK;
 }
 
-int32_t ptb_lamb_step(const ptb_lamb_hyper* hyper, const ptb_lamb_tensor* tensors, int32_t n,
-                      float* norms, void* workspace, void* stream) {
+namespace {
+// Checks of one LAMB call (everything but the scratch); fills the kernels'
+// tensor list and hyper-parameters.
+int32_t lamb_args(const ptb_lamb_hyper* hyper, const ptb_lamb_tensor* tensors, int32_t n,
+                  float* norms, ptb::LambTensor* ts, ptb::LambHyper* hp, size_t* scratch_bytes) {
   if (hyper == nullptr || tensors == nullptr) return PTB_ERR_NULL;
-  size_t need = 0;
-  const int32_t st = ptb_lamb_workspace_bytes(tensors, n, &need);
+  const int32_t st = ptb_lamb_workspace_bytes(tensors, n, scratch_bytes);
   if (st != PTB_OK) return st;
   const ptb_lamb_hyper& h = *hyper;
   if (!isfinite(h.lr) || !(h.beta1 >= 0.0f && h.beta1 < 1.0f) ||
@@ -973,16 +979,42 @@ int32_t ptb_lamb_step(const ptb_lamb_hyper* hyper, const ptb_lamb_tensor* tensor
     const int32_t pc = check_ptrs({t.theta, t.m, t.v, t.grad, t.weight});
     if (pc != PTB_OK) return pc;
   }
-  const int32_t pc = check_ptrs({norms, workspace});
+  const int32_t pc = check_ptrs({norms});
   if (pc != PTB_OK) return pc;
-  ptb::LambTensor ts[PTB_LAMB_MAX_TENSORS];
   for (int i = 0; i < n; ++i)
     ts[i] = ptb::LambTensor{tensors[i].theta, tensors[i].m, tensors[i].v,
                             static_cast<const u16*>(tensors[i].grad),
                             static_cast<u16*>(tensors[i].weight), static_cast<long>(tensors[i].numel)};
-  const ptb::LambHyper hp{h.lr, h.beta1, h.beta2, h.eps, h.step};
+  *hp = ptb::LambHyper{h.lr, h.beta1, h.beta2, h.eps, h.step};
+  return PTB_OK;
+}
+}  // namespace
+
+int32_t ptb_lamb_step(const ptb_lamb_hyper* hyper, const ptb_lamb_tensor* tensors, int32_t n,
+                      float* norms, void* workspace, void* stream) {
+  ptb::LambTensor ts[PTB_LAMB_MAX_TENSORS];
+  ptb::LambHyper hp;
+  size_t need = 0;
+  int32_t st = lamb_args(hyper, tensors, n, norms, ts, &hp, &need);
+  if (st != PTB_OK) return st;
+  st = check_ptrs({workspace});
+  if (st != PTB_OK) return st;
   PTB_HIP(ptb::launch_lamb(ts, n, hp, static_cast<double*>(workspace), norms,
                            reinterpret_cast<hipStream_t>(stream)));
+  return PTB_OK;
+}
+
+int32_t ptb_lamb_step_noalloc(const ptb_lamb_hyper* hyper, const ptb_lamb_tensor* tensors,
+                              int32_t n, float* norms, void* stream) {
+  ptb::LambTensor ts[PTB_LAMB_MAX_TENSORS];
+  ptb::LambHyper hp;
+  size_t need = 0;
+  const int32_t st = lamb_args(hyper, tensors, n, norms, ts, &hp, &need);
+  if (st != PTB_OK) return st;
+  if (need > ptb::kLambStaticScratchBytes) return PTB_ERR_SCRATCH;
+  double* scratch = nullptr;  // this device's copy of the static array
+  PTB_HIP(ptb::lamb_static_scratch(&scratch));
+  PTB_HIP(ptb::launch_lamb(ts, n, hp, scratch, norms, reinterpret_cast<hipStream_t>(stream)));
   return PTB_OK;
 }
 

@@ -27,7 +27,9 @@ PTB_ERR_WINDOW = -5
 PTB_ERR_EPS = -6
 PTB_ERR_HIP = -7
 PTB_ERR_ARG = -8
+PTB_ERR_SCRATCH = -9
 PTB_LAMB_MAX_TENSORS = 32
+PTB_LAMB_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 SAVED_SLOTS = ("a", "mu", "rstd", "qkv", "u", "g", "c", "lse", "a_lo", "qk_lo")
 SERIAL_SAVED_SLOTS = ("a1", "mu1", "rstd1", "a1_lo", "qkv", "qk_lo", "c", "lse", "x1", "a2",
@@ -116,6 +118,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ptb_lamb_step": (ctypes.c_int32, [ctypes.POINTER(ptb_lamb_hyper),
                                            ctypes.POINTER(ptb_lamb_tensor), ctypes.c_int32,
                                            _P, _P, _P]),
+        "ptb_lamb_step_noalloc": (ctypes.c_int32, [ctypes.POINTER(ptb_lamb_hyper),
+                                                   ctypes.POINTER(ptb_lamb_tensor),
+                                                   ctypes.c_int32, _P, _P]),
         "ptb_fp8_weights_bytes": (ctypes.c_int32, [_D, _I, ctypes.POINTER(ctypes.c_size_t)]),
         "ptb_fp8_weights_layout": (ctypes.c_int32, [_D, _I, ctypes.POINTER(ctypes.c_size_t)]),
         "ptb_fp8_quantize": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _P]),
@@ -350,6 +355,15 @@ def ptb_lamb_step(hyper: ptb_lamb_hyper, tensors, norms, workspace, stream=None,
     return _done(st, "ptb_lamb_step", check)
 
 
+def ptb_lamb_step_noalloc(hyper: ptb_lamb_hyper, tensors, norms, stream=None,
+                          check: bool = True) -> int:
+    """ptb_lamb_step with the library's static scratch instead of a workspace."""
+    arr = lamb_tensor_list(tensors)
+    st = load_library().ptb_lamb_step_noalloc(ctypes.byref(hyper), arr, len(arr), _ptr(norms),
+                                              _stream(stream))
+    return _done(st, "ptb_lamb_step_noalloc", check)
+
+
 # ---- FP8 GEMM variant: see include/ptb.h
 PTB_FP8_FWD_STAGES = 6
 PTB_FP8_BWD_STAGES = 8
@@ -442,7 +456,8 @@ def exported_symbols() -> Sequence[str]:
             "ptb_forward_timed", "ptb_backward_timed", "ptb_serial_saved_bytes",
             "ptb_serial_workspace_bytes", "ptb_serial_saved_layout", "ptb_serial_forward",
             "ptb_serial_backward", "ptb_serial_forward_timed", "ptb_serial_backward_timed",
-            "ptb_lamb_workspace_bytes", "ptb_lamb_step", "ptb_fp8_weights_bytes",
+            "ptb_lamb_workspace_bytes", "ptb_lamb_step", "ptb_lamb_step_noalloc",
+            "ptb_fp8_weights_bytes",
             "ptb_fp8_weights_layout", "ptb_fp8_quantize", "ptb_fp8_quantize_mx",
             "ptb_fp8_saved_bytes",
             "ptb_fp8_workspace_bytes", "ptb_fp8_cast_weights", "ptb_fp8_forward",
