@@ -78,6 +78,8 @@ def stage_work(w):
     attn_pairs = w.batch * w.heads * window_pairs(w.seq, w.window)
     fwd = {
         "layernorm_fwd": ("bytes", T * h * 2 * 2 + T * 8),
+        # read the q, k columns of W_qkv (bf16), write their fp16 copy
+        "cast_wqk_f16": ("bytes", h * 2 * hl * (2 + 2)),
         "gemm_qkv_fc1": ("flops", 2 * T * h * N1),
         "attention_fwd": ("flops", 2 * 2 * attn_pairs * w.head_dim),
         "gemm_o_fc2_residual": ("flops", 2 * T * K2 * h),
@@ -94,7 +96,8 @@ def stage_work(w):
     return fwd, bwd
 
 
-STAGE_SOURCE = {"gemm": "gemm.hip", "attention": "attention.hip", "layernorm": "layernorm.hip"}
+STAGE_SOURCE = {"gemm": "gemm.hip", "attention": "attention.hip", "layernorm": "layernorm.hip",
+                "cast": "layernorm.hip"}
 
 
 def source_sha256(stage: str) -> str:

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define PTB_ABI_VERSION 8
+#define PTB_ABI_VERSION 9
 
 enum ptb_status {
   PTB_OK = 0,
@@ -126,8 +126,9 @@ int32_t ptb_saved_bytes(const ptb_dims* dims, size_t* bytes);
 
 /* Bytes of scratch (`workspace`) that ptb_forward and ptb_backward need:
  * fp32 partial sums of matrix-product tiles that are split over several
- * workgroups, their arrival counters, and the backward's intermediate
- * gradients (dc, dZ, da, the LayerNorm column partials). */
+ * workgroups, their arrival counters, the forward's fp16 copy of the q, k
+ * columns of W_qkv, and the backward's intermediate gradients (dc, dZ, da,
+ * the LayerNorm column partials). */
 int32_t ptb_workspace_bytes(const ptb_dims* dims, size_t* bytes);
 
 /* Byte offsets inside `saved` of what ptb_forward stores there, for
@@ -141,18 +142,21 @@ int32_t ptb_workspace_bytes(const ptb_dims* dims, size_t* bytes);
  *   PTB_SAVED_C    attention output          bf16 [T, h_l] (head-major cols)
  *   PTB_SAVED_LSE  base-2 log-sum-exp of the logits scaled by log2(e)/sqrt(d)
  *                                            fp32 [b, n, s]
- *   PTB_SAVED_A_LO rounding residual of a: bf16(LN(x) - a)   bf16 [T, h]
- *   PTB_SAVED_QK_LO rounding residual of the q and k columns of qkv
- *                                            bf16 [T, 2*h_l]
- * The logits q.k/sqrt(d) are formed from q and k carried as such bf16 pairs
- * (value + residual), computed from [a | a_lo]: with the large logits of wide
- * layers a plain bf16 rounding of a, q or k shifts every logit by a few
- * thousandths, which the softmax turns into a comparable relative error of the
- * attention output and of the q, k gradients.
+ *   PTB_SAVED_A16  fp16 copy of LN(x)         fp16 [T, h]
+ *   PTB_SAVED_QK16 the q and k columns of qkv in fp16: a16 W_q|k with fp16
+ *                  operands and fp32 sums    fp16 [T, 2*h_l]
+ * The logits q.k/sqrt(d) are one fp16 product of these q and k (10 mantissa
+ * bits instead of bf16's 7): with the large logits of wide layers a bf16
+ * rounding of LN(x), q or k shifts every logit by a few thousandths, which
+ * the softmax turns into a comparable relative error of the attention output
+ * and of the q, k gradients.  fp16 has a narrower range than bf16: q, k and
+ * LN(x) are saturated at +-65504 (far outside what a LayerNorm output and
+ * 0.02-scale weights produce), and weights below 2^-14 in magnitude enter the
+ * q, k product as fp16 subnormals (absolute error <= 2^-25).
  * `offsets` must have room for PTB_SAVED_COUNT entries. */
 enum ptb_saved_slot {
   PTB_SAVED_A = 0, PTB_SAVED_MU, PTB_SAVED_RSTD, PTB_SAVED_QKV, PTB_SAVED_U,
-  PTB_SAVED_G, PTB_SAVED_C, PTB_SAVED_LSE, PTB_SAVED_A_LO, PTB_SAVED_QK_LO,
+  PTB_SAVED_G, PTB_SAVED_C, PTB_SAVED_LSE, PTB_SAVED_A16, PTB_SAVED_QK16,
   PTB_SAVED_COUNT
 };
 int32_t ptb_saved_layout(const ptb_dims* dims, size_t* offsets);
@@ -168,8 +172,11 @@ int32_t ptb_forward(const ptb_dims* dims,
                     const void* w_fc1, const void* w_fc2,
                     void* y, void* saved, void* workspace, void* stream);
 
-/* Backward of one layer for upstream gradient dy [T, h], reading the `saved`
- * of the matching ptb_forward and the same x and weights.  Writes dx (which
+/* Backward of one layer (the gradient of eq (4), MegaScale notes, section
+ * 1.1) for upstream gradient dy [T, h], reading the `saved` of the matching
+ * ptb_forward and the same x and weights.  The attention probabilities are
+ * recomputed from the saved log-sum-exp, never stored (selective recompute
+ * of the core attention, same notes, section 1.3).  Writes dx (which
  * includes the residual path dy), d_ln_gamma, d_ln_beta and the four weight
  * gradients.  `workspace` holds ptb_workspace_bytes(dims) bytes of scratch. */
 int32_t ptb_backward(const ptb_dims* dims,
@@ -187,14 +194,15 @@ int32_t ptb_backward(const ptb_dims* dims,
  * `stream` right before stage i is enqueued and event 2*i+1 right after it, so
  * hipEventElapsedTime(events[2i], events[2i+1]) is the device time of stage i.
  * The events are created and owned by the caller.  Stages:
- *   forward  (PTB_FWD_STAGES = 4): 0 LayerNorm, 1 [QKV | FC1] GEMM + GeLU,
- *            2 attention, 3 [O ; FC2] GEMM + residual;
+ *   forward  (PTB_FWD_STAGES = 5): 0 LayerNorm, 1 fp16 copy of the q, k
+ *            columns of W_qkv, 2 [QKV | FC1] GEMM + GeLU, 3 attention,
+ *            4 [O ; FC2] GEMM + residual;
  *   backward (PTB_BWD_STAGES = 6): 0 dgrad [O ; FC2] + GeLU', 1 attention
  *            backward (3 kernels), 2 wgrad [O ; FC2], 3 dgrad [QKV | FC1],
  *            4 wgrad [QKV | FC1], 5 LayerNorm backward (2 kernels).
  * Each GEMM stage is exactly one kernel launch.  Each call also clears the
  * tile counters in `workspace` with one small kernel ahead of stage 0. */
-#define PTB_FWD_STAGES 4
+#define PTB_FWD_STAGES 5
 #define PTB_BWD_STAGES 6
 int32_t ptb_forward_timed(const ptb_dims* dims,
                           const void* x,
@@ -235,14 +243,14 @@ int32_t ptb_backward_timed(const ptb_dims* dims,
 /* What ptb_serial_forward stores in `saved` (byte offsets from
  * ptb_serial_saved_layout; `offsets` must have room for
  * PTB_SERIAL_SAVED_COUNT entries):
- *   A1, MU1, RSTD1, A1_LO   LN1(x) as for the parallel block (PTB_SAVED_A ...)
- *   QKV, QK_LO, C, LSE      as PTB_SAVED_QKV, _QK_LO, _C, _LSE
+ *   A1, MU1, RSTD1, A1_16   LN1(x) as for the parallel block (PTB_SAVED_A ...)
+ *   QKV, QK16, C, LSE       as PTB_SAVED_QKV, _QK16, _C, _LSE
  *   X1                      x + Attn(a1) W_o          bf16 [T, h]
  *   A2, MU2, RSTD2          LN2(x1) and its row statistics
  *   U, G                    a2 W_fc1 and GeLU of it   bf16 [T, f] */
 enum ptb_serial_saved_slot {
-  PTB_SERIAL_A1 = 0, PTB_SERIAL_MU1, PTB_SERIAL_RSTD1, PTB_SERIAL_A1_LO,
-  PTB_SERIAL_QKV, PTB_SERIAL_QK_LO, PTB_SERIAL_C, PTB_SERIAL_LSE,
+  PTB_SERIAL_A1 = 0, PTB_SERIAL_MU1, PTB_SERIAL_RSTD1, PTB_SERIAL_A1_16,
+  PTB_SERIAL_QKV, PTB_SERIAL_QK16, PTB_SERIAL_C, PTB_SERIAL_LSE,
   PTB_SERIAL_X1, PTB_SERIAL_A2, PTB_SERIAL_MU2, PTB_SERIAL_RSTD2,
   PTB_SERIAL_U, PTB_SERIAL_G,
   PTB_SERIAL_SAVED_COUNT
@@ -277,13 +285,14 @@ int32_t ptb_serial_backward(const ptb_dims* dims,
                             void* workspace, void* stream);
 
 /* Stage timing as for ptb_forward_timed.  Stages:
- *   forward  (PTB_SERIAL_FWD_STAGES = 7): 0 LN1, 1 QKV GEMM, 2 attention,
- *            3 O GEMM + residual, 4 LN2, 5 FC1 GEMM + GeLU, 6 FC2 GEMM + residual;
+ *   forward  (PTB_SERIAL_FWD_STAGES = 8): 0 LN1, 1 fp16 copy of W_q|k,
+ *            2 QKV GEMM, 3 attention, 4 O GEMM + residual, 5 LN2,
+ *            6 FC1 GEMM + GeLU, 7 FC2 GEMM + residual;
  *   backward (PTB_SERIAL_BWD_STAGES = 11): 0 dgrad FC2 + GeLU', 1 wgrad FC2,
  *            2 dgrad FC1, 3 wgrad FC1, 4 LN2 backward (+ dy), 5 dgrad O,
  *            6 wgrad O, 7 attention backward, 8 dgrad QKV, 9 wgrad QKV,
  *            10 LN1 backward (+ dx1). */
-#define PTB_SERIAL_FWD_STAGES 7
+#define PTB_SERIAL_FWD_STAGES 8
 #define PTB_SERIAL_BWD_STAGES 11
 int32_t ptb_serial_forward_timed(const ptb_dims* dims,
                                  const void* x,
@@ -400,7 +409,7 @@ int32_t ptb_lamb_step_noalloc(const ptb_lamb_hyper* hyper, const ptb_lamb_tensor
  * the FP8 copies pad their contiguous dimension with zero codes to a
  * multiple of 128.  Inputs, outputs and ownership are as for the bf16 calls.
  * `saved` (ptb_fp8_saved_bytes) holds the parallel block's slots at the
- * offsets ptb_saved_layout gives (A_LO is not written), followed by the
+ * offsets ptb_saved_layout gives (A16 is not written), followed by the
  * transposed E4M3 copies of a and [c | g] and their amax or block scales, which the forward
  * casts for the weight gradients;
  * the calls are asynchronous on `stream` and return PTB_ERR_HIP if a launch

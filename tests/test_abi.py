@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert P.ptb_abi_version() == 8
+    assert P.ptb_abi_version() == 9
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert P.ptb_status_string(code) and P.ptb_status_string(code) != "unknown status"
     assert P.ptb_status_string(12345) == "unknown status"
@@ -92,14 +92,19 @@ def test_saved_layout_is_ordered_aligned_and_sized(lib):
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     T, h, hl, f = 512, 256, 256, 1024
     sizes = dict(a=T * h * 2, mu=T * 4, rstd=T * 4, qkv=T * 3 * hl * 2, u=T * f * 2,
-                 g=T * f * 2, c=T * hl * 2, lse=2 * 4 * 256 * 4, a_lo=T * h * 2,
-                 qk_lo=T * 2 * hl * 2)
+                 g=T * f * 2, c=T * hl * 2, lse=2 * 4 * 256 * 4, a16=T * h * 2,
+                 qk16=T * 2 * hl * 2)
     for a_, b_ in zip(P.SAVED_SLOTS, P.SAVED_SLOTS[1:]):
         assert lay[b_] - lay[a_] >= sizes[a_]
-    assert P.ptb_saved_bytes(d) >= lay["qk_lo"] + sizes["qk_lo"]
+    assert P.ptb_saved_bytes(d) >= lay["qk16"] + sizes["qk16"]
     # split-tile partials (2 fp32 256x256 tiles per workgroup, 256 workgroups)
     # come first, then the backward's dc, dZ and da
     assert P.ptb_workspace_bytes(d) >= 2 * 256 * 256 * 256 * 4 + T * (3 * hl + f) * 2 + T * h * 2
+    # the forward's fp16 copy of W_qkv's q, k columns fits in the workspace too
+    assert P.ptb_workspace_bytes(d) >= 2 * 256 * 256 * 256 * 4 + h * 2 * hl * 2
+    wide = good_dims(batch=1, seq=64, hidden=4096, heads=32, head_dim=128, ffn=64)
+    assert P.ptb_workspace_bytes(wide) >= 4096 * 2 * 4096 * 2
+    assert P.ptb_serial_workspace_bytes(wide) >= 4096 * 2 * 4096 * 2
 
 
 def test_forward_backward_reject_null_and_misaligned_before_any_hip_call(lib):
@@ -135,8 +140,8 @@ def test_serial_saved_layout_is_ordered_aligned_and_sized(lib):
     offs = [lay[k] for k in P.SERIAL_SAVED_SLOTS]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     T, h, hl, f = 512, 256, 256, 1024
-    sizes = dict(a1=T * h * 2, mu1=T * 4, rstd1=T * 4, a1_lo=T * h * 2, qkv=T * 3 * hl * 2,
-                 qk_lo=T * 2 * hl * 2, c=T * hl * 2, lse=2 * 4 * 256 * 4, x1=T * h * 2,
+    sizes = dict(a1=T * h * 2, mu1=T * 4, rstd1=T * 4, a1_16=T * h * 2, qkv=T * 3 * hl * 2,
+                 qk16=T * 2 * hl * 2, c=T * hl * 2, lse=2 * 4 * 256 * 4, x1=T * h * 2,
                  a2=T * h * 2, mu2=T * 4, rstd2=T * 4, u=T * f * 2, g=T * f * 2)
     for a_, b_ in zip(P.SERIAL_SAVED_SLOTS, P.SERIAL_SAVED_SLOTS[1:]):
         assert lay[b_] - lay[a_] >= sizes[a_]

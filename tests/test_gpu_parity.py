@@ -6,8 +6,8 @@ Frobenius error against the bar REL_TOL = 1e-2 (bf16 operands, fp32
 accumulation).  The residual paths dominate y and dx, so y - x and dx - dy are
 compared as well, against a bar that adds the bf16 rounding floor of the
 output to the 1e-2 relative error of the branch.  The layer-0 intermediates the forward stashes (LayerNorm
-output, QKV, u, GeLU(u), attention output, log-sum-exp) are checked too, which
-localises a failure to one kernel.
+output and its fp16 copy, QKV and the fp16 q and k, u, GeLU(u), attention
+output, log-sum-exp) are checked too, which localises a failure to one kernel.
 """
 import numpy as np
 import pytest
@@ -86,9 +86,19 @@ def compare(w, inp, ref, st, tol=REL_TOL, check_intermediates=True):
         for name, key in (("a", "a"), ("qkv", "qkv"), ("u", "u"), ("g", "g"), ("c", "c"),
                           ("mu", "mu"), ("rstd", "rstd")):
             errs[f"L0.{name}"] = rel_fro(_to_np(st.saved_tensor(0, name)), c0[key])
+        # the fp16 copies the logit path runs on: LN(x) and the q, k columns
+        hl = w.h_local
+        errs["L0.a16"] = rel_fro(_to_np(st.saved_tensor(0, "a16")), c0["a"])
+        errs["L0.qk16"] = rel_fro(_to_np(st.saved_tensor(0, "qk16")), c0["qkv"][:, :2 * hl])
+        # lse is the base-2 log of each row's softmax normaliser Z: it is
+        # judged like every other tensor, by the relative error of what it
+        # encodes, 2^dlse - 1 per row, RMS over the rows (the relative
+        # Frobenius error of Z measured row by row); the largest |dlse| is
+        # logged beside it.
         lse = _to_np(st.saved_tensor(0, "lse"))
-        lse_ref = oracle_lse2(c0, w)
-        errs["L0.lse(abs)"] = float(np.max(np.abs(lse - lse_ref)))
+        dl = lse - oracle_lse2(c0, w)
+        errs["L0.lse"] = float(np.sqrt(np.mean(np.expm1(dl * np.log(2.0)) ** 2)))
+        log(f"[{w.name}] max |dlse| (log2 units) = {float(np.max(np.abs(dl))):.2e}")
     log(f"[{w.name}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not np.isfinite(v) or v > tol}
     assert not bad, f"parity failures (tol {tol}): {bad}"

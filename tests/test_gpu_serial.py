@@ -65,6 +65,9 @@ def test_serial_block_parity(name, w, random_ln):
     for name_, key in (("a1", "a1"), ("x1", "x1"), ("a2", "a2"), ("qkv", "qkv"), ("c", "c"),
                        ("u", "u"), ("g", "g"), ("mu2", "mu2"), ("rstd2", "rstd2")):
         errs[f"saved.{name_}"] = rel_fro(_np(blk.saved_tensor(name_)), cache[key])
+    hl = w.h_local
+    errs["saved.a1_16"] = rel_fro(_np(blk.saved_tensor("a1_16")), cache["a1"])
+    errs["saved.qk16"] = rel_fro(_np(blk.saved_tensor("qk16")), cache["qkv"][:, :2 * hl])
     log(f"[serial {name}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not np.isfinite(v) or v > REL_TOL}
     assert not bad, f"parity failures (tol {REL_TOL}): {bad}"

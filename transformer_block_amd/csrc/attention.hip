@@ -13,8 +13,8 @@
 // post, recompute section).  Key tiles that lie wholly outside every query's
 // window are never visited, so the work is O(s * w), not O(s^2).
 //
-// Matrix-core mapping.  Every contraction is a v_mfma_f32_32x32x16_bf16.  The
-// forward computes S^T = K Q^T so that each lane owns one query column: the
+// Matrix-core mapping.  Every contraction is a 32x32x16 MFMA: fp16 for the
+// logits and the products with dS, bf16 for the rest.  The forward computes S^T = K Q^T so that each lane owns one query column: the
 // row max and row sum of the online softmax are lane-local plus one exchange
 // with the lane 32 apart, and O^T = V^T P^T reuses the S^T accumulator
 // registers directly as the B operand (the key order inside a 16-key step is
@@ -26,13 +26,15 @@
 // query-parallel kernel for dQ (S^T, lane = query), so no atomics are needed
 // and results are deterministic.
 //
-// Logit precision.  q and k arrive as bf16 pairs (value and rounding residual,
-// both from the fp32 projection), and every logit is formed as
-// q_hi.k_hi + q_lo.k_hi + q_hi.k_lo: three matrix-core products whose sum
-// carries ~16 mantissa bits.  With large logits a single bf16 rounding of q or
-// k would shift every logit by a few thousandths, which the softmax turns into
-// a relative error of the same size in the output and, through dS, in the
-// gradients of q and k.
+// Logit precision.  q and k arrive in fp16 (10 mantissa bits, from an fp32
+// product of the fp16 copies of LN(x) and of the q, k weight columns), and
+// every logit is one fp16 matrix-core product.  With the large logits of wide
+// layers a bf16 rounding of LN(x), q or k would shift every logit by a few
+// thousandths, which the softmax turns into a relative error of the same size
+// in the output and, through dS, in the gradients of q and k; fp16 cuts that
+// shift by 8x at the same cost as bf16.  dS goes to fp16 as well for the
+// products with k and q (dQ = dS K, dK = dS^T Q); P and dO stay bf16 (dV =
+// P^T dO, dP = dO V^T, O = P V).
 #include "attention_common.h"
 
 namespace ptb {
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const u16* __restrict__
 
 // ------------------------------------------------------------ dK and dV
 // Key rows of 128 (4 waves x 32, lane = key), query stages of QS = 32 staged
-// by DMA one stage ahead, two stages of three row-major tiles: Q, Q_lo and dO
+// by DMA one stage ahead, two stages of two row-major tiles: Q (fp16) and dO
 // (A operands of S = Q K^T and dP = dO V^T, and, read transposed with the
 // rows in the accumulator's order, of dK^T += Q^T dS and dV^T += dO^T P).
 // The stage's log-sum-exp and delta go to LDS through registers, loaded one
@@ -78,12 +80,12 @@ constexpr int QS = 32;
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
-    const u16* __restrict__ qkv, const u16* __restrict__ qk_lo, const u16* __restrict__ dcg,
+    const u16* __restrict__ qkv, const u16* __restrict__ qk16, const u16* __restrict__ dcg,
     const float* __restrict__ lse, const float* __restrict__ delta, u16* __restrict__ dz,
     int ld_dz, int s, int n, int window, int nkt, RowSplit rsp) {
   constexpr int NKS = D / 16, ND = D / 32;
   constexpr int OPB = QS * D;  // u16 elements of one operand's tile
-  constexpr int STG = 3 * OPB;
+  constexpr int STG = 2 * OPB;
   __shared__ __attribute__((aligned(1024))) u16 qs[2 * STG];
   __shared__ __attribute__((aligned(16))) float ld_lds[2][2][QS];  // [stage][lse, delta][query]
   __shared__ int arrival;
@@ -93,12 +95,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const int l32 = lane & 31, g = lane >> 5;
   const int hd = blockIdx.y, bi = blockIdx.z;
   const int hl = n * D, ld = 3 * hl;
-  const u16* Qg = qkv + static_cast<size_t>(bi) * s * ld + hd * D;
-  const u16* Kg = Qg + hl;
-  const u16* Vg = Qg + 2 * hl;
+  const u16* Qh = qk16 + static_cast<size_t>(bi) * s * (2 * hl) + hd * D;  // fp16
+  const u16* Kh = Qh + hl;
+  const u16* Vg = qkv + static_cast<size_t>(bi) * s * ld + hd * D + 2 * hl;  // bf16
   const u16* dOg = dcg + static_cast<size_t>(bi) * s * hl + hd * D;
-  const u16* Qlg = qk_lo + static_cast<size_t>(bi) * s * (2 * hl) + hd * D;
-  const u16* Klg = Qlg + hl;
   const float* lse_h = lse + (static_cast<size_t>(bi) * n + hd) * s;
   const float* dl_h = delta + (static_cast<size_t>(bi) * n + hd) * s;
   const RowItem item = decode_row_item<false>(static_cast<int>(blockIdx.x), nkt, s, window, rsp.ch);
@@ -107,15 +107,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 
   const int q_begin = item.span.begin;
   const int q_end = item.span.end;
-  TileDma<D, QS, false> dq_r, dql_r, do_r;
-  dq_r.init(Qg, ld, s, wave, lane);
-  dql_r.init(Qlg, 2 * hl, s, wave, lane);
+  TileDma<D, QS, false> dq_r, do_r;
+  dq_r.init(Qh, 2 * hl, s, wave, lane);
   do_r.init(dOg, hl, s, wave, lane);
   const uint32_t qs_lds = __builtin_amdgcn_readfirstlane(lds_address(qs));
   auto issue = [&](uint32_t lds, int qt0) {
     dq_r.issue(lds, qt0, wave);
-    dql_r.issue(lds + OPB * 2, qt0, wave);
-    do_r.issue(lds + 2 * OPB * 2, qt0, wave);
+    do_r.issue(lds + OPB * 2, qt0, wave);
   };
   // log-sum-exp (threads 0..31) and delta (32..63) of one stage's queries
   auto load_ld = [&](int qt0) {
@@ -129,18 +127,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     if (tid < 64) ld_lds[0][tid >> 5][tid & 31] = ldv;
   }
 
-  bf16x8 kf[NKS], kl[NKS], vf[NKS];
+  bf16x8 kf[NKS], vf[NKS];  // fp16 keys, bf16 values of this lane's key
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a, c = a;
+    uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
     if (kj < s) {
-      a = *reinterpret_cast<const uint4*>(Kg + kj * ld + ks * 16 + g * 8);
+      a = *reinterpret_cast<const uint4*>(Kh + kj * (2 * hl) + ks * 16 + g * 8);
       b = *reinterpret_cast<const uint4*>(Vg + kj * ld + ks * 16 + g * 8);
-      c = *reinterpret_cast<const uint4*>(Klg + kj * (2 * hl) + ks * 16 + g * 8);
     }
     kf[ks] = as_bf16x8(a);
     vf[ks] = as_bf16x8(b);
-    kl[ks] = as_bf16x8(c);
   }
   const float sc = kLog2e / sqrtf(static_cast<float>(D));
   f32x16 dv[ND], dk[ND];
@@ -159,8 +155,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
       ldv = load_ld(qt0 + QS);
     }
     const u16* q_lds = qs + stage * STG;
-    const u16* ql_lds = q_lds + OPB;
-    const u16* do_lds = q_lds + 2 * OPB;
+    const u16* do_lds = q_lds + OPB;
     const float* lse_s = ld_lds[stage][0];
     const float* dl_s = ld_lds[stage][1];
 
@@ -174,25 +169,21 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
       // query fragments of k-step ks + 1 read under the MFMAs of k-step ks
       // (one wave per SIMD: a read issued just before its MFMA would leave
       // the LDS latency exposed)
-      bf16x8 fq[2], fql[2], fdo[2];
+      bf16x8 fq[2], fdo[2];
       fq[0] = row_frag<D>(q_lds, l32, g);
-      fql[0] = row_frag<D>(ql_lds, l32, g);
       fdo[0] = row_frag<D>(do_lds, l32, g);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const int c = ks & 1;
         if (ks + 1 < NKS) {
           fq[c ^ 1] = row_frag<D>(q_lds, l32, (ks + 1) * 2 + g);
-          fql[c ^ 1] = row_frag<D>(ql_lds, l32, (ks + 1) * 2 + g);
           fdo[c ^ 1] = row_frag<D>(do_lds, l32, (ks + 1) * 2 + g);
         }
-        sp = mfma32x32x16(fq[c], kf[ks], ks == 0 ? zero : sp);
-        sp = mfma32x32x16(fql[c], kf[ks], sp);
-        sp = mfma32x32x16(fq[c], kl[ks], sp);
+        sp = mfma32x32x16_f16(fq[c], kf[ks], ks == 0 ? zero : sp);
         dp = mfma32x32x16(fdo[c], vf[ks], ks == 0 ? zero : dp);
         if (ks + 1 < NKS) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS reads
-          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMAs
         }
       }
       if (!full) {
@@ -226,11 +217,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 #pragma unroll
       for (int e2 = 0; e2 < 2; ++e2) {
         const bf16x8 pb = pack8(sp, e2 * 8);
-        const bf16x8 dsb = pack8(dp, e2 * 8);
+        const bf16x8 dsh = pack8h(dp, e2 * 8);
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
           dv[db] = mfma32x32x16(frag_rows_tr<D>(do_lds, db * 32, e2, lane), pb, dv[db]);
-          dk[db] = mfma32x32x16(frag_rows_tr<D>(q_lds, db * 32, e2, lane), dsb, dk[db]);
+          dk[db] = mfma32x32x16_f16(frag_rows_tr<D>(q_lds, db * 32, e2, lane), dsh, dk[db]);
         }
       }
     }
@@ -296,21 +287,22 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 
 // ------------------------------------------------------------------- dQ
 // Query rows of 128 (4 waves x 32), key tiles of BKQ staged by DMA one tile
-// ahead, two stages of three row-major tiles: K, K_lo and V (the A operands
+// ahead, two stages of two row-major tiles: K (fp16) and V (the A operands
 // of S^T = K Q^T and dP^T = V dO^T; K read transposed, rows in the
 // accumulator's order, is also the A operand of dQ^T += K^T dS^T).  With
-// 32-key tiles the two stages take 48 KB for D = 128 and two workgroups share
+// 32-key tiles the two stages take 32 KB for D = 128 and two workgroups share
 // a CU, so one wave's softmax runs under the other's MFMAs.
 constexpr int BKQ = 32;
 constexpr int KBQ = BKQ / 32;  // 32 x 32 S^T blocks per tile
 template <int D>
 __global__ __launch_bounds__(256, BKQ == 32 ? 2 : 1) void attn_bwd_dq_kernel(
-    const u16* __restrict__ qkv, const u16* __restrict__ qk_lo, const u16* __restrict__ dcg,
+    const u16* __restrict__ qkv, const u16* __restrict__ qk16, const u16* __restrict__ dcg,
     const float* __restrict__ lse, const float* __restrict__ delta, u16* __restrict__ dz,
     int ld_dz, int s, int n, int window, int nqt, RowSplit rsp) {
   constexpr int NKS = D / 16, ND = D / 32;
   constexpr int OPB = BKQ * D;  // u16 elements of one operand's tile
-  __shared__ __attribute__((aligned(1024))) u16 kv[2 * 3 * OPB];
+  constexpr int STG = 2 * OPB;  // one stage: K (fp16), V (bf16)
+  __shared__ __attribute__((aligned(1024))) u16 kv[2 * STG];
   __shared__ int arrival;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -321,40 +313,34 @@ __global__ __launch_bounds__(256, BKQ == 32 ? 2 : 1) void attn_bwd_dq_kernel(
   const int qt = item.row;
   const int hd = blockIdx.y, bi = blockIdx.z;
   const int hl = n * D, ld = 3 * hl;
-  const u16* Qg = qkv + static_cast<size_t>(bi) * s * ld + hd * D;
-  const u16* Kg = Qg + hl;
-  const u16* Vg = Qg + 2 * hl;
+  const u16* Qh = qk16 + static_cast<size_t>(bi) * s * (2 * hl) + hd * D;  // fp16
+  const u16* Kh = Qh + hl;
+  const u16* Vg = qkv + static_cast<size_t>(bi) * s * ld + hd * D + 2 * hl;  // bf16
   const u16* dOg = dcg + static_cast<size_t>(bi) * s * hl + hd * D;
-  const u16* Qlg = qk_lo + static_cast<size_t>(bi) * s * (2 * hl) + hd * D;
-  const u16* Klg = Qlg + hl;
   const int q0 = qt * BQ, qw0 = q0 + wave * 32, qi = qw0 + l32;
 
   const int kv_begin = item.span.begin;
   const int kv_end = item.span.end;
-  TileDma<D, BKQ, false> dk, dkl, dv;
-  dk.init(Kg, ld, s, wave, lane);
-  dkl.init(Klg, 2 * hl, s, wave, lane);
+  TileDma<D, BKQ, false> dk, dv;
+  dk.init(Kh, 2 * hl, s, wave, lane);
   dv.init(Vg, ld, s, wave, lane);
   const uint32_t kv_lds = __builtin_amdgcn_readfirstlane(lds_address(kv));
   auto issue = [&](uint32_t lds, int kt0) {
     dk.issue(lds, kt0, wave);
-    dkl.issue(lds + OPB * 2, kt0, wave);
-    dv.issue(lds + 2 * OPB * 2, kt0, wave);
+    dv.issue(lds + OPB * 2, kt0, wave);
   };
   if (kv_begin < kv_end) issue(kv_lds, kv_begin);
 
-  bf16x8 qf[NKS], ql[NKS], of[NKS];
+  bf16x8 qf[NKS], of[NKS];  // fp16 query, bf16 dO fragments of this lane's query
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a, c = a;
+    uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
     if (qi < s) {
-      a = *reinterpret_cast<const uint4*>(Qg + qi * ld + ks * 16 + g * 8);
+      a = *reinterpret_cast<const uint4*>(Qh + qi * (2 * hl) + ks * 16 + g * 8);
       b = *reinterpret_cast<const uint4*>(dOg + qi * hl + ks * 16 + g * 8);
-      c = *reinterpret_cast<const uint4*>(Qlg + qi * (2 * hl) + ks * 16 + g * 8);
     }
     qf[ks] = as_bf16x8(a);
     of[ks] = as_bf16x8(b);
-    ql[ks] = as_bf16x8(c);
   }
   const size_t hrow = (static_cast<size_t>(bi) * n + hd) * s;
   const float lq = qi < s ? lse[hrow + qi] : 0.0f;
@@ -371,10 +357,9 @@ __global__ __launch_bounds__(256, BKQ == 32 ? 2 : 1) void attn_bwd_dq_kernel(
   for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKQ) {
     wait_vm_lds<0>();  // this wave's loads of tile kt0 landed
     __syncthreads();   // every wave's; the other stage is free again
-    if (kt0 + BKQ < kv_end) issue(kv_lds + (stage ^ 1) * (3 * OPB * 2), kt0 + BKQ);
-    const u16* k_lds = kv + stage * 3 * OPB;
-    const u16* kl_lds = k_lds + OPB;
-    const u16* v_lds = k_lds + 2 * OPB;
+    if (kt0 + BKQ < kv_end) issue(kv_lds + (stage ^ 1) * (STG * 2), kt0 + BKQ);
+    const u16* k_lds = kv + stage * STG;
+    const u16* v_lds = k_lds + OPB;
     stage ^= 1;
 
     const bool any = qw0 < s && qw0 + 31 >= kt0 && qw0 - (kt0 + BKQ - 1) < window;
@@ -390,10 +375,8 @@ __global__ __launch_bounds__(256, BKQ == 32 ? 2 : 1) void attn_bwd_dq_kernel(
       dpt[kb] = zero;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 kh = row_frag<D>(k_lds, kb * 32 + l32, ks * 2 + g);
-        st[kb] = mfma32x32x16(kh, qf[ks], ks == 0 ? zero : st[kb]);
-        st[kb] = mfma32x32x16(row_frag<D>(kl_lds, kb * 32 + l32, ks * 2 + g), qf[ks], st[kb]);
-        st[kb] = mfma32x32x16(kh, ql[ks], st[kb]);
+        st[kb] = mfma32x32x16_f16(row_frag<D>(k_lds, kb * 32 + l32, ks * 2 + g), qf[ks],
+                                  ks == 0 ? zero : st[kb]);
         dpt[kb] = mfma32x32x16(row_frag<D>(v_lds, kb * 32 + l32, ks * 2 + g), of[ks],
                                ks == 0 ? zero : dpt[kb]);
       }
@@ -424,10 +407,10 @@ __global__ __launch_bounds__(256, BKQ == 32 ? 2 : 1) void attn_bwd_dq_kernel(
     for (int kb = 0; kb < KBQ; ++kb)
 #pragma unroll
       for (int e2 = 0; e2 < 2; ++e2) {
-        const bf16x8 dsb = pack8(st[kb], e2 * 8);
+        const bf16x8 dsh = pack8h(st[kb], e2 * 8);
 #pragma unroll
         for (int db = 0; db < ND; ++db)
-          dq[db] = mfma32x32x16(frag_rows_tr<D>(k_lds, db * 32, kb * 2 + e2, lane), dsb, dq[db]);
+          dq[db] = mfma32x32x16_f16(frag_rows_tr<D>(k_lds, db * 32, kb * 2 + e2, lane), dsh, dq[db]);
       }
   }
 
@@ -479,7 +462,7 @@ __global__ __launch_bounds__(256, BKQ == 32 ? 2 : 1) void attn_bwd_dq_kernel(
 }
 
 template <int D>
-hipError_t bwd_d(const u16* qkv, const u16* qk_lo, const u16* c, const float* lse,
+hipError_t bwd_d(const u16* qkv, const u16* qk16, const u16* c, const float* lse,
                  const u16* dc, float* delta, u16* dz, int ld_dz, int b, int s, int n,
                  int window, const AttnScratch& sc, hipStream_t st) {
   const int T = b * s;
@@ -494,7 +477,7 @@ hipError_t bwd_d(const u16* qkv, const u16* qk_lo, const u16* c, const float* ls
   int kitems = 0;
   e = plan_rows<false>(b, s, n, window, nkt, 2 * BKB * D, sc, &rk, &kitems);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(kitems, n, b), dim3(256), 0, st, qkv, qk_lo,
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(kitems, n, b), dim3(256), 0, st, qkv, qk16,
                      dc, lse, delta, dz, ld_dz, s, n, window, nkt, rk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -503,21 +486,21 @@ hipError_t bwd_d(const u16* qkv, const u16* qk_lo, const u16* c, const float* ls
   int qitems = 0;
   e = plan_rows<true>(b, s, n, window, nqt, BQ * D, sc, &rq, &qitems);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(qitems, n, b), dim3(256), 0, st, qkv, qk_lo, dc,
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(qitems, n, b), dim3(256), 0, st, qkv, qk16, dc,
                      lse, delta, dz, ld_dz, s, n, window, nqt, rq);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attention_bwd(const u16* qkv, const u16* qk_lo, const u16* c,
+hipError_t launch_attention_bwd(const u16* qkv, const u16* qk16, const u16* c,
                                 const float* lse, const u16* dc, float* delta, u16* dz,
                                 int ld_dz, int b, int s, int n, int d, int window,
                                 const AttnScratch& sc, hipStream_t st) {
   if (d == 128)
-    return bwd_d<128>(qkv, qk_lo, c, lse, dc, delta, dz, ld_dz, b, s, n, window, sc, st);
+    return bwd_d<128>(qkv, qk16, c, lse, dc, delta, dz, ld_dz, b, s, n, window, sc, st);
   if (d == 64)
-    return bwd_d<64>(qkv, qk_lo, c, lse, dc, delta, dz, ld_dz, b, s, n, window, sc, st);
+    return bwd_d<64>(qkv, qk16, c, lse, dc, delta, dz, ld_dz, b, s, n, window, sc, st);
   return hipErrorInvalidValue;
 }
 

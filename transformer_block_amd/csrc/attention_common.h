@@ -77,6 +77,18 @@ __device__ __forceinline__ bf16x8 tfrag(const u16* base, int r, int k0, int g) {
   return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
+// Eight accumulator values as fp16 (round to nearest even, no saturation:
+// the attention's dS values stay far inside the fp16 range).
+__device__ __forceinline__ uint32_t pack2h_pk(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, h2));
+}
+__device__ __forceinline__ bf16x8 pack8h(const f32x16& a, int base) {
+  return as_bf16x8(make_uint4(pack2h_pk(a[base + 0], a[base + 1]), pack2h_pk(a[base + 2], a[base + 3]),
+                              pack2h_pk(a[base + 4], a[base + 5]), pack2h_pk(a[base + 6], a[base + 7])));
+}
+
 __device__ __forceinline__ bf16x8 pack8(const f32x16& a, int base) {
   return as_bf16x8(make_uint4(pack2bf_pk(a[base + 0], a[base + 1]), pack2bf_pk(a[base + 2], a[base + 3]),
                               pack2bf_pk(a[base + 4], a[base + 5]), pack2bf_pk(a[base + 6], a[base + 7])));

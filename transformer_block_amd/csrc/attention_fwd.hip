@@ -7,25 +7,26 @@ namespace {
 
 // ------------------------------------------------------------------ forward
 // Stage of BKF keys in LDS, filled by DMA one tile ahead of the matrix cores,
-// two stages: K and K_lo row-major (read by row_frag), V in the outer layout
+// two stages: fp16 K row-major (read by row_frag), bf16 V in the outer layout
 // with its rows in the S^T accumulator's key order (read transposed).
 constexpr float kStale = 8.0f;
 
-// Keys per LDS tile: 32 keys keep the two stages at 48 KB for D = 128, so two
+// Keys per LDS tile: 32 keys keep the two stages at 32 KB for D = 128, so two
 // workgroups share a CU and one's softmax and barrier waits run beside the
-// other's MFMAs (64-key tiles, 96 KB, allow one).
+// other's MFMAs.
 constexpr int BKF = 32;
 constexpr int KB = BKF / 32;  // 32 x 32 S^T blocks per tile
 
 template <int D>
-__global__ __launch_bounds__(256, BKF == 32 ? 2 : 1) void attn_fwd_kernel(const u16* __restrict__ qkv,
-                                                       const u16* __restrict__ qk_lo,
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const u16* __restrict__ qkv,
+                                                       const u16* __restrict__ qk16,
                                                        u16* __restrict__ cout,
                                                        float* __restrict__ lse, int s, int n,
                                                        int window, int nqt, RowSplit rs) {
   constexpr int NKS = D / 16, ND = D / 32;
   constexpr int OPB = BKF * D;  // u16 elements of one operand's tile
-  __shared__ __attribute__((aligned(1024))) u16 kv[2 * 3 * OPB];
+  constexpr int STG = 2 * OPB;  // one stage: K (fp16), V (bf16)
+  __shared__ __attribute__((aligned(1024))) u16 kv[2 * STG];
   __shared__ int arrival;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -36,38 +37,30 @@ __global__ __launch_bounds__(256, BKF == 32 ? 2 : 1) void attn_fwd_kernel(const 
   const int qt = item.row;
   const int hd = blockIdx.y, bi = blockIdx.z;
   const int hl = n * D, ld = 3 * hl;
-  const u16* Qg = qkv + static_cast<size_t>(bi) * s * ld + hd * D;
-  const u16* Kg = Qg + hl;
-  const u16* Vg = Qg + 2 * hl;
-  const u16* Qlg = qk_lo + static_cast<size_t>(bi) * s * (2 * hl) + hd * D;
-  const u16* Klg = Qlg + hl;
+  const u16* Qh = qk16 + static_cast<size_t>(bi) * s * (2 * hl) + hd * D;  // fp16
+  const u16* Kh = Qh + hl;
+  const u16* Vg = qkv + static_cast<size_t>(bi) * s * ld + hd * D + 2 * hl;  // bf16
   const int q0 = qt * BQ, qw0 = q0 + wave * 32, qi = qw0 + l32;
 
   const int kv_begin = item.span.begin;
   const int kv_end = item.span.end;
-  TileDma<D, BKF, false> dk, dkl;
+  TileDma<D, BKF, false> dk;
   TileDma<D, BKF, true> dv;
-  dk.init(Kg, ld, s, wave, lane);
-  dkl.init(Klg, 2 * hl, s, wave, lane);
+  dk.init(Kh, 2 * hl, s, wave, lane);
   dv.init(Vg, ld, s, wave, lane);
   const uint32_t kv_lds = __builtin_amdgcn_readfirstlane(lds_address(kv));
   auto issue = [&](uint32_t lds, int kt0) {
     dk.issue(lds, kt0, wave);
-    dkl.issue(lds + OPB * 2, kt0, wave);
-    dv.issue(lds + 2 * OPB * 2, kt0, wave);
+    dv.issue(lds + OPB * 2, kt0, wave);
   };
   if (kv_begin < kv_end) issue(kv_lds, kv_begin);
 
-  bf16x8 qf[NKS], ql[NKS];
+  bf16x8 qf[NKS];  // fp16 query fragments (B operand of S^T = K Q^T)
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    uint4 t = make_uint4(0u, 0u, 0u, 0u), u = t;
-    if (qi < s) {
-      t = *reinterpret_cast<const uint4*>(Qg + qi * ld + ks * 16 + g * 8);
-      u = *reinterpret_cast<const uint4*>(Qlg + qi * (2 * hl) + ks * 16 + g * 8);
-    }
+    uint4 t = make_uint4(0u, 0u, 0u, 0u);
+    if (qi < s) t = *reinterpret_cast<const uint4*>(Qh + qi * (2 * hl) + ks * 16 + g * 8);
     qf[ks] = as_bf16x8(t);
-    ql[ks] = as_bf16x8(u);
   }
 
   // Running max m is kept in scaled (log2) units: p = exp2(logit * sc - m).
@@ -83,10 +76,9 @@ __global__ __launch_bounds__(256, BKF == 32 ? 2 : 1) void attn_fwd_kernel(const 
   for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKF) {
     wait_vm_lds<0>();  // this wave's loads of tile kt0 landed
     __syncthreads();   // every wave's; the other stage is free again
-    if (kt0 + BKF < kv_end) issue(kv_lds + (stage ^ 1) * (3 * OPB * 2), kt0 + BKF);
-    const u16* k_lds = kv + stage * 3 * OPB;
-    const u16* kl_lds = k_lds + OPB;
-    const u16* v_lds = k_lds + 2 * OPB;
+    if (kt0 + BKF < kv_end) issue(kv_lds + (stage ^ 1) * (STG * 2), kt0 + BKF);
+    const u16* k_lds = kv + stage * STG;
+    const u16* v_lds = k_lds + OPB;
     stage ^= 1;
 
     const bool any = qw0 < s && qw0 + 31 >= kt0 && qw0 - (kt0 + BKF - 1) < window;
@@ -96,28 +88,18 @@ __global__ __launch_bounds__(256, BKF == 32 ? 2 : 1) void attn_fwd_kernel(const 
     // each chain's first product takes a literal zero accumulator
     const f32x16 zero = {};
     f32x16 st[KB];
-    // key fragments of step t + 1 (t = 16-wide k-step ks of key block kb)
-    // read under the MFMAs of step t
-    constexpr int NT = KB * NKS;
-    bf16x8 fk[2], fkl[2];
-    fk[0] = row_frag<D>(k_lds, l32, g);
-    fkl[0] = row_frag<D>(kl_lds, l32, g);
+    // S^T = K Q^T in fp16, one MFMA per 16-wide k-step: the tile's key
+    // fragments are all read first, the products chained after them
+    bf16x8 fk[KB][NKS];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int kb = t / NKS, ks = t % NKS, c = t & 1;
-      if (t + 1 < NT) {
-        const int r = ((t + 1) / NKS) * 32 + l32, kk = ((t + 1) % NKS) * 2 + g;
-        fk[c ^ 1] = row_frag<D>(k_lds, r, kk);
-        fkl[c ^ 1] = row_frag<D>(kl_lds, r, kk);
-      }
-      st[kb] = mfma32x32x16(fk[c], qf[ks], ks == 0 ? zero : st[kb]);
-      st[kb] = mfma32x32x16(fkl[c], qf[ks], st[kb]);
-      st[kb] = mfma32x32x16(fk[c], ql[ks], st[kb]);
-      if (t + 1 < NT) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // MFMAs
-      }
-    }
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) fk[kb][ks] = row_frag<D>(k_lds, kb * 32 + l32, ks * 2 + g);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        st[kb] = mfma32x32x16_f16(fk[kb][ks], qf[ks], ks == 0 ? zero : st[kb]);
     float mx = -INFINITY;
     if (full) {
 #pragma unroll
@@ -241,25 +223,25 @@ __global__ __launch_bounds__(256, BKF == 32 ? 2 : 1) void attn_fwd_kernel(const 
 }
 
 template <int D>
-hipError_t fwd_d(const u16* qkv, const u16* qk_lo, u16* c, float* lse, int b, int s, int n,
+hipError_t fwd_d(const u16* qkv, const u16* qk16, u16* c, float* lse, int b, int s, int n,
                  int window, const AttnScratch& sc, hipStream_t st) {
   const int nqt = (s + BQ - 1) / BQ;
   RowSplit rs;
   int items = 0;
   const hipError_t e = plan_rows<true>(b, s, n, window, nqt, BQ * D + 2 * 256, sc, &rs, &items);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(items, n, b), dim3(256), 0, st, qkv, qk_lo, c, lse,
+  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(items, n, b), dim3(256), 0, st, qkv, qk16, c, lse,
                      s, n, window, nqt, rs);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attention_fwd(const u16* qkv, const u16* qk_lo, u16* c, float* lse, int b,
+hipError_t launch_attention_fwd(const u16* qkv, const u16* qk16, u16* c, float* lse, int b,
                                 int s, int n, int d, int window, const AttnScratch& sc,
                                 hipStream_t st) {
-  if (d == 128) return fwd_d<128>(qkv, qk_lo, c, lse, b, s, n, window, sc, st);
-  if (d == 64) return fwd_d<64>(qkv, qk_lo, c, lse, b, s, n, window, sc, st);
+  if (d == 128) return fwd_d<128>(qkv, qk16, c, lse, b, s, n, window, sc, st);
+  if (d == 64) return fwd_d<64>(qkv, qk16, c, lse, b, s, n, window, sc, st);
   return hipErrorInvalidValue;
 }
 

@@ -45,6 +45,31 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// The same product with fp16 operands (v_mfma_f32_32x32x16_f16, same lane
+// layout and rate).  Fragments travel as 16-bit words in bf16x8 containers.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16 mfma32x32x16_f16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// fp32 -> fp16, round to nearest even, saturated to the largest finite fp16
+// (65504) so that an out-of-range value never becomes an infinity.
+constexpr float kF16Max = 65504.0f;
+__device__ __forceinline__ uint32_t pack2h(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  lo = __builtin_amdgcn_fmed3f(lo, -kF16Max, kF16Max);
+  hi = __builtin_amdgcn_fmed3f(hi, -kF16Max, kF16Max);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, h2));
+}
+__device__ __forceinline__ float lo_h(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
+}
+__device__ __forceinline__ float hi_h(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ i32x8 cat8(uint4 lo, uint4 hi) {

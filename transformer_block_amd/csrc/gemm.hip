@@ -335,6 +335,16 @@ __device__ __forceinline__ void store16bf(u16* p, const float* v) {
   reinterpret_cast<uint4*>(p)[1] = b;
 }
 
+__device__ __forceinline__ void store16h(u16* p, const float* v) {
+  uint4 a, b;
+  a.x = pack2h(v[0], v[1]);   a.y = pack2h(v[2], v[3]);
+  a.z = pack2h(v[4], v[5]);   a.w = pack2h(v[6], v[7]);
+  b.x = pack2h(v[8], v[9]);   b.y = pack2h(v[10], v[11]);
+  b.z = pack2h(v[12], v[13]); b.w = pack2h(v[14], v[15]);
+  reinterpret_cast<uint4*>(p)[0] = a;
+  reinterpret_cast<uint4*>(p)[1] = b;
+}
+
 __device__ __forceinline__ void load16bf(const u16* p, float* v) {
   const uint4 a = reinterpret_cast<const uint4*>(p)[0];
   const uint4 b = reinterpret_cast<const uint4*>(p)[1];
@@ -363,24 +373,9 @@ template <int MODE>
 __device__ __forceinline__ void epi_row16(const Epilogue& e, int region, int r, int c, float* v) {
   if constexpr (MODE == EPI_QKV_GELU || MODE == EPI_QKV_SWIGLU) {
     const int gc = c + e.col_base;
-    if (region == 0) {
-      float lo[16];
-      uint4 a, b;
-      uint32_t* w = reinterpret_cast<uint32_t*>(&a);
-      uint32_t* x = reinterpret_cast<uint32_t*>(&b);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        w[i] = pack2bf(v[2 * i], v[2 * i + 1]);
-        x[i] = pack2bf(v[8 + 2 * i], v[9 + 2 * i]);
-        lo[2 * i] = v[2 * i] - lo_bf(w[i]);
-        lo[2 * i + 1] = v[2 * i + 1] - hi_bf(w[i]);
-        lo[8 + 2 * i] = v[8 + 2 * i] - lo_bf(x[i]);
-        lo[9 + 2 * i] = v[9 + 2 * i] - hi_bf(x[i]);
-      }
-      uint4* o = reinterpret_cast<uint4*>(e.o0 + r * e.ld0 + gc);
-      o[0] = a;
-      o[1] = b;
-      store16bf(e.o3 + r * e.ld3 + gc, lo);
+    if (region == 0) {  // the q, k columns: bf16 and fp16 copies
+      store16bf(e.o0 + r * e.ld0 + gc, v);
+      store16h(e.o3 + r * e.ld3 + gc, v);
     } else if (region == 1 || MODE == EPI_QKV_SWIGLU) {  // SwiGLU's FC1 side: epi_swiglu16
       store16bf(e.o0 + r * e.ld0 + gc, v);
     } else {
@@ -556,8 +551,11 @@ __device__ __forceinline__ int part_slot(const SkPlan& pl, int i) {
 // FMT 0: bf16 operands; FP8 operands otherwise, FMT - 1 = fa + 2 fb with
 // fa, fb the operands' formats (Fp8Format: 0 E4M3, 1 E5M2).  MX: FP8 with
 // block scales instead of current scales.
-template <int AMAJ, int BMAJ, int MODE, int FMT = 0, bool MX = false>
+// H0: problem 0's operands are fp16 (v_mfma_f32_32x32x16_f16), problem 1's
+// bf16; the same tiles, layouts and loads carry both.
+template <int AMAJ, int BMAJ, int MODE, int FMT = 0, bool MX = false, bool H0 = false>
 __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
+  static_assert(!H0 || FMT == 0, "fp16 operands are 16-bit");
   constexpr bool F8 = FMT != 0;
   static_assert(!MX || F8, "block scales come with FP8 operands");
   // MX loop: XS single-buffers the A fragments (below); the other MX modes
@@ -647,11 +645,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
     for (int j = 0; j < FN; ++j)
       fb[slot][j] = frag<BMAJ>(st + TILE * BK, wn * WN + j * 32, ks, lane, koff[ks]);
   };
-  auto mma = [&](int slot) {
+  auto mma = [&](int slot, auto f16) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(fa[slot][i], fb[slot][j], acc[i][j]);
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (decltype(f16)::value)
+          acc[i][j] = mfma32x32x16_f16(fa[slot][i], fb[slot][j], acc[i][j]);
+        else
+          acc[i][j] = mfma32x32x16(fa[slot][i], fb[slot][j], acc[i][j]);
+      }
   };
   // FP8: the 32 bytes of bf16 k-steps 2 half and 2 half + 1 (64 k-values).
   // MX (double-buffered loop): the scale codes of the lane's row in each
@@ -825,25 +828,33 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
         pin8();
       }
     } else {
-    rd(ring, 0, 0);
-    for (int j = 0; j < len; ++j) {
-      u16* cur = ring + (j & 1) * STAGE;
-      rd(cur, 1, 1);
-      mma(0);
-      pin();
-      rd(cur, 2, 0);
-      mma(1);
-      pin();
-      rd(cur, 3, 1);
-      mma(0);
-      pin();
-      wait_vm_lds<0>();  // tile j+1 landed (the loader waves' loads)
-      __syncthreads();   // tile j+1 in LDS for every wave; tile j read by every wave
-      issue_to(s, j & 1, j + 2);
-      rd(ring + ((j + 1) & 1) * STAGE, 0, 0);  // unused after the last step
-      mma(1);
-      pin();
-    }
+      auto loop16 = [&](auto f16) {
+        rd(ring, 0, 0);
+        for (int j = 0; j < len; ++j) {
+          u16* cur = ring + (j & 1) * STAGE;
+          rd(cur, 1, 1);
+          mma(0, f16);
+          pin();
+          rd(cur, 2, 0);
+          mma(1, f16);
+          pin();
+          rd(cur, 3, 1);
+          mma(0, f16);
+          pin();
+          wait_vm_lds<0>();  // tile j+1 landed (the loader waves' loads)
+          __syncthreads();   // tile j+1 in LDS for every wave; tile j read by every wave
+          issue_to(s, j & 1, j + 2);
+          rd(ring + ((j + 1) & 1) * STAGE, 0, 0);  // unused after the last step
+          mma(1, f16);
+          pin();
+        }
+      };
+      if constexpr (H0) {
+        if (s.prob == 0) loop16(std::true_type{});
+        else loop16(std::false_type{});
+      } else {
+        loop16(std::false_type{});
+      }
     }
 
     // ---- the next item's first stage tile goes out before this one's
@@ -1287,12 +1298,14 @@ hipError_t launch_plan_fp8(const SkPlan& pl, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int AMAJ, int BMAJ, int MODE>
+template <int AMAJ, int BMAJ, int MODE, bool H0 = false>
 hipError_t launch_plan(const SkPlan& pl, int grid, hipStream_t s) {
+  static_assert(!H0 || !(AMAJ == KMAJOR && BMAJ == KMAJOR), "fp16 problems run on eight waves");
   if constexpr (AMAJ == KMAJOR && BMAJ == KMAJOR)
     hipLaunchKernelGGL((gemm_kernel4<AMAJ, BMAJ, MODE>), dim3(grid), dim3(256), 0, s, pl);
   else
-    hipLaunchKernelGGL((gemm_sk_kernel<AMAJ, BMAJ, MODE>), dim3(grid), dim3(64 * WAVES), 0, s, pl);
+    hipLaunchKernelGGL((gemm_sk_kernel<AMAJ, BMAJ, MODE, 0, false, H0>), dim3(grid),
+                       dim3(64 * WAVES), 0, s, pl);
   return hipGetLastError();
 }
 
@@ -1386,11 +1399,20 @@ hipError_t launch_zero_i32(int* p, int n, hipStream_t s) {
 
 hipError_t launch_gemm_group(const GemmProblem* probs, int nprob, Major a_major,
                              Major b_major, EpiMode mode, const GemmScratch& ws,
-                             hipStream_t s) {
+                             hipStream_t s, bool f16_prob0) {
   SkPlan pl;
   int grid = 0;
   const hipError_t e = build_plan(probs, nprob, a_major, b_major, ws, 0, &pl, &grid);
   if (e != hipSuccess) return e;
+  if (f16_prob0) {
+    // fp16 problem 0: the [q | k] product beside [v | FC1] (eight waves)
+    if (a_major != KMAJOR || b_major != OUTER_MAJOR) return hipErrorInvalidValue;
+    if (mode == EPI_QKV_GELU)
+      return launch_plan<KMAJOR, OUTER_MAJOR, EPI_QKV_GELU, true>(pl, grid, s);
+    if (mode == EPI_QKV_SWIGLU)
+      return launch_plan<KMAJOR, OUTER_MAJOR, EPI_QKV_SWIGLU, true>(pl, grid, s);
+    return hipErrorInvalidValue;
+  }
   if (a_major == KMAJOR && b_major == OUTER_MAJOR) {
     if (mode == EPI_QKV_GELU) return launch_plan<KMAJOR, OUTER_MAJOR, EPI_QKV_GELU>(pl, grid, s);
     if (mode == EPI_QKV_SWIGLU)

@@ -35,7 +35,7 @@ enum Major { KMAJOR = 0, OUTER_MAJOR = 1 };
 // What the GEMM does with each fp32 result v at (row r, column c).
 enum EpiMode {
   EPI_QKV_GELU = 0,  // with gc = c + col_base: gc < split: o0[r*ld0+gc] = bf16(v), and
-                     // for gc < lo_cols also o3[r*ld3+gc] = bf16(v - bf16(v));
+                     // for gc < lo_cols also o3[r*ld3+gc] = fp16(v) (saturated);
                      // else o1 = v (u), o2 = GeLU(v) (g) at column gc - split
   EPI_RESIDUAL = 1,  // o0[r*ld0+c] = v + i0[r*ld0+c]
   EPI_DGELU = 2,     // c < split: o0[r*ld0+c] = v; else o1[r*ld1+col_off1+c-split] =
@@ -119,10 +119,12 @@ hipError_t launch_gemm(int M, int N, int K, const Operand& A, Major a_major,
                        const Epilogue& epi, const GemmScratch& scratch, hipStream_t stream);
 
 // Up to two independent products sharing operand orders and epilogue kind,
-// in one launch (the tiles of both fill the GPU together).
+// in one launch (the tiles of both fill the GPU together).  f16_prob0:
+// problem 0's operands hold fp16 values instead of bf16 (the [q | k]
+// product of the [QKV | FC1] launch; KMAJOR x OUTER_MAJOR, EPI_QKV_* only).
 hipError_t launch_gemm_group(const GemmProblem* probs, int nprob, Major a_major,
                              Major b_major, EpiMode mode, const GemmScratch& scratch,
-                             hipStream_t stream);
+                             hipStream_t stream, bool f16_prob0 = false);
 
 // FP8 product: both operands k-contiguous 8-bit matrices (element (r, k) at
 // byte r*ld + k, ld a multiple of 16), K a multiple of 128, fa / fb their
@@ -176,12 +178,18 @@ hipError_t launch_cast_mx(const CastSrc& x, Fp8Format fmt, uint8_t* rows, int ld
                           int rs_ld, uint8_t* cols, int ldc, uint32_t* cs, int cs_ld,
                           hipStream_t stream);
 
-// LayerNorm forward over rows of x [T, h]: a = bf16(LN(x)) and its rounding
-// residual a_lo = bf16(LN(x) - a) (skipped when a_lo is null), mu, rstd (fp32).
-// rms: RMSNorm instead (no mean, no beta; mu is written as 0).
+// LayerNorm forward over rows of x [T, h]: a = bf16(LN(x)) and an fp16 copy
+// a16 = fp16(LN(x)) of the same fp32 values (skipped when a16 is null), mu,
+// rstd (fp32).  rms: RMSNorm instead (no mean, no beta; mu is written as 0).
 hipError_t launch_layernorm_fwd(const u16* x, const u16* gamma, const u16* beta,
-                                u16* a, u16* a_lo, float* mu, float* rstd, int T, int h,
+                                u16* a, u16* a16, float* mu, float* rstd, int T, int h,
                                 float eps, hipStream_t stream, bool rms = false);
+
+// dst = fp16(src) for a [rows, cols] block of a row-major bf16 matrix (cols
+// and both row strides multiples of 8; rounding to nearest even, saturated
+// at 65504).
+hipError_t launch_cast_f16(const u16* src, int ld_src, int rows, int cols, u16* dst, int ld_dst,
+                           hipStream_t stream);
 
 // LayerNorm backward plus residual: dx = dy + LN'(da); per-block partial sums
 // of dgamma, dbeta into `partials` [nblk, 2, h], then reduced into bf16.
@@ -205,16 +213,18 @@ struct AttnScratch {
 // Compute units of the current device (0 if the query fails).
 int device_compute_units();
 
-// Sliding-window causal flash attention, forward: reads q, k, v column blocks
-// of qkv [b*s, 3*n*d] and the rounding residuals of q and k, qk_lo [b*s, 2*n*d];
-// writes c [b*s, n*d] and the base-2 log-sum-exp lse [b, n, s].
-hipError_t launch_attention_fwd(const u16* qkv, const u16* qk_lo, u16* c, float* lse,
+// Sliding-window causal flash attention, forward: reads the bf16 v column
+// block of qkv [b*s, 3*n*d] and the fp16 q and k of qk16 [b*s, 2*n*d]
+// (logits from one fp16 product); writes c [b*s, n*d] and the base-2
+// log-sum-exp lse [b, n, s].
+hipError_t launch_attention_fwd(const u16* qkv, const u16* qk16, u16* c, float* lse,
                                 int b, int s, int n, int d, int window,
                                 const AttnScratch& scratch, hipStream_t stream);
 
 // Attention backward.  delta[b,n,s] = rowsum(dc * c) per head first, then
 // dk, dv and dq written into the first 3*n*d columns of dz [b*s, ld_dz].
-hipError_t launch_attention_bwd(const u16* qkv, const u16* qk_lo, const u16* c,
+// q and k are read from qk16 (fp16), v from qkv (bf16).
+hipError_t launch_attention_bwd(const u16* qkv, const u16* qk16, const u16* c,
                                 const float* lse, const u16* dc, float* delta, u16* dz,
                                 int ld_dz, int b, int s, int n, int d, int window,
                                 const AttnScratch& scratch, hipStream_t stream);

@@ -8,14 +8,16 @@
 // Forward: one 256-thread workgroup per token row; the row (h <= 16384 bf16)
 // is read once into registers with 16-byte loads, mean and variance come from
 // two block reductions over the register copy, and a = gamma*(x-mu)*rstd+beta
-// is written back in bf16 with 16-byte stores, together with its rounding
-// residual a_lo = bf16(a_fp32 - a) (used where bf16 rounding of a would be
-// amplified: the query/key projection feeding the softmax logits).
+// is written back in bf16 with 16-byte stores, together with an fp16 copy a16
+// of the same fp32 values (used where bf16 rounding of a would be amplified:
+// the query/key projection feeding the softmax logits, formed in fp16).
 // Backward: each workgroup walks a strided set of rows (the next row's loads
 // in flight while the current one is finished), computes
 //   dx = dy + rstd * (g - mean(g) - xhat * mean(g * xhat)),  g = da * gamma,
 // and keeps per-column partial sums of dgamma = sum da*xhat and dbeta = sum da
 // in registers; a second kernel reduces the per-workgroup partials.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(LN_THREADS) void ln_fwd_kernel(const u16* __restric
                                                             const u16* __restrict__ gamma,
                                                             const u16* __restrict__ beta,
                                                             u16* __restrict__ a,
-                                                            u16* __restrict__ a_lo,
+                                                            u16* __restrict__ a16,
                                                             float* __restrict__ mu_out,
                                                             float* __restrict__ rstd_out,
                                                             int h, float eps) {
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(LN_THREADS) void ln_fwd_kernel(const u16* __restric
   const float var = block_sum(sq, red) / static_cast<float>(h);
   const float rstd = 1.0f / sqrtf(var + eps);
   u16* ar = a + static_cast<size_t>(row) * h;
-  u16* alr = a_lo != nullptr ? a_lo + static_cast<size_t>(row) * h : nullptr;
+  u16* ahr = a16 != nullptr ? a16 + static_cast<size_t>(row) * h : nullptr;
 #pragma unroll
   for (int i = 0; i < LN_MAXCH; ++i) {
     const int c = tid + i * LN_THREADS;
@@ -88,20 +90,59 @@ __global__ __launch_bounds__(LN_THREADS) void ln_fwd_kernel(const u16* __restric
       float gm[8], bt[8];
       unpack8(*reinterpret_cast<const uint4*>(gamma + c * 8), gm);
       if (!RMS) unpack8(*reinterpret_cast<const uint4*>(beta + c * 8), bt);
-      uint32_t o[4], ol[4];
+      uint32_t o[4], oh[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float v0 = (v[i][2 * j] - mu) * rstd * gm[2 * j] + (RMS ? 0.0f : bt[2 * j]);
         const float v1 = (v[i][2 * j + 1] - mu) * rstd * gm[2 * j + 1] + (RMS ? 0.0f : bt[2 * j + 1]);
         o[j] = pack2bf(v0, v1);
-        ol[j] = pack2bf(v0 - lo_bf(o[j]), v1 - hi_bf(o[j]));
+        oh[j] = pack2h(v0, v1);
       }
       *reinterpret_cast<uint4*>(ar + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
-      if (a_lo != nullptr)
-        *reinterpret_cast<uint4*>(alr + c * 8) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+      if (a16 != nullptr)
+        *reinterpret_cast<uint4*>(ahr + c * 8) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
     }
   }
   if (tid == 0) { mu_out[row] = mu; rstd_out[row] = rstd; }
+}
+
+// dst[r][c] = fp16(src[r][c]) for a [rows, cols] block of a bf16 matrix
+// (cols a multiple of 8, row strides ld_src and ld_dst in elements): the
+// fp16 copy of the query/key columns of W_qkv for the fp16 q, k product.
+// Each thread converts 8 consecutive values per 16-byte load and store, four
+// loads in flight.  The conversion is exact for every bf16 value inside the
+// fp16 normal range; smaller magnitudes round to fp16 subnormals (absolute
+// error <= 2^-25) and larger ones saturate at 65504.
+__global__ __launch_bounds__(256) void cast_f16_kernel(const u16* __restrict__ src, int ld_src,
+                                                       u16* __restrict__ dst, int ld_dst,
+                                                       int cols8, long total8) {
+  const long stride = static_cast<long>(gridDim.x) * 256;
+  for (long base = static_cast<long>(blockIdx.x) * 256 + threadIdx.x; base < total8;
+       base += 4 * stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const long i = base + u * stride;
+      if (i < total8) {
+        const long r = i / cols8, c = (i % cols8) * 8;
+        v[u] = *reinterpret_cast<const uint4*>(src + r * ld_src + c);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const long i = base + u * stride;
+      if (i < total8) {
+        const long r = i / cols8, c = (i % cols8) * 8;
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(&v[u]);
+        uint4 o;
+        o.x = pack2h(lo_bf(w[0]), hi_bf(w[0]));
+        o.y = pack2h(lo_bf(w[1]), hi_bf(w[1]));
+        o.z = pack2h(lo_bf(w[2]), hi_bf(w[2]));
+        o.w = pack2h(lo_bf(w[3]), hi_bf(w[3]));
+        *reinterpret_cast<uint4*>(dst + r * ld_dst + c) = o;
+      }
+    }
+  }
 }
 
 constexpr int LNB_THREADS = 512;  // 8 waves: two per SIMD, up to 256 VGPRs each
@@ -280,11 +321,23 @@ __global__ __launch_bounds__(64 * LNR_WAVES) void ln_bwd_reduce_kernel(
 }  // namespace
 
 hipError_t launch_layernorm_fwd(const u16* x, const u16* gamma, const u16* beta, u16* a,
-                                u16* a_lo, float* mu, float* rstd, int T, int h, float eps,
+                                u16* a16, float* mu, float* rstd, int T, int h, float eps,
                                 hipStream_t s, bool rms) {
   if (T <= 0) return hipSuccess;
   hipLaunchKernelGGL(rms ? ln_fwd_kernel<true> : ln_fwd_kernel<false>, dim3(T), dim3(LN_THREADS),
-                     0, s, x, gamma, beta, a, a_lo, mu, rstd, h, eps);
+                     0, s, x, gamma, beta, a, a16, mu, rstd, h, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_f16(const u16* src, int ld_src, int rows, int cols, u16* dst, int ld_dst,
+                           hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (cols % 8 != 0 || ld_src % 8 != 0 || ld_dst % 8 != 0 || ld_src < cols || ld_dst < cols)
+    return hipErrorInvalidValue;
+  const long total8 = static_cast<long>(rows) * (cols / 8);
+  const long blocks = std::min<long>((total8 + 4 * 256 - 1) / (4 * 256), 4096);
+  hipLaunchKernelGGL(cast_f16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, src,
+                     ld_src, dst, ld_dst, cols / 8, total8);
   return hipGetLastError();
 }
 

@@ -4,9 +4,10 @@
 //   y = x + Attn(LN(x)) + MLP(LN(x))
 // (MegaScale reading notes, section 1.1, eq (4)).
 //
-// Forward, four launches on the caller's stream:
-//   LN(x) -> a (+ residual a_lo);  a x [W_qkv | W_fc1] -> qkv, u, g = GeLU(u)
-//   (the q, k columns from [a | a_lo], kept as value + residual);
+// Forward, five launches on the caller's stream:
+//   LN(x) -> a (+ its fp16 copy a16);  the q, k columns of W_qkv -> fp16;
+//   a x [W_qkv | W_fc1] -> qkv, u, g = GeLU(u) (the q, k columns as the fp16
+//   product a16 x W_q|k, kept in bf16 and in fp16 for the logits);
 //   sliding-window flash attention -> c, lse;  [c | g] x [W_o ; W_fc2] + x -> y.
 // Backward:
 //   dy x [W_o ; W_fc2]^T -> dc, du = dg * GeLU'(u);  attention backward
@@ -22,6 +23,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <climits>
 #include <initializer_list>
 
@@ -94,8 +96,8 @@ SavedLayout saved_layout(const Shape& s) {
   put(PTB_SAVED_G, s.T * s.f * 2);
   put(PTB_SAVED_C, s.T * s.hl * 2);
   put(PTB_SAVED_LSE, s.b * s.n * s.s * 4);
-  put(PTB_SAVED_A_LO, s.T * s.h * 2);
-  put(PTB_SAVED_QK_LO, s.T * 2 * s.hl * 2);
+  put(PTB_SAVED_A16, s.T * s.h * 2);
+  put(PTB_SAVED_QK16, s.T * 2 * s.hl * 2);
   L.total = o;
   return L;
 }
@@ -115,24 +117,30 @@ int max_gemm_tiles(const Shape& s) {
 }
 
 struct WorkLayout {
-  size_t gemm_partials, counters, dc, dz, da, delta, partials, total;
+  size_t gemm_partials, counters, dc, dz, da, delta, partials, wqk16, total;
   int max_tiles;
 };
 
-// Forward scratch is the leading part (GEMM partial tiles and counters);
-// the backward uses all of it.
+// Bytes of the fp16 copy of W_qkv's q and k columns, [h, 2 h_l].
+size_t wqk16_bytes(const Shape& s) { return static_cast<size_t>(s.h) * 2 * s.hl * 2; }
+
+// GEMM partial tiles and counters first (forward and backward), then the
+// backward's intermediate gradients; the forward's fp16 copy of the q, k
+// weight columns lies over the latter (the forward is done with it before
+// the backward starts).
 WorkLayout work_layout(const Shape& s) {
   WorkLayout W;
   size_t o = 0;
   W.max_tiles = max_gemm_tiles(s);
   W.gemm_partials = o; o = align_up(o + ptb::kGemmPartialBytes);
   W.counters = o; o = align_up(o + static_cast<size_t>(W.max_tiles) * 4);
+  W.wqk16 = o;
   W.dc = o; o = align_up(o + s.T * s.hl * 2);
   W.dz = o; o = align_up(o + s.T * s.N1 * 2);
   W.da = o; o = align_up(o + s.T * s.h * 2);
   W.delta = o; o = align_up(o + s.b * s.n * s.s * 4);
   W.partials = o; o = align_up(o + static_cast<size_t>(ptb::layernorm_bwd_blocks(s.T)) * 2 * s.h * 4);
-  W.total = o;
+  W.total = std::max(o, align_up(W.wqk16 + wqk16_bytes(s)));
   return W;
 }
 
@@ -149,9 +157,9 @@ SerialSavedLayout serial_saved_layout(const Shape& s) {
   put(PTB_SERIAL_A1, s.T * s.h * 2);
   put(PTB_SERIAL_MU1, s.T * 4);
   put(PTB_SERIAL_RSTD1, s.T * 4);
-  put(PTB_SERIAL_A1_LO, s.T * s.h * 2);
+  put(PTB_SERIAL_A1_16, s.T * s.h * 2);
   put(PTB_SERIAL_QKV, s.T * 3 * s.hl * 2);
-  put(PTB_SERIAL_QK_LO, s.T * 2 * s.hl * 2);
+  put(PTB_SERIAL_QK16, s.T * 2 * s.hl * 2);
   put(PTB_SERIAL_C, s.T * s.hl * 2);
   put(PTB_SERIAL_LSE, s.b * s.n * s.s * 4);
   put(PTB_SERIAL_X1, s.T * s.h * 2);
@@ -182,7 +190,7 @@ int serial_max_tiles(const Shape& s) {
 // forward needs), then the backward's intermediate gradients.  da holds the
 // LN2 input gradient, then the LN1 one.
 struct SerialWorkLayout {
-  size_t gemm_partials, counters, du, da, dx1, dc, dz, delta, partials, total;
+  size_t gemm_partials, counters, du, da, dx1, dc, dz, delta, partials, wqk16, total;
   int max_tiles;
 };
 
@@ -192,6 +200,7 @@ SerialWorkLayout serial_work_layout(const Shape& s) {
   W.max_tiles = serial_max_tiles(s);
   W.gemm_partials = o; o = align_up(o + ptb::kGemmPartialBytes);
   W.counters = o; o = align_up(o + static_cast<size_t>(W.max_tiles) * 4);
+  W.wqk16 = o;  // forward only, over the backward's region
   W.du = o; o = align_up(o + s.T * s.f1 * 2);
   W.da = o; o = align_up(o + s.T * s.h * 2);
   W.dx1 = o; o = align_up(o + s.T * s.h * 2);
@@ -199,7 +208,7 @@ SerialWorkLayout serial_work_layout(const Shape& s) {
   W.dz = o; o = align_up(o + s.T * 3 * s.hl * 2);
   W.delta = o; o = align_up(o + s.b * s.n * s.s * 4);
   W.partials = o; o = align_up(o + static_cast<size_t>(ptb::layernorm_bwd_blocks(s.T)) * 2 * s.h * 4);
-  W.total = o;
+  W.total = std::max(o, align_up(W.wqk16 + wqk16_bytes(s)));
   return W;
 }
 
@@ -512,30 +521,34 @@ int32_t ptb_forward_timed(const ptb_dims* dims, const void* x, const void* ln_ga
   u16* g = at<u16>(saved, L.off[PTB_SAVED_G]);
   u16* c = at<u16>(saved, L.off[PTB_SAVED_C]);
   float* lse = at<float>(saved, L.off[PTB_SAVED_LSE]);
-  u16* a_lo = at<u16>(saved, L.off[PTB_SAVED_A_LO]);
-  u16* qk_lo = at<u16>(saved, L.off[PTB_SAVED_QK_LO]);
+  u16* a16 = at<u16>(saved, L.off[PTB_SAVED_A16]);
+  u16* qk16 = at<u16>(saved, L.off[PTB_SAVED_QK16]);
+  u16* wqk16 = at<u16>(workspace, W.wqk16);
   const u16* X = static_cast<const u16*>(x);
   const u16* Wqkv = static_cast<const u16*>(w_qkv);
 
   PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
   PTB_STAGE(0, ptb::launch_layernorm_fwd(X, static_cast<const u16*>(ln_gamma),
-                                    static_cast<const u16*>(ln_beta), a, a_lo, mu, rstd,
+                                    static_cast<const u16*>(ln_beta), a, a16, mu, rstd,
                                     static_cast<int>(s.T), static_cast<int>(s.h), dims->ln_eps,
                                     strm, s.rms));
+  PTB_STAGE(1, ptb::launch_cast_f16(Wqkv, static_cast<int>(3 * s.hl), static_cast<int>(s.h),
+                                    static_cast<int>(2 * s.hl), wqk16,
+                                    static_cast<int>(2 * s.hl), strm));
   {  // [QKV | FC1] projection in one launch of two products:
-     //   [q | k] = [a | a_lo] x [W_q|k ; W_q|k]   (stored as value + residual)
+     //   [q | k] = a16 x W_q|k in fp16 (stored in bf16 and in fp16)
      //   [v | u] = a x [W_v | W_fc1], with g = GeLU(u) on the FC1 columns
      //   (SwiGLU: u = [u1 | u3] in 32-column blocks, g = silu(u1) * u3)
     ptb::Epilogue e{};
     e.o0 = qkv; e.ld0 = static_cast<int>(3 * s.hl);
     e.o1 = u; e.o2 = g; e.ld1 = static_cast<int>(s.f1); e.ld2 = static_cast<int>(s.f);
-    e.o3 = qk_lo; e.ld3 = static_cast<int>(2 * s.hl); e.lo_cols = static_cast<int>(2 * s.hl);
+    e.o3 = qk16; e.ld3 = static_cast<int>(2 * s.hl); e.lo_cols = static_cast<int>(2 * s.hl);
     e.split = static_cast<int>(3 * s.hl);
     ptb::GemmProblem pr[2];
     pr[0].M = static_cast<int>(s.T); pr[0].N = static_cast<int>(2 * s.hl);
-    pr[0].K = static_cast<int>(2 * s.h);
-    pr[0].A = two(a, s.h, s.T, a_lo, s.h, s.T, s.h, 1);
-    pr[0].B = two(Wqkv, 3 * s.hl, s.h, Wqkv, 3 * s.hl, s.h, s.h, 1);
+    pr[0].K = static_cast<int>(s.h);
+    pr[0].A = one(a16, s.h, s.T);
+    pr[0].B = one(wqk16, 2 * s.hl, s.h);
     pr[0].epi = e;
     pr[0].epi.col_base = 0;
     pr[1].M = static_cast<int>(s.T); pr[1].N = static_cast<int>(s.hl + s.f1);
@@ -546,19 +559,19 @@ int32_t ptb_forward_timed(const ptb_dims* dims, const void* x, const void* ln_ga
     pr[1].B.bytes0 = view_bytes(3 * s.hl, s.h, s.hl);
     pr[1].epi = e;
     pr[1].epi.col_base = static_cast<int>(2 * s.hl);
-    PTB_STAGE(1, ptb::launch_gemm_group(pr, 2, ptb::KMAJOR, ptb::OUTER_MAJOR,
+    PTB_STAGE(2, ptb::launch_gemm_group(pr, 2, ptb::KMAJOR, ptb::OUTER_MAJOR,
                                         s.swiglu ? ptb::EPI_QKV_SWIGLU : ptb::EPI_QKV_GELU, gs,
-                                        strm));
+                                        strm, /*f16_prob0=*/true));
   }
   const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
                             gs.max_tiles, ptb::device_compute_units()};
-  PTB_STAGE(2, ptb::launch_attention_fwd(qkv, qk_lo, c, lse, static_cast<int>(s.b),
+  PTB_STAGE(3, ptb::launch_attention_fwd(qkv, qk16, c, lse, static_cast<int>(s.b),
                                     static_cast<int>(s.s), static_cast<int>(s.n),
                                     static_cast<int>(s.d), static_cast<int>(s.w), as, strm));
   {  // [O ; FC2] projection plus the residual
     ptb::Epilogue e{};
     e.o0 = static_cast<u16*>(y); e.i0 = X; e.ld0 = static_cast<int>(s.h);
-    PTB_STAGE(3, ptb::launch_gemm(
+    PTB_STAGE(4, ptb::launch_gemm(
         static_cast<int>(s.T), static_cast<int>(s.h), static_cast<int>(s.K2),
         two(c, s.hl, s.T, g, s.f, s.T, s.hl, 1), ptb::KMAJOR,
         two(static_cast<const u16*>(w_o), s.h, s.hl, static_cast<const u16*>(w_fc2), s.h, s.f,
@@ -591,7 +604,7 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
   const u16* g = at<u16>(saved, L.off[PTB_SAVED_G]);
   const u16* c = at<u16>(saved, L.off[PTB_SAVED_C]);
   const float* lse = at<float>(saved, L.off[PTB_SAVED_LSE]);
-  const u16* qk_lo = at<u16>(saved, L.off[PTB_SAVED_QK_LO]);
+  const u16* qk16 = at<u16>(saved, L.off[PTB_SAVED_QK16]);
   u16* dc = at<u16>(workspace, W.dc);
   u16* dz = at<u16>(workspace, W.dz);
   u16* da = at<u16>(workspace, W.da);
@@ -619,7 +632,7 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
   }
   const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
                             gs.max_tiles, ptb::device_compute_units()};
-  PTB_STAGE(1, ptb::launch_attention_bwd(qkv, qk_lo, c, lse, dc, delta, dz, static_cast<int>(s.N1),
+  PTB_STAGE(1, ptb::launch_attention_bwd(qkv, qk16, c, lse, dc, delta, dz, static_cast<int>(s.N1),
                                     static_cast<int>(s.b), static_cast<int>(s.s),
                                     static_cast<int>(s.n), static_cast<int>(s.d),
                                     static_cast<int>(s.w), as, strm));
@@ -723,9 +736,10 @@ int32_t ptb_serial_forward_timed(const ptb_dims* dims, const void* x, const void
   u16* a1 = at<u16>(saved, L.off[PTB_SERIAL_A1]);
   float* mu1 = at<float>(saved, L.off[PTB_SERIAL_MU1]);
   float* rstd1 = at<float>(saved, L.off[PTB_SERIAL_RSTD1]);
-  u16* a1_lo = at<u16>(saved, L.off[PTB_SERIAL_A1_LO]);
+  u16* a1_16 = at<u16>(saved, L.off[PTB_SERIAL_A1_16]);
   u16* qkv = at<u16>(saved, L.off[PTB_SERIAL_QKV]);
-  u16* qk_lo = at<u16>(saved, L.off[PTB_SERIAL_QK_LO]);
+  u16* qk16 = at<u16>(saved, L.off[PTB_SERIAL_QK16]);
+  u16* wqk16 = at<u16>(workspace, W.wqk16);
   u16* c = at<u16>(saved, L.off[PTB_SERIAL_C]);
   float* lse = at<float>(saved, L.off[PTB_SERIAL_LSE]);
   u16* x1 = at<u16>(saved, L.off[PTB_SERIAL_X1]);
@@ -740,18 +754,21 @@ int32_t ptb_serial_forward_timed(const ptb_dims* dims, const void* x, const void
 
   PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
   PTB_STAGE(0, ptb::launch_layernorm_fwd(X, static_cast<const u16*>(ln1_gamma),
-                                         static_cast<const u16*>(ln1_beta), a1, a1_lo, mu1,
+                                         static_cast<const u16*>(ln1_beta), a1, a1_16, mu1,
                                          rstd1, T, h, dims->ln_eps, strm, s.rms));
-  {  // QKV projection, one launch of two products: [q | k] from [a1 | a1_lo]
-     // (value + residual, as in the parallel block) and v from a1
+  PTB_STAGE(1, ptb::launch_cast_f16(Wqkv, static_cast<int>(3 * s.hl), h,
+                                    static_cast<int>(2 * s.hl), wqk16,
+                                    static_cast<int>(2 * s.hl), strm));
+  {  // QKV projection, one launch of two products: [q | k] = a1_16 x W_q|k in
+     // fp16 (as in the parallel block) and v from a1
     ptb::Epilogue e{};
     e.o0 = qkv; e.ld0 = static_cast<int>(3 * s.hl);
-    e.o3 = qk_lo; e.ld3 = static_cast<int>(2 * s.hl); e.lo_cols = static_cast<int>(2 * s.hl);
+    e.o3 = qk16; e.ld3 = static_cast<int>(2 * s.hl); e.lo_cols = static_cast<int>(2 * s.hl);
     e.split = static_cast<int>(3 * s.hl);
     ptb::GemmProblem pr[2];
-    pr[0].M = T; pr[0].N = static_cast<int>(2 * s.hl); pr[0].K = static_cast<int>(2 * s.h);
-    pr[0].A = two(a1, s.h, s.T, a1_lo, s.h, s.T, s.h, 1);
-    pr[0].B = two(Wqkv, 3 * s.hl, s.h, Wqkv, 3 * s.hl, s.h, s.h, 1);
+    pr[0].M = T; pr[0].N = static_cast<int>(2 * s.hl); pr[0].K = h;
+    pr[0].A = one(a1_16, s.h, s.T);
+    pr[0].B = one(wqk16, 2 * s.hl, s.h);
     pr[0].epi = e;
     pr[0].epi.col_base = 0;
     pr[1].M = T; pr[1].N = static_cast<int>(s.hl); pr[1].K = h;
@@ -760,22 +777,22 @@ int32_t ptb_serial_forward_timed(const ptb_dims* dims, const void* x, const void
     pr[1].B.bytes0 = pr[1].B.bytes1 = view_bytes(3 * s.hl, s.h, s.hl);
     pr[1].epi = e;
     pr[1].epi.col_base = static_cast<int>(2 * s.hl);
-    PTB_STAGE(1, ptb::launch_gemm_group(pr, 2, ptb::KMAJOR, ptb::OUTER_MAJOR,
-                                        ptb::EPI_QKV_GELU, gs, strm));
+    PTB_STAGE(2, ptb::launch_gemm_group(pr, 2, ptb::KMAJOR, ptb::OUTER_MAJOR,
+                                        ptb::EPI_QKV_GELU, gs, strm, /*f16_prob0=*/true));
   }
   const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
                             gs.max_tiles, ptb::device_compute_units()};
-  PTB_STAGE(2, ptb::launch_attention_fwd(qkv, qk_lo, c, lse, static_cast<int>(s.b),
+  PTB_STAGE(3, ptb::launch_attention_fwd(qkv, qk16, c, lse, static_cast<int>(s.b),
                                          static_cast<int>(s.s), static_cast<int>(s.n),
                                          static_cast<int>(s.d), static_cast<int>(s.w), as, strm));
   {  // x1 = x + c W_o
     ptb::Epilogue e{};
     e.o0 = x1; e.i0 = X; e.ld0 = h;
-    PTB_STAGE(3, ptb::launch_gemm(T, h, static_cast<int>(s.hl), one(c, s.hl, s.T), ptb::KMAJOR,
+    PTB_STAGE(4, ptb::launch_gemm(T, h, static_cast<int>(s.hl), one(c, s.hl, s.T), ptb::KMAJOR,
                                   one(static_cast<const u16*>(w_o), s.h, s.hl), ptb::OUTER_MAJOR,
                                   ptb::EPI_RESIDUAL, e, gs, strm));
   }
-  PTB_STAGE(4, ptb::launch_layernorm_fwd(x1, static_cast<const u16*>(ln2_gamma),
+  PTB_STAGE(5, ptb::launch_layernorm_fwd(x1, static_cast<const u16*>(ln2_gamma),
                                          static_cast<const u16*>(ln2_beta), a2, nullptr, mu2,
                                          rstd2, T, h, dims->ln_eps, strm, s.rms));
   {  // u = a2 W_fc1, g = GeLU(u) (SwiGLU: silu(u1) * u3): every column on the
@@ -783,7 +800,7 @@ int32_t ptb_serial_forward_timed(const ptb_dims* dims, const void* x, const void
     ptb::Epilogue e{};
     e.o1 = u; e.o2 = g; e.ld1 = static_cast<int>(s.f1); e.ld2 = static_cast<int>(s.f);
     e.split = 0; e.lo_cols = 0; e.col_base = 0;
-    PTB_STAGE(5, ptb::launch_gemm(T, static_cast<int>(s.f1), h, one(a2, s.h, s.T), ptb::KMAJOR,
+    PTB_STAGE(6, ptb::launch_gemm(T, static_cast<int>(s.f1), h, one(a2, s.h, s.T), ptb::KMAJOR,
                                   one(static_cast<const u16*>(w_fc1), s.f1, s.h),
                                   ptb::OUTER_MAJOR,
                                   s.swiglu ? ptb::EPI_QKV_SWIGLU : ptb::EPI_QKV_GELU, e, gs,
@@ -792,7 +809,7 @@ int32_t ptb_serial_forward_timed(const ptb_dims* dims, const void* x, const void
   {  // y = x1 + g W_fc2
     ptb::Epilogue e{};
     e.o0 = static_cast<u16*>(y); e.i0 = x1; e.ld0 = h;
-    PTB_STAGE(6, ptb::launch_gemm(T, h, static_cast<int>(s.f), one(g, s.f, s.T), ptb::KMAJOR,
+    PTB_STAGE(7, ptb::launch_gemm(T, h, static_cast<int>(s.f), one(g, s.f, s.T), ptb::KMAJOR,
                                   one(static_cast<const u16*>(w_fc2), s.h, s.f),
                                   ptb::OUTER_MAJOR, ptb::EPI_RESIDUAL, e, gs, strm));
   }
@@ -821,7 +838,7 @@ int32_t ptb_serial_backward_timed(const ptb_dims* dims, const void* dy, const vo
   const float* mu1 = at<float>(saved, L.off[PTB_SERIAL_MU1]);
   const float* rstd1 = at<float>(saved, L.off[PTB_SERIAL_RSTD1]);
   const u16* qkv = at<u16>(saved, L.off[PTB_SERIAL_QKV]);
-  const u16* qk_lo = at<u16>(saved, L.off[PTB_SERIAL_QK_LO]);
+  const u16* qk16 = at<u16>(saved, L.off[PTB_SERIAL_QK16]);
   const u16* c = at<u16>(saved, L.off[PTB_SERIAL_C]);
   const float* lse = at<float>(saved, L.off[PTB_SERIAL_LSE]);
   const u16* x1 = at<u16>(saved, L.off[PTB_SERIAL_X1]);
@@ -900,7 +917,7 @@ int32_t ptb_serial_backward_timed(const ptb_dims* dims, const void* dy, const vo
   }
   const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
                             gs.max_tiles, ptb::device_compute_units()};
-  PTB_STAGE(7, ptb::launch_attention_bwd(qkv, qk_lo, c, lse, dc, delta, dz, 3 * hl,
+  PTB_STAGE(7, ptb::launch_attention_bwd(qkv, qk16, c, lse, dc, delta, dz, 3 * hl,
                                          static_cast<int>(s.b), static_cast<int>(s.s),
                                          static_cast<int>(s.n), static_cast<int>(s.d),
                                          static_cast<int>(s.w), as, strm));
@@ -1156,7 +1173,7 @@ int32_t ptb_fp8_forward(const ptb_dims* dims, int32_t recipe, const void* x,
   u16* g = at<u16>(saved, L.off[PTB_SAVED_G]);
   u16* c = at<u16>(saved, L.off[PTB_SAVED_C]);
   float* lse = at<float>(saved, L.off[PTB_SAVED_LSE]);
-  u16* qk_lo = at<u16>(saved, L.off[PTB_SAVED_QK_LO]);
+  u16* qk16 = at<u16>(saved, L.off[PTB_SAVED_QK16]);
   float* samax = at<float>(saved, SL.amax);  // [0] a, [1] [c | g] (current scaling)
   const float* wamax = mx ? nullptr : at<float>(fp8_weights, WL.amax);
 
@@ -1177,7 +1194,7 @@ int32_t ptb_fp8_forward(const ptb_dims* dims, int32_t recipe, const void* x,
     pr.epi.o0 = qkv; pr.epi.ld0 = static_cast<int>(3 * s.hl);
     pr.epi.o1 = u; pr.epi.o2 = g; pr.epi.ld1 = static_cast<int>(s.f);
     pr.epi.ld2 = static_cast<int>(s.f);
-    pr.epi.o3 = qk_lo; pr.epi.ld3 = static_cast<int>(2 * s.hl);
+    pr.epi.o3 = qk16; pr.epi.ld3 = static_cast<int>(2 * s.hl);
     pr.epi.lo_cols = static_cast<int>(2 * s.hl);
     pr.epi.split = static_cast<int>(3 * s.hl);
     PTB_STAGE(2, gemm8(mx, pr, copy_at(workspace, W.a8), ptb::FP8_E4M3, samax,
@@ -1186,7 +1203,7 @@ int32_t ptb_fp8_forward(const ptb_dims* dims, int32_t recipe, const void* x,
   }
   const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
                             gs.max_tiles, ptb::device_compute_units()};
-  PTB_STAGE(3, ptb::launch_attention_fwd(qkv, qk_lo, c, lse, static_cast<int>(s.b),
+  PTB_STAGE(3, ptb::launch_attention_fwd(qkv, qk16, c, lse, static_cast<int>(s.b),
                                     static_cast<int>(s.s), static_cast<int>(s.n),
                                     static_cast<int>(s.d), static_cast<int>(s.w), as, strm));
   PTB_STAGE(4, cast_copies(mx, cast_two(c, s.hl, g, s.f, s.hl, 0, s.T, s.K2), ptb::FP8_E4M3,
@@ -1226,7 +1243,7 @@ int32_t ptb_fp8_backward(const ptb_dims* dims, int32_t recipe, const void* dy,
   const u16* u = at<u16>(saved, L.off[PTB_SAVED_U]);
   const u16* c = at<u16>(saved, L.off[PTB_SAVED_C]);
   const float* lse = at<float>(saved, L.off[PTB_SAVED_LSE]);
-  const u16* qk_lo = at<u16>(saved, L.off[PTB_SAVED_QK_LO]);
+  const u16* qk16 = at<u16>(saved, L.off[PTB_SAVED_QK16]);
   u16* dc = at<u16>(workspace, W.base.dc);
   u16* dz = at<u16>(workspace, W.base.dz);
   u16* da = at<u16>(workspace, W.base.da);
@@ -1258,7 +1275,7 @@ int32_t ptb_fp8_backward(const ptb_dims* dims, int32_t recipe, const void* dy,
   }
   const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
                             gs.max_tiles, ptb::device_compute_units()};
-  PTB_STAGE(2, ptb::launch_attention_bwd(qkv, qk_lo, c, lse, dc, delta, dz, static_cast<int>(s.N1),
+  PTB_STAGE(2, ptb::launch_attention_bwd(qkv, qk16, c, lse, dc, delta, dz, static_cast<int>(s.N1),
                                     static_cast<int>(s.b), static_cast<int>(s.s),
                                     static_cast<int>(s.n), static_cast<int>(s.d),
                                     static_cast<int>(s.w), as, strm));

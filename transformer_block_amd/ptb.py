@@ -31,8 +31,8 @@ PTB_ERR_SCRATCH = -9
 PTB_LAMB_MAX_TENSORS = 32
 PTB_LAMB_NOALLOC_SCRATCH_BYTES = 4 << 20
 
-SAVED_SLOTS = ("a", "mu", "rstd", "qkv", "u", "g", "c", "lse", "a_lo", "qk_lo")
-SERIAL_SAVED_SLOTS = ("a1", "mu1", "rstd1", "a1_lo", "qkv", "qk_lo", "c", "lse", "x1", "a2",
+SAVED_SLOTS = ("a", "mu", "rstd", "qkv", "u", "g", "c", "lse", "a16", "qk16")
+SERIAL_SAVED_SLOTS = ("a1", "mu1", "rstd1", "a1_16", "qkv", "qk16", "c", "lse", "x1", "a2",
                       "mu2", "rstd2", "u", "g")
 
 
@@ -213,9 +213,10 @@ def ptb_backward(dims: ptb_dims, dy, x, ln_gamma, w_qkv, w_o, w_fc1, w_fc2, save
     return _done(st, "ptb_backward", check)
 
 
-PTB_FWD_STAGES = 4
+PTB_FWD_STAGES = 5
 PTB_BWD_STAGES = 6
-FWD_STAGE_NAMES = ("layernorm_fwd", "gemm_qkv_fc1", "attention_fwd", "gemm_o_fc2_residual")
+FWD_STAGE_NAMES = ("layernorm_fwd", "cast_wqk_f16", "gemm_qkv_fc1", "attention_fwd",
+                   "gemm_o_fc2_residual")
 BWD_STAGE_NAMES = ("gemm_dgrad_o_fc2", "attention_bwd", "gemm_wgrad_o_fc2",
                    "gemm_dgrad_qkv_fc1", "gemm_wgrad_qkv_fc1", "layernorm_bwd")
 
@@ -252,9 +253,10 @@ def ptb_backward_timed(dims: ptb_dims, dy, x, ln_gamma, w_qkv, w_o, w_fc1, w_fc2
 
 
 # ---- serial (standard) block, for comparison: see include/ptb.h
-PTB_SERIAL_FWD_STAGES = 7
+PTB_SERIAL_FWD_STAGES = 8
 PTB_SERIAL_BWD_STAGES = 11
-SERIAL_FWD_STAGE_NAMES = ("layernorm1_fwd", "gemm_qkv", "attention_fwd", "gemm_o_residual",
+SERIAL_FWD_STAGE_NAMES = ("layernorm1_fwd", "cast_wqk_f16", "gemm_qkv", "attention_fwd",
+                          "gemm_o_residual",
                           "layernorm2_fwd", "gemm_fc1_gelu", "gemm_fc2_residual")
 SERIAL_BWD_STAGE_NAMES = ("gemm_dgrad_fc2", "gemm_wgrad_fc2", "gemm_dgrad_fc1",
                           "gemm_wgrad_fc1", "layernorm2_bwd", "gemm_dgrad_o", "gemm_wgrad_o",

@@ -101,10 +101,10 @@ class LayerStack:
                   "u": ((T, w.fc1_width), torch.bfloat16), "g": ((T, f), torch.bfloat16),
                   "c": ((T, hl), torch.bfloat16),
                   "lse": ((w.batch, w.heads, w.seq), torch.float32),
-                  "a_lo": ((T, h), torch.bfloat16), "qk_lo": ((T, 2 * hl), torch.bfloat16)}
+                  "a16": ((T, h), torch.float16), "qk16": ((T, 2 * hl), torch.float16)}
         off = P.ptb_saved_layout(self.dims)[name]
         shape, dt = shapes[name]
-        nbytes = int(np.prod(shape)) * (2 if dt == torch.bfloat16 else 4)
+        nbytes = int(np.prod(shape)) * (4 if dt == torch.float32 else 2)
         return self.saved[li][off:off + nbytes].view(dt).view(shape)
 
 
@@ -161,13 +161,14 @@ class SerialBlock:
         T, h, hl, f = w.tokens, w.hidden, w.h_local, w.ffn
         bf, f32 = torch.bfloat16, torch.float32
         shapes = {"a1": ((T, h), bf), "mu1": ((T,), f32), "rstd1": ((T,), f32),
-                  "a1_lo": ((T, h), bf), "qkv": ((T, 3 * hl), bf), "qk_lo": ((T, 2 * hl), bf),
+                  "a1_16": ((T, h), torch.float16), "qkv": ((T, 3 * hl), bf),
+                  "qk16": ((T, 2 * hl), torch.float16),
                   "c": ((T, hl), bf), "lse": ((w.batch, w.heads, w.seq), f32),
                   "x1": ((T, h), bf), "a2": ((T, h), bf), "mu2": ((T,), f32),
                   "rstd2": ((T,), f32), "u": ((T, w.fc1_width), bf), "g": ((T, f), bf)}
         off = P.ptb_serial_saved_layout(self.dims)[name]
         shape, dt = shapes[name]
-        nbytes = int(np.prod(shape)) * (2 if dt == bf else 4)
+        nbytes = int(np.prod(shape)) * (4 if dt == f32 else 2)
         return self.saved[off:off + nbytes].view(dt).view(shape)
 
 
@@ -232,9 +233,10 @@ class Fp8Layer:
         T, h, hl, f = w.tokens, w.hidden, w.h_local, w.ffn
         bf, f32 = torch.bfloat16, torch.float32
         shapes = {"a": ((T, h), bf), "mu": ((T,), f32), "rstd": ((T,), f32),
-                  "qkv": ((T, 3 * hl), bf), "qk_lo": ((T, 2 * hl), bf), "c": ((T, hl), bf),
+                  "qkv": ((T, 3 * hl), bf), "qk16": ((T, 2 * hl), torch.float16),
+                  "c": ((T, hl), bf),
                   "lse": ((w.batch, w.heads, w.seq), f32), "u": ((T, f), bf), "g": ((T, f), bf)}
         off = P.ptb_saved_layout(self.dims)[name]
         shape, dt = shapes[name]
-        nbytes = int(np.prod(shape)) * (2 if dt == bf else 4)
+        nbytes = int(np.prod(shape)) * (4 if dt == f32 else 2)
         return self.saved[off:off + nbytes].view(dt).view(shape)
