@@ -23,8 +23,10 @@ Pages followed (cited by title and section):
 Readings taken where the pages are silent (each is also a documented choice of
 the library): window = the w most recent keys including the query itself
 (0 <= i - j < w); causal; softmax scale 1/sqrt(d); LayerNorm (not RMSNorm) with
-biased variance and eps inside the square root; exact-erf GeLU; no biases, no
-dropout; QKV columns ordered [Q heads | K heads | V heads], each head's d
+biased variance and eps inside the square root; exact-erf GeLU; no biases;
+dropout (optional, [MS] 1.3) on the block's branch output before the residual
+add, given as a multiplier matrix (0 or 1/(1-p) per element, drawn by
+oracle/dropout_oracle.py); QKV columns ordered [Q heads | K heads | V heads], each head's d
 columns contiguous, and the attention output ``c`` uses the same head order for
 the rows of ``W_o``.
 
@@ -304,9 +306,12 @@ def merge_heads(t: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 def ptb_forward(x: np.ndarray, p: Dict[str, np.ndarray], batch: int, seq: int,
                 heads: int, head_dim: int, window: int, eps: float,
-                fc: FlopCounter | None = None, norm: str = "layernorm", mlp: str = "gelu"):
+                fc: FlopCounter | None = None, norm: str = "layernorm", mlp: str = "gelu",
+                drop: np.ndarray | None = None):
     """x: [T, h]; p holds ln_gamma, ln_beta, w_qkv [h,3hl], w_o [hl,h],
-    w_fc1 [h,f] ([h,2f] for SwiGLU), w_fc2 [f,h] (float64).  Returns (y, cache)."""
+    w_fc1 [h,f] ([h,2f] for SwiGLU), w_fc2 [f,h] (float64).  drop: None, or the
+    dropout multiplier [T, h] of the branch output (0 dropped, 1/(1-p) kept):
+    y = x + drop * (Attn + MLP).  Returns (y, cache)."""
     hl = heads * head_dim
     a, mu, rstd = norm_forward(norm, x, p["ln_gamma"], p["ln_beta"], eps)
     # attention branch
@@ -320,9 +325,10 @@ def ptb_forward(x: np.ndarray, p: Dict[str, np.ndarray], batch: int, seq: int,
     # MLP branch on the same LN output
     u, g = mlp_forward(mlp, a, p["w_fc1"], fc)
     mlp_out = _mm(g, p["w_fc2"], fc)
-    y = x + attn_out + mlp_out
+    branch = attn_out + mlp_out
+    y = x + (branch if drop is None else drop * branch)
     cache = dict(x=x, a=a, mu=mu, rstd=rstd, q=q, k=k, v=v, c=c, u=u, g=g,
-                 qkv=qkv, norm=norm, mlp=mlp)
+                 qkv=qkv, norm=norm, mlp=mlp, drop=drop)
     return y, cache
 
 
@@ -331,11 +337,14 @@ def ptb_backward(dy: np.ndarray, cache: dict, p: Dict[str, np.ndarray],
     """Gradients of ptb_forward for upstream gradient dy [T, h]."""
     x, a, c, u, g = cache["x"], cache["a"], cache["c"], cache["u"], cache["g"]
     q, k, v = cache["q"], cache["k"], cache["v"]
+    # the branch output's gradient passes the dropout mask; the residual's does not
+    drop = cache.get("drop")
+    db = dy if drop is None else drop * dy
     # output projections of both branches
-    dc = _mm(dy, p["w_o"].T, fc)
-    dg = _mm(dy, p["w_fc2"].T, fc)
-    dw_o = _mm(c.T, dy, fc)
-    dw_fc2 = _mm(g.T, dy, fc)
+    dc = _mm(db, p["w_o"].T, fc)
+    dg = _mm(db, p["w_fc2"].T, fc)
+    dw_o = _mm(c.T, db, fc)
+    dw_fc2 = _mm(g.T, db, fc)
     # MLP branch
     dw_fc1, da_mlp = mlp_backward(cache["mlp"], dg, u, a, p["w_fc1"], fc)
     # attention branch
@@ -356,11 +365,13 @@ def ptb_backward(dy: np.ndarray, cache: dict, p: Dict[str, np.ndarray],
 def ptb_stack_forward(x: np.ndarray, params: List[Dict[str, np.ndarray]],
                       batch: int, seq: int, heads: int, head_dim: int,
                       window: int, eps: float, fc: FlopCounter | None = None,
-                      norm: str = "layernorm", mlp: str = "gelu"):
-    """L stacked layers: x_{l+1} = PTB(x_l; theta_l).  Returns (y, caches)."""
+                      norm: str = "layernorm", mlp: str = "gelu", drops=None):
+    """L stacked layers: x_{l+1} = PTB(x_l; theta_l); drops: None or one
+    dropout multiplier (or None) per layer.  Returns (y, caches)."""
     caches = []
-    for p in params:
-        x, cache = ptb_forward(x, p, batch, seq, heads, head_dim, window, eps, fc, norm, mlp)
+    for li, p in enumerate(params):
+        x, cache = ptb_forward(x, p, batch, seq, heads, head_dim, window, eps, fc, norm, mlp,
+                               drop=None if drops is None else drops[li])
         caches.append(cache)
     return x, caches
 
@@ -392,8 +403,11 @@ def ptb_stack_backward(dy: np.ndarray, caches: list,
 # ---------------------------------------------------------------------------
 def serial_forward(x: np.ndarray, p: Dict[str, np.ndarray], batch: int, seq: int,
                    heads: int, head_dim: int, window: int, eps: float,
-                   fc: FlopCounter | None = None, norm: str = "layernorm", mlp: str = "gelu"):
-    """x: [T, h] -> (y, cache) for the serial block above."""
+                   fc: FlopCounter | None = None, norm: str = "layernorm", mlp: str = "gelu",
+                   drop1: np.ndarray | None = None, drop2: np.ndarray | None = None):
+    """x: [T, h] -> (y, cache) for the serial block above; drop1, drop2: the
+    dropout multipliers of the attention and MLP branch outputs (or None):
+    x1 = x + drop1 * Attn(a1) W_o, y = x1 + drop2 * MLP(a2)."""
     hl = heads * head_dim
     a1, mu1, rstd1 = norm_forward(norm, x, p["ln_gamma"], p["ln_beta"], eps)
     qkv = _mm(a1, p["w_qkv"], fc)
@@ -401,12 +415,15 @@ def serial_forward(x: np.ndarray, p: Dict[str, np.ndarray], batch: int, seq: int
     k = split_heads(qkv[:, hl:2 * hl], batch, seq, heads, head_dim)
     v = split_heads(qkv[:, 2 * hl:], batch, seq, heads, head_dim)
     c = merge_heads(attention_forward(q, k, v, window, fc))
-    x1 = x + _mm(c, p["w_o"], fc)
+    h2 = _mm(c, p["w_o"], fc)
+    x1 = x + (h2 if drop1 is None else drop1 * h2)
     a2, mu2, rstd2 = norm_forward(norm, x1, p["ln2_gamma"], p["ln2_beta"], eps)
     u, g = mlp_forward(mlp, a2, p["w_fc1"], fc)
-    y = x1 + _mm(g, p["w_fc2"], fc)
+    m = _mm(g, p["w_fc2"], fc)
+    y = x1 + (m if drop2 is None else drop2 * m)
     cache = dict(x=x, a1=a1, mu1=mu1, rstd1=rstd1, qkv=qkv, q=q, k=k, v=v, c=c,
-                 x1=x1, a2=a2, mu2=mu2, rstd2=rstd2, u=u, g=g, norm=norm, mlp=mlp)
+                 x1=x1, a2=a2, mu2=mu2, rstd2=rstd2, u=u, g=g, norm=norm, mlp=mlp,
+                 drop1=drop1, drop2=drop2)
     return y, cache
 
 
@@ -414,16 +431,20 @@ def serial_backward(dy: np.ndarray, cache: dict, p: Dict[str, np.ndarray],
                     window: int, fc: FlopCounter | None = None) -> Dict[str, np.ndarray]:
     """Gradients of serial_forward for upstream gradient dy [T, h]: the MLP
     sub-block first, then the attention sub-block, each with its residual."""
-    # MLP sub-block: y = x1 + GeLU(LN2(x1) W_fc1) W_fc2
-    dg = _mm(dy, p["w_fc2"].T, fc)
-    dw_fc2 = _mm(cache["g"].T, dy, fc)
+    # MLP sub-block: y = x1 + drop2 * GeLU(LN2(x1) W_fc1) W_fc2
+    d2 = cache.get("drop2")
+    dm = dy if d2 is None else d2 * dy
+    dg = _mm(dm, p["w_fc2"].T, fc)
+    dw_fc2 = _mm(cache["g"].T, dm, fc)
     dw_fc1, da2 = mlp_backward(cache["mlp"], dg, cache["u"], cache["a2"], p["w_fc1"], fc)
     dx1_ln, dgamma2, dbeta2 = norm_backward(cache["norm"], da2, cache["x1"], p["ln2_gamma"],
                                             cache["mu2"], cache["rstd2"])
     dx1 = dy + dx1_ln
-    # attention sub-block: x1 = x + Attn(LN1(x)) W_o
-    dc = _mm(dx1, p["w_o"].T, fc)
-    dw_o = _mm(cache["c"].T, dx1, fc)
+    # attention sub-block: x1 = x + drop1 * Attn(LN1(x)) W_o
+    d1 = cache.get("drop1")
+    dh = dx1 if d1 is None else d1 * dx1
+    dc = _mm(dh, p["w_o"].T, fc)
+    dw_o = _mm(cache["c"].T, dh, fc)
     q, k, v = cache["q"], cache["k"], cache["v"]
     b, n, s, d = q.shape
     dq, dk, dv = attention_backward(q, k, v, split_heads(dc, b, s, n, d), window, fc)
