@@ -23,9 +23,10 @@ Prints one JSON line.  Besides the throughput it carries:
   serial_block: the same workload through the serial (standard) block of the
                 MegaScale notes' eq (3), timed the same way: what the parallel
                 block buys on one GPU (--no-serial skips it);
-  variant:      the same workload with RMSNorm and the SwiGLU MLP (MegaScale's
-                own fused kernels, notes section 1.3; --no-variant skips it),
-                model FLOPs counting the SwiGLU MLP's 3 h f weights;
+  variant:      the same workload with RMSNorm, the SwiGLU MLP and dropout
+                (p = 0.1) on the branch output (MegaScale's own fused kernels,
+                notes section 1.3; --no-variant skips it), model FLOPs
+                counting the SwiGLU MLP's 3 h f weights;
   optimizer:    one LAMB step (the notes' eq (7)) over every parameter tensor
                 of the workload, fp32 masters and moments, against the HBM
                 roofline (40 algorithmic bytes per parameter); --no-optimizer
@@ -266,6 +267,9 @@ def time_serial(w, inp, warmup: int, steps: int, ptb_ms: float) -> dict:
             "parallel_speedup": round(ms / ptb_ms, 4), "stages_ms": stages}
 
 
+VARIANT_DROPOUT = 0.1  # dropout rate of the variant leg's branch output
+
+
 def time_variant(w, warmup: int, steps: int, base_ms: float) -> dict:
     """The layer stack with RMSNorm and the SwiGLU MLP on the same shape:
     mean ms per fwd+bwd step and per stage (HIP events, one stream)."""
@@ -276,8 +280,9 @@ def time_variant(w, warmup: int, steps: int, base_ms: float) -> dict:
     from transformer_block_amd.flops import workload_model_flops
     from transformer_block_amd.runner import LayerStack
 
-    print("bench: timing the RMSNorm + SwiGLU variant", file=sys.stderr, flush=True)
-    wv = w.replace(name=w.name + "_rmsnorm_swiglu", norm="rmsnorm", mlp="swiglu")
+    print("bench: timing the RMSNorm + SwiGLU + dropout variant", file=sys.stderr, flush=True)
+    wv = w.replace(name=w.name + "_rmsnorm_swiglu_dropout", norm="rmsnorm", mlp="swiglu",
+                   dropout_p=VARIANT_DROPOUT, dropout_seed=2024)
     st = LayerStack(wv, I.make_inputs(wv), "cuda")
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -305,7 +310,8 @@ def time_variant(w, warmup: int, steps: int, base_ms: float) -> dict:
     F = workload_model_flops(wv)
     tflops = F / (ms * 1e-3) / 1e12
     del st
-    return {"norm": "rmsnorm", "mlp": "swiglu", "ms_per_step": round(ms, 4),
+    return {"norm": "rmsnorm", "mlp": "swiglu", "dropout_p": VARIANT_DROPOUT,
+            "ms_per_step": round(ms, 4),
             "value": round(tflops, 2), "unit": "TFLOP/s", "mfu": round(tflops / PEAK_BF16_TFLOPS, 4),
             "model_flops_per_step": F, "stages_ms": stages}
 

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define PTB_ABI_VERSION 9
+#define PTB_ABI_VERSION 10
 
 enum ptb_status {
   PTB_OK = 0,
@@ -94,7 +94,26 @@ typedef struct ptb_dims {
   float ln_eps;      /* LayerNorm epsilon, added to the variance, > 0         */
   int32_t norm;      /* PTB_NORM_LAYERNORM (0) or PTB_NORM_RMSNORM (1)         */
   int32_t mlp;       /* PTB_MLP_GELU (0) or PTB_MLP_SWIGLU (1)                 */
+  float dropout_p;          /* dropout rate, 0 <= p < 1; 0 = no dropout        */
+  uint32_t dropout_layer;   /* this layer's index (< 2^31): picks its masks    */
+  uint64_t dropout_seed;    /* generator key                                   */
 } ptb_dims;
+
+/* Dropout (MegaScale notes, section 1.3: dropout fused into the layer, its
+ * activations kept for backward).  With dropout_p = p > 0 the block's branch
+ * output is dropped before the residual add:
+ *   parallel block  y  = x  + D0 * (Attn(a) W_o + MLP(a))
+ *   serial block    x1 = x  + D0 * Attn(a1) W_o,   y = x1 + D1 * MLP(a2)
+ * where D_b is 0 for a dropped element and 1/(1 - p) (fp32) for a kept one.
+ * Element e = t h + c of the [T, h] branch output is kept iff word e & 3 of
+ * Philox-4x32-10 (Salmon et al., "Parallel Random Numbers: As Easy as 1, 2,
+ * 3", SC'11) of the counter (e >> 2, 2 dropout_layer + b, 0, 0) under the key
+ * (dropout_seed mod 2^32, dropout_seed >> 32) is >= floor(p 2^32).  The mask
+ * is never stored: the forward's [O ; FC2] epilogue applies it, and the
+ * backward regenerates it from the same key (the "kept" activation is the
+ * key); pass the same dims to both.  ptb_dropout_mask writes the mask itself.
+ * The FP8 calls take p = 0 only (PTB_ERR_ARG otherwise).  A zero-initialised
+ * ptb_dims has no dropout. */
 
 /* Layer variants (MegaScale notes, section 1.3: the fused RMSNorm and SwiGLU
  * kernels of MegaScale's own model; the default is the layer above).
@@ -189,6 +208,13 @@ int32_t ptb_backward(const ptb_dims* dims,
                      void* dw_qkv, void* dw_o, void* dw_fc1, void* dw_fc2,
                      void* workspace, void* stream);
 
+/* Dropout mask of `n` elements (e = 0 .. n-1) of one generator stream, as the
+ * layer draws it: mask[e] = 1 if element e is kept, 0 if dropped (device
+ * bytes, caller-owned).  stream = 2 * layer (+ 1 for the serial block's MLP
+ * branch).  PTB_ERR_ARG unless 0 <= p < 1 and 0 <= n < 2^32 - 4. */
+int32_t ptb_dropout_mask(uint64_t seed, uint32_t stream, float p, int64_t n, void* mask,
+                         void* stream_handle);
+
 /* Stage timing.  The same calls with an array of hipEvent_t handles
  * (`stage_events`, 2 per stage, NULL entries skipped): event 2*i is recorded on
  * `stream` right before stage i is enqueued and event 2*i+1 right after it, so
@@ -197,7 +223,8 @@ int32_t ptb_backward(const ptb_dims* dims,
  *   forward  (PTB_FWD_STAGES = 5): 0 LayerNorm, 1 fp16 copy of the q, k
  *            columns of W_qkv, 2 [QKV | FC1] GEMM + GeLU, 3 attention,
  *            4 [O ; FC2] GEMM + residual;
- *   backward (PTB_BWD_STAGES = 6): 0 dgrad [O ; FC2] + GeLU', 1 attention
+ *   backward (PTB_BWD_STAGES = 6): 0 dgrad [O ; FC2] + GeLU' (under dropout
+ *            preceded by the regenerated mask applied to dy), 1 attention
  *            backward (3 kernels), 2 wgrad [O ; FC2], 3 dgrad [QKV | FC1],
  *            4 wgrad [QKV | FC1], 5 LayerNorm backward (2 kernels).
  * Each GEMM stage is exactly one kernel launch.  Each call also clears the
@@ -289,7 +316,8 @@ int32_t ptb_serial_backward(const ptb_dims* dims,
  *            2 QKV GEMM, 3 attention, 4 O GEMM + residual, 5 LN2,
  *            6 FC1 GEMM + GeLU, 7 FC2 GEMM + residual;
  *   backward (PTB_SERIAL_BWD_STAGES = 11): 0 dgrad FC2 + GeLU', 1 wgrad FC2,
- *            2 dgrad FC1, 3 wgrad FC1, 4 LN2 backward (+ dy), 5 dgrad O,
+ *            2 dgrad FC1, 3 wgrad FC1, 4 LN2 backward (+ dy), 5 dgrad O
+ *            (stages 0 and 5 under dropout preceded by the masks),
  *            6 wgrad O, 7 attention backward, 8 dgrad QKV, 9 wgrad QKV,
  *            10 LN1 backward (+ dx1). */
 #define PTB_SERIAL_FWD_STAGES 8

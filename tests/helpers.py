@@ -29,13 +29,24 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+def dropout_multipliers(w: I.Workload):
+    """Per-layer dropout multipliers of the parallel block (None without
+    dropout): layer l draws stream 2 l."""
+    if w.dropout_p == 0.0:
+        return None
+    from oracle import dropout_oracle as D
+    return [D.dropout_multiplier((w.tokens, w.hidden), w.dropout_seed, D.layer_stream(li),
+                                 w.dropout_p) for li in range(w.layers)]
+
+
 def oracle_run(w: I.Workload, inp: dict) -> dict:
     f = I.bf16_bits_to_f64
     x = f(inp["x"])
     dy = f(inp["dy"])
     params = [{k: f(v) for k, v in lay.items()} for lay in inp["layers"]]
     y, caches = O.ptb_stack_forward(x, params, w.batch, w.seq, w.heads, w.head_dim,
-                                    w.window, w.ln_eps, norm=w.norm, mlp=w.mlp)
+                                    w.window, w.ln_eps, norm=w.norm, mlp=w.mlp,
+                                    drops=dropout_multipliers(w))
     dx, grads = O.ptb_stack_backward(dy, caches, params, w.window)
     return dict(x=x, dy=dy, y=y, dx=dx, grads=grads, caches=caches)
 

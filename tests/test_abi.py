@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert P.ptb_abi_version() == 9
+    assert P.ptb_abi_version() == 10
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert P.ptb_status_string(code) and P.ptb_status_string(code) != "unknown status"
     assert P.ptb_status_string(12345) == "unknown status"
@@ -70,6 +70,11 @@ def good_dims(**kw):
     (dict(norm=1), P.PTB_OK),
     (dict(mlp=1), P.PTB_OK),
     (dict(norm=1, mlp=1), P.PTB_OK),
+    (dict(dropout_p=-0.1), P.PTB_ERR_ARG),
+    (dict(dropout_p=1.0), P.PTB_ERR_ARG),
+    (dict(dropout_p=float("nan")), P.PTB_ERR_ARG),
+    (dict(dropout_layer=2 ** 31), P.PTB_ERR_ARG),
+    (dict(dropout_p=0.5, dropout_layer=7, dropout_seed=2 ** 63 + 5), P.PTB_OK),
     (dict(norm=2), P.PTB_ERR_ARG),
     (dict(norm=-1), P.PTB_ERR_ARG),
     (dict(mlp=2), P.PTB_ERR_ARG),
@@ -347,3 +352,17 @@ def test_fp8_calls_reject_bad_arguments_before_any_hip_call(lib):
 def load_fmt_error(lib):
     """An unknown format code is rejected."""
     return lib.ptb_fp8_quantize(0x10000, 64, 64, 7, 0x10000, 0x10000, None, None)
+
+
+def test_dropout_mask_and_fp8_dropout_checks(lib):
+    A = 0x10000
+    for p in (-0.5, 1.0, float("nan")):
+        assert P.ptb_dropout_mask(1, 0, p, 16, A, stream=0, check=False) == P.PTB_ERR_ARG
+    assert P.ptb_dropout_mask(1, 0, 0.1, -1, A, stream=0, check=False) == P.PTB_ERR_ARG
+    assert P.ptb_dropout_mask(1, 0, 0.1, 2 ** 32, A, stream=0, check=False) == P.PTB_ERR_ARG
+    assert P.ptb_dropout_mask(1, 0, 0.1, 16, None, stream=0, check=False) == P.PTB_ERR_NULL
+    # the FP8 calls take no dropout
+    d = good_dims(dropout_p=0.1)
+    n = ctypes.c_size_t(0)
+    assert lib.ptb_fp8_weights_bytes(ctypes.byref(d), 0, ctypes.byref(n)) == P.PTB_ERR_ARG
+    assert lib.ptb_fp8_weights_bytes(ctypes.byref(good_dims()), 0, ctypes.byref(n)) == P.PTB_OK

@@ -20,6 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libptb.so")
 SOURCES = ["gemm.hip", "attention_fwd.hip", "attention.hip", "layernorm.hip", "lamb.hip", "fp8_cast.hip",
+           "dropout.hip",
            "ptb_api.cpp"]
 # Per-source code generation options.  The attention forward rescales its
 # output accumulators with vector ALU instructions; with the accumulators in

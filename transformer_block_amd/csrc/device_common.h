@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace ptb {
 
 typedef uint16_t u16;
@@ -117,6 +119,39 @@ __device__ __forceinline__ f32x16 mx_step(int i, int j, i32x8 a, i32x8 b, f32x16
   if (i == 2) return mfma32x32x64_f8_mx<FA, FB, 2, 1>(a, b, c, sa, sb);
   return mfma32x32x64_f8_mx<FA, FB, 3, 1>(a, b, c, sa, sb);
 }
+// Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC'11): ten rounds of a keyed bijection of a 128-bit
+// counter.  Each round takes the 64-bit products of counter words 0 and 2
+// with the two round multipliers and forms
+//   (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0));
+// the key words advance by the two Weyl constants between rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+  constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(M0, c.x), lo0 = M0 * c.x;
+    const uint32_t hi1 = __umulhi(M1, c.z), lo1 = M1 * c.z;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    k0 += W0;
+    k1 += W1;
+  }
+  return c;
+}
+
+// v[0..15] = the values of elements e0 .. e0 + 15 (e0 a multiple of 4) after
+// dropout.
+__device__ __forceinline__ void dropout16(const Dropout& d, uint32_t e0, float* v) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 w = philox4x32_10(make_uint4((e0 >> 2) + q, d.stream, 0u, 0u), d.k0, d.k1);
+    v[4 * q + 0] = w.x >= d.t ? v[4 * q + 0] * d.scale : 0.0f;
+    v[4 * q + 1] = w.y >= d.t ? v[4 * q + 1] * d.scale : 0.0f;
+    v[4 * q + 2] = w.z >= d.t ? v[4 * q + 2] * d.scale : 0.0f;
+    v[4 * q + 3] = w.w >= d.t ? v[4 * q + 3] * d.scale : 0.0f;
+  }
+}
+
 // Largest finite value of the 8-bit formats: E4M3 448, E5M2 57344.
 __device__ __forceinline__ constexpr float fp8_max(int fmt) { return fmt ? 57344.0f : 448.0f; }
 

@@ -386,6 +386,7 @@ __device__ __forceinline__ void epi_row16(const Epilogue& e, int region, int r, 
       store16bf(e.o2 + r * e.ld1 + cc, v);
     }
   } else if constexpr (MODE == EPI_RESIDUAL) {
+    if (e.drop.on) dropout16(e.drop, static_cast<uint32_t>(r * e.ld0 + c), v);
     float xr[16];
     load16bf(e.i0 + r * e.ld0 + c, xr);
 #pragma unroll

@@ -37,7 +37,8 @@ enum EpiMode {
   EPI_QKV_GELU = 0,  // with gc = c + col_base: gc < split: o0[r*ld0+gc] = bf16(v), and
                      // for gc < lo_cols also o3[r*ld3+gc] = fp16(v) (saturated);
                      // else o1 = v (u), o2 = GeLU(v) (g) at column gc - split
-  EPI_RESIDUAL = 1,  // o0[r*ld0+c] = v + i0[r*ld0+c]
+  EPI_RESIDUAL = 1,  // o0[r*ld0+c] = D(v) + i0[r*ld0+c], D the dropout `drop` of element
+                     // r*ld0+c (the identity when drop.on = 0)
   EPI_DGELU = 2,     // c < split: o0[r*ld0+c] = v; else o1[r*ld1+col_off1+c-split] =
                      //   v * GeLU'(i0[r*ld2 + c-split])
   EPI_STORE2_COLS = 3,  // c < split: o0[r*ld0+c]; else o1[r*ld1 + c-split]
@@ -56,6 +57,19 @@ enum EpiMode {
                         // o1[... + 32] = v * silu(u1)
 };
 
+// Dropout of a [rows, ld] tensor (the block's branch output, before the
+// residual add): element e = r * ld + c is kept iff word e & 3 of
+// Philox-4x32-10 of the counter (e >> 2, stream, 0, 0) under the key
+// (k0, k1) is >= t = floor(p 2^32), and a kept element is multiplied by
+// scale = 1 / (1 - p).  on = 0 for p = 0 (nothing dropped or scaled).
+struct Dropout {
+  uint32_t k0, k1;    // key: the seed's low and high words
+  uint32_t stream;    // 2 * layer (+ 1 for the serial block's MLP branch)
+  uint32_t t;         // keep threshold
+  float scale;
+  int on;
+};
+
 struct Epilogue {
   u16* o0;
   u16* o1;
@@ -68,6 +82,7 @@ struct Epilogue {
   int col_base;
   int lo_cols;
   int split;
+  Dropout drop;  // EPI_RESIDUAL: dropout of the product before the residual add
 };
 
 // One matrix product C[M,N] = A[M,K] * B[K,N] and what happens to C.
@@ -177,6 +192,13 @@ hipError_t launch_cast_fp8(const CastSrc& x, Fp8Format fmt, const float* amax, u
 hipError_t launch_cast_mx(const CastSrc& x, Fp8Format fmt, uint8_t* rows, int ldr, uint32_t* rs,
                           int rs_ld, uint8_t* cols, int ldc, uint32_t* cs, int cs_ld,
                           hipStream_t stream);
+
+// dst[e] = D(src[e]) for e < n (n a multiple of 8, 16-byte aligned bf16
+// arrays): the dropout of the backward's upstream gradient of a branch.
+hipError_t launch_dropout_apply(const u16* src, u16* dst, long n, const Dropout& d,
+                                hipStream_t stream);
+// mask[e] = 1 if element e is kept, else 0, for e < n (bytes).
+hipError_t launch_dropout_mask(uint8_t* mask, long n, const Dropout& d, hipStream_t stream);
 
 // LayerNorm forward over rows of x [T, h]: a = bf16(LN(x)) and an fp16 copy
 // a16 = fp16(LN(x)) of the same fp32 values (skipped when a16 is null), mu,

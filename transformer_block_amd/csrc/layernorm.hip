@@ -109,37 +109,32 @@ __global__ __launch_bounds__(LN_THREADS) void ln_fwd_kernel(const u16* __restric
 // dst[r][c] = fp16(src[r][c]) for a [rows, cols] block of a bf16 matrix
 // (cols a multiple of 8, row strides ld_src and ld_dst in elements): the
 // fp16 copy of the query/key columns of W_qkv for the fp16 q, k product.
-// Each thread converts 8 consecutive values per 16-byte load and store, four
-// loads in flight.  The conversion is exact for every bf16 value inside the
-// fp16 normal range; smaller magnitudes round to fp16 subnormals (absolute
-// error <= 2^-25) and larger ones saturate at 65504.
+// Each workgroup converts CAST_ROWS consecutive rows; a thread takes 16-byte
+// chunks c = tid, tid + 256, ... of every one of them, all rows' loads issued
+// before the first store.  The conversion is exact for every bf16 value
+// inside the fp16 normal range; smaller magnitudes round to fp16 subnormals
+// (absolute error <= 2^-25) and larger ones saturate at 65504.
+constexpr int CAST_ROWS = 4;
 __global__ __launch_bounds__(256) void cast_f16_kernel(const u16* __restrict__ src, int ld_src,
                                                        u16* __restrict__ dst, int ld_dst,
-                                                       int cols8, long total8) {
-  const long stride = static_cast<long>(gridDim.x) * 256;
-  for (long base = static_cast<long>(blockIdx.x) * 256 + threadIdx.x; base < total8;
-       base += 4 * stride) {
-    uint4 v[4];
+                                                       int rows, int cols8) {
+  const int r0 = blockIdx.x * CAST_ROWS;
+  const int nr = rows - r0 < CAST_ROWS ? rows - r0 : CAST_ROWS;
+  for (int c = threadIdx.x; c < cols8; c += 256) {
+    uint4 v[CAST_ROWS];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const long i = base + u * stride;
-      if (i < total8) {
-        const long r = i / cols8, c = (i % cols8) * 8;
-        v[u] = *reinterpret_cast<const uint4*>(src + r * ld_src + c);
-      }
-    }
+    for (int u = 0; u < CAST_ROWS; ++u)
+      if (u < nr) v[u] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(r0 + u) * ld_src + c * 8);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const long i = base + u * stride;
-      if (i < total8) {
-        const long r = i / cols8, c = (i % cols8) * 8;
+    for (int u = 0; u < CAST_ROWS; ++u) {
+      if (u < nr) {
         const uint32_t* w = reinterpret_cast<const uint32_t*>(&v[u]);
         uint4 o;
         o.x = pack2h(lo_bf(w[0]), hi_bf(w[0]));
         o.y = pack2h(lo_bf(w[1]), hi_bf(w[1]));
         o.z = pack2h(lo_bf(w[2]), hi_bf(w[2]));
         o.w = pack2h(lo_bf(w[3]), hi_bf(w[3]));
-        *reinterpret_cast<uint4*>(dst + r * ld_dst + c) = o;
+        *reinterpret_cast<uint4*>(dst + static_cast<size_t>(r0 + u) * ld_dst + c * 8) = o;
       }
     }
   }
@@ -334,10 +329,9 @@ hipError_t launch_cast_f16(const u16* src, int ld_src, int rows, int cols, u16* 
   if (rows <= 0 || cols <= 0) return hipSuccess;
   if (cols % 8 != 0 || ld_src % 8 != 0 || ld_dst % 8 != 0 || ld_src < cols || ld_dst < cols)
     return hipErrorInvalidValue;
-  const long total8 = static_cast<long>(rows) * (cols / 8);
-  const long blocks = std::min<long>((total8 + 4 * 256 - 1) / (4 * 256), 4096);
-  hipLaunchKernelGGL(cast_f16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, src,
-                     ld_src, dst, ld_dst, cols / 8, total8);
+  const int blocks = (rows + CAST_ROWS - 1) / CAST_ROWS;
+  hipLaunchKernelGGL(cast_f16_kernel, dim3(blocks), dim3(256), 0, s, src, ld_src, dst, ld_dst,
+                     rows, cols / 8);
   return hipGetLastError();
 }
 

@@ -59,6 +59,8 @@ int32_t check_dims(const ptb_dims* dims, Shape* out) {
   if ((p.norm != PTB_NORM_LAYERNORM && p.norm != PTB_NORM_RMSNORM) ||
       (p.mlp != PTB_MLP_GELU && p.mlp != PTB_MLP_SWIGLU))
     return PTB_ERR_ARG;
+  if (!(p.dropout_p >= 0.0f && p.dropout_p < 1.0f) || p.dropout_layer > 0x7fffffffu)
+    return PTB_ERR_ARG;
   Shape s;
   s.b = p.batch; s.s = p.seq; s.h = p.hidden; s.n = p.heads; s.d = p.head_dim; s.f = p.ffn;
   s.w = p.window < p.seq ? p.window : p.seq;  // a window >= seq is full causal attention
@@ -77,6 +79,21 @@ int32_t check_dims(const ptb_dims* dims, Shape* out) {
     return PTB_ERR_DIMS;
   if (out) *out = s;
   return PTB_OK;
+}
+
+// The dropout of one branch output of the layer (MegaScale notes, section
+// 1.3): stream 2 * layer + branch, threshold floor(p 2^32), scale 1 / (1 - p);
+// off for p = 0.
+ptb::Dropout dropout_of(const ptb_dims& p, uint32_t branch) {
+  ptb::Dropout d{};
+  if (p.dropout_p == 0.0f) return d;
+  d.on = 1;
+  d.k0 = static_cast<uint32_t>(p.dropout_seed & 0xffffffffu);
+  d.k1 = static_cast<uint32_t>(p.dropout_seed >> 32);
+  d.stream = 2u * p.dropout_layer + branch;
+  d.t = static_cast<uint32_t>(floor(static_cast<double>(p.dropout_p) * 4294967296.0));
+  d.scale = 1.0f / (1.0f - p.dropout_p);
+  return d;
 }
 
 struct SavedLayout {
@@ -117,7 +134,7 @@ int max_gemm_tiles(const Shape& s) {
 }
 
 struct WorkLayout {
-  size_t gemm_partials, counters, dc, dz, da, delta, partials, wqk16, total;
+  size_t gemm_partials, counters, dc, dz, da, delta, partials, dym, wqk16, total;
   int max_tiles;
 };
 
@@ -140,6 +157,7 @@ WorkLayout work_layout(const Shape& s) {
   W.da = o; o = align_up(o + s.T * s.h * 2);
   W.delta = o; o = align_up(o + s.b * s.n * s.s * 4);
   W.partials = o; o = align_up(o + static_cast<size_t>(ptb::layernorm_bwd_blocks(s.T)) * 2 * s.h * 4);
+  W.dym = o; o = align_up(o + s.T * s.h * 2);  // dropout of dy (the branch output's gradient)
   W.total = std::max(o, align_up(W.wqk16 + wqk16_bytes(s)));
   return W;
 }
@@ -190,7 +208,7 @@ int serial_max_tiles(const Shape& s) {
 // forward needs), then the backward's intermediate gradients.  da holds the
 // LN2 input gradient, then the LN1 one.
 struct SerialWorkLayout {
-  size_t gemm_partials, counters, du, da, dx1, dc, dz, delta, partials, wqk16, total;
+  size_t gemm_partials, counters, du, da, dx1, dc, dz, delta, partials, dym, wqk16, total;
   int max_tiles;
 };
 
@@ -208,6 +226,7 @@ SerialWorkLayout serial_work_layout(const Shape& s) {
   W.dz = o; o = align_up(o + s.T * 3 * s.hl * 2);
   W.delta = o; o = align_up(o + s.b * s.n * s.s * 4);
   W.partials = o; o = align_up(o + static_cast<size_t>(ptb::layernorm_bwd_blocks(s.T)) * 2 * s.h * 4);
+  W.dym = o; o = align_up(o + s.T * s.h * 2);  // dropout of dy, then of dx1
   W.total = std::max(o, align_up(W.wqk16 + wqk16_bytes(s)));
   return W;
 }
@@ -310,7 +329,8 @@ Fp8SavedLayout fp8_saved_layout(const Shape& s, bool mx) {
 int32_t check_fp8_dims(const ptb_dims* dims, int32_t recipe, Shape* s) {
   const int32_t st = check_dims(dims, s);
   if (st != PTB_OK) return st;
-  if (s->swiglu || (recipe != PTB_FP8_CURRENT && recipe != PTB_FP8_MX)) return PTB_ERR_ARG;
+  if (s->swiglu || dims->dropout_p != 0.0f || (recipe != PTB_FP8_CURRENT && recipe != PTB_FP8_MX))
+    return PTB_ERR_ARG;
   // FP8 operands are addressed with 32-bit byte offsets as well: every copy
   // (rows x padded contiguous dimension, one byte each) stays below 2^31
   const size_t T = s->T, h = s->h, N1 = s->N1, K2 = s->K2;
@@ -571,6 +591,7 @@ int32_t ptb_forward_timed(const ptb_dims* dims, const void* x, const void* ln_ga
   {  // [O ; FC2] projection plus the residual
     ptb::Epilogue e{};
     e.o0 = static_cast<u16*>(y); e.i0 = X; e.ld0 = static_cast<int>(s.h);
+    e.drop = dropout_of(*dims, 0);  // y = x + D * (Attn + MLP)
     PTB_STAGE(4, ptb::launch_gemm(
         static_cast<int>(s.T), static_cast<int>(s.h), static_cast<int>(s.K2),
         two(c, s.hl, s.T, g, s.f, s.T, s.hl, 1), ptb::KMAJOR,
@@ -614,6 +635,11 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
                             at<int>(workspace, W.counters), W.max_tiles};
   const u16* DY = static_cast<const u16*>(dy);
   const int T = static_cast<int>(s.T), h = static_cast<int>(s.h);
+  // the gradient of the branch output: dy, or D * dy under dropout (the
+  // mask regenerated from its key); the residual path takes dy itself
+  const ptb::Dropout drop = dropout_of(*dims, 0);
+  u16* dym = at<u16>(workspace, W.dym);
+  const u16* DB = drop.on ? dym : DY;
 
   PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
 
@@ -624,11 +650,18 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
     e.o1 = dz; e.ld1 = static_cast<int>(s.N1); e.col_off1 = static_cast<int>(3 * s.hl);
     e.i0 = u; e.ld2 = static_cast<int>(s.f1);
     e.split = static_cast<int>(s.hl);
-    PTB_STAGE(0, ptb::launch_gemm(
-        T, static_cast<int>(s.K2), h, one(DY, s.h, s.T), ptb::KMAJOR,
-        two(static_cast<const u16*>(w_o), s.h, s.hl, static_cast<const u16*>(w_fc2), s.h, s.f,
-            s.hl, 0),
-        ptb::KMAJOR, s.swiglu ? ptb::EPI_DSWIGLU : ptb::EPI_DGELU, e, gs, strm));
+    auto stage0 = [&]() -> hipError_t {
+      if (drop.on) {
+        const hipError_t er = ptb::launch_dropout_apply(DY, dym, s.T * s.h, drop, strm);
+        if (er != hipSuccess) return er;
+      }
+      return ptb::launch_gemm(
+          T, static_cast<int>(s.K2), h, one(DB, s.h, s.T), ptb::KMAJOR,
+          two(static_cast<const u16*>(w_o), s.h, s.hl, static_cast<const u16*>(w_fc2), s.h, s.f,
+              s.hl, 0),
+          ptb::KMAJOR, s.swiglu ? ptb::EPI_DSWIGLU : ptb::EPI_DGELU, e, gs, strm);
+    };
+    PTB_STAGE(0, stage0());
   }
   const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
                             gs.max_tiles, ptb::device_compute_units()};
@@ -642,7 +675,7 @@ int32_t ptb_backward_timed(const ptb_dims* dims, const void* dy, const void* x,
     e.o1 = static_cast<u16*>(dw_fc2); e.ld1 = h;
     e.split = static_cast<int>(s.hl);
     PTB_STAGE(2, ptb::launch_gemm(static_cast<int>(s.K2), h, T, two(c, s.hl, s.T, g, s.f, s.T, s.hl, 0),
-                             ptb::OUTER_MAJOR, one(DY, s.h, s.T), ptb::OUTER_MAJOR,
+                             ptb::OUTER_MAJOR, one(DB, s.h, s.T), ptb::OUTER_MAJOR,
                              ptb::EPI_STORE2_ROWS, e, gs, strm));
   }
   {  // dgrad through [QKV | FC1]: da = dZ [W_qkv | W_fc1]^T
@@ -788,6 +821,7 @@ int32_t ptb_serial_forward_timed(const ptb_dims* dims, const void* x, const void
   {  // x1 = x + c W_o
     ptb::Epilogue e{};
     e.o0 = x1; e.i0 = X; e.ld0 = h;
+    e.drop = dropout_of(*dims, 0);  // x1 = x + D1 * Attn W_o
     PTB_STAGE(4, ptb::launch_gemm(T, h, static_cast<int>(s.hl), one(c, s.hl, s.T), ptb::KMAJOR,
                                   one(static_cast<const u16*>(w_o), s.h, s.hl), ptb::OUTER_MAJOR,
                                   ptb::EPI_RESIDUAL, e, gs, strm));
@@ -809,6 +843,7 @@ int32_t ptb_serial_forward_timed(const ptb_dims* dims, const void* x, const void
   {  // y = x1 + g W_fc2
     ptb::Epilogue e{};
     e.o0 = static_cast<u16*>(y); e.i0 = x1; e.ld0 = h;
+    e.drop = dropout_of(*dims, 1);  // y = x1 + D2 * MLP
     PTB_STAGE(7, ptb::launch_gemm(T, h, static_cast<int>(s.f), one(g, s.f, s.T), ptb::KMAJOR,
                                   one(static_cast<const u16*>(w_fc2), s.h, s.f),
                                   ptb::OUTER_MAJOR, ptb::EPI_RESIDUAL, e, gs, strm));
@@ -860,23 +895,37 @@ int32_t ptb_serial_backward_timed(const ptb_dims* dims, const void* dy, const vo
   const int T = static_cast<int>(s.T), h = static_cast<int>(s.h);
   const int hl = static_cast<int>(s.hl), f = static_cast<int>(s.f);
   const int f1 = static_cast<int>(s.f1);
+  // gradients of the two branch outputs under dropout: D2 * dy for the MLP,
+  // D1 * dx1 for attention (masks regenerated from their keys, into dym one
+  // after the other); the residual paths take dy and dx1 themselves
+  const ptb::Dropout drop1 = dropout_of(*dims, 0), drop2 = dropout_of(*dims, 1);
+  u16* dym = at<u16>(workspace, W.dym);
+  const u16* DB2 = drop2.on ? dym : DY;
+  const u16* DB1 = drop1.on ? dym : dx1;
 
   PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
-  {  // du = (dy W_fc2^T) * GeLU'(u) (SwiGLU: du1, du3): every column on the
+  {  // du = (D2 dy W_fc2^T) * GeLU'(u) (SwiGLU: du1, du3): every column on the
      // activation side of the split
     ptb::Epilogue e{};
     e.o1 = du; e.ld1 = f1; e.col_off1 = 0;
     e.i0 = u; e.ld2 = f1;
     e.split = 0;
-    PTB_STAGE(0, ptb::launch_gemm(T, f, h, one(DY, s.h, s.T), ptb::KMAJOR,
-                                  one(static_cast<const u16*>(w_fc2), s.h, s.f), ptb::KMAJOR,
-                                  s.swiglu ? ptb::EPI_DSWIGLU : ptb::EPI_DGELU, e, gs, strm));
+    auto stage0 = [&]() -> hipError_t {
+      if (drop2.on) {
+        const hipError_t er = ptb::launch_dropout_apply(DY, dym, s.T * s.h, drop2, strm);
+        if (er != hipSuccess) return er;
+      }
+      return ptb::launch_gemm(T, f, h, one(DB2, s.h, s.T), ptb::KMAJOR,
+                              one(static_cast<const u16*>(w_fc2), s.h, s.f), ptb::KMAJOR,
+                              s.swiglu ? ptb::EPI_DSWIGLU : ptb::EPI_DGELU, e, gs, strm);
+    };
+    PTB_STAGE(0, stage0());
   }
-  {  // dW_fc2 = g^T dy
+  {  // dW_fc2 = g^T (D2 dy)
     ptb::Epilogue e{};
     e.o0 = static_cast<u16*>(dw_fc2); e.ld0 = h;
     e.split = f;  // one output
-    PTB_STAGE(1, ptb::launch_gemm(f, h, T, one(g, s.f, s.T), ptb::OUTER_MAJOR, one(DY, s.h, s.T),
+    PTB_STAGE(1, ptb::launch_gemm(f, h, T, one(g, s.f, s.T), ptb::OUTER_MAJOR, one(DB2, s.h, s.T),
                                   ptb::OUTER_MAJOR, ptb::EPI_STORE2_ROWS, e, gs, strm));
   }
   {  // da2 = du W_fc1^T
@@ -899,20 +948,27 @@ int32_t ptb_serial_backward_timed(const ptb_dims* dims, const void* dy, const vo
   PTB_STAGE(4, ptb::launch_layernorm_bwd(da, x1, static_cast<const u16*>(ln2_gamma), mu2, rstd2,
                                          DY, dx1, partials, static_cast<u16*>(d_ln2_gamma),
                                          static_cast<u16*>(d_ln2_beta), T, h, strm, s.rms));
-  {  // dc = dx1 W_o^T
+  {  // dc = (D1 dx1) W_o^T
     ptb::Epilogue e{};
     e.o0 = dc; e.ld0 = hl;
     e.split = hl;
-    PTB_STAGE(5, ptb::launch_gemm(T, hl, h, one(dx1, s.h, s.T), ptb::KMAJOR,
-                                  one(static_cast<const u16*>(w_o), s.h, s.hl), ptb::KMAJOR,
-                                  ptb::EPI_STORE2_COLS, e, gs, strm));
+    auto stage5 = [&]() -> hipError_t {
+      if (drop1.on) {
+        const hipError_t er = ptb::launch_dropout_apply(dx1, dym, s.T * s.h, drop1, strm);
+        if (er != hipSuccess) return er;
+      }
+      return ptb::launch_gemm(T, hl, h, one(DB1, s.h, s.T), ptb::KMAJOR,
+                              one(static_cast<const u16*>(w_o), s.h, s.hl), ptb::KMAJOR,
+                              ptb::EPI_STORE2_COLS, e, gs, strm);
+    };
+    PTB_STAGE(5, stage5());
   }
-  {  // dW_o = c^T dx1
+  {  // dW_o = c^T (D1 dx1)
     ptb::Epilogue e{};
     e.o0 = static_cast<u16*>(dw_o); e.ld0 = h;
     e.split = hl;
     PTB_STAGE(6, ptb::launch_gemm(hl, h, T, one(c, s.hl, s.T), ptb::OUTER_MAJOR,
-                                  one(dx1, s.h, s.T), ptb::OUTER_MAJOR, ptb::EPI_STORE2_ROWS, e,
+                                  one(DB1, s.h, s.T), ptb::OUTER_MAJOR, ptb::EPI_STORE2_ROWS, e,
                                   gs, strm));
   }
   const ptb::AttnScratch as{gs.partials, ptb::kGemmPartialBytes / sizeof(float), gs.counters,
@@ -1032,6 +1088,26 @@ int32_t ptb_lamb_step_noalloc(const ptb_lamb_hyper* hyper, const ptb_lamb_tensor
   double* scratch = nullptr;  // this device's copy of the static array
   PTB_HIP(ptb::lamb_static_scratch(&scratch));
   PTB_HIP(ptb::launch_lamb(ts, n, hp, scratch, norms, reinterpret_cast<hipStream_t>(stream)));
+  return PTB_OK;
+}
+
+int32_t ptb_dropout_mask(uint64_t seed, uint32_t stream, float p, int64_t n, void* mask,
+                         void* stream_handle) {
+  if (!(p >= 0.0f && p < 1.0f) || n < 0 || n >= (int64_t(1) << 32) - 4) return PTB_ERR_ARG;
+  if (mask == nullptr) return PTB_ERR_NULL;
+  ptb_dims d{};
+  d.dropout_p = p;
+  d.dropout_seed = seed;
+  ptb::Dropout dr = dropout_of(d, 0);
+  dr.stream = stream;
+  if (!dr.on) {  // p = 0: every element kept
+    dr.on = 1;
+    dr.t = 0;
+    dr.k0 = static_cast<uint32_t>(seed & 0xffffffffu);
+    dr.k1 = static_cast<uint32_t>(seed >> 32);
+  }
+  PTB_HIP(ptb::launch_dropout_mask(static_cast<uint8_t*>(mask), n, dr,
+                                   reinterpret_cast<hipStream_t>(stream_handle)));
   return PTB_OK;
 }
 

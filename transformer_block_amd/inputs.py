@@ -46,6 +46,8 @@ class Workload:
     ln_eps: float = 1e-5
     norm: str = "layernorm"   # or "rmsnorm"
     mlp: str = "gelu"         # or "swiglu" (W1 | W3 in w_fc1, 32-column blocks)
+    dropout_p: float = 0.0    # dropout rate of the branch output (0 = none)
+    dropout_seed: int = 0     # key of the dropout masks
 
     @property
     def tokens(self) -> int:

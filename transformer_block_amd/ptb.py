@@ -47,7 +47,9 @@ class ptb_dims(ctypes.Structure):
                 ("hidden", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("ln_eps", ctypes.c_float),
-                ("norm", ctypes.c_int32), ("mlp", ctypes.c_int32)]
+                ("norm", ctypes.c_int32), ("mlp", ctypes.c_int32),
+                ("dropout_p", ctypes.c_float), ("dropout_layer", ctypes.c_uint32),
+                ("dropout_seed", ctypes.c_uint64)]
 
 
 PTB_NORM_LAYERNORM, PTB_NORM_RMSNORM = 0, 1
@@ -56,10 +58,12 @@ NORM_KINDS = {"layernorm": PTB_NORM_LAYERNORM, "rmsnorm": PTB_NORM_RMSNORM}
 MLP_KINDS = {"gelu": PTB_MLP_GELU, "swiglu": PTB_MLP_SWIGLU}
 
 
-def dims_of(w) -> ptb_dims:
-    """ptb_dims of a Workload (transformer_block_amd.inputs)."""
+def dims_of(w, layer: int = 0) -> ptb_dims:
+    """ptb_dims of a Workload (transformer_block_amd.inputs) for layer `layer`
+    (which picks the layer's dropout masks)."""
     return ptb_dims(w.batch, w.seq, w.hidden, w.heads, w.head_dim, w.ffn, w.window,
-                    w.ln_eps, NORM_KINDS[w.norm], MLP_KINDS[w.mlp])
+                    w.ln_eps, NORM_KINDS[w.norm], MLP_KINDS[w.mlp], w.dropout_p, layer,
+                    w.dropout_seed)
 
 
 class ptb_lamb_hyper(ctypes.Structure):
@@ -121,6 +125,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ptb_lamb_step_noalloc": (ctypes.c_int32, [ctypes.POINTER(ptb_lamb_hyper),
                                                    ctypes.POINTER(ptb_lamb_tensor),
                                                    ctypes.c_int32, _P, _P]),
+        "ptb_dropout_mask": (ctypes.c_int32, [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_float,
+                                              ctypes.c_int64, _P, _P]),
         "ptb_fp8_weights_bytes": (ctypes.c_int32, [_D, _I, ctypes.POINTER(ctypes.c_size_t)]),
         "ptb_fp8_weights_layout": (ctypes.c_int32, [_D, _I, ctypes.POINTER(ctypes.c_size_t)]),
         "ptb_fp8_quantize": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _P]),
@@ -366,6 +372,14 @@ def ptb_lamb_step_noalloc(hyper: ptb_lamb_hyper, tensors, norms, stream=None,
     return _done(st, "ptb_lamb_step_noalloc", check)
 
 
+# ---- dropout masks: see include/ptb.h
+def ptb_dropout_mask(seed: int, stream_id: int, p: float, n: int, mask, stream=None,
+                     check: bool = True) -> int:
+    """mask: a device uint8 tensor of >= n elements (1 kept, 0 dropped)."""
+    st = load_library().ptb_dropout_mask(seed, stream_id, p, n, _ptr(mask), _stream(stream))
+    return _done(st, "ptb_dropout_mask", check)
+
+
 # ---- FP8 GEMM variant: see include/ptb.h
 PTB_FP8_FWD_STAGES = 6
 PTB_FP8_BWD_STAGES = 8
@@ -459,6 +473,7 @@ def exported_symbols() -> Sequence[str]:
             "ptb_serial_workspace_bytes", "ptb_serial_saved_layout", "ptb_serial_forward",
             "ptb_serial_backward", "ptb_serial_forward_timed", "ptb_serial_backward_timed",
             "ptb_lamb_workspace_bytes", "ptb_lamb_step", "ptb_lamb_step_noalloc",
+            "ptb_dropout_mask",
             "ptb_fp8_weights_bytes",
             "ptb_fp8_weights_layout", "ptb_fp8_quantize", "ptb_fp8_quantize_mx",
             "ptb_fp8_saved_bytes",

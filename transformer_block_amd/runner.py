@@ -34,6 +34,8 @@ class LayerStack:
     def __init__(self, w: Workload, inputs: dict, device: str = "cuda"):
         self.w = w
         self.dims = P.dims_of(w)
+        # per-layer dims: the layer index picks the layer's dropout masks
+        self.layer_dims = [P.dims_of(w, li) for li in range(w.layers)]
         self.device = torch.device(device)
         dev = self.device
         self.x = to_device_bf16(inputs["x"], dev)
@@ -71,7 +73,7 @@ class LayerStack:
     def forward(self, stream=None, events=None) -> None:
         """events: optional per-layer lists of 2*PTB_FWD_STAGES hipEvent_t handles."""
         for li, p in enumerate(self.params):
-            P.ptb_forward_timed(self.dims, self.layer_input(li), p["ln_gamma"], p["ln_beta"],
+            P.ptb_forward_timed(self.layer_dims[li], self.layer_input(li), p["ln_gamma"], p["ln_beta"],
                                 p["w_qkv"], p["w_o"], p["w_fc1"], p["w_fc2"], self.ys[li],
                                 self.saved[li], self.workspace, stream,
                                 events[li] if events else None)
@@ -81,7 +83,8 @@ class LayerStack:
         g = self.dy
         for li in range(len(self.params) - 1, -1, -1):
             p, gr = self.params[li], self.grads[li]
-            P.ptb_backward_timed(self.dims, g, self.layer_input(li), p["ln_gamma"], p["w_qkv"],
+            P.ptb_backward_timed(self.layer_dims[li], g, self.layer_input(li), p["ln_gamma"],
+                                 p["w_qkv"],
                                  p["w_o"], p["w_fc1"], p["w_fc2"], self.saved[li], self.dxs[li],
                                  gr["d_ln_gamma"], gr["d_ln_beta"], gr["dw_qkv"], gr["dw_o"],
                                  gr["dw_fc1"], gr["dw_fc2"], self.workspace, stream,
