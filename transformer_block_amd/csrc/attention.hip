@@ -71,12 +71,13 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const u16* __restrict__
 
 // ------------------------------------------------------------ dK and dV
 // Key rows of 128 (4 waves x 32, lane = key), query stages of QS = 32 staged
-// by DMA one stage ahead, two stages of two row-major tiles: Q (fp16) and dO
-// (A operands of S = Q K^T and dP = dO V^T, and, read transposed with the
-// rows in the accumulator's order, of dK^T += Q^T dS and dV^T += dO^T P).
-// The stage's log-sum-exp and delta go to LDS through registers, loaded one
-// stage ahead.
+// by DMA in a ring of BNST stages (BNST - 1 in flight while one is
+// computed), each two row-major tiles, Q (fp16) and dO (A operands of
+// S = Q K^T and dP = dO V^T, and, read transposed with the rows in the
+// accumulator's order, of dK^T += Q^T dS and dV^T += dO^T P), and the
+// stage's log-sum-exp and delta (the same DMA, 32 floats each).
 constexpr int QS = 32;
+constexpr int BNST = 4;
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
@@ -86,8 +87,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   constexpr int NKS = D / 16, ND = D / 32;
   constexpr int OPB = QS * D;  // u16 elements of one operand's tile
   constexpr int STG = 2 * OPB;
-  __shared__ __attribute__((aligned(1024))) u16 qs[2 * STG];
-  __shared__ __attribute__((aligned(16))) float ld_lds[2][2][QS];  // [stage][lse, delta][query]
+  __shared__ __attribute__((aligned(1024))) u16 qs[BNST * STG];
+  // per stage: the DMA of the log-sum-exp and of delta, 1 KB each (the first
+  // QS floats are the stage's queries; the rest of each KB receives zeros)
+  __shared__ __attribute__((aligned(1024))) float ld_lds[BNST][2][256];
   __shared__ int arrival;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -108,24 +111,40 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const int q_begin = item.span.begin;
   const int q_end = item.span.end;
   TileDma<D, QS, false> dq_r, do_r;
+  // loads per stage and wave: the two tiles' share, plus the log-sum-exp and
+  // delta loads, which every wave issues alike (identical values to the same
+  // LDS bytes) so that every wave counts the same loads
+  constexpr int LPT = 2 * TileDma<D, QS, false>::LPW + 2;
   dq_r.init(Qh, 2 * hl, s, wave, lane);
   do_r.init(dOg, hl, s, wave, lane);
   const uint32_t qs_lds = __builtin_amdgcn_readfirstlane(lds_address(qs));
-  auto issue = [&](uint32_t lds, int qt0) {
-    dq_r.issue(lds, qt0, wave);
-    do_r.issue(lds + OPB * 2, qt0, wave);
+  const uint32_t ld_base = __builtin_amdgcn_readfirstlane(lds_address(ld_lds));
+  const i32x4 lse_desc = make_desc(reinterpret_cast<const u16*>(lse_h), static_cast<uint32_t>(s) * 4);
+  const i32x4 dl_desc = make_desc(reinterpret_cast<const u16*>(dl_h), static_cast<uint32_t>(s) * 4);
+  // lanes 0..7 carry the 32 floats of a stage (16 bytes each); the others
+  // read out of range (zeros, no memory traffic)
+  const int ld_voff = lane < QS / 4 ? lane * 16 : kOutOfRange;
+  // stage st <- queries qt0 .. qt0 + QS - 1, or loads that only keep the
+  // count in flight constant (qt0 past the span)
+  auto issue = [&](int st, int qt0) {
+    const uint32_t lds = qs_lds + st * (STG * 2);
+    const uint32_t ldl = ld_base + st * (2 * 256 * 4);
+    if (qt0 < q_end) {
+      dq_r.issue(lds, qt0, wave);
+      do_r.issue(lds + OPB * 2, qt0, wave);
+      lds_dma16(lse_desc, ldl, ld_voff, qt0 * 4);
+      lds_dma16(dl_desc, ldl + 256 * 4, ld_voff, qt0 * 4);
+    } else {
+      dq_r.issue_none(lds, wave);
+      do_r.issue_none(lds + OPB * 2, wave);
+      // every lane out of range through its own offset (kOutOfRange + 0
+      // cannot wrap below the buffer's size)
+      lds_dma16(lse_desc, ldl, kOutOfRange, 0);
+      lds_dma16(dl_desc, ldl + 256 * 4, kOutOfRange, 0);
+    }
   };
-  // log-sum-exp (threads 0..31) and delta (32..63) of one stage's queries
-  auto load_ld = [&](int qt0) {
-    const int q = qt0 + (tid & 31);
-    return (tid < 64 && q < s) ? (tid < 32 ? lse_h[q] : dl_h[q]) : 0.0f;
-  };
-  float ldv = 0.0f;
-  if (q_begin < q_end) {
-    issue(qs_lds, q_begin);
-    ldv = load_ld(q_begin);
-    if (tid < 64) ld_lds[0][tid >> 5][tid & 31] = ldv;
-  }
+#pragma unroll
+  for (int i = 0; i < BNST - 1; ++i) issue(i, q_begin + i * QS);
 
   bf16x8 kf[NKS], vf[NKS];  // fp16 keys, bf16 values of this lane's key
 #pragma unroll
@@ -138,6 +157,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     kf[ks] = as_bf16x8(a);
     vf[ks] = as_bf16x8(b);
   }
+  // The key and value fragments are complete before the loop (the compiler
+  // does not see the DMA loads: left to itself it would wait for every
+  // outstanding load at their first use inside the loop, every iteration).
+  wait_vm_lds<0>();
   const float sc = kLog2e / sqrtf(static_cast<float>(D));
   f32x16 dv[ND], dk[ND];
 #pragma unroll
@@ -147,13 +170,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 
   int stage = 0;
   for (int qt0 = q_begin; qt0 < q_end; qt0 += QS) {
-    wait_vm_lds<0>();  // this wave's loads of stage qt0 landed (and its lse/delta stores)
-    __syncthreads();   // every wave's; the other stage is free again
-    const bool more = qt0 + QS < q_end;
-    if (more) {
-      issue(qs_lds + (stage ^ 1) * (STG * 2), qt0 + QS);
-      ldv = load_ld(qt0 + QS);
-    }
+    // this wave's loads of stage qt0 landed (BNST - 2 later stages' may still
+    // be in flight: loads complete in order)
+    wait_vm_lds<(BNST - 2) * LPT>();
+    __syncthreads();  // every wave's; the stage read last iteration is free again
+    issue(stage == 0 ? BNST - 1 : stage - 1, qt0 + (BNST - 1) * QS);
     const u16* q_lds = qs + stage * STG;
     const u16* do_lds = q_lds + OPB;
     const float* lse_s = ld_lds[stage][0];
@@ -225,10 +246,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
         }
       }
     }
-    // the next stage's log-sum-exp and delta (every wave done with that stage)
-    if (more && tid < 64) ld_lds[stage ^ 1][tid >> 5][tid & 31] = ldv;
-    stage ^= 1;
+    stage = stage == BNST - 1 ? 0 : stage + 1;
   }
+  // the trailing loads (beyond the span) land before the LDS can be reused
+  wait_vm_lds<0>();
 
   if (item.nchunks > 1) {
     // A chunk of a split key row: store dk, dv (device scope), count in; the
@@ -286,13 +307,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 }
 
 // ------------------------------------------------------------------- dQ
-// Query rows of 128 (4 waves x 32), key tiles of BKQ staged by DMA one tile
-// ahead, two stages of two row-major tiles: K (fp16) and V (the A operands
-// of S^T = K Q^T and dP^T = V dO^T; K read transposed, rows in the
-// accumulator's order, is also the A operand of dQ^T += K^T dS^T).  With
-// 32-key tiles the two stages take 32 KB for D = 128 and two workgroups share
-// a CU, so one wave's softmax runs under the other's MFMAs.
+// Query rows of 128 (4 waves x 32), key tiles of BKQ staged by DMA in a ring
+// of QNST stages (QNST - 1 in flight while one is computed), each two
+// row-major tiles: K (fp16) and V (the A operands of S^T = K Q^T and
+// dP^T = V dO^T; K read transposed, rows in the accumulator's order, is also
+// the A operand of dQ^T += K^T dS^T).  With 32-key tiles a stage takes 16 KB
+// for D = 128 and two workgroups share a CU, so one wave's softmax runs under
+// the other's MFMAs.
 constexpr int BKQ = 32;
+constexpr int QNST = 4;
 constexpr int KBQ = BKQ / 32;  // 32 x 32 S^T blocks per tile
 template <int D>
 __global__ __launch_bounds__(256, BKQ == 32 ? 2 : 1) void attn_bwd_dq_kernel(
@@ -302,7 +325,7 @@ __global__ __launch_bounds__(256, BKQ == 32 ? 2 : 1) void attn_bwd_dq_kernel(
   constexpr int NKS = D / 16, ND = D / 32;
   constexpr int OPB = BKQ * D;  // u16 elements of one operand's tile
   constexpr int STG = 2 * OPB;  // one stage: K (fp16), V (bf16)
-  __shared__ __attribute__((aligned(1024))) u16 kv[2 * STG];
+  __shared__ __attribute__((aligned(1024))) u16 kv[QNST * STG];
   __shared__ int arrival;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -322,14 +345,24 @@ __global__ __launch_bounds__(256, BKQ == 32 ? 2 : 1) void attn_bwd_dq_kernel(
   const int kv_begin = item.span.begin;
   const int kv_end = item.span.end;
   TileDma<D, BKQ, false> dk, dv;
+  constexpr int LPT = 2 * TileDma<D, BKQ, false>::LPW;  // loads per tile and wave
   dk.init(Kh, 2 * hl, s, wave, lane);
   dv.init(Vg, ld, s, wave, lane);
   const uint32_t kv_lds = __builtin_amdgcn_readfirstlane(lds_address(kv));
-  auto issue = [&](uint32_t lds, int kt0) {
-    dk.issue(lds, kt0, wave);
-    dv.issue(lds + OPB * 2, kt0, wave);
+  // tile kt0 into ring stage st, or (kt0 past the span) loads that only keep
+  // the count of loads in flight constant
+  auto issue = [&](int st, int kt0) {
+    const uint32_t lds = kv_lds + st * (STG * 2);
+    if (kt0 < kv_end) {
+      dk.issue(lds, kt0, wave);
+      dv.issue(lds + OPB * 2, kt0, wave);
+    } else {
+      dk.issue_none(lds, wave);
+      dv.issue_none(lds + OPB * 2, wave);
+    }
   };
-  if (kv_begin < kv_end) issue(kv_lds, kv_begin);
+#pragma unroll
+  for (int i = 0; i < QNST - 1; ++i) issue(i, kv_begin + i * BKQ);
 
   bf16x8 qf[NKS], of[NKS];  // fp16 query, bf16 dO fragments of this lane's query
 #pragma unroll
@@ -346,6 +379,8 @@ __global__ __launch_bounds__(256, BKQ == 32 ? 2 : 1) void attn_bwd_dq_kernel(
   const float lq = qi < s ? lse[hrow + qi] : 0.0f;
   const float dq_delta = qi < s ? delta[hrow + qi] : 0.0f;
   const float sc = kLog2e / sqrtf(static_cast<float>(D));
+  // every one of these loads complete before the loop (see the dK/dV kernel)
+  wait_vm_lds<0>();
 
   f32x16 dq[ND];
 #pragma unroll
@@ -355,12 +390,14 @@ __global__ __launch_bounds__(256, BKQ == 32 ? 2 : 1) void attn_bwd_dq_kernel(
 
   int stage = 0;
   for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKQ) {
-    wait_vm_lds<0>();  // this wave's loads of tile kt0 landed
-    __syncthreads();   // every wave's; the other stage is free again
-    if (kt0 + BKQ < kv_end) issue(kv_lds + (stage ^ 1) * (STG * 2), kt0 + BKQ);
+    // this wave's loads of tile kt0 landed (QNST - 2 later tiles' may still
+    // be in flight: loads complete in order)
+    wait_vm_lds<(QNST - 2) * LPT>();
+    __syncthreads();  // every wave's; the stage read last iteration is free again
+    issue(stage == 0 ? QNST - 1 : stage - 1, kt0 + (QNST - 1) * BKQ);
     const u16* k_lds = kv + stage * STG;
     const u16* v_lds = k_lds + OPB;
-    stage ^= 1;
+    stage = stage == QNST - 1 ? 0 : stage + 1;
 
     const bool any = qw0 < s && qw0 + 31 >= kt0 && qw0 - (kt0 + BKQ - 1) < window;
     if (!any) continue;
@@ -413,6 +450,9 @@ __global__ __launch_bounds__(256, BKQ == 32 ? 2 : 1) void attn_bwd_dq_kernel(
           dq[db] = mfma32x32x16_f16(frag_rows_tr<D>(k_lds, db * 32, kb * 2 + e2, lane), dsh, dq[db]);
       }
   }
+
+  // the trailing loads (beyond the span) land before the LDS can be reused
+  wait_vm_lds<0>();
 
   if (item.nchunks > 1) {
     // A chunk of a split query row: store dq (device scope), count in; the

@@ -197,6 +197,14 @@ struct TileDma {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) lds_dma16(desc, lds + (wave * LPW + i) * 1024, off[i], soff);
   }
+  // the same loads with an offset beyond any operand: they return zeros
+  // without touching memory (zeros land in [lds, lds + 2 R D)), so that a
+  // wave's count of loads in flight stays the same past the last tile
+  __device__ __forceinline__ void issue_none(uint32_t lds, int wave) const {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i)
+      lds_dma16(desc, lds + (wave * LPW + i) * 1024, off[i], kOutOfRange);
+  }
 };
 
 // ------------------------------------------------------- row splitting

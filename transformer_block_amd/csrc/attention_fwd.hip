@@ -11,11 +11,14 @@ namespace {
 // with its rows in the S^T accumulator's key order (read transposed).
 constexpr float kStale = 8.0f;
 
-// Keys per LDS tile: 32 keys keep the two stages at 32 KB for D = 128, so two
-// workgroups share a CU and one's softmax and barrier waits run beside the
-// other's MFMAs.
+// Keys per LDS tile and stages of the ring: 32 keys per tile, FNST stages
+// (FNST - 1 tiles in flight while one is computed; 16 KB each for D = 128),
+// two workgroups per CU, so one's softmax and barrier waits run beside the
+// other's MFMAs.  One stage of lead is not enough once each logit is a single
+// fp16 MFMA: a tile's compute is then shorter than the latency of its loads.
 constexpr int BKF = 32;
 constexpr int KB = BKF / 32;  // 32 x 32 S^T blocks per tile
+constexpr int FNST = 4;
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const u16* __restrict__ qkv,
@@ -26,7 +29,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const u16* __restrict_
   constexpr int NKS = D / 16, ND = D / 32;
   constexpr int OPB = BKF * D;  // u16 elements of one operand's tile
   constexpr int STG = 2 * OPB;  // one stage: K (fp16), V (bf16)
-  __shared__ __attribute__((aligned(1024))) u16 kv[2 * STG];
+  __shared__ __attribute__((aligned(1024))) u16 kv[FNST * STG];
   __shared__ int arrival;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -46,14 +49,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const u16* __restrict_
   const int kv_end = item.span.end;
   TileDma<D, BKF, false> dk;
   TileDma<D, BKF, true> dv;
+  constexpr int LPT = TileDma<D, BKF, false>::LPW + TileDma<D, BKF, true>::LPW;  // loads/tile/wave
   dk.init(Kh, 2 * hl, s, wave, lane);
   dv.init(Vg, ld, s, wave, lane);
   const uint32_t kv_lds = __builtin_amdgcn_readfirstlane(lds_address(kv));
-  auto issue = [&](uint32_t lds, int kt0) {
-    dk.issue(lds, kt0, wave);
-    dv.issue(lds + OPB * 2, kt0, wave);
+  // tile kt0 into ring stage st, or (kt0 past the span) loads that only keep
+  // the count of loads in flight constant
+  auto issue = [&](int st, int kt0) {
+    const uint32_t lds = kv_lds + st * (STG * 2);
+    if (kt0 < kv_end) {
+      dk.issue(lds, kt0, wave);
+      dv.issue(lds + OPB * 2, kt0, wave);
+    } else {
+      dk.issue_none(lds, wave);
+      dv.issue_none(lds + OPB * 2, wave);
+    }
   };
-  if (kv_begin < kv_end) issue(kv_lds, kv_begin);
+#pragma unroll
+  for (int i = 0; i < FNST - 1; ++i) issue(i, kv_begin + i * BKF);
 
   bf16x8 qf[NKS];  // fp16 query fragments (B operand of S^T = K Q^T)
 #pragma unroll
@@ -62,6 +75,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const u16* __restrict_
     if (qi < s) t = *reinterpret_cast<const uint4*>(Qh + qi * (2 * hl) + ks * 16 + g * 8);
     qf[ks] = as_bf16x8(t);
   }
+  // The query fragments are complete before the loop.  Without this wait the
+  // compiler, which does not see the DMA loads, would place a wait for every
+  // outstanding load before their first use inside the loop, draining the
+  // key tiles in flight on every iteration.
+  wait_vm_lds<0>();
 
   // Running max m is kept in scaled (log2) units: p = exp2(logit * sc - m).
   const float sc = kLog2e / sqrtf(static_cast<float>(D));
@@ -74,12 +92,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const u16* __restrict_
 
   int stage = 0;
   for (int kt0 = kv_begin; kt0 < kv_end; kt0 += BKF) {
-    wait_vm_lds<0>();  // this wave's loads of tile kt0 landed
-    __syncthreads();   // every wave's; the other stage is free again
-    if (kt0 + BKF < kv_end) issue(kv_lds + (stage ^ 1) * (STG * 2), kt0 + BKF);
+    // this wave's loads of tile kt0 landed (FNST - 2 later tiles' may still
+    // be in flight: loads complete in order)
+    wait_vm_lds<(FNST - 2) * LPT>();
+    __syncthreads();  // every wave's; the stage read last iteration is free again
+    issue(stage == 0 ? FNST - 1 : stage - 1, kt0 + (FNST - 1) * BKF);
     const u16* k_lds = kv + stage * STG;
     const u16* v_lds = k_lds + OPB;
-    stage ^= 1;
+    stage = stage == FNST - 1 ? 0 : stage + 1;
 
     const bool any = qw0 < s && qw0 + 31 >= kt0 && qw0 - (kt0 + BKF - 1) < window;
     if (!any) continue;
@@ -161,6 +181,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const u16* __restrict_
           o[db] = mfma32x32x16(frag_outer<BKF>(v_lds, db * 32, kb * 2 + e2, lane), pb, o[db]);
       }
   }
+
+  // the trailing loads (beyond the span) write zeros into the ring: every
+  // one of them lands before the workgroup can finish and its LDS be reused
+  wait_vm_lds<0>();
 
   if (item.nchunks > 1) {
     // A chunk of a split row: store o, m and l (device scope), count in; the
