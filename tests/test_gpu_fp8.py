@@ -247,6 +247,7 @@ CASES = [
     ("window1_d64_s77", W("f8w1", 2, 77, 192, 3, 64, 384, 1, seed=914), True),
     ("h2048_s2048_w512", I.WORKLOADS["h2048_s2048_w512"], False),
     ("gpt175b_tp8_share_s2048", I.WORKLOADS["gpt175b_tp8_share_s2048"], False),
+    ("long_h4096_s8192_w1024", I.WORKLOADS["long_h4096_s8192_w1024"], False),
 ]
 
 

@@ -30,6 +30,7 @@ CASES = [
                          mlp="swiglu"), True),
     ("h2048_s2048_w512", I.WORKLOADS["h2048_s2048_w512"], False),
     ("gpt175b_tp8_share_s2048", I.WORKLOADS["gpt175b_tp8_share_s2048"], False),
+    ("long_h4096_s8192_w1024", I.WORKLOADS["long_h4096_s8192_w1024"], False),
 ]
 
 
