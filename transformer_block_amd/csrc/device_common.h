@@ -101,24 +101,25 @@ __device__ __forceinline__ f32x16 mfma32x32x64_f8_mx(i32x8 a, i32x8 b, f32x16 c,
                                                          static_cast<int>(sa), OSB,
                                                          static_cast<int>(sb));
 }
-
-
 // The scaled MFMA with A's scale in byte i of sa and B's in byte j of sb
-// (i < 4, j < 2 known at compile time after unrolling).
-template <int FA, int FB>
-__device__ __forceinline__ f32x16 mx_step(int i, int j, i32x8 a, i32x8 b, f32x16 c, uint32_t sa,
-                                          uint32_t sb) {
-  if (j == 0) {
-    if (i == 0) return mfma32x32x64_f8_mx<FA, FB, 0, 0>(a, b, c, sa, sb);
-    if (i == 1) return mfma32x32x64_f8_mx<FA, FB, 1, 0>(a, b, c, sa, sb);
-    if (i == 2) return mfma32x32x64_f8_mx<FA, FB, 2, 0>(a, b, c, sa, sb);
-    return mfma32x32x64_f8_mx<FA, FB, 3, 0>(a, b, c, sa, sb);
-  }
-  if (i == 0) return mfma32x32x64_f8_mx<FA, FB, 0, 1>(a, b, c, sa, sb);
-  if (i == 1) return mfma32x32x64_f8_mx<FA, FB, 1, 1>(a, b, c, sa, sb);
-  if (i == 2) return mfma32x32x64_f8_mx<FA, FB, 2, 1>(a, b, c, sa, sb);
-  return mfma32x32x64_f8_mx<FA, FB, 3, 1>(a, b, c, sa, sb);
+// (i, j < 4; both selects immediates after unrolling).
+template <int FA, int FB, int I>
+__device__ __forceinline__ f32x16 mx_step4_i(int j, i32x8 a, i32x8 b, f32x16 c, uint32_t sa,
+                                             uint32_t sb) {
+  if (j == 0) return mfma32x32x64_f8_mx<FA, FB, I, 0>(a, b, c, sa, sb);
+  if (j == 1) return mfma32x32x64_f8_mx<FA, FB, I, 1>(a, b, c, sa, sb);
+  if (j == 2) return mfma32x32x64_f8_mx<FA, FB, I, 2>(a, b, c, sa, sb);
+  return mfma32x32x64_f8_mx<FA, FB, I, 3>(a, b, c, sa, sb);
 }
+template <int FA, int FB>
+__device__ __forceinline__ f32x16 mx_step4(int i, int j, i32x8 a, i32x8 b, f32x16 c, uint32_t sa,
+                                           uint32_t sb) {
+  if (i == 0) return mx_step4_i<FA, FB, 0>(j, a, b, c, sa, sb);
+  if (i == 1) return mx_step4_i<FA, FB, 1>(j, a, b, c, sa, sb);
+  if (i == 2) return mx_step4_i<FA, FB, 2>(j, a, b, c, sa, sb);
+  return mx_step4_i<FA, FB, 3>(j, a, b, c, sa, sb);
+}
+
 // Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
 // Easy as 1, 2, 3", SC'11): ten rounds of a keyed bijection of a 128-bit
 // counter.  Each round takes the 64-bit products of counter words 0 and 2

@@ -369,7 +369,10 @@ __device__ __forceinline__ void epi_swiglu16(const Epilogue& e, int r, int cc, f
   store16bf(e.o2 + r * e.ld2 + 32 * j + w, u1);
 }
 
-template <int MODE>
+// DROP: the residual epilogue may drop (bf16 products; FP8 layers take no
+// dropout, and leaving the mask code out keeps the four-wave kernel's
+// unrolled epilogue small enough to keep its accumulators in registers)
+template <int MODE, bool DROP = true>
 __device__ __forceinline__ void epi_row16(const Epilogue& e, int region, int r, int c, float* v) {
   if constexpr (MODE == EPI_QKV_GELU || MODE == EPI_QKV_SWIGLU) {
     const int gc = c + e.col_base;
@@ -386,7 +389,7 @@ __device__ __forceinline__ void epi_row16(const Epilogue& e, int region, int r, 
       store16bf(e.o2 + r * e.ld1 + cc, v);
     }
   } else if constexpr (MODE == EPI_RESIDUAL) {
-    if (e.drop.on) dropout16(e.drop, static_cast<uint32_t>(r * e.ld0 + c), v);
+    if (DROP && e.drop.on) dropout16(e.drop, static_cast<uint32_t>(r * e.ld0 + c), v);
     float xr[16];
     load16bf(e.i0 + r * e.ld0 + c, xr);
 #pragma unroll
@@ -549,22 +552,16 @@ __device__ __forceinline__ int part_slot(const SkPlan& pl, int i) {
   return i < pl.full_items ? i : pl.full_slots + (i - pl.full_items);
 }
 
-// FMT 0: bf16 operands; FP8 operands otherwise, FMT - 1 = fa + 2 fb with
-// fa, fb the operands' formats (Fp8Format: 0 E4M3, 1 E5M2).  MX: FP8 with
-// block scales instead of current scales.
+// FMT 0: bf16 operands; FP8 operands with per-tensor (current) scales
+// otherwise, FMT - 1 = fa + 2 fb with fa, fb the operands' formats
+// (Fp8Format: 0 E4M3, 1 E5M2).  Block-scaled FP8 runs on the four-wave
+// kernel below.
 // H0: problem 0's operands are fp16 (v_mfma_f32_32x32x16_f16), problem 1's
 // bf16; the same tiles, layouts and loads carry both.
-template <int AMAJ, int BMAJ, int MODE, int FMT = 0, bool MX = false, bool H0 = false>
+template <int AMAJ, int BMAJ, int MODE, int FMT = 0, bool H0 = false>
 __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
   static_assert(!H0 || FMT == 0, "fp16 operands are 16-bit");
   constexpr bool F8 = FMT != 0;
-  static_assert(!MX || F8, "block scales come with FP8 operands");
-  // MX loop: XS single-buffers the A fragments (below); the other MX modes
-  // keep the double-buffered FP8 loop with packed scale bytes.  Each mode
-  // takes the variant that measured faster for it: the scaled MFMA leaves
-  // the kernel short of registers either way, and the epilogue decides how
-  // the spills fall.
-  constexpr bool XS = MX && (MODE == EPI_QKV_GELU || MODE == EPI_DGELU);
   constexpr int FA = F8 ? (FMT - 1) & 1 : 0, FB = F8 ? (FMT - 1) >> 1 : 0;
   constexpr int ESZ = F8 ? 1 : 2;          // operand bytes per element
   constexpr int KSTEP = BK * 2 / ESZ;      // k-values per stage tile (128-byte rows)
@@ -575,8 +572,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
   // EPI_LD fp32) lies in stage 1, which is idle from an item's last k-step
   // until the next item's second stage tile goes out after the epilogue.
   __shared__ __attribute__((aligned(1024))) u16 ring[NSTAGE * STAGE];
-  // MX: per stage the scale words of the A tile's 256 rows, then the B tile's
-  __shared__ __attribute__((aligned(1024))) uint32_t sring[MX ? NSTAGE * 2 * TILE : 1];
   __shared__ int arrival;
   float* const epi_stage = reinterpret_cast<float*>(ring + STAGE);
   static_assert(WAVES * 32 * EPI_LD * 4 <= STAGE * 2, "epilogue staging fits in one stage");
@@ -601,7 +596,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
   int item = v;
   Item s = decode_item(pl, item);
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_address(ring));
-  const uint32_t sring_lds = __builtin_amdgcn_readfirstlane(lds_address(sring));
 
   auto setup = [&](const Item& sg) {
     const GemmProblem& P = pl.p[sg.prob];
@@ -618,20 +612,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
     const uint32_t lds = ring_lds + slot * (STAGE * 2);
     la.issue(lds, wave, k0, valid);
     lb.issue(lds + TILE * BK * 2, wave, k0, valid);
-    if constexpr (MX) {
-      // scale words of the tile's 256 rows at this k-step: 1 KB per operand,
-      // one load by wave 0 (A) and one by wave 1 (B); rows past the array
-      // read as zero (their operand rows are zero too)
-      if (wave < 2) {
-        const int ks = sg.kb + (valid ? j : 0);
-        const int row0 = wave ? sg.n0 : sg.m0;
-        const int ld = wave ? pl.scale_ldb : pl.scale_lda;
-        const i32x4 d = wave ? make_desc(reinterpret_cast<const u16*>(pl.scale_b), pl.scale_bytes_b)
-                             : make_desc(reinterpret_cast<const u16*>(pl.scale_a), pl.scale_bytes_a);
-        lds_dma16(d, sring_lds + (slot * 2 + wave) * (TILE * 4), lane * 16,
-                  valid ? (ks * ld + row0) * 4 : kOutOfRange);
-      }
-    }
   };
 
   int koff[4];
@@ -658,26 +638,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
       }
   };
   // FP8: the 32 bytes of bf16 k-steps 2 half and 2 half + 1 (64 k-values).
-  // MX (double-buffered loop): the scale codes of the lane's row in each
-  // fragment, for the block the matrix cores take from this lane (byte
-  // 2 half + h of the row's word, see below), packed one byte per fragment
-  // (sa8: A fragment i in byte i, sb8: B fragment j in byte j) for the
-  // MFMA's immediate byte selects.
   i32x8 ga[2][FM], gb[2][FN];
-  uint32_t sa8[2], sb8[2];
   auto rd8 = [&](const u16* st, int half, int slot) {
     const int k0 = koff[2 * half], k1 = koff[2 * half + 1];
-    if constexpr (MX && !XS) {
-      const uint32_t* sw = sring + ((st - ring) / STAGE) * (2 * TILE) + (lane & 31);
-      const uint32_t bit = 16 * half + 8 * (lane >> 5);
-      uint32_t pa = 0, pb = 0;
-#pragma unroll
-      for (int i = 0; i < FM; ++i) pa |= ((sw[wm * WM + i * 32] >> bit) & 0xffu) << (8 * i);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) pb |= ((sw[TILE + wn * WN + j * 32] >> bit) & 0xffu) << (8 * j);
-      sa8[slot] = pa;
-      sb8[slot] = pb;
-    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const u16* t = st + (wm * WM + i * 32) * BK;
@@ -695,69 +658,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        if constexpr (!MX)
-          acc[i][j] = mfma32x32x64_f8<FA, FB>(ga[slot][i], gb[slot][j], acc[i][j]);
-        else
-          acc[i][j] = mx_step<FA, FB>(i, j, ga[slot][i], gb[slot][j], acc[i][j], sa8[slot], sb8[slot]);
-      }
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = mfma32x32x64_f8<FA, FB>(ga[slot][i], gb[slot][j], acc[i][j]);
   };
   auto pin8 = [&]() {
-    constexpr int R = (MX ? 3 : 2) * (FM + FN);
+    constexpr int R = 2 * (FM + FN);
 #pragma unroll
     for (int i = 0; i < FM * FN; ++i) {
       __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
       __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, R - FM * FN, 0);
-  };
-  // MX.  Lane half h holds k [64 half + 16 h, +16) and [64 half + 32 + 16 h,
-  // +16) of the stage tile, so the matrix cores' k-block b of this half is
-  // the tile's 32-wide block 2 half + b, whose scale they take from lane half
-  // b: each lane reads byte 2 half + h of its row's scale word.  The scaled
-  // MFMA needs about 20 registers more than the plain one, so the A fragments
-  // are single-buffered here: fragment i is read again, for the next half,
-  // right after its last MFMA, with the other fragments' MFMAs to cover the
-  // read; the B fragments stay double-buffered.
-  uint32_t xsa[FM], xsb[2][FN];
-  const uint8_t* const sbytes = reinterpret_cast<const uint8_t*>(sring);
-  auto xbyte = [&](int stage, int row, int half) -> uint32_t {
-    return sbytes[(stage * 2 * TILE + row) * 4 + 2 * half + (lane >> 5)];
-  };
-  auto xrdA = [&](const u16* st, int stage, int half, int i) {
-    const u16* t = st + (wm * WM + i * 32) * BK;
-    ga[0][i] = cat8(*reinterpret_cast<const uint4*>(t + koff[2 * half]),
-                    *reinterpret_cast<const uint4*>(t + koff[2 * half + 1]));
-    xsa[i] = xbyte(stage, wm * WM + i * 32 + (lane & 31), half);
-  };
-  auto xrdB = [&](const u16* st, int stage, int half, int slot) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const u16* t = st + TILE * BK + (wn * WN + j * 32) * BK;
-      gb[slot][j] = cat8(*reinterpret_cast<const uint4*>(t + koff[2 * half]),
-                         *reinterpret_cast<const uint4*>(t + koff[2 * half + 1]));
-      xsb[slot][j] = xbyte(stage, TILE + wn * WN + j * 32 + (lane & 31), half);
-    }
-  };
-  // one half-step: the MFMAs of A fragment i against both B fragments, then
-  // fragment i of the next half (tile st, half `half`)
-  auto xhalf = [&](int slot, const u16* st, int stage, int half) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = mfma32x32x64_f8_mx<FA, FB, 0, 0>(ga[0][i], gb[slot][j], acc[i][j], xsa[i],
-                                                     xsb[slot][j]);
-      xrdA(st, stage, half, i);
-    }
-  };
-  auto xpin = [&]() {
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 3 * FN, 0);  // next B fragments + scales
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, FN, 0);
-      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 3, 0);  // next A fragment i + scale
-    }
   };
   // LDS reads of the next k-step spread between this k-step's MFMAs
   auto pin = [&]() {
@@ -794,26 +705,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    if constexpr (XS) {
-      // two scaled FP8 MFMA half-steps of 64 k per stage tile
-#pragma unroll
-      for (int i = 0; i < FM; ++i) xrdA(ring, 0, 0, i);
-      xrdB(ring, 0, 0, 0);
-      for (int j = 0; j < len; ++j) {
-        const int stg = j & 1, nst = (j + 1) & 1;
-        const u16* cur = ring + stg * STAGE;
-        xrdB(cur, stg, 1, 1);
-        xhalf(0, cur, stg, 1);
-        xpin();
-        wait_vm_lds<0>();
-        __syncthreads();
-        issue_to(s, j & 1, j + 2);
-        const u16* nxt = ring + nst * STAGE;
-        xrdB(nxt, nst, 0, 0);  // unused after the last step
-        xhalf(1, nxt, nst, 0);
-        xpin();
-      }
-    } else if constexpr (F8) {
+    if constexpr (F8) {
       // the same pipeline with two FP8 MFMA steps of 64 k per stage tile
       rd8(ring, 0, 0);
       for (int j = 0; j < len; ++j) {
@@ -893,7 +785,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
       const int my_slot = part_slot(pl, item);
       float held[MODE == EPI_QKV_SWIGLU ? 16 : 1];
       float dq = 1.0f;  // FP8: 1 / (sA sB)
-      if constexpr (F8 && !MX)
+      if constexpr (F8)
         dq = inv_scale(*pl.amax_a, fp8_max(FA)) * inv_scale(*pl.amax_b, fp8_max(FB));
       for (;;) {
 #pragma unroll
@@ -951,10 +843,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
                     epi_swiglu16(e, r, cb - 32 + e.col_base - e.split + ec, held, vals);
                   }
                 } else if (cb < P.N && r < P.M) {
-                  epi_row16<MODE>(e, region, r, cb + ec, vals);
+                  epi_row16<MODE, FMT == 0>(e, region, r, cb + ec, vals);
                 }
               } else {
-                if (cb < P.N && r < P.M) epi_row16<MODE>(e, region, r, cb + ec, vals);
+                if (cb < P.N && r < P.M) epi_row16<MODE, FMT == 0>(e, region, r, cb + ec, vals);
               }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -984,19 +876,33 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
   }
 }
 
-// The four-wave kernel (one wave per SIMD, 128 x 128 outputs per wave),
-// kept for the two products whose operands are both k-contiguous (the dgrad
-// products): there A goes through registers (loaded at the start of a k-step,
-// written at its end) and B by DMA, which splits the operand stream over both
-// paths, and that measures faster than the eight-wave kernel's DMA-only
-// stream.  Same items, epilogue and partials as the eight-wave kernel.
-template <int AMAJ, int BMAJ, int MODE>
+// The four-wave kernel (one wave per SIMD, 128 x 128 outputs per wave, the
+// accumulators in AGPRs), kept for the two products whose operands are both
+// k-contiguous (the dgrad products): there A goes through registers (loaded
+// at the start of a k-step, written at its end) and B by DMA, which splits
+// the operand stream over both paths, and that measures faster than the
+// eight-wave kernel's DMA-only stream.  Same items, epilogue and partials as
+// the eight-wave kernel.
+// MX: every product on block-scaled FP8 operands (FMT - 1 = fa + 2 fb).  The
+// scaled MFMA needs about 20 registers more than the plain one, which the
+// eight-wave kernel does not have; here the accumulators sit in AGPRs and the
+// fragments of both halves of a stage tile fit in VGPRs.  Both operands go by
+// DMA (32 KB each per 128-wide k-step), the tile's scale words (1 KB per
+// operand) beside them into a small LDS ring.
+template <int AMAJ, int BMAJ, int MODE, int FMT = 0, bool MX = false>
 __global__ __launch_bounds__(256, 1) void gemm_kernel4(SkPlan pl) {
+  constexpr bool F8 = FMT != 0;
+  static_assert(!MX || F8, "block scales come with FP8 operands");
+  static_assert(!F8 || (AMAJ == KMAJOR && BMAJ == KMAJOR), "FP8 operands are k-contiguous");
+  constexpr int FA = F8 ? (FMT - 1) & 1 : 0, FB = F8 ? (FMT - 1) >> 1 : 0;
+  constexpr int KSTEP = F8 ? 2 * BK : BK;  // k-values per stage tile (128-byte rows)
   constexpr int WM = 128, WN = 128, FM = 4, FN = 4;
   constexpr int RA = (AMAJ == KMAJOR) ? FM : 2 * FM;  // LDS read instructions per k-step
   constexpr int RB = (BMAJ == KMAJOR) ? FN : 2 * FN;
   __shared__ __attribute__((aligned(1024))) u16 ring[NSTAGE * STAGE];
   __shared__ __attribute__((aligned(16))) float epi_stage[4 * 32 * EPI_LD];
+  // MX: per stage the scale words of the A tile's 256 rows, then the B tile's
+  __shared__ __attribute__((aligned(1024))) uint32_t sring[MX ? NSTAGE * 2 * TILE : 1];
   __shared__ int arrival;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1016,12 +922,18 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel4(SkPlan pl) {
   // registers and B by LDS DMA, which splits the operand stream over both
   // paths; otherwise both go by DMA (measured per product: see the notes on
   // the main loop).
-  constexpr bool AREG = (AMAJ == KMAJOR && BMAJ == KMAJOR);
-  std::conditional_t<AREG, RegLoader<AMAJ>, StageLoader<AMAJ>> la;
-  StageLoader<BMAJ> lb;
+  constexpr bool AREG = (AMAJ == KMAJOR && BMAJ == KMAJOR) && !F8;
+  std::conditional_t<F8, StageLoaderP<KMAJOR, 1>,
+                     std::conditional_t<AREG, RegLoader<AMAJ>, StageLoader<AMAJ>>> la;
+  std::conditional_t<F8, StageLoaderP<KMAJOR, 1>, StageLoader<BMAJ>> lb;
   int item = v;
   Item s = decode_item(pl, item);
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_address(ring));
+  const uint32_t sring_lds = __builtin_amdgcn_readfirstlane(lds_address(sring));
+  const int sop = __builtin_amdgcn_readfirstlane(wave) & 1;  // MX: scale words staged by this wave
+  const i32x4 sdesc = sop ? make_desc(reinterpret_cast<const u16*>(pl.scale_b), pl.scale_bytes_b)
+                          : make_desc(reinterpret_cast<const u16*>(pl.scale_a), pl.scale_bytes_a);
+  const int sld = sop ? pl.scale_ldb : pl.scale_lda;
 
   auto setup = [&](const Item& sg) {
     const GemmProblem& P = pl.p[sg.prob];
@@ -1033,10 +945,21 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel4(SkPlan pl) {
   // segment's end the loads are out of range (zeros, no memory traffic)
   auto issue_to = [&](const Item& sg, int slot, int j) {
     const bool valid = j < sg.len;
-    const int k0 = (sg.kb + (valid ? j : 0)) * BK;
+    const int k0 = (sg.kb + (valid ? j : 0)) * KSTEP;
     const uint32_t lds = ring_lds + slot * (STAGE * 2);
     if constexpr (!AREG) la.issue(lds, wave, k0, valid);
     lb.issue(lds + TILE * BK * 2, wave, k0, valid);
+    if constexpr (MX) {
+      // scale words of the tile's 256 rows at this k-step: 1 KB per operand,
+      // one load per wave, of operand sop (A: 0, B: 1); waves 2 and 3 repeat
+      // waves 0 and 1 (the same bytes to the same place), which keeps the
+      // loop free of branches.  Rows past the array read as zero (their
+      // operand rows are zero too).
+      const int ks = sg.kb + (valid ? j : 0);
+      const int row0 = sop ? sg.n0 : sg.m0;
+      lds_dma16(sdesc, sring_lds + (slot * 2 + sop) * (TILE * 4), lane * 16,
+                valid ? (ks * sld + row0) * 4 : kOutOfRange);
+    }
   };
   // A through registers (AREG): load stage tile j of A, then write it to LDS
   v4u stg[AREG ? 8 : 1];
@@ -1087,6 +1010,73 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel4(SkPlan pl) {
     if constexpr (R < FM * FN) __builtin_amdgcn_sched_group_barrier(SG_MFMA, FM * FN - R, 0);
     if constexpr (R > FM * FN) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, R - FM * FN, 0);
   };
+  // MX: the 32 bytes of one 64-wide half of a stage tile per fragment (bf16
+  // k-steps 2 half and 2 half + 1 of the same rows), and the scale code of
+  // the lane's row for the block the matrix cores take from this lane: lane
+  // half h holds k [64 half + 16 h, +16) and [64 half + 32 + 16 h, +16), so
+  // the matrix cores' block b of this half is the tile's 32-wide block
+  // 2 half + b, whose scale they take from lane half b: byte 2 half + h of the
+  // row's word.  Packed one byte per fragment (sa8 byte i: A fragment i, sb8
+  // byte j: B fragment j) for the MFMA's immediate byte selects.
+  int koff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) koff[ks] = kfrag_offset(ks, lane);
+  i32x8 ga[2][F8 ? FM : 1], gb[2][F8 ? FN : 1];
+  uint32_t sa8[2], sb8[2];
+  auto rd8 = [&](const u16* st, int half, int slot) {
+    if constexpr (F8) {
+      const int k0 = koff[2 * half], k1 = koff[2 * half + 1];
+      if constexpr (MX) {
+        const uint32_t* sw = sring + ((st - ring) / STAGE) * (2 * TILE) + (lane & 31);
+        const uint32_t bit = 16 * half + 8 * (lane >> 5);
+        uint32_t pa = 0, pb = 0;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) pa |= ((sw[wm * WM + i * 32] >> bit) & 0xffu) << (8 * i);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) pb |= ((sw[TILE + wn * WN + j * 32] >> bit) & 0xffu) << (8 * j);
+        sa8[slot] = pa;
+        sb8[slot] = pb;
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const u16* t = st + (wm * WM + i * 32) * BK;
+        ga[slot][i] = cat8(*reinterpret_cast<const uint4*>(t + k0),
+                           *reinterpret_cast<const uint4*>(t + k1));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const u16* t = st + TILE * BK + (wn * WN + j * 32) * BK;
+        gb[slot][j] = cat8(*reinterpret_cast<const uint4*>(t + k0),
+                           *reinterpret_cast<const uint4*>(t + k1));
+      }
+    }
+  };
+  auto mma8 = [&](int slot) {
+    if constexpr (MX) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = mx_step4<FA, FB>(i, j, ga[slot][i], gb[slot][j], acc[i][j], sa8[slot],
+                                       sb8[slot]);
+    } else if constexpr (F8) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = mfma32x32x64_f8<FA, FB>(ga[slot][i], gb[slot][j], acc[i][j]);
+    }
+  };
+  // the next half's fragment and scale reads between this half's MFMAs
+  auto pin8 = [&]() {
+    constexpr int R = (MX ? 3 : 2) * (FM + FN);
+#pragma unroll
+    for (int i = 0; i < FM * FN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    }
+    if constexpr (R > FM * FN) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, R - FM * FN, 0);
+  };
 
   prologue(s);
   for (;;) {
@@ -1109,8 +1099,23 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel4(SkPlan pl) {
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    rd(ring, 0, 0);
-    if constexpr (AREG) {
+    if constexpr (F8) {
+      // two FP8 MFMA half-steps of 64 k per 128-wide stage tile
+      rd8(ring, 0, 0);
+      for (int j = 0; j < len; ++j) {
+        u16* cur = ring + (j & 1) * STAGE;
+        rd8(cur, 1, 1);
+        mma8(0);
+        pin8();
+        wait_vm_lds<0>();  // tile j+1 landed (operands and scale words)
+        __syncthreads();   // tile j+1 in LDS for every wave; tile j read by every wave
+        issue_to(s, j & 1, j + 2);
+        rd8(ring + ((j + 1) & 1) * STAGE, 0, 0);  // unused after the last step
+        mma8(1);
+        pin8();
+      }
+    } else if constexpr (AREG) {
+      rd(ring, 0, 0);
       // A's tile j+1 is loaded into registers at the start of step j (its
       // loads spread between the first k-step's MFMAs) and written to the
       // free stage at the end; B's tile j+2 goes by DMA after the barrier.
@@ -1140,6 +1145,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel4(SkPlan pl) {
         pin();
       }
     } else {
+      rd(ring, 0, 0);
       for (int j = 0; j < len; ++j) {
         u16* cur = ring + (j & 1) * STAGE;
         rd(cur, 1, 1);
@@ -1193,6 +1199,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel4(SkPlan pl) {
       int phase = nparts > 1 ? 0 : 1;
       bool summed = false;  // phase 1 on a sum of partials
       const int my_slot = part_slot(pl, item);
+      float dq = 1.0f;  // FP8 with per-tensor scales: 1 / (sA sB)
+      if constexpr (F8 && !MX)
+        dq = inv_scale(*pl.amax_a, fp8_max(FA)) * inv_scale(*pl.amax_b, fp8_max(FB));
       for (;;) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -1230,10 +1239,14 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel4(SkPlan pl) {
                   first = false;
                 });
               }
+              if constexpr (F8 && !MX) {
+#pragma unroll
+                for (int t = 0; t < 16; ++t) vals[t] *= dq;
+              }
               const int r0 = s.m0 + wm * WM + i * 32, cb = s.n0 + wn * WN + j * 32;
               const int region = __builtin_amdgcn_readfirstlane(epi_region<MODE>(e, r0, cb));
               const int r = r0 + er;
-              if (cb < P.N && r < P.M) epi_row16<MODE>(e, region, r, cb + ec, vals);
+              if (cb < P.N && r < P.M) epi_row16<MODE, FMT == 0>(e, region, r, cb + ec, vals);
             }
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -1292,10 +1305,18 @@ bool operand_ok(const Operand& op) {
          op.ld1 > 0 && op.split >= 0 && (op.split % 64 == 0 || op.split >= (1 << 30));
 }
 
+// FP8 products run on the four-wave kernel, except the weight gradients
+// with current scales (E4M3 x E5M2): their k-extent is the token count, a
+// short main loop per tile, and there the eight-wave kernel, whose epilogue
+// is spread over twice the waves, measured faster.
 template <int MODE, int FMT, bool MX = false>
 hipError_t launch_plan_fp8(const SkPlan& pl, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_sk_kernel<KMAJOR, KMAJOR, MODE, FMT, MX>), dim3(grid), dim3(64 * WAVES),
-                     0, s, pl);
+  if constexpr (!MX && FMT - 1 == FP8_E4M3 + 2 * FP8_E5M2)
+    hipLaunchKernelGGL((gemm_sk_kernel<KMAJOR, KMAJOR, MODE, FMT>), dim3(grid), dim3(64 * WAVES),
+                       0, s, pl);
+  else
+    hipLaunchKernelGGL((gemm_kernel4<KMAJOR, KMAJOR, MODE, FMT, MX>), dim3(grid), dim3(256), 0, s,
+                       pl);
   return hipGetLastError();
 }
 
@@ -1305,7 +1326,7 @@ hipError_t launch_plan(const SkPlan& pl, int grid, hipStream_t s) {
   if constexpr (AMAJ == KMAJOR && BMAJ == KMAJOR)
     hipLaunchKernelGGL((gemm_kernel4<AMAJ, BMAJ, MODE>), dim3(grid), dim3(256), 0, s, pl);
   else
-    hipLaunchKernelGGL((gemm_sk_kernel<AMAJ, BMAJ, MODE, 0, false, H0>), dim3(grid),
+    hipLaunchKernelGGL((gemm_sk_kernel<AMAJ, BMAJ, MODE, 0, H0>), dim3(grid),
                        dim3(64 * WAVES), 0, s, pl);
   return hipGetLastError();
 }

@@ -38,7 +38,8 @@ enum EpiMode {
                      // for gc < lo_cols also o3[r*ld3+gc] = fp16(v) (saturated);
                      // else o1 = v (u), o2 = GeLU(v) (g) at column gc - split
   EPI_RESIDUAL = 1,  // o0[r*ld0+c] = D(v) + i0[r*ld0+c], D the dropout `drop` of element
-                     // r*ld0+c (the identity when drop.on = 0)
+                     // r*ld0+c (the identity when drop.on = 0; FP8 products ignore
+                     // `drop`: FP8 layers take no dropout)
   EPI_DGELU = 2,     // c < split: o0[r*ld0+c] = v; else o1[r*ld1+col_off1+c-split] =
                      //   v * GeLU'(i0[r*ld2 + c-split])
   EPI_STORE2_COLS = 3,  // c < split: o0[r*ld0+c]; else o1[r*ld1 + c-split]
