@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define PTB_ABI_VERSION 10
+#define PTB_ABI_VERSION 11
 
 enum ptb_status {
   PTB_OK = 0,
@@ -466,9 +466,12 @@ int32_t ptb_fp8_workspace_bytes(const ptb_dims* dims, int32_t recipe, size_t* by
  *   W2T    E4M3 [h][pad128(K2)]   W2^T, K2 = n d + f
  *   W2     E4M3 [K2][pad128(h)]   W2
  *   W1T_S, W1_S, W2T_S, W2_S  PTB_FP8_MX only: the block scales of each
- *          copy, uint32 words [pad128(k)/128][pad64(rows)] for a copy of
- *          `rows` rows and contraction extent k: word [j][r] holds in byte b
- *          the E8M0 scale of row r's k-block 4 j + b (32 values)
+ *          copy, pad128(k)/128 x pad128(rows) x 4 bytes for a copy of `rows`
+ *          rows and contraction extent k, one E8M0 code per row and k-block
+ *          of 32 values, in the order the matrix cores' lanes consume them:
+ *          with r = 128 g + 32 i + l (i < 4, l < 32), the code of row r's
+ *          k-block 4 j + b (b < 4) is byte
+ *            4 (j pad128(rows) + 128 g) + 16 l + 8 (b & 1) + 4 (b >> 1) + i
  * pad128(v) / pad64(v) round up to a multiple of 128 / 64; padding codes
  * are zero, padding blocks and rows have scale code 127.  Parts a recipe
  * does not use (AMAX under PTB_FP8_MX, the scales under PTB_FP8_CURRENT)
@@ -492,11 +495,11 @@ int32_t ptb_fp8_quantize(const void* x, int32_t rows, int32_t cols, int32_t form
                          void* q, void* qt, void* stream);
 
 /* The block-scaled (PTB_FP8_MX) cast on its own, for the same x: codes
- * row-wise to q [rows][pad128(cols)] with scale words q_scales
- * [pad128(cols)/128][pad64(rows)] (blocks along each row), and/or
- * transposed to qt [cols][pad128(rows)] with qt_scales
- * [pad128(rows)/128][pad64(cols)] (blocks along each column of x); word
- * layout as for the weight buffer's scale parts.  A copy is written when
+ * row-wise to q [rows][pad128(cols)] with scales q_scales
+ * (pad128(cols)/128 x pad128(rows) x 4 bytes, blocks along each row),
+ * and/or transposed to qt [cols][pad128(rows)] with qt_scales
+ * (pad128(rows)/128 x pad128(cols) x 4 bytes, blocks along each column of
+ * x); byte order as for the weight buffer's scale parts.  A copy is written when
  * both its pointers are non-NULL.  The same kernel as the layer's casts. */
 int32_t ptb_fp8_quantize_mx(const void* x, int32_t rows, int32_t cols, int32_t format, void* q,
                             void* q_scales, void* qt, void* qt_scales, void* stream);

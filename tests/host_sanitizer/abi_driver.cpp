@@ -113,8 +113,8 @@ void run_quantize() {
     expect(ptb_fp8_quantize(x.p, rows, cols, PTB_FP8_E4M3, static_cast<float*>(amax.p), q.p,
                             qt.p, nullptr), PTB_OK, "ptb_fp8_quantize");
     const size_t p128r = (rows + 127) / 128 * 128, p128c = (cols + 127) / 128 * 128;
-    Buf mq(rows * p128c), mqs(p128c / 128 * p64r * 4), mqt(cols * p128r),
-        mqts(p128r / 128 * p64c * 4);
+    Buf mq(rows * p128c), mqs(p128c / 128 * p128r * 4), mqt(cols * p128r),
+        mqts(p128r / 128 * p128c * 4);
     expect(ptb_fp8_quantize_mx(x.p, rows, cols, PTB_FP8_E5M2, mq.p, mqs.p, mqt.p, mqts.p, nullptr),
            PTB_OK, "ptb_fp8_quantize_mx");
   }

@@ -147,8 +147,9 @@ hipError_t launch_gemm_mx(const GemmProblem& p, Fp8Format, const MxScales& sa, F
   touch_operand(p.B);
   touch_epilogue(p, mode);
   const long ks = pad128(p.K) / 128;
-  touch_matrix(sa.p, ks, sa.ld, p.M, 4);
-  touch_matrix(sb.p, ks, sb.ld, p.N, 4);
+  // the kernel reads the scales of whole 256-row tiles, bounded by the array
+  touch_matrix(sa.p, ks, sa.ld, sa.ld, 4);
+  touch_matrix(sb.p, ks, sb.ld, sb.ld, 4);
   touch_scratch(s);
   return hipSuccess;
 }

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert P.ptb_abi_version() == 10
+    assert P.ptb_abi_version() == 11
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert P.ptb_status_string(code) and P.ptb_status_string(code) != "unknown status"
     assert P.ptb_status_string(12345) == "unknown status"
@@ -282,15 +282,14 @@ def test_fp8_weight_layout_and_sizes(lib):
 
 
 def test_fp8_mx_weight_layout_and_sizes(lib):
-    """Block scaling: no amax; each copy followed by its scale words
-    [pad128(k)/128][pad64(rows)] (4 bytes each); the workspace and the stash
-    grow by the scale words of their copies."""
+    """Block scaling: no amax; each copy followed by its scales,
+    pad128(k)/128 x pad128(rows) x 4 bytes; the workspace and the stash grow
+    by the scales of their copies."""
     d = good_dims()
     h, hl, f, T = 256, 256, 1024, 512
     N1, K2 = 3 * hl + f, hl + f
     pad = lambda v: (v + 127) // 128 * 128
-    p64 = lambda v: (v + 63) // 64 * 64
-    words = lambda rows, k: pad(k) // 128 * p64(rows) * 4
+    words = lambda rows, k: pad(k) // 128 * pad(rows) * 4
     lay = P.ptb_fp8_weights_layout(d, "mx")
     assert lay["amax"] == P.FP8_ABSENT
     order = ("w1t", "w1t_s", "w1", "w1_s", "w2t", "w2t_s", "w2", "w2_s")

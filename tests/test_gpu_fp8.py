@@ -112,16 +112,22 @@ def test_quantize_small_and_ragged_shapes(fmt, rows, cols):
     assert not gott[:, rows:].any()
 
 
-def _mx_words(sc, kp, rows_p):
-    """Scale words [kp/128][rows_p] from block codes sc [rows, nblocks]
-    (blocks along k): byte b of word [j][r] = sc[r, 4 j + b], 127 where the
-    block or the row is padding."""
+def _mx_scale_bytes(sc, kp, rows_p):
+    """The scales of a block-scaled copy as the ABI lays them out, from block
+    codes sc [rows, nblocks] (blocks along k), 127 where the block or the row
+    is padding: [kp/128][4 rows_p] bytes; with r = 128 g + 32 i + l, the code
+    of row r's block 4 j + b sits in row j at byte
+    512 g + 16 l + 8 (b & 1) + 4 (b >> 1) + i."""
     rows, nb = sc.shape
-    full = np.full((rows_p, kp // 32), 127, dtype=np.uint32)
+    full = np.full((rows_p, kp // 32), 127, dtype=np.uint8)
     full[:rows, :nb] = sc
-    full = full.reshape(rows_p, kp // 128, 4)
-    words = full[:, :, 0] | full[:, :, 1] << 8 | full[:, :, 2] << 16 | full[:, :, 3] << 24
-    return words.T.copy()
+    r = np.arange(rows_p)[:, None]
+    b = np.arange(4)[None, :]
+    pos = 512 * (r // 128) + 16 * (r % 32) + 8 * (b & 1) + 4 * (b >> 1) + (r // 32) % 4
+    assert np.array_equal(np.sort(pos.ravel()), np.arange(4 * rows_p))  # a permutation
+    out = np.empty((kp // 128, 4 * rows_p), dtype=np.uint8)
+    out[:, pos.ravel()] = full.reshape(rows_p, kp // 128, 4).transpose(1, 0, 2).reshape(kp // 128, -1)
+    return out
 
 
 def _check_mx_copies(q, qs, qt, qts, x, fmt):
@@ -129,27 +135,25 @@ def _check_mx_copies(q, qs, qt, qts, x, fmt):
     against the oracle, padding included."""
     rows, cols = x.shape
     p128 = lambda v: (v + 127) // 128 * 128
-    p64 = lambda v: (v + 63) // 64 * 64
     codes, sc, _ = F8.mx_quantize(x, fmt, axis=1)
     got = q.cpu().numpy()
     np.testing.assert_array_equal(got[:, :cols], codes)
     assert not got[:, cols:].any()
-    np.testing.assert_array_equal(qs.cpu().numpy().view(np.uint32),
-                                  _mx_words(sc, p128(cols), p64(rows)))
+    np.testing.assert_array_equal(qs.cpu().numpy().view(np.uint8).reshape(p128(cols) // 128, -1),
+                                  _mx_scale_bytes(sc, p128(cols), p128(rows)))
     codes0, sc0, _ = F8.mx_quantize(x, fmt, axis=0)
     gott = qt.cpu().numpy()
     np.testing.assert_array_equal(gott[:, :rows], codes0.T)
     assert not gott[:, rows:].any()
-    np.testing.assert_array_equal(qts.cpu().numpy().view(np.uint32),
-                                  _mx_words(sc0.T, p128(rows), p64(cols)))
+    np.testing.assert_array_equal(qts.cpu().numpy().view(np.uint8).reshape(p128(rows) // 128, -1),
+                                  _mx_scale_bytes(sc0.T, p128(rows), p128(cols)))
 
 
 def _mx_buffers(rows, cols, dev):
     p128 = lambda v: (v + 127) // 128 * 128
-    p64 = lambda v: (v + 63) // 64 * 64
     fill = lambda shape, dt: torch.full(shape, 0x55, dtype=dt, device=dev)
-    return (fill((rows, p128(cols)), torch.uint8), fill((p128(cols) // 128, p64(rows)), torch.int32),
-            fill((cols, p128(rows)), torch.uint8), fill((p128(rows) // 128, p64(cols)), torch.int32))
+    return (fill((rows, p128(cols)), torch.uint8), fill((p128(cols) // 128, p128(rows)), torch.int32),
+            fill((cols, p128(rows)), torch.uint8), fill((p128(rows) // 128, p128(cols)), torch.int32))
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
@@ -196,15 +200,14 @@ def test_cast_weights_mx_match_the_oracle():
     w1 = np.concatenate([f(lay["w_qkv"]), f(lay["w_fc1"])], axis=1)
     w2 = np.concatenate([f(lay["w_o"]), f(lay["w_fc2"])], axis=0)
     p128 = lambda v: (v + 127) // 128 * 128
-    p64 = lambda v: (v + 63) // 64 * 64
     for name, mat, tname in (("w1", w1, "w1t"), ("w2", w2, "w2t")):
         R, C = mat.shape
         view = lambda o, shape, dt: buf[o:o + int(np.prod(shape)) * (4 if dt == torch.int32 else 1)
                                         ].view(dt).view(shape)
         q = view(off[name], (R, p128(C)), torch.uint8)
-        qs = view(off[name + "_s"], (p128(C) // 128, p64(R)), torch.int32)
+        qs = view(off[name + "_s"], (p128(C) // 128, p128(R)), torch.int32)
         qt = view(off[tname], (C, p128(R)), torch.uint8)
-        qts = view(off[tname + "_s"], (p128(R) // 128, p64(C)), torch.int32)
+        qts = view(off[tname + "_s"], (p128(R) // 128, p128(C)), torch.int32)
         _check_mx_copies(q, qs, qt, qts, mat, F8.E4M3)
 
 

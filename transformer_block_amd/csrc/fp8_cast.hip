@@ -180,7 +180,8 @@ __device__ __forceinline__ float mx_mult(uint32_t c) {
 // One tile of X as cast_kernel, block-scaled.  Thread (br, bc) owns rows
 // r0 + 4 br .. +3 and columns c0 + 8 bc .. +7.  Row-wise: the 32-column
 // block of a row spans threads bc & ~3 .. +3; threads bc = 0 collect the four
-// block codes of their rows (the k-step's scale word) and write four words.
+// block codes of their rows (the tile is one k-step) and write them where
+// mx_scale_byte puts them.
 // Transposed: the 32-row block of a column spans waves 2 blk and 2 blk + 1;
 // each wave reduces its 16 rows by shuffles and leaves the column maxima in
 // LDS.
@@ -223,15 +224,20 @@ __global__ __launch_bounds__(256) void mx_cast_kernel(CastSrc x, uint8_t* rows, 
       const int r = r0 + 4 * br + i;
       if (r < x.R) *reinterpret_cast<uint2*>(rows + static_cast<size_t>(r) * ldr + c) = q;
     }
-    uint32_t word[4];
+    uint32_t blk[4][4];  // [row i][block b]
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      word[i] = code[i] | static_cast<uint32_t>(__shfl(static_cast<int>(code[i]), lane + 4)) << 8 |
-                static_cast<uint32_t>(__shfl(static_cast<int>(code[i]), lane + 8)) << 16 |
-                static_cast<uint32_t>(__shfl(static_cast<int>(code[i]), lane + 12)) << 24;
-    if (bc == 0 && r0 < rs_ld)
-      *reinterpret_cast<uint4*>(rs + static_cast<size_t>(c0 / CC) * rs_ld + r0 + 4 * br) =
-          make_uint4(word[0], word[1], word[2], word[3]);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        blk[i][b] = static_cast<uint32_t>(__shfl(static_cast<int>(code[i]), lane + 4 * b));
+    if (bc == 0 && r0 < rs_ld) {
+      uint8_t* sb = reinterpret_cast<uint8_t*>(rs);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          sb[mx_scale_byte(c0 / CC, r0 + 4 * br + i, b, rs_ld)] = static_cast<uint8_t>(blk[i][b]);
+    }
   }
   if (cols == nullptr || r0 >= ldc) return;
 #pragma unroll
@@ -249,11 +255,13 @@ __global__ __launch_bounds__(256) void mx_cast_kernel(CastSrc x, uint8_t* rows, 
     tt[col * TSW + br] = quant4<FMT>(val(0, j), val(1, j), val(2, j), val(3, j), s);
   }
   if (tid < CC && c0 + tid < cs_ld) {
-    // this tile's two k-blocks of column c0 + tid: bytes (r0 % 128) / 32 + 0, 1
-    const uint32_t pair = mx_code<FMT>(umax(cmax[tid], cmax[CC + tid])) |
-                          mx_code<FMT>(umax(cmax[2 * CC + tid], cmax[3 * CC + tid])) << 8;
-    uint8_t* base = reinterpret_cast<uint8_t*>(cs + static_cast<size_t>(r0 / 128) * cs_ld + c0 + tid);
-    *reinterpret_cast<uint16_t*>(base + (r0 % 128) / 32) = static_cast<uint16_t>(pair);
+    // this tile's two k-blocks of column c0 + tid: blocks (r0 % 128) / 32 + 0, 1
+    uint8_t* sb = reinterpret_cast<uint8_t*>(cs);
+    const int b0 = (r0 % 128) / 32;
+    sb[mx_scale_byte(r0 / 128, c0 + tid, b0, cs_ld)] =
+        static_cast<uint8_t>(mx_code<FMT>(umax(cmax[tid], cmax[CC + tid])));
+    sb[mx_scale_byte(r0 / 128, c0 + tid, b0 + 1, cs_ld)] =
+        static_cast<uint8_t>(mx_code<FMT>(umax(cmax[2 * CC + tid], cmax[3 * CC + tid])));
   }
   __syncthreads();
   const int oc = tid >> 1, ow = (tid & 1) * 8;
@@ -315,10 +323,10 @@ hipError_t launch_cast_mx(const CastSrc& x, Fp8Format fmt, uint8_t* rows, int ld
   if (!src_ok(x) || (rows == nullptr && cols == nullptr)) return hipErrorInvalidValue;
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   if (rows != nullptr && (ldr < x.C || ldr % CC != 0 || !al(rows) || rs == nullptr || !al(rs) ||
-                          rs_ld < x.R || rs_ld % 64 != 0))
+                          rs_ld < x.R || rs_ld % 128 != 0))
     return hipErrorInvalidValue;
   if (cols != nullptr && (ldc < x.R || ldc % CC != 0 || !al(cols) || cs == nullptr || !al(cs) ||
-                          cs_ld < x.C || cs_ld % 64 != 0))
+                          cs_ld < x.C || cs_ld % 128 != 0))
     return hipErrorInvalidValue;
   // tiles over every code and scale word either copy holds (padding included)
   int rspan = x.R, cspan = x.C;

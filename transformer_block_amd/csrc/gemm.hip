@@ -1010,32 +1010,28 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel4(SkPlan pl) {
     if constexpr (R < FM * FN) __builtin_amdgcn_sched_group_barrier(SG_MFMA, FM * FN - R, 0);
     if constexpr (R > FM * FN) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, R - FM * FN, 0);
   };
-  // MX: the 32 bytes of one 64-wide half of a stage tile per fragment (bf16
-  // k-steps 2 half and 2 half + 1 of the same rows), and the scale code of
-  // the lane's row for the block the matrix cores take from this lane: lane
-  // half h holds k [64 half + 16 h, +16) and [64 half + 32 + 16 h, +16), so
-  // the matrix cores' block b of this half is the tile's 32-wide block
-  // 2 half + b, whose scale they take from lane half b: byte 2 half + h of the
-  // row's word.  Packed one byte per fragment (sa8 byte i: A fragment i, sb8
-  // byte j: B fragment j) for the MFMA's immediate byte selects.
+  // FP8: the 32 bytes of one 64-wide half of a stage tile per fragment (bf16
+  // k-steps 2 half and 2 half + 1 of the same rows).  MX: lane half h' holds
+  // k [64 half + 16 h', +16) and [64 half + 32 + 16 h', +16), so the matrix
+  // cores' block b of this half is the tile's 32-wide block 2 half + b, whose
+  // scale they take from lane half b.  In the scale layout (mx_scale_byte)
+  // the lane finds the codes of its four fragments' rows for both halves in
+  // 8 bytes, word 0 for half 0 and word 1 for half 1, byte i for fragment i:
+  // the operands of the MFMA's immediate byte selects, one word per half
+  // and operand, read with that half's fragments.
   int koff[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) koff[ks] = kfrag_offset(ks, lane);
   i32x8 ga[2][F8 ? FM : 1], gb[2][F8 ? FN : 1];
   uint32_t sa8[2], sb8[2];
+  const int srec = 4 * (lane & 31) + 2 * (lane >> 5);  // the lane's 8 bytes, in words
   auto rd8 = [&](const u16* st, int half, int slot) {
     if constexpr (F8) {
       const int k0 = koff[2 * half], k1 = koff[2 * half + 1];
       if constexpr (MX) {
-        const uint32_t* sw = sring + ((st - ring) / STAGE) * (2 * TILE) + (lane & 31);
-        const uint32_t bit = 16 * half + 8 * (lane >> 5);
-        uint32_t pa = 0, pb = 0;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) pa |= ((sw[wm * WM + i * 32] >> bit) & 0xffu) << (8 * i);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) pb |= ((sw[TILE + wn * WN + j * 32] >> bit) & 0xffu) << (8 * j);
-        sa8[slot] = pa;
-        sb8[slot] = pb;
+        const uint32_t* sw = sring + ((st - ring) / STAGE) * (2 * TILE) + srec + half;
+        sa8[slot] = sw[wm * WM];
+        sb8[slot] = sw[TILE + wn * WN];
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -1067,9 +1063,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel4(SkPlan pl) {
           acc[i][j] = mfma32x32x64_f8<FA, FB>(ga[slot][i], gb[slot][j], acc[i][j]);
     }
   };
-  // the next half's fragment and scale reads between this half's MFMAs
-  auto pin8 = [&]() {
-    constexpr int R = (MX ? 3 : 2) * (FM + FN);
+  // the next half's fragment reads (half 0: and the scale reads) between
+  // this half's MFMAs
+  auto pin8 = [&](auto next_half) {
+    constexpr int R = 2 * (FM + FN) + (MX ? 2 : 0);
 #pragma unroll
     for (int i = 0; i < FM * FN; ++i) {
       __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
@@ -1106,13 +1103,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel4(SkPlan pl) {
         u16* cur = ring + (j & 1) * STAGE;
         rd8(cur, 1, 1);
         mma8(0);
-        pin8();
+        pin8(std::integral_constant<int, 1>{});
         wait_vm_lds<0>();  // tile j+1 landed (operands and scale words)
         __syncthreads();   // tile j+1 in LDS for every wave; tile j read by every wave
         issue_to(s, j & 1, j + 2);
         rd8(ring + ((j + 1) & 1) * STAGE, 0, 0);  // unused after the last step
         mma8(1);
-        pin8();
+        pin8(std::integral_constant<int, 0>{});
       }
     } else if constexpr (AREG) {
       rd(ring, 0, 0);
@@ -1482,7 +1479,7 @@ hipError_t launch_gemm_mx(const GemmProblem& prob, Fp8Format fa, const MxScales&
   // every row of both operands
   if (prob.A.ld0 % 16 != 0 || prob.A.ld1 % 16 != 0 || prob.B.ld0 % 16 != 0 ||
       prob.B.ld1 % 16 != 0 || prob.K % (2 * BK) != 0 || sa.p == nullptr || sb.p == nullptr ||
-      sa.ld < prob.M || sb.ld < prob.N || sa.ld % 64 != 0 || sb.ld % 64 != 0)
+      sa.ld < prob.M || sb.ld < prob.N || sa.ld % 128 != 0 || sb.ld % 128 != 0)
     return hipErrorInvalidValue;
   const size_t ks = static_cast<size_t>(prob.K) / (2 * BK);
   if (ks * sa.ld * 4 >= (1UL << 31) || ks * sb.ld * 4 >= (1UL << 31)) return hipErrorInvalidValue;

@@ -99,9 +99,18 @@ enum Fp8Format { FP8_E4M3 = 0, FP8_E5M2 = 1 };
 
 // Block-scaled (MX) FP8: blocks of 32 consecutive values along a copy's
 // contiguous (contraction) dimension, one E8M0 scale each (code e means
-// 2^(e - 127)).  A copy's scales are 32-bit words, one per (128-wide k-step,
-// row): word[ks * ld + r] holds in byte b the code of k-block 4 ks + b of row
-// r; ld >= rows and a multiple of 64.  The GEMM reads them as they are.
+// 2^(e - 127)).  A copy's scales are ld bytes x 4 per 128-wide k-step ks
+// (ld >= rows, a multiple of 128), in the order the matrix cores' lanes take
+// them: for row r = 128 g + 32 i + l (i < 4, l < 32), the code of k-block
+// 4 ks + b sits at byte mx_scale_byte(ks, r, b, ld) = 4 (ks ld + 128 g) +
+// 16 l + 8 (b & 1) + 4 (b >> 1) + i.  A wave holding rows 128 g + 32 i + l
+// (fragment i of lane l and l + 32) then finds in the 8 bytes at
+// 16 l + 8 h' of the group the codes lane half h' supplies for both
+// 64-wide halves of the k-step, one byte per fragment.
+constexpr size_t mx_scale_byte(int ks, int r, int b, int ld) {
+  return 4 * (static_cast<size_t>(ks) * ld + (r & ~127)) + 16 * (r & 31) + 8 * (b & 1) +
+         4 * (b >> 1) + ((r >> 5) & 3);
+}
 struct MxScales {
   const uint32_t* p;
   int ld;
@@ -186,10 +195,10 @@ hipError_t launch_cast_fp8(const CastSrc& x, Fp8Format fmt, const float* amax, u
 
 // Block-scaled FP8 copies of X: code = RNE(clamp(x 2^-X, -FMAX, FMAX)) with
 // X = floor(log2 amax_block) - emax (emax 8 for E4M3, 15 for E5M2; 0 for an
-// all-zero block), written row-wise to rows [R][ldr] with scale words rs
-// (ld rs_ld >= R) and/or transposed to cols [C][ldc] with scale words cs
-// (ld cs_ld >= C).  ldr and ldc are multiples of 128 (whole k-steps);
-// padding codes are zero, padding blocks and rows get code 127.
+// all-zero block), written row-wise to rows [R][ldr] with scales rs
+// (MxScales layout, ld rs_ld >= R) and/or transposed to cols [C][ldc] with
+// scales cs (ld cs_ld >= C).  ldr and ldc are multiples of 128 (whole
+// k-steps); padding codes are zero, padding blocks and rows get code 127.
 hipError_t launch_cast_mx(const CastSrc& x, Fp8Format fmt, uint8_t* rows, int ldr, uint32_t* rs,
                           int rs_ld, uint8_t* cols, int ldc, uint32_t* cs, int cs_ld,
                           hipStream_t stream);

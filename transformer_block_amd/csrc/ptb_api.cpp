@@ -238,7 +238,7 @@ size_t pad64(size_t v) { return (v + 63) & ~static_cast<size_t>(63); }
 
 // One FP8 copy of an operand: `rows` rows of codes, contraction extent k
 // padded to kp = pad128(k), and under block scaling its scale words
-// [kp / 128][pad64(rows)].
+// (mx_scale_byte layout) [kp / 128][pad128(rows)] words.
 struct Fp8Copy {
   size_t codes, scales;  // byte offsets (scales: SIZE_MAX when absent)
   size_t rows, kp;
@@ -253,7 +253,7 @@ Fp8Copy add_copy(size_t* o, size_t rows, size_t k, bool mx) {
   c.scales = SIZE_MAX;
   if (mx) {
     c.scales = *o;
-    *o = align_up(*o + c.kp / 128 * pad64(rows) * sizeof(uint32_t));
+    *o = align_up(*o + c.kp / 128 * pad128(rows) * sizeof(uint32_t));
   }
   return c;
 }
@@ -412,18 +412,18 @@ hipError_t cast_fp8(const ptb::CastSrc& x, ptb::Fp8Format fmt, float* amax, uint
   } while (0)
 
 // An FP8 copy in a caller buffer: codes [rows][kp] and, under block
-// scaling, scale words [kp / 128][pad64(rows)].
+// scaling, scale words [kp / 128][pad128(rows)] (mx_scale_byte layout).
 struct Copy8 {
   uint8_t* q;
   uint32_t* s;
   size_t ld;   // kp
-  int sld;     // pad64(rows)
+  int sld;     // pad128(rows)
   size_t rows;
 };
 Copy8 copy_at(void* base, const Fp8Copy& c) {
   return Copy8{at<uint8_t>(base, c.codes),
                c.scales == SIZE_MAX ? nullptr : at<uint32_t>(base, c.scales), c.kp,
-               static_cast<int>(pad64(c.rows)), c.rows};
+               static_cast<int>(pad128(c.rows)), c.rows};
 }
 Copy8 copy_at(const void* base, const Fp8Copy& c) {
   return copy_at(const_cast<void*>(base), c);
@@ -1192,9 +1192,9 @@ int32_t ptb_fp8_quantize_mx(const void* x, int32_t rows, int32_t cols, int32_t f
   PTB_HIP(ptb::launch_cast_mx(
       cast_one(x, cols, rows, cols), format == PTB_FP8_E4M3 ? ptb::FP8_E4M3 : ptb::FP8_E5M2,
       row_copy ? static_cast<uint8_t*>(q) : nullptr, static_cast<int>(pad128(C)),
-      row_copy ? static_cast<uint32_t*>(q_scales) : nullptr, static_cast<int>(pad64(R)),
+      row_copy ? static_cast<uint32_t*>(q_scales) : nullptr, static_cast<int>(pad128(R)),
       col_copy ? static_cast<uint8_t*>(qt) : nullptr, static_cast<int>(pad128(R)),
-      col_copy ? static_cast<uint32_t*>(qt_scales) : nullptr, static_cast<int>(pad64(C)),
+      col_copy ? static_cast<uint32_t*>(qt_scales) : nullptr, static_cast<int>(pad128(C)),
       reinterpret_cast<hipStream_t>(stream)));
   return PTB_OK;
 }
