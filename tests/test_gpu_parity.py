@@ -47,6 +47,12 @@ EDGE_CASES = [
                                     mlp="swiglu"), True),
     ("rmsnorm_swiglu_stack2", W("rsw2", 2, 130, 256, 2, 128, 512, 48, layers=2, seed=28,
                                 norm="rmsnorm", mlp="swiglu"), True),
+    # the widest rows (h = 16384) and the 175B share's row width at 300 tokens:
+    # the LayerNorm backward's workgroups then hold one or two rows each
+    ("widest_rows_h16384", W("h16k", 1, 300, 16384, 1, 128, 256, 64, seed=29), True),
+    ("widest_rows_h16384_rmsnorm", W("h16kr", 1, 300, 16384, 1, 128, 256, 64, seed=31,
+                                     norm="rmsnorm"), True),
+    ("rows_h12288_s300", W("h12k", 1, 300, 12288, 1, 128, 256, 64, seed=32), True),
 ]
 
 
