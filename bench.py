@@ -78,7 +78,9 @@ def stage_work(w):
     N1, K2 = 3 * hl + f, hl + f
     attn_pairs = w.batch * w.heads * window_pairs(w.seq, w.window)
     fwd = {
-        "layernorm_fwd": ("bytes", T * h * 2 * 2 + T * 8),
+        # x read; a (bf16) and its fp16 copy (the q, k product's operand)
+        # written; the row statistics
+        "layernorm_fwd": ("bytes", T * h * 2 * 3 + T * 8),
         # read the q, k columns of W_qkv (bf16), write their fp16 copy
         "cast_wqk_f16": ("bytes", h * 2 * hl * (2 + 2)),
         "gemm_qkv_fc1": ("flops", 2 * T * h * N1),

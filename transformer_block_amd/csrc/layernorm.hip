@@ -109,33 +109,40 @@ __global__ __launch_bounds__(LN_THREADS) void ln_fwd_kernel(const u16* __restric
 // dst[r][c] = fp16(src[r][c]) for a [rows, cols] block of a bf16 matrix
 // (cols a multiple of 8, row strides ld_src and ld_dst in elements): the
 // fp16 copy of the query/key columns of W_qkv for the fp16 q, k product.
-// Each workgroup converts CAST_ROWS consecutive rows; a thread takes 16-byte
-// chunks c = tid, tid + 256, ... of every one of them, all rows' loads issued
-// before the first store.  The conversion is exact for every bf16 value
-// inside the fp16 normal range; smaller magnitudes round to fp16 subnormals
-// (absolute error <= 2^-25) and larger ones saturate at 65504.
-constexpr int CAST_ROWS = 4;
+// The block's 16-byte chunks are numbered row by row; thread t of workgroup
+// g converts chunks 2048 g + t + 256 u (u < CAST_CHUNKS), all eight loads
+// issued before the first store, consecutive threads on consecutive chunks.
+// The conversion is exact for every bf16 value inside the fp16 normal range;
+// smaller magnitudes round to fp16 subnormals (absolute error <= 2^-25) and
+// larger ones saturate at 65504.
+constexpr int CAST_CHUNKS = 8;
 __global__ __launch_bounds__(256) void cast_f16_kernel(const u16* __restrict__ src, int ld_src,
                                                        u16* __restrict__ dst, int ld_dst,
                                                        int rows, int cols8) {
-  const int r0 = blockIdx.x * CAST_ROWS;
-  const int nr = rows - r0 < CAST_ROWS ? rows - r0 : CAST_ROWS;
-  for (int c = threadIdx.x; c < cols8; c += 256) {
-    uint4 v[CAST_ROWS];
+  const int total = rows * cols8;  // < 2^31 (checked by the launcher)
+  const int base = blockIdx.x * (256 * CAST_CHUNKS) + threadIdx.x;
+  uint4 v[CAST_CHUNKS];
+  int off[CAST_CHUNKS];  // destination element offset, -1 past the block
 #pragma unroll
-    for (int u = 0; u < CAST_ROWS; ++u)
-      if (u < nr) v[u] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(r0 + u) * ld_src + c * 8);
+  for (int u = 0; u < CAST_CHUNKS; ++u) {
+    const int idx = base + 256 * u;
+    off[u] = -1;
+    if (idx < total) {
+      const int r = idx / cols8, c = idx - r * cols8;
+      v[u] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(r) * ld_src + c * 8);
+      off[u] = r * ld_dst + c * 8;
+    }
+  }
 #pragma unroll
-    for (int u = 0; u < CAST_ROWS; ++u) {
-      if (u < nr) {
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(&v[u]);
-        uint4 o;
-        o.x = pack2h(lo_bf(w[0]), hi_bf(w[0]));
-        o.y = pack2h(lo_bf(w[1]), hi_bf(w[1]));
-        o.z = pack2h(lo_bf(w[2]), hi_bf(w[2]));
-        o.w = pack2h(lo_bf(w[3]), hi_bf(w[3]));
-        *reinterpret_cast<uint4*>(dst + static_cast<size_t>(r0 + u) * ld_dst + c * 8) = o;
-      }
+  for (int u = 0; u < CAST_CHUNKS; ++u) {
+    if (off[u] >= 0) {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(&v[u]);
+      uint4 o;
+      o.x = pack2h(lo_bf(w[0]), hi_bf(w[0]));
+      o.y = pack2h(lo_bf(w[1]), hi_bf(w[1]));
+      o.z = pack2h(lo_bf(w[2]), hi_bf(w[2]));
+      o.w = pack2h(lo_bf(w[3]), hi_bf(w[3]));
+      *reinterpret_cast<uint4*>(dst + off[u]) = o;
     }
   }
 }
@@ -327,9 +334,11 @@ hipError_t launch_layernorm_fwd(const u16* x, const u16* gamma, const u16* beta,
 hipError_t launch_cast_f16(const u16* src, int ld_src, int rows, int cols, u16* dst, int ld_dst,
                            hipStream_t s) {
   if (rows <= 0 || cols <= 0) return hipSuccess;
-  if (cols % 8 != 0 || ld_src % 8 != 0 || ld_dst % 8 != 0 || ld_src < cols || ld_dst < cols)
+  if (cols % 8 != 0 || ld_src % 8 != 0 || ld_dst % 8 != 0 || ld_src < cols || ld_dst < cols ||
+      static_cast<long>(rows) * ld_dst >= (1L << 31) || static_cast<long>(rows) * (cols / 8) >= (1L << 31))
     return hipErrorInvalidValue;
-  const int blocks = (rows + CAST_ROWS - 1) / CAST_ROWS;
+  const long chunks = static_cast<long>(rows) * (cols / 8);
+  const int blocks = static_cast<int>((chunks + 256 * CAST_CHUNKS - 1) / (256 * CAST_CHUNKS));
   hipLaunchKernelGGL(cast_f16_kernel, dim3(blocks), dim3(256), 0, s, src, ld_src, dst, ld_dst,
                      rows, cols / 8);
   return hipGetLastError();
