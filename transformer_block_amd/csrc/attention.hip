@@ -259,14 +259,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const size_t slot0 = (static_cast<size_t>(bi) * n + hd) * rsp.split_slots;
     const int first_slot = item.slot - item.chunk;
     {
-      float* pp = rsp.partials + (slot0 + item.slot) * PER_SLOT;
+      const __amdgpu_buffer_rsrc_t pr = dev_rsrc(rsp.partials + (slot0 + item.slot) * PER_SLOT, PER_SLOT);
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          st_dev(pp + ((wave * ND + db) * 16 + e) * 64 + lane, dk[db][e]);
-          st_dev(pp + BKB * D + ((wave * ND + db) * 16 + e) * 64 + lane, dv[db][e]);
-        }
+      for (int db = 0; db < ND; ++db) {
+        st16_dev(pr, (wave * ND + db) * 1024, lane, dk[db]);
+        st16_dev(pr, BKB * D + (wave * ND + db) * 1024, lane, dv[db]);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -275,16 +273,19 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     if (__builtin_amdgcn_readfirstlane(arrival) != item.nchunks - 1) return;
     if (tid == 0) rsp.counters[row_id] = 0;
     for (int c = 0; c < item.nchunks; ++c) {
-      const float* pp = rsp.partials + (slot0 + first_slot + c) * PER_SLOT;
+      const __amdgpu_buffer_rsrc_t pr =
+          dev_rsrc(rsp.partials + (slot0 + first_slot + c) * PER_SLOT, PER_SLOT);
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
+      for (int db = 0; db < ND; ++db) {
+        float a[16], v[16];
+        ld16_dev(pr, (wave * ND + db) * 1024, lane, a);
+        ld16_dev(pr, BKB * D + (wave * ND + db) * 1024, lane, v);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float a = ld_dev(pp + ((wave * ND + db) * 16 + e) * 64 + lane);
-          const float v = ld_dev(pp + BKB * D + ((wave * ND + db) * 16 + e) * 64 + lane);
-          dk[db][e] = c == 0 ? a : dk[db][e] + a;
-          dv[db][e] = c == 0 ? v : dv[db][e] + v;
+          dk[db][e] = c == 0 ? a[e] : dk[db][e] + a[e];
+          dv[db][e] = c == 0 ? v[e] : dv[db][e] + v[e];
         }
+      }
     }
   }
 
@@ -462,11 +463,9 @@ __global__ __launch_bounds__(256, BKQ == 32 ? 2 : 1) void attn_bwd_dq_kernel(
     const size_t slot0 = (static_cast<size_t>(bi) * n + hd) * rsp.split_slots;
     const int first_slot = item.slot - item.chunk;
     {
-      float* pp = rsp.partials + (slot0 + item.slot) * PER_SLOT;
+      const __amdgpu_buffer_rsrc_t pr = dev_rsrc(rsp.partials + (slot0 + item.slot) * PER_SLOT, PER_SLOT);
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) st_dev(pp + ((wave * ND + db) * 16 + e) * 64 + lane, dq[db][e]);
+      for (int db = 0; db < ND; ++db) st16_dev(pr, (wave * ND + db) * 1024, lane, dq[db]);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -475,14 +474,15 @@ __global__ __launch_bounds__(256, BKQ == 32 ? 2 : 1) void attn_bwd_dq_kernel(
     if (__builtin_amdgcn_readfirstlane(arrival) != item.nchunks - 1) return;
     if (tid == 0) rsp.counters[row_id] = 0;
     for (int c = 0; c < item.nchunks; ++c) {
-      const float* pp = rsp.partials + (slot0 + first_slot + c) * PER_SLOT;
+      const __amdgpu_buffer_rsrc_t pr =
+          dev_rsrc(rsp.partials + (slot0 + first_slot + c) * PER_SLOT, PER_SLOT);
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
+      for (int db = 0; db < ND; ++db) {
+        float a[16];
+        ld16_dev(pr, (wave * ND + db) * 1024, lane, a);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float a = ld_dev(pp + ((wave * ND + db) * 16 + e) * 64 + lane);
-          dq[db][e] = c == 0 ? a : dq[db][e] + a;
-        }
+        for (int e = 0; e < 16; ++e) dq[db][e] = c == 0 ? a[e] : dq[db][e] + a[e];
+      }
     }
   }
 

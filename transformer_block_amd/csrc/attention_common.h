@@ -277,6 +277,36 @@ __device__ __forceinline__ float ld_dev(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A lane's 16 fp32 values of a 1024-float block of a split row's partial, at
+// device scope in 16-byte accesses: the cache policy of relaxed agent-scope
+// atomics (sc1) on buffer loads and stores.  Value e of lane l sits at float
+// [e / 4][l][e % 4] of the block, so one access covers 1 KB.  `blk` is the
+// block's first float in the slot that `r` covers (below 2^29 floats).
+constexpr int kDevPolicy = 16;  // sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(float* slot, int floats) {
+  return __builtin_amdgcn_make_buffer_rsrc(slot, static_cast<short>(0), floats * 4, 0x00020000);
+}
+template <typename V>
+__device__ __forceinline__ void st16_dev(__amdgpu_buffer_rsrc_t r, int blk, int lane, const V& v) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const unsigned d0 = __float_as_uint(v[4 * q]), d1 = __float_as_uint(v[4 * q + 1]);
+    const unsigned d2 = __float_as_uint(v[4 * q + 2]), d3 = __float_as_uint(v[4 * q + 3]);
+    typedef unsigned u4v __attribute__((ext_vector_type(4)));
+    const u4v d = {d0, d1, d2, d3};
+    __builtin_amdgcn_raw_buffer_store_b128(d, r, (blk + q * 256 + lane * 4) * 4, 0, kDevPolicy);
+  }
+}
+__device__ __forceinline__ void ld16_dev(__amdgpu_buffer_rsrc_t r, int blk, int lane, float* v) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const auto d = __builtin_amdgcn_raw_buffer_load_b128(r, (blk + q * 256 + lane * 4) * 4, 0,
+                                                         kDevPolicy);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[4 * q + k] = __uint_as_float(d[k]);
+  }
+}
+
 // Scratch of the split rows of one launch.
 struct RowSplit {
   float* partials;  // slot-major; `per_slot` floats each

@@ -195,10 +195,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const u16* __restrict_
     const int first_slot = item.slot - item.chunk;
     {
       float* pp = rs.partials + (slot0 + item.slot) * PER_SLOT;
+      const __amdgpu_buffer_rsrc_t pr = dev_rsrc(pp, PER_SLOT);
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) st_dev(pp + ((wave * ND + db) * 16 + e) * 64 + lane, o[db][e]);
+      for (int db = 0; db < ND; ++db) st16_dev(pr, (wave * ND + db) * 1024, lane, o[db]);
       st_dev(pp + BQ * D + tid, m);
       st_dev(pp + BQ * D + 256 + tid, l);
     }
@@ -218,13 +217,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const u16* __restrict_
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[db][e] = 0.0f;
     for (int c = 0; c < item.nchunks; ++c) {
-      const float* pp = rs.partials + (slot0 + first_slot + c) * PER_SLOT;
+      float* pp = rs.partials + (slot0 + first_slot + c) * PER_SLOT;
+      const __amdgpu_buffer_rsrc_t pr = dev_rsrc(pp, PER_SLOT);
       const float f = exp2f(ld_dev(pp + BQ * D + tid) - ms);
       l += f * ld_dev(pp + BQ * D + 256 + tid);
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
+      for (int db = 0; db < ND; ++db) {
+        float x[16];
+        ld16_dev(pr, (wave * ND + db) * 1024, lane, x);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[db][e] += f * ld_dev(pp + ((wave * ND + db) * 16 + e) * 64 + lane);
+        for (int e = 0; e < 16; ++e) o[db][e] += f * x[e];
+      }
     }
     m = mm;
   }

@@ -451,14 +451,40 @@ __device__ __forceinline__ int epi_region(const Epilogue& e, int r0, int cb) {
   }
 }
 
-// fp32 store and load at device (agent) scope: coherent across the XCDs, whose
-// L2s are not, without writing back or invalidating a whole L2 as a fence
-// would.  Used for the partial sums of split tiles.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// The fp32 partial sums of split tiles, stored and loaded at device (agent)
+// scope: coherent across the XCDs, whose L2s are not, without writing back or
+// invalidating a whole L2 as a fence would.  The cache policy is the one the
+// compiler gives relaxed agent-scope atomics (sc1), here on 16-byte buffer
+// accesses: a lane's 16 values of a 32 x 32 block sit as four float4 at
+// [quad][lane], so one access of a quad covers 1 KB contiguous.  Offsets are
+// bytes into the partial area (kGemmPartialBytes < 2^31).
+constexpr int kCoherentPolicy = 16;  // sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* partials) {
+  return __builtin_amdgcn_make_buffer_rsrc(partials, static_cast<short>(0),
+                                           static_cast<int>(kGemmPartialBytes), 0x00020000);
 }
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store_part16(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                             const float* v) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const v4u d = {__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
+                   __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])};
+    __builtin_amdgcn_raw_buffer_store_b128(d, r, static_cast<int>(off + 1024 * q), 0,
+                                           kCoherentPolicy);
+  }
+}
+__device__ __forceinline__ void load_part16(__amdgpu_buffer_rsrc_t r, uint32_t off, float* v) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const v4u d =
+        __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off + 1024 * q), 0, kCoherentPolicy);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[4 * q + e] = __uint_as_float(d[e]);
+  }
+}
+// Byte offset of a lane's values of block `blk` (of 64 in a tile) in slot `slot`.
+__device__ __forceinline__ uint32_t part_offset(int slot, int blk, int lane) {
+  return static_cast<uint32_t>(slot) * (PARTIAL_FLOATS * 4) + blk * 4096 + lane * 16;
 }
 
 // Scheduling groups (instruction classes for __builtin_amdgcn_sched_group_barrier).
@@ -596,6 +622,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
   int item = v;
   Item s = decode_item(pl, item);
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_address(ring));
+  const __amdgpu_buffer_rsrc_t prs = partial_rsrc(pl.partials);
 
   auto setup = [&](const Item& sg) {
     const GemmProblem& P = pl.p[sg.prob];
@@ -771,7 +798,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
     //     phase 1 with all the partials;
     //   phase 1: the epilogue, on the sum of the tile's partials (in a fixed
     //     order, so the result does not depend on the order of arrival).
-    // Partial slot layout: [wave][i][j][16 values][64 lanes] fp32.
+    // Partial slot layout: block (wave, i, j) of 4 KB, [quad][lane][4] fp32.
     {
       const GemmProblem& P = pl.p[s.prob];
       const Epilogue& e = P.epi;
@@ -803,24 +830,28 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_sk_kernel(SkPlan pl) {
               vals[4 * t] = x.x; vals[4 * t + 1] = x.y; vals[4 * t + 2] = x.z; vals[4 * t + 3] = x.w;
             }
             __builtin_amdgcn_wave_barrier();
-            // this lane's 16 values of the block, element t at [t][lane]:
-            // each store or load of one t covers 256 contiguous bytes
-            const size_t boff = static_cast<size_t>(((wave * FM + i) * FN + j) * 1024 + lane);
+            // this lane's 16 values of the block (see store_part16)
+            const int blk = (wave * FM + i) * FN + j;
             if (phase == 0) {
-              float* pw = pl.partials + static_cast<size_t>(my_slot) * PARTIAL_FLOATS + boff;
-#pragma unroll
-              for (int t = 0; t < 16; ++t) store_coherent(pw + t * 64, vals[t]);
+              store_part16(prs, part_offset(my_slot, blk, lane), vals);
             } else {
               if (summed) {
+                // every piece's partial in the tile's fixed order; this
+                // piece's own values are still at hand (the bits it stored)
+                float own[16];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) own[t] = vals[t];
                 bool first = true;
                 for_each_part(pl, s.prob, s.tile, [&](int part) {
-                  const float* pr =
-                      pl.partials + static_cast<size_t>(part_slot(pl, part)) * PARTIAL_FLOATS + boff;
+                  float x[16];
+                  if (part == item) {
 #pragma unroll
-                  for (int t = 0; t < 16; ++t) {
-                    const float x = load_coherent(pr + t * 64);
-                    vals[t] = first ? x : vals[t] + x;
+                    for (int t = 0; t < 16; ++t) x[t] = own[t];
+                  } else {
+                    load_part16(prs, part_offset(part_slot(pl, part), blk, lane), x);
                   }
+#pragma unroll
+                  for (int t = 0; t < 16; ++t) vals[t] = first ? x[t] : vals[t] + x[t];
                   first = false;
                 });
               }
@@ -930,6 +961,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel4(SkPlan pl) {
   Item s = decode_item(pl, item);
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_address(ring));
   const uint32_t sring_lds = __builtin_amdgcn_readfirstlane(lds_address(sring));
+  const __amdgpu_buffer_rsrc_t prs = partial_rsrc(pl.partials);
   const int sop = __builtin_amdgcn_readfirstlane(wave) & 1;  // MX: scale words staged by this wave
   const i32x4 sdesc = sop ? make_desc(reinterpret_cast<const u16*>(pl.scale_b), pl.scale_bytes_b)
                           : make_desc(reinterpret_cast<const u16*>(pl.scale_a), pl.scale_bytes_a);
@@ -1184,7 +1216,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel4(SkPlan pl) {
     //     phase 1 with all the partials;
     //   phase 1: the epilogue, on the sum of the tile's partials (in a fixed
     //     order, so the result does not depend on the order of arrival).
-    // Partial slot layout: [wave][i][j][16 values][64 lanes] fp32.
+    // Partial slot layout: block (wave, i, j) of 4 KB, [quad][lane][4] fp32.
     {
       const GemmProblem& P = pl.p[s.prob];
       const Epilogue& e = P.epi;
@@ -1215,24 +1247,28 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel4(SkPlan pl) {
               vals[4 * t] = x.x; vals[4 * t + 1] = x.y; vals[4 * t + 2] = x.z; vals[4 * t + 3] = x.w;
             }
             __builtin_amdgcn_wave_barrier();
-            // this lane's 16 values of the block, element t at [t][lane]:
-            // each store or load of one t covers 256 contiguous bytes
-            const size_t boff = static_cast<size_t>(((wave * FM + i) * FN + j) * 1024 + lane);
+            // this lane's 16 values of the block (see store_part16)
+            const int blk = (wave * FM + i) * FN + j;
             if (phase == 0) {
-              float* pw = pl.partials + static_cast<size_t>(my_slot) * PARTIAL_FLOATS + boff;
-#pragma unroll
-              for (int t = 0; t < 16; ++t) store_coherent(pw + t * 64, vals[t]);
+              store_part16(prs, part_offset(my_slot, blk, lane), vals);
             } else {
               if (summed) {
+                // every piece's partial in the tile's fixed order; this
+                // piece's own values are still at hand (the bits it stored)
+                float own[16];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) own[t] = vals[t];
                 bool first = true;
                 for_each_part(pl, s.prob, s.tile, [&](int part) {
-                  const float* pr =
-                      pl.partials + static_cast<size_t>(part_slot(pl, part)) * PARTIAL_FLOATS + boff;
+                  float x[16];
+                  if (part == item) {
 #pragma unroll
-                  for (int t = 0; t < 16; ++t) {
-                    const float x = load_coherent(pr + t * 64);
-                    vals[t] = first ? x : vals[t] + x;
+                    for (int t = 0; t < 16; ++t) x[t] = own[t];
+                  } else {
+                    load_part16(prs, part_offset(part_slot(pl, part), blk, lane), x);
                   }
+#pragma unroll
+                  for (int t = 0; t < 16; ++t) vals[t] = first ? x[t] : vals[t] + x[t];
                   first = false;
                 });
               }
@@ -1381,10 +1417,22 @@ hipError_t build_plan(const GemmProblem* probs, int nprob, Major a_major, Major 
     if (t1 > 0) item_len = min(item_len, pl.iters[1] / pl.pieces[1]);
     long st = 1;
     if (rem > 0) {
-      st = tail_split > 0 ? tail_split : G / rem;
-      st = std::min<long>(st, std::max(1, item_len / 16));
-      st = std::min<long>(st, item_len);
-      st = std::max<long>(st, 1);
+      const long max_st = std::max<long>(1, std::min<long>(item_len / 16, kGemmPartialSlots / rem));
+      if (tail_split > 0) {
+        st = std::min<long>(tail_split, std::max(1, item_len / 16));
+      } else {
+        // pieces per tile of the last round: the least time on the busiest
+        // workgroup, ceil(rem st / G) pieces of ceil(len / st) k-steps each
+        // plus, for a split tile, about 4 + 4 st k-steps of writing and
+        // summing fp32 partials per piece (measured: 336-tile and 384-tile
+        // products at the 175B share, 3 and 2 pieces)
+        long best = -1;
+        for (long c = 1; c <= max_st; ++c) {
+          const long t = (rem * c + G - 1) / G * ((item_len + c - 1) / c + (c > 1 ? 4 + 4 * c : 0));
+          if (best < 0 || t < best) { best = t; st = c; }
+        }
+      }
+      st = std::max<long>(std::min<long>(st, item_len), 1);
     }
     const long nitems = full + rem * st;
     const bool base_split = pl.pieces[0] > 1 || pl.pieces[1] > 1;
