@@ -6,10 +6,10 @@ benchmark's CPU-baseline leg may import or run this module; it shares no code
 with the HIP path, which implements the same published generator on its own.
 
 Page followed: [MS] Zhongzhu Zhou, "MegaScale: ByteDance 如何在 12,288 块 GPU 上
-实现 55% MFU 的大规模 LLM 训练", section 1.3: MegaScale fuses dropout with the
-norm ("融合 RMSNorm + Dropout"), and selective recompute keeps the activations
-of the cheap operators, dropout's among them.  The page names neither the
-generator nor where the dropout sits; the readings taken:
+实现 55% MFU 的大规模 LLM 训练", section 1.3: MegaScale fuses dropout into its
+normalisation kernel, and selective recompute keeps the activations of the
+cheap operators, dropout's among them.  The page names neither the generator
+nor where the dropout sits; the readings taken:
 
 * where: on the block's branch output, before the residual add.  Parallel
   block (eq (4)): y = x + M * (Attn(LN x) W_o + MLP(LN x)), one mask over
