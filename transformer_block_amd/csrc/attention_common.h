@@ -18,11 +18,22 @@ constexpr int BKV = 64;   // keys per LDS tile (forward, dQ)
 constexpr int BKB = 128;  // keys per workgroup (dK/dV): 4 waves x 32
 constexpr int BQB = 64;   // queries per LDS tile (dK/dV)
 
-// Rows of D bf16 in LDS, addressed in 16-byte chunks, XOR-swizzled.
+// Rows of D bf16 in LDS, addressed in 16-byte chunks: chunk c of row r sits
+// at chunk slot c ^ rowswz<D>(r).  The LDS serves 64 banks of 4 bytes; a
+// 16-byte read is served 16 lanes at a time, an 8-byte read (plain or
+// transposing) 32 lanes at a time.  The swizzle keeps both fragment reads
+// below free of bank conflicts:
+//   D = 128 (256-byte rows, each spanning every bank): the two 2-bit fields
+//     of r & 15 trade places, so 16 aligned consecutive rows read at one
+//     chunk take 16 distinct slots, and the 4 aligned rows x 4 aligned chunks
+//     of 32 lanes of a transposing read take 4 distinct groups of 4 slots;
+//   D = 64 (128-byte rows, the row's parity picking half of the banks): rows
+//     of one parity among 16 aligned rows take 8 distinct slots, and rows
+//     4a + p and 4a + 2 + p take different halves of the row.
 template <int D>
 __device__ __forceinline__ int rowswz(int r) {
-  if constexpr (D == 128) return swz256(r);
-  else return swz128(r);
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 template <int D>
 __device__ __forceinline__ u16* row_chunk(u16* base, int r, int c) {
@@ -65,18 +76,6 @@ __device__ __forceinline__ bf16x8 frag_rows_tr(const u16* tile, int rb, int ks, 
   return as_bf16x8(u);
 }
 
-// Transposed tiles: D rows of 64 bf16, addressed in 8-byte slots of 4.
-__device__ __forceinline__ uint2 tslot(const u16* base, int r, int slot) {
-  return *reinterpret_cast<const uint2*>(base + r * 64 + ((slot ^ swz8b(r)) << 2));
-}
-// A operand "X^T[d][k]" for k = 4g..4g+3 and 8+4g..8+4g+3 inside a 16-step
-// starting at tile column k0.
-__device__ __forceinline__ bf16x8 tfrag(const u16* base, int r, int k0, int g) {
-  const uint2 lo = tslot(base, r, (k0 >> 2) + g);
-  const uint2 hi = tslot(base, r, (k0 >> 2) + 2 + g);
-  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
-
 // Eight accumulator values as fp16 (round to nearest even, no saturation:
 // the attention's dS values stay far inside the fp16 range).
 __device__ __forceinline__ uint32_t pack2h_pk(float lo, float hi) {
@@ -93,56 +92,6 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& a, int base) {
   return as_bf16x8(make_uint4(pack2bf_pk(a[base + 0], a[base + 1]), pack2bf_pk(a[base + 2], a[base + 3]),
                               pack2bf_pk(a[base + 4], a[base + 5]), pack2bf_pk(a[base + 6], a[base + 7])));
 }
-
-// A 64 x D tile of a row-major matrix (row stride ld) held in registers:
-// thread t owns rows 4*kg .. 4*kg+3 and the 8 columns of chunk dc.
-template <int D>
-struct Tile64 {
-  static constexpr int DC = D / 8;          // chunks per row
-  static constexpr int ACTIVE = 16 * DC;    // threads holding data
-  uint4 v[4];
-
-  __device__ __forceinline__ void load(const u16* g, int ld, int row0, int nrows, int tid) {
-    const int dc = tid % DC, kg = tid / DC;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int r = row0 + kg * 4 + kk;
-      v[kk] = make_uint4(0u, 0u, 0u, 0u);
-      if (tid < ACTIVE && r < nrows)
-        v[kk] = *reinterpret_cast<const uint4*>(g + r * ld + dc * 8);
-    }
-  }
-  __device__ __forceinline__ void store_rows(u16* lds, int tid) const {
-    if (tid >= ACTIVE) return;
-    const int dc = tid % DC, kg = tid / DC;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) *reinterpret_cast<uint4*>(row_chunk<D>(lds, kg * 4 + kk, dc)) = v[kk];
-  }
-  // Writes the transpose: LDS row d (= column of the tile) holds 64 values.
-  __device__ __forceinline__ void store_transposed(u16* lds, int tid) const {
-    if (tid >= ACTIVE) return;
-    const int dc = tid % DC, kg = tid / DC;
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&v[0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&v[1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&v[2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&v[3]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d = dc * 8 + j;
-      const int wi = j >> 1;
-      uint32_t a0, a1;
-      if (j & 1) {
-        a0 = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
-        a1 = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
-      } else {
-        a0 = (w0[wi] & 0xffffu) | (w1[wi] << 16);
-        a1 = (w2[wi] & 0xffffu) | (w3[wi] << 16);
-      }
-      *reinterpret_cast<uint2*>(lds + d * 64 + ((kg ^ swz8b(d)) << 2)) = make_uint2(a0, a1);
-    }
-  }
-};
-
 
 // ------------------------------------------------- DMA-staged tiles
 // A tile of R rows (keys or queries) x D columns goes from HBM to LDS by DMA

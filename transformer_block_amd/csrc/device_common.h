@@ -206,22 +206,6 @@ __device__ __forceinline__ float silu_grad_f(float u) {
   return sg + u * sg * (1.0f - sg);
 }
 
-// LDS swizzle for tiles stored as rows of 64 bf16 (128 bytes = 8 chunks of
-// 16 bytes): chunk c of row r lives at chunk slot c ^ swz128(r).  Rows r..r+7
-// (and r..r+15 counting the row parity) read at one logical chunk land in
-// distinct banks, and so do rows r, r+8, r+16, ... written at one chunk.
-__device__ __forceinline__ int swz128(int r) { return (r ^ (r >> 3)) & 7; }
-
-// Swizzle for rows of 64 bf16 addressed in 8-byte slots (16 slots per row).
-__device__ __forceinline__ int swz8b(int r) { return (r ^ (r >> 4)) & 15; }
-
-// Swizzle for rows of 128 bf16 (256 bytes = 16 chunks of 16 bytes): chunk c
-// of row r at slot c ^ swz256(r).  Conflict-free for 16-byte row reads (8 or
-// 16 consecutive rows at one chunk) and for the transposing 8-byte reads of
-// two adjacent chunks in 4 rows (every 16-lane group of ds_read_b64_tr_b16,
-// rows in perm16 order).
-__device__ __forceinline__ int swz256(int r) { return ((2 * (r & 7)) ^ ((r >> 3) & 1)) & 15; }
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
