@@ -96,7 +96,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int hd = blockIdx.y, bi = blockIdx.z;
+  const RowBlock rb = row_block(rsp, n);
+  const int hd = rb.hd, bi = rb.bi;
   const int hl = n * D, ld = 3 * hl;
   const u16* Qh = qk16 + static_cast<size_t>(bi) * s * (2 * hl) + hd * D;  // fp16
   const u16* Kh = Qh + hl;
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const u16* dOg = dcg + static_cast<size_t>(bi) * s * hl + hd * D;
   const float* lse_h = lse + (static_cast<size_t>(bi) * n + hd) * s;
   const float* dl_h = delta + (static_cast<size_t>(bi) * n + hd) * s;
-  const RowItem item = decode_row_item<false>(static_cast<int>(blockIdx.x), nkt, s, window, rsp.ch);
+  const RowItem item = decode_row_item<false>(rb.item, nkt, s, window, rsp.ch);
   if (item.nchunks == 0) return;
   const int kb0 = item.row * BKB, kw0 = kb0 + wave * 32, kj = kw0 + l32;
 
@@ -332,10 +333,11 @@ __global__ __launch_bounds__(256, BKQ == 32 ? 2 : 1) void attn_bwd_dq_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const RowItem item = decode_row_item<true>(static_cast<int>(blockIdx.x), nqt, s, window, rsp.ch);
+  const RowBlock rb = row_block(rsp, n);
+  const RowItem item = decode_row_item<true>(rb.item, nqt, s, window, rsp.ch);
   if (item.nchunks == 0) return;
   const int qt = item.row;
-  const int hd = blockIdx.y, bi = blockIdx.z;
+  const int hd = rb.hd, bi = rb.bi;
   const int hl = n * D, ld = 3 * hl;
   const u16* Qh = qk16 + static_cast<size_t>(bi) * s * (2 * hl) + hd * D;  // fp16
   const u16* Kh = Qh + hl;
@@ -515,18 +517,20 @@ hipError_t bwd_d(const u16* qkv, const u16* qk16, const u16* c, const float* lse
   const int nkt = (s + BKB - 1) / BKB;
   RowSplit rk;
   int kitems = 0;
-  e = plan_rows<false>(b, s, n, window, nkt, 2 * BKB * D, sc, &rk, &kitems);
+  e = plan_rows<false>(b, s, n, window, nkt, 2 * BKB * D, launch_slots(attn_bwd_dkdv_kernel<D>, sc),
+                       sc, &rk, &kitems);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(kitems, n, b), dim3(256), 0, st, qkv, qk16,
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(kitems * rk.nb), dim3(256), 0, st, qkv, qk16,
                      dc, lse, delta, dz, ld_dz, s, n, window, nkt, rk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqt = (s + BQ - 1) / BQ;
   RowSplit rq;
   int qitems = 0;
-  e = plan_rows<true>(b, s, n, window, nqt, BQ * D, sc, &rq, &qitems);
+  e = plan_rows<true>(b, s, n, window, nqt, BQ * D, launch_slots(attn_bwd_dq_kernel<D>, sc), sc,
+                      &rq, &qitems);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(qitems, n, b), dim3(256), 0, st, qkv, qk16, dc,
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(qitems * rq.nb), dim3(256), 0, st, qkv, qk16, dc,
                      lse, delta, dz, ld_dz, s, n, window, nqt, rq);
   return hipGetLastError();
 }

@@ -6,6 +6,11 @@
 
 #include <math.h>
 
+#include <algorithm>
+#include <functional>
+#include <queue>
+#include <vector>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -262,43 +267,151 @@ struct RowSplit {
   int* counters;    // one per (batch, head, row): zero on entry, left zero
   int ch;           // tiles per chunk
   int split_slots;  // partial slots per (batch, head)
+  int nb;           // batches x heads
 };
 
-// Chunk length for the rows of one launch: enough items for about two per
-// CU, whole rows when that already holds, and the partials of the split rows
-// within the scratch (chunks grow until they fit).
+// The item, head and batch of this workgroup.  The grid is one-dimensional,
+// (batch, head) fastest and then the item, so that the hardware, which hands
+// out workgroups in index order, starts every head's longest items before any
+// head's shorter ones (items are numbered longest first within a head).
+struct RowBlock {
+  int item, hd, bi;
+};
+__device__ __forceinline__ RowBlock row_block(const RowSplit& rs, int n) {
+  const int x = static_cast<int>(blockIdx.x);
+  const int hb = x % rs.nb;
+  RowBlock r;
+  r.item = x / rs.nb;
+  r.hd = hb % n;
+  r.bi = hb / n;
+  return r;
+}
+
+// Chunk length for the rows of one launch, chosen on a model of the
+// dispatch.  The hardware hands out workgroups in grid order (row_block) to
+// `slots` places at a time (workgroups per CU x CUs), each to the first place
+// that frees up.  An item costs its 64-wide tiles plus a fixed start (loading
+// its own rows, filling the ring); a chunk of a split row also stores its
+// partial, and the last chunk of a row merges them.  The candidates are the
+// lengths at which the longest row's chunk count changes; the one with the
+// earliest simulated finish wins (the longer on ties: fewer partials), among
+// those whose partials fit the scratch.  The choice is kept per thread for
+// the last shape asked (the simulation is the costly part).
+struct RowPlanKey {
+  int b, s, n, window, nrows, per_slot, slots, max_counters;
+  size_t partial_floats;
+  bool operator==(const RowPlanKey& o) const {
+    return b == o.b && s == o.s && n == o.n && window == o.window && nrows == o.nrows &&
+           per_slot == o.per_slot && slots == o.slots && max_counters == o.max_counters &&
+           partial_floats == o.partial_floats;
+  }
+};
+
+// Places for workgroups of `kernel` (256 threads) on the device: workgroups
+// per CU as the compiler's resource use allows, times the CUs.
+template <typename K>
+int launch_slots(K kernel, const AttnScratch& sc) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  return per_cu * (sc.cus > 0 ? sc.cus : 256);
+}
+
 template <bool QUERY_ROWS>
-hipError_t plan_rows(int b, int s, int n, int window, int nrows, int per_slot,
+hipError_t plan_rows(int b, int s, int n, int window, int nrows, int per_slot, int slots,
                      const AttnScratch& sc, RowSplit* rs, int* items_per_head) {
-  long total = 0;
-  for (int r = 0; r < nrows; ++r)
-    total += row_tiles(QUERY_ROWS ? query_row(r, s, window) : key_row(r, s, window));
-  total *= static_cast<long>(b) * n;
-  const long target = 2L * (sc.cus > 0 ? sc.cus : 256);
-  long ch = (total + target - 1) / target;
-  if (ch < 4) ch = 4;
-  if (ch > (1 << 20)) ch = 1 << 20;
-  for (;;) {
+  const long nb = static_cast<long>(b) * n;
+  if (nb <= 0 || nrows <= 0 || slots <= 0) return hipErrorInvalidValue;
+  // rows in item order (decode_row_item): longest first
+  std::vector<int> tiles(nrows);
+  int tmax = 1;
+  for (int i = 0; i < nrows; ++i) {
+    const int row = QUERY_ROWS ? nrows - 1 - i : i;
+    tiles[i] = row_tiles(QUERY_ROWS ? query_row(row, s, window) : key_row(row, s, window));
+    tmax = std::max(tmax, tiles[i]);
+  }
+  auto chunks = [](int nt, long ch) { return nt <= 0 ? 1L : (nt + ch - 1) / ch; };
+  auto fits = [&](long ch, long* items_out) {
     long items = 0, split = 0;
-    for (int r = 0; r < nrows; ++r) {
-      const int nc = row_chunks(QUERY_ROWS ? query_row(r, s, window) : key_row(r, s, window),
-                                static_cast<int>(ch));
+    for (int nt : tiles) {
+      const long nc = chunks(nt, ch);
       items += nc;
       if (nc > 1) split += nc;
     }
-    const long need = split * b * n * per_slot;
-    if ((split == 0 || (need <= static_cast<long>(sc.partial_floats) &&
-                        static_cast<long>(b) * n * nrows <= sc.max_counters)) &&
-        items < (1L << 30)) {
-      rs->partials = sc.partials;
-      rs->counters = sc.counters;
-      rs->ch = static_cast<int>(ch);
-      rs->split_slots = static_cast<int>(split);
-      *items_per_head = static_cast<int>(items);
-      return hipSuccess;
+    *items_out = items;
+    return (split == 0 || (split * nb * per_slot <= static_cast<long>(sc.partial_floats) &&
+                           nb * nrows <= sc.max_counters)) &&
+           items * nb < (1L << 31);
+  };
+  // partial store and merge, in tiles, scaled from the forward's measured
+  // costs (64 KB partials: 0.7 and 0.4 per chunk)
+  const double pscale = per_slot / (128.0 * 128.0 + 512.0);
+  auto finish = [&](long ch) {
+    std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+    double end = 0.0;
+    for (int i = 0; i < nrows; ++i) {
+      const long nc = chunks(tiles[i], ch);
+      for (long x = 0; x < nc; ++x) {
+        const long t = std::min<long>(ch, tiles[i] - x * ch);
+        double cost = 2.3 + static_cast<double>(std::max<long>(t, 0));
+        if (nc > 1) cost += 0.7 * pscale + (x == nc - 1 ? 0.4 * pscale * nc : 0.0);
+        for (long h = 0; h < nb; ++h) {
+          double t0 = 0.0;
+          if (static_cast<long>(free_at.size()) >= slots) {
+            t0 = free_at.top();
+            free_at.pop();
+          }
+          free_at.push(t0 + cost);
+          end = std::max(end, t0 + cost);
+        }
+      }
     }
-    ch *= 2;  // fewer, longer chunks
+    return end;
+  };
+  const RowPlanKey key{b, s, n, window, nrows, per_slot, slots, sc.max_counters, sc.partial_floats};
+  thread_local RowPlanKey last_key{};
+  thread_local long last_ch = 0;
+  long best = 0;
+  if (last_ch > 0 && last_key == key) {
+    best = last_ch;
+  } else {
+    double best_t = 0.0;
+    long prev = -1, items = 0;
+    for (int k = 1; k <= tmax && k <= 64; ++k) {
+      const long ch = (tmax + k - 1) / k;
+      if (ch == prev) continue;
+      prev = ch;
+      if (!fits(ch, &items)) continue;
+      // beyond this many workgroups the simulation costs more than it saves
+      if (items * nb > 200000 && best > 0) break;
+      const double t = finish(ch);
+      if (best == 0 || t < best_t - 1e-9) {
+        best = ch;
+        best_t = t;
+      }
+    }
+    // nothing fits: chunks grow until the partials do
+    for (long ch = tmax; best == 0; ch *= 2) {
+      if (fits(ch, &items)) best = ch;
+      if (ch > (1L << 20)) return hipErrorInvalidValue;
+    }
+    last_key = key;
+    last_ch = best;
   }
+  long items = 0, split = 0;
+  for (int nt : tiles) {
+    const long nc = chunks(nt, best);
+    items += nc;
+    if (nc > 1) split += nc;
+  }
+  rs->partials = sc.partials;
+  rs->counters = sc.counters;
+  rs->ch = static_cast<int>(best);
+  rs->split_slots = static_cast<int>(split);
+  rs->nb = static_cast<int>(nb);
+  *items_per_head = static_cast<int>(items);
+  return hipSuccess;
 }
 
 }  // namespace

@@ -35,10 +35,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const u16* __restrict_
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const RowItem item = decode_row_item<true>(static_cast<int>(blockIdx.x), nqt, s, window, rs.ch);
+  const RowBlock rb = row_block(rs, n);
+  const RowItem item = decode_row_item<true>(rb.item, nqt, s, window, rs.ch);
   if (item.nchunks == 0) return;
   const int qt = item.row;
-  const int hd = blockIdx.y, bi = blockIdx.z;
+  const int hd = rb.hd, bi = rb.bi;
   const int hl = n * D, ld = 3 * hl;
   const u16* Qh = qk16 + static_cast<size_t>(bi) * s * (2 * hl) + hd * D;  // fp16
   const u16* Kh = Qh + hl;
@@ -255,9 +256,10 @@ hipError_t fwd_d(const u16* qkv, const u16* qk16, u16* c, float* lse, int b, int
   const int nqt = (s + BQ - 1) / BQ;
   RowSplit rs;
   int items = 0;
-  const hipError_t e = plan_rows<true>(b, s, n, window, nqt, BQ * D + 2 * 256, sc, &rs, &items);
+  const hipError_t e = plan_rows<true>(b, s, n, window, nqt, BQ * D + 2 * 256,
+                                       launch_slots(attn_fwd_kernel<D>, sc), sc, &rs, &items);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(items, n, b), dim3(256), 0, st, qkv, qk16, c, lse,
+  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(items * rs.nb), dim3(256), 0, st, qkv, qk16, c, lse,
                      s, n, window, nqt, rs);
   return hipGetLastError();
 }
