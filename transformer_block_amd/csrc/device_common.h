@@ -169,9 +169,11 @@ __device__ __forceinline__ float inv_scale(float amax, float fmax) {
 // Mathematical Functions, formula 7.1.26 (|error| <= 1.5e-7 for all x):
 //   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
 //   t = 1 / (1 + p x), x >= 0, and erf(-x) = -erf(x).
-// Inline straight-line code: a library call here would force every live
-// accumulator of the GEMM epilogue to be saved around it.
-__device__ __forceinline__ float erf_as(float x) {
+// erf_as_e takes e = exp(-x^2) from the caller (GeLU's derivative shares it
+// with the normal density).  Inline straight-line code: a library call here
+// would force every live accumulator of the GEMM epilogue to be saved around
+// it.
+__device__ __forceinline__ float erf_as_e(float x, float e) {
   const float ax = fabsf(x);
   const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
   float poly = 1.061405429f;
@@ -180,9 +182,9 @@ __device__ __forceinline__ float erf_as(float x) {
   poly = poly * t - 0.284496736f;
   poly = poly * t + 0.254829592f;
   poly *= t;
-  const float r = 1.0f - poly * __expf(-ax * ax);
-  return copysignf(r, x);
+  return copysignf(1.0f - poly * e, x);
 }
+__device__ __forceinline__ float erf_as(float x) { return erf_as_e(x, __expf(-x * x)); }
 
 // Exact GeLU u * Phi(u) and its derivative Phi(u) + u * phi(u), with
 // Phi(u) = (1 + erf(u / sqrt 2)) / 2 and phi(u) = exp(-u^2 / 2) / sqrt(2 pi).
@@ -190,9 +192,9 @@ __device__ __forceinline__ float gelu_f(float u) {
   return 0.5f * u * (1.0f + erf_as(u * 0.70710678118654752f));
 }
 __device__ __forceinline__ float gelu_grad_f(float u) {
-  const float cdf = 0.5f * (1.0f + erf_as(u * 0.70710678118654752f));
-  const float pdf = 0.39894228040143268f * __expf(-0.5f * u * u);
-  return cdf + u * pdf;
+  const float e = __expf(-0.5f * u * u);  // exp(-x^2) at x = u / sqrt 2
+  const float cdf = 0.5f * (1.0f + erf_as_e(u * 0.70710678118654752f, e));
+  return cdf + u * (0.39894228040143268f * e);
 }
 
 // SiLU u * sigmoid(u) and its derivative s + u s (1 - s), s = sigmoid(u)
