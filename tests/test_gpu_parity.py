@@ -53,6 +53,10 @@ EDGE_CASES = [
     ("widest_rows_h16384_rmsnorm", W("h16kr", 1, 300, 16384, 1, 128, 256, 64, seed=31,
                                      norm="rmsnorm"), True),
     ("rows_h12288_s300", W("h12k", 1, 300, 12288, 1, 128, 256, 64, seed=32), True),
+    # attention's dispatch: more (batch, head) pairs (576) than workgroup places,
+    # and one head whose 32 long causal rows are cut into many chunks
+    ("many_heads_b9_n64_d64", W("mh", 9, 130, 4096, 64, 64, 256, 1000, seed=33), False),
+    ("long_rows_s4096_one_head", W("lr", 1, 4096, 128, 1, 128, 256, 4096, seed=34), False),
 ]
 
 
