@@ -295,16 +295,24 @@ __device__ __forceinline__ RowBlock row_block(const RowSplit& rs, int n) {
 // partial, and the last chunk of a row merges them.  The candidates are the
 // lengths at which the longest row's chunk count changes; the one with the
 // earliest simulated finish wins (the longer on ties: fewer partials), among
-// those whose partials fit the scratch.  The choice is kept per thread for
-// the last shape asked (the simulation is the costly part).
+// those whose partials fit the scratch.  `tile_cost` scales every cost (a
+// kernel build whose tiles take longer), `finish` receives the simulated
+// finish in those units.  The choice is kept per thread for the last few
+// shapes asked (the simulation is the costly part).
 struct RowPlanKey {
   int b, s, n, window, nrows, per_slot, slots, max_counters;
   size_t partial_floats;
+  double tile_cost;
   bool operator==(const RowPlanKey& o) const {
     return b == o.b && s == o.s && n == o.n && window == o.window && nrows == o.nrows &&
            per_slot == o.per_slot && slots == o.slots && max_counters == o.max_counters &&
-           partial_floats == o.partial_floats;
+           partial_floats == o.partial_floats && tile_cost == o.tile_cost;
   }
+};
+struct RowPlanEntry {
+  RowPlanKey key;
+  long ch;
+  double finish;
 };
 
 // Places for workgroups of `kernel` (256 threads) on the device: workgroups
@@ -320,7 +328,8 @@ int launch_slots(K kernel, const AttnScratch& sc) {
 
 template <bool QUERY_ROWS>
 hipError_t plan_rows(int b, int s, int n, int window, int nrows, int per_slot, int slots,
-                     const AttnScratch& sc, RowSplit* rs, int* items_per_head) {
+                     const AttnScratch& sc, RowSplit* rs, int* items_per_head,
+                     double tile_cost = 1.0, double* finish = nullptr) {
   const long nb = static_cast<long>(b) * n;
   if (nb <= 0 || nrows <= 0 || slots <= 0) return hipErrorInvalidValue;
   // rows in item order (decode_row_item): longest first
@@ -347,7 +356,7 @@ hipError_t plan_rows(int b, int s, int n, int window, int nrows, int per_slot, i
   // partial store and merge, in tiles, scaled from the forward's measured
   // costs (64 KB partials: 0.7 and 0.4 per chunk)
   const double pscale = per_slot / (128.0 * 128.0 + 512.0);
-  auto finish = [&](long ch) {
+  auto simulate = [&](long ch) {
     std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
     double end = 0.0;
     for (int i = 0; i < nrows; ++i) {
@@ -356,6 +365,7 @@ hipError_t plan_rows(int b, int s, int n, int window, int nrows, int per_slot, i
         const long t = std::min<long>(ch, tiles[i] - x * ch);
         double cost = 2.3 + static_cast<double>(std::max<long>(t, 0));
         if (nc > 1) cost += 0.7 * pscale + (x == nc - 1 ? 0.4 * pscale * nc : 0.0);
+        cost *= tile_cost;
         for (long h = 0; h < nb; ++h) {
           double t0 = 0.0;
           if (static_cast<long>(free_at.size()) >= slots) {
@@ -369,14 +379,20 @@ hipError_t plan_rows(int b, int s, int n, int window, int nrows, int per_slot, i
     }
     return end;
   };
-  const RowPlanKey key{b, s, n, window, nrows, per_slot, slots, sc.max_counters, sc.partial_floats};
-  thread_local RowPlanKey last_key{};
-  thread_local long last_ch = 0;
+  const RowPlanKey key{b,  s, n, window, nrows, per_slot, slots, sc.max_counters, sc.partial_floats,
+                       tile_cost};
+  constexpr int kCache = 4;
+  thread_local RowPlanEntry cache[kCache] = {};
+  thread_local int next_slot = 0;
   long best = 0;
-  if (last_ch > 0 && last_key == key) {
-    best = last_ch;
+  double best_t = 0.0;
+  const RowPlanEntry* hit = nullptr;
+  for (const RowPlanEntry& c : cache)
+    if (c.ch > 0 && c.key == key) hit = &c;
+  if (hit != nullptr) {
+    best = hit->ch;
+    best_t = hit->finish;
   } else {
-    double best_t = 0.0;
     long prev = -1, items = 0;
     for (int k = 1; k <= tmax && k <= 64; ++k) {
       const long ch = (tmax + k - 1) / k;
@@ -385,7 +401,7 @@ hipError_t plan_rows(int b, int s, int n, int window, int nrows, int per_slot, i
       if (!fits(ch, &items)) continue;
       // beyond this many workgroups the simulation costs more than it saves
       if (items * nb > 200000 && best > 0) break;
-      const double t = finish(ch);
+      const double t = simulate(ch);
       if (best == 0 || t < best_t - 1e-9) {
         best = ch;
         best_t = t;
@@ -393,12 +409,16 @@ hipError_t plan_rows(int b, int s, int n, int window, int nrows, int per_slot, i
     }
     // nothing fits: chunks grow until the partials do
     for (long ch = tmax; best == 0; ch *= 2) {
-      if (fits(ch, &items)) best = ch;
+      if (fits(ch, &items)) {
+        best = ch;
+        best_t = simulate(ch);
+      }
       if (ch > (1L << 20)) return hipErrorInvalidValue;
     }
-    last_key = key;
-    last_ch = best;
+    cache[next_slot] = RowPlanEntry{key, best, best_t};
+    next_slot = (next_slot + 1) % kCache;
   }
+  if (finish != nullptr) *finish = best_t;
   long items = 0, split = 0;
   for (int nt : tiles) {
     const long nc = chunks(nt, best);

@@ -13,15 +13,22 @@ constexpr float kStale = 8.0f;
 
 // Keys per LDS tile and stages of the ring: 32 keys per tile, FNST stages
 // (FNST - 1 tiles in flight while one is computed; 16 KB each for D = 128),
-// two workgroups per CU, so one's softmax and barrier waits run beside the
-// other's MFMAs.  One stage of lead is not enough once each logit is a single
-// fp16 MFMA: a tile's compute is then shorter than the latency of its loads.
+// so that one workgroup's softmax and barrier waits run beside another's
+// MFMAs.  One stage of lead is not enough once each logit is a single fp16
+// MFMA: a tile's compute is then shorter than the latency of its loads.  Two
+// builds: four stages with two workgroups per CU, and three stages with
+// three (48 KB of LDS and at most 168 registers each); more workgroups per CU
+// hide more latency (+13% forward throughput on the 5120-hidden stack) but
+// make each item slower (the 175B share's few long rows: 40 -> 47 us), so
+// the launcher picks by the dispatch model (plan_rows).
 constexpr int BKF = 32;
 constexpr int KB = BKF / 32;  // 32 x 32 S^T blocks per tile
-constexpr int FNST = 4;
+// time per tile of a workgroup with three per CU, relative to two per CU
+// (measured: 1.5 x the workgroups per CU for 1.13 x the throughput)
+constexpr double kFwd3TileCost = 1.33;
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const u16* __restrict__ qkv,
+template <int D, int FNST>
+__global__ __launch_bounds__(256, FNST == 4 ? 2 : 3) void attn_fwd_kernel(const u16* __restrict__ qkv,
                                                        const u16* __restrict__ qk16,
                                                        u16* __restrict__ cout,
                                                        float* __restrict__ lse, int s, int n,
@@ -254,13 +261,22 @@ template <int D>
 hipError_t fwd_d(const u16* qkv, const u16* qk16, u16* c, float* lse, int b, int s, int n,
                  int window, const AttnScratch& sc, hipStream_t st) {
   const int nqt = (s + BQ - 1) / BQ;
-  RowSplit rs;
-  int items = 0;
-  const hipError_t e = plan_rows<true>(b, s, n, window, nqt, BQ * D + 2 * 256,
-                                       launch_slots(attn_fwd_kernel<D>, sc), sc, &rs, &items);
+  RowSplit rs2, rs3;
+  int items2 = 0, items3 = 0;
+  double t2 = 0.0, t3 = 0.0;
+  hipError_t e = plan_rows<true>(b, s, n, window, nqt, BQ * D + 2 * 256,
+                                 launch_slots(attn_fwd_kernel<D, 4>, sc), sc, &rs2, &items2, 1.0,
+                                 &t2);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(items * rs.nb), dim3(256), 0, st, qkv, qk16, c, lse,
-                     s, n, window, nqt, rs);
+  e = plan_rows<true>(b, s, n, window, nqt, BQ * D + 2 * 256, launch_slots(attn_fwd_kernel<D, 3>, sc),
+                      sc, &rs3, &items3, kFwd3TileCost, &t3);
+  if (e != hipSuccess) return e;
+  if (t3 < t2)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, 3>), dim3(items3 * rs3.nb), dim3(256), 0, st, qkv, qk16,
+                       c, lse, s, n, window, nqt, rs3);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, 4>), dim3(items2 * rs2.nb), dim3(256), 0, st, qkv, qk16,
+                       c, lse, s, n, window, nqt, rs2);
   return hipGetLastError();
 }
 
