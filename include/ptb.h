@@ -40,8 +40,10 @@
  * per-device cache of the compute-unit count (set once, with the same value,
  * by whichever call comes first) and, for the one allocation-free call
  * (ptb_lamb_step_noalloc), the per-device address of its static scratch
- * array.  Calls on different streams with different buffers (workspace
- * included) may run concurrently.  `saved` is written by ptb_forward and read by ptb_backward;
+ * array; each calling thread also keeps, in thread-local storage, the
+ * attention chunk lengths it computed for its last four shapes (the same
+ * value a fresh computation gives).  Calls on different streams with
+ * different buffers (workspace included) may run concurrently.  `saved` is written by ptb_forward and read by ptb_backward;
  * it must stay untouched in between.  `workspace` is scratch for the duration
  * of one call: its contents need no initialisation and are not kept.
  * Outputs are overwritten, never accumulated into.
