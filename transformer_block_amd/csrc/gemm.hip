@@ -218,6 +218,19 @@ struct StageLoaderP {
     for (int i = 0; i < 8; ++i)
       lds_dma16(d, lds + (wave * 8 + i) * 1024, (i & 1) ? v1 : v0, soff + i * step);
   }
+  // load i (0..7) of issue alone
+  __device__ __forceinline__ void issue_one(uint32_t lds, int wave, int k0, bool valid, int i) const {
+    const bool kseg = split_on_k && k0 >= split;
+    const int krel = kseg ? k0 - split : k0;
+    const int ld = kseg ? ldB : ldA;
+    const int row = kseg ? rowB : rowA;
+    const i32x4 d = kseg ? dB : dA;
+    const int v0 = kseg ? vB[0] : vA[0], v1 = kseg ? vB[1] : vA[1];
+    int soff = (MAJ == KMAJOR) ? (row * ld + krel) * ESZ : krel * ld * 2;
+    int step = 8 * ld * ESZ;
+    if (!valid) { soff = kOutOfRange; step = 0; }
+    lds_dma16(d, lds + (wave * 8 + i) * 1024, (i & 1) ? v1 : v0, soff + i * step);
+  }
 };
 
 // The same stage tile loaded through registers instead (global -> VGPR ->
@@ -1107,6 +1120,54 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel4(SkPlan pl) {
     if constexpr (R > FM * FN) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, R - FM * FN, 0);
   };
 
+  // FP8, after a k-step's barrier: the half-step's sixteen MFMAs (slot 1),
+  // each followed by one DMA load of the stage tile after next and one
+  // fragment read of the next half (slot 0).  A DMA issue can wait for room
+  // in the memory pipeline's queue; placed after an MFMA it waits while that
+  // MFMA runs instead of holding up the MFMAs behind it.  Two empty asm
+  // statements (they emit nothing) hold the order, being ordered with the
+  // DMA as asm with side effects: one takes the MFMA's result as an input,
+  // so the MFMA cannot sink below the DMA after it, the other claims to
+  // rewrite an operand of the next MFMA, so that one cannot rise above it.
+  auto half_dma8 = [&](const Item& sg, int slot, int j, const u16* st) {
+    if constexpr (F8) {
+      static_assert(FM * FN == 16 && 2 * (FM + FN) == 16, "one load and one read per MFMA");
+      const bool valid = j < sg.len;
+      const int k0 = (sg.kb + (valid ? j : 0)) * KSTEP;
+      const uint32_t lds = ring_lds + slot * (STAGE * 2);
+      const int k0f = koff[0], k1f = koff[1];
+      uint4 x0;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int i = t / FN, jj = t % FN;
+        if (t > 0) asm volatile("" : "+v"(gb[1][jj]));
+        if constexpr (MX)
+          acc[i][jj] = mx_step4<FA, FB>(i, jj, ga[1][i], gb[1][jj], acc[i][jj], sa8[1], sb8[1]);
+        else
+          acc[i][jj] = mfma32x32x64_f8<FA, FB>(ga[1][i], gb[1][jj], acc[i][jj]);
+        asm volatile("" ::"a"(acc[i][jj]));
+        if (t < 8) la.issue_one(lds, wave, k0, valid, t);
+        else lb.issue_one(lds + TILE * BK * 2, wave, k0, valid, t - 8);
+        const int f = (t & 7) >> 1;
+        const u16* base = t < 8 ? st + (wm * WM + f * 32) * BK
+                                : st + TILE * BK + (wn * WN + f * 32) * BK;
+        const uint4 x = *reinterpret_cast<const uint4*>(base + ((t & 1) ? k1f : k0f));
+        if ((t & 1) == 0) x0 = x;
+        else if (t < 8) ga[0][f] = cat8(x0, x);
+        else gb[0][f] = cat8(x0, x);
+      }
+      if constexpr (MX) {
+        const int ks = sg.kb + (valid ? j : 0);
+        const int row0 = sop ? sg.n0 : sg.m0;
+        lds_dma16(sdesc, sring_lds + (slot * 2 + sop) * (TILE * 4), lane * 16,
+                  valid ? (ks * sld + row0) * 4 : kOutOfRange);
+        const uint32_t* sw = sring + ((st - ring) / STAGE) * (2 * TILE) + srec;
+        sa8[0] = sw[wm * WM];
+        sb8[0] = sw[TILE + wn * WN];
+      }
+    }
+  };
+
   prologue(s);
   for (;;) {
     // ---- main loop over the segment's 64-wide k-steps, two stages: step j
@@ -1138,10 +1199,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel4(SkPlan pl) {
         pin8(std::integral_constant<int, 1>{});
         wait_vm_lds<0>();  // tile j+1 landed (operands and scale words)
         __syncthreads();   // tile j+1 in LDS for every wave; tile j read by every wave
-        issue_to(s, j & 1, j + 2);
-        rd8(ring + ((j + 1) & 1) * STAGE, 0, 0);  // unused after the last step
-        mma8(1);
-        pin8(std::integral_constant<int, 0>{});
+        // tile j+2's loads; the reads are unused after the last step
+        half_dma8(s, j & 1, j + 2, ring + ((j + 1) & 1) * STAGE);
       }
     } else if constexpr (AREG) {
       rd(ring, 0, 0);
