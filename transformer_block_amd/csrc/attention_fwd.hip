@@ -73,21 +73,32 @@ __global__ __launch_bounds__(256, FNST == 4 ? 2 : 3) void attn_fwd_kernel(const 
       dv.issue_none(lds + OPB * 2, wave);
     }
   };
+  // The row's queries go by DMA too, first, into the ring's last two stages
+  // (four tiles of 32 rows, 32 KB), then the first FNST - 2 key tiles; the
+  // wave waits for the queries only, reads its fragments, and after a
+  // barrier the stage they used receives key tile FNST - 2.  The first tile's
+  // products can then start while the later tiles are still on their way.
+  static_assert(BQ == 4 * BKF && FNST >= 3, "the queries fill two ring stages");
+  {
+    TileDma<D, BKF, false> dq;
+    dq.init(Qh, 2 * hl, s, wave, lane);
+    const uint32_t q_lds = kv_lds + (FNST - 2) * (STG * 2);
 #pragma unroll
-  for (int i = 0; i < FNST - 1; ++i) issue(i, kv_begin + i * BKF);
-
-  bf16x8 qf[NKS];  // fp16 query fragments (B operand of S^T = K Q^T)
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    uint4 t = make_uint4(0u, 0u, 0u, 0u);
-    if (qi < s) t = *reinterpret_cast<const uint4*>(Qh + qi * (2 * hl) + ks * 16 + g * 8);
-    qf[ks] = as_bf16x8(t);
+    for (int t = 0; t < BQ / BKF; ++t) dq.issue(q_lds + t * (OPB * 2), q0 + t * BKF, wave);
   }
-  // The query fragments are complete before the loop.  Without this wait the
-  // compiler, which does not see the DMA loads, would place a wait for every
-  // outstanding load before their first use inside the loop, draining the
-  // key tiles in flight on every iteration.
-  wait_vm_lds<0>();
+#pragma unroll
+  for (int i = 0; i < FNST - 2; ++i) issue(i, kv_begin + i * BKF);
+  wait_vm_lds<(FNST - 2) * LPT>();  // this wave's query loads landed
+  __syncthreads();                  // every wave's
+  bf16x8 qf[NKS];  // fp16 query fragments (B operand of S^T = K Q^T); rows past s are zeros
+  {
+    const u16* q_w = kv + (FNST - 2) * STG + wave * OPB;  // this wave's 32 queries
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = row_frag<D>(q_w, l32, ks * 2 + g);
+  }
+  wait_vm_lds<63>();  // (LDS only) every fragment read here ...
+  __syncthreads();    // ... and in every wave before the stage is refilled
+  issue(FNST - 2, kv_begin + (FNST - 2) * BKF);
 
   // Running max m is kept in scaled (log2) units: p = exp2(logit * sc - m).
   const float sc = kLog2e / sqrtf(static_cast<float>(D));
