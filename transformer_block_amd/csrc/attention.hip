@@ -146,6 +146,23 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   };
 #pragma unroll
   for (int i = 0; i < BNST - 1; ++i) issue(i, q_begin + i * QS);
+  // load p of issue alone (p < NP; the same loads, in the same order)
+  constexpr int NP = LPT;
+  auto issue_piece = [&](int st, int qt0, int p) {
+    const uint32_t lds = qs_lds + st * (STG * 2);
+    const uint32_t ldl = ld_base + st * (2 * 256 * 4);
+    const bool valid = qt0 < q_end;
+    constexpr int L = TileDma<D, QS, false>::LPW;
+    if (p < L) {
+      dq_r.issue_one(lds, qt0, wave, p, valid);
+    } else if (p < 2 * L) {
+      do_r.issue_one(lds + OPB * 2, qt0, wave, p - L, valid);
+    } else if (p == 2 * L) {
+      lds_dma16(lse_desc, ldl, valid ? ld_voff : kOutOfRange, valid ? qt0 * 4 : 0);
+    } else {
+      lds_dma16(dl_desc, ldl + 256 * 4, valid ? ld_voff : kOutOfRange, valid ? qt0 * 4 : 0);
+    }
+  };
 
   bf16x8 kf[NKS], vf[NKS];  // fp16 keys, bf16 values of this lane's key
 #pragma unroll
@@ -175,13 +192,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     // be in flight: loads complete in order)
     wait_vm_lds<(BNST - 2) * LPT>();
     __syncthreads();  // every wave's; the stage read last iteration is free again
-    issue(stage == 0 ? BNST - 1 : stage - 1, qt0 + (BNST - 1) * QS);
+    const int nst = stage == 0 ? BNST - 1 : stage - 1, nq = qt0 + (BNST - 1) * QS;
     const u16* q_lds = qs + stage * STG;
     const u16* do_lds = q_lds + OPB;
     const float* lse_s = ld_lds[stage][0];
     const float* dl_s = ld_lds[stage][1];
 
     const bool any = kw0 < s && qt0 + QS - 1 >= kw0 && qt0 - (kw0 + 31) < window;
+    if (!any) issue(nst, nq);
     if (any) {
       const bool full = qt0 >= kw0 + 31 && qt0 + QS - 1 - kw0 < window && qt0 + QS <= s;
       // each chain's first product takes a literal zero accumulator (no
@@ -201,13 +219,23 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
           fq[c ^ 1] = row_frag<D>(q_lds, l32, (ks + 1) * 2 + g);
           fdo[c ^ 1] = row_frag<D>(do_lds, l32, (ks + 1) * 2 + g);
         }
+        if (ks > 0) asm volatile("" : "+v"(fq[c]), "+v"(fdo[c]));
         sp = mfma32x32x16_f16(fq[c], kf[ks], ks == 0 ? zero : sp);
         dp = mfma32x32x16(fdo[c], vf[ks], ks == 0 ? zero : dp);
+        // the next stage's loads after the first NP pairs of products, one
+        // per pair: with one wave per SIMD, a burst of loads ahead of the
+        // products would hold them all up while the loads wait to issue.
+        // The empty asm statements (no instructions) keep that order.
+        if (ks < NP) {
+          asm volatile("" ::"a"(sp), "a"(dp));
+          issue_piece(nst, nq, ks);
+        }
         if (ks + 1 < NKS) {
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMAs
         }
       }
+      static_assert(NP <= NKS, "one load per pair of products");
       if (!full) {
         // a stage on the diagonal or the window's edge: keep queries in
         // [lo, hi] of this lane's key, as offsets from the lane's first query

@@ -151,6 +151,10 @@ struct TileDma {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) lds_dma16(desc, lds + (wave * LPW + i) * 1024, off[i], soff);
   }
+  // load i (0..LPW-1) of issue, or of issue_none (valid false), alone
+  __device__ __forceinline__ void issue_one(uint32_t lds, int row0, int wave, int i, bool valid) const {
+    lds_dma16(desc, lds + (wave * LPW + i) * 1024, off[i], valid ? row0 * ld * 2 : kOutOfRange);
+  }
   // the same loads with an offset beyond any operand: they return zeros
   // without touching memory (zeros land in [lds, lds + 2 R D)), so that a
   // wave's count of loads in flight stays the same past the last tile
