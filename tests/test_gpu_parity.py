@@ -57,6 +57,9 @@ EDGE_CASES = [
     # and one head whose 32 long causal rows are cut into many chunks
     ("many_heads_b9_n64_d64", W("mh", 9, 130, 4096, 64, 64, 256, 1000, seed=33), False),
     ("long_rows_s4096_one_head", W("lr", 1, 4096, 128, 1, 128, 256, 4096, seed=34), False),
+    # 2304 rows of 128 queries at d = 128, each with a ragged last row: enough
+    # rows for the dispatch model to launch the three-per-CU forward build
+    ("many_rows_b96_s1000_d128", W("mr", 96, 1000, 384, 3, 128, 256, 200, seed=35), False),
 ]
 
 
