@@ -226,26 +226,63 @@ __global__ __launch_bounds__(256, FNST == 4 ? 2 : 3) void attn_fwd_kernel(const 
     __syncthreads();
     if (__builtin_amdgcn_readfirstlane(arrival) != item.nchunks - 1) return;
     if (tid == 0) rs.counters[row_id] = 0;
+    // Chunks in batches of MB, every load of a batch issued before its values
+    // are used (each is a round trip to device memory): the maxima first,
+    // then per batch the m and l, and the o partials summed in chunk order.
+    // The two-per-CU build at d = 128 has the registers to keep this chunk's
+    // own o (the bits it stored) instead of loading it back.
+    constexpr int MB = 8;
+    const int nch = item.nchunks;
+    const float* ml0 = rs.partials + (slot0 + first_slot) * PER_SLOT + BQ * D + tid;
     float mm = -INFINITY;
-    for (int c = 0; c < item.nchunks; ++c)
-      mm = fmaxf(mm, ld_dev(rs.partials + (slot0 + first_slot + c) * PER_SLOT + BQ * D + tid));
+    for (int c0 = 0; c0 < nch; c0 += MB) {
+      float mv[MB];
+#pragma unroll
+      for (int k = 0; k < MB; ++k)
+        mv[k] = c0 + k < nch ? ld_dev(ml0 + static_cast<size_t>(c0 + k) * PER_SLOT) : -INFINITY;
+#pragma unroll
+      for (int k = 0; k < MB; ++k) mm = fmaxf(mm, mv[k]);
+    }
     const float ms = (mm == -INFINITY) ? 0.0f : mm;
+    constexpr bool OWN = FNST == 4 && D == 128;
+    f32x16 own[OWN ? ND : 1];
+    if constexpr (OWN) {
+#pragma unroll
+      for (int db = 0; db < ND; ++db) own[db] = o[db];
+    }
     l = 0.0f;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[db][e] = 0.0f;
-    for (int c = 0; c < item.nchunks; ++c) {
-      float* pp = rs.partials + (slot0 + first_slot + c) * PER_SLOT;
-      const __amdgpu_buffer_rsrc_t pr = dev_rsrc(pp, PER_SLOT);
-      const float f = exp2f(ld_dev(pp + BQ * D + tid) - ms);
-      l += f * ld_dev(pp + BQ * D + 256 + tid);
+    for (int c0 = 0; c0 < nch; c0 += MB) {
+      float mv[MB], lv[MB];
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        float x[16];
-        ld16_dev(pr, (wave * ND + db) * 1024, lane, x);
+      for (int k = 0; k < MB; ++k) {
+        const float* q = ml0 + static_cast<size_t>(c0 + k) * PER_SLOT;
+        mv[k] = c0 + k < nch ? ld_dev(q) : 0.0f;
+        lv[k] = c0 + k < nch ? ld_dev(q + 256) : 0.0f;
+      }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[db][e] += f * x[e];
+      for (int k = 0; k < MB; ++k) {
+        const int c = c0 + k;
+        if (c >= nch) break;
+        const float f = exp2f(mv[k] - ms);
+        l += f * lv[k];
+        const __amdgpu_buffer_rsrc_t pr =
+            dev_rsrc(rs.partials + (slot0 + first_slot + c) * PER_SLOT, PER_SLOT);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          float x[16];
+          if (OWN && c == item.chunk) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) x[e] = own[db][e];
+          } else {
+            ld16_dev(pr, (wave * ND + db) * 1024, lane, x);
+          }
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[db][e] += f * x[e];
+        }
       }
     }
     m = mm;
