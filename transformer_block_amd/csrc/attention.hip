@@ -301,20 +301,36 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     __syncthreads();
     if (__builtin_amdgcn_readfirstlane(arrival) != item.nchunks - 1) return;
     if (tid == 0) rsp.counters[row_id] = 0;
+    // At d = 128 (one workgroup per CU) this chunk's own partial stays in
+    // registers and only the others are loaded back; the smaller build would
+    // lose its second workgroup per CU to the copy. The sum keeps chunk order.
+    constexpr bool OWN = D == 128;
+    f32x16 ok[OWN ? ND : 1], ov[OWN ? ND : 1];
+    if constexpr (OWN) {
+#pragma unroll
+      for (int db = 0; db < ND; ++db) { ok[db] = dk[db]; ov[db] = dv[db]; }
+    }
     for (int c = 0; c < item.nchunks; ++c) {
-      const __amdgpu_buffer_rsrc_t pr =
-          dev_rsrc(rsp.partials + (slot0 + first_slot + c) * PER_SLOT, PER_SLOT);
+      f32x16 a[ND], v[ND];
+      if (OWN && c == item.chunk) {
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        float a[16], v[16];
-        ld16_dev(pr, (wave * ND + db) * 1024, lane, a);
-        ld16_dev(pr, BKB * D + (wave * ND + db) * 1024, lane, v);
+        for (int db = 0; db < ND; ++db) { a[db] = ok[OWN ? db : 0]; v[db] = ov[OWN ? db : 0]; }
+      } else {
+        const __amdgpu_buffer_rsrc_t pr =
+            dev_rsrc(rsp.partials + (slot0 + first_slot + c) * PER_SLOT, PER_SLOT);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          dk[db][e] = c == 0 ? a[e] : dk[db][e] + a[e];
-          dv[db][e] = c == 0 ? v[e] : dv[db][e] + v[e];
+        for (int db = 0; db < ND; ++db) {
+          ld16_dev(pr, (wave * ND + db) * 1024, lane, reinterpret_cast<float*>(&a[db]));
+          ld16_dev(pr, BKB * D + (wave * ND + db) * 1024, lane, reinterpret_cast<float*>(&v[db]));
         }
       }
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          dk[db][e] = c == 0 ? a[db][e] : dk[db][e] + a[db][e];
+          dv[db][e] = c == 0 ? v[db][e] : dv[db][e] + v[db][e];
+        }
     }
   }
 
@@ -503,16 +519,26 @@ __global__ __launch_bounds__(256, BKQ == 32 ? 2 : 1) void attn_bwd_dq_kernel(
     __syncthreads();
     if (__builtin_amdgcn_readfirstlane(arrival) != item.nchunks - 1) return;
     if (tid == 0) rsp.counters[row_id] = 0;
+    // This chunk's own partial is still in registers: only the others are
+    // loaded back, and the sum keeps chunk order.
+    f32x16 oq[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) oq[db] = dq[db];
     for (int c = 0; c < item.nchunks; ++c) {
-      const __amdgpu_buffer_rsrc_t pr =
-          dev_rsrc(rsp.partials + (slot0 + first_slot + c) * PER_SLOT, PER_SLOT);
+      f32x16 a[ND];
+      if (c == item.chunk) {
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        float a[16];
-        ld16_dev(pr, (wave * ND + db) * 1024, lane, a);
+        for (int db = 0; db < ND; ++db) a[db] = oq[db];
+      } else {
+        const __amdgpu_buffer_rsrc_t pr =
+            dev_rsrc(rsp.partials + (slot0 + first_slot + c) * PER_SLOT, PER_SLOT);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) dq[db][e] = c == 0 ? a[e] : dq[db][e] + a[e];
+        for (int db = 0; db < ND; ++db) ld16_dev(pr, (wave * ND + db) * 1024, lane, reinterpret_cast<float*>(&a[db]));
       }
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dq[db][e] = c == 0 ? a[db][e] : dq[db][e] + a[db][e];
     }
   }
 
