@@ -109,32 +109,36 @@ __global__ __launch_bounds__(LN_THREADS) void ln_fwd_kernel(const u16* __restric
 // dst[r][c] = fp16(src[r][c]) for a [rows, cols] block of a bf16 matrix
 // (cols a multiple of 8, row strides ld_src and ld_dst in elements): the
 // fp16 copy of the query/key columns of W_qkv for the fp16 q, k product.
-// The block's 16-byte chunks are numbered row by row; thread t of workgroup
-// g converts chunks 2048 g + t + 256 u (u < CAST_CHUNKS), all eight loads
+// The block's 16-byte chunks are numbered row by row; workgroup g converts
+// chunks [cpb g, cpb (g + 1)), thread t those at t + 256 u, all of its loads
 // issued before the first store, consecutive threads on consecutive chunks.
+// The launcher makes the grid one wave of the device's resident workgroups
+// where the chunks allow, each with the same share to within one chunk per
+// thread (no second, mostly idle wave of workgroups).
 // The conversion is exact for every bf16 value inside the fp16 normal range;
 // smaller magnitudes round to fp16 subnormals (absolute error <= 2^-25) and
 // larger ones saturate at 65504.
-constexpr int CAST_CHUNKS = 8;
+constexpr int CAST_MAX_PER = 10;  // chunks per thread at most
 __global__ __launch_bounds__(256) void cast_f16_kernel(const u16* __restrict__ src, int ld_src,
                                                        u16* __restrict__ dst, int ld_dst,
-                                                       int rows, int cols8) {
+                                                       int rows, int cols8, int cpb) {
   const int total = rows * cols8;  // < 2^31 (checked by the launcher)
-  const int base = blockIdx.x * (256 * CAST_CHUNKS) + threadIdx.x;
-  uint4 v[CAST_CHUNKS];
-  int off[CAST_CHUNKS];  // destination element offset, -1 past the block
+  const int first = blockIdx.x * cpb, len = min(cpb, total - first);
+  uint4 v[CAST_MAX_PER];
+  int off[CAST_MAX_PER];  // destination element offset, -1 past the block
 #pragma unroll
-  for (int u = 0; u < CAST_CHUNKS; ++u) {
-    const int idx = base + 256 * u;
+  for (int u = 0; u < CAST_MAX_PER; ++u) {
+    const int rel = static_cast<int>(threadIdx.x) + 256 * u;
     off[u] = -1;
-    if (idx < total) {
+    if (rel < len) {
+      const int idx = first + rel;
       const int r = idx / cols8, c = idx - r * cols8;
       v[u] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(r) * ld_src + c * 8);
       off[u] = r * ld_dst + c * 8;
     }
   }
 #pragma unroll
-  for (int u = 0; u < CAST_CHUNKS; ++u) {
+  for (int u = 0; u < CAST_MAX_PER; ++u) {
     if (off[u] >= 0) {
       const uint32_t* w = reinterpret_cast<const uint32_t*>(&v[u]);
       uint4 o;
@@ -338,9 +342,19 @@ hipError_t launch_cast_f16(const u16* src, int ld_src, int rows, int cols, u16* 
       static_cast<long>(rows) * ld_dst >= (1L << 31) || static_cast<long>(rows) * (cols / 8) >= (1L << 31))
     return hipErrorInvalidValue;
   const long chunks = static_cast<long>(rows) * (cols / 8);
-  const int blocks = static_cast<int>((chunks + 256 * CAST_CHUNKS - 1) / (256 * CAST_CHUNKS));
-  hipLaunchKernelGGL(cast_f16_kernel, dim3(blocks), dim3(256), 0, s, src, ld_src, dst, ld_dst,
-                     rows, cols / 8);
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cast_f16_kernel, 256, 0) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  const int cus = device_compute_units();
+  const long slots = static_cast<long>(per_cu) * (cus > 0 ? cus : 256);
+  // one wave of workgroups if each thread's share stays within CAST_MAX_PER
+  // chunks, else as many full workgroups as that takes
+  const long blocks = std::max<long>(std::min<long>(slots, (chunks + 255) / 256),
+                                     (chunks + 256L * CAST_MAX_PER - 1) / (256L * CAST_MAX_PER));
+  const long cpb = (chunks + blocks - 1) / blocks;  // <= 256 * CAST_MAX_PER
+  hipLaunchKernelGGL(cast_f16_kernel, dim3(static_cast<unsigned>((chunks + cpb - 1) / cpb)), dim3(256),
+                     0, s, src, ld_src, dst, ld_dst, rows, cols / 8, static_cast<int>(cpb));
   return hipGetLastError();
 }
 
