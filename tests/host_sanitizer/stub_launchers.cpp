@@ -196,7 +196,9 @@ hipError_t launch_dropout_mask(uint8_t* mask, long n, const Dropout&, hipStream_
 }
 
 hipError_t launch_layernorm_fwd(const u16* x, const u16* gamma, const u16* beta, u16* a, u16* a16,
-                                float* mu, float* rstd, int T, int h, float, hipStream_t, bool) {
+                                float* mu, float* rstd, int T, int h, float, hipStream_t, bool,
+                                int* clear, int nclear) {
+  touch(clear, static_cast<size_t>(nclear > 0 ? nclear : 0) * 4);
   touch(x, static_cast<size_t>(T) * h * 2);
   touch(a, static_cast<size_t>(T) * h * 2);
   touch(a16, static_cast<size_t>(T) * h * 2);

@@ -213,9 +213,11 @@ hipError_t launch_dropout_mask(uint8_t* mask, long n, const Dropout& d, hipStrea
 // LayerNorm forward over rows of x [T, h]: a = bf16(LN(x)) and an fp16 copy
 // a16 = fp16(LN(x)) of the same fp32 values (skipped when a16 is null), mu,
 // rstd (fp32).  rms: RMSNorm instead (no mean, no beta; mu is written as 0).
+// clear[0, nclear), if given, is set to zero by the same launch.
 hipError_t launch_layernorm_fwd(const u16* x, const u16* gamma, const u16* beta,
                                 u16* a, u16* a16, float* mu, float* rstd, int T, int h,
-                                float eps, hipStream_t stream, bool rms = false);
+                                float eps, hipStream_t stream, bool rms = false,
+                                int* clear = nullptr, int nclear = 0);
 
 // dst = fp16(src) for a [rows, cols] block of a row-major bf16 matrix (cols
 // and both row strides multiples of 8; rounding to nearest even, saturated

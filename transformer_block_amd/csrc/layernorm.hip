@@ -45,6 +45,8 @@ __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
 
 // RMS: RMSNorm instead, a = gamma * x / sqrt(mean(x^2) + eps), no beta; the
 // row mean is stored as 0 so that the backward's xhat = (x - mu) * rstd holds.
+// clear[0, nclear) is set to zero on the way (the arrival counters of the
+// launches that follow in the same stream), which saves a launch of its own.
 template <bool RMS>
 __global__ __launch_bounds__(LN_THREADS) void ln_fwd_kernel(const u16* __restrict__ x,
                                                             const u16* __restrict__ gamma,
@@ -53,9 +55,12 @@ __global__ __launch_bounds__(LN_THREADS) void ln_fwd_kernel(const u16* __restric
                                                             u16* __restrict__ a16,
                                                             float* __restrict__ mu_out,
                                                             float* __restrict__ rstd_out,
-                                                            int h, float eps) {
+                                                            int h, float eps,
+                                                            int* __restrict__ clear, int nclear) {
   __shared__ float red[4];
   const int row = blockIdx.x, tid = threadIdx.x;
+  for (int i = row * LN_THREADS + tid; i < nclear; i += static_cast<int>(gridDim.x) * LN_THREADS)
+    clear[i] = 0;
   const int nch = h >> 3;
   const u16* xr = x + static_cast<size_t>(row) * h;
   float v[LN_MAXCH][8];
@@ -328,10 +333,11 @@ __global__ __launch_bounds__(64 * LNR_WAVES) void ln_bwd_reduce_kernel(
 
 hipError_t launch_layernorm_fwd(const u16* x, const u16* gamma, const u16* beta, u16* a,
                                 u16* a16, float* mu, float* rstd, int T, int h, float eps,
-                                hipStream_t s, bool rms) {
-  if (T <= 0) return hipSuccess;
+                                hipStream_t s, bool rms, int* clear, int nclear) {
+  if (clear == nullptr || nclear < 0) nclear = 0;
+  if (T <= 0) return launch_zero_i32(clear, nclear, s);
   hipLaunchKernelGGL(rms ? ln_fwd_kernel<true> : ln_fwd_kernel<false>, dim3(T), dim3(LN_THREADS),
-                     0, s, x, gamma, beta, a, a16, mu, rstd, h, eps);
+                     0, s, x, gamma, beta, a, a16, mu, rstd, h, eps, clear, nclear);
   return hipGetLastError();
 }
 

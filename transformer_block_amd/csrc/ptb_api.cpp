@@ -547,11 +547,11 @@ int32_t ptb_forward_timed(const ptb_dims* dims, const void* x, const void* ln_ga
   const u16* X = static_cast<const u16*>(x);
   const u16* Wqkv = static_cast<const u16*>(w_qkv);
 
-  PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
+  // the LayerNorm launch also clears the arrival counters of the launches after it
   PTB_STAGE(0, ptb::launch_layernorm_fwd(X, static_cast<const u16*>(ln_gamma),
                                     static_cast<const u16*>(ln_beta), a, a16, mu, rstd,
                                     static_cast<int>(s.T), static_cast<int>(s.h), dims->ln_eps,
-                                    strm, s.rms));
+                                    strm, s.rms, gs.counters, gs.max_tiles));
   PTB_STAGE(1, ptb::launch_cast_f16(Wqkv, static_cast<int>(3 * s.hl), static_cast<int>(s.h),
                                     static_cast<int>(2 * s.hl), wqk16,
                                     static_cast<int>(2 * s.hl), strm));
@@ -785,10 +785,11 @@ int32_t ptb_serial_forward_timed(const ptb_dims* dims, const void* x, const void
   const u16* Wqkv = static_cast<const u16*>(w_qkv);
   const int T = static_cast<int>(s.T), h = static_cast<int>(s.h);
 
-  PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
+  // the LayerNorm launch also clears the arrival counters of the launches after it
   PTB_STAGE(0, ptb::launch_layernorm_fwd(X, static_cast<const u16*>(ln1_gamma),
                                          static_cast<const u16*>(ln1_beta), a1, a1_16, mu1,
-                                         rstd1, T, h, dims->ln_eps, strm, s.rms));
+                                         rstd1, T, h, dims->ln_eps, strm, s.rms, gs.counters,
+                                         gs.max_tiles));
   PTB_STAGE(1, ptb::launch_cast_f16(Wqkv, static_cast<int>(3 * s.hl), h,
                                     static_cast<int>(2 * s.hl), wqk16,
                                     static_cast<int>(2 * s.hl), strm));
@@ -1253,13 +1254,13 @@ int32_t ptb_fp8_forward(const ptb_dims* dims, int32_t recipe, const void* x,
   float* samax = at<float>(saved, SL.amax);  // [0] a, [1] [c | g] (current scaling)
   const float* wamax = mx ? nullptr : at<float>(fp8_weights, WL.amax);
 
-  PTB_HIP(ptb::launch_zero_i32(gs.counters, gs.max_tiles, strm));
   PTB_HIP(ptb::launch_zero_i32(reinterpret_cast<int*>(samax), 2, strm));
+  // the LayerNorm launch also clears the arrival counters of the launches after it
   PTB_STAGE(0, ptb::launch_layernorm_fwd(static_cast<const u16*>(x),
                                     static_cast<const u16*>(ln_gamma),
                                     static_cast<const u16*>(ln_beta), a, nullptr, mu, rstd,
                                     static_cast<int>(s.T), static_cast<int>(s.h), dims->ln_eps,
-                                    strm, s.rms));
+                                    strm, s.rms, gs.counters, gs.max_tiles));
   // a row-wise for the [QKV | FC1] product, transposed (stashed) for its
   // weight gradient
   PTB_STAGE(1, cast_copies(mx, cast_one(a, s.h, s.T, s.h), ptb::FP8_E4M3, samax,
