@@ -230,7 +230,8 @@ int32_t ptb_dropout_mask(uint64_t seed, uint32_t stream, float p, int64_t n, voi
  *            backward (3 kernels), 2 wgrad [O ; FC2], 3 dgrad [QKV | FC1],
  *            4 wgrad [QKV | FC1], 5 LayerNorm backward (2 kernels).
  * Each GEMM stage is exactly one kernel launch.  Each call also clears the
- * tile counters in `workspace` with one small kernel ahead of stage 0. */
+ * tile counters in `workspace`: the forward inside stage 0's LayerNorm
+ * launch, the backward with one small kernel ahead of stage 0. */
 #define PTB_FWD_STAGES 5
 #define PTB_BWD_STAGES 6
 int32_t ptb_forward_timed(const ptb_dims* dims,
