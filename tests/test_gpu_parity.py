@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from transformer_block_amd import inputs as I
-from transformer_block_amd.runner import LayerStack, bf16_to_numpy_f64
+from transformer_block_amd.runner import Fp8Layer, LayerStack, SerialBlock, bf16_to_numpy_f64
 
 from .helpers import REL_TOL, log, oracle_lse2, oracle_run, rel_fro
 
@@ -137,6 +137,36 @@ def test_repeat_runs_are_bitwise_identical():
     st.step()
     torch.cuda.synchronize()
     second = [st.y, st.dx] + list(st.grads[0].values())
+    for a, b in zip(first, second):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("kind", ["parallel", "serial", "fp8_current", "fp8_mx"])
+def test_a_dirty_workspace_gives_the_same_bits(kind):
+    """Every call clears the arrival counters it finds in `workspace` (the
+    forward inside its LayerNorm launch, the backward with a kernel of its
+    own) and writes every other scratch value before reading it: a step on a
+    workspace filled with 0xFF bytes reproduces a step on the workspace the
+    previous step left, bit for bit.  Uncleared counters would leave split
+    GEMM tiles and attention rows unmerged (there is no wait on them, so the
+    outcome would be wrong values, not a hang)."""
+    # K = 2048 in the weight gradients: their tail tiles are split (and the
+    # attention rows too), so the counters are in use
+    w = W("dirty", 1, 2048, 256, 2, 128, 512, 300, seed=36)
+    inp = I.make_inputs(w, random_ln=True)
+    st = (LayerStack(w, inp, "cuda") if kind == "parallel" else
+          SerialBlock(w, inp, "cuda") if kind == "serial" else
+          Fp8Layer(w, inp, "cuda", recipe=kind[4:]))
+    grads = st.grads[0] if kind == "parallel" else st.grads
+    log(f"dirty workspace: {kind}, {st.workspace.numel()} bytes")
+    st.step()
+    torch.cuda.synchronize()
+    first = [st.y.clone(), st.dx.clone()] + [t.clone() for t in grads.values()]
+    st.workspace.fill_(255)
+    torch.cuda.synchronize()
+    st.step()
+    torch.cuda.synchronize()
+    second = [st.y, st.dx] + list(grads.values())
     for a, b in zip(first, second):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
