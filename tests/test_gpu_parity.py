@@ -141,28 +141,38 @@ def test_repeat_runs_are_bitwise_identical():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("shape", ["split", "ragged"])
 @pytest.mark.parametrize("kind", ["parallel", "serial", "fp8_current", "fp8_mx"])
-def test_a_dirty_workspace_gives_the_same_bits(kind):
+def test_a_dirty_workspace_gives_the_same_bits(kind, shape):
     """Every call clears the arrival counters it finds in `workspace` (the
     forward inside its LayerNorm launch, the backward with a kernel of its
-    own) and writes every other scratch value before reading it: a step on a
-    workspace filled with 0xFF bytes reproduces a step on the workspace the
+    own) and writes every other scratch, stash and FP8-copy value, padding
+    included, before it is read: a step on `workspace`, `saved` and the FP8
+    weight copies filled with 0xFF bytes reproduces a step on what the
     previous step left, bit for bit.  Uncleared counters would leave split
-    GEMM tiles and attention rows unmerged (there is no wait on them, so the
+    GEMM tiles and attention rows unmerged (nothing waits on them, so the
     outcome would be wrong values, not a hang)."""
-    # K = 2048 in the weight gradients: their tail tiles are split (and the
-    # attention rows too), so the counters are in use
-    w = W("dirty", 1, 2048, 256, 2, 128, 512, 300, seed=36)
+    if shape == "split":
+        # K = 2048 in the weight gradients: their tail tiles are split (and
+        # the attention rows too), so the counters are in use
+        w = W("dirty", 1, 2048, 256, 2, 128, 512, 300, seed=36)
+    else:
+        # 400 tokens: the FP8 copies pad their token dimension to 512
+        w = W("dirtyr", 2, 200, 256, 2, 128, 512, 80, seed=37)
     inp = I.make_inputs(w, random_ln=True)
     st = (LayerStack(w, inp, "cuda") if kind == "parallel" else
           SerialBlock(w, inp, "cuda") if kind == "serial" else
           Fp8Layer(w, inp, "cuda", recipe=kind[4:]))
     grads = st.grads[0] if kind == "parallel" else st.grads
-    log(f"dirty workspace: {kind}, {st.workspace.numel()} bytes")
+    dirty = [st.workspace] + (list(st.saved) if kind == "parallel" else [st.saved])
+    if kind.startswith("fp8"):
+        dirty.append(st.fp8_weights)
+    log(f"dirty workspace: {kind}, {shape}, {sum(t.numel() for t in dirty)} bytes")
     st.step()
     torch.cuda.synchronize()
     first = [st.y.clone(), st.dx.clone()] + [t.clone() for t in grads.values()]
-    st.workspace.fill_(255)
+    for t in dirty:
+        t.fill_(255)
     torch.cuda.synchronize()
     st.step()
     torch.cuda.synchronize()
